@@ -1,0 +1,278 @@
+"""CPU float64 oracle for large-head-dim scaled-dot-product attention (forward + backward).
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path imports this module: only the tests, the
+``smoke()`` check and the benchmark's ``cpu_baseline`` leg call it. It shares no code, tables or
+helpers with the HIP kernels.
+
+What is computed, and where the ffpa-attn user guide fixes it:
+
+* The method keeps the contract of PyTorch's scaled_dot_product_attention ("Backends Overview",
+  section "Automatic SDPA fallback": the entry point is SDPA-aligned). So per query head h, with
+  S = scale * Q_h K_g^T, the output is O = softmax(S) V_g and the log-sum-exp is the natural-log
+  LSE_i = log sum_j exp(S_ij) over the legal keys j.
+* Causal masking is tail-aligned, i.e. bottom-right: key j is legal for query i iff
+  j <= i + (Nkv - Nq) ("Triton Backend", section "Feature support", Shapes; "CuTe-DSL Backend",
+  section "Hard constraints", SM100 dedicated range; section "Varlen (packed THD) API": applied per
+  sequence).
+* GQA/MQA is a zero-stride broadcast of the KV heads: query head h reads KV head h // (Hq/Hkv), and
+  the gradient of a broadcast is the sum over the query heads that share it ("CuTe-DSL Backend",
+  "Hard constraints").
+* Rows with no legal key produce O = 0, LSE = -inf and exactly zero gradient ("CuTe-DSL Backend",
+  "Hard constraints").
+* LSE is float32 [H_q, T_q] for packed varlen input ("CuTe-DSL Backend", "Varlen (packed THD)
+  API"); dense LSE is [B, H_q, N_q] (a reading: the pages state only the varlen shape).
+* The backward has the four stages preprocess, dV, dK, dQ ("CuTe-DSL Backend", "Blackwell status"):
+  Delta = rowsum(dO * O), dV = P^T dO, dP = dO V^T, dS = P * (dP - Delta), dK = scale dS^T Q,
+  dQ = scale dS K. These are the exact gradients of L = sum(dO * O); the oracle writes the
+  definition out and leaves the split into kernels to the GPU side.
+
+Everything is the plain definition in float64 NumPy: S is materialised per (batch, KV group).
+Queries are independent rows, so they are processed in row blocks to bound memory; that changes
+nothing but the order in which the dK/dV sums over query rows are added.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+__all__ = [
+    "legal_mask", "softmax_rows", "group_forward", "group_backward",
+    "attn_fwd", "attn_bwd", "varlen_fwd", "varlen_bwd", "preprocess_delta", "fwd_rows",
+]
+
+# Query rows per block when S is materialised: 2048 rows x 8192 keys x 8 B = 128 MiB per array.
+_ROW_BLOCK = 2048
+
+
+def legal_mask(rows: np.ndarray, nq: int, nkv: int, causal: bool) -> np.ndarray:
+    """Boolean [len(rows), nkv]: key j is legal for query i (tail-aligned causal when ``causal``)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(nkv, dtype=np.int64)[None, :]
+    if not causal:
+        return np.ones((rows.shape[0], nkv), dtype=bool)
+    return j <= rows[:, None] + (nkv - nq)
+
+
+def softmax_rows(s: np.ndarray, legal: np.ndarray):
+    """Row softmax over the legal entries of ``s``; returns (P, LSE).
+
+    Rows without a legal entry get P = 0 and LSE = -inf.
+    """
+    has = legal.any(axis=1)
+    s_masked = np.where(legal, s, -np.inf)
+    m = np.where(has, np.max(np.where(legal, s, -np.inf), axis=1, initial=-np.inf), 0.0)
+    e = np.where(legal, np.exp(s_masked - m[:, None]), 0.0)
+    z = e.sum(axis=1)
+    safe_z = np.where(has, z, 1.0)
+    p = np.where(has[:, None], e / safe_z[:, None], 0.0)
+    lse = np.where(has, m + np.log(safe_z), -np.inf)
+    return p, lse
+
+
+def group_forward(qg: np.ndarray, kg: np.ndarray, vg: np.ndarray, scale: float, causal: bool):
+    """One KV group. qg [G, Nq, D]; kg, vg [Nkv, D]. Returns O [G, Nq, D], LSE [G, Nq]."""
+    g_, nq, d = qg.shape
+    nkv = kg.shape[0]
+    o = np.zeros((g_, nq, d), dtype=np.float64)
+    lse = np.full((g_, nq), -np.inf, dtype=np.float64)
+    if nq == 0 or nkv == 0:
+        return o, lse
+    for h in range(g_):
+        for r0 in range(0, nq, _ROW_BLOCK):
+            rows = np.arange(r0, min(nq, r0 + _ROW_BLOCK))
+            s = scale * (qg[h, rows] @ kg.T)
+            p, l_ = softmax_rows(s, legal_mask(rows, nq, nkv, causal))
+            o[h, rows] = p @ vg
+            lse[h, rows] = l_
+    return o, lse
+
+
+def group_backward(qg, kg, vg, dog, scale: float, causal: bool):
+    """Gradients of L = sum(dO * O) for one KV group.
+
+    qg, dog [G, Nq, D]; kg, vg [Nkv, D]. Returns dQ [G, Nq, D], dK [Nkv, D], dV [Nkv, D], and the
+    forward's O [G, Nq, D], LSE [G, Nq] and Delta [G, Nq] (float64).
+    """
+    g_, nq, d = qg.shape
+    nkv = kg.shape[0]
+    dq = np.zeros_like(qg, dtype=np.float64)
+    dk = np.zeros((nkv, d), dtype=np.float64)
+    dv = np.zeros((nkv, d), dtype=np.float64)
+    o = np.zeros((g_, nq, d), dtype=np.float64)
+    lse = np.full((g_, nq), -np.inf, dtype=np.float64)
+    delta = np.zeros((g_, nq), dtype=np.float64)
+    if nq == 0 or nkv == 0:
+        return dq, dk, dv, o, lse, delta
+    for h in range(g_):
+        for r0 in range(0, nq, _ROW_BLOCK):
+            rows = np.arange(r0, min(nq, r0 + _ROW_BLOCK))
+            q_b = qg[h, rows]
+            do_b = dog[h, rows]
+            s = scale * (q_b @ kg.T)
+            p, l_ = softmax_rows(s, legal_mask(rows, nq, nkv, causal))
+            o_b = p @ vg
+            # Stage 1 (preprocess): Delta_i = sum_d dO_id * O_id.
+            dlt = np.sum(do_b * o_b, axis=1)
+            # Stage 2 (dV): dV += P^T dO.
+            dv += p.T @ do_b
+            # dP = dO V^T ; dS = P * (dP - Delta).
+            dp = do_b @ vg.T
+            ds = p * (dp - dlt[:, None])
+            # Stage 3 (dK): dK += scale dS^T Q.
+            dk += scale * (ds.T @ q_b)
+            # Stage 4 (dQ): dQ = scale dS K.
+            dq[h, rows] = scale * (ds @ kg)
+            o[h, rows] = o_b
+            lse[h, rows] = l_
+            delta[h, rows] = dlt
+    return dq, dk, dv, o, lse, delta
+
+
+def _threads() -> int:
+    n = os.environ.get("FFPA_ORACLE_THREADS")
+    if n:
+        return max(1, int(n))
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _map_groups(fn, items):
+    workers = min(_threads(), max(1, len(items)))
+    if workers == 1:
+        return [fn(it) for it in items]
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))
+
+
+def attn_fwd(q, k, v, *, scale: float, causal: bool):
+    """Dense forward. q [B,Hq,Nq,D]; k, v [B,Hkv,Nkv,D]. Returns (O [B,Hq,Nq,D], LSE [B,Hq,Nq])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    b, hq, nq, d = q.shape
+    hkv = k.shape[1]
+    assert hq % hkv == 0, "Hq must be a multiple of Hkv"
+    gsz = hq // hkv
+    o = np.zeros((b, hq, nq, d))
+    lse = np.zeros((b, hq, nq))
+    items = [(bi, g) for bi in range(b) for g in range(hkv)]
+
+    def run(it):
+        bi, g = it
+        return group_forward(q[bi, g * gsz:(g + 1) * gsz], k[bi, g], v[bi, g], scale, causal)
+
+    for (bi, g), (og, lg) in zip(items, _map_groups(run, items)):
+        o[bi, g * gsz:(g + 1) * gsz] = og
+        lse[bi, g * gsz:(g + 1) * gsz] = lg
+    return o, lse
+
+
+def attn_bwd(q, k, v, do, *, scale: float, causal: bool):
+    """Dense backward of L = sum(dO * O). Returns (dQ, dK, dV) float64 with the input shapes."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    b, hq, nq, d = q.shape
+    hkv = k.shape[1]
+    gsz = hq // hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    items = [(bi, g) for bi in range(b) for g in range(hkv)]
+
+    def run(it):
+        bi, g = it
+        sl = slice(g * gsz, (g + 1) * gsz)
+        return group_backward(q[bi, sl], k[bi, g], v[bi, g], do[bi, sl], scale, causal)[:3]
+
+    for (bi, g), (dqg, dkg, dvg) in zip(items, _map_groups(run, items)):
+        dq[bi, g * gsz:(g + 1) * gsz] = dqg
+        dk[bi, g] = dkg
+        dv[bi, g] = dvg
+    return dq, dk, dv
+
+
+def preprocess_delta(o, do) -> np.ndarray:
+    """Backward stage 1: Delta = rowsum(dO * O) over the last axis."""
+    return np.sum(_f64(do) * _f64(o), axis=-1)
+
+
+def _seq_slices(cu):
+    cu = [int(x) for x in _f64(cu).astype(np.int64)]
+    return [(cu[s], cu[s + 1]) for s in range(len(cu) - 1)]
+
+
+def varlen_fwd(q, k, v, cu_q, cu_k, *, scale: float, causal: bool):
+    """Packed forward. q [Tq,Hq,D]; k, v [Tk,Hkv,D]; cu_* int [B+1].
+
+    Returns (O [Tq,Hq,D], LSE [Hq,Tq]). Each sequence s attends within its own slice, with the
+    causal mask aligned to the end of that slice.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    tq, hq, d = q.shape
+    hkv = k.shape[1]
+    gsz = hq // hkv
+    o = np.zeros((tq, hq, d))
+    lse = np.full((hq, tq), -np.inf)
+    sq, sk = _seq_slices(cu_q), _seq_slices(cu_k)
+    items = [(s, g) for s in range(len(sq)) for g in range(hkv)]
+
+    def run(it):
+        s, g = it
+        (q0, q1), (k0, k1) = sq[s], sk[s]
+        qg = np.transpose(q[q0:q1, g * gsz:(g + 1) * gsz], (1, 0, 2))
+        return group_forward(qg, k[k0:k1, g], v[k0:k1, g], scale, causal)
+
+    for (s, g), (og, lg) in zip(items, _map_groups(run, items)):
+        q0, q1 = sq[s]
+        o[q0:q1, g * gsz:(g + 1) * gsz] = np.transpose(og, (1, 0, 2))
+        lse[g * gsz:(g + 1) * gsz, q0:q1] = lg
+    return o, lse
+
+
+def varlen_bwd(q, k, v, do, cu_q, cu_k, *, scale: float, causal: bool):
+    """Packed backward. Returns (dQ [Tq,Hq,D], dK [Tk,Hkv,D], dV [Tk,Hkv,D]) float64."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    tq, hq, d = q.shape
+    hkv = k.shape[1]
+    gsz = hq // hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    sq, sk = _seq_slices(cu_q), _seq_slices(cu_k)
+    items = [(s, g) for s in range(len(sq)) for g in range(hkv)]
+
+    def run(it):
+        s, g = it
+        (q0, q1), (k0, k1) = sq[s], sk[s]
+        sl = slice(g * gsz, (g + 1) * gsz)
+        qg = np.transpose(q[q0:q1, sl], (1, 0, 2))
+        dog = np.transpose(do[q0:q1, sl], (1, 0, 2))
+        return group_backward(qg, k[k0:k1, g], v[k0:k1, g], dog, scale, causal)[:3]
+
+    for (s, g), (dqg, dkg, dvg) in zip(items, _map_groups(run, items)):
+        (q0, q1), (k0, k1) = sq[s], sk[s]
+        dq[q0:q1, g * gsz:(g + 1) * gsz] = np.transpose(dqg, (1, 0, 2))
+        dk[k0:k1, g] += dkg
+        dv[k0:k1, g] += dvg
+    return dq, dk, dv
+
+
+def fwd_rows(q_head, k_head, v_head, rows, *, scale: float, causal: bool):
+    """Forward for selected query rows of one head: q_head [Nq,D], k/v_head [Nkv,D].
+
+    Rows are independent, so this is the same definition restricted to ``rows``; it lets a test
+    check sampled outputs of a full-size launch one row at a time.
+    """
+    qh, kh, vh = _f64(q_head), _f64(k_head), _f64(v_head)
+    nq, nkv = qh.shape[0], kh.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    s = scale * (qh[rows] @ kh.T)
+    p, lse = softmax_rows(s, legal_mask(rows, nq, nkv, causal))
+    return p @ vh, lse

@@ -1,0 +1,371 @@
+"""Pins for the CPU float64 oracle (no GPU needed).
+
+Each check ties the oracle to something other than itself: hand-derived cases, closed forms,
+invariants, brute force on tiny inputs, central finite differences, and PyTorch's own SDPA +
+autograd as an independent library routine. Together they are chosen so that a dropped scale,
+a wrong sign, a top-left instead of bottom-right causal offset, a wrong GQA head map or a
+transposed operand fails at least one test.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------------------------------------
+# Hand-derived cases (tests/golden/hand_cases.json; derivations in the file).
+# ----------------------------------------------------------------------------------------------
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_golden_hand_cases(case):
+    scale = case["scale"]
+    w = np.array(case["weights"][0], dtype=np.float64)
+    k = np.stack([np.log(w) / scale, np.zeros_like(w)], axis=1)          # [Nkv, 2]
+    q = np.array(case["q"], dtype=np.float64)                              # [Nq, 2]
+    v = np.array(case["v"], dtype=np.float64)
+    do = np.array(case["do"], dtype=np.float64)
+    qd, kd, vd, dod = q[None, None], k[None, None], v[None, None], do[None, None]
+    o, lse = ref.attn_fwd(qd, kd, vd, scale=scale, causal=case["causal"])
+    np.testing.assert_allclose(o[0, 0], np.array(case["expect_o"], dtype=np.float64), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], np.log(np.array(case["expect_lse_exp"], dtype=np.float64)),
+                               rtol=0, atol=1e-12)
+    dq, dk, dv = ref.attn_bwd(qd, kd, vd, dod, scale=scale, causal=case["causal"])
+    np.testing.assert_allclose(dv[0, 0], np.array(case["expect_dv"]), rtol=0, atol=1e-12)
+    ds = np.array(case["expect_ds"], dtype=np.float64)                     # [Nq, Nkv], by hand
+    # Closed forms from the derivation: dK_j = scale sum_i dS_ij q_i ; dQ_i = scale sum_j dS_ij k_j.
+    exp_dk = np.array([[scale * sum(ds[i, j] * q[i, c] for i in range(q.shape[0])) for c in range(2)]
+                       for j in range(k.shape[0])])
+    exp_dq = np.array([[scale * sum(ds[i, j] * k[j, c] for j in range(k.shape[0])) for c in range(2)]
+                       for i in range(q.shape[0])])
+    np.testing.assert_allclose(dk[0, 0], exp_dk, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dq[0, 0], exp_dq, rtol=0, atol=1e-12)
+    if case["name"] == "three_keys_scale_one":
+        # dQ written with the logarithms of the weights, as in the derivation text.
+        assert abs(dq[0, 0, 0, 0] - (-1.5 * math.log(2) + 1.25 * math.log(5))) < 1e-12
+
+
+# ----------------------------------------------------------------------------------------------
+# P-a: constant V rows give O = that row, for every row with a legal key.
+# ----------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v(causal):
+    r = rng(1)
+    q = r.standard_normal((2, 4, 9, 16))
+    k = r.standard_normal((2, 2, 6, 16))
+    c = r.standard_normal(16)
+    v = np.broadcast_to(c, (2, 2, 6, 16)).copy()
+    o, lse = ref.attn_fwd(q, k, v, scale=0.3, causal=causal)
+    legal_rows = ref.legal_mask(np.arange(9), 9, 6, causal).any(axis=1)
+    np.testing.assert_allclose(o[:, :, legal_rows], np.broadcast_to(c, o[:, :, legal_rows].shape), atol=1e-13)
+    assert np.all(o[:, :, ~legal_rows] == 0.0)
+
+
+# ----------------------------------------------------------------------------------------------
+# P-b: softmax rows sum to one; P-d: LSE against brute-force log-sum-exp with math.fsum.
+# ----------------------------------------------------------------------------------------------
+def test_softmax_rows_sum_to_one():
+    r = rng(2)
+    s = r.standard_normal((7, 11)) * 3
+    for causal, nq in [(False, 7), (True, 7), (True, 11)]:
+        rows = np.arange(7)
+        legal = ref.legal_mask(rows, nq, 11, causal)
+        p, _ = ref.softmax_rows(s, legal)
+        sums = p.sum(axis=1)
+        np.testing.assert_allclose(sums[legal.any(axis=1)], 1.0, atol=1e-14)
+        assert np.all(p[~legal] == 0.0)
+
+
+def test_lse_brute_force():
+    r = rng(3)
+    q = r.standard_normal((1, 1, 5, 8))
+    k = r.standard_normal((1, 1, 7, 8)) * 2.0
+    v = r.standard_normal((1, 1, 7, 8))
+    scale = 0.7
+    for causal in (False, True):
+        _, lse = ref.attn_fwd(q, k, v, scale=scale, causal=causal)
+        for i in range(5):
+            terms = []
+            for j in range(7):
+                if causal and j > i + (7 - 5):
+                    continue
+                sij = scale * math.fsum(float(q[0, 0, i, c]) * float(k[0, 0, j, c]) for c in range(8))
+                terms.append(math.exp(sij))
+            assert abs(lse[0, 0, i] - math.log(math.fsum(terms))) < 1e-12
+
+
+# ----------------------------------------------------------------------------------------------
+# P-c: causal with Nq == Nkv: row 0 sees only key 0, so O_0 = V_0 and LSE_0 = S_00.
+# ----------------------------------------------------------------------------------------------
+def test_causal_row0():
+    r = rng(4)
+    q = r.standard_normal((1, 3, 10, 12))
+    k = r.standard_normal((1, 3, 10, 12))
+    v = r.standard_normal((1, 3, 10, 12))
+    o, lse = ref.attn_fwd(q, k, v, scale=0.25, causal=True)
+    np.testing.assert_allclose(o[0, :, 0], v[0, :, 0], atol=1e-15)
+    np.testing.assert_allclose(lse[0, :, 0], 0.25 * np.einsum("hd,hd->h", q[0, :, 0], k[0, :, 0]), atol=1e-14)
+
+
+# ----------------------------------------------------------------------------------------------
+# P-f: Q = 0 gives uniform weights over the legal keys: prefix means pin the bottom-right offset.
+# ----------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("nq,nkv", [(6, 6), (4, 9), (9, 4)])
+def test_zero_query_prefix_means(nq, nkv):
+    r = rng(5)
+    q = np.zeros((1, 2, nq, 8))
+    k = r.standard_normal((1, 2, nkv, 8))
+    v = r.standard_normal((1, 2, nkv, 8))
+    o, lse = ref.attn_fwd(q, k, v, scale=1.0, causal=True)
+    for i in range(nq):
+        last = i + nkv - nq                  # last legal key (bottom-right alignment)
+        if last < 0:
+            assert np.all(o[0, :, i] == 0.0) and np.all(np.isneginf(lse[0, :, i]))
+            continue
+        np.testing.assert_allclose(o[0, :, i], v[0, :, :last + 1].mean(axis=1), atol=1e-14)
+        np.testing.assert_allclose(lse[0, :, i], math.log(last + 1), atol=1e-14)
+    o2, lse2 = ref.attn_fwd(q, k, v, scale=1.0, causal=False)
+    np.testing.assert_allclose(o2[0], np.broadcast_to(v[0].mean(axis=1, keepdims=True), o2[0].shape), atol=1e-14)
+    np.testing.assert_allclose(lse2, math.log(nkv), atol=1e-14)
+
+
+# ----------------------------------------------------------------------------------------------
+# P-g: a single key: O_i = V_0 and LSE_i = S_i0.
+# ----------------------------------------------------------------------------------------------
+def test_single_key():
+    r = rng(6)
+    q = r.standard_normal((1, 2, 5, 8))
+    k = r.standard_normal((1, 2, 1, 8))
+    v = r.standard_normal((1, 2, 1, 8))
+    o, lse = ref.attn_fwd(q, k, v, scale=0.5, causal=False)
+    np.testing.assert_allclose(o[0], np.broadcast_to(v[0], o[0].shape), atol=1e-15)
+    np.testing.assert_allclose(lse[0], 0.5 * np.einsum("hnd,hd->hn", q[0], k[0, :, 0]), atol=1e-14)
+
+
+# ----------------------------------------------------------------------------------------------
+# P-e: gradients against central finite differences of L = sum(dO * O).
+# ----------------------------------------------------------------------------------------------
+def _fd_check(q, k, v, do, scale, causal, varlen=None):
+    eps = 1e-6
+
+    def loss(qq, kk, vv):
+        if varlen is None:
+            o, _ = ref.attn_fwd(qq, kk, vv, scale=scale, causal=causal)
+        else:
+            o, _ = ref.varlen_fwd(qq, kk, vv, varlen[0], varlen[1], scale=scale, causal=causal)
+        return float(np.sum(do * o))
+
+    if varlen is None:
+        grads = ref.attn_bwd(q, k, v, do, scale=scale, causal=causal)
+    else:
+        grads = ref.varlen_bwd(q, k, v, do, varlen[0], varlen[1], scale=scale, causal=causal)
+    for which, (x, g) in enumerate(zip((q, k, v), grads)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][idx] += eps
+            lp = loss(*args)
+            args[which][idx] -= 2 * eps
+            lm = loss(*args)
+            num[idx] = (lp - lm) / (2 * eps)
+        err = np.linalg.norm(num - g) / max(np.linalg.norm(num), 1e-30)
+        assert err < 1e-6, f"grad {'qkv'[which]} rel err {err}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fd_gqa(causal):
+    r = rng(7)
+    q = r.standard_normal((2, 4, 5, 8))
+    k = r.standard_normal((2, 2, 7, 8))
+    v = r.standard_normal((2, 2, 7, 8))
+    do = r.standard_normal((2, 4, 5, 8))
+    _fd_check(q, k, v, do, 0.4, causal)
+
+
+def test_fd_cross_causal_with_empty_rows():
+    r = rng(8)
+    q = r.standard_normal((1, 2, 7, 6))
+    k = r.standard_normal((1, 1, 5, 6))
+    v = r.standard_normal((1, 1, 5, 6))
+    do = r.standard_normal((1, 2, 7, 6))
+    _fd_check(q, k, v, do, 0.5, True)
+    dq, _, _ = ref.attn_bwd(q, k, v, do, scale=0.5, causal=True)
+    assert np.all(dq[:, :, :2] == 0.0)     # rows 0 and 1 have no legal key (i + 5 - 7 < 0)
+
+
+def test_fd_varlen():
+    r = rng(9)
+    cu_q = np.array([0, 3, 3, 8])
+    cu_k = np.array([0, 4, 6, 6])
+    q = r.standard_normal((8, 2, 6))
+    k = r.standard_normal((6, 1, 6))
+    v = r.standard_normal((6, 1, 6))
+    do = r.standard_normal((8, 2, 6))
+    for causal in (False, True):
+        _fd_check(q, k, v, do, 0.6, causal, varlen=(cu_q, cu_k))
+
+
+# ----------------------------------------------------------------------------------------------
+# P-h: invariants of the backward.
+# ----------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    r = rng(10)
+    nq, nkv = 9, 6
+    q = r.standard_normal((1, 4, nq, 8))
+    k = r.standard_normal((1, 2, nkv, 8))
+    v = r.standard_normal((1, 2, nkv, 8))
+    do = r.standard_normal((1, 4, nq, 8))
+    dq, dk, dv = ref.attn_bwd(q, k, v, do, scale=0.3, causal=causal)
+    # sum_j dS_ij = 0 for each row, so the KV-axis sum of dK vanishes for every KV head.
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    # sum_j P_ij = 1 for non-empty rows, so sum_j dV_j = sum over non-empty rows of the group's dO.
+    rows_ok = ref.legal_mask(np.arange(nq), nq, nkv, causal).any(axis=1)
+    expect = do[:, :, rows_ok].reshape(1, 2, 2, -1, 8).sum(axis=(2, 3))
+    np.testing.assert_allclose(dv.sum(axis=2), expect, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------------
+# P-i: GQA equals MHA on repeat_interleave'd K/V (grads are group sums); varlen equals dense.
+# ----------------------------------------------------------------------------------------------
+def test_gqa_equals_repeated_mha():
+    r = rng(11)
+    q = r.standard_normal((2, 6, 5, 8))
+    k = r.standard_normal((2, 2, 7, 8))
+    v = r.standard_normal((2, 2, 7, 8))
+    do = r.standard_normal((2, 6, 5, 8))
+    kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)
+    for causal in (False, True):
+        o1, l1 = ref.attn_fwd(q, k, v, scale=0.4, causal=causal)
+        o2, l2 = ref.attn_fwd(q, kr, vr, scale=0.4, causal=causal)
+        np.testing.assert_allclose(o1, o2, atol=1e-14)
+        np.testing.assert_allclose(l1, l2, atol=1e-14)
+        g1 = ref.attn_bwd(q, k, v, do, scale=0.4, causal=causal)
+        g2 = ref.attn_bwd(q, kr, vr, do, scale=0.4, causal=causal)
+        np.testing.assert_allclose(g1[0], g2[0], atol=1e-13)
+        np.testing.assert_allclose(g1[1], g2[1].reshape(2, 2, 3, 7, 8).sum(axis=2), atol=1e-13)
+        np.testing.assert_allclose(g1[2], g2[2].reshape(2, 2, 3, 7, 8).sum(axis=2), atol=1e-13)
+
+
+def test_varlen_equals_dense_per_sequence():
+    r = rng(12)
+    lq, lk = [3, 0, 5, 4], [4, 2, 2, 6]
+    cu_q, cu_k = np.cumsum([0] + lq), np.cumsum([0] + lk)
+    q = r.standard_normal((sum(lq), 4, 8))
+    k = r.standard_normal((sum(lk), 2, 8))
+    v = r.standard_normal((sum(lk), 2, 8))
+    do = r.standard_normal((sum(lq), 4, 8))
+    for causal in (False, True):
+        o, lse = ref.varlen_fwd(q, k, v, cu_q, cu_k, scale=0.5, causal=causal)
+        dq, dk, dv = ref.varlen_bwd(q, k, v, do, cu_q, cu_k, scale=0.5, causal=causal)
+        for s in range(4):
+            qs = q[cu_q[s]:cu_q[s + 1]].transpose(1, 0, 2)[None]
+            ks = k[cu_k[s]:cu_k[s + 1]].transpose(1, 0, 2)[None]
+            vs = v[cu_k[s]:cu_k[s + 1]].transpose(1, 0, 2)[None]
+            dos = do[cu_q[s]:cu_q[s + 1]].transpose(1, 0, 2)[None]
+            od, ld = ref.attn_fwd(qs, ks, vs, scale=0.5, causal=causal)
+            np.testing.assert_allclose(o[cu_q[s]:cu_q[s + 1]], od[0].transpose(1, 0, 2), atol=1e-14)
+            np.testing.assert_allclose(lse[:, cu_q[s]:cu_q[s + 1]], ld[0], atol=1e-14)
+            gd = ref.attn_bwd(qs, ks, vs, dos, scale=0.5, causal=causal)
+            np.testing.assert_allclose(dq[cu_q[s]:cu_q[s + 1]], gd[0][0].transpose(1, 0, 2), atol=1e-13)
+            np.testing.assert_allclose(dk[cu_k[s]:cu_k[s + 1]], gd[1][0].transpose(1, 0, 2), atol=1e-13)
+            np.testing.assert_allclose(dv[cu_k[s]:cu_k[s + 1]], gd[2][0].transpose(1, 0, 2), atol=1e-13)
+
+
+# ----------------------------------------------------------------------------------------------
+# P-j: PyTorch float64 SDPA with an explicit boolean mask, plus torch autograd, as an independent
+# library routine (never is_causal: PyTorch's causal flag is top-left aligned).
+# ----------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("nq,nkv,causal", [(6, 6, False), (6, 6, True), (5, 9, True), (12, 7, False)])
+def test_against_torch_sdpa(nq, nkv, causal):
+    r = rng(13)
+    d = 16
+    q = r.standard_normal((2, 4, nq, d))
+    k = r.standard_normal((2, 2, nkv, d))
+    v = r.standard_normal((2, 2, nkv, d))
+    do = r.standard_normal((2, 4, nq, d))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = ref.attn_fwd(q, k, v, scale=scale, causal=causal)
+    dq, dk, dv = ref.attn_bwd(q, k, v, do, scale=scale, causal=causal)
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    mask = torch.tensor(ref.legal_mask(np.arange(nq), nq, nkv, causal) if causal else np.ones((nq, nkv), bool))
+    ke = tk.repeat_interleave(2, dim=1)
+    ve = tv.repeat_interleave(2, dim=1)
+    to = torch.nn.functional.scaled_dot_product_attention(tq, ke, ve, attn_mask=mask, scale=scale)
+    to.backward(torch.tensor(do))
+    np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+    # LSE via torch.logsumexp of the masked scores.
+    s = scale * torch.matmul(torch.tensor(q), torch.tensor(k).repeat_interleave(2, dim=1).transpose(-1, -2))
+    s = s.masked_fill(~mask, float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------------
+# P-k: rows without a legal key are exactly O = 0, LSE = -inf and zero gradient; they also add
+# nothing to dK/dV.
+# ----------------------------------------------------------------------------------------------
+def test_empty_rows_exact():
+    r = rng(14)
+    q = r.standard_normal((1, 2, 8, 8))
+    k = r.standard_normal((1, 2, 3, 8))
+    v = r.standard_normal((1, 2, 3, 8))
+    do = r.standard_normal((1, 2, 8, 8))
+    o, lse = ref.attn_fwd(q, k, v, scale=0.5, causal=True)
+    assert np.all(o[:, :, :5] == 0.0) and np.all(np.isneginf(lse[:, :, :5]))
+    dq, dk, dv = ref.attn_bwd(q, k, v, do, scale=0.5, causal=True)
+    assert np.all(dq[:, :, :5] == 0.0)
+    do2 = do.copy()
+    do2[:, :, :5] = 1e6                    # gradient flowing into empty rows must not reach dK/dV
+    _, dk2, dv2 = ref.attn_bwd(q, k, v, do2, scale=0.5, causal=True)
+    np.testing.assert_array_equal(dk, dk2)
+    np.testing.assert_array_equal(dv, dv2)
+    # varlen: a sequence with no keys gives empty rows too.
+    cu_q, cu_k = np.array([0, 2, 5]), np.array([0, 0, 3])
+    qv = r.standard_normal((5, 2, 8))
+    kv_ = r.standard_normal((3, 2, 8))
+    vv = r.standard_normal((3, 2, 8))
+    ov, lv = ref.varlen_fwd(qv, kv_, vv, cu_q, cu_k, scale=0.5, causal=False)
+    assert np.all(ov[:2] == 0.0) and np.all(np.isneginf(lv[:, :2]))
+
+
+def test_preprocess_delta():
+    r = rng(15)
+    o = r.standard_normal((2, 3, 4, 5))
+    do = r.standard_normal((2, 3, 4, 5))
+    delta = ref.preprocess_delta(o, do)
+    for idx in np.ndindex(2, 3, 4):
+        assert abs(delta[idx] - math.fsum(float(a) * float(b) for a, b in zip(o[idx], do[idx]))) < 1e-12
+
+
+def test_fwd_rows_matches_full():
+    r = rng(16)
+    q = r.standard_normal((1, 1, 20, 8))
+    k = r.standard_normal((1, 1, 13, 8))
+    v = r.standard_normal((1, 1, 13, 8))
+    for causal in (False, True):
+        o, lse = ref.attn_fwd(q, k, v, scale=0.3, causal=causal)
+        rows = np.array([0, 5, 7, 19])
+        orow, lrow = ref.fwd_rows(q[0, 0], k[0, 0], v[0, 0], rows, scale=0.3, causal=causal)
+        np.testing.assert_allclose(orow, o[0, 0, rows], atol=1e-14)
+        np.testing.assert_allclose(lrow, lse[0, 0, rows], atol=1e-14)
