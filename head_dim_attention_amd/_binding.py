@@ -1,0 +1,232 @@
+"""ctypes binding of libffpa.so: one Python function per C entry point, same names.
+
+The functions only marshal arguments: they check tensor metadata, allocate outputs with PyTorch
+(device memory), pass raw device pointers and the current HIP stream, and map status codes to
+exceptions (INVALID_ARGUMENT -> ValueError, NOT_SUPPORTED -> NotImplementedError, HIP -> RuntimeError,
+as the ffpa-attn user guide's "Backends Overview" and "CuTe-DSL Backend" pages describe the error
+kinds). Every step of the computation runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "FFPA_OK", "FFPA_ERR_INVALID_ARGUMENT", "FFPA_ERR_NOT_SUPPORTED", "FFPA_ERR_HIP",
+    "library_path", "load_library", "ffpa_status_string",
+    "ffpa_fwd", "ffpa_bwd", "ffpa_varlen_fwd", "ffpa_varlen_bwd",
+]
+
+FFPA_OK = 0
+FFPA_ERR_INVALID_ARGUMENT = 1
+FFPA_ERR_NOT_SUPPORTED = 2
+FFPA_ERR_HIP = 3
+
+_DTYPES = {torch.bfloat16: 0, torch.float16: 1}
+_LIB = None
+_LOCK = threading.Lock()
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+_SIGNATURES = {
+    "ffpa_fwd": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp],
+    "ffpa_bwd": [_vp] * 10 + [_i] * 7 + [_f, _i, _vp],
+    "ffpa_varlen_fwd": [_vp] * 7 + [_i] * 9 + [_f, _i, _vp],
+    "ffpa_varlen_bwd": [_vp] * 12 + [_i] * 9 + [_f, _i, _vp],
+}
+
+
+def library_path() -> str:
+    return os.environ.get("FFPA_LIBRARY", os.path.join(os.path.dirname(os.path.abspath(__file__)), "libffpa.so"))
+
+
+def load_library():
+    """Load libffpa.so once; raise if it has not been built."""
+    global _LIB
+    with _LOCK:
+        if _LIB is not None:
+            return _LIB
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"libffpa.so not found at {path}; build it with "
+                               "`python -m head_dim_attention_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.ffpa_status_string.argtypes = [ctypes.c_int]
+        lib.ffpa_status_string.restype = ctypes.c_char_p
+        _LIB = lib
+        return lib
+
+
+def ffpa_status_string(status: int) -> str:
+    return load_library().ffpa_status_string(int(status)).decode()
+
+
+def _raise_for(status: int, name: str) -> None:
+    if status == FFPA_OK:
+        return
+    msg = f"{name}: {ffpa_status_string(status)}"
+    if status == FFPA_ERR_INVALID_ARGUMENT:
+        raise ValueError(msg)
+    if status == FFPA_ERR_NOT_SUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise NotImplementedError(f"unsupported dtype {t.dtype}; ffpa kernels take float16 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def _dev(t: torch.Tensor, what: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a GPU tensor (got {t.device})")
+    return t.contiguous()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _scale(scale: Optional[float], d: int) -> float:
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def _same(ref: torch.Tensor, *ts):
+    for t in ts:
+        if t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q, k, v (and o, dout) must share dtype and device")
+
+
+def ffpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+             scale: Optional[float] = None):
+    """Dense forward. q [B,Hq,Nq,D], k/v [B,Hkv,Nkv,D] -> (o [B,Hq,Nq,D], lse fp32 [B,Hq,Nq])."""
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    _same(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,Hq,Nq,D] and k, v [B,Hkv,Nkv,D]")
+    b, hq, nq, d = q.shape
+    _, hkv, nkv, dk = k.shape
+    if k.shape[0] != b or dk != d:
+        raise ValueError("batch and head dim of q, k, v must match")
+    o = torch.empty_like(q)
+    lse = torch.empty((b, hq, nq), dtype=torch.float32, device=q.device)
+    st = load_library().ffpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv, d,
+                                 _dtype_code(q), _scale(scale, d), int(bool(causal)), _stream(q))
+    _raise_for(st, "ffpa_fwd")
+    return o, lse
+
+
+def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float] = None):
+    """Dense backward -> (dq, dk, dv) with the shapes and dtype of q, k, v."""
+    q, k, v, o, dout = (_dev(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")))
+    lse = _dev(lse, "lse")
+    _same(q, k, v, o, dout)
+    b, hq, nq, d = q.shape
+    _, hkv, nkv, _ = k.shape
+    if o.shape != q.shape or dout.shape != q.shape or lse.shape != (b, hq, nq) or lse.dtype != torch.float32:
+        raise ValueError("o and dout must match q; lse must be float32 [B,Hq,Nq]")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    delta = torch.empty((b, hq, nq), dtype=torch.float32, device=q.device)
+    st = load_library().ffpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, nq, nkv, d,
+                                 _dtype_code(q), _scale(scale, d), int(bool(causal)), _stream(q))
+    _raise_for(st, "ffpa_bwd")
+    return dq, dk, dv
+
+
+def _check_cu(cu: torch.Tensor, total: int, what: str) -> list[int]:
+    if cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() < 2:
+        raise ValueError(f"{what} must be int32 [batch+1]")
+    host = cu.detach().to("cpu").tolist()
+    if host[0] != 0 or any(b < a for a, b in zip(host, host[1:])) or host[-1] != total:
+        raise ValueError(f"{what} must start at 0, be non-decreasing and end at {total}")
+    return host
+
+
+def _varlen_meta(q, k, cu_q, cu_k, max_q, max_k, validate):
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("varlen expects packed q [Tq,Hq,D] and k, v [Tk,Hkv,D]")
+    tq, tk = q.shape[0], k.shape[0]
+    if cu_k is None:
+        cu_k = cu_q
+    if validate:
+        hq_ = _check_cu(cu_q, tq, "cu_seqlens_q")
+        hk_ = _check_cu(cu_k, tk, "cu_seqlens_k")
+        if len(hq_) != len(hk_):
+            raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+        lq = [b - a for a, b in zip(hq_, hq_[1:])]
+        lk = [b - a for a, b in zip(hk_, hk_[1:])]
+        if max_q is None:
+            max_q = max(lq)
+        if max_k is None:
+            max_k = max(lk)
+        if max(lq) > max_q or max(lk) > max_k:
+            raise ValueError("max_seqlen_q / max_seqlen_k smaller than a sequence length")
+    if max_q is None or max_k is None:
+        raise ValueError("max_seqlen_q and max_seqlen_k are required when validate=False")
+    return cu_k, int(max_q), int(max_k)
+
+
+def ffpa_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
+                    causal: bool = False, scale: Optional[float] = None, validate: bool = True):
+    """Packed forward. q [Tq,Hq,D], k/v [Tk,Hkv,D] -> (o [Tq,Hq,D], lse fp32 [Hq,Tq])."""
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    _same(q, k, v)
+    cu_q = _dev(cu_seqlens_q, "cu_seqlens_q")
+    cu_k = _dev(cu_seqlens_k, "cu_seqlens_k") if cu_seqlens_k is not None else None
+    cu_k, max_q, max_k = _varlen_meta(q, k, cu_q, cu_k, max_seqlen_q, max_seqlen_k, validate)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    st = load_library().ffpa_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_q), _ptr(cu_k),
+                                        cu_q.numel() - 1, max_q, max_k, tq, tk, hq, hkv, d, _dtype_code(q),
+                                        _scale(scale, d), int(bool(causal)), _stream(q))
+    _raise_for(st, "ffpa_varlen_fwd")
+    return o, lse
+
+
+def ffpa_varlen_bwd(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None,
+                    max_seqlen_k=None, causal: bool = False, scale: Optional[float] = None,
+                    validate: bool = True):
+    """Packed backward -> (dq [Tq,Hq,D], dk [Tk,Hkv,D], dv [Tk,Hkv,D])."""
+    q, k, v, o, dout = (_dev(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")))
+    lse = _dev(lse, "lse")
+    _same(q, k, v, o, dout)
+    cu_q = _dev(cu_seqlens_q, "cu_seqlens_q")
+    cu_k = _dev(cu_seqlens_k, "cu_seqlens_k") if cu_seqlens_k is not None else None
+    cu_k, max_q, max_k = _varlen_meta(q, k, cu_q, cu_k, max_seqlen_q, max_seqlen_k, validate)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    if o.shape != q.shape or dout.shape != q.shape or lse.shape != (hq, tq) or lse.dtype != torch.float32:
+        raise ValueError("o and dout must match q; lse must be float32 [Hq,Tq]")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    delta = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    st = load_library().ffpa_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
+                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_q), _ptr(cu_k), cu_q.numel() - 1,
+                                        max_q, max_k, tq, tk, hq, hkv, d, _dtype_code(q), _scale(scale, d),
+                                        int(bool(causal)), _stream(q))
+    _raise_for(st, "ffpa_varlen_bwd")
+    return dq, dk, dv

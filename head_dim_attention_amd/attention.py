@@ -1,0 +1,74 @@
+"""Autograd entry points over the C ABI: the SDPA-style dense call and the packed varlen call.
+
+ffpa_attn_func mirrors the dense entry point of the ffpa-attn user guide ("Backends Overview",
+section "Choosing a backend": o = ffpa_attn_func(q, k, v), backward through autograd), and
+ffpa_attn_varlen_func mirrors its FlashAttention-style varlen call ("CuTe-DSL Backend", section
+"Varlen (packed THD) API": returns (out, lse) with return_lse=True). Both run only the library's
+HIP kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+
+__all__ = ["ffpa_attn_func", "ffpa_attn_varlen_func"]
+
+
+class _FFPAAttn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale):
+        o, lse = B.ffpa_fwd(q, k, v, causal=causal, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.scale = causal, scale
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, dlse):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = B.ffpa_bwd(q, k, v, o, do, lse, causal=ctx.causal, scale=ctx.scale)
+        return dq, dk, dv, None, None
+
+
+class _FFPAVarlen(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cu_q, cu_k, max_q, max_k, causal, scale):
+        o, lse = B.ffpa_varlen_fwd(q, k, v, cu_q, cu_k, max_q, max_k, causal=causal, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse, cu_q, cu_k)
+        ctx.meta = (max_q, max_k, causal, scale)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, dlse):
+        q, k, v, o, lse, cu_q, cu_k = ctx.saved_tensors
+        max_q, max_k, causal, scale = ctx.meta
+        dq, dk, dv = B.ffpa_varlen_bwd(q, k, v, o, do, lse, cu_q, cu_k, max_q, max_k, causal=causal,
+                                       scale=scale, validate=False)
+        return dq, dk, dv, None, None, None, None, None, None
+
+
+def ffpa_attn_func(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool = False,
+                   scale: Optional[float] = None, return_lse: bool = False):
+    """Attention over dense [B, H, N, D] tensors (fp16/bf16, D in 320..1024, D % 32 == 0).
+
+    Causal masking is bottom-right aligned; Hq may be any multiple of Hkv (GQA/MQA).
+    """
+    o, lse = _FFPAAttn.apply(q, k, v, bool(is_causal), scale)
+    return (o, lse) if return_lse else o
+
+
+def ffpa_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
+                          causal: bool = False, scale: Optional[float] = None, return_lse: bool = False):
+    """Attention over packed [T, H, D] tensors with int32 cu_seqlens [B+1] (None for k means the q ones)."""
+    if cu_seqlens_k is None:
+        cu_seqlens_k = cu_seqlens_q
+    if max_seqlen_q is None or max_seqlen_k is None:
+        lq = (cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()
+        lk = (cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item()
+        max_seqlen_q = lq if max_seqlen_q is None else max_seqlen_q
+        max_seqlen_k = lk if max_seqlen_k is None else max_seqlen_k
+    o, lse = _FFPAVarlen.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, int(max_seqlen_q), int(max_seqlen_k),
+                               bool(causal), scale)
+    return (o, lse) if return_lse else o

@@ -1,0 +1,147 @@
+// Host side of libffpa.so: argument validation, launch geometry and the C ABI (include/ffpa.h).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/ffpa.h"
+#include "ffpa_params.h"
+
+namespace ffpa {
+hipError_t launch_fwd(const AttnParams& p, int fp16, hipStream_t st);
+}  // namespace ffpa
+
+using ffpa::AttnParams;
+
+namespace {
+
+bool bad_dtype(int dtype) { return dtype != FFPA_DTYPE_BF16 && dtype != FFPA_DTYPE_FP16; }
+
+// Shared checks of every entry point; NOT_SUPPORTED is reported only for otherwise valid calls.
+int check_common(int hq, int hkv, int d, int dtype, float scale, int causal) {
+  if (hq < 1 || hkv < 1 || hq % hkv != 0) return FFPA_ERR_INVALID_ARGUMENT;
+  if (bad_dtype(dtype)) return FFPA_ERR_INVALID_ARGUMENT;
+  if (causal != 0 && causal != 1) return FFPA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FFPA_ERR_INVALID_ARGUMENT;
+  if (d < 320 || d > 1024 || d % 32 != 0) return FFPA_ERR_NOT_SUPPORTED;
+  return FFPA_OK;
+}
+
+AttnParams dense_params(int batch, int hq, int hkv, int nq, int nkv, int d, float scale, int causal) {
+  AttnParams p{};
+  p.q_row = d;
+  p.q_head = nq * d;
+  p.q_batch = (long long)hq * nq * d;
+  p.k_row = d;
+  p.k_head = nkv * d;
+  p.k_batch = (long long)hkv * nkv * d;
+  p.lse_head = nq;
+  p.lse_batch = (long long)hq * nq;
+  p.batch = batch;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.group = hq / hkv;
+  p.nq = nq;
+  p.nkv = nkv;
+  p.d = d;
+  p.causal = causal;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return p;
+}
+
+AttnParams varlen_params(int batch, int max_q, int max_k, int total_q, int hq, int hkv, int d, float scale,
+                         int causal, const int32_t* cu_q, const int32_t* cu_k) {
+  AttnParams p{};
+  p.q_row = hq * d;
+  p.q_head = d;
+  p.k_row = hkv * d;
+  p.k_head = d;
+  p.lse_head = total_q;
+  p.cu_q = cu_q;
+  p.cu_k = cu_k != nullptr ? cu_k : cu_q;
+  p.batch = batch;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.group = hq / hkv;
+  p.nq = max_q;
+  p.nkv = max_k;
+  p.d = d;
+  p.causal = causal;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return p;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? FFPA_OK : FFPA_ERR_HIP; }
+
+// Sizes in elements must stay addressable with the kernels' 32-bit row/head arithmetic.
+bool too_big_dense(int batch, int h, int n, int d) {
+  const long long per_head = (long long)n * d;
+  return per_head > (1LL << 31) - 1 || (long long)batch * h * per_head > (1LL << 46);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+             int nq, int nkv, int d, int dtype, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FFPA_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
+  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  if (st != FFPA_OK) return st;
+  if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
+  AttnParams p = dense_params(batch, hq, hkv, nq, nkv, d, scale, causal);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  return to_status(ffpa::launch_fwd(p, dtype == FFPA_DTYPE_FP16, (hipStream_t)stream));
+}
+
+int ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k, int total_q,
+                    int total_k, int hq, int hkv, int d, int dtype, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q) return FFPA_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+    return FFPA_ERR_INVALID_ARGUMENT;
+  if (max_seqlen_q > total_q || max_seqlen_k > total_k) return FFPA_ERR_INVALID_ARGUMENT;
+  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  if (st != FFPA_OK) return st;
+  if ((long long)total_q * hq * d > (1LL << 31) - 1 || (long long)total_k * hkv * d > (1LL << 31) - 1)
+    return FFPA_ERR_INVALID_ARGUMENT;
+  if (total_q == 0 || max_seqlen_q == 0) return FFPA_OK;
+  AttnParams p = varlen_params(batch, max_seqlen_q, max_seqlen_k, total_q, hq, hkv, d, scale, causal,
+                               cu_seqlens_q, cu_seqlens_k);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  return to_status(ffpa::launch_fwd(p, dtype == FFPA_DTYPE_FP16, (hipStream_t)stream));
+}
+
+const char* ffpa_status_string(int status) {
+  switch (status) {
+    case FFPA_OK: return "FFPA_OK";
+    case FFPA_ERR_INVALID_ARGUMENT: return "FFPA_ERR_INVALID_ARGUMENT: invalid argument";
+    case FFPA_ERR_NOT_SUPPORTED: return "FFPA_ERR_NOT_SUPPORTED: head dim must be a multiple of 32 in [320, 1024]";
+    case FFPA_ERR_HIP: return "FFPA_ERR_HIP: a HIP launch or runtime call failed";
+    default: return "FFPA_ERR_UNKNOWN: unknown status code";
+  }
+}
+
+}  // extern "C"
+
+// TEMPORARY: backward entry points until the backward kernels land.
+extern "C" int ffpa_bwd(const void*, const void*, const void*, const void*, const void*, const float*, float*,
+                        void*, void*, void*, int, int, int, int, int, int, int, float, int, void*) {
+  return FFPA_ERR_NOT_SUPPORTED;
+}
+extern "C" int ffpa_varlen_bwd(const void*, const void*, const void*, const void*, const void*, const float*,
+                               float*, void*, void*, void*, const int32_t*, const int32_t*, int, int, int, int,
+                               int, int, int, int, int, float, int, void*) {
+  return FFPA_ERR_NOT_SUPPORTED;
+}

@@ -1,0 +1,155 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// Conventions used by every kernel in this library:
+//  * A workgroup is 4 wave64s. Waves are arranged NR x NC: NR row groups of stationary rows
+//    (queries in the forward and dQ kernels, keys in the dK/dV kernel) and NC column groups that
+//    each own DW = NDB*32 of the (padded) head dim. Partial sums over the head dim are combined
+//    across the NC waves of a row group through LDS.
+//  * Matrix products use v_mfma_f32_32x32x16_{bf16,f16}. Lane l = 32*h + n holds, for an A
+//    operand, row (l%32) and k = 8h..8h+7; for a B operand, column (l%32) and the same k; the
+//    16 fp32 results of a C block sit at row 8*(r/4) + 4h + (r%4), column l%32.
+//  * Streamed tiles are 32 rows x RS bytes in LDS, row-major, with the 16-byte chunks of each row
+//    permuted by an XOR swizzle so that both the row reads (ds_read_b128) and the transposed reads
+//    (ds_read_b64_tr_b16) touch distinct banks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ffpa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) char lds_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct BF16 {};
+struct FP16 {};
+
+template <class T> struct Elt;
+
+template <> struct Elt<BF16> {
+  static __device__ __forceinline__ f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  // Round two fp32 values to nearest-even bf16 and pack (lo in bits 0..15).
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    bf16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t x) {
+    return __builtin_bit_cast(float, (uint32_t)x << 16);
+  }
+};
+
+template <> struct Elt<FP16> {
+  static __device__ __forceinline__ f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t x) {
+    return (float)__builtin_bit_cast(_Float16, x);
+  }
+};
+
+// XOR applied to the 16-byte chunk index of LDS row `row`. Within any 16 consecutive rows it is
+// a bijection onto 0..15 (row reads of 16 lanes hit 16 distinct chunks), and for 4 consecutive
+// rows starting at a multiple of 4 it yields 4 distinct multiples of 4 (transposed reads of a
+// 16-lane group hit distinct chunks).
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// MFMA row m of a streamed A operand is loaded from tile row row_perm(m), which exchanges bits 2
+// and 3 of m. With that order, C-block register r of a lane in half h holds tile row
+// c_row(r, h) = 16*(r/8) + 8h + 4*((r/4)%2) + r%4, so registers 8kb..8kb+7 cover the consecutive
+// tile rows 16kb + 8h + 0..7: exactly the k-slots of a B operand for k-step kb. A C block of
+// scores can then feed the next product as a B operand without moving data between lanes.
+__device__ __forceinline__ int row_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+__device__ __forceinline__ int c_row(int r, int h) { return 16 * (r >> 3) + 8 * h + 4 * ((r >> 2) & 1) + (r & 3); }
+
+__device__ __forceinline__ u32x4_t lds_read_b128(const lds_t* base, int byte_off) {
+  return *(const __attribute__((address_space(3))) u32x4_t*)(base + byte_off);
+}
+
+__device__ __forceinline__ void lds_write_b128(lds_t* base, int byte_off, u32x4_t v) {
+  *(__attribute__((address_space(3))) u32x4_t*)(base + byte_off) = v;
+}
+
+__device__ __forceinline__ f32x4_t lds_read_f4(const lds_t* base, int byte_off) {
+  return *(const __attribute__((address_space(3))) f32x4_t*)(base + byte_off);
+}
+
+__device__ __forceinline__ void lds_write_f4(lds_t* base, int byte_off, f32x4_t v) {
+  *(__attribute__((address_space(3))) f32x4_t*)(base + byte_off) = v;
+}
+
+// Transposed read (ds_read_b64_tr_b16). Within each 16-lane group, source lane s supplies the
+// address of 4 consecutive 16-bit elements ("row s"); lane i receives element i%4 of rows
+// i/4, i/4+4, i/4+8, i/4+12.
+__device__ __forceinline__ s16x4_t lds_read_tr16(const lds_t* base, int byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(base + byte_off));
+}
+
+__device__ __forceinline__ u32x4_t join_tr(s16x4_t lo, s16x4_t hi) {
+  u32x2_t a = __builtin_bit_cast(u32x2_t, lo);
+  u32x2_t b = __builtin_bit_cast(u32x2_t, hi);
+  return (u32x4_t){a.x, a.y, b.x, b.y};
+}
+
+// Asynchronous 16-byte global -> LDS copy: lane l writes LDS bytes [lds + 16 l, lds + 16 l + 16).
+// `lds` must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* gptr, lds_t* lds) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Buffer resource over [base, base + bytes) for raw (unformatted) 32-bit accesses.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Same copy through a buffer resource: lane l reads base + voff(lane) + soff (soff wave-uniform)
+// and writes LDS bytes [lds + 16 l, lds + 16 l + 16).
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff, lds_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Combine the values of lanes l and l ^ 32 (the two halves of a wave). Both lanes of a pair
+// add/compare the same two operands (commutative), so they get bit-identical results.
+__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32); }
+__device__ __forceinline__ float half_max(float x) { return fmaxf(x, other_half(x)); }
+__device__ __forceinline__ float half_sum(float x) { return x + other_half(x); }
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Geometry of one (batch or sequence) slice, resolved from dense strides or cu_seqlens.
+struct SeqView {
+  long long q_off, k_off, lse_off;
+  int lq, lk;
+};
+
+}  // namespace ffpa

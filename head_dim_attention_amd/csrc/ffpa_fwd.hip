@@ -1,0 +1,410 @@
+// Forward kernel: split-D online-softmax attention for large head dims on gfx950.
+//
+// What it computes (ffpa-attn user guide): O = softmax(scale * Q K^T) V with the SDPA contract
+// ("Backends Overview", "Automatic SDPA fallback"), bottom-right causal masking and GQA head
+// broadcast ("Triton Backend", "Feature support"; "CuTe-DSL Backend", "Hard constraints"), rows
+// without a legal key giving O = 0 and LSE = -inf, and an fp32 natural-log LSE
+// ("CuTe-DSL Backend", "Varlen (packed THD) API").
+//
+// How it maps to gfx950:
+//  * One workgroup (4 wave64s) owns BQ = NR*QB*32 queries of one head. Each wave keeps QB*32
+//    queries x DW head-dim columns of Q in registers (B operand of S^T = K Q^T) and the matching
+//    O^T block as fp32 MFMA accumulators ("O accumulator held per D chunk").
+//  * K and V stream through LDS in 32-key tiles, copied straight from global memory with 16-byte
+//    global_load_lds (no VGPR staging), double-buffered when a tile pair fits twice in the 160 KB.
+//  * Scores are formed transposed (keys x queries): each lane owns one query column, so the row
+//    max/sum over keys is an in-lane reduction plus one exchange between the two wave halves.
+//    The C block of scores is, with the key permutation described in ffpa_device.h, already the B
+//    operand of O^T += V^T P^T; V^T comes from LDS with ds_read_b64_tr_b16.
+//  * The NC waves sharing a query block each hold part of the head dim; their partial scores are
+//    added through LDS in a fixed commutative pattern so every wave gets bit-identical S.
+//  * Softmax runs in the exp2 domain with a lazily updated reference max: O and l are rescaled
+//    only when a row max grows by more than 2^8, which leaves the result unchanged (the same
+//    reference is used for numerator and denominator) and removes the per-tile O rescale.
+#include "ffpa_device.h"
+#include "ffpa_params.h"
+
+namespace ffpa {
+
+__device__ __forceinline__ SeqView seq_view(const AttnParams& p, int s) {
+  SeqView v;
+  if (p.cu_q != nullptr) {
+    const int q0 = p.cu_q[s], k0 = p.cu_k[s];
+    v.lq = p.cu_q[s + 1] - q0;
+    v.lk = p.cu_k[s + 1] - k0;
+    v.q_off = (long long)q0 * p.q_row;
+    v.k_off = (long long)k0 * p.k_row;
+    v.lse_off = q0;
+  } else {
+    v.lq = p.nq;
+    v.lk = p.nkv;
+    v.q_off = (long long)s * p.q_batch;
+    v.k_off = (long long)s * p.k_batch;
+    v.lse_off = (long long)s * p.lse_batch;
+  }
+  return v;
+}
+
+template <int NC, int NDB, int QB, int NBUF>
+struct FwdCfg {
+  static constexpr int NR = 4 / NC;
+  static constexpr int DW = NDB * 32;                    // head-dim columns per wave
+  static constexpr int DPAD = NC * DW;                   // padded head dim
+  static constexpr int RS = DPAD <= 512 ? 1024 : 2048;   // LDS row stride (bytes), power of two
+  static constexpr int BQ = NR * QB * 32;                // queries per workgroup
+  static constexpr int TILE = 32 * RS;                   // one 32-row K or V tile in LDS
+  static constexpr int XBYTES = 4 * QB * 16 * 64 * 4;    // partial scores of the 4 waves
+  static constexpr int LDS = NBUF * 2 * TILE + XBYTES;
+  static constexpr int NINSTR = TILE / 1024 / 4;         // 1 KB DMA instructions per wave per tile
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <class T, int NC, int NDB, int QB, int NBUF>
+__global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
+  using C = FwdCfg<NC, NDB, QB, NBUF>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
+  lds_t* smem = (lds_t*)smem_raw;
+
+  // Work item: XCD-aware decode. Consecutive workgroup ids go round-robin over the 8 XCDs, so
+  // item = (id % 8) * (grid / 8) + id / 8 gives each XCD a contiguous run of (head, tile) items
+  // and the tiles of one KV head share that XCD's L2.
+  const int L = blockIdx.x;
+  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  if (item >= p.total) return;
+  int t = item % p.ntiles;
+  const int hs = item / p.ntiles;
+  const int h = hs % p.hq;
+  const int s = hs / p.hq;
+  if (p.causal) t = p.ntiles - 1 - t;  // heaviest causal tiles first
+
+  const SeqView sv = seq_view(p, s);
+  const int qt0 = t * C::BQ;
+  if (qt0 >= sv.lq) return;
+  const int kvh = h / p.group;
+
+  const int w = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int rg = w / NC;
+  const int cg = w % NC;
+  const int qw0 = qt0 + rg * QB * 32;
+
+  const uint16_t* qh = (const uint16_t*)p.q + sv.q_off + (long long)h * p.q_head;
+  const int row_bytes = p.k_row * 2;
+  const char* kbase = (const char*)p.k + 2 * (sv.k_off + (long long)kvh * p.k_head);
+  const char* vbase = (const char*)p.v + 2 * (sv.k_off + (long long)kvh * p.k_head);
+  const uint32_t span = (uint32_t)min((long long)max(sv.lk, 1) * row_bytes, (long long)0xFFFFFFF0);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, span);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, span);
+
+  const int off = sv.lk - sv.lq;  // tail alignment of the causal mask
+  int kend = sv.lk;
+  if (p.causal) kend = min(kend, qt0 + C::BQ + off);
+  const int ntk = kend > 0 ? (kend + 31) >> 5 : 0;
+
+  // Q block of this wave as B operands: lane (h, n) holds query n, dims 16 kb + 8 h + 0..7.
+  u32x4_t qreg[QB][2 * NDB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = min(qw0 + qb * 32 + l32, sv.lq - 1);
+    const uint16_t* qrow = qh + (long long)qi * p.q_row;
+#pragma unroll
+    for (int kb = 0; kb < 2 * NDB; ++kb) {
+      const int dim = cg * C::DW + kb * 16 + hh * 8;
+      qreg[qb][kb] = dim < p.d ? *(const u32x4_t*)(qrow + dim) : (u32x4_t){0u, 0u, 0u, 0u};
+    }
+  }
+
+  f32x16_t oacc[QB][NDB];
+  float mref[QB], lsum[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    mref[qb] = -INFINITY;
+    lsum[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[qb][db] = (f32x16_t){};
+  }
+
+  lds_t* xbuf = smem + NBUF * 2 * C::TILE;
+
+  // DMA: instruction ii of this wave fills LDS bytes [1024 i, 1024 i + 1024) of a tile, i = w + 4 ii,
+  // i.e. tile row R = i / (RS / 1024) (uniform per instruction). Lane l writes physical chunk
+  // pc = (i % (RS/1024)) * 64 + l, holding logical chunk pc ^ swz(R) (clamped into the head dim:
+  // padded chunks hold finite duplicates that never reach a result). The column offset is
+  // loop-invariant (VGPR); the row offset, clamped to the last key, is scalar.
+  constexpr int IPR = C::RS / 1024;  // DMA instructions per LDS row
+  const int dch = p.d >> 3;
+  int voff[C::NINSTR];
+#pragma unroll
+  for (int ii = 0; ii < C::NINSTR; ++ii) {
+    const int i = w + 4 * ii;
+    const int R = i / IPR;
+    const int pc = (i % IPR) * 64 + lane;
+    voff[ii] = min(pc ^ swz(R), dch - 1) << 4;
+  }
+  auto issue = [&](__amdgpu_buffer_rsrc_t rs, int j, lds_t* dst) {
+#pragma unroll
+    for (int ii = 0; ii < C::NINSTR; ++ii) {
+      const int i = w + 4 * ii;
+      const int R = i / IPR;
+      const int row = min(j * 32 + R, sv.lk - 1);
+      dma16_buf(rs, voff[ii], row * row_bytes, dst + i * 1024);
+    }
+  };
+
+  const int krow = row_perm(l32);
+  const int kswz = swz(krow);
+  const int g16 = lane >> 4;
+  const int r16 = lane & 15;
+
+  // ---- pipeline pieces (each runs the same barriers in every wave) --------------------------
+  auto top = [&](int j) {
+    if constexpr (NBUF == 2) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (j + 1 < ntk) {
+        lds_t* nk = smem + ((j + 1) & 1) * 2 * C::TILE;
+        issue(krs, j + 1, nk);
+        issue(vrs, j + 1, nk + C::TILE);
+      }
+    } else {
+      wait_vmcnt<C::NINSTR>();  // K_j has landed; V_j may still be in flight
+      __syncthreads();
+    }
+  };
+
+  // Full S^T (keys x queries) of tile j for this wave's query block, masked.
+  auto scores = [&](int j, f32x16_t (&sacc)[QB]) {
+    const lds_t* kt = smem + (NBUF == 2 ? (j & 1) : 0) * 2 * C::TILE;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) sacc[qb] = (f32x16_t){};
+#pragma unroll
+    for (int kb = 0; kb < 2 * NDB; ++kb) {
+      const int chunk = (cg * C::DW >> 3) + 2 * kb + hh;
+      const u32x4_t a = lds_read_b128(kt, krow * C::RS + ((chunk ^ kswz) << 4));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb] = Elt<T>::mma(a, qreg[qb][kb], sacc[qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        lds_write_f4(xbuf, (((w * QB + qb) * 4 + r4) * 64 + lane) * 16,
+                     (f32x4_t){sacc[qb][4 * r4], sacc[qb][4 * r4 + 1], sacc[qb][4 * r4 + 2], sacc[qb][4 * r4 + 3]});
+    __syncthreads();
+    if constexpr (NBUF == 1) {
+      if (j + 1 < ntk) issue(krs, j + 1, smem);
+    }
+    // Add the partial sums of the row group's waves in a fixed commutative pattern, so that
+    // every wave of the row group ends with bit-identical scores.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int base = rg * NC;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        auto rd = [&](int wv) { return lds_read_f4(xbuf, (((wv * QB + qb) * 4 + r4) * 64 + lane) * 16); };
+        f32x4_t mine = (f32x4_t){sacc[qb][4 * r4], sacc[qb][4 * r4 + 1], sacc[qb][4 * r4 + 2], sacc[qb][4 * r4 + 3]};
+        mine = mine + rd(base + (cg ^ 1));
+        if constexpr (NC == 4) {
+          const int o0 = base + ((cg & 2) ^ 2);
+          mine = mine + (rd(o0) + rd(o0 + 1));
+        }
+        sacc[qb][4 * r4] = mine.x; sacc[qb][4 * r4 + 1] = mine.y;
+        sacc[qb][4 * r4 + 2] = mine.z; sacc[qb][4 * r4 + 3] = mine.w;
+      }
+    }
+    // Mask tail keys and the causal diagonal (only on tiles that need it).
+    const bool need_mask = (j * 32 + 32 > sv.lk) || (p.causal && j * 32 + 31 > qw0 + off);
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qi = qw0 + qb * 32 + l32;
+        const int lim = p.causal ? min(qi + off, sv.lk - 1) : sv.lk - 1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (j * 32 + c_row(r, hh) > lim) sacc[qb][r] = -INFINITY;
+      }
+    }
+  };
+
+  // P = exp2(S * scale*log2e - mref), l += rowsum P, packed as B operands.
+  auto make_p = [&](f32x16_t (&sacc)[QB], uint32_t (&pb)[QB][2][4]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mu = mref[qb] == -INFINITY ? 0.f : mref[qb];
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = fast_exp2(sacc[qb][r] * p.scale_log2 - mu);
+        sacc[qb][r] = pv;
+        rs += pv;
+      }
+      lsum[qb] += rs;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pb[qb][kb2][e] = Elt<T>::pack2(sacc[qb][8 * kb2 + 2 * e], sacc[qb][8 * kb2 + 2 * e + 1]);
+    }
+  };
+
+  // Row maxima of the tile in log2 units.
+  auto tile_max = [&](const f32x16_t (&sacc)[QB], float (&mt)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float m = sacc[qb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) m = fmaxf(m, sacc[qb][r]);
+      mt[qb] = half_max(m) * p.scale_log2;
+    }
+  };
+
+  auto pv = [&](int j, const uint32_t (&pb)[QB][2][4]) {
+    if constexpr (NBUF == 1) {
+      if (j + 1 < ntk) wait_vmcnt<C::NINSTR>(); else wait_vmcnt<0>();  // V_j has landed
+      __syncthreads();
+    }
+    const lds_t* vt = smem + (NBUF == 2 ? (j & 1) : 0) * 2 * C::TILE + C::TILE;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = cg * C::DW + 32 * db + 16 * (g16 & 1) + 4 * (r16 & 3);
+      const int chunk = d >> 3;
+      const int within = (d & 7) << 1;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int k0 = 16 * kb2 + 8 * hh + (r16 >> 2);
+        const int k1 = k0 + 4;
+        const s16x4_t lo = lds_read_tr16(vt, k0 * C::RS + ((chunk ^ swz(k0)) << 4) + within);
+        const s16x4_t hi = lds_read_tr16(vt, k1 * C::RS + ((chunk ^ swz(k1)) << 4) + within);
+        const u32x4_t a = join_tr(lo, hi);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const u32x4_t bop = {pb[qb][kb2][0], pb[qb][kb2][1], pb[qb][kb2][2], pb[qb][kb2][3]};
+          oacc[qb][db] = Elt<T>::mma(a, bop, oacc[qb][db]);
+        }
+      }
+    }
+    if constexpr (NBUF == 1) {
+      __syncthreads();
+      if (j + 1 < ntk) issue(vrs, j + 1, smem + C::TILE);
+    }
+  };
+
+  if (ntk > 0) {
+    issue(krs, 0, smem);
+    issue(vrs, 0, smem + C::TILE);
+  }
+
+  // ---- fast loop: the reference max of a row is fixed at its first finite tile max. The loop
+  // leaves (per wave) as soon as a tile max exceeds the reference by more than 2^8, so O never
+  // needs rescaling here and exp2 stays below 256.
+  int j = 0;
+  f32x16_t sacc[QB];
+  for (; j < ntk; ++j) {
+    top(j);
+    scores(j, sacc);
+    float mt[QB];
+    tile_max(sacc, mt);
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (mref[qb] == -INFINITY) mref[qb] = mt[qb];
+      grow |= mt[qb] > mref[qb] + 8.0f;
+    }
+    if (__any(grow)) break;
+    uint32_t pb[QB][2][4];
+    make_p(sacc, pb);
+    pv(j, pb);
+  }
+
+  // ---- rescaling loop (entered only after a large growth of a row max): standard online
+  // softmax with a lazily updated reference. Tile j's scores are already in sacc.
+  if (j < ntk) {
+    bool fresh = false;
+    for (; j < ntk; ++j) {
+      if (fresh) {
+        top(j);
+        scores(j, sacc);
+      }
+      fresh = true;
+      float mt[QB];
+      tile_max(sacc, mt);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const bool nd = mt[qb] > mref[qb] + 8.0f;
+        const float alpha = nd ? fast_exp2(mref[qb] - mt[qb]) : 1.0f;
+        if (nd) mref[qb] = mt[qb];
+        lsum[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
+      }
+      uint32_t pb[QB][2][4];
+      make_p(sacc, pb);
+      pv(j, pb);
+    }
+  }
+
+  // ---- epilogue: O = O^T / l, LSE = ln(2) * (mref + log2 l); empty rows give 0 and -inf
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = half_sum(lsum[qb]);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int qi = qw0 + qb * 32 + l32;
+    if (qi < sv.lq) {
+      uint16_t* orow = (uint16_t*)p.o + sv.q_off + (long long)h * p.q_head + (long long)qi * p.q_row;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = cg * C::DW + 32 * db + 8 * i4 + 4 * hh;
+          if (d < p.d) {
+            const f32x16_t& o = oacc[qb][db];
+            const u32x2_t pk = {Elt<T>::pack2(o[4 * i4] * inv, o[4 * i4 + 1] * inv),
+                                Elt<T>::pack2(o[4 * i4 + 2] * inv, o[4 * i4 + 3] * inv)};
+            *(u32x2_t*)(orow + d) = pk;
+          }
+        }
+      if (cg == 0 && hh == 0)
+        p.lse[sv.lse_off + (long long)h * p.lse_head + qi] =
+            lt > 0.f ? (mref[qb] + fast_log2(lt)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <class T, int NC, int NDB>
+static hipError_t launch_fwd_cfg(AttnParams p, hipStream_t st) {
+  constexpr int QB = 1;
+  constexpr int NBUF = (2 * 2 * FwdCfg<NC, NDB, QB, 1>::TILE + FwdCfg<NC, NDB, QB, 1>::XBYTES) <= 160 * 1024 ? 2 : 1;
+  using C = FwdCfg<NC, NDB, QB, NBUF>;
+  p.ntiles = (p.nq + C::BQ - 1) / C::BQ;
+  p.total = p.batch * p.hq * p.ntiles;
+  if (p.total == 0) return hipSuccess;
+  const int grid = (p.total + 7) & ~7;
+  hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF>), dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_fwd_t(const AttnParams& p, hipStream_t st) {
+  if (p.d <= 512) {
+    switch ((p.d + 63) / 64) {
+      case 5: return launch_fwd_cfg<T, 2, 5>(p, st);
+      case 6: return launch_fwd_cfg<T, 2, 6>(p, st);
+      case 7: return launch_fwd_cfg<T, 2, 7>(p, st);
+      default: return launch_fwd_cfg<T, 2, 8>(p, st);
+    }
+  }
+  switch ((p.d + 127) / 128) {
+    case 5: return launch_fwd_cfg<T, 4, 5>(p, st);
+    case 6: return launch_fwd_cfg<T, 4, 6>(p, st);
+    case 7: return launch_fwd_cfg<T, 4, 7>(p, st);
+    default: return launch_fwd_cfg<T, 4, 8>(p, st);
+  }
+}
+
+hipError_t launch_fwd(const AttnParams& p, int fp16, hipStream_t st) {
+  return fp16 ? launch_fwd_t<FP16>(p, st) : launch_fwd_t<BF16>(p, st);
+}
+
+}  // namespace ffpa

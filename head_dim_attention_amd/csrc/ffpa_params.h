@@ -1,0 +1,38 @@
+// Launch parameters shared by the host dispatcher and the kernels (plain data, no HIP types).
+#pragma once
+
+#include <stdint.h>
+
+namespace ffpa {
+
+struct AttnParams {
+  // Tensors. o/dout/dq share q's strides; v/dk/dv share k's strides; lse/delta share lse strides.
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o_in;     // backward: forward output O
+  const void* dout;     // backward: dO
+  void* o;              // forward output
+  float* lse;           // forward output
+  const float* lse_in;  // backward input
+  float* delta;         // backward: Delta = rowsum(dO * O)
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* cu_q;  // varlen: [batch+1]; NULL for dense
+  const int32_t* cu_k;
+  // Dense strides in elements (unused for varlen except row/head strides).
+  long long q_batch, k_batch, lse_batch;
+  int q_row, q_head, k_row, k_head, lse_head;
+  // Problem.
+  int batch, hq, hkv, group;  // group = hq / hkv
+  int nq, nkv;                // dense lengths, or max lengths for varlen
+  int d, causal;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+  // Grid decode.
+  int ntiles;  // row tiles per (sequence, head)
+  int total;   // work items = batch * heads * ntiles
+};
+
+}  // namespace ffpa

@@ -1,0 +1,117 @@
+/*
+ * ffpa.h -- C ABI of the MI355X (gfx950) large-head-dim attention library (libffpa.so).
+ *
+ * The library computes fused scaled-dot-product attention for head dims D = 320..1024
+ * (D % 32 == 0) in bf16 or fp16 storage with fp32 accumulation: a forward pass that returns O
+ * and a float32 log-sum-exp, and a backward pass in four stages (preprocess Delta =
+ * rowsum(dO * O), then dV, dK and dQ). It follows the operation the ffpa-attn user guide defines:
+ *
+ *   - "Backends Overview", section "Automatic SDPA fallback": the entry points keep PyTorch's
+ *     scaled_dot_product_attention contract, O = softmax(scale * Q K^T) V;
+ *   - "Triton Backend", section "Feature support": causal masking is tail-aligned (bottom-right),
+ *     cross-attention (Nq != Nkv), GQA/MQA and non-aligned N are supported;
+ *   - "CuTe-DSL Backend", section "Hard constraints": GQA/MQA is a zero-stride head broadcast, and
+ *     rows with no legal key give O = 0, LSE = -inf and exactly zero gradient;
+ *   - "CuTe-DSL Backend", section "Varlen (packed THD) API": packed [T, H, D] tensors with int32
+ *     cu_seqlens [B+1] starting at 0, causal applied per sequence, LSE returned as float32
+ *     [H_q, T_q];
+ *   - "CuTe-DSL Backend", section "Blackwell status": the backward runs as preprocess, dV, dK, dQ.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers to contiguous buffers owned by the caller. The
+ *     library allocates no memory and keeps no state between calls.
+ *   - Element (b, h, n, d) of a dense [B, H, N, D] tensor sits at ((b*H + h)*N + n)*D + d;
+ *     element (t, h, d) of a packed [T, H, D] tensor sits at (t*H + h)*D + d.
+ *   - Query head h reads KV head h / (Hq / Hkv).
+ *   - Causal: key j is legal for query i iff j <= i + (Nkv - Nq) (per sequence for varlen).
+ *   - dtype: FFPA_DTYPE_BF16 or FFPA_DTYPE_FP16; q, k, v, o, dout, dq, dk, dv all use it.
+ *   - scale multiplies Q K^T before the softmax; it must be finite and > 0 (1/sqrt(D) is the
+ *     SDPA default).
+ *   - stream: a hipStream_t (NULL = the default stream). Work is enqueued asynchronously; results
+ *     are valid once the stream has been synchronised. The backward's launches are ordered on it.
+ *   - Return value: an ffpa_status_t. Arguments are validated on the host before anything is
+ *     enqueued; a non-OK status means nothing was launched. FFPA_ERR_HIP reports a failed launch.
+ *   - Inputs are assumed finite. Buffers may not alias each other except q/k/v among themselves.
+ */
+#ifndef FFPA_H_
+#define FFPA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FFPA_DTYPE_BF16 = 0,
+  FFPA_DTYPE_FP16 = 1
+} ffpa_dtype_t;
+
+typedef enum {
+  FFPA_OK = 0,
+  FFPA_ERR_INVALID_ARGUMENT = 1, /* null pointer, size < 1, Hq % Hkv != 0, bad enum, causal not 0/1, scale <= 0 */
+  FFPA_ERR_NOT_SUPPORTED = 2,    /* D outside [320, 1024] or D % 32 != 0 */
+  FFPA_ERR_HIP = 3               /* a HIP launch or runtime call failed */
+} ffpa_status_t;
+
+/*
+ * Dense forward ("Backends Overview", "Automatic SDPA fallback"; "CuTe-DSL Backend",
+ * "Hard constraints").
+ *   q    [batch, hq,  nq,  d]   in
+ *   k, v [batch, hkv, nkv, d]   in
+ *   o    [batch, hq,  nq,  d]   out, softmax(scale q k^T) v rounded to dtype; 0 for empty rows
+ *   lse  [batch, hq,  nq] fp32  out, natural-log log-sum-exp of the scaled scores; -inf for empty rows
+ * Requires batch, hq, hkv, nq, nkv >= 1 and hq % hkv == 0.
+ */
+int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int batch, int hq, int hkv, int nq, int nkv, int d,
+             int dtype, float scale, int causal, void* stream);
+
+/*
+ * Dense backward of L = sum(dout * o) ("CuTe-DSL Backend", "Blackwell status": preprocess, dV,
+ * dK, dQ). Takes the forward's inputs, its outputs o and lse, and dout [batch, hq, nq, d].
+ *   delta [batch, hq, nq] fp32   caller-owned workspace, overwritten with rowsum(dout * o)
+ *   dq    [batch, hq, nq, d]     out
+ *   dk, dv [batch, hkv, nkv, d]  out; sums over the hq/hkv query heads that share a KV head
+ * Gradients are accumulated in fp32 and rounded to dtype once. Rows with lse = -inf contribute
+ * nothing and get dq = 0.
+ */
+int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, float* delta, void* dq, void* dk, void* dv,
+             int batch, int hq, int hkv, int nq, int nkv, int d,
+             int dtype, float scale, int causal, void* stream);
+
+/*
+ * Packed (THD) varlen forward ("CuTe-DSL Backend", "Varlen (packed THD) API").
+ *   q [total_q, hq, d]; k, v [total_k, hkv, d]; o [total_q, hq, d]; lse [hq, total_q] fp32.
+ *   cu_seqlens_q [batch+1], cu_seqlens_k [batch+1]: device int32, start at 0, non-decreasing,
+ *     end at total_q / total_k. cu_seqlens_k == NULL means cu_seqlens_k = cu_seqlens_q.
+ *   max_seqlen_q / max_seqlen_k bound every sequence length (they size the launch grid).
+ * Sequence s attends queries [cu_q[s], cu_q[s+1]) to keys [cu_k[s], cu_k[s+1]); sequences of
+ * length 0 are allowed. The device contents of cu_seqlens are not read on the host: contents
+ * that break the rules above are undefined behaviour.
+ */
+int ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                    int hq, int hkv, int d, int dtype, float scale, int causal, void* stream);
+
+/*
+ * Packed (THD) varlen backward; arguments as ffpa_varlen_fwd plus o, dout [total_q, hq, d],
+ * the forward's lse [hq, total_q], a caller-owned fp32 workspace delta [hq, total_q], and the
+ * outputs dq [total_q, hq, d], dk, dv [total_k, hkv, d].
+ */
+int ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, float* delta, void* dq, void* dk, void* dv,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                    int hq, int hkv, int d, int dtype, float scale, int causal, void* stream);
+
+/* Human-readable name of a status code; never NULL. */
+const char* ffpa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFPA_H_ */
