@@ -9,6 +9,7 @@
 
 namespace ffpa {
 hipError_t launch_fwd(const AttnParams& p, int fp16, hipStream_t st);
+hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total, hipStream_t st);
 }  // namespace ffpa
 
 using ffpa::AttnParams;
@@ -123,6 +124,66 @@ int ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float*
   return to_status(ffpa::launch_fwd(p, dtype == FFPA_DTYPE_FP16, (hipStream_t)stream));
 }
 
+int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq, int nkv, int d,
+             int dtype, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FFPA_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
+  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  if (st != FFPA_OK) return st;
+  if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
+  const long long nrows = (long long)batch * hq * nq;
+  if (nrows > (1LL << 31) - 1) return FFPA_ERR_INVALID_ARGUMENT;
+  AttnParams p = dense_params(batch, hq, hkv, nq, nkv, d, scale, causal);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o_in = o;
+  p.dout = dout;
+  p.lse_in = lse;
+  p.delta = delta;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, (int)nrows, 0, (hipStream_t)stream));
+}
+
+int ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    float* delta, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k, int total_q,
+                    int total_k, int hq, int hkv, int d, int dtype, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv || !cu_seqlens_q)
+    return FFPA_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+    return FFPA_ERR_INVALID_ARGUMENT;
+  if (max_seqlen_q > total_q || max_seqlen_k > total_k) return FFPA_ERR_INVALID_ARGUMENT;
+  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  if (st != FFPA_OK) return st;
+  if ((long long)total_q * hq * d > (1LL << 31) - 1 || (long long)total_k * hkv * d > (1LL << 31) - 1)
+    return FFPA_ERR_INVALID_ARGUMENT;
+  if (total_k == 0 || max_seqlen_k == 0) {
+    // No keys at all: dK and dV are empty, every query row is empty and gets dQ = 0.
+    if (total_q > 0) {
+      const hipError_t e = hipMemsetAsync(dq, 0, (size_t)total_q * hq * d * 2, (hipStream_t)stream);
+      if (e != hipSuccess) return FFPA_ERR_HIP;
+    }
+    return FFPA_OK;
+  }
+  AttnParams p = varlen_params(batch, max_seqlen_q, max_seqlen_k, total_q, hq, hkv, d, scale, causal,
+                               cu_seqlens_q, cu_seqlens_k);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o_in = o;
+  p.dout = dout;
+  p.lse_in = lse;
+  p.delta = delta;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, total_q * hq, total_q, (hipStream_t)stream));
+}
+
 const char* ffpa_status_string(int status) {
   switch (status) {
     case FFPA_OK: return "FFPA_OK";
@@ -134,14 +195,3 @@ const char* ffpa_status_string(int status) {
 }
 
 }  // extern "C"
-
-// TEMPORARY: backward entry points until the backward kernels land.
-extern "C" int ffpa_bwd(const void*, const void*, const void*, const void*, const void*, const float*, float*,
-                        void*, void*, void*, int, int, int, int, int, int, int, float, int, void*) {
-  return FFPA_ERR_NOT_SUPPORTED;
-}
-extern "C" int ffpa_varlen_bwd(const void*, const void*, const void*, const void*, const void*, const float*,
-                               float*, void*, void*, void*, const int32_t*, const int32_t*, int, int, int, int,
-                               int, int, int, int, int, float, int, void*) {
-  return FFPA_ERR_NOT_SUPPORTED;
-}

@@ -1,0 +1,398 @@
+// Backward kernels for large-head-dim attention on gfx950.
+//
+// The backward of L = sum(dO * O) runs in four stages, as the ffpa-attn user guide describes for
+// its D=512 Blackwell path ("CuTe-DSL Backend", "Blackwell status": preprocess, dV, dK, dQ, split
+// because one unsplit dK/dV tile does not fit on chip). On gfx950 the same split keeps every
+// kernel's register-resident state at or below two operand blocks plus one fp32 accumulator:
+//
+//   preprocess  Delta_i = sum_d dO_id O_id                           (HBM-bound streaming)
+//   dV          dV_j += sum_i P_ij dO_i,  P = exp(scale S - LSE)     (keys stationary)
+//   dK          dK_j += scale sum_i dS_ij Q_i, dS = P (dP - Delta), dP = dO V^T (keys stationary)
+//   dQ          dQ_i += scale sum_j dS_ij K_j                         (queries stationary)
+//
+// All accumulation is fp32 in registers over the whole sweep (no atomics, deterministic); GQA
+// key/value gradients are summed over the query heads of their group inside the same workgroup
+// ("CuTe-DSL Backend", "Hard constraints": zero-stride broadcast). Rows whose LSE is -inf (no legal
+// key) get P = 0 and so contribute nothing and receive zero gradient.
+//
+// The dV/dK/dQ kernels share one skeleton with the forward kernel: 4 wave64s as NR x NC, the
+// stationary rows' operands in registers as MFMA B operands, the other side streamed through LDS
+// in 32-row tiles (buffer_load...lds), partial head-dim products combined through LDS, scores in a
+// C-block layout whose registers feed the accumulating product directly as B operands, and the
+// accumulating product's A operand read transposed from the streamed tile (ds_read_b64_tr_b16).
+#include "ffpa_device.h"
+#include "ffpa_params.h"
+
+namespace ffpa {
+
+// ------------------------------------------------------------------------------------------------
+// Stage 1: Delta = rowsum(dO * O) in fp32 from the stored (rounded) O.
+// One wave per row, 8 elements (16 bytes) per lane per step, 4 rows per wave.
+// ------------------------------------------------------------------------------------------------
+template <class T>
+__device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float a0, a1, b0, b1;
+    Elt<T>::unpack2(a[e], a0, a1);
+    Elt<T>::unpack2(b[e], b0, b1);
+    s += a0 * b0;
+    s += a1 * b1;
+  }
+  return s;
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) ffpa_bwd_preprocess_kernel(AttnParams p, int nrows, int varlen_total) {
+  constexpr int RPW = 4;
+  const int wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const long long row0 = ((long long)blockIdx.x * 4 + wv) * RPW;
+  float acc[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    acc[r] = 0.f;
+    const long long row = row0 + r;
+    if (row < nrows) {
+      const uint16_t* o = (const uint16_t*)p.o_in + row * p.d;
+      const uint16_t* g = (const uint16_t*)p.dout + row * p.d;
+      for (int c = lane * 8; c < p.d; c += 512) acc[r] += dot8<T>(*(const u32x4_t*)(o + c), *(const u32x4_t*)(g + c));
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc[r] += __shfl_xor(acc[r], m);
+    const long long row = row0 + r;
+    if (lane == 0 && row < nrows) {
+      // Dense rows are ordered (b, h, n) like Delta; packed rows are (t, h) and Delta is [H, T].
+      const long long idx = varlen_total > 0 ? (row % p.hq) * varlen_total + row / p.hq : row;
+      p.delta[idx] = acc[r];
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Stages 2-4: dV, dK, dQ.
+// ------------------------------------------------------------------------------------------------
+enum BwdMode { kDQ = 0, kDK = 1, kDV = 2 };
+
+template <int NC, int NDB, int NBUF, int NX>
+struct BwdCfg {
+  static constexpr int NR = 4 / NC;
+  static constexpr int DW = NDB * 32;
+  static constexpr int DPAD = NC * DW;
+  static constexpr int RS = DPAD <= 512 ? 1024 : 2048;
+  static constexpr int BOWN = NR * 32;                 // stationary rows per workgroup
+  static constexpr int TILE = 32 * RS;
+  static constexpr int XBYTES = 4 * NX * 16 * 64 * 4;  // NX partial C blocks per wave
+  static constexpr int LDS = NBUF * 2 * TILE + XBYTES;
+  static constexpr int NINSTR = TILE / 1024 / 4;
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <class T, int MODE, int NC, int NDB, int NBUF>
+__global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
+  constexpr bool OWN_Q = MODE == kDQ;   // stationary rows are queries (dQ) or keys (dK, dV)
+  constexpr bool HAS_DP = MODE != kDV;  // dK and dQ need dP = dO V^T
+  constexpr int NX = HAS_DP ? 2 : 1;
+  using C = BwdCfg<NC, NDB, NBUF, NX>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
+  lds_t* smem = (lds_t*)smem_raw;
+
+  const int L = blockIdx.x;
+  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  if (item >= p.total) return;
+  const int heads = OWN_Q ? p.hq : p.hkv;
+  int t = item % p.ntiles;
+  const int hs = item / p.ntiles;
+  const int hd = hs % heads;
+  const int s = hs / heads;
+  if (OWN_Q && p.causal) t = p.ntiles - 1 - t;  // heaviest causal tiles first
+
+  const SeqView sv = seq_view(p, s);
+  const int own_len = OWN_Q ? sv.lq : sv.lk;
+  const int o0 = t * C::BOWN;
+  if (o0 >= own_len) return;
+
+  const int w = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int rg = w / NC;
+  const int cg = w % NC;
+  const int ow0 = o0 + rg * 32;
+  const int off = sv.lk - sv.lq;
+
+  // ---- stationary operands: lane (h, n) holds own row n, dims 16 kb + 8 h + 0..7
+  const int own_row = OWN_Q ? p.q_row : p.k_row;
+  const long long own_base = OWN_Q ? sv.q_off + (long long)hd * p.q_head : sv.k_off + (long long)hd * p.k_head;
+  const uint16_t* r1src = (const uint16_t*)(OWN_Q ? p.q : p.k) + own_base;
+  const uint16_t* r2src = (const uint16_t*)(OWN_Q ? p.dout : p.v) + own_base;
+  u32x4_t r1[2 * NDB];
+  u32x4_t r2[HAS_DP ? 2 * NDB : 1];
+  {
+    const long long oi = min(ow0 + l32, own_len - 1);
+#pragma unroll
+    for (int kb = 0; kb < 2 * NDB; ++kb) {
+      const int dim = cg * C::DW + kb * 16 + hh * 8;
+      const bool in = dim < p.d;
+      r1[kb] = in ? *(const u32x4_t*)(r1src + oi * own_row + dim) : (u32x4_t){0u, 0u, 0u, 0u};
+      if constexpr (HAS_DP)
+        r2[kb] = in ? *(const u32x4_t*)(r2src + oi * own_row + dim) : (u32x4_t){0u, 0u, 0u, 0u};
+    }
+  }
+
+  // dQ: the query's LSE (log2 units; +inf for an empty row makes P = 0) and Delta are per lane.
+  float lse2_own = 0.f, dlt_own = 0.f;
+  if constexpr (OWN_Q) {
+    const long long qi = sv.lse_off + (long long)hd * p.lse_head + min(ow0 + l32, sv.lq - 1);
+    const float l = p.lse_in[qi];
+    lse2_own = l == -INFINITY ? INFINITY : l * kLog2e;
+    dlt_own = p.delta[qi];
+  }
+
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = (f32x16_t){};
+
+  // ---- streamed side
+  const int str_len = OWN_Q ? sv.lk : sv.lq;
+  const int str_row = OWN_Q ? p.k_row : p.q_row;
+  const int row_bytes = str_row * 2;
+  int nsteps, nqt = 1, qt_first = 0;
+  if constexpr (OWN_Q) {
+    int kend = sv.lk;
+    if (p.causal) kend = min(kend, o0 + C::BOWN + off);
+    nsteps = kend > 0 ? (kend + 31) >> 5 : 0;
+  } else {
+    const int qfirst = p.causal ? max(0, o0 - off) : 0;
+    qt_first = qfirst >> 5;
+    nqt = sv.lq > qfirst ? ((sv.lq + 31) >> 5) - qt_first : 0;
+    nsteps = p.group * nqt;
+  }
+  auto step_head = [&](int st) { return OWN_Q ? hd / p.group : hd * p.group + st / nqt; };
+  auto step_row0 = [&](int st) { return OWN_Q ? st * 32 : (qt_first + st % nqt) * 32; };
+  auto str_base = [&](int head) {
+    return OWN_Q ? sv.k_off + (long long)head * p.k_head : sv.q_off + (long long)head * p.q_head;
+  };
+  const uint32_t span = (uint32_t)min((long long)max(str_len, 1) * row_bytes, (long long)0xFFFFFFF0);
+
+  constexpr int IPR = C::RS / 1024;
+  const int dch = p.d >> 3;
+  int voff[C::NINSTR];
+#pragma unroll
+  for (int ii = 0; ii < C::NINSTR; ++ii) {
+    const int i = w + 4 * ii;
+    const int R = i / IPR;
+    const int pc = (i % IPR) * 64 + lane;
+    voff[ii] = min(pc ^ swz(R), dch - 1) << 4;
+  }
+  // Tile 1 feeds the scores (K for dQ, Q for dK/dV); tile 2 feeds dP (V for dQ, dO for dK) or the
+  // dV product (dO).
+  auto issue = [&](int st, int buf) {
+    const int head = step_head(st);
+    const int row0 = step_row0(st);
+    const long long base = str_base(head);
+    const __amdgpu_buffer_rsrc_t rs1 = make_rsrc((const uint16_t*)(OWN_Q ? p.k : p.q) + base, span);
+    const __amdgpu_buffer_rsrc_t rs2 = make_rsrc((const uint16_t*)(OWN_Q ? p.v : p.dout) + base, span);
+    lds_t* t1 = smem + buf * 2 * C::TILE;
+#pragma unroll
+    for (int ii = 0; ii < C::NINSTR; ++ii) {
+      const int i = w + 4 * ii;
+      const int row = min(row0 + i / IPR, str_len - 1);
+      dma16_buf(rs1, voff[ii], row * row_bytes, t1 + i * 1024);
+      dma16_buf(rs2, voff[ii], row * row_bytes, t1 + C::TILE + i * 1024);
+    }
+  };
+
+  const int krow = row_perm(l32);
+  const int kswz = swz(krow);
+  const int g16 = lane >> 4;
+  const int r16 = lane & 15;
+  lds_t* xbuf = smem + NBUF * 2 * C::TILE;
+
+  if (nsteps > 0) issue(0, 0);
+
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = NBUF == 2 ? (st & 1) : 0;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if constexpr (NBUF == 2) {
+      if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
+    }
+    const lds_t* t1 = smem + buf * 2 * C::TILE;
+    const lds_t* t2 = t1 + C::TILE;
+    const int row0 = step_row0(st);
+
+    // ---- partial S (and dP) over this wave's head-dim columns: C[streamed row][own row]
+    f32x16_t sacc = (f32x16_t){}, dpacc = (f32x16_t){};
+#pragma unroll
+    for (int kb = 0; kb < 2 * NDB; ++kb) {
+      const int chunk = (cg * C::DW >> 3) + 2 * kb + hh;
+      const int a_off = krow * C::RS + ((chunk ^ kswz) << 4);
+      sacc = Elt<T>::mma(lds_read_b128(t1, a_off), r1[kb], sacc);
+      if constexpr (HAS_DP) dpacc = Elt<T>::mma(lds_read_b128(t2, a_off), r2[kb], dpacc);
+    }
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      lds_write_f4(xbuf, (((w * NX + 0) * 4 + r4) * 64 + lane) * 16,
+                   (f32x4_t){sacc[4 * r4], sacc[4 * r4 + 1], sacc[4 * r4 + 2], sacc[4 * r4 + 3]});
+      if constexpr (HAS_DP)
+        lds_write_f4(xbuf, (((w * NX + 1) * 4 + r4) * 64 + lane) * 16,
+                     (f32x4_t){dpacc[4 * r4], dpacc[4 * r4 + 1], dpacc[4 * r4 + 2], dpacc[4 * r4 + 3]});
+    }
+    __syncthreads();
+    // Fixed commutative combination (bit-identical in every wave of the row group).
+    auto combine = [&](f32x16_t& v, int m) {
+      const int base = rg * NC;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        auto rd = [&](int wv) { return lds_read_f4(xbuf, (((wv * NX + m) * 4 + r4) * 64 + lane) * 16); };
+        f32x4_t mine = (f32x4_t){v[4 * r4], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]};
+        mine = mine + rd(base + (cg ^ 1));
+        if constexpr (NC == 4) {
+          const int o1 = base + ((cg & 2) ^ 2);
+          mine = mine + (rd(o1) + rd(o1 + 1));
+        }
+        v[4 * r4] = mine.x; v[4 * r4 + 1] = mine.y; v[4 * r4 + 2] = mine.z; v[4 * r4 + 3] = mine.w;
+      }
+    };
+    combine(sacc, 0);
+    if constexpr (HAS_DP) combine(dpacc, 1);
+
+    // ---- P (and dS) for the 16 (streamed, own) pairs of this lane
+    const int head = step_head(st);
+    const float* lrow = nullptr;
+    const float* drow = nullptr;
+    if constexpr (!OWN_Q) {
+      lrow = p.lse_in + sv.lse_off + (long long)head * p.lse_head;
+      drow = p.delta + sv.lse_off + (long long)head * p.lse_head;
+    }
+    uint32_t bop[2][4];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float v2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int rr = r + u;
+        const int si = row0 + c_row(rr, hh);  // streamed index
+        const int oi = ow0 + l32;             // own index
+        const int qi = OWN_Q ? oi : si;
+        const int ki = OWN_Q ? si : oi;
+        const bool legal = ki < sv.lk && qi < sv.lq && (!p.causal || ki <= qi + off);
+        float lse2, dlt;
+        if constexpr (OWN_Q) {
+          lse2 = lse2_own;
+          dlt = dlt_own;
+        } else {
+          // Both halves of the wave read row-uniform values (scalar loads), then select.
+          const int qa = min(row0 + c_row(rr, 0), sv.lq - 1);
+          const int qb = min(row0 + c_row(rr, 1), sv.lq - 1);
+          const float la = lrow[qa], lb = lrow[qb];
+          const float l = hh ? lb : la;
+          lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+          dlt = hh ? drow[qb] : drow[qa];
+        }
+        const float pv = legal ? fast_exp2(sacc[rr] * p.scale_log2 - lse2) : 0.f;
+        v2[u] = HAS_DP ? pv * (dpacc[rr] - dlt) : pv;
+      }
+      bop[r >> 3][(r & 7) >> 1] = Elt<T>::pack2(v2[0], v2[1]);
+    }
+
+    // ---- acc^T[d][own] += A[d][streamed] * B[streamed][own], A read transposed from the tile
+    const lds_t* tt = MODE == kDV ? t2 : t1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = cg * C::DW + 32 * db + 16 * (g16 & 1) + 4 * (r16 & 3);
+      const int chunk = d >> 3;
+      const int within = (d & 7) << 1;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int k0 = 16 * kb2 + 8 * hh + (r16 >> 2);
+        const int k1 = k0 + 4;
+        const s16x4_t lo = lds_read_tr16(tt, k0 * C::RS + ((chunk ^ swz(k0)) << 4) + within);
+        const s16x4_t hi = lds_read_tr16(tt, k1 * C::RS + ((chunk ^ swz(k1)) << 4) + within);
+        const u32x4_t bv = {bop[kb2][0], bop[kb2][1], bop[kb2][2], bop[kb2][3]};
+        acc[db] = Elt<T>::mma(join_tr(lo, hi), bv, acc[db]);
+      }
+    }
+
+    if constexpr (NBUF == 1) {
+      __syncthreads();
+      if (st + 1 < nsteps) issue(st + 1, 0);
+    }
+  }
+
+  // ---- epilogue: scale, round once to the storage dtype, store own rows
+  const float osc = MODE == kDV ? 1.0f : p.scale;
+  const int oi = ow0 + l32;
+  if (oi < own_len) {
+    uint16_t* dst = (uint16_t*)(MODE == kDQ ? p.dq : (MODE == kDK ? p.dk : p.dv)) + own_base + (long long)oi * own_row;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = cg * C::DW + 32 * db + 8 * i4 + 4 * hh;
+        if (d < p.d) {
+          const f32x16_t& a = acc[db];
+          const u32x2_t pk = {Elt<T>::pack2(a[4 * i4] * osc, a[4 * i4 + 1] * osc),
+                              Elt<T>::pack2(a[4 * i4 + 2] * osc, a[4 * i4 + 3] * osc)};
+          *(u32x2_t*)(dst + d) = pk;
+        }
+      }
+  }
+}
+
+template <class T, int MODE, int NC, int NDB>
+static hipError_t launch_bwd_cfg(AttnParams p, hipStream_t st) {
+  constexpr int NX = MODE != kDV ? 2 : 1;
+  constexpr int NBUF = (2 * 2 * BwdCfg<NC, NDB, 1, NX>::TILE + BwdCfg<NC, NDB, 1, NX>::XBYTES) <= 160 * 1024 ? 2 : 1;
+  using C = BwdCfg<NC, NDB, NBUF, NX>;
+  const bool own_q = MODE == kDQ;
+  p.ntiles = ((own_q ? p.nq : p.nkv) + C::BOWN - 1) / C::BOWN;
+  p.total = p.batch * (own_q ? p.hq : p.hkv) * p.ntiles;
+  if (p.total == 0) return hipSuccess;
+  const int grid = (p.total + 7) & ~7;
+  hipLaunchKernelGGL((ffpa_bwd_kernel<T, MODE, NC, NDB, NBUF>), dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <class T, int MODE>
+static hipError_t launch_bwd_mode(const AttnParams& p, hipStream_t st) {
+  if (p.d <= 512) {
+    switch ((p.d + 63) / 64) {
+      case 5: return launch_bwd_cfg<T, MODE, 2, 5>(p, st);
+      case 6: return launch_bwd_cfg<T, MODE, 2, 6>(p, st);
+      case 7: return launch_bwd_cfg<T, MODE, 2, 7>(p, st);
+      default: return launch_bwd_cfg<T, MODE, 2, 8>(p, st);
+    }
+  }
+  switch ((p.d + 127) / 128) {
+    case 5: return launch_bwd_cfg<T, MODE, 4, 5>(p, st);
+    case 6: return launch_bwd_cfg<T, MODE, 4, 6>(p, st);
+    case 7: return launch_bwd_cfg<T, MODE, 4, 7>(p, st);
+    default: return launch_bwd_cfg<T, MODE, 4, 8>(p, st);
+  }
+}
+
+template <class T>
+static hipError_t launch_bwd_t(const AttnParams& p, int nrows, int varlen_total, hipStream_t st) {
+  if (nrows > 0) {
+    const int blocks = (nrows + 15) / 16;
+    hipLaunchKernelGGL(ffpa_bwd_preprocess_kernel<T>, dim3(blocks), dim3(256), 0, st, p, nrows, varlen_total);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch_bwd_mode<T, kDV>(p, st);
+  if (e == hipSuccess) e = launch_bwd_mode<T, kDK>(p, st);
+  if (e == hipSuccess) e = launch_bwd_mode<T, kDQ>(p, st);
+  return e;
+}
+
+hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total, hipStream_t st) {
+  return fp16 ? launch_bwd_t<FP16>(p, nrows, varlen_total, st) : launch_bwd_t<BF16>(p, nrows, varlen_total, st);
+}
+
+}  // namespace ffpa

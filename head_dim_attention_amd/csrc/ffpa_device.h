@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ffpa_params.h"
+
 namespace ffpa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -52,6 +54,10 @@ template <> struct Elt<BF16> {
   static __device__ __forceinline__ float to_f32(uint16_t x) {
     return __builtin_bit_cast(float, (uint32_t)x << 16);
   }
+  static __device__ __forceinline__ void unpack2(uint32_t x, float& lo, float& hi) {
+    lo = __builtin_bit_cast(float, x << 16);
+    hi = __builtin_bit_cast(float, x & 0xffff0000u);
+  }
 };
 
 template <> struct Elt<FP16> {
@@ -65,6 +71,11 @@ template <> struct Elt<FP16> {
   }
   static __device__ __forceinline__ float to_f32(uint16_t x) {
     return (float)__builtin_bit_cast(_Float16, x);
+  }
+  static __device__ __forceinline__ void unpack2(uint32_t x, float& lo, float& hi) {
+    const f16x2_t v = __builtin_bit_cast(f16x2_t, x);
+    lo = (float)v.x;
+    hi = (float)v.y;
   }
 };
 
@@ -151,5 +162,25 @@ struct SeqView {
   long long q_off, k_off, lse_off;
   int lq, lk;
 };
+
+// Resolve slice s: a dense batch entry (strides) or a packed sequence (cu_seqlens).
+__device__ __forceinline__ SeqView seq_view(const AttnParams& p, int s) {
+  SeqView v;
+  if (p.cu_q != nullptr) {
+    const int q0 = p.cu_q[s], k0 = p.cu_k[s];
+    v.lq = p.cu_q[s + 1] - q0;
+    v.lk = p.cu_k[s + 1] - k0;
+    v.q_off = (long long)q0 * p.q_row;
+    v.k_off = (long long)k0 * p.k_row;
+    v.lse_off = q0;
+  } else {
+    v.lq = p.nq;
+    v.lk = p.nkv;
+    v.q_off = (long long)s * p.q_batch;
+    v.k_off = (long long)s * p.k_batch;
+    v.lse_off = (long long)s * p.lse_batch;
+  }
+  return v;
+}
 
 }  // namespace ffpa

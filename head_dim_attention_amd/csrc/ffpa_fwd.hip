@@ -26,25 +26,6 @@
 
 namespace ffpa {
 
-__device__ __forceinline__ SeqView seq_view(const AttnParams& p, int s) {
-  SeqView v;
-  if (p.cu_q != nullptr) {
-    const int q0 = p.cu_q[s], k0 = p.cu_k[s];
-    v.lq = p.cu_q[s + 1] - q0;
-    v.lk = p.cu_k[s + 1] - k0;
-    v.q_off = (long long)q0 * p.q_row;
-    v.k_off = (long long)k0 * p.k_row;
-    v.lse_off = q0;
-  } else {
-    v.lq = p.nq;
-    v.lk = p.nkv;
-    v.q_off = (long long)s * p.q_batch;
-    v.k_off = (long long)s * p.k_batch;
-    v.lse_off = (long long)s * p.lse_batch;
-  }
-  return v;
-}
-
 template <int NC, int NDB, int QB, int NBUF>
 struct FwdCfg {
   static constexpr int NR = 4 / NC;

@@ -1,0 +1,142 @@
+"""GPU parity of the four-stage backward (preprocess, dV, dK, dQ) against the float64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import ref
+from tests.gpu_helpers import check_grads, to64
+
+pytestmark = pytest.mark.gpu
+
+BF, FP = torch.bfloat16, torch.float16
+
+# (B, Hq, Hkv, Nq, Nkv, D, dtype, causal)
+DENSE_CASES = [
+    (1, 2, 2, 64, 64, 320, BF, False),
+    (1, 2, 2, 33, 33, 320, FP, True),
+    (2, 4, 2, 65, 200, 352, BF, True),
+    (1, 2, 1, 200, 65, 512, FP, True),
+    (1, 3, 3, 129, 129, 512, BF, False),
+    (1, 4, 1, 130, 130, 544, BF, True),
+    (1, 2, 2, 1, 300, 1024, FP, False),
+    (1, 2, 2, 257, 257, 1024, BF, True),
+    (1, 8, 2, 100, 333, 768, FP, False),
+    (1, 2, 2, 96, 1, 416, BF, False),
+    (1, 4, 2, 70, 40, 896, FP, True),
+]
+
+
+def _ids(c):
+    b, hq, hkv, nq, nkv, d, dt, causal = c
+    return f"b{b}h{hq}x{hkv}q{nq}k{nkv}d{d}{'bf16' if dt == BF else 'fp16'}{'c' if causal else ''}"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import head_dim_attention_amd as F
+    F.load_library()
+    return F
+
+
+def _run_dense(lib, q, k, v, do, causal, scale):
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = lib.ffpa_fwd(qc, kc, vc, causal=causal, scale=scale)
+    dq, dk, dv = lib.ffpa_bwd(qc, kc, vc, o, doc, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=_ids)
+def test_bwd_dense(lib, case):
+    b, hq, hkv, nq, nkv, d, dt, causal = case
+    q, k, v, do = W.dense_inputs(b, hq, hkv, nq, nkv, d, dt, seed=4321 + nq + d)
+    scale = 1.0 / math.sqrt(d)
+    print(f"case {_ids(case)}", flush=True)
+    _, _, dq, dk, dv = _run_dense(lib, q, k, v, do, causal, scale)
+    g_ref = ref.attn_bwd(q, k, v, do, scale=np.float64(np.float32(scale)), causal=causal)
+    check_grads((dq, dk, dv), g_ref, _ids(case))
+
+
+def test_bwd_empty_rows_zero_grad(lib):
+    """Causal with Nq > Nkv: rows without a legal key get dQ = 0 exactly and add nothing to dK/dV."""
+    q, k, v, do = W.dense_inputs(1, 2, 2, 100, 30, 320, FP, seed=21)
+    _, _, dq, dk, dv = _run_dense(lib, q, k, v, do, True, None)
+    assert torch.all(dq[:, :, :70] == 0)
+    do2 = do.clone()
+    do2[:, :, :70] = 100.0
+    _, _, dq2, dk2, dv2 = _run_dense(lib, q, k, v, do2, True, None)
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    assert torch.all(dq2[:, :, :70] == 0)
+
+
+def test_bwd_deterministic(lib):
+    q, k, v, do = W.dense_inputs(1, 4, 2, 200, 200, 512, BF, seed=22)
+    r1 = _run_dense(lib, q, k, v, do, True, None)
+    r2 = _run_dense(lib, q, k, v, do, True, None)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+def test_bwd_gqa_matches_group_sum(lib):
+    """GQA dK/dV equal the group sums of MHA gradients on repeated K/V (to fp32 accumulation)."""
+    q, k, v, do = W.dense_inputs(1, 8, 2, 96, 96, 512, BF, seed=23)
+    _, _, dq1, dk1, dv1 = _run_dense(lib, q, k, v, do, True, None)
+    _, _, dq2, dk2, dv2 = _run_dense(lib, q, k.repeat_interleave(4, 1), v.repeat_interleave(4, 1), do, True, None)
+    assert torch.equal(dq1, dq2)
+    g = lambda x: to64(x).reshape(1, 2, 4, 96, 512).sum(axis=2)
+    for a, b in ((dk1, dk2), (dv1, dv2)):
+        x, y = to64(a), g(b)
+        assert np.linalg.norm(x - y) / np.linalg.norm(y) < 1e-2
+
+
+def test_bwd_autograd_wrapper(lib):
+    q, k, v, do = W.dense_inputs(1, 2, 1, 80, 80, 448, BF, seed=24)
+    qc, kc, vc = (x.cuda().requires_grad_(True) for x in (q, k, v))
+    o = lib.ffpa_attn_func(qc, kc, vc, is_causal=True)
+    o.backward(do.cuda())
+    _, _, dq, dk, dv = _run_dense(lib, q, k, v, do, True, None)
+    assert torch.equal(qc.grad, dq) and torch.equal(kc.grad, dk) and torch.equal(vc.grad, dv)
+
+
+VARLEN_CASES = [
+    ([17, 64, 200, 1], [17, 64, 200, 1], 4, 4, 512, BF, True),
+    ([0, 33, 130, 64], [5, 0, 64, 130], 4, 2, 320, FP, True),
+    ([50, 7, 129], [80, 200, 3], 2, 1, 1024, BF, False),
+    ([64, 64], [64, 64], 2, 2, 704, FP, True),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: f"q{c[0]}k{c[1]}h{c[2]}x{c[3]}d{c[4]}{'c' if c[6] else ''}")
+def test_bwd_varlen(lib, case):
+    lq, lk, hq, hkv, d, dt, causal = case
+    q, k, v, do, cu_q, cu_k = W.varlen_inputs(lq, lk, hq, hkv, d, dt, seed=77 + d)
+    scale = 1.0 / math.sqrt(d)
+    qc, kc, vc, doc, cq, ck = q.cuda(), k.cuda(), v.cuda(), do.cuda(), cu_q.cuda(), cu_k.cuda()
+    o, lse = lib.ffpa_varlen_fwd(qc, kc, vc, cq, ck, causal=causal, scale=scale)
+    dq, dk, dv = lib.ffpa_varlen_bwd(qc, kc, vc, o, doc, lse, cq, ck, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    g_ref = ref.varlen_bwd(q, k, v, do, cu_q.numpy(), cu_k.numpy(), scale=np.float64(np.float32(scale)),
+                           causal=causal)
+    check_grads((dq, dk, dv), g_ref, f"varlen {lq} {lk}")
+
+
+def test_bwd_varlen_equals_dense(lib):
+    """A packed batch gives the same gradients as separate dense calls per sequence."""
+    lens = [40, 97, 64]
+    q, k, v, do, cu_q, cu_k = W.varlen_inputs(lens, lens, 2, 2, 512, BF, seed=25)
+    qc, kc, vc, doc, cq = q.cuda(), k.cuda(), v.cuda(), do.cuda(), cu_q.cuda()
+    o, lse = lib.ffpa_varlen_fwd(qc, kc, vc, cq, causal=True)
+    dq, dk, dv = lib.ffpa_varlen_bwd(qc, kc, vc, o, doc, lse, cq, causal=True)
+    torch.cuda.synchronize()
+    for s, n in enumerate(lens):
+        a, b = int(cu_q[s]), int(cu_q[s + 1])
+        sl = lambda x: x[a:b].transpose(0, 1).unsqueeze(0).contiguous()
+        od, lsed = lib.ffpa_fwd(sl(qc), sl(kc), sl(vc), causal=True)
+        g = lib.ffpa_bwd(sl(qc), sl(kc), sl(vc), od, sl(doc), lsed, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(od, sl(o)) and torch.equal(lsed[0], lse[:, a:b])
+        for x, y in zip((dq, dk, dv), g):
+            assert torch.equal(sl(x), y)
