@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "FFPA_OK", "FFPA_ERR_INVALID_ARGUMENT", "FFPA_ERR_NOT_SUPPORTED", "FFPA_ERR_HIP",
     "library_path", "load_library", "ffpa_status_string",
-    "ffpa_fwd", "ffpa_bwd", "ffpa_varlen_fwd", "ffpa_varlen_bwd",
+    "ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd",
 ]
 
 FFPA_OK = 0
@@ -38,6 +38,7 @@ _f = ctypes.c_float
 _SIGNATURES = {
     "ffpa_fwd": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp],
     "ffpa_bwd": [_vp] * 10 + [_i] * 7 + [_f, _i, _vp],
+    "ffpa_bwd_stage": [_i] + [_vp] * 10 + [_i] * 7 + [_f, _i, _vp],
     "ffpa_varlen_fwd": [_vp] * 7 + [_i] * 9 + [_f, _i, _vp],
     "ffpa_varlen_bwd": [_vp] * 12 + [_i] * 9 + [_f, _i, _vp],
 }
@@ -152,6 +153,24 @@ def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float]
                                  _dtype_code(q), _scale(scale, d), int(bool(causal)), _stream(q))
     _raise_for(st, "ffpa_bwd")
     return dq, dk, dv
+
+
+def ffpa_bwd_stage(stage: int, q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool = False,
+                   scale: Optional[float] = None):
+    """Run one backward stage (0 preprocess, 1 dV, 2 dK, 3 dQ) into caller-provided buffers.
+
+    All tensors must be contiguous GPU tensors with ffpa_bwd's shapes; delta is float32 [B,Hq,Nq].
+    """
+    for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (lse, "lse"), (delta, "delta"),
+                 (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if not (isinstance(x, torch.Tensor) and x.device.type == "cuda" and x.is_contiguous()):
+            raise ValueError(f"{n} must be a contiguous GPU tensor")
+    b, hq, nq, d = q.shape
+    _, hkv, nkv, _ = k.shape
+    st = load_library().ffpa_bwd_stage(int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                       _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, nq, nkv, d,
+                                       _dtype_code(q), _scale(scale, d), int(bool(causal)), _stream(q))
+    _raise_for(st, "ffpa_bwd_stage")
 
 
 def _check_cu(cu: torch.Tensor, total: int, what: str) -> list[int]:

@@ -9,7 +9,7 @@
 
 namespace ffpa {
 hipError_t launch_fwd(const AttnParams& p, int fp16, hipStream_t st);
-hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total, hipStream_t st);
+hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total, hipStream_t st, int stage);
 }  // namespace ffpa
 
 using ffpa::AttnParams;
@@ -124,9 +124,10 @@ int ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float*
   return to_status(ffpa::launch_fwd(p, dtype == FFPA_DTYPE_FP16, (hipStream_t)stream));
 }
 
-int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-             float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq, int nkv, int d,
-             int dtype, float scale, int causal, void* stream) {
+static int dense_bwd(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv,
+                     int nq, int nkv, int d, int dtype, float scale, int causal, void* stream) {
+  if (stage < -1 || stage > 3) return FFPA_ERR_INVALID_ARGUMENT;
   if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
   const int st = check_common(hq, hkv, d, dtype, scale, causal);
@@ -145,7 +146,22 @@ int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, (int)nrows, 0, (hipStream_t)stream));
+  return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, (int)nrows, 0, (hipStream_t)stream, stage));
+}
+
+int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq, int nkv, int d,
+             int dtype, float scale, int causal, void* stream) {
+  return dense_bwd(-1, q, k, v, o, dout, lse, delta, dq, dk, dv, batch, hq, hkv, nq, nkv, d, dtype, scale, causal,
+                   stream);
+}
+
+int ffpa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq,
+                   int nkv, int d, int dtype, float scale, int causal, void* stream) {
+  if (stage < 0 || stage > 3) return FFPA_ERR_INVALID_ARGUMENT;
+  return dense_bwd(stage, q, k, v, o, dout, lse, delta, dq, dk, dv, batch, hq, hkv, nq, nkv, d, dtype, scale, causal,
+                   stream);
 }
 
 int ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -181,7 +197,7 @@ int ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, 
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, total_q * hq, total_q, (hipStream_t)stream));
+  return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, total_q * hq, total_q, (hipStream_t)stream, -1));
 }
 
 const char* ffpa_status_string(int status) {

@@ -378,21 +378,29 @@ static hipError_t launch_bwd_mode(const AttnParams& p, hipStream_t st) {
 }
 
 template <class T>
-static hipError_t launch_bwd_t(const AttnParams& p, int nrows, int varlen_total, hipStream_t st) {
-  if (nrows > 0) {
-    const int blocks = (nrows + 15) / 16;
-    hipLaunchKernelGGL(ffpa_bwd_preprocess_kernel<T>, dim3(blocks), dim3(256), 0, st, p, nrows, varlen_total);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+static hipError_t launch_stage_t(int stage, const AttnParams& p, int nrows, int varlen_total, hipStream_t st) {
+  switch (stage) {
+    case 0:
+      if (nrows > 0) {
+        const int blocks = (nrows + 15) / 16;
+        hipLaunchKernelGGL(ffpa_bwd_preprocess_kernel<T>, dim3(blocks), dim3(256), 0, st, p, nrows, varlen_total);
+        return hipGetLastError();
+      }
+      return hipSuccess;
+    case 1: return launch_bwd_mode<T, kDV>(p, st);
+    case 2: return launch_bwd_mode<T, kDK>(p, st);
+    default: return launch_bwd_mode<T, kDQ>(p, st);
   }
-  hipError_t e = launch_bwd_mode<T, kDV>(p, st);
-  if (e == hipSuccess) e = launch_bwd_mode<T, kDK>(p, st);
-  if (e == hipSuccess) e = launch_bwd_mode<T, kDQ>(p, st);
-  return e;
 }
 
-hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total, hipStream_t st) {
-  return fp16 ? launch_bwd_t<FP16>(p, nrows, varlen_total, st) : launch_bwd_t<BF16>(p, nrows, varlen_total, st);
+// Stage 0 = preprocess, 1 = dV, 2 = dK, 3 = dQ; -1 runs all four in order.
+hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total, hipStream_t st, int stage) {
+  for (int s = stage < 0 ? 0 : stage; s <= (stage < 0 ? 3 : stage); ++s) {
+    const hipError_t e = fp16 ? launch_stage_t<FP16>(s, p, nrows, varlen_total, st)
+                              : launch_stage_t<BF16>(s, p, nrows, varlen_total, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace ffpa

@@ -82,6 +82,18 @@ int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int dtype, float scale, int causal, void* stream);
 
 /*
+ * One stage of the dense backward, with exactly the arguments of ffpa_bwd plus `stage`:
+ *   0 = preprocess (writes delta), 1 = dV, 2 = dK, 3 = dQ.
+ * ffpa_bwd is these four launches in order; stages 2 and 3 read the delta written by stage 0.
+ * Lets a caller time or schedule the launches individually ("CuTe-DSL Backend", "Blackwell
+ * status": the backward is four launches). Returns FFPA_ERR_INVALID_ARGUMENT for another stage.
+ */
+int ffpa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, float* delta, void* dq, void* dk, void* dv,
+                   int batch, int hq, int hkv, int nq, int nkv, int d,
+                   int dtype, float scale, int causal, void* stream);
+
+/*
  * Packed (THD) varlen forward ("CuTe-DSL Backend", "Varlen (packed THD) API").
  *   q [total_q, hq, d]; k, v [total_k, hkv, d]; o [total_q, hq, d]; lse [hq, total_q] fp32.
  *   cu_seqlens_q [batch+1], cu_seqlens_k [batch+1]: device int32, start at 0, non-decreasing,
