@@ -32,7 +32,7 @@ HBM_PEAK_GBS = 8000.0
 # Algorithmic flops per legal pair and query head, by kernel (D multiplies these).
 KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "dv": 4, "dk": 6, "dq": 6}
 STAGES = ("fwd", "pre", "dv", "dk", "dq")
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "traffic_dense_d512_n8192.json")
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "traffic_dense_d512_n8192.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "head_dim_attention_amd", "csrc", f)
                   for f in ("ffpa_device.h", "ffpa_params.h", "ffpa_fwd.hip", "ffpa_bwd.hip")]
 
