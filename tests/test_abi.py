@@ -1,0 +1,164 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every declared entry point, and
+validates arguments on the host (returning a status before touching the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ffpa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(ffpa_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from head_dim_attention_amd import _binding
+    path = _binding.library_path()
+    if not os.path.exists(path):
+        pytest.fail(f"libffpa.so is not built at {path}: run python -m head_dim_attention_amd.build")
+    return _binding.load_library()
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared()
+    for n in ("ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd", "ffpa_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), f"{name} declared in include/ffpa.h but not exported"
+
+
+def test_status_strings(lib):
+    from head_dim_attention_amd import _binding as B
+    for code in (0, 1, 2, 3, 99):
+        s = B.ffpa_status_string(code)
+        assert isinstance(s, str) and s
+    assert "INVALID" in B.ffpa_status_string(1)
+    assert "NOT_SUPPORTED" in B.ffpa_status_string(2)
+
+
+# A fake non-null device pointer: validation returns before anything dereferences it.
+P = ctypes.c_void_p(0x1000)
+N = ctypes.c_void_p(0)
+S = ctypes.c_void_p(0)
+
+
+def _fwd(lib, b=1, hq=2, hkv=2, nq=64, nkv=64, d=512, dtype=0, scale=0.04, causal=0, ptrs=None):
+    ptrs = ptrs or [P] * 5
+    return lib.ffpa_fwd(*ptrs, b, hq, hkv, nq, nkv, d, dtype, scale, causal, S)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(b=0), 1), (dict(nq=0), 1), (dict(nkv=0), 1), (dict(hq=3, hkv=2), 1), (dict(hkv=0), 1),
+    (dict(dtype=2), 1), (dict(dtype=-1), 1), (dict(causal=2), 1), (dict(scale=0.0), 1), (dict(scale=-1.0), 1),
+    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
+    (dict(d=288), 2), (dict(d=1056), 2), (dict(d=336), 2), (dict(d=64), 2),
+])
+def test_fwd_validation(lib, kw, expect):
+    assert _fwd(lib, **kw) == expect
+
+
+def test_fwd_null_pointers(lib):
+    for i in range(5):
+        ptrs = [P] * 5
+        ptrs[i] = N
+        assert _fwd(lib, ptrs=ptrs) == 1
+
+
+def _bwd(lib, stage=None, b=1, hq=2, hkv=1, nq=64, nkv=64, d=640, dtype=1, scale=0.04, causal=1, ptrs=None):
+    ptrs = ptrs or [P] * 10
+    args = (*ptrs, b, hq, hkv, nq, nkv, d, dtype, scale, causal, S)
+    return lib.ffpa_bwd(*args) if stage is None else lib.ffpa_bwd_stage(stage, *args)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(b=0), 1), (dict(hq=3, hkv=2), 1), (dict(d=300), 2), (dict(dtype=5), 1), (dict(scale=0.0), 1),
+    (dict(stage=4), 1), (dict(stage=-1), 1), (dict(stage=2, d=2048), 2),
+])
+def test_bwd_validation(lib, kw, expect):
+    assert _bwd(lib, **kw) == expect
+
+
+def test_bwd_null_pointers(lib):
+    for i in range(10):
+        ptrs = [P] * 10
+        ptrs[i] = N
+        assert _bwd(lib, ptrs=ptrs) == 1
+
+
+def _vfwd(lib, batch=2, mq=64, mk=64, tq=128, tk=128, hq=4, hkv=2, d=512, dtype=0, scale=0.04, causal=1,
+          ptrs=None):
+    ptrs = ptrs or [P] * 7
+    return lib.ffpa_varlen_fwd(*ptrs, batch, mq, mk, tq, tk, hq, hkv, d, dtype, scale, causal, S)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(batch=0), 1), (dict(mq=-1), 1), (dict(tq=-1), 1), (dict(mq=200), 1), (dict(mk=300), 1),
+    (dict(hq=5), 1), (dict(d=100), 2), (dict(causal=-1), 1),
+])
+def test_varlen_fwd_validation(lib, kw, expect):
+    assert _vfwd(lib, **kw) == expect
+
+
+def test_varlen_null_pointers(lib):
+    for i in range(6):  # q, k, v, o, lse, cu_seqlens_q are required; cu_seqlens_k may be NULL
+        ptrs = [P] * 7
+        ptrs[i] = N
+        assert _vfwd(lib, ptrs=ptrs) == 1
+    args = [P] * 12
+    args[3] = N
+    assert lib.ffpa_varlen_bwd(*args, 2, 64, 64, 128, 128, 4, 2, 512, 0, 0.04, 1, S) == 1
+
+
+def test_varlen_empty_batch_is_a_noop(lib):
+    # total_q == 0: nothing to compute, no launch, OK (no GPU needed).
+    assert _vfwd(lib, tq=0, mq=0) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import head_dim_attention_amd as F
+    q = torch.zeros(1, 2, 8, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        F.ffpa_fwd(q, q, q)
+
+
+def test_binding_rejects_bad_dtype_before_launch():
+    from head_dim_attention_amd import _binding as B
+    with pytest.raises(NotImplementedError):
+        B._dtype_code(torch.zeros(1, dtype=torch.float32))
+
+
+def test_binding_checks_cu_seqlens_on_host():
+    from head_dim_attention_amd import _binding as B
+    ok = torch.tensor([0, 3, 3, 8], dtype=torch.int32)
+    assert B._check_cu(ok, 8, "cu") == [0, 3, 3, 8]
+    for bad, total in ((torch.tensor([1, 3, 8], dtype=torch.int32), 8),
+                       (torch.tensor([0, 5, 3, 8], dtype=torch.int32), 8),
+                       (torch.tensor([0, 3, 7], dtype=torch.int32), 8),
+                       (torch.tensor([0, 3, 8], dtype=torch.int64), 8)):
+        with pytest.raises(ValueError):
+            B._check_cu(bad, total, "cu")
+
+
+def test_bench_refuses_multi_gpu():
+    import bench
+    assert bench.main(["--gpus", "2"]) == 2
+
+
+def test_bench_legal_pair_count():
+    import bench
+    assert bench.legal_pairs(4, 4, False) == 16
+    assert bench.legal_pairs(4, 4, True) == 10
+    assert bench.legal_pairs(5, 3, True) == 0 + 0 + 1 + 2 + 3
+    assert bench.legal_pairs(3, 5, True) == 3 + 4 + 5
+    n = 8192
+    assert bench.legal_pairs(n, n, True) == n * (n + 1) // 2
