@@ -22,9 +22,12 @@ ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for all device code: the compiler is kept from emitting
 # v_pk_{add,mul,fma}_f32.
+# MFMA accumulators are kept in VGPRs (-amdgpu-mfma-vgpr-form): the kernels read every score block
+# with VALU instructions, and the stationary MFMA operands then go to AGPRs instead.
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-I", os.path.join(ROOT, "include"),
 ]
 
@@ -52,28 +55,33 @@ def _run(cmd: list[str], verbose: bool) -> None:
         print(err, file=sys.stderr)
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
+def build(jobs: int | None = None, verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
+    """Compile every source under csrc/ and link `out` (default: the in-package libffpa.so)."""
     cc = hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    bdir = BUILD if out == LIB else out + ".objs"
+    os.makedirs(bdir, exist_ok=True)
     srcs = sources()
-    objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    objs = [os.path.join(bdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2)))
+    flags = [*HIP_FLAGS, *extra_flags]
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, [cc, *HIP_FLAGS, "-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
+        futs = [ex.submit(_run, [cc, *flags, "-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--out", default=LIB, help="output library path (variants for comparison)")
+    ap.add_argument("--extra-flag", action="append", default=[], help="extra hipcc flag (repeatable)")
     a = ap.parse_args(argv)
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs, a.verbose, os.path.abspath(a.out), a.extra_flag))
     return 0
 
 

@@ -195,8 +195,8 @@ __global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
     const int head = step_head(st);
     const int row0 = step_row0(st);
     const long long base = str_base(head);
-    const __amdgpu_buffer_rsrc_t rs1 = make_rsrc((const uint16_t*)(OWN_Q ? p.k : p.q) + base, span);
-    const __amdgpu_buffer_rsrc_t rs2 = make_rsrc((const uint16_t*)(OWN_Q ? p.v : p.dout) + base, span);
+    const i32x4_t rs1 = make_rsrc((const uint16_t*)(OWN_Q ? p.k : p.q) + base, span);
+    const i32x4_t rs2 = make_rsrc((const uint16_t*)(OWN_Q ? p.v : p.dout) + base, span);
     lds_t* t1 = smem + buf * 2 * C::TILE;
 #pragma unroll
     for (int ii = 0; ii < C::NINSTR; ++ii) {
@@ -213,14 +213,37 @@ __global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
   const int r16 = lane & 15;
   lds_t* xbuf = smem + NBUF * 2 * C::TILE;
 
-  if (nsteps > 0) issue(0, 0);
+  // dK/dV: LSE (log2 units; +inf for an empty row makes P = 0) and Delta of streamed query row
+  // row0 + l % 32, loaded one step ahead and after that step's tile copy, so the wait that makes
+  // the tile visible covers them too.
+  // The raw values are kept until use so that no instruction waits on the loads early.
+  float lse_next = 0.f, dlt_next = 0.f;
+  auto load_row_stats = [&](int st) {
+    if constexpr (!OWN_Q) {
+      const long long li = sv.lse_off + (long long)step_head(st) * p.lse_head + min(step_row0(st) + l32, sv.lq - 1);
+      lse_next = p.lse_in[li];
+      dlt_next = p.delta[li];
+    }
+  };
+
+  if (nsteps > 0) {
+    issue(0, 0);
+    load_row_stats(0);
+  }
+  // Stationary operands, row statistics and tile 0 are complete before the loop.
+  wait_all();
 
   for (int st = 0; st < nsteps; ++st) {
     const int buf = NBUF == 2 ? (st & 1) : 0;
     wait_vmcnt<0>();
-    __syncthreads();
+    lds_barrier();
+    const float lse2_cur = lse_next == -INFINITY ? INFINITY : lse_next * kLog2e;
+    const float dlt_cur = dlt_next;
     if constexpr (NBUF == 2) {
-      if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
+      if (st + 1 < nsteps) {
+        issue(st + 1, buf ^ 1);
+        load_row_stats(st + 1);
+      }
     }
     const lds_t* t1 = smem + buf * 2 * C::TILE;
     const lds_t* t2 = t1 + C::TILE;
@@ -243,7 +266,7 @@ __global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
         lds_write_f4(xbuf, (((w * NX + 1) * 4 + r4) * 64 + lane) * 16,
                      (f32x4_t){dpacc[4 * r4], dpacc[4 * r4 + 1], dpacc[4 * r4 + 2], dpacc[4 * r4 + 3]});
     }
-    __syncthreads();
+    lds_barrier();
     // Fixed commutative combination (bit-identical in every wave of the row group).
     auto combine = [&](f32x16_t& v, int m) {
       const int base = rg * NC;
@@ -263,12 +286,23 @@ __global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
     if constexpr (HAS_DP) combine(dpacc, 1);
 
     // ---- P (and dS) for the 16 (streamed, own) pairs of this lane
-    const int head = step_head(st);
-    const float* lrow = nullptr;
-    const float* drow = nullptr;
-    if constexpr (!OWN_Q) {
-      lrow = p.lse_in + sv.lse_off + (long long)head * p.lse_head;
-      drow = p.delta + sv.lse_off + (long long)head * p.lse_head;
+    // dK/dV: the streamed rows are queries; lane l holds LSE/Delta of query row0 + l % 32 and the
+    // values of the 16 rows c_row(r, h) a lane needs are broadcast with ds_bpermute.
+    const float lse2_lane = OWN_Q ? lse2_own : lse2_cur;
+    const float dlt_lane = OWN_Q ? dlt_own : dlt_cur;
+    const int bp_base = (8 * hh) << 2;  // byte address of lane 8h for ds_bpermute
+    auto row_val = [&](float x, int r) -> float {
+      if constexpr (OWN_Q) return x;
+      const int c = 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);  // c_row(r, h) - 8h
+      return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp_base + 4 * c, __builtin_bit_cast(int, x)));
+    };
+    // Masking is needed only on tiles that cross the causal diagonal or the end of either side.
+    const int oi = ow0 + l32;
+    bool need_mask;
+    if constexpr (OWN_Q) {
+      need_mask = (row0 + 32 > sv.lk) || (p.causal && row0 + 31 > ow0 + off);
+    } else {
+      need_mask = (row0 + 32 > sv.lq) || (p.causal && ow0 + 31 > row0 + off);
     }
     uint32_t bop[2][4];
 #pragma unroll
@@ -277,26 +311,17 @@ __global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int rr = r + u;
-        const int si = row0 + c_row(rr, hh);  // streamed index
-        const int oi = ow0 + l32;             // own index
-        const int qi = OWN_Q ? oi : si;
-        const int ki = OWN_Q ? si : oi;
-        const bool legal = ki < sv.lk && qi < sv.lq && (!p.causal || ki <= qi + off);
-        float lse2, dlt;
-        if constexpr (OWN_Q) {
-          lse2 = lse2_own;
-          dlt = dlt_own;
-        } else {
-          // Both halves of the wave read row-uniform values (scalar loads), then select.
-          const int qa = min(row0 + c_row(rr, 0), sv.lq - 1);
-          const int qb = min(row0 + c_row(rr, 1), sv.lq - 1);
-          const float la = lrow[qa], lb = lrow[qb];
-          const float l = hh ? lb : la;
-          lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-          dlt = hh ? drow[qb] : drow[qa];
+        const float lse2 = row_val(lse2_lane, rr);
+        float pv = fast_exp2(sacc[rr] * p.scale_log2 - lse2);
+        if (need_mask) {
+          const int si = row0 + c_row(rr, hh);
+          const int qi = OWN_Q ? oi : si;
+          const int ki = OWN_Q ? si : oi;
+          const bool legal = ki < sv.lk && qi < sv.lq && (!p.causal || ki <= qi + off);
+          pv = legal ? pv : 0.f;
         }
-        const float pv = legal ? fast_exp2(sacc[rr] * p.scale_log2 - lse2) : 0.f;
-        v2[u] = HAS_DP ? pv * (dpacc[rr] - dlt) : pv;
+        if constexpr (HAS_DP) pv = pv * (dpacc[rr] - row_val(dlt_lane, rr));
+        v2[u] = pv;
       }
       bop[r >> 3][(r & 7) >> 1] = Elt<T>::pack2(v2[0], v2[1]);
     }
@@ -320,8 +345,11 @@ __global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
     }
 
     if constexpr (NBUF == 1) {
-      __syncthreads();
-      if (st + 1 < nsteps) issue(st + 1, 0);
+      lds_barrier();
+      if (st + 1 < nsteps) {
+        issue(st + 1, 0);
+        load_row_stats(st + 1);
+      }
     }
   }
 

@@ -129,21 +129,64 @@ __device__ __forceinline__ void dma16(const void* gptr, lds_t* lds) {
   __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// Buffer resource over [base, base + bytes) for raw (unformatted) 32-bit accesses.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource descriptor over [base, base + bytes) for raw (unformatted) 32-bit accesses:
+// base address in words 0-1 (stride 0), size in word 2, data format 32 in word 3.
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  return (i32x4_t){(int32_t)(uint32_t)b, (int32_t)((b >> 32) & 0xffff), (int32_t)bytes, 0x00020000};
 }
 
-// Same copy through a buffer resource: lane l reads base + voff(lane) + soff (soff wave-uniform)
-// and writes LDS bytes [lds + 16 l, lds + 16 l + 16).
-__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff, lds_t* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+// Asynchronous 16-byte copy through a buffer resource: lane l reads base + voff(lane) + soff and
+// writes LDS bytes [lds + 16 l, lds + 16 l + 16) (buffer_load_dwordx4 ... lds, LDS address in M0).
+// It is issued as inline asm on purpose: the compiler then does not track it, and so does not wait
+// for an in-flight prefetch of the next tile before reading the current one. Callers make copied
+// data visible explicitly: wait_vmcnt() in every issuing wave, then lds_barrier().
+// M0 is saved and restored around the copy, so its value is unchanged for the compiler.
+__device__ __forceinline__ void dma16_buf(i32x4_t r, int voff, int soff, lds_t* lds) {
+  // All scalar operands are wave-uniform by construction; readfirstlane makes that explicit.
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  r = (i32x4_t){__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
+                __builtin_amdgcn_readfirstlane(r.z), __builtin_amdgcn_readfirstlane(r.w)};
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(r), "s"(soff), "s"(m)
+      : "memory");
 }
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding. Issued through the
+// builtin so the compiler accounts for it in its own wait tracking.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 15));
+}
+
+// Wait for every outstanding memory operation of this wave.
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0)); }
+
+// Workgroup barrier that orders LDS accesses only. __syncthreads() adds a release fence that also
+// waits for every outstanding global load, including asynchronous global->LDS prefetches of the
+// next tile, which would expose their full latency at every exchange. Prefetched tiles are made
+// visible separately: wait_vmcnt() in every issuing wave, then this barrier. The empty asm
+// statements keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

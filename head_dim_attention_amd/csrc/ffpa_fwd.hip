@@ -43,8 +43,11 @@ struct FwdCfg {
 template <class T, int NC, int NDB, int QB, int NBUF>
 __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
   using C = FwdCfg<NC, NDB, QB, NBUF>;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
-  lds_t* smem = (lds_t*)smem_raw;
+  __shared__ __attribute__((aligned(1024))) char k0_raw[C::TILE], v0_raw[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1_raw[NBUF == 2 ? C::TILE : 16], v1_raw[NBUF == 2 ? C::TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char x_raw[C::XBYTES];
+  auto kbuf = [&](int b) { return b ? (lds_t*)k1_raw : (lds_t*)k0_raw; };
+  auto vbuf = [&](int b) { return b ? (lds_t*)v1_raw : (lds_t*)v0_raw; };
 
   // Work item: XCD-aware decode. Consecutive workgroup ids go round-robin over the 8 XCDs, so
   // item = (id % 8) * (grid / 8) + id / 8 gives each XCD a contiguous run of (head, tile) items
@@ -76,8 +79,8 @@ __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
   const char* kbase = (const char*)p.k + 2 * (sv.k_off + (long long)kvh * p.k_head);
   const char* vbase = (const char*)p.v + 2 * (sv.k_off + (long long)kvh * p.k_head);
   const uint32_t span = (uint32_t)min((long long)max(sv.lk, 1) * row_bytes, (long long)0xFFFFFFF0);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, span);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, span);
+  const i32x4_t krs = make_rsrc(kbase, span);
+  const i32x4_t vrs = make_rsrc(vbase, span);
 
   const int off = sv.lk - sv.lq;  // tail alignment of the causal mask
   int kend = sv.lk;
@@ -107,7 +110,7 @@ __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
     for (int db = 0; db < NDB; ++db) oacc[qb][db] = (f32x16_t){};
   }
 
-  lds_t* xbuf = smem + NBUF * 2 * C::TILE;
+  lds_t* const xbuf = (lds_t*)x_raw;
 
   // DMA: instruction ii of this wave fills LDS bytes [1024 i, 1024 i + 1024) of a tile, i = w + 4 ii,
   // i.e. tile row R = i / (RS / 1024) (uniform per instruction). Lane l writes physical chunk
@@ -124,7 +127,7 @@ __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
     const int pc = (i % IPR) * 64 + lane;
     voff[ii] = min(pc ^ swz(R), dch - 1) << 4;
   }
-  auto issue = [&](__amdgpu_buffer_rsrc_t rs, int j, lds_t* dst) {
+  auto issue = [&](i32x4_t rs, int j, lds_t* dst) {
 #pragma unroll
     for (int ii = 0; ii < C::NINSTR; ++ii) {
       const int i = w + 4 * ii;
@@ -143,39 +146,42 @@ __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
   auto top = [&](int j) {
     if constexpr (NBUF == 2) {
       wait_vmcnt<0>();
-      __syncthreads();
+      lds_barrier();
       if (j + 1 < ntk) {
-        lds_t* nk = smem + ((j + 1) & 1) * 2 * C::TILE;
-        issue(krs, j + 1, nk);
-        issue(vrs, j + 1, nk + C::TILE);
+        issue(krs, j + 1, kbuf((j + 1) & 1));
+        issue(vrs, j + 1, vbuf((j + 1) & 1));
       }
     } else {
       wait_vmcnt<C::NINSTR>();  // K_j has landed; V_j may still be in flight
-      __syncthreads();
+      lds_barrier();
     }
   };
 
   // Full S^T (keys x queries) of tile j for this wave's query block, masked.
   auto scores = [&](int j, f32x16_t (&sacc)[QB]) {
-    const lds_t* kt = smem + (NBUF == 2 ? (j & 1) : 0) * 2 * C::TILE;
+    const lds_t* kt = kbuf(NBUF == 2 ? (j & 1) : 0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) sacc[qb] = (f32x16_t){};
+    // All K operands of the tile are read before the products so the LDS latency overlaps.
+    u32x4_t ka[2 * NDB];
 #pragma unroll
     for (int kb = 0; kb < 2 * NDB; ++kb) {
       const int chunk = (cg * C::DW >> 3) + 2 * kb + hh;
-      const u32x4_t a = lds_read_b128(kt, krow * C::RS + ((chunk ^ kswz) << 4));
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[qb] = Elt<T>::mma(a, qreg[qb][kb], sacc[qb]);
+      ka[kb] = lds_read_b128(kt, krow * C::RS + ((chunk ^ kswz) << 4));
     }
+#pragma unroll
+    for (int kb = 0; kb < 2 * NDB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb] = Elt<T>::mma(ka[kb], qreg[qb][kb], sacc[qb]);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
         lds_write_f4(xbuf, (((w * QB + qb) * 4 + r4) * 64 + lane) * 16,
                      (f32x4_t){sacc[qb][4 * r4], sacc[qb][4 * r4 + 1], sacc[qb][4 * r4 + 2], sacc[qb][4 * r4 + 3]});
-    __syncthreads();
+    lds_barrier();
     if constexpr (NBUF == 1) {
-      if (j + 1 < ntk) issue(krs, j + 1, smem);
+      if (j + 1 < ntk) issue(krs, j + 1, kbuf(0));
     }
     // Add the partial sums of the row group's waves in a fixed commutative pattern, so that
     // every wave of the row group ends with bit-identical scores.
@@ -244,9 +250,11 @@ __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
   auto pv = [&](int j, const uint32_t (&pb)[QB][2][4]) {
     if constexpr (NBUF == 1) {
       if (j + 1 < ntk) wait_vmcnt<C::NINSTR>(); else wait_vmcnt<0>();  // V_j has landed
-      __syncthreads();
+      lds_barrier();
     }
-    const lds_t* vt = smem + (NBUF == 2 ? (j & 1) : 0) * 2 * C::TILE + C::TILE;
+    const lds_t* vt = vbuf(NBUF == 2 ? (j & 1) : 0);
+    // All V^T operands of the tile are read before the products.
+    u32x4_t va[NDB][2];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int d = cg * C::DW + 32 * db + 16 * (g16 & 1) + 4 * (r16 & 3);
@@ -258,24 +266,30 @@ __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
         const int k1 = k0 + 4;
         const s16x4_t lo = lds_read_tr16(vt, k0 * C::RS + ((chunk ^ swz(k0)) << 4) + within);
         const s16x4_t hi = lds_read_tr16(vt, k1 * C::RS + ((chunk ^ swz(k1)) << 4) + within);
-        const u32x4_t a = join_tr(lo, hi);
+        va[db][kb2] = join_tr(lo, hi);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const u32x4_t bop = {pb[qb][kb2][0], pb[qb][kb2][1], pb[qb][kb2][2], pb[qb][kb2][3]};
-          oacc[qb][db] = Elt<T>::mma(a, bop, oacc[qb][db]);
+          oacc[qb][db] = Elt<T>::mma(va[db][kb2], bop, oacc[qb][db]);
         }
-      }
-    }
     if constexpr (NBUF == 1) {
-      __syncthreads();
-      if (j + 1 < ntk) issue(vrs, j + 1, smem + C::TILE);
+      lds_barrier();
+      if (j + 1 < ntk) issue(vrs, j + 1, vbuf(0));
     }
   };
 
   if (ntk > 0) {
-    issue(krs, 0, smem);
-    issue(vrs, 0, smem + C::TILE);
+    issue(krs, 0, kbuf(0));
+    issue(vrs, 0, vbuf(0));
   }
+  // The Q operands (and tile 0) are complete before the loop, so the loop never waits for them.
+  wait_all();
 
   // ---- fast loop: the reference max of a row is fixed at its first finite tile max. The loop
   // leaves (per wave) as soon as a tile max exceeds the reference by more than 2^8, so O never
@@ -301,29 +315,25 @@ __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
 
   // ---- rescaling loop (entered only after a large growth of a row max): standard online
   // softmax with a lazily updated reference. Tile j's scores are already in sacc.
-  if (j < ntk) {
-    bool fresh = false;
-    for (; j < ntk; ++j) {
-      if (fresh) {
-        top(j);
-        scores(j, sacc);
-      }
-      fresh = true;
-      float mt[QB];
-      tile_max(sacc, mt);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const bool nd = mt[qb] > mref[qb] + 8.0f;
-        const float alpha = nd ? fast_exp2(mref[qb] - mt[qb]) : 1.0f;
-        if (nd) mref[qb] = mt[qb];
-        lsum[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
-      }
-      uint32_t pb[QB][2][4];
-      make_p(sacc, pb);
-      pv(j, pb);
+  for (bool fresh = false; j < ntk; ++j, fresh = true) {
+    if (fresh) {
+      top(j);
+      scores(j, sacc);
     }
+    float mt[QB];
+    tile_max(sacc, mt);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const bool nd = mt[qb] > mref[qb] + 8.0f;
+      const float alpha = nd ? fast_exp2(mref[qb] - mt[qb]) : 1.0f;
+      if (nd) mref[qb] = mt[qb];
+      lsum[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
+    }
+    uint32_t pb[QB][2][4];
+    make_p(sacc, pb);
+    pv(j, pb);
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln(2) * (mref + log2 l); empty rows give 0 and -inf
