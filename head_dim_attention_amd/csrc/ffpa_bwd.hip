@@ -78,26 +78,26 @@ __global__ void __launch_bounds__(256) ffpa_bwd_preprocess_kernel(AttnParams p, 
 // ------------------------------------------------------------------------------------------------
 enum BwdMode { kDQ = 0, kDK = 1, kDV = 2 };
 
-template <int NC, int NDB, int NBUF, int NX>
+template <int NC, int NDB, int NBUF, int NX, int NW>
 struct BwdCfg {
-  static constexpr int NR = 4 / NC;
+  static constexpr int NR = NW / NC;
   static constexpr int DW = NDB * 32;
   static constexpr int DPAD = NC * DW;
   static constexpr int RS = DPAD <= 512 ? 1024 : 2048;
   static constexpr int BOWN = NR * 32;                 // stationary rows per workgroup
   static constexpr int TILE = 32 * RS;
-  static constexpr int XBYTES = 4 * NX * 16 * 64 * 4;  // NX partial C blocks per wave
+  static constexpr int XBYTES = NW * NX * 16 * 64 * 4;  // NX partial C blocks per wave
   static constexpr int LDS = NBUF * 2 * TILE + XBYTES;
-  static constexpr int NINSTR = TILE / 1024 / 4;
+  static constexpr int NINSTR = TILE / 1024 / NW;
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <class T, int MODE, int NC, int NDB, int NBUF>
-__global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
+template <class T, int MODE, int NC, int NDB, int NBUF, int NW>
+__global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p) {
   constexpr bool OWN_Q = MODE == kDQ;   // stationary rows are queries (dQ) or keys (dK, dV)
   constexpr bool HAS_DP = MODE != kDV;  // dK and dQ need dP = dO V^T
   constexpr int NX = HAS_DP ? 2 : 1;
-  using C = BwdCfg<NC, NDB, NBUF, NX>;
+  using C = BwdCfg<NC, NDB, NBUF, NX, NW>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
   lds_t* smem = (lds_t*)smem_raw;
 
@@ -184,7 +184,7 @@ __global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
   int voff[C::NINSTR];
 #pragma unroll
   for (int ii = 0; ii < C::NINSTR; ++ii) {
-    const int i = w + 4 * ii;
+    const int i = w + NW * ii;
     const int R = i / IPR;
     const int pc = (i % IPR) * 64 + lane;
     voff[ii] = min(pc ^ swz(R), dch - 1) << 4;
@@ -200,7 +200,7 @@ __global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
     lds_t* t1 = smem + buf * 2 * C::TILE;
 #pragma unroll
     for (int ii = 0; ii < C::NINSTR; ++ii) {
-      const int i = w + 4 * ii;
+      const int i = w + NW * ii;
       const int row = min(row0 + i / IPR, str_len - 1);
       dma16_buf(rs1, voff[ii], row * row_bytes, t1 + i * 1024);
       dma16_buf(rs2, voff[ii], row * row_bytes, t1 + C::TILE + i * 1024);
@@ -211,7 +211,39 @@ __global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
   const int kswz = swz(krow);
   const int g16 = lane >> 4;
   const int r16 = lane & 15;
+  const int cbase = cg * C::DW >> 3;  // first 16-byte chunk of this wave's head-dim columns
   lds_t* xbuf = smem + NBUF * 2 * C::TILE;
+
+  // LDS byte offsets of this lane's operands within a tile. When the wave's first chunk is a
+  // multiple of 16, the swizzle (which permutes the low 4 bits of the chunk index) leaves the
+  // higher bits alone, so every offset is one of 8 per-lane bases plus a compile-time constant.
+  constexpr bool kAligned = (C::DW % 128) == 0;
+  // Streamed rows as A operand of the partial products: tile row row_perm(m), chunk cbase + 2 kb + h.
+  int alds[8];
+#pragma unroll
+  for (int lo = 0; lo < 8; ++lo) alds[lo] = krow * C::RS + ((cbase + ((2 * lo + hh) ^ kswz)) << 4);
+  auto a_off = [&](int kb) {
+    if constexpr (kAligned) return alds[kb & 7] + ((kb >> 3) << 8);
+    return krow * C::RS + (((cbase + 2 * kb + hh) ^ kswz) << 4);
+  };
+  // Transposed reads of the streamed tile (A operand of the accumulating product): tile row
+  // k = 16 kb2 + 8 h + 4 half + r16/4, head-dim column cg DW + 32 db + 16 (g16 % 2) + 4 (r16 % 4).
+  const int tclo = 2 * (g16 & 1) + ((r16 & 3) >> 1);
+  const int twithin = ((4 * (r16 & 3)) & 7) << 1;
+  int tlds[2][4];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int k = 8 * hh + 4 * half + (r16 >> 2);
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4)
+      tlds[half][d4] = k * C::RS + ((cbase + ((4 * d4 + tclo) ^ swz(k))) << 4) + twithin;
+  }
+  auto t_off = [&](int db, int kb2, int half) {
+    if constexpr (kAligned) return tlds[half][db & 3] + ((db >> 2) << 8) + kb2 * 16 * C::RS;
+    const int k = 16 * kb2 + 8 * hh + 4 * half + (r16 >> 2);
+    const int chunk = cbase + 4 * db + tclo;
+    return k * C::RS + ((chunk ^ swz(k)) << 4) + twithin;
+  };
 
   // dK/dV: LSE (log2 units; +inf for an empty row makes P = 0) and Delta of streamed query row
   // row0 + l % 32, loaded one step ahead and after that step's tile copy, so the wait that makes
@@ -253,10 +285,9 @@ __global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
     f32x16_t sacc = (f32x16_t){}, dpacc = (f32x16_t){};
 #pragma unroll
     for (int kb = 0; kb < 2 * NDB; ++kb) {
-      const int chunk = (cg * C::DW >> 3) + 2 * kb + hh;
-      const int a_off = krow * C::RS + ((chunk ^ kswz) << 4);
-      sacc = Elt<T>::mma(lds_read_b128(t1, a_off), r1[kb], sacc);
-      if constexpr (HAS_DP) dpacc = Elt<T>::mma(lds_read_b128(t2, a_off), r2[kb], dpacc);
+      const int ao = a_off(kb);
+      sacc = Elt<T>::mma(lds_read_b128(t1, ao), r1[kb], sacc);
+      if constexpr (HAS_DP) dpacc = Elt<T>::mma(lds_read_b128(t2, ao), r2[kb], dpacc);
     }
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -330,15 +361,10 @@ __global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
     const lds_t* tt = MODE == kDV ? t2 : t1;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int d = cg * C::DW + 32 * db + 16 * (g16 & 1) + 4 * (r16 & 3);
-      const int chunk = d >> 3;
-      const int within = (d & 7) << 1;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const int k0 = 16 * kb2 + 8 * hh + (r16 >> 2);
-        const int k1 = k0 + 4;
-        const s16x4_t lo = lds_read_tr16(tt, k0 * C::RS + ((chunk ^ swz(k0)) << 4) + within);
-        const s16x4_t hi = lds_read_tr16(tt, k1 * C::RS + ((chunk ^ swz(k1)) << 4) + within);
+        const s16x4_t lo = lds_read_tr16(tt, t_off(db, kb2, 0));
+        const s16x4_t hi = lds_read_tr16(tt, t_off(db, kb2, 1));
         const u32x4_t bv = {bop[kb2][0], bop[kb2][1], bop[kb2][2], bop[kb2][3]};
         acc[db] = Elt<T>::mma(join_tr(lo, hi), bv, acc[db]);
       }
@@ -376,14 +402,17 @@ __global__ void __launch_bounds__(256, 1) ffpa_bwd_kernel(AttnParams p) {
 template <class T, int MODE, int NC, int NDB>
 static hipError_t launch_bwd_cfg(AttnParams p, hipStream_t st) {
   constexpr int NX = MODE != kDV ? 2 : 1;
-  constexpr int NBUF = (2 * 2 * BwdCfg<NC, NDB, 1, NX>::TILE + BwdCfg<NC, NDB, 1, NX>::XBYTES) <= 160 * 1024 ? 2 : 1;
-  using C = BwdCfg<NC, NDB, NBUF, NX>;
+  // Two waves per SIMD where the per-wave state fits 256 registers (dV for D <= 512), else one.
+  constexpr int NW = (MODE == kDV && NC == 2) ? 8 : 4;
+  using C1 = BwdCfg<NC, NDB, 1, NX, NW>;
+  constexpr int NBUF = (2 * 2 * C1::TILE + C1::XBYTES) <= 160 * 1024 ? 2 : 1;
+  using C = BwdCfg<NC, NDB, NBUF, NX, NW>;
   const bool own_q = MODE == kDQ;
   p.ntiles = ((own_q ? p.nq : p.nkv) + C::BOWN - 1) / C::BOWN;
   p.total = p.batch * (own_q ? p.hq : p.hkv) * p.ntiles;
   if (p.total == 0) return hipSuccess;
   const int grid = (p.total + 7) & ~7;
-  hipLaunchKernelGGL((ffpa_bwd_kernel<T, MODE, NC, NDB, NBUF>), dim3(grid), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((ffpa_bwd_kernel<T, MODE, NC, NDB, NBUF, NW>), dim3(grid), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
 

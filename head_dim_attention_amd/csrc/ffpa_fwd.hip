@@ -7,9 +7,10 @@
 // ("CuTe-DSL Backend", "Varlen (packed THD) API").
 //
 // How it maps to gfx950:
-//  * One workgroup (4 wave64s) owns BQ = NR*QB*32 queries of one head. Each wave keeps QB*32
-//    queries x DW head-dim columns of Q in registers (B operand of S^T = K Q^T) and the matching
-//    O^T block as fp32 MFMA accumulators ("O accumulator held per D chunk").
+//  * One workgroup of NW wave64s (8, two per SIMD, for D <= 512; else 4) owns BQ = NR*QB*32
+//    queries of one head, so each K/V tile copied into LDS serves 128 (or 32) queries. Each wave
+//    keeps QB*32 queries x DW head-dim columns of Q in registers (B operand of S^T = K Q^T) and
+//    the matching O^T block as fp32 MFMA accumulators ("O accumulator held per D chunk").
 //  * K and V stream through LDS in 32-key tiles, copied straight from global memory with 16-byte
 //    global_load_lds (no VGPR staging), double-buffered when a tile pair fits twice in the 160 KB.
 //  * Scores are formed transposed (keys x queries): each lane owns one query column, so the row
@@ -26,23 +27,23 @@
 
 namespace ffpa {
 
-template <int NC, int NDB, int QB, int NBUF>
+template <int NC, int NDB, int QB, int NBUF, int NW>
 struct FwdCfg {
-  static constexpr int NR = 4 / NC;
+  static constexpr int NR = NW / NC;                     // query row groups
   static constexpr int DW = NDB * 32;                    // head-dim columns per wave
   static constexpr int DPAD = NC * DW;                   // padded head dim
   static constexpr int RS = DPAD <= 512 ? 1024 : 2048;   // LDS row stride (bytes), power of two
   static constexpr int BQ = NR * QB * 32;                // queries per workgroup
   static constexpr int TILE = 32 * RS;                   // one 32-row K or V tile in LDS
-  static constexpr int XBYTES = 4 * QB * 16 * 64 * 4;    // partial scores of the 4 waves
+  static constexpr int XBYTES = NW * QB * 16 * 64 * 4;   // partial scores of all waves
   static constexpr int LDS = NBUF * 2 * TILE + XBYTES;
-  static constexpr int NINSTR = TILE / 1024 / 4;         // 1 KB DMA instructions per wave per tile
+  static constexpr int NINSTR = TILE / 1024 / NW;        // 1 KB DMA instructions per wave per tile
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <class T, int NC, int NDB, int QB, int NBUF>
-__global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
-  using C = FwdCfg<NC, NDB, QB, NBUF>;
+template <class T, int NC, int NDB, int QB, int NBUF, int NW>
+__global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p) {
+  using C = FwdCfg<NC, NDB, QB, NBUF, NW>;
   __shared__ __attribute__((aligned(1024))) char k0_raw[C::TILE], v0_raw[C::TILE];
   __shared__ __attribute__((aligned(1024))) char k1_raw[NBUF == 2 ? C::TILE : 16], v1_raw[NBUF == 2 ? C::TILE : 16];
   __shared__ __attribute__((aligned(1024))) char x_raw[C::XBYTES];
@@ -122,7 +123,7 @@ __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
   int voff[C::NINSTR];
 #pragma unroll
   for (int ii = 0; ii < C::NINSTR; ++ii) {
-    const int i = w + 4 * ii;
+    const int i = w + NW * ii;
     const int R = i / IPR;
     const int pc = (i % IPR) * 64 + lane;
     voff[ii] = min(pc ^ swz(R), dch - 1) << 4;
@@ -130,7 +131,7 @@ __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
   auto issue = [&](i32x4_t rs, int j, lds_t* dst) {
 #pragma unroll
     for (int ii = 0; ii < C::NINSTR; ++ii) {
-      const int i = w + 4 * ii;
+      const int i = w + NW * ii;
       const int R = i / IPR;
       const int row = min(j * 32 + R, sv.lk - 1);
       dma16_buf(rs, voff[ii], row * row_bytes, dst + i * 1024);
@@ -141,6 +142,39 @@ __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
   const int kswz = swz(krow);
   const int g16 = lane >> 4;
   const int r16 = lane & 15;
+  const int cbase = cg * C::DW >> 3;  // first 16-byte chunk of this wave's head-dim columns
+
+  // LDS byte offsets of this lane's operands within a tile. When the wave's first chunk is a
+  // multiple of 16, the swizzle (which permutes the low 4 bits of the chunk index) leaves the
+  // higher bits alone, so every offset is one of 8 per-lane bases plus a compile-time constant.
+  constexpr bool kAligned = (C::DW % 128) == 0;
+  // K rows (A operand of S^T): tile row row_perm(m), chunk cbase + 2 kb + h.
+  int klds[8];
+#pragma unroll
+  for (int lo = 0; lo < 8; ++lo) klds[lo] = krow * C::RS + ((cbase + ((2 * lo + hh) ^ kswz)) << 4);
+  auto k_off = [&](int kb) {
+    if constexpr (kAligned) return klds[kb & 7] + ((kb >> 3) << 8);
+    return krow * C::RS + (((cbase + 2 * kb + hh) ^ kswz) << 4);
+  };
+  // V^T (A operand of O^T += V^T P^T) via transposed reads: key row
+  // k = 16 kb2 + 8 h + 4 half + r16/4, head-dim column d = cg DW + 32 db + 16 (g16 % 2) + 4 (r16 % 4).
+  // swz(k) does not depend on kb2 or db, and 4 db touches chunk bits 2-3 only through (db % 4).
+  const int vclo = 2 * (g16 & 1) + ((r16 & 3) >> 1);
+  const int vwithin = ((4 * (r16 & 3)) & 7) << 1;
+  int vlds[2][4];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int k = 8 * hh + 4 * half + (r16 >> 2);
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4)
+      vlds[half][d4] = k * C::RS + ((cbase + ((4 * d4 + vclo) ^ swz(k))) << 4) + vwithin;
+  }
+  auto vt_off = [&](int db, int kb2, int half) {
+    if constexpr (kAligned) return vlds[half][db & 3] + ((db >> 2) << 8) + kb2 * 16 * C::RS;
+    const int k = 16 * kb2 + 8 * hh + 4 * half + (r16 >> 2);
+    const int chunk = cbase + 4 * db + vclo;
+    return k * C::RS + ((chunk ^ swz(k)) << 4) + vwithin;
+  };
 
   // ---- pipeline pieces (each runs the same barriers in every wave) --------------------------
   auto top = [&](int j) {
@@ -162,17 +196,12 @@ __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
     const lds_t* kt = kbuf(NBUF == 2 ? (j & 1) : 0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) sacc[qb] = (f32x16_t){};
-    // All K operands of the tile are read before the products so the LDS latency overlaps.
-    u32x4_t ka[2 * NDB];
 #pragma unroll
     for (int kb = 0; kb < 2 * NDB; ++kb) {
-      const int chunk = (cg * C::DW >> 3) + 2 * kb + hh;
-      ka[kb] = lds_read_b128(kt, krow * C::RS + ((chunk ^ kswz) << 4));
+      const u32x4_t a = lds_read_b128(kt, k_off(kb));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb] = Elt<T>::mma(a, qreg[qb][kb], sacc[qb]);
     }
-#pragma unroll
-    for (int kb = 0; kb < 2 * NDB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[qb] = Elt<T>::mma(ka[kb], qreg[qb][kb], sacc[qb]);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -253,31 +282,20 @@ __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
       lds_barrier();
     }
     const lds_t* vt = vbuf(NBUF == 2 ? (j & 1) : 0);
-    // All V^T operands of the tile are read before the products.
-    u32x4_t va[NDB][2];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int d = cg * C::DW + 32 * db + 16 * (g16 & 1) + 4 * (r16 & 3);
-      const int chunk = d >> 3;
-      const int within = (d & 7) << 1;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const int k0 = 16 * kb2 + 8 * hh + (r16 >> 2);
-        const int k1 = k0 + 4;
-        const s16x4_t lo = lds_read_tr16(vt, k0 * C::RS + ((chunk ^ swz(k0)) << 4) + within);
-        const s16x4_t hi = lds_read_tr16(vt, k1 * C::RS + ((chunk ^ swz(k1)) << 4) + within);
-        va[db][kb2] = join_tr(lo, hi);
-      }
-    }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+        const s16x4_t lo = lds_read_tr16(vt, vt_off(db, kb2, 0));
+        const s16x4_t hi = lds_read_tr16(vt, vt_off(db, kb2, 1));
+        const u32x4_t a = join_tr(lo, hi);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const u32x4_t bop = {pb[qb][kb2][0], pb[qb][kb2][1], pb[qb][kb2][2], pb[qb][kb2][3]};
-          oacc[qb][db] = Elt<T>::mma(va[db][kb2], bop, oacc[qb][db]);
+          oacc[qb][db] = Elt<T>::mma(a, bop, oacc[qb][db]);
         }
+      }
+    }
     if constexpr (NBUF == 1) {
       lds_barrier();
       if (j + 1 < ntk) issue(vrs, j + 1, vbuf(0));
@@ -366,13 +384,16 @@ __global__ void __launch_bounds__(256, 1) ffpa_fwd_kernel(AttnParams p) {
 template <class T, int NC, int NDB>
 static hipError_t launch_fwd_cfg(AttnParams p, hipStream_t st) {
   constexpr int QB = 1;
-  constexpr int NBUF = (2 * 2 * FwdCfg<NC, NDB, QB, 1>::TILE + FwdCfg<NC, NDB, QB, 1>::XBYTES) <= 160 * 1024 ? 2 : 1;
-  using C = FwdCfg<NC, NDB, QB, NBUF>;
+  // Two waves per SIMD where the per-wave state fits 256 registers (D <= 512), else one.
+  constexpr int NW = NC == 2 ? 8 : 4;
+  using C1 = FwdCfg<NC, NDB, QB, 1, NW>;
+  constexpr int NBUF = (2 * 2 * C1::TILE + C1::XBYTES) <= 160 * 1024 ? 2 : 1;
+  using C = FwdCfg<NC, NDB, QB, NBUF, NW>;
   p.ntiles = (p.nq + C::BQ - 1) / C::BQ;
   p.total = p.batch * p.hq * p.ntiles;
   if (p.total == 0) return hipSuccess;
   const int grid = (p.total + 7) & ~7;
-  hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF>), dim3(grid), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF, NW>), dim3(grid), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
 
