@@ -15,15 +15,21 @@
 // ("CuTe-DSL Backend", "Hard constraints": zero-stride broadcast). Rows whose LSE is -inf (no legal
 // key) get P = 0 and so contribute nothing and receive zero gradient.
 //
-// The dV/dK/dQ kernels share one skeleton with the forward kernel: 4 wave64s as NR x NC, the
+// The dV/dK/dQ kernels share one skeleton with the forward kernel: NW wave64s as NR x NC, the
 // stationary rows' operands in registers as MFMA B operands, the other side streamed through LDS
 // in 32-row tiles (buffer_load...lds), partial head-dim products combined through LDS, scores in a
 // C-block layout whose registers feed the accumulating product directly as B operands, and the
 // accumulating product's A operand read transposed from the streamed tile (ds_read_b64_tr_b16).
+// For D <= 512, dV runs 8 waves (NC = 2) and dK/dQ run the 8-wave reduce-scatter variant below
+// (NC = 4), both at two waves per SIMD; larger head dims use 4 waves (NC = 4), one per SIMD.
 #include "ffpa_device.h"
 #include "ffpa_params.h"
 
 namespace ffpa {
+// MFMAs whose LDS operands are requested ahead of the one issuing (see pin_lds_mfma_pipeline).
+#ifndef BWD_AHEAD
+#define BWD_AHEAD 2
+#endif
 
 // ------------------------------------------------------------------------------------------------
 // Stage 1: Delta = rowsum(dO * O) in fp32 from the stored (rounded) O.
@@ -192,12 +198,11 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
   // Tile 1 feeds the scores (K for dQ, Q for dK/dV); tile 2 feeds dP (V for dQ, dO for dK) or the
   // dV product (dO).
   auto issue = [&](int st, int buf) {
-    const int head = step_head(st);
-    const int row0 = step_row0(st);
-    const long long base = str_base(head);
+    const long long base = str_base(step_head(st));
     const i32x4_t rs1 = make_rsrc((const uint16_t*)(OWN_Q ? p.k : p.q) + base, span);
     const i32x4_t rs2 = make_rsrc((const uint16_t*)(OWN_Q ? p.v : p.dout) + base, span);
     lds_t* t1 = smem + buf * 2 * C::TILE;
+    const int row0 = step_row0(st);
 #pragma unroll
     for (int ii = 0; ii < C::NINSTR; ++ii) {
       const int i = w + NW * ii;
@@ -214,35 +219,33 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
   const int cbase = cg * C::DW >> 3;  // first 16-byte chunk of this wave's head-dim columns
   lds_t* xbuf = smem + NBUF * 2 * C::TILE;
 
-  // LDS byte offsets of this lane's operands within a tile. When the wave's first chunk is a
-  // multiple of 16, the swizzle (which permutes the low 4 bits of the chunk index) leaves the
-  // higher bits alone, so every offset is one of 8 per-lane bases plus a compile-time constant.
+  // LDS byte addresses of this lane's operands in a tile at LDS address `tile`. When the wave's
+  // first chunk is a multiple of 16, the swizzle (an XOR on the low 4 bits of the 16-byte chunk
+  // index) touches only address bits 4-7, which are zero in the row, column-group and tile bases:
+  // every operand address is then one per-lane base XOR a compile-time constant, plus a constant.
   constexpr bool kAligned = (C::DW % 128) == 0;
   // Streamed rows as A operand of the partial products: tile row row_perm(m), chunk cbase + 2 kb + h.
-  int alds[8];
-#pragma unroll
-  for (int lo = 0; lo < 8; ++lo) alds[lo] = krow * C::RS + ((cbase + ((2 * lo + hh) ^ kswz)) << 4);
-  auto a_off = [&](int kb) {
-    if constexpr (kAligned) return alds[kb & 7] + ((kb >> 3) << 8);
-    return krow * C::RS + (((cbase + 2 * kb + hh) ^ kswz) << 4);
+  const uint32_t alane = krow * C::RS + (cbase << 4) + ((hh ^ kswz) << 4);
+  auto a_addr = [&](uint32_t tile, int kb) -> uint32_t {
+    if constexpr (kAligned) return ((tile + alane) ^ ((kb & 7) << 5)) + ((kb >> 3) << 8);
+    return tile + krow * C::RS + (((cbase + 2 * kb + hh) ^ kswz) << 4);
   };
   // Transposed reads of the streamed tile (A operand of the accumulating product): tile row
-  // k = 16 kb2 + 8 h + 4 half + r16/4, head-dim column cg DW + 32 db + 16 (g16 % 2) + 4 (r16 % 4).
+  // k = 16 kb2 + 8 h + 4 half + r16/4, head-dim column cg DW + 32 db + 16 (g16 % 2) + 4 (r16 % 4),
+  // i.e. chunk cbase + 4 db + tclo. swz(k) does not depend on kb2.
   const int tclo = 2 * (g16 & 1) + ((r16 & 3) >> 1);
   const int twithin = ((4 * (r16 & 3)) & 7) << 1;
-  int tlds[2][4];
+  uint32_t tlane[2];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int k = 8 * hh + 4 * half + (r16 >> 2);
-#pragma unroll
-    for (int d4 = 0; d4 < 4; ++d4)
-      tlds[half][d4] = k * C::RS + ((cbase + ((4 * d4 + tclo) ^ swz(k))) << 4) + twithin;
+    tlane[half] = k * C::RS + (cbase << 4) + ((tclo ^ swz(k)) << 4) + twithin;
   }
-  auto t_off = [&](int db, int kb2, int half) {
-    if constexpr (kAligned) return tlds[half][db & 3] + ((db >> 2) << 8) + kb2 * 16 * C::RS;
+  auto t_addr = [&](uint32_t tile, int db, int kb2, int half) -> uint32_t {
+    if constexpr (kAligned)
+      return ((tile + tlane[half]) ^ ((db & 3) << 6)) + ((db >> 2) << 8) + kb2 * 16 * C::RS;
     const int k = 16 * kb2 + 8 * hh + 4 * half + (r16 >> 2);
-    const int chunk = cbase + 4 * db + tclo;
-    return k * C::RS + ((chunk ^ swz(k)) << 4) + twithin;
+    return tile + k * C::RS + (((cbase + 4 * db + tclo) ^ swz(k)) << 4) + twithin;
   };
 
   // dK/dV: LSE (log2 units; +inf for an empty row makes P = 0) and Delta of streamed query row
@@ -271,11 +274,10 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
     lds_barrier();
     const float lse2_cur = lse_next == -INFINITY ? INFINITY : lse_next * kLog2e;
     const float dlt_cur = dlt_next;
-    if constexpr (NBUF == 2) {
-      if (st + 1 < nsteps) {
-        issue(st + 1, buf ^ 1);
-        load_row_stats(st + 1);
-      }
+    // The next step's tiles go into the buffer the barrier above released.
+    if (NBUF == 2 && st + 1 < nsteps) {
+      issue(st + 1, buf ^ 1);
+      load_row_stats(st + 1);
     }
     const lds_t* t1 = smem + buf * 2 * C::TILE;
     const lds_t* t2 = t1 + C::TILE;
@@ -283,12 +285,13 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
 
     // ---- partial S (and dP) over this wave's head-dim columns: C[streamed row][own row]
     f32x16_t sacc = (f32x16_t){}, dpacc = (f32x16_t){};
+    constexpr int KSTEPS = 2 * NDB;
 #pragma unroll
-    for (int kb = 0; kb < 2 * NDB; ++kb) {
-      const int ao = a_off(kb);
-      sacc = Elt<T>::mma(lds_read_b128(t1, ao), r1[kb], sacc);
-      if constexpr (HAS_DP) dpacc = Elt<T>::mma(lds_read_b128(t2, ao), r2[kb], dpacc);
+    for (int kb = 0; kb < KSTEPS; ++kb) {
+      sacc = Elt<T>::mma(lds_read_b128_at(a_addr(lds_addr(t1), kb)), r1[kb], sacc);
+      if constexpr (HAS_DP) dpacc = Elt<T>::mma(lds_read_b128_at(a_addr(lds_addr(t2), kb)), r2[kb], dpacc);
     }
+    pin_lds_mfma_pipeline<KSTEPS * (HAS_DP ? 2 : 1), BWD_AHEAD, 1>();
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       lds_write_f4(xbuf, (((w * NX + 0) * 4 + r4) * 64 + lane) * 16,
@@ -363,12 +366,13 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const s16x4_t lo = lds_read_tr16(tt, t_off(db, kb2, 0));
-        const s16x4_t hi = lds_read_tr16(tt, t_off(db, kb2, 1));
+        const s16x4_t lo = lds_read_tr16_at(t_addr(lds_addr(tt), db, kb2, 0));
+        const s16x4_t hi = lds_read_tr16_at(t_addr(lds_addr(tt), db, kb2, 1));
         const u32x4_t bv = {bop[kb2][0], bop[kb2][1], bop[kb2][2], bop[kb2][3]};
         acc[db] = Elt<T>::mma(join_tr(lo, hi), bv, acc[db]);
       }
     }
+    pin_lds_mfma_pipeline<2 * NDB, BWD_AHEAD, 2>();
 
     if constexpr (NBUF == 1) {
       lds_barrier();
@@ -399,6 +403,328 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// dK and dQ for D <= 512 with two waves per SIMD.
+//
+// Eight waves form NR = 2 row groups of NC = 4; a wave holds 32 stationary rows x D/4 head-dim
+// columns of both stationary operands and of the fp32 accumulator, which fits 256 registers.
+// The four partial score blocks of a row group are combined by a reduce-scatter: wave cg
+// finishes only the 8 streamed rows of register quarter cg (registers 4cg..4cg+3 of the C block),
+// computes dS for them, and the bf16 dS quarters are then all-gathered, so each wave does a
+// quarter of the softmax-gradient arithmetic and exchanges half the partial-sum bytes of a full
+// all-reduce. The tile read only by the partial products (dO for dK, V for dQ) has one buffer
+// and is refilled as soon as every wave has passed the exchange barrier; the tile also read by
+// the accumulating product is double-buffered. dK's per-query LSE and Delta come with the query
+// tile into LDS and are read by broadcast.
+// ------------------------------------------------------------------------------------------------
+template <int NDB>
+struct RsCfg {
+  static constexpr int NC = 4, NW = 8, NR = 2;
+  static constexpr int DW = NDB * 32;
+  static constexpr int RS = 1024;                // LDS row stride (bytes), padded head dim <= 512
+  static constexpr int BOWN = NR * 32;           // stationary rows per workgroup
+  static constexpr int TILE = 32 * RS;
+  static constexpr int PIECE = 64 * 16;          // one f32x4 per lane
+  static constexpr int T2_OFF = 2 * TILE;        // single-buffered tile
+  static constexpr int X_OFF = 3 * TILE;         // [wave][3 partner quarters][S, dP] pieces
+  static constexpr int G_OFF = X_OFF + NW * 3 * 2 * PIECE;  // [wave] packed dS quarter, 8 B/lane
+  static constexpr int ST_OFF = G_OFF + NW * 64 * 8;        // [buffer][LSE, Delta] x 64 floats
+  static constexpr int LDS = ST_OFF + 2 * 2 * 256;
+  static constexpr int NINSTR = TILE / 1024 / NW;
+  static_assert(4 * DW <= 512 && LDS <= 160 * 1024, "LDS budget");
+};
+
+template <class T, int MODE, int NDB>
+__global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
+  static_assert(MODE == kDQ || MODE == kDK, "dK and dQ only");
+  constexpr bool OWN_Q = MODE == kDQ;
+  using C = RsCfg<NDB>;
+  constexpr int NC = C::NC, NW = C::NW;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
+  lds_t* smem = (lds_t*)smem_raw;
+
+  const int L = blockIdx.x;
+  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  if (item >= p.total) return;
+  const int heads = OWN_Q ? p.hq : p.hkv;
+  int t = item % p.ntiles;
+  const int hs = item / p.ntiles;
+  const int hd = hs % heads;
+  const int s = hs / heads;
+  if (OWN_Q && p.causal) t = p.ntiles - 1 - t;  // heaviest causal tiles first
+
+  const SeqView sv = seq_view(p, s);
+  const int own_len = OWN_Q ? sv.lq : sv.lk;
+  const int o0 = t * C::BOWN;
+  if (o0 >= own_len) return;
+
+  const int w = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int rg = w / NC;
+  const int cg = w % NC;
+  const int ow0 = o0 + rg * 32;
+  const int off = sv.lk - sv.lq;
+
+  // ---- stationary operands: lane (h, n) holds own row n, dims 16 kb + 8 h + 0..7
+  const int own_row = OWN_Q ? p.q_row : p.k_row;
+  const long long own_base = OWN_Q ? sv.q_off + (long long)hd * p.q_head : sv.k_off + (long long)hd * p.k_head;
+  const uint16_t* r1src = (const uint16_t*)(OWN_Q ? p.q : p.k) + own_base;
+  const uint16_t* r2src = (const uint16_t*)(OWN_Q ? p.dout : p.v) + own_base;
+  u32x4_t r1[2 * NDB], r2[2 * NDB];
+  {
+    const long long oi = min(ow0 + l32, own_len - 1);
+#pragma unroll
+    for (int kb = 0; kb < 2 * NDB; ++kb) {
+      const int dim = cg * C::DW + kb * 16 + hh * 8;
+      const bool in = dim < p.d;
+      r1[kb] = in ? *(const u32x4_t*)(r1src + oi * own_row + dim) : (u32x4_t){0u, 0u, 0u, 0u};
+      r2[kb] = in ? *(const u32x4_t*)(r2src + oi * own_row + dim) : (u32x4_t){0u, 0u, 0u, 0u};
+    }
+  }
+  // dQ: the query's LSE (log2 units; +inf for an empty row makes P = 0) and Delta are per lane.
+  float lse2_own = 0.f, dlt_own = 0.f;
+  if constexpr (OWN_Q) {
+    const long long qi = sv.lse_off + (long long)hd * p.lse_head + min(ow0 + l32, sv.lq - 1);
+    const float l = p.lse_in[qi];
+    lse2_own = l == -INFINITY ? INFINITY : l * kLog2e;
+    dlt_own = p.delta[qi];
+  }
+
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = (f32x16_t){};
+
+  // ---- streamed side
+  const int str_len = OWN_Q ? sv.lk : sv.lq;
+  const int row_bytes = (OWN_Q ? p.k_row : p.q_row) * 2;
+  int nsteps, nqt = 1, qt_first = 0;
+  if constexpr (OWN_Q) {
+    int kend = sv.lk;
+    if (p.causal) kend = min(kend, o0 + C::BOWN + off);
+    nsteps = kend > 0 ? (kend + 31) >> 5 : 0;
+  } else {
+    const int qfirst = p.causal ? max(0, o0 - off) : 0;
+    qt_first = qfirst >> 5;
+    nqt = sv.lq > qfirst ? ((sv.lq + 31) >> 5) - qt_first : 0;
+    nsteps = p.group * nqt;
+  }
+  auto step_head = [&](int st) { return OWN_Q ? hd / p.group : hd * p.group + st / nqt; };
+  auto step_row0 = [&](int st) { return OWN_Q ? st * 32 : (qt_first + st % nqt) * 32; };
+  auto str_base = [&](int head) {
+    return OWN_Q ? sv.k_off + (long long)head * p.k_head : sv.q_off + (long long)head * p.q_head;
+  };
+  const uint32_t span = (uint32_t)min((long long)max(str_len, 1) * row_bytes, (long long)0xFFFFFFF0);
+  const int dch = p.d >> 3;
+  int voff[C::NINSTR];
+#pragma unroll
+  for (int ii = 0; ii < C::NINSTR; ++ii) voff[ii] = min(lane ^ swz(w + NW * ii), dch - 1) << 4;
+
+  // Tile 1 (K for dQ, Q for dK) of step st into buffer buf, with dK's row statistics.
+  auto issue_t1 = [&](int st, int buf) {
+    const int head = step_head(st);
+    const int row0 = step_row0(st);
+    const i32x4_t rs = make_rsrc((const uint16_t*)(OWN_Q ? p.k : p.q) + str_base(head), span);
+    lds_t* dst = smem + buf * C::TILE;
+#pragma unroll
+    for (int ii = 0; ii < C::NINSTR; ++ii) {
+      const int i = w + NW * ii;
+      dma16_buf(rs, voff[ii], min(row0 + i, str_len - 1) * row_bytes, dst + i * 1024);
+    }
+    if constexpr (!OWN_Q) {
+      if (w == 0) {
+        const long long li = sv.lse_off + (long long)head * p.lse_head;
+        const uint32_t bytes = (uint32_t)max(sv.lq, 1) * 4;
+        const int vo = min(row0 + l32, sv.lq - 1) * 4;
+        lds_t* sd = smem + C::ST_OFF + buf * 512;
+        dma4_buf(make_rsrc(p.lse_in + li, bytes), vo, sd);
+        dma4_buf(make_rsrc(p.delta + li, bytes), vo, sd + 256);
+      }
+    }
+  };
+  // Tile 2 (V for dQ, dO for dK) of step st into its single buffer.
+  auto issue_t2 = [&](int st) {
+    const int row0 = step_row0(st);
+    const i32x4_t rs = make_rsrc((const uint16_t*)(OWN_Q ? p.v : p.dout) + str_base(step_head(st)), span);
+    lds_t* dst = smem + C::T2_OFF;
+#pragma unroll
+    for (int ii = 0; ii < C::NINSTR; ++ii) {
+      const int i = w + NW * ii;
+      dma16_buf(rs, voff[ii], min(row0 + i, str_len - 1) * row_bytes, dst + i * 1024);
+    }
+  };
+
+  const int krow = row_perm(l32);
+  const int kswz = swz(krow);
+  const int g16 = lane >> 4;
+  const int r16 = lane & 15;
+  const int cbase = cg * C::DW >> 3;
+  // LDS operand addresses (see the forward kernel): with a 16-chunk-aligned column base every
+  // address is one per-lane base XOR a constant, plus a constant.
+  constexpr bool kAligned = (C::DW % 128) == 0;
+  const uint32_t alane = krow * C::RS + (cbase << 4) + ((hh ^ kswz) << 4);
+  auto a_addr = [&](uint32_t tile, int kb) -> uint32_t {
+    if constexpr (kAligned) return ((tile + alane) ^ ((kb & 7) << 5)) + ((kb >> 3) << 8);
+    return tile + krow * C::RS + (((cbase + 2 * kb + hh) ^ kswz) << 4);
+  };
+  const int tclo = 2 * (g16 & 1) + ((r16 & 3) >> 1);
+  const int twithin = ((4 * (r16 & 3)) & 7) << 1;
+  uint32_t tlane[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int k = 8 * hh + 4 * half + (r16 >> 2);
+    tlane[half] = k * C::RS + (cbase << 4) + ((tclo ^ swz(k)) << 4) + twithin;
+  }
+  auto t_addr = [&](uint32_t tile, int db, int kb2, int half) -> uint32_t {
+    if constexpr (kAligned)
+      return ((tile + tlane[half]) ^ ((db & 3) << 6)) + ((db >> 2) << 8) + kb2 * 16 * C::RS;
+    const int k = 16 * kb2 + 8 * hh + 4 * half + (r16 >> 2);
+    return tile + k * C::RS + (((cbase + 4 * db + tclo) ^ swz(k)) << 4) + twithin;
+  };
+  lds_t* const xbuf = smem + C::X_OFF;
+  lds_t* const gbuf = smem + C::G_OFF;
+  // Rows of this wave's register quarter, relative to the tile: 16 (cg/2) + 8 h + 4 (cg%2) + 0..3.
+  const int qrow = 16 * (cg >> 1) + 8 * hh + 4 * (cg & 1);
+
+  if (nsteps > 0) {
+    issue_t1(0, 0);
+    issue_t2(0);
+  }
+  wait_all();  // stationary operands, dQ's row statistics and the first tiles
+
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    wait_vmcnt<0>();
+    lds_barrier();  // (A) this step's tiles are visible; every wave has finished the last step
+    const bool more = st + 1 < nsteps;
+    if (more) issue_t1(st + 1, buf ^ 1);
+    const uint32_t t1 = lds_addr(smem + buf * C::TILE);
+    const uint32_t t2 = lds_addr(smem + C::T2_OFF);
+    const int row0 = step_row0(st);
+
+    // ---- partial S and dP over this wave's head-dim columns: C[streamed row][own row]
+    f32x16_t sacc = (f32x16_t){}, dpacc = (f32x16_t){};
+#pragma unroll
+    for (int kb = 0; kb < 2 * NDB; ++kb) {
+      sacc = Elt<T>::mma(lds_read_b128_at(a_addr(t1, kb)), r1[kb], sacc);
+      dpacc = Elt<T>::mma(lds_read_b128_at(a_addr(t2, kb)), r2[kb], dpacc);
+    }
+    pin_lds_mfma_pipeline<4 * NDB, 2, 1>();
+    // Partner quarters to the exchange: slot j holds quarter (cg + 1 + j) % 4.
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int q = (cg + 1 + j) & 3;
+      const int base = ((w * 3 + j) * 2) * C::PIECE + lane * 16;
+      lds_write_f4(xbuf, base, (f32x4_t){sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]});
+      lds_write_f4(xbuf, base + C::PIECE,
+                   (f32x4_t){dpacc[4 * q], dpacc[4 * q + 1], dpacc[4 * q + 2], dpacc[4 * q + 3]});
+    }
+    lds_barrier();  // (B) partial sums visible; every wave has finished reading tile 2
+    if (more) issue_t2(st + 1);
+
+    // ---- reduce this wave's quarter: own part + partners in a fixed order
+    f32x4_t sq = (f32x4_t){sacc[4 * cg], sacc[4 * cg + 1], sacc[4 * cg + 2], sacc[4 * cg + 3]};
+    f32x4_t dq = (f32x4_t){dpacc[4 * cg], dpacc[4 * cg + 1], dpacc[4 * cg + 2], dpacc[4 * cg + 3]};
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      const int pc = (cg + i) & 3;            // partner column group
+      const int j = (cg - pc - 1) & 3;        // its slot holding quarter cg
+      const int base = (((rg * NC + pc) * 3 + j) * 2) * C::PIECE + lane * 16;
+      sq = sq + lds_read_f4(xbuf, base);
+      dq = dq + lds_read_f4(xbuf, base + C::PIECE);
+    }
+
+    // ---- P and dS for the 4 (streamed, own) pairs of this lane's quarter
+    f32x4_t lse2q, dltq;
+    if constexpr (OWN_Q) {
+      lse2q = (f32x4_t){lse2_own, lse2_own, lse2_own, lse2_own};
+      dltq = (f32x4_t){dlt_own, dlt_own, dlt_own, dlt_own};
+    } else {
+      const lds_t* sd = smem + C::ST_OFF + buf * 512;
+      const f32x4_t lr = lds_read_f4(sd, qrow * 4);
+      dltq = lds_read_f4(sd, 256 + qrow * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lse2q[i] = lr[i] == -INFINITY ? INFINITY : lr[i] * kLog2e;
+    }
+    const int oi = ow0 + l32;
+    bool need_mask;
+    if constexpr (OWN_Q) {
+      need_mask = (row0 + 32 > sv.lk) || (p.causal && row0 + 31 > ow0 + off);
+    } else {
+      need_mask = (row0 + 32 > sv.lq) || (p.causal && ow0 + 31 > row0 + off);
+    }
+    float ds[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float pv = fast_exp2(sq[i] * p.scale_log2 - lse2q[i]);
+      if (need_mask) {
+        const int si = row0 + qrow + i;
+        const int qi = OWN_Q ? oi : si;
+        const int ki = OWN_Q ? si : oi;
+        const bool legal = ki < sv.lk && qi < sv.lq && (!p.causal || ki <= qi + off);
+        pv = legal ? pv : 0.f;
+      }
+      ds[i] = pv * (dq[i] - dltq[i]);
+    }
+    const u32x2_t mine = {Elt<T>::pack2(ds[0], ds[1]), Elt<T>::pack2(ds[2], ds[3])};
+    *(__attribute__((address_space(3))) u32x2_t*)(gbuf + w * 512 + lane * 8) = mine;
+    lds_barrier();  // (C) dS quarters visible
+
+    // ---- all-gather dS: quarter q gives B-operand words 2 (q % 2), +1 of k-block q / 2
+    uint32_t bop[2][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x2_t v = mine;
+      if (q != cg) v = *(const __attribute__((address_space(3))) u32x2_t*)(gbuf + (rg * NC + q) * 512 + lane * 8);
+      bop[q >> 1][2 * (q & 1)] = v.x;
+      bop[q >> 1][2 * (q & 1) + 1] = v.y;
+    }
+
+    // ---- acc^T[d][own] += A[d][streamed] * dS[streamed][own], A read transposed from tile 1
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const s16x4_t lo = lds_read_tr16_at(t_addr(t1, db, kb2, 0));
+        const s16x4_t hi = lds_read_tr16_at(t_addr(t1, db, kb2, 1));
+        const u32x4_t bv = {bop[kb2][0], bop[kb2][1], bop[kb2][2], bop[kb2][3]};
+        acc[db] = Elt<T>::mma(join_tr(lo, hi), bv, acc[db]);
+      }
+    }
+    pin_lds_mfma_pipeline<2 * NDB, 2, 2>();
+  }
+
+  // ---- epilogue: scale, round once to the storage dtype, store own rows
+  const int oi = ow0 + l32;
+  if (oi < own_len) {
+    uint16_t* dst = (uint16_t*)(OWN_Q ? p.dq : p.dk) + own_base + (long long)oi * own_row;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = cg * C::DW + 32 * db + 8 * i4 + 4 * hh;
+        if (d < p.d) {
+          const f32x16_t& a = acc[db];
+          const u32x2_t pk = {Elt<T>::pack2(a[4 * i4] * p.scale, a[4 * i4 + 1] * p.scale),
+                              Elt<T>::pack2(a[4 * i4 + 2] * p.scale, a[4 * i4 + 3] * p.scale)};
+          *(u32x2_t*)(dst + d) = pk;
+        }
+      }
+  }
+}
+
+template <class T, int MODE, int NDB>
+static hipError_t launch_bwd_rs(AttnParams p, hipStream_t st) {
+  using C = RsCfg<NDB>;
+  p.ntiles = ((MODE == kDQ ? p.nq : p.nkv) + C::BOWN - 1) / C::BOWN;
+  p.total = p.batch * (MODE == kDQ ? p.hq : p.hkv) * p.ntiles;
+  if (p.total == 0) return hipSuccess;
+  const int grid = (p.total + 7) & ~7;
+  hipLaunchKernelGGL((ffpa_bwd_rs_kernel<T, MODE, NDB>), dim3(grid), dim3(64 * C::NW), 0, st, p);
+  return hipGetLastError();
+}
+
 template <class T, int MODE, int NC, int NDB>
 static hipError_t launch_bwd_cfg(AttnParams p, hipStream_t st) {
   constexpr int NX = MODE != kDV ? 2 : 1;
@@ -418,6 +744,12 @@ static hipError_t launch_bwd_cfg(AttnParams p, hipStream_t st) {
 
 template <class T, int MODE>
 static hipError_t launch_bwd_mode(const AttnParams& p, hipStream_t st) {
+  if constexpr (MODE != kDV) {
+    if (p.d <= 512) {
+      if (p.d > 384) return launch_bwd_rs<T, MODE, 4>(p, st);
+      return launch_bwd_rs<T, MODE, 3>(p, st);
+    }
+  }
   if (p.d <= 512) {
     switch ((p.d + 63) / 64) {
       case 5: return launch_bwd_cfg<T, MODE, 2, 5>(p, st);

@@ -117,6 +117,15 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const lds_t* base, int byte_off
       (__attribute__((address_space(3))) s16x4_t*)(base + byte_off));
 }
 
+// Reads at a raw LDS byte address (for addresses formed by XOR from a per-lane base).
+__device__ __forceinline__ uint32_t lds_addr(const lds_t* p) { return (uint32_t)(uintptr_t)p; }
+__device__ __forceinline__ u32x4_t lds_read_b128_at(uint32_t a) {
+  return *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)a;
+}
+__device__ __forceinline__ s16x4_t lds_read_tr16_at(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(uintptr_t)a);
+}
+
 __device__ __forceinline__ u32x4_t join_tr(s16x4_t lo, s16x4_t hi) {
   u32x2_t a = __builtin_bit_cast(u32x2_t, lo);
   u32x2_t b = __builtin_bit_cast(u32x2_t, hi);
@@ -133,9 +142,12 @@ typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 // Buffer resource descriptor over [base, base + bytes) for raw (unformatted) 32-bit accesses:
 // base address in words 0-1 (stride 0), size in word 2, data format 32 in word 3.
+// The descriptor is wave-uniform; readfirstlane keeps it in scalar registers.
 __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t b = (uint64_t)base;
-  return (i32x4_t){(int32_t)(uint32_t)b, (int32_t)((b >> 32) & 0xffff), (int32_t)bytes, 0x00020000};
+  return (i32x4_t){__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)b),
+                   __builtin_amdgcn_readfirstlane((int32_t)((b >> 32) & 0xffff)),
+                   __builtin_amdgcn_readfirstlane((int32_t)bytes), 0x00020000};
 }
 
 // Asynchronous 16-byte copy through a buffer resource: lane l reads base + voff(lane) + soff and
@@ -145,11 +157,10 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
 // data visible explicitly: wait_vmcnt() in every issuing wave, then lds_barrier().
 // M0 is saved and restored around the copy, so its value is unchanged for the compiler.
 __device__ __forceinline__ void dma16_buf(i32x4_t r, int voff, int soff, lds_t* lds) {
-  // All scalar operands are wave-uniform by construction; readfirstlane makes that explicit.
+  // All scalar operands are wave-uniform by construction; readfirstlane makes that explicit for
+  // the LDS address and row offset (r comes from make_rsrc, already scalar).
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   soff = __builtin_amdgcn_readfirstlane(soff);
-  r = (i32x4_t){__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
-                __builtin_amdgcn_readfirstlane(r.z), __builtin_amdgcn_readfirstlane(r.w)};
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -158,6 +169,37 @@ __device__ __forceinline__ void dma16_buf(i32x4_t r, int voff, int soff, lds_t* 
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(voff), "s"(r), "s"(soff), "s"(m)
+      : "memory");
+}
+
+// Scheduling pin for a run of N MFMAs fed by LDS reads in the current scheduling region: the
+// reads of the first AHEAD MFMAs first, then alternately one MFMA and the reads of a later one,
+// then the last AHEAD MFMAs. Each MFMA then finds its operand already loaded instead of waiting
+// for the full LDS latency. R = LDS reads per MFMA. (Mask bits: 0x008 MFMA, 0x100 LDS read.)
+template <int N, int AHEAD, int R>
+__device__ __forceinline__ void pin_lds_mfma_pipeline() {
+  static_assert(AHEAD >= 1 && AHEAD <= N, "pipeline depth");
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * R, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
+// Asynchronous 4-byte copy through a buffer resource: lane l reads base + voff(lane) and writes
+// LDS bytes [lds + 4 l, lds + 4 l + 4). Same tracking rules as dma16_buf.
+__device__ __forceinline__ void dma4_buf(i32x4_t r, int voff, lds_t* lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(r), "s"(m)
       : "memory");
 }
 

@@ -26,6 +26,10 @@
 #include "ffpa_params.h"
 
 namespace ffpa {
+// MFMAs whose LDS operands are requested ahead of the one issuing (see pin_lds_mfma_pipeline).
+#ifndef FWD_AHEAD
+#define FWD_AHEAD 2
+#endif
 
 template <int NC, int NDB, int QB, int NBUF, int NW>
 struct FwdCfg {
@@ -144,36 +148,33 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   const int r16 = lane & 15;
   const int cbase = cg * C::DW >> 3;  // first 16-byte chunk of this wave's head-dim columns
 
-  // LDS byte offsets of this lane's operands within a tile. When the wave's first chunk is a
-  // multiple of 16, the swizzle (which permutes the low 4 bits of the chunk index) leaves the
-  // higher bits alone, so every offset is one of 8 per-lane bases plus a compile-time constant.
+  // LDS byte addresses of this lane's operands in a tile at LDS address `tile`. When the wave's
+  // first chunk is a multiple of 16, the swizzle (an XOR on the low 4 bits of the 16-byte chunk
+  // index) touches only address bits 4-7, which are zero in the row, column-group and tile bases:
+  // every operand address is then one per-lane base XOR a compile-time constant, plus a constant.
   constexpr bool kAligned = (C::DW % 128) == 0;
   // K rows (A operand of S^T): tile row row_perm(m), chunk cbase + 2 kb + h.
-  int klds[8];
-#pragma unroll
-  for (int lo = 0; lo < 8; ++lo) klds[lo] = krow * C::RS + ((cbase + ((2 * lo + hh) ^ kswz)) << 4);
-  auto k_off = [&](int kb) {
-    if constexpr (kAligned) return klds[kb & 7] + ((kb >> 3) << 8);
-    return krow * C::RS + (((cbase + 2 * kb + hh) ^ kswz) << 4);
+  const uint32_t klane = krow * C::RS + (cbase << 4) + ((hh ^ kswz) << 4);
+  auto k_addr = [&](uint32_t tile, int kb) -> uint32_t {
+    if constexpr (kAligned) return ((tile + klane) ^ ((kb & 7) << 5)) + ((kb >> 3) << 8);
+    return tile + krow * C::RS + (((cbase + 2 * kb + hh) ^ kswz) << 4);
   };
   // V^T (A operand of O^T += V^T P^T) via transposed reads: key row
-  // k = 16 kb2 + 8 h + 4 half + r16/4, head-dim column d = cg DW + 32 db + 16 (g16 % 2) + 4 (r16 % 4).
-  // swz(k) does not depend on kb2 or db, and 4 db touches chunk bits 2-3 only through (db % 4).
+  // k = 16 kb2 + 8 h + 4 half + r16/4, head-dim column d = cg DW + 32 db + 16 (g16 % 2) + 4 (r16 % 4),
+  // i.e. chunk cbase + 4 db + vclo. swz(k) does not depend on kb2.
   const int vclo = 2 * (g16 & 1) + ((r16 & 3) >> 1);
   const int vwithin = ((4 * (r16 & 3)) & 7) << 1;
-  int vlds[2][4];
+  uint32_t vlane[2];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int k = 8 * hh + 4 * half + (r16 >> 2);
-#pragma unroll
-    for (int d4 = 0; d4 < 4; ++d4)
-      vlds[half][d4] = k * C::RS + ((cbase + ((4 * d4 + vclo) ^ swz(k))) << 4) + vwithin;
+    vlane[half] = k * C::RS + (cbase << 4) + ((vclo ^ swz(k)) << 4) + vwithin;
   }
-  auto vt_off = [&](int db, int kb2, int half) {
-    if constexpr (kAligned) return vlds[half][db & 3] + ((db >> 2) << 8) + kb2 * 16 * C::RS;
+  auto v_addr = [&](uint32_t tile, int db, int kb2, int half) -> uint32_t {
+    if constexpr (kAligned)
+      return ((tile + vlane[half]) ^ ((db & 3) << 6)) + ((db >> 2) << 8) + kb2 * 16 * C::RS;
     const int k = 16 * kb2 + 8 * hh + 4 * half + (r16 >> 2);
-    const int chunk = cbase + 4 * db + vclo;
-    return k * C::RS + ((chunk ^ swz(k)) << 4) + vwithin;
+    return tile + k * C::RS + (((cbase + 4 * db + vclo) ^ swz(k)) << 4) + vwithin;
   };
 
   // ---- pipeline pieces (each runs the same barriers in every wave) --------------------------
@@ -198,10 +199,11 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     for (int qb = 0; qb < QB; ++qb) sacc[qb] = (f32x16_t){};
 #pragma unroll
     for (int kb = 0; kb < 2 * NDB; ++kb) {
-      const u32x4_t a = lds_read_b128(kt, k_off(kb));
+      const u32x4_t a = lds_read_b128_at(k_addr(lds_addr(kt), kb));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) sacc[qb] = Elt<T>::mma(a, qreg[qb][kb], sacc[qb]);
     }
+    if constexpr (QB == 1) pin_lds_mfma_pipeline<2 * NDB, FWD_AHEAD, 1>();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -286,8 +288,8 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const s16x4_t lo = lds_read_tr16(vt, vt_off(db, kb2, 0));
-        const s16x4_t hi = lds_read_tr16(vt, vt_off(db, kb2, 1));
+        const s16x4_t lo = lds_read_tr16_at(v_addr(lds_addr(vt), db, kb2, 0));
+        const s16x4_t hi = lds_read_tr16_at(v_addr(lds_addr(vt), db, kb2, 1));
         const u32x4_t a = join_tr(lo, hi);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -296,6 +298,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
         }
       }
     }
+    if constexpr (QB == 1) pin_lds_mfma_pipeline<2 * NDB, FWD_AHEAD, 2>();
     if constexpr (NBUF == 1) {
       lds_barrier();
       if (j + 1 < ntk) issue(vrs, j + 1, vbuf(0));
