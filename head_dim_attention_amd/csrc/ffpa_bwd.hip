@@ -555,7 +555,15 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
     }
   };
 
-  const int krow = row_perm(l32);
+  // Register quarter i of the C block (registers 4i..4i+3) covers tile rows 16 (i/2) + 8 h +
+  // 4 (i%2) + 0..3. Wave cg reads its A operand with the quarter bits of the row index (bits 4
+  // and 2) rotated by cg, so register quarter i holds the rows of quarter (i + cg) % 4: the quarter
+  // the wave finishes is always registers 0..3 and the partners' quarters are registers 4..15.
+  auto rot_quarter = [&](int row) {
+    const int q = (((row >> 4) & 1) << 1 | ((row >> 2) & 1)) + cg;
+    return (row & ~0x14) | (((q >> 1) & 1) << 4) | ((q & 1) << 2);
+  };
+  const int krow = rot_quarter(row_perm(l32));
   const int kswz = swz(krow);
   const int g16 = lane >> 4;
   const int r16 = lane & 15;
@@ -611,10 +619,11 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
       dpacc = Elt<T>::mma(lds_read_b128_at(a_addr(t2, kb)), r2[kb], dpacc);
     }
     pin_lds_mfma_pipeline<4 * NDB, 2, 1>();
-    // Partner quarters to the exchange: slot j holds quarter (cg + 1 + j) % 4.
+    // Partner quarters to the exchange: slot j holds register quarter j + 1, i.e. quarter
+    // (cg + 1 + j) % 4.
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      const int q = (cg + 1 + j) & 3;
+      const int q = j + 1;
       const int base = ((w * 3 + j) * 2) * C::PIECE + lane * 16;
       lds_write_f4(xbuf, base, (f32x4_t){sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]});
       lds_write_f4(xbuf, base + C::PIECE,
@@ -624,12 +633,12 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
     if (more) issue_t2(st + 1);
 
     // ---- reduce this wave's quarter: own part + partners in a fixed order
-    f32x4_t sq = (f32x4_t){sacc[4 * cg], sacc[4 * cg + 1], sacc[4 * cg + 2], sacc[4 * cg + 3]};
-    f32x4_t dq = (f32x4_t){dpacc[4 * cg], dpacc[4 * cg + 1], dpacc[4 * cg + 2], dpacc[4 * cg + 3]};
+    f32x4_t sq = (f32x4_t){sacc[0], sacc[1], sacc[2], sacc[3]};
+    f32x4_t dq = (f32x4_t){dpacc[0], dpacc[1], dpacc[2], dpacc[3]};
 #pragma unroll
     for (int i = 1; i < 4; ++i) {
       const int pc = (cg + i) & 3;            // partner column group
-      const int j = (cg - pc - 1) & 3;        // its slot holding quarter cg
+      const int j = ((cg - pc) & 3) - 1;      // its slot holding quarter cg
       const int base = (((rg * NC + pc) * 3 + j) * 2) * C::PIECE + lane * 16;
       sq = sq + lds_read_f4(xbuf, base);
       dq = dq + lds_read_f4(xbuf, base + C::PIECE);
