@@ -197,20 +197,41 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
   }
   // Tile 1 feeds the scores (K for dQ, Q for dK/dV); tile 2 feeds dP (V for dQ, dO for dK) or the
   // dV product (dO).
-  auto issue = [&](int st, int buf) {
+  // A step index past the end is clamped to the last step (its copies then land in a buffer that
+  // is not read again).
+  struct StepSrc {
+    i32x4_t r1, r2;
+    int row0;
+  };
+  auto step_src = [&](int st) {
+    st = min(st, nsteps - 1);
     const long long base = str_base(step_head(st));
-    const i32x4_t rs1 = make_rsrc((const uint16_t*)(OWN_Q ? p.k : p.q) + base, span);
-    const i32x4_t rs2 = make_rsrc((const uint16_t*)(OWN_Q ? p.v : p.dout) + base, span);
-    lds_t* t1 = smem + buf * 2 * C::TILE;
-    const int row0 = step_row0(st);
+    StepSrc x;
+    x.r1 = make_rsrc((const uint16_t*)(OWN_Q ? p.k : p.q) + base, span);
+    x.r2 = make_rsrc((const uint16_t*)(OWN_Q ? p.v : p.dout) + base, span);
+    x.row0 = step_row0(st);
+    return x;
+  };
+  // Copy ii of tile `which` (1 or 2) of a step into buffer buf.
+  auto copy1 = [&](const StepSrc& x, int buf, int which, int ii) {
+    const int i = w + NW * ii;
+    const int row = min(x.row0 + i / IPR, str_len - 1);
+    dma16_buf(which == 1 ? x.r1 : x.r2, voff[ii], row * row_bytes,
+              smem + buf * 2 * C::TILE + (which - 1) * C::TILE + i * 1024);
+  };
+  auto issue = [&](int st, int buf) {
+    const StepSrc x = step_src(st);
 #pragma unroll
     for (int ii = 0; ii < C::NINSTR; ++ii) {
-      const int i = w + NW * ii;
-      const int row = min(row0 + i / IPR, str_len - 1);
-      dma16_buf(rs1, voff[ii], row * row_bytes, t1 + i * 1024);
-      dma16_buf(rs2, voff[ii], row * row_bytes, t1 + C::TILE + i * 1024);
+      copy1(x, buf, 1, ii);
+      copy1(x, buf, 2, ii);
     }
   };
+  // With two buffers, the copies of step st + 1 are spread over the partial products of step st
+  // (both of its buffers were released at the barrier that opens step st): the copy path moves
+  // about 64 B per clock per CU, so a whole step issued at once would hold every wave at the issue.
+  // Copy c of the 2 * NINSTR of a step is issued after MFMA spread_at(n, c) of a run of n.
+  auto spread_at = [](int n, int c) { return (c * n) / (2 * C::NINSTR); };
 
   const int krow = row_perm(l32);
   const int kswz = swz(krow);
@@ -274,11 +295,8 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
     lds_barrier();
     const float lse2_cur = lse_next == -INFINITY ? INFINITY : lse_next * kLog2e;
     const float dlt_cur = dlt_next;
-    // The next step's tiles go into the buffer the barrier above released.
-    if (NBUF == 2 && st + 1 < nsteps) {
-      issue(st + 1, buf ^ 1);
-      load_row_stats(st + 1);
-    }
+    if (NBUF == 2 && st + 1 < nsteps) load_row_stats(st + 1);
+    const StepSrc xn = step_src(st + 1);
     const lds_t* t1 = smem + buf * 2 * C::TILE;
     const lds_t* t2 = t1 + C::TILE;
     const int row0 = step_row0(st);
@@ -290,6 +308,11 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
     for (int kb = 0; kb < KSTEPS; ++kb) {
       sacc = Elt<T>::mma(lds_read_b128_at(a_addr(lds_addr(t1), kb)), r1[kb], sacc);
       if constexpr (HAS_DP) dpacc = Elt<T>::mma(lds_read_b128_at(a_addr(lds_addr(t2), kb)), r2[kb], dpacc);
+      if constexpr (NBUF == 2) {
+#pragma unroll
+        for (int c = 0; c < 2 * C::NINSTR; ++c)
+          if (kb == spread_at(KSTEPS, c)) copy1(xn, buf ^ 1, 1 + (c & 1), c >> 1);
+      }
     }
     pin_lds_mfma_pipeline<KSTEPS * (HAS_DP ? 2 : 1), BWD_AHEAD, 1>();
 #pragma unroll
@@ -382,6 +405,8 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
       }
     }
   }
+  // Copies issued during the last step land in LDS that the next workgroup may own.
+  wait_vmcnt<0>();
 
   // ---- epilogue: scale, round once to the storage dtype, store own rows
   const float osc = MODE == kDV ? 1.0f : p.scale;
@@ -521,39 +546,45 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
 #pragma unroll
   for (int ii = 0; ii < C::NINSTR; ++ii) voff[ii] = min(lane ^ swz(w + NW * ii), dch - 1) << 4;
 
-  // Tile 1 (K for dQ, Q for dK) of step st into buffer buf, with dK's row statistics.
-  auto issue_t1 = [&](int st, int buf) {
-    const int head = step_head(st);
-    const int row0 = step_row0(st);
-    const i32x4_t rs = make_rsrc((const uint16_t*)(OWN_Q ? p.k : p.q) + str_base(head), span);
-    lds_t* dst = smem + buf * C::TILE;
-#pragma unroll
-    for (int ii = 0; ii < C::NINSTR; ++ii) {
-      const int i = w + NW * ii;
-      dma16_buf(rs, voff[ii], min(row0 + i, str_len - 1) * row_bytes, dst + i * 1024);
-    }
+  // Copies of step st: tile 1 (K for dQ, Q for dK) into buffer buf, tile 2 (V for dQ, dO for dK)
+  // into its single buffer, and dK's row statistics. A step index past the end is clamped to the
+  // last step (its copies then land in buffers that are not read again).
+  struct StepSrc {
+    i32x4_t r1, r2;
+    int row0, head;
+  };
+  auto step_src = [&](int st) {
+    st = min(st, nsteps - 1);
+    StepSrc x;
+    x.head = step_head(st);
+    x.row0 = step_row0(st);
+    x.r1 = make_rsrc((const uint16_t*)(OWN_Q ? p.k : p.q) + str_base(x.head), span);
+    x.r2 = make_rsrc((const uint16_t*)(OWN_Q ? p.v : p.dout) + str_base(x.head), span);
+    return x;
+  };
+  auto copy_t1 = [&](const StepSrc& x, int buf, int ii) {
+    const int i = w + NW * ii;
+    dma16_buf(x.r1, voff[ii], min(x.row0 + i, str_len - 1) * row_bytes, smem + buf * C::TILE + i * 1024);
+  };
+  auto copy_t2 = [&](const StepSrc& x, int ii) {
+    const int i = w + NW * ii;
+    dma16_buf(x.r2, voff[ii], min(x.row0 + i, str_len - 1) * row_bytes, smem + C::T2_OFF + i * 1024);
+  };
+  auto copy_stats = [&](const StepSrc& x, int buf) {
     if constexpr (!OWN_Q) {
       if (w == 0) {
-        const long long li = sv.lse_off + (long long)head * p.lse_head;
+        const long long li = sv.lse_off + (long long)x.head * p.lse_head;
         const uint32_t bytes = (uint32_t)max(sv.lq, 1) * 4;
-        const int vo = min(row0 + l32, sv.lq - 1) * 4;
+        const int vo = min(x.row0 + l32, sv.lq - 1) * 4;
         lds_t* sd = smem + C::ST_OFF + buf * 512;
         dma4_buf(make_rsrc(p.lse_in + li, bytes), vo, sd);
         dma4_buf(make_rsrc(p.delta + li, bytes), vo, sd + 256);
       }
     }
   };
-  // Tile 2 (V for dQ, dO for dK) of step st into its single buffer.
-  auto issue_t2 = [&](int st) {
-    const int row0 = step_row0(st);
-    const i32x4_t rs = make_rsrc((const uint16_t*)(OWN_Q ? p.v : p.dout) + str_base(step_head(st)), span);
-    lds_t* dst = smem + C::T2_OFF;
-#pragma unroll
-    for (int ii = 0; ii < C::NINSTR; ++ii) {
-      const int i = w + NW * ii;
-      dma16_buf(rs, voff[ii], min(row0 + i, str_len - 1) * row_bytes, dst + i * 1024);
-    }
-  };
+  // MFMA index (of a run of n) after which copy ii is issued: the copy path moves about 64 B per
+  // clock per CU, so a whole tile issued at once would hold every wave at the issue.
+  auto spread_at = [](int n, int ii) { return (ii * n) / C::NINSTR; };
 
   // Register quarter i of the C block (registers 4i..4i+3) covers tile rows 16 (i/2) + 8 h +
   // 4 (i%2) + 0..3. Wave cg reads its A operand with the quarter bits of the row index (bits 4
@@ -596,17 +627,26 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
   const int qrow = 16 * (cg >> 1) + 8 * hh + 4 * (cg & 1);
 
   if (nsteps > 0) {
-    issue_t1(0, 0);
-    issue_t2(0);
+    const StepSrc x0 = step_src(0);
+    copy_stats(x0, 0);
+#pragma unroll
+    for (int ii = 0; ii < C::NINSTR; ++ii) {
+      copy_t1(x0, 0, ii);
+      copy_t2(x0, ii);
+    }
   }
   wait_all();  // stationary operands, dQ's row statistics and the first tiles
 
+  // The copies of step st + 1 are issued during step st: its statistics after barrier A, tile 1
+  // spread over the partial products (its other buffer was released at barrier A), tile 2 right
+  // after barrier B, which releases its single buffer (as early as possible, so that it lands
+  // before step st + 1). All are waited for before barrier A of step st + 1.
   for (int st = 0; st < nsteps; ++st) {
     const int buf = st & 1;
     wait_vmcnt<0>();
     lds_barrier();  // (A) this step's tiles are visible; every wave has finished the last step
-    const bool more = st + 1 < nsteps;
-    if (more) issue_t1(st + 1, buf ^ 1);
+    const StepSrc xn = step_src(st + 1);
+    copy_stats(xn, buf ^ 1);
     const uint32_t t1 = lds_addr(smem + buf * C::TILE);
     const uint32_t t2 = lds_addr(smem + C::T2_OFF);
     const int row0 = step_row0(st);
@@ -617,6 +657,9 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
     for (int kb = 0; kb < 2 * NDB; ++kb) {
       sacc = Elt<T>::mma(lds_read_b128_at(a_addr(t1, kb)), r1[kb], sacc);
       dpacc = Elt<T>::mma(lds_read_b128_at(a_addr(t2, kb)), r2[kb], dpacc);
+#pragma unroll
+      for (int ii = 0; ii < C::NINSTR; ++ii)
+        if (kb == spread_at(2 * NDB, ii)) copy_t1(xn, buf ^ 1, ii);
     }
     pin_lds_mfma_pipeline<4 * NDB, 2, 1>();
     // Partner quarters to the exchange: slot j holds register quarter j + 1, i.e. quarter
@@ -630,7 +673,8 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
                    (f32x4_t){dpacc[4 * q], dpacc[4 * q + 1], dpacc[4 * q + 2], dpacc[4 * q + 3]});
     }
     lds_barrier();  // (B) partial sums visible; every wave has finished reading tile 2
-    if (more) issue_t2(st + 1);
+#pragma unroll
+    for (int ii = 0; ii < C::NINSTR; ++ii) copy_t2(xn, ii);
 
     // ---- reduce this wave's quarter: own part + partners in a fixed order
     f32x4_t sq = (f32x4_t){sacc[0], sacc[1], sacc[2], sacc[3]};
@@ -703,6 +747,8 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
     }
     pin_lds_mfma_pipeline<2 * NDB, 2, 2>();
   }
+  // Copies issued during the last step land in LDS that the next workgroup may own.
+  wait_vmcnt<0>();
 
   // ---- epilogue: scale, round once to the storage dtype, store own rows
   const int oi = ow0 + l32;

@@ -132,15 +132,22 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     const int pc = (i % IPR) * 64 + lane;
     voff[ii] = min(pc ^ swz(R), dch - 1) << 4;
   }
+  auto issue1 = [&](i32x4_t rs, int j, lds_t* dst, int ii) {
+    const int i = w + NW * ii;
+    const int row = min(j * 32 + i / IPR, sv.lk - 1);
+    dma16_buf(rs, voff[ii], row * row_bytes, dst + i * 1024);
+  };
   auto issue = [&](i32x4_t rs, int j, lds_t* dst) {
 #pragma unroll
-    for (int ii = 0; ii < C::NINSTR; ++ii) {
-      const int i = w + NW * ii;
-      const int R = i / IPR;
-      const int row = min(j * 32 + R, sv.lk - 1);
-      dma16_buf(rs, voff[ii], row * row_bytes, dst + i * 1024);
-    }
+    for (int ii = 0; ii < C::NINSTR; ++ii) issue1(rs, j, dst, ii);
   };
+  // With two buffers, the copies of tile j + 1 are spread over the MFMAs of step j (K during the
+  // scores, V during P V): the copy path moves about 64 B per clock per CU, so a whole tile issued
+  // at once would hold every wave at the issue for hundreds of cycles. They are issued for every
+  // step, the last one included (rows clamped, into a buffer no longer read), so that no branch
+  // splits the MFMA sequence; the kernel waits for them before it exits.
+  // MFMA index after which copy ii of a run of N MFMAs is issued.
+  auto spread_at = [](int n, int ii) { return (ii * n) / C::NINSTR; };
 
   const int krow = row_perm(l32);
   const int kswz = swz(krow);
@@ -180,12 +187,9 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   // ---- pipeline pieces (each runs the same barriers in every wave) --------------------------
   auto top = [&](int j) {
     if constexpr (NBUF == 2) {
-      wait_vmcnt<0>();
+      // In flight: K_j (issued during the scores of step j - 1), then V_j. K_j is needed now.
+      wait_vmcnt<C::NINSTR>();
       lds_barrier();
-      if (j + 1 < ntk) {
-        issue(krs, j + 1, kbuf((j + 1) & 1));
-        issue(vrs, j + 1, vbuf((j + 1) & 1));
-      }
     } else {
       wait_vmcnt<C::NINSTR>();  // K_j has landed; V_j may still be in flight
       lds_barrier();
@@ -202,6 +206,11 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
       const u32x4_t a = lds_read_b128_at(k_addr(lds_addr(kt), kb));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) sacc[qb] = Elt<T>::mma(a, qreg[qb][kb], sacc[qb]);
+      if constexpr (NBUF == 2) {
+#pragma unroll
+        for (int ii = 0; ii < C::NINSTR; ++ii)
+          if (kb == spread_at(2 * NDB, ii)) issue1(krs, j + 1, kbuf((j + 1) & 1), ii);
+      }
     }
     if constexpr (QB == 1) pin_lds_mfma_pipeline<2 * NDB, FWD_AHEAD, 1>();
 #pragma unroll
@@ -210,6 +219,9 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
       for (int r4 = 0; r4 < 4; ++r4)
         lds_write_f4(xbuf, (((w * QB + qb) * 4 + r4) * 64 + lane) * 16,
                      (f32x4_t){sacc[qb][4 * r4], sacc[qb][4 * r4 + 1], sacc[qb][4 * r4 + 2], sacc[qb][4 * r4 + 3]});
+    // In flight: V_j (issued during P V of step j - 1), then K_{j+1}. V_j is needed after this
+    // barrier.
+    if constexpr (NBUF == 2) wait_vmcnt<C::NINSTR>();
     lds_barrier();
     if constexpr (NBUF == 1) {
       if (j + 1 < ntk) issue(krs, j + 1, kbuf(0));
@@ -296,6 +308,11 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
           const u32x4_t bop = {pb[qb][kb2][0], pb[qb][kb2][1], pb[qb][kb2][2], pb[qb][kb2][3]};
           oacc[qb][db] = Elt<T>::mma(a, bop, oacc[qb][db]);
         }
+        if constexpr (NBUF == 2) {
+#pragma unroll
+          for (int ii = 0; ii < C::NINSTR; ++ii)
+            if (2 * db + kb2 == spread_at(2 * NDB, ii)) issue1(vrs, j + 1, vbuf((j + 1) & 1), ii);
+        }
       }
     }
     if constexpr (QB == 1) pin_lds_mfma_pipeline<2 * NDB, FWD_AHEAD, 2>();
@@ -356,6 +373,9 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     make_p(sacc, pb);
     pv(j, pb);
   }
+
+  // Copies issued during the last step land in LDS that the next workgroup may own.
+  wait_vmcnt<0>();
 
   // ---- epilogue: O = O^T / l, LSE = ln(2) * (mref + log2 l); empty rows give 0 and -inf
 #pragma unroll
