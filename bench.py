@@ -5,7 +5,9 @@ Metric: attention TFLOPS (forward, and forward+backward) at D=512, N=8192, bf16,
 of the dense bf16 MFMA peak. A step is one pass of the whole path over one batch of synthetic
 inputs already resident in HBM: the forward kernel, then the four backward launches
 (preprocess, dV, dK, dQ). Credited flops per legal (query, key) pair and query head: 4*D forward,
-10*D backward (the recomputation inside the backward is not credited).
+10*D backward (the recomputation inside the backward is not credited). By default the backward
+runs with the library's dS workspace (dK stores dS, dQ multiplies it by K); --no-ds-workspace
+times the recomputing dQ kernel instead.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line (rank 0).
@@ -29,8 +31,10 @@ METRIC = "attention TFLOPS (fwd, fwd+bwd) at D=512 N=8192 bf16; % of MFMA peak"
 # 256 CUs x 2.4 GHz x 4096 dense bf16/fp16 flop per clock per CU.
 PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
-# Algorithmic flops per legal pair and query head, by kernel (D multiplies these).
+# Algorithmic flops per legal pair and query head, by kernel (D multiplies these). dQ does 6 D when
+# it recomputes S, P, dP and dS, and 2 D when it multiplies the stored dS by K.
 KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "dv": 4, "dk": 6, "dq": 6}
+DQ_FLOPS_PER_PAIR_D_STORED_DS = 2
 STAGES = ("fwd", "pre", "dv", "dk", "dq")
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "traffic_dense_d512_n8192.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "head_dim_attention_amd", "csrc", f)
@@ -63,6 +67,8 @@ def parse_args(argv=None):
     ap.add_argument("--workload", default="dense_d512_n8192")
     ap.add_argument("--seed", type=int, default=2024)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-ds-workspace", action="store_true",
+                    help="backward without the dS workspace (dQ recomputes S, P, dP and dS)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration under rocprofv3)")
     return ap.parse_args(argv)
@@ -166,6 +172,11 @@ def main(argv=None) -> int:
     delta = torch.empty_like(lse)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     lib = F.load_library()
+    ws_bytes = 0 if args.no_ds_workspace else F.ffpa_bwd_workspace_bytes(b, hq, nq, nkv)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
+    flops_d = dict(KERNEL_FLOPS_PER_PAIR_D)
+    if ws is not None:
+        flops_d["dq"] = DQ_FLOPS_PER_PAIR_D_STORED_DS
     dt = 0 if w.dtype == "bf16" else 1
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -178,7 +189,7 @@ def main(argv=None) -> int:
 
     def bwd_stage(i):
         st = lib.ffpa_bwd_stage(i, P(qd), P(kd), P(vd), P(o), P(dod), P(lse), P(delta), P(dq), P(dk), P(dv),
-                                b, hq, hkv, nq, nkv, d, dt, scale, int(causal), sp)
+                                b, hq, hkv, nq, nkv, d, dt, scale, int(causal), P(ws), ws_bytes, sp)
         if st:
             raise RuntimeError(F.ffpa_status_string(st))
 
@@ -214,12 +225,12 @@ def main(argv=None) -> int:
 
     # Dominant kernel: the longest of the compute kernels.
     dom = max(("fwd", "dv", "dk", "dq"), key=lambda n: stage_ms[n])
-    dom_flops = KERNEL_FLOPS_PER_PAIR_D[dom] * d * pairs
+    dom_flops = flops_d[dom] * d * pairs
     achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
     traffic = load_traffic(dom)
     kernels = {}
     for n in ("fwd", "dv", "dk", "dq"):
-        fl = KERNEL_FLOPS_PER_PAIR_D[n] * d * pairs
+        fl = flops_d[n] * d * pairs
         kernels[n] = {"ms": round(stage_ms[n], 4), "algorithmic_tflops": round(fl / (stage_ms[n] * 1e-3) / 1e12, 2),
                       "frac": round(fl / (stage_ms[n] * 1e-3) / 1e12 / PEAK_TFLOPS, 4)}
     pre_bytes = 2.0 * b * hq * nq * d * qd.element_size() + 4.0 * b * hq * nq
@@ -246,6 +257,8 @@ def main(argv=None) -> int:
         "fwdbwd_frac_of_peak": round(value / PEAK_TFLOPS, 4),
         "peak_tflops": PEAK_TFLOPS,
         "event_ms_per_step": round(step_ms, 4),
+        "dq_path": (f"stored dS ({ws_bytes / 2**30:.2f} GiB workspace)" if ws is not None
+                    else "recompute S, P, dP, dS"),
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic},

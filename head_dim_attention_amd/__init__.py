@@ -5,7 +5,8 @@ this package is its ctypes binding plus autograd wrappers. PyTorch provides devi
 streams only.
 """
 from ._binding import (  # noqa: F401
-    FFPA_ERR_HIP, FFPA_ERR_INVALID_ARGUMENT, FFPA_ERR_NOT_SUPPORTED, FFPA_OK, ffpa_bwd, ffpa_bwd_stage, ffpa_fwd,
-    ffpa_status_string, ffpa_varlen_bwd, ffpa_varlen_fwd, library_path, load_library,
+    FFPA_ERR_HIP, FFPA_ERR_INVALID_ARGUMENT, FFPA_ERR_NOT_SUPPORTED, FFPA_OK, ffpa_bwd, ffpa_bwd_stage,
+    ffpa_bwd_workspace_bytes, ffpa_fwd, ffpa_status_string, ffpa_varlen_bwd, ffpa_varlen_bwd_workspace_bytes,
+    ffpa_varlen_fwd, library_path, load_library,
 )
 from .attention import ffpa_attn_func, ffpa_attn_varlen_func  # noqa: F401

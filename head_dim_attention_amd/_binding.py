@@ -20,6 +20,7 @@ __all__ = [
     "FFPA_OK", "FFPA_ERR_INVALID_ARGUMENT", "FFPA_ERR_NOT_SUPPORTED", "FFPA_ERR_HIP",
     "library_path", "load_library", "ffpa_status_string",
     "ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd",
+    "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes",
 ]
 
 FFPA_OK = 0
@@ -34,13 +35,18 @@ _LOCK = threading.Lock()
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
+_sz = ctypes.c_size_t
 
 _SIGNATURES = {
     "ffpa_fwd": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp],
-    "ffpa_bwd": [_vp] * 10 + [_i] * 7 + [_f, _i, _vp],
-    "ffpa_bwd_stage": [_i] + [_vp] * 10 + [_i] * 7 + [_f, _i, _vp],
+    "ffpa_bwd": [_vp] * 10 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
+    "ffpa_bwd_stage": [_i] + [_vp] * 10 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "ffpa_varlen_fwd": [_vp] * 7 + [_i] * 9 + [_f, _i, _vp],
-    "ffpa_varlen_bwd": [_vp] * 12 + [_i] * 9 + [_f, _i, _vp],
+    "ffpa_varlen_bwd": [_vp] * 12 + [_i] * 9 + [_f, _i, _vp, _sz, _vp],
+}
+_SIZE_FUNCTIONS = {
+    "ffpa_bwd_workspace_bytes": [_i] * 4,
+    "ffpa_varlen_bwd_workspace_bytes": [_i] * 4,
 }
 
 
@@ -63,6 +69,10 @@ def load_library():
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        for name, args in _SIZE_FUNCTIONS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = _sz
         lib.ffpa_status_string.argtypes = [ctypes.c_int]
         lib.ffpa_status_string.restype = ctypes.c_char_p
         _LIB = lib
@@ -135,8 +145,30 @@ def ffpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = F
     return o, lse
 
 
-def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float] = None):
-    """Dense backward -> (dq, dk, dv) with the shapes and dtype of q, k, v."""
+def ffpa_bwd_workspace_bytes(batch: int, hq: int, nq: int, nkv: int) -> int:
+    """Bytes of the optional dS workspace of the dense backward (0: not available)."""
+    return int(load_library().ffpa_bwd_workspace_bytes(int(batch), int(hq), int(nq), int(nkv)))
+
+
+def ffpa_varlen_bwd_workspace_bytes(hq: int, total_q: int, max_seqlen_q: int, max_seqlen_k: int) -> int:
+    """Bytes of the optional dS workspace of the varlen backward (0: not available)."""
+    return int(load_library().ffpa_varlen_bwd_workspace_bytes(int(hq), int(total_q), int(max_seqlen_q),
+                                                               int(max_seqlen_k)))
+
+
+def _workspace(nbytes: int, like: torch.Tensor):
+    """Device workspace of nbytes (None when nbytes is 0), and its size to pass."""
+    if nbytes <= 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=like.device), nbytes
+
+
+def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float] = None, store_ds: bool = True):
+    """Dense backward -> (dq, dk, dv) with the shapes and dtype of q, k, v.
+
+    store_ds: let the dK stage store dS in a temporary workspace of ffpa_bwd_workspace_bytes() bytes so
+    that the dQ stage multiplies it by K instead of recomputing it (False: O(N) memory, recompute).
+    """
     q, k, v, o, dout = (_dev(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")))
     lse = _dev(lse, "lse")
     _same(q, k, v, o, dout)
@@ -148,28 +180,36 @@ def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float]
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     delta = torch.empty((b, hq, nq), dtype=torch.float32, device=q.device)
+    ws, nws = _workspace(ffpa_bwd_workspace_bytes(b, hq, nq, nkv) if store_ds else 0, q)
     st = load_library().ffpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
                                  _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, nq, nkv, d,
-                                 _dtype_code(q), _scale(scale, d), int(bool(causal)), _stream(q))
+                                 _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(ws), nws, _stream(q))
     _raise_for(st, "ffpa_bwd")
     return dq, dk, dv
 
 
 def ffpa_bwd_stage(stage: int, q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool = False,
-                   scale: Optional[float] = None):
+                   scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
     """Run one backward stage (0 preprocess, 1 dV, 2 dK, 3 dQ) into caller-provided buffers.
 
     All tensors must be contiguous GPU tensors with ffpa_bwd's shapes; delta is float32 [B,Hq,Nq].
+    workspace: optional dS workspace (a GPU tensor of at least ffpa_bwd_workspace_bytes() bytes),
+    the same for stages 2 and 3.
     """
+    if workspace is not None and not (isinstance(workspace, torch.Tensor) and workspace.device.type == "cuda"
+                                      and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
     for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (lse, "lse"), (delta, "delta"),
                  (dq, "dq"), (dk, "dk"), (dv, "dv")):
         if not (isinstance(x, torch.Tensor) and x.device.type == "cuda" and x.is_contiguous()):
             raise ValueError(f"{n} must be a contiguous GPU tensor")
     b, hq, nq, d = q.shape
     _, hkv, nkv, _ = k.shape
+    nws = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load_library().ffpa_bwd_stage(int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                        _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, nq, nkv, d,
-                                       _dtype_code(q), _scale(scale, d), int(bool(causal)), _stream(q))
+                                       _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(workspace), nws,
+                                       _stream(q))
     _raise_for(st, "ffpa_bwd_stage")
 
 
@@ -227,8 +267,8 @@ def ffpa_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None,
 
 def ffpa_varlen_bwd(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None,
                     max_seqlen_k=None, causal: bool = False, scale: Optional[float] = None,
-                    validate: bool = True):
-    """Packed backward -> (dq [Tq,Hq,D], dk [Tk,Hkv,D], dv [Tk,Hkv,D])."""
+                    validate: bool = True, store_ds: bool = True):
+    """Packed backward -> (dq [Tq,Hq,D], dk [Tk,Hkv,D], dv [Tk,Hkv,D]). store_ds as in ffpa_bwd."""
     q, k, v, o, dout = (_dev(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")))
     lse = _dev(lse, "lse")
     _same(q, k, v, o, dout)
@@ -243,9 +283,10 @@ def ffpa_varlen_bwd(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k=None, max_
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     delta = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    ws, nws = _workspace(ffpa_varlen_bwd_workspace_bytes(hq, tq, max_q, max_k) if store_ds else 0, q)
     st = load_library().ffpa_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
                                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_q), _ptr(cu_k), cu_q.numel() - 1,
                                         max_q, max_k, tq, tk, hq, hkv, d, _dtype_code(q), _scale(scale, d),
-                                        int(bool(causal)), _stream(q))
+                                        int(bool(causal)), _ptr(ws), nws, _stream(q))
     _raise_for(st, "ffpa_varlen_bwd")
     return dq, dk, dv

@@ -82,6 +82,31 @@ bool too_big_dense(int batch, int h, int n, int d) {
   return per_head > (1LL << 31) - 1 || (long long)batch * h * per_head > (1LL << 46);
 }
 
+long long round_up8(long long x) { return (x + 7) & ~7LL; }
+
+// Bytes of one head's stored dS block of nq rows of round_up8(nkv) elements; the dQ pass
+// addresses it with 32-bit byte offsets, so larger blocks use the recomputing dQ kernel.
+bool ds_block_ok(long long nq, long long nkv) { return nq * round_up8(nkv) * 2 <= (1LL << 31) - 4096; }
+
+size_t dense_ds_bytes(int batch, int hq, int nq, int nkv) {
+  if (batch < 1 || hq < 1 || nq < 1 || nkv < 1 || !ds_block_ok(nq, nkv)) return 0;
+  return (size_t)batch * hq * nq * round_up8(nkv) * 2;
+}
+
+size_t varlen_ds_bytes(int hq, int total_q, int max_q, int max_k) {
+  if (hq < 1 || total_q < 1 || max_q < 1 || max_k < 1 || !ds_block_ok(max_q, max_k)) return 0;
+  return (size_t)hq * total_q * round_up8(max_k) * 2;
+}
+
+// Attach a caller workspace for dS. NULL selects the recomputing dQ kernel; a workspace smaller
+// than `need` is an invalid argument; need == 0 (not available for these sizes) ignores it.
+int attach_ds(AttnParams& p, void* ws, size_t ws_bytes, size_t need) {
+  if (ws == nullptr || need == 0) return FFPA_OK;
+  if (ws_bytes < need) return FFPA_ERR_INVALID_ARGUMENT;
+  p.ds = ws;
+  return FFPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -126,7 +151,8 @@ int ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float*
 
 static int dense_bwd(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
                      const float* lse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv,
-                     int nq, int nkv, int d, int dtype, float scale, int causal, void* stream) {
+                     int nq, int nkv, int d, int dtype, float scale, int causal, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   if (stage < -1 || stage > 3) return FFPA_ERR_INVALID_ARGUMENT;
   if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
@@ -146,28 +172,41 @@ static int dense_bwd(int stage, const void* q, const void* k, const void* v, con
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
+  const int ws = attach_ds(p, workspace, workspace_bytes, dense_ds_bytes(batch, hq, nq, nkv));
+  if (ws != FFPA_OK) return ws;
+  p.ds_row = (int)round_up8(nkv);
+  p.ds_head = (long long)nq * p.ds_row;
+  p.ds_batch = (long long)hq * p.ds_head;
   return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, (int)nrows, 0, (hipStream_t)stream, stage));
+}
+
+size_t ffpa_bwd_workspace_bytes(int batch, int hq, int nq, int nkv) { return dense_ds_bytes(batch, hq, nq, nkv); }
+
+size_t ffpa_varlen_bwd_workspace_bytes(int hq, int total_q, int max_seqlen_q, int max_seqlen_k) {
+  return varlen_ds_bytes(hq, total_q, max_seqlen_q, max_seqlen_k);
 }
 
 int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
              float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq, int nkv, int d,
-             int dtype, float scale, int causal, void* stream) {
+             int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
   return dense_bwd(-1, q, k, v, o, dout, lse, delta, dq, dk, dv, batch, hq, hkv, nq, nkv, d, dtype, scale, causal,
-                   stream);
+                   workspace, workspace_bytes, stream);
 }
 
 int ffpa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq,
-                   int nkv, int d, int dtype, float scale, int causal, void* stream) {
+                   int nkv, int d, int dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   if (stage < 0 || stage > 3) return FFPA_ERR_INVALID_ARGUMENT;
   return dense_bwd(stage, q, k, v, o, dout, lse, delta, dq, dk, dv, batch, hq, hkv, nq, nkv, d, dtype, scale, causal,
-                   stream);
+                   workspace, workspace_bytes, stream);
 }
 
 int ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                     float* delta, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
                     const int32_t* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k, int total_q,
-                    int total_k, int hq, int hkv, int d, int dtype, float scale, int causal, void* stream) {
+                    int total_k, int hq, int hkv, int d, int dtype, float scale, int causal, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv || !cu_seqlens_q)
     return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
@@ -197,6 +236,8 @@ int ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, 
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
+  const int ws = attach_ds(p, workspace, workspace_bytes, varlen_ds_bytes(hq, total_q, max_seqlen_q, max_seqlen_k));
+  if (ws != FFPA_OK) return ws;
   return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, total_q * hq, total_q, (hipStream_t)stream, -1));
 }
 

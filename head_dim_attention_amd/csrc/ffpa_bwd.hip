@@ -30,6 +30,17 @@ namespace ffpa {
 #ifndef BWD_AHEAD
 #define BWD_AHEAD 2
 #endif
+// Cache policy of the dS stores (written once, read once by the dQ pass).
+#ifndef DS_STORE_CPOL
+#define DS_STORE_CPOL 2
+#endif
+// Same, for the two-group dK/dQ kernel, whose MFMA phases run one wave per SIMD at a time.
+#ifndef PP_AHEAD_M1
+#define PP_AHEAD_M1 2
+#endif
+#ifndef PP_AHEAD_M2
+#define PP_AHEAD_M2 2
+#endif
 
 // ------------------------------------------------------------------------------------------------
 // Stage 1: Delta = rowsum(dO * O) in fp32 from the stored (rounded) O.
@@ -130,6 +141,9 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
   const int cg = w % NC;
   const int ow0 = o0 + rg * 32;
   const int off = sv.lk - sv.lq;
+  const bool store_ds = MODE == kDK && p.ds != nullptr;
+  DsView dsv{};
+  if (store_ds) dsv = ds_view(p, s, sv);
 
   // ---- stationary operands: lane (h, n) holds own row n, dims 16 kb + 8 h + 0..7
   const int own_row = OWN_Q ? p.q_row : p.k_row;
@@ -381,6 +395,18 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
         v2[u] = pv;
       }
       bop[r >> 3][(r & 7) >> 1] = Elt<T>::pack2(v2[0], v2[1]);
+      if constexpr (MODE == kDK) {
+        // Optionally store the rounded dS (the value the accumulating product uses) for dQ.
+        if (store_ds && oi < sv.lk) {
+          const uint32_t pk = bop[r >> 3][(r & 7) >> 1];
+          uint16_t* dsp = (uint16_t*)p.ds + dsv.base + (long long)step_head(st) * dsv.head + oi;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int qi = row0 + c_row(r + u, hh);
+            if (qi < sv.lq) dsp[(long long)qi * dsv.row] = (uint16_t)(u ? pk >> 16 : pk & 0xffff);
+          }
+        }
+      }
     }
 
     // ---- acc^T[d][own] += A[d][streamed] * B[streamed][own], A read transposed from the tile
@@ -429,42 +455,60 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
 }
 
 // ------------------------------------------------------------------------------------------------
-// dK and dQ for D <= 512 with two waves per SIMD.
+// dK and dQ for D <= 512 with two waves per SIMD, as a two-group ping-pong.
 //
-// Eight waves form NR = 2 row groups of NC = 4; a wave holds 32 stationary rows x D/4 head-dim
+// Eight waves form two row groups of NC = 4; a wave holds 32 stationary rows x D/4 head-dim
 // columns of both stationary operands and of the fp32 accumulator, which fits 256 registers.
-// The four partial score blocks of a row group are combined by a reduce-scatter: wave cg
-// finishes only the 8 streamed rows of register quarter cg (registers 4cg..4cg+3 of the C block),
-// computes dS for them, and the bf16 dS quarters are then all-gathered, so each wave does a
-// quarter of the softmax-gradient arithmetic and exchanges half the partial-sum bytes of a full
-// all-reduce. The tile read only by the partial products (dO for dK, V for dQ) has one buffer
-// and is refilled as soon as every wave has passed the exchange barrier; the tile also read by
-// the accumulating product is double-buffered. dK's per-query LSE and Delta come with the query
-// tile into LDS and are read by broadcast.
+// One step over 32 streamed rows is four phases per wave:
+//   M1a, M1b  partial S and dP over the wave's head-dim columns (split in two runs of MFMAs), then
+//             the partner quarters go to the exchange buffer;
+//   V1        reduce-scatter: wave cg finishes the 8 streamed rows of register quarter cg, computes
+//             dS for them and writes its bf16 dS quarter (a quarter of the softmax-gradient work
+//             per wave, half the partial-sum bytes of a full all-reduce);
+//   M2        all-gather of the dS quarters, then the accumulating product with its A operand read
+//             transposed from tile 1.
+// The second row group runs two phases behind the first, and every phase ends at a workgroup
+// barrier. The two waves of a SIMD (one per group) are then always in different phases: while one
+// does the exchange and the exponentials (V1) or issues the gather, the other keeps the SIMD's
+// matrix core busy, instead of both waiting on the same exchange at the same time.
+//
+//   slot:     0              1               2              3
+//   group 0:  M1a(st)        M1b(st)         V1(st)         M2(st)
+//   group 1:  V1(st-1)       M2(st-1)        M1a(st)        M1b(st)
+//
+// Buffers: tiles 1 and 2 are double-buffered; the exchange and dS-gather buffers are shared by the
+// two groups (a group writes them in one slot and reads them in the next, while the other group
+// is between its own write and read). Copies of step st + 1: tile 2 by group 0 during M1a(st),
+// tile 1 by group 1 during M1a(st) (after group 1's M2(st-1) released that buffer), dK's row
+// statistics by wave 0 at M1b(st); all complete before slot 0 of step st + 1.
 // ------------------------------------------------------------------------------------------------
 template <int NDB>
-struct RsCfg {
-  static constexpr int NC = 4, NW = 8, NR = 2;
+struct PpCfg {
+  static constexpr int NC = 4, NW = 8;
   static constexpr int DW = NDB * 32;
   static constexpr int RS = 1024;                // LDS row stride (bytes), padded head dim <= 512
-  static constexpr int BOWN = NR * 32;           // stationary rows per workgroup
+  static constexpr int BOWN = 2 * 32;            // stationary rows per workgroup
   static constexpr int TILE = 32 * RS;
   static constexpr int PIECE = 64 * 16;          // one f32x4 per lane
-  static constexpr int T2_OFF = 2 * TILE;        // single-buffered tile
-  static constexpr int X_OFF = 3 * TILE;         // [wave][3 partner quarters][S, dP] pieces
-  static constexpr int G_OFF = X_OFF + NW * 3 * 2 * PIECE;  // [wave] packed dS quarter, 8 B/lane
-  static constexpr int ST_OFF = G_OFF + NW * 64 * 8;        // [buffer][LSE, Delta] x 64 floats
+  static constexpr int T1_OFF = 0;               // [2] tile 1
+  static constexpr int T2_OFF = 2 * TILE;        // [2] tile 2
+  static constexpr int X_OFF = 4 * TILE;         // [cg][3 partner quarters][S, dP] pieces
+  static constexpr int G_OFF = X_OFF + NC * 3 * 2 * PIECE;  // [cg] packed dS quarter, 8 B/lane
+  static constexpr int ST_OFF = G_OFF + NC * 64 * 8;        // [buffer][LSE, Delta] x 64 floats
   static constexpr int LDS = ST_OFF + 2 * 2 * 256;
-  static constexpr int NINSTR = TILE / 1024 / NW;
+  static constexpr int NCOPY = TILE / 1024 / 4;  // copies per wave of a tile (one group copies it)
+  static constexpr int KSTEPS = 2 * NDB;         // k-steps of the partial products
+  static constexpr int KA = (3 * KSTEPS) / 4;    // k-steps in M1a (M1b shares its slot with M2)
   static_assert(4 * DW <= 512 && LDS <= 160 * 1024, "LDS budget");
 };
 
-template <class T, int MODE, int NDB>
-__global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
+template <class T, int MODE, int NDB, bool STORE_DS>
+__global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
   static_assert(MODE == kDQ || MODE == kDK, "dK and dQ only");
+  static_assert(!STORE_DS || MODE == kDK, "dS is stored by the dK kernel");
   constexpr bool OWN_Q = MODE == kDQ;
-  using C = RsCfg<NDB>;
-  constexpr int NC = C::NC, NW = C::NW;
+  using C = PpCfg<NDB>;
+  constexpr int NC = C::NC;
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
   lds_t* smem = (lds_t*)smem_raw;
 
@@ -482,14 +526,17 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
   const int own_len = OWN_Q ? sv.lq : sv.lk;
   const int o0 = t * C::BOWN;
   if (o0 >= own_len) return;
+  // dK can also store dS for a dQ pass that multiplies it by K (no recomputation there).
+  DsView dsv{};
+  if constexpr (STORE_DS) dsv = ds_view(p, s, sv);
 
   const int w = wave_id();
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5;
   const int l32 = lane & 31;
-  const int rg = w / NC;
-  const int cg = w % NC;
-  const int ow0 = o0 + rg * 32;
+  const int grp = w >> 2;  // 0: leading row group, 1: trailing row group
+  const int cg = w & 3;
+  const int ow0 = o0 + grp * 32;
   const int off = sv.lk - sv.lq;
 
   // ---- stationary operands: lane (h, n) holds own row n, dims 16 kb + 8 h + 0..7
@@ -497,11 +544,11 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
   const long long own_base = OWN_Q ? sv.q_off + (long long)hd * p.q_head : sv.k_off + (long long)hd * p.k_head;
   const uint16_t* r1src = (const uint16_t*)(OWN_Q ? p.q : p.k) + own_base;
   const uint16_t* r2src = (const uint16_t*)(OWN_Q ? p.dout : p.v) + own_base;
-  u32x4_t r1[2 * NDB], r2[2 * NDB];
+  u32x4_t r1[C::KSTEPS], r2[C::KSTEPS];
   {
     const long long oi = min(ow0 + l32, own_len - 1);
 #pragma unroll
-    for (int kb = 0; kb < 2 * NDB; ++kb) {
+    for (int kb = 0; kb < C::KSTEPS; ++kb) {
       const int dim = cg * C::DW + kb * 16 + hh * 8;
       const bool in = dim < p.d;
       r1[kb] = in ? *(const u32x4_t*)(r1src + oi * own_row + dim) : (u32x4_t){0u, 0u, 0u, 0u};
@@ -542,15 +589,16 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
   };
   const uint32_t span = (uint32_t)min((long long)max(str_len, 1) * row_bytes, (long long)0xFFFFFFF0);
   const int dch = p.d >> 3;
-  int voff[C::NINSTR];
+  // Copy ii of this wave fills tile row i = cg + 4 ii; lane l writes physical chunk l, holding
+  // logical chunk l ^ swz(i) (clamped into the head dim). swz(i) depends on ii % 4 only.
+  int voff[4];
 #pragma unroll
-  for (int ii = 0; ii < C::NINSTR; ++ii) voff[ii] = min(lane ^ swz(w + NW * ii), dch - 1) << 4;
+  for (int ii = 0; ii < 4; ++ii) voff[ii] = min(lane ^ swz(cg + 4 * ii), dch - 1) << 4;
 
-  // Copies of step st: tile 1 (K for dQ, Q for dK) into buffer buf, tile 2 (V for dQ, dO for dK)
-  // into its single buffer, and dK's row statistics. A step index past the end is clamped to the
-  // last step (its copies then land in buffers that are not read again).
+  // Source of step st (clamped to the last step: copies past the end land in buffers that are not
+  // read again). This group's tile: tile 2 for group 0, tile 1 for group 1.
   struct StepSrc {
-    i32x4_t r1, r2;
+    i32x4_t rs;
     int row0, head;
   };
   auto step_src = [&](int st) {
@@ -558,33 +606,26 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
     StepSrc x;
     x.head = step_head(st);
     x.row0 = step_row0(st);
-    x.r1 = make_rsrc((const uint16_t*)(OWN_Q ? p.k : p.q) + str_base(x.head), span);
-    x.r2 = make_rsrc((const uint16_t*)(OWN_Q ? p.v : p.dout) + str_base(x.head), span);
+    const uint16_t* src = grp == 0 ? (const uint16_t*)(OWN_Q ? p.v : p.dout) : (const uint16_t*)(OWN_Q ? p.k : p.q);
+    x.rs = make_rsrc(src + str_base(x.head), span);
     return x;
   };
-  auto copy_t1 = [&](const StepSrc& x, int buf, int ii) {
-    const int i = w + NW * ii;
-    dma16_buf(x.r1, voff[ii], min(x.row0 + i, str_len - 1) * row_bytes, smem + buf * C::TILE + i * 1024);
+  auto copy_tile = [&](const StepSrc& x, int buf, int ii) {
+    const int i = cg + 4 * ii;
+    lds_t* dst = smem + (grp == 0 ? C::T2_OFF : C::T1_OFF) + buf * C::TILE + i * 1024;
+    dma16_buf(x.rs, voff[ii & 3], min(x.row0 + i, str_len - 1) * row_bytes, dst);
   };
-  auto copy_t2 = [&](const StepSrc& x, int ii) {
-    const int i = w + NW * ii;
-    dma16_buf(x.r2, voff[ii], min(x.row0 + i, str_len - 1) * row_bytes, smem + C::T2_OFF + i * 1024);
-  };
-  auto copy_stats = [&](const StepSrc& x, int buf) {
+  auto copy_stats = [&](int st, int buf) {
     if constexpr (!OWN_Q) {
-      if (w == 0) {
-        const long long li = sv.lse_off + (long long)x.head * p.lse_head;
-        const uint32_t bytes = (uint32_t)max(sv.lq, 1) * 4;
-        const int vo = min(x.row0 + l32, sv.lq - 1) * 4;
-        lds_t* sd = smem + C::ST_OFF + buf * 512;
-        dma4_buf(make_rsrc(p.lse_in + li, bytes), vo, sd);
-        dma4_buf(make_rsrc(p.delta + li, bytes), vo, sd + 256);
-      }
+      st = min(st, nsteps - 1);
+      const long long li = sv.lse_off + (long long)step_head(st) * p.lse_head;
+      const uint32_t bytes = (uint32_t)max(sv.lq, 1) * 4;
+      const int vo = min(step_row0(st) + l32, sv.lq - 1) * 4;
+      lds_t* sd = smem + C::ST_OFF + buf * 512;
+      dma4_buf(make_rsrc(p.lse_in + li, bytes), vo, sd);
+      dma4_buf(make_rsrc(p.delta + li, bytes), vo, sd + 256);
     }
   };
-  // MFMA index (of a run of n) after which copy ii is issued: the copy path moves about 64 B per
-  // clock per CU, so a whole tile issued at once would hold every wave at the issue.
-  auto spread_at = [](int n, int ii) { return (ii * n) / C::NINSTR; };
 
   // Register quarter i of the C block (registers 4i..4i+3) covers tile rows 16 (i/2) + 8 h +
   // 4 (i%2) + 0..3. Wave cg reads its A operand with the quarter bits of the row index (bits 4
@@ -625,81 +666,84 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
   lds_t* const gbuf = smem + C::G_OFF;
   // Rows of this wave's register quarter, relative to the tile: 16 (cg/2) + 8 h + 4 (cg%2) + 0..3.
   const int qrow = 16 * (cg >> 1) + 8 * hh + 4 * (cg & 1);
+  auto t1_addr = [&](int st) { return lds_addr(smem + C::T1_OFF + (st & 1) * C::TILE); };
+  auto t2_addr = [&](int st) { return lds_addr(smem + C::T2_OFF + (st & 1) * C::TILE); };
+  // MFMA index (of a run of n) after which copy ii is issued: the copy path moves about 64 B per
+  // clock per CU, so a whole tile issued at once would hold the waves at the issue.
+  auto spread_at = [](int n, int ii) { return (ii * n) / C::NCOPY; };
 
-  if (nsteps > 0) {
-    const StepSrc x0 = step_src(0);
-    copy_stats(x0, 0);
-#pragma unroll
-    for (int ii = 0; ii < C::NINSTR; ++ii) {
-      copy_t1(x0, 0, ii);
-      copy_t2(x0, ii);
-    }
-  }
-  wait_all();  // stationary operands, dQ's row statistics and the first tiles
+  f32x16_t sacc, dpacc;
+  f32x4_t sq_own, dq_own;  // this wave's own quarter of the partial S and dP, kept for V1
+  uint32_t bop[2][4];
 
-  // The copies of step st + 1 are issued during step st: its statistics after barrier A, tile 1
-  // spread over the partial products (its other buffer was released at barrier A), tile 2 right
-  // after barrier B, which releases its single buffer (as early as possible, so that it lands
-  // before step st + 1). All are waited for before barrier A of step st + 1.
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    wait_vmcnt<0>();
-    lds_barrier();  // (A) this step's tiles are visible; every wave has finished the last step
+  // ---- phase M1a: first KA k-steps of the partial products, with this group's copies of st + 1
+  auto m1a = [&](int st) {
+    const uint32_t t1 = t1_addr(st), t2 = t2_addr(st);
     const StepSrc xn = step_src(st + 1);
-    copy_stats(xn, buf ^ 1);
-    const uint32_t t1 = lds_addr(smem + buf * C::TILE);
-    const uint32_t t2 = lds_addr(smem + C::T2_OFF);
-    const int row0 = step_row0(st);
-
-    // ---- partial S and dP over this wave's head-dim columns: C[streamed row][own row]
-    f32x16_t sacc = (f32x16_t){}, dpacc = (f32x16_t){};
+    const int nb = (st + 1) & 1;
+    sacc = (f32x16_t){};
+    dpacc = (f32x16_t){};
 #pragma unroll
-    for (int kb = 0; kb < 2 * NDB; ++kb) {
+    for (int kb = 0; kb < C::KA; ++kb) {
       sacc = Elt<T>::mma(lds_read_b128_at(a_addr(t1, kb)), r1[kb], sacc);
       dpacc = Elt<T>::mma(lds_read_b128_at(a_addr(t2, kb)), r2[kb], dpacc);
 #pragma unroll
-      for (int ii = 0; ii < C::NINSTR; ++ii)
-        if (kb == spread_at(2 * NDB, ii)) copy_t1(xn, buf ^ 1, ii);
+      for (int ii = 0; ii < C::NCOPY; ++ii)
+        if (kb == spread_at(C::KA, ii)) copy_tile(xn, nb, ii);
     }
-    pin_lds_mfma_pipeline<4 * NDB, 2, 1>();
-    // Partner quarters to the exchange: slot j holds register quarter j + 1, i.e. quarter
-    // (cg + 1 + j) % 4.
+    pin_lds_mfma_pipeline<2 * C::KA, PP_AHEAD_M1, 1>();
+  };
+  // ---- phase M1b: remaining k-steps, then the partner quarters to the exchange buffer
+  auto m1b = [&](int st) {
+    if (grp == 0 && w == 0) copy_stats(st + 1, (st + 1) & 1);
+    const uint32_t t1 = t1_addr(st), t2 = t2_addr(st);
+#pragma unroll
+    for (int kb = C::KA; kb < C::KSTEPS; ++kb) {
+      sacc = Elt<T>::mma(lds_read_b128_at(a_addr(t1, kb)), r1[kb], sacc);
+      dpacc = Elt<T>::mma(lds_read_b128_at(a_addr(t2, kb)), r2[kb], dpacc);
+    }
+    pin_lds_mfma_pipeline<2 * (C::KSTEPS - C::KA), (PP_AHEAD_M1 < 2 * (C::KSTEPS - C::KA) ? PP_AHEAD_M1 : 2 * (C::KSTEPS - C::KA)), 1>();
+    // Slot j holds register quarter j + 1, i.e. quarter (cg + 1 + j) % 4.
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       const int q = j + 1;
-      const int base = ((w * 3 + j) * 2) * C::PIECE + lane * 16;
+      const int base = ((cg * 3 + j) * 2) * C::PIECE + lane * 16;
       lds_write_f4(xbuf, base, (f32x4_t){sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]});
       lds_write_f4(xbuf, base + C::PIECE,
                    (f32x4_t){dpacc[4 * q], dpacc[4 * q + 1], dpacc[4 * q + 2], dpacc[4 * q + 3]});
     }
-    lds_barrier();  // (B) partial sums visible; every wave has finished reading tile 2
-#pragma unroll
-    for (int ii = 0; ii < C::NINSTR; ++ii) copy_t2(xn, ii);
-
-    // ---- reduce this wave's quarter: own part + partners in a fixed order
-    f32x4_t sq = (f32x4_t){sacc[0], sacc[1], sacc[2], sacc[3]};
-    f32x4_t dq = (f32x4_t){dpacc[0], dpacc[1], dpacc[2], dpacc[3]};
+    sq_own = (f32x4_t){sacc[0], sacc[1], sacc[2], sacc[3]};
+    dq_own = (f32x4_t){dpacc[0], dpacc[1], dpacc[2], dpacc[3]};
+  };
+  // ---- phase V1: reduce this wave's quarter (own part + partners in a fixed order), P and dS
+  u32x2_t mine;
+  // dS row piece of this lane, its byte offset and the head block's buffer resource: formed in V1,
+  // stored at the start of M2 (so V1 does not wait for the transposed reads).
+  u32x4_t ds_piece = {0u, 0u, 0u, 0u};
+  uint32_t ds_boff = 0xFFFFFFF0u;
+  __amdgpu_buffer_rsrc_t ds_rs = __builtin_amdgcn_make_buffer_rsrc(p.dq, 0, 0, 0x00020000);
+  auto v1 = [&](int st) {
+    f32x4_t sq = sq_own, dq = dq_own;
 #pragma unroll
     for (int i = 1; i < 4; ++i) {
-      const int pc = (cg + i) & 3;            // partner column group
-      const int j = ((cg - pc) & 3) - 1;      // its slot holding quarter cg
-      const int base = (((rg * NC + pc) * 3 + j) * 2) * C::PIECE + lane * 16;
+      const int pc = (cg + i) & 3;        // partner column group
+      const int j = ((cg - pc) & 3) - 1;  // its slot holding quarter cg
+      const int base = ((pc * 3 + j) * 2) * C::PIECE + lane * 16;
       sq = sq + lds_read_f4(xbuf, base);
       dq = dq + lds_read_f4(xbuf, base + C::PIECE);
     }
-
-    // ---- P and dS for the 4 (streamed, own) pairs of this lane's quarter
     f32x4_t lse2q, dltq;
     if constexpr (OWN_Q) {
       lse2q = (f32x4_t){lse2_own, lse2_own, lse2_own, lse2_own};
       dltq = (f32x4_t){dlt_own, dlt_own, dlt_own, dlt_own};
     } else {
-      const lds_t* sd = smem + C::ST_OFF + buf * 512;
+      const lds_t* sd = smem + C::ST_OFF + (st & 1) * 512;
       const f32x4_t lr = lds_read_f4(sd, qrow * 4);
       dltq = lds_read_f4(sd, 256 + qrow * 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) lse2q[i] = lr[i] == -INFINITY ? INFINITY : lr[i] * kLog2e;
     }
+    const int row0 = step_row0(st);
     const int oi = ow0 + l32;
     bool need_mask;
     if constexpr (OWN_Q) {
@@ -720,21 +764,41 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
       }
       ds[i] = pv * (dq[i] - dltq[i]);
     }
-    const u32x2_t mine = {Elt<T>::pack2(ds[0], ds[1]), Elt<T>::pack2(ds[2], ds[3])};
-    *(__attribute__((address_space(3))) u32x2_t*)(gbuf + w * 512 + lane * 8) = mine;
-    lds_barrier();  // (C) dS quarters visible
-
-    // ---- all-gather dS: quarter q gives B-operand words 2 (q % 2), +1 of k-block q / 2
-    uint32_t bop[2][4];
+    mine = (u32x2_t){Elt<T>::pack2(ds[0], ds[1]), Elt<T>::pack2(ds[2], ds[3])};
+    *(__attribute__((address_space(3))) u32x2_t*)(gbuf + cg * 512 + lane * 8) = mine;
+    if constexpr (STORE_DS) {
+      // Store the rounded dS the accumulating product uses, dS[query][key], as 16-byte row pieces.
+      // The wave's quarter, just written to the gather buffer (lane (h, key n): 4 query rows),
+      // is read back transposed: in 16-lane group g (g = 0, 1 <-> h = g) source lane s = t + 4 m
+      // points at key 8 t + m (first read) or 8 t + 4 + m (second), so lane i receives keys
+      // 8 (i/4) + 0..7 of query row qrow(g) + i%4. Lanes 32..63 and pieces outside the sequence
+      // (rows >= Lq, or starting at or past the padded row end) get an offset past the block, which
+      // the buffer range check discards.
+      const int g = (lane >> 4) & 1, sl = lane & 15, i16 = lane & 15;
+      const lds_t* gq = gbuf + cg * 512 + (32 * g + 8 * (sl & 3) + (sl >> 2)) * 8;
+      ds_piece = join_tr(lds_read_tr16(gq, 0), lds_read_tr16(gq, 32));
+      const int rq = row0 + 16 * (cg >> 1) + 8 * g + 4 * (cg & 1) + (i16 & 3);
+      const int key0 = ow0 + 8 * (i16 >> 2);
+      const bool ok = lane < 32 && rq < sv.lq && key0 < dsv.row;
+      ds_boff = ok ? (uint32_t)((rq * dsv.row + key0) * 2) : 0xFFFFFFF0u;
+      uint16_t* head_blk = (uint16_t*)p.ds + dsv.base + (long long)step_head(st) * dsv.head;
+      ds_rs = __builtin_amdgcn_make_buffer_rsrc(head_blk, 0, (int)((long long)sv.lq * dsv.row * 2), 0x00020000);
+    }
+  };
+  // ---- phase M2: all-gather dS (quarter q gives B-operand words 2 (q % 2), +1 of k-block q / 2),
+  // then acc^T[d][own] += A[d][streamed] * dS[streamed][own], A read transposed from tile 1
+  auto m2 = [&](int st) {
+    if constexpr (STORE_DS)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, ds_piece), ds_rs, (int)ds_boff, 0,
+                                             DS_STORE_CPOL);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       u32x2_t v = mine;
-      if (q != cg) v = *(const __attribute__((address_space(3))) u32x2_t*)(gbuf + (rg * NC + q) * 512 + lane * 8);
+      if (q != cg) v = *(const __attribute__((address_space(3))) u32x2_t*)(gbuf + q * 512 + lane * 8);
       bop[q >> 1][2 * (q & 1)] = v.x;
       bop[q >> 1][2 * (q & 1) + 1] = v.y;
     }
-
-    // ---- acc^T[d][own] += A[d][streamed] * dS[streamed][own], A read transposed from tile 1
+    const uint32_t t1 = t1_addr(st);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -745,7 +809,54 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
         acc[db] = Elt<T>::mma(join_tr(lo, hi), bv, acc[db]);
       }
     }
-    pin_lds_mfma_pipeline<2 * NDB, 2, 2>();
+    pin_lds_mfma_pipeline<2 * NDB, PP_AHEAD_M2, 2>();
+  };
+
+  if (nsteps > 0) {
+    const StepSrc x0 = step_src(0);
+#pragma unroll
+    for (int ii = 0; ii < C::NCOPY; ++ii) copy_tile(x0, 0, ii);
+    if (w == 0) copy_stats(0, 0);
+  }
+  wait_all();  // stationary operands, dQ's row statistics and the tiles of step 0
+  lds_barrier();
+
+  // Each group runs its own straight-line loop of four phases per step, so that its accumulators
+  // stay in place; both run 4 nsteps + 2 barriers, group 1 two slots later than group 0. Every
+  // copy of step st + 1 has been issued by the end of slot 3 of step st (group 0 in its M1a,
+  // group 1 in its M1a two slots later): each wave completes its own before that barrier.
+  if (nsteps > 0) {
+    if (grp == 0) {
+      for (int st = 0; st < nsteps; ++st) {
+        m1a(st);
+        lds_barrier();
+        m1b(st);
+        lds_barrier();
+        v1(st);
+        lds_barrier();
+        m2(st);
+        // Issued since the last wait, in order: the tile copies (M1a), the row statistics (M1b) and,
+        // when dS is stored, its store (M2): that one may stay in flight.
+        wait_vmcnt<STORE_DS ? 1 : 0>();
+        lds_barrier();
+      }
+      lds_barrier();
+      lds_barrier();
+    } else {
+      lds_barrier();
+      lds_barrier();
+      for (int st = 0; st < nsteps; ++st) {
+        m1a(st);
+        lds_barrier();
+        m1b(st);
+        wait_vmcnt<0>();
+        lds_barrier();
+        v1(st);
+        lds_barrier();
+        m2(st);
+        lds_barrier();
+      }
+    }
   }
   // Copies issued during the last step land in LDS that the next workgroup may own.
   wait_vmcnt<0>();
@@ -770,14 +881,258 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_rs_kernel(AttnParams p) {
 }
 
 template <class T, int MODE, int NDB>
-static hipError_t launch_bwd_rs(AttnParams p, hipStream_t st) {
-  using C = RsCfg<NDB>;
+static hipError_t launch_bwd_pp(AttnParams p, hipStream_t st) {
+  using C = PpCfg<NDB>;
   p.ntiles = ((MODE == kDQ ? p.nq : p.nkv) + C::BOWN - 1) / C::BOWN;
   p.total = p.batch * (MODE == kDQ ? p.hq : p.hkv) * p.ntiles;
   if (p.total == 0) return hipSuccess;
   const int grid = (p.total + 7) & ~7;
-  hipLaunchKernelGGL((ffpa_bwd_rs_kernel<T, MODE, NDB>), dim3(grid), dim3(64 * C::NW), 0, st, p);
+  if (MODE == kDK && p.ds != nullptr)
+    hipLaunchKernelGGL((ffpa_bwd_pp_kernel<T, kDK, NDB, true>), dim3(grid), dim3(64 * C::NW), 0, st, p);
+  else
+    hipLaunchKernelGGL((ffpa_bwd_pp_kernel<T, MODE, NDB, false>), dim3(grid), dim3(64 * C::NW), 0, st, p);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------
+// dQ from a stored dS: dQ_i = scale * sum_j dS_ij K_j (fp32 accumulation, one rounding).
+//
+// With dS written by the dK kernel (same rounding as the value its own product uses), the dQ stage
+// is a plain product instead of a recomputation of S, P, dP and dS: 2 D flops per legal pair
+// instead of 6 D, for dense B * Hq * Nq * Nkv dS elements of HBM workspace. A workgroup owns 128
+// queries of one head and one chunk of up to 512 head-dim columns; its 8 waves are 2 query groups
+// x 4 column groups, each wave 64 queries (two 32-row MFMA blocks) x DW columns of fp32
+// accumulators. Per step of 32 keys the K rows of the chunk (32 x 1 KB, swizzled as elsewhere)
+// and the 128 x 32 dS block (64-byte rows, 16-byte chunks XOR-swizzled by bits 2-3 of the row)
+// are copied into LDS, double-buffered, with the next step's copies spread over the current
+// step's MFMAs. acc^T[d][q] += K^T[d][k] dS^T[k][q]: K^T is read transposed (ds_read_b64_tr_b16)
+// and used for both query blocks; dS^T is one 16-byte row read per query block and k-block.
+// Causal and ragged tiles mask dS to 0 where the key is not legal (those entries were not
+// written by the dK kernel).
+// ------------------------------------------------------------------------------------------------
+template <int NDB>
+struct DqCfg {
+  static constexpr int NW = 8;
+  static constexpr int QB = 2;                 // 32-query MFMA blocks per wave
+  static constexpr int DW = NDB * 32;          // head-dim columns per wave
+  static constexpr int DWG = 4 * DW;           // head-dim columns per workgroup (one chunk)
+  static constexpr int BQ = 2 * QB * 32;       // queries per workgroup
+  static constexpr int RS = 1024;              // K tile row stride (bytes)
+  static constexpr int KTILE = 32 * RS;
+  static constexpr int STILE = BQ * 64;        // dS block: BQ rows x 32 keys x 2 bytes
+  static constexpr int STAGE = KTILE + STILE;
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int KCOPY = KTILE / 1024 / NW;  // K copies per wave per step
+  static constexpr int SCOPY = STILE / 1024 / NW;  // dS copies per wave per step
+  static_assert(DWG <= 512 && SCOPY >= 1 && LDS <= 160 * 1024, "tile budget");
+};
+
+template <class T, int NDB>
+__global__ void __launch_bounds__(512, 2) ffpa_dq_from_ds_kernel(AttnParams p, int nchunk) {
+  using C = DqCfg<NDB>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
+  lds_t* smem = (lds_t*)smem_raw;
+
+  const int L = blockIdx.x;
+  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  if (item >= p.total) return;
+  const int qt = item % p.ntiles;
+  const int rest = item / p.ntiles;
+  const int chunk = rest % nchunk;
+  const int hs = rest / nchunk;
+  const int h = hs % p.hq;
+  const int s = hs / p.hq;
+
+  const SeqView sv = seq_view(p, s);
+  const int q0 = qt * C::BQ;
+  if (q0 >= sv.lq) return;
+  const DsView dsv = ds_view(p, s, sv);
+  const int kvh = h / p.group;
+  const int d0 = chunk * C::DWG;
+
+  const int w = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int qg = w >> 2;
+  const int dg = w & 3;
+  const int off = sv.lk - sv.lq;
+
+  int kend = sv.lk;
+  if (p.causal) kend = min(kend, q0 + C::BQ + off);
+  const int nsteps = kend > 0 ? (kend + 31) >> 5 : 0;
+
+  f32x16_t acc[C::QB][NDB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[qb][db] = (f32x16_t){};
+
+  // ---- copies. K rows of this chunk: copy ii of wave w fills tile row i = w + 8 ii; lane l writes
+  // physical chunk l, holding logical chunk l ^ swz(i) of the chunk (clamped into the head dim).
+  const char* kbase = (const char*)p.k + 2 * (sv.k_off + (long long)kvh * p.k_head);
+  const int krow_bytes = p.k_row * 2;
+  const i32x4_t krs = make_rsrc(kbase, (uint32_t)min((long long)max(sv.lk, 1) * krow_bytes, (long long)0xFFFFFFF0));
+  const int dch = p.d >> 3;
+  int kvoff[C::KCOPY];
+#pragma unroll
+  for (int ii = 0; ii < C::KCOPY; ++ii) kvoff[ii] = min((d0 >> 3) + (lane ^ swz(w + 8 * ii)), dch - 1) << 4;
+  // dS rows: copy ii of wave w fills block rows 16 i .. 16 i + 15, i = w + 8 ii; lane l writes
+  // row 16 i + l / 4, physical chunk l % 4 = logical chunk (l % 4) ^ ((row >> 2) & 3). The whole
+  // byte offset goes in the per-lane operand, which the buffer range check covers: pieces past the
+  // head's block (the last step's keys beyond the padded row of the last row) read as 0. The
+  // block size is a multiple of 16 bytes, so no piece straddles its end.
+  const uint16_t* dsh = (const uint16_t*)p.ds + dsv.base + (long long)h * dsv.head;
+  const i32x4_t srs = make_rsrc(dsh, (uint32_t)((long long)sv.lq * dsv.row * 2));
+  int svoff[C::SCOPY];
+#pragma unroll
+  for (int ii = 0; ii < C::SCOPY; ++ii) {
+    const int r = 16 * (w + 8 * ii) + (lane >> 2);
+    const int qrow = min(q0 + r, sv.lq - 1);
+    svoff[ii] = qrow * dsv.row * 2 + ((((lane & 3) ^ ((r >> 2) & 3))) << 4);
+  }
+  auto copy = [&](int j, int buf, int c) {
+    lds_t* stage = smem + buf * C::STAGE;
+    if (c < C::KCOPY) {
+      const int i = w + 8 * c;
+      dma16_buf(krs, kvoff[c], min(j * 32 + i, sv.lk - 1) * krow_bytes, stage + i * 1024);
+    } else {
+      const int ii = c - C::KCOPY;
+      dma16_buf(srs, svoff[ii] + j * 64, 0, stage + C::KTILE + (w + 8 * ii) * 1024);
+    }
+  };
+  constexpr int NCOPY = C::KCOPY + C::SCOPY;
+  constexpr int NMMA = 2 * NDB * C::QB;
+  auto spread_at = [](int c) { return (c * NMMA) / NCOPY; };
+
+  // ---- operand addresses. K^T (A operand) by transposed reads as in the other kernels; the
+  // chunk's column base inside the tile is dg * DW (tile columns are chunk-relative).
+  const int g16 = lane >> 4;
+  const int r16 = lane & 15;
+  const int cbase = dg * C::DW >> 3;
+  const int tclo = 2 * (g16 & 1) + ((r16 & 3) >> 1);
+  const int twithin = ((4 * (r16 & 3)) & 7) << 1;
+  constexpr bool kAligned = (C::DW % 128) == 0;
+  uint32_t tlane[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int k = 8 * hh + 4 * half + (r16 >> 2);
+    tlane[half] = k * C::RS + (cbase << 4) + ((tclo ^ swz(k)) << 4) + twithin;
+  }
+  auto t_addr = [&](uint32_t tile, int db, int kb2, int half) -> uint32_t {
+    if constexpr (kAligned)
+      return ((tile + tlane[half]) ^ ((db & 3) << 6)) + ((db >> 2) << 8) + kb2 * 16 * C::RS;
+    const int k = 16 * kb2 + 8 * hh + 4 * half + (r16 >> 2);
+    return tile + k * C::RS + (((cbase + 4 * db + tclo) ^ swz(k)) << 4) + twithin;
+  };
+  // dS^T (B operand): lane (h, n) reads query row r = 64 qg + 32 qb + n, keys 16 kb2 + 8 h + 0..7,
+  // i.e. logical chunk 2 kb2 + h of the row.
+  auto s_addr = [&](uint32_t tile, int qb, int kb2) -> uint32_t {
+    const int r = 64 * qg + 32 * qb + l32;
+    return tile + C::KTILE + r * 64 + (((2 * kb2 + hh) ^ ((r >> 2) & 3)) << 4);
+  };
+
+  if (nsteps > 0) {
+#pragma unroll
+    for (int c = 0; c < NCOPY; ++c) copy(0, 0, c);
+  }
+  wait_all();
+
+  for (int j = 0; j < nsteps; ++j) {
+    const int buf = j & 1;
+    wait_vmcnt<0>();
+    lds_barrier();  // step j's tiles are visible; every wave has finished step j - 1
+    const uint32_t tile = lds_addr(smem + buf * C::STAGE);
+    const int jn = min(j + 1, nsteps - 1);  // past the end: a harmless re-copy into the free buffer
+
+    // dS^T operands of both query blocks; masked where the key is not legal.
+    u32x4_t bs[C::QB][2];
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) bs[qb][kb2] = lds_read_b128_at(s_addr(tile, qb, kb2));
+    const bool need_mask = (j * 32 + 32 > sv.lk) || (p.causal && j * 32 + 31 > q0 + 64 * qg + off);
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        const int qi = q0 + 64 * qg + 32 * qb + l32;
+        const int lim = p.causal ? min(qi + off, sv.lk - 1) : sv.lk - 1;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int k0 = j * 32 + 16 * kb2 + 8 * hh + 2 * e;
+            uint32_t x = bs[qb][kb2][e];
+            if (k0 > lim) x &= 0xffff0000u;
+            if (k0 + 1 > lim) x &= 0x0000ffffu;
+            bs[qb][kb2][e] = x;
+          }
+      }
+    }
+    int mi = 0;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const s16x4_t lo = lds_read_tr16_at(t_addr(tile, db, kb2, 0));
+        const s16x4_t hi = lds_read_tr16_at(t_addr(tile, db, kb2, 1));
+        const u32x4_t a = join_tr(lo, hi);
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb) {
+          acc[qb][db] = Elt<T>::mma(a, bs[qb][kb2], acc[qb][db]);
+#pragma unroll
+          for (int c = 0; c < NCOPY; ++c)
+            if (mi == spread_at(c)) copy(jn, buf ^ 1, c);
+          ++mi;
+        }
+      }
+    }
+  }
+  // Copies issued during the last step land in LDS that the next workgroup may own.
+  wait_vmcnt<0>();
+
+  // ---- epilogue: scale, round once, store rows < lq and columns < D
+  uint16_t* dqh = (uint16_t*)p.dq + sv.q_off + (long long)h * p.q_head;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int qi = q0 + 64 * qg + 32 * qb + l32;
+    if (qi < sv.lq) {
+      uint16_t* dst = dqh + (long long)qi * p.q_row;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = d0 + dg * C::DW + 32 * db + 8 * i4 + 4 * hh;
+          if (d < p.d) {
+            const f32x16_t& a = acc[qb][db];
+            const u32x2_t pk = {Elt<T>::pack2(a[4 * i4] * p.scale, a[4 * i4 + 1] * p.scale),
+                                Elt<T>::pack2(a[4 * i4 + 2] * p.scale, a[4 * i4 + 3] * p.scale)};
+            *(u32x2_t*)(dst + d) = pk;
+          }
+        }
+    }
+  }
+}
+
+template <class T, int NDB>
+static hipError_t launch_dq_from_ds(AttnParams p, int nchunk, hipStream_t st) {
+  using C = DqCfg<NDB>;
+  p.ntiles = (p.nq + C::BQ - 1) / C::BQ;
+  p.total = p.batch * p.hq * nchunk * p.ntiles;
+  if (p.total == 0) return hipSuccess;
+  const int grid = (p.total + 7) & ~7;
+  hipLaunchKernelGGL((ffpa_dq_from_ds_kernel<T, NDB>), dim3(grid), dim3(64 * C::NW), 0, st, p, nchunk);
+  return hipGetLastError();
+}
+
+// Head-dim chunking of the dQ-from-dS pass: chunks of at most 512 columns, each covered by four
+// waves of 96 or 128 columns.
+template <class T>
+static hipError_t launch_dq_ds_t(const AttnParams& p, hipStream_t st) {
+  const int nchunk = (p.d + 511) / 512;
+  const int per = (p.d + nchunk - 1) / nchunk;
+  if (per <= 384) return launch_dq_from_ds<T, 3>(p, nchunk, st);
+  return launch_dq_from_ds<T, 4>(p, nchunk, st);
 }
 
 template <class T, int MODE, int NC, int NDB>
@@ -801,8 +1156,8 @@ template <class T, int MODE>
 static hipError_t launch_bwd_mode(const AttnParams& p, hipStream_t st) {
   if constexpr (MODE != kDV) {
     if (p.d <= 512) {
-      if (p.d > 384) return launch_bwd_rs<T, MODE, 4>(p, st);
-      return launch_bwd_rs<T, MODE, 3>(p, st);
+      if (p.d > 384) return launch_bwd_pp<T, MODE, 4>(p, st);
+      return launch_bwd_pp<T, MODE, 3>(p, st);
     }
   }
   if (p.d <= 512) {
@@ -832,8 +1187,8 @@ static hipError_t launch_stage_t(int stage, const AttnParams& p, int nrows, int 
       }
       return hipSuccess;
     case 1: return launch_bwd_mode<T, kDV>(p, st);
-    case 2: return launch_bwd_mode<T, kDK>(p, st);
-    default: return launch_bwd_mode<T, kDQ>(p, st);
+    case 2: return launch_bwd_mode<T, kDK>(p, st);  // also stores dS when p.ds is set
+    default: return p.ds != nullptr ? launch_dq_ds_t<T>(p, st) : launch_bwd_mode<T, kDQ>(p, st);
   }
 }
 

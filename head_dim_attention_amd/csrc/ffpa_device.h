@@ -268,4 +268,29 @@ __device__ __forceinline__ SeqView seq_view(const AttnParams& p, int s) {
   return v;
 }
 
+// Stored-dS geometry of slice s: element offset of (s, head 0, row 0, key 0), the head stride and
+// the row stride (keys padded to a multiple of 8 elements, so 16-byte pieces stay aligned).
+struct DsView {
+  long long base, head;
+  int row;
+};
+
+__device__ __forceinline__ int round_up8(int x) { return (x + 7) & ~7; }
+
+__device__ __forceinline__ DsView ds_view(const AttnParams& p, int s, const SeqView& sv) {
+  DsView v;
+  if (p.cu_q != nullptr) {
+    long long pre = 0;
+    for (int t = 0; t < s; ++t) pre += (long long)(p.cu_q[t + 1] - p.cu_q[t]) * round_up8(p.cu_k[t + 1] - p.cu_k[t]);
+    v.row = round_up8(sv.lk);
+    v.head = (long long)sv.lq * v.row;
+    v.base = pre * p.hq;
+  } else {
+    v.row = p.ds_row;
+    v.head = p.ds_head;
+    v.base = (long long)s * p.ds_batch;
+  }
+  return v;
+}
+
 }  // namespace ffpa

@@ -21,6 +21,13 @@ struct AttnParams {
   void* dv;
   const int32_t* cu_q;  // varlen: [batch+1]; NULL for dense
   const int32_t* cu_k;
+  // Stored dS (same dtype as q), or NULL. Row (b or sequence s, query head h, query i) holds keys
+  // 0..nkv-1 padded to ds_row = round_up(nkv, 8) elements. Dense: element offset
+  // b * ds_batch + h * ds_head + i * ds_row + j. Varlen: sequence s starts at hq * P_s with
+  // P_s = sum over earlier sequences of Lq * round_up(Lk, 8), head h at + h * Lq_s * round_up(Lk_s, 8).
+  void* ds;
+  long long ds_batch, ds_head;
+  int ds_row;
   // Dense strides in elements (unused for varlen except row/head strides).
   long long q_batch, k_batch, lse_batch;
   int q_row, q_head, k_row, k_head, lse_head;

@@ -32,10 +32,22 @@
  *   - Return value: an ffpa_status_t. Arguments are validated on the host before anything is
  *     enqueued; a non-OK status means nothing was launched. FFPA_ERR_HIP reports a failed launch.
  *   - Inputs are assumed finite. Buffers may not alias each other except q/k/v among themselves.
+ *
+ * Optional dS workspace of the backward entry points (workspace, workspace_bytes)
+ *   NULL: the dQ stage recomputes S, P, dP and dS from q, k, v and dout (memory O(N)).
+ *   Non-NULL: the dK stage also stores the rounded dS = P * (dP - Delta) (dtype, the value its own
+ *     product uses) into the workspace, and the dQ stage computes dq = scale * dS k from it
+ *     instead of recomputing: 2 D instead of 6 D flops per (query, key) pair, for
+ *     ffpa_bwd_workspace_bytes() bytes of device memory (B * Hq * Nq * round_up(Nkv, 8) * 2).
+ *     The workspace is caller-owned device memory; its contents are scratch. A workspace smaller
+ *     than the size function's value is FFPA_ERR_INVALID_ARGUMENT. When the size function returns
+ *     0 (a head's dS block would exceed 2^31 bytes) the workspace is ignored and dQ recomputes.
+ *   Both choices give the same result up to the order of fp32 additions.
  */
 #ifndef FFPA_H_
 #define FFPA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -68,30 +80,40 @@ int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int dtype, float scale, int causal, void* stream);
 
 /*
+ * Bytes of the optional dS workspace of ffpa_bwd / ffpa_bwd_stage for these sizes:
+ * batch * hq * nq * round_up(nkv, 8) * 2, or 0 when the stored-dS dQ pass is not available
+ * (a head's dS block above 2^31 bytes) or a size is < 1. Host function; launches nothing.
+ */
+size_t ffpa_bwd_workspace_bytes(int batch, int hq, int nq, int nkv);
+
+/*
  * Dense backward of L = sum(dout * o) ("CuTe-DSL Backend", "Blackwell status": preprocess, dV,
  * dK, dQ). Takes the forward's inputs, its outputs o and lse, and dout [batch, hq, nq, d].
  *   delta [batch, hq, nq] fp32   caller-owned workspace, overwritten with rowsum(dout * o)
  *   dq    [batch, hq, nq, d]     out
  *   dk, dv [batch, hkv, nkv, d]  out; sums over the hq/hkv query heads that share a KV head
+ *   workspace, workspace_bytes   optional dS workspace (see above), or NULL, 0
  * Gradients are accumulated in fp32 and rounded to dtype once. Rows with lse = -inf contribute
  * nothing and get dq = 0.
  */
 int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, float* delta, void* dq, void* dk, void* dv,
              int batch, int hq, int hkv, int nq, int nkv, int d,
-             int dtype, float scale, int causal, void* stream);
+             int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One stage of the dense backward, with exactly the arguments of ffpa_bwd plus `stage`:
  *   0 = preprocess (writes delta), 1 = dV, 2 = dK, 3 = dQ.
  * ffpa_bwd is these four launches in order; stages 2 and 3 read the delta written by stage 0.
+ * With a dS workspace, stage 2 writes dS into it and stage 3 reads it: pass the same workspace
+ * to both (stage 3 with a workspace that stage 2 did not fill gives undefined dq).
  * Lets a caller time or schedule the launches individually ("CuTe-DSL Backend", "Blackwell
  * status": the backward is four launches). Returns FFPA_ERR_INVALID_ARGUMENT for another stage.
  */
 int ffpa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, float* delta, void* dq, void* dk, void* dv,
                    int batch, int hq, int hkv, int nq, int nkv, int d,
-                   int dtype, float scale, int causal, void* stream);
+                   int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Packed (THD) varlen forward ("CuTe-DSL Backend", "Varlen (packed THD) API").
@@ -109,15 +131,24 @@ int ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float*
                     int hq, int hkv, int d, int dtype, float scale, int causal, void* stream);
 
 /*
+ * Bytes of the optional dS workspace of ffpa_varlen_bwd: hq * total_q * round_up(max_seqlen_k, 8)
+ * * 2, a bound on the packed per-sequence layout (sequence by sequence, then head, then
+ * query row, keys padded to a multiple of 8) that holds for every cu_seqlens consistent with the
+ * max_seqlen values; 0 when not available (see ffpa_bwd_workspace_bytes). Host function.
+ */
+size_t ffpa_varlen_bwd_workspace_bytes(int hq, int total_q, int max_seqlen_q, int max_seqlen_k);
+
+/*
  * Packed (THD) varlen backward; arguments as ffpa_varlen_fwd plus o, dout [total_q, hq, d],
- * the forward's lse [hq, total_q], a caller-owned fp32 workspace delta [hq, total_q], and the
- * outputs dq [total_q, hq, d], dk, dv [total_k, hkv, d].
+ * the forward's lse [hq, total_q], a caller-owned fp32 workspace delta [hq, total_q], the
+ * outputs dq [total_q, hq, d], dk, dv [total_k, hkv, d], and the optional dS workspace.
  */
 int ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, float* delta, void* dq, void* dk, void* dv,
                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                     int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
-                    int hq, int hkv, int d, int dtype, float scale, int causal, void* stream);
+                    int hq, int hkv, int d, int dtype, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code; never NULL. */
 const char* ffpa_status_string(int status);

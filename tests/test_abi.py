@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "ffpa.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(ffpa_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(ffpa_\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -28,7 +28,8 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     names = _declared()
-    for n in ("ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd", "ffpa_status_string"):
+    for n in ("ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd", "ffpa_status_string",
+              "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes"):
         assert n in names
 
 
@@ -74,18 +75,34 @@ def test_fwd_null_pointers(lib):
         assert _fwd(lib, ptrs=ptrs) == 1
 
 
-def _bwd(lib, stage=None, b=1, hq=2, hkv=1, nq=64, nkv=64, d=640, dtype=1, scale=0.04, causal=1, ptrs=None):
+def _bwd(lib, stage=None, b=1, hq=2, hkv=1, nq=64, nkv=64, d=640, dtype=1, scale=0.04, causal=1, ptrs=None,
+         ws=N, ws_bytes=0):
     ptrs = ptrs or [P] * 10
-    args = (*ptrs, b, hq, hkv, nq, nkv, d, dtype, scale, causal, S)
+    args = (*ptrs, b, hq, hkv, nq, nkv, d, dtype, scale, causal, ws, ws_bytes, S)
     return lib.ffpa_bwd(*args) if stage is None else lib.ffpa_bwd_stage(stage, *args)
 
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(b=0), 1), (dict(hq=3, hkv=2), 1), (dict(d=300), 2), (dict(dtype=5), 1), (dict(scale=0.0), 1),
     (dict(stage=4), 1), (dict(stage=-1), 1), (dict(stage=2, d=2048), 2),
+    # a dS workspace smaller than ffpa_bwd_workspace_bytes() is rejected before any launch
+    (dict(ws=P, ws_bytes=2 * 64 * 64 * 2 - 1), 1), (dict(stage=3, ws=P, ws_bytes=16), 1),
 ])
 def test_bwd_validation(lib, kw, expect):
     assert _bwd(lib, **kw) == expect
+
+
+def test_workspace_sizes(lib):
+    from head_dim_attention_amd import _binding as B
+    # B * Hq * Nq * round_up(Nkv, 8) * 2 bytes of dtype-sized dS
+    assert B.ffpa_bwd_workspace_bytes(1, 32, 8192, 8192) == 32 * 8192 * 8192 * 2
+    assert B.ffpa_bwd_workspace_bytes(2, 3, 5, 13) == 2 * 3 * 5 * 16 * 2
+    assert B.ffpa_bwd_workspace_bytes(1, 1, 7, 8) == 7 * 8 * 2
+    assert B.ffpa_bwd_workspace_bytes(0, 1, 7, 8) == 0
+    # a head's block above 2^31 bytes: not available (the library then recomputes dQ)
+    assert B.ffpa_bwd_workspace_bytes(1, 1, 40000, 40000) == 0
+    assert B.ffpa_varlen_bwd_workspace_bytes(4, 100, 60, 41) == 4 * 100 * 48 * 2
+    assert B.ffpa_varlen_bwd_workspace_bytes(4, 0, 0, 41) == 0
 
 
 def test_bwd_null_pointers(lib):
@@ -116,7 +133,9 @@ def test_varlen_null_pointers(lib):
         assert _vfwd(lib, ptrs=ptrs) == 1
     args = [P] * 12
     args[3] = N
-    assert lib.ffpa_varlen_bwd(*args, 2, 64, 64, 128, 128, 4, 2, 512, 0, 0.04, 1, S) == 1
+    assert lib.ffpa_varlen_bwd(*args, 2, 64, 64, 128, 128, 4, 2, 512, 0, 0.04, 1, N, 0, S) == 1
+    # too small a dS workspace
+    assert lib.ffpa_varlen_bwd(*([P] * 12), 2, 64, 64, 128, 128, 4, 2, 512, 0, 0.04, 1, P, 1024, S) == 1
 
 
 def test_varlen_empty_batch_is_a_noop(lib):

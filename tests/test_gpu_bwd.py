@@ -1,4 +1,8 @@
-"""GPU parity of the four-stage backward (preprocess, dV, dK, dQ) against the float64 oracle."""
+"""GPU parity of the four-stage backward (preprocess, dV, dK, dQ) against the float64 oracle.
+
+Every parity case runs both dQ paths: with the dS workspace (dK stores dS, dQ multiplies it by K)
+and without it (dQ recomputes S, P, dP and dS).
+"""
 import math
 
 import numpy as np
@@ -41,41 +45,58 @@ def lib():
     return F
 
 
-def _run_dense(lib, q, k, v, do, causal, scale):
+def _run_dense(lib, q, k, v, do, causal, scale, store_ds=True):
     qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
     o, lse = lib.ffpa_fwd(qc, kc, vc, causal=causal, scale=scale)
-    dq, dk, dv = lib.ffpa_bwd(qc, kc, vc, o, doc, lse, causal=causal, scale=scale)
+    dq, dk, dv = lib.ffpa_bwd(qc, kc, vc, o, doc, lse, causal=causal, scale=scale, store_ds=store_ds)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv
 
 
+PATHS = pytest.mark.parametrize("store_ds", [True, False], ids=["ds", "recompute"])
+
+
+@PATHS
 @pytest.mark.parametrize("case", DENSE_CASES, ids=_ids)
-def test_bwd_dense(lib, case):
+def test_bwd_dense(lib, case, store_ds):
     b, hq, hkv, nq, nkv, d, dt, causal = case
     q, k, v, do = W.dense_inputs(b, hq, hkv, nq, nkv, d, dt, seed=4321 + nq + d)
     scale = 1.0 / math.sqrt(d)
-    print(f"case {_ids(case)}", flush=True)
-    _, _, dq, dk, dv = _run_dense(lib, q, k, v, do, causal, scale)
+    print(f"case {_ids(case)} store_ds={store_ds}", flush=True)
+    _, _, dq, dk, dv = _run_dense(lib, q, k, v, do, causal, scale, store_ds)
     g_ref = ref.attn_bwd(q, k, v, do, scale=np.float64(np.float32(scale)), causal=causal)
     check_grads((dq, dk, dv), g_ref, _ids(case))
 
 
-def test_bwd_empty_rows_zero_grad(lib):
+def test_bwd_ds_path_matches_recompute(lib):
+    """The two dQ paths: dK and dV are the same launches (bit-identical); dQ agrees to fp32 order."""
+    q, k, v, do = W.dense_inputs(1, 4, 2, 161, 203, 512, BF, seed=26)
+    for causal in (False, True):
+        _, _, dq1, dk1, dv1 = _run_dense(lib, q, k, v, do, causal, None, True)
+        _, _, dq2, dk2, dv2 = _run_dense(lib, q, k, v, do, causal, None, False)
+        assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+        x, y = to64(dq1), to64(dq2)
+        assert np.linalg.norm(x - y) / np.linalg.norm(y) < 5e-3
+
+
+@PATHS
+def test_bwd_empty_rows_zero_grad(lib, store_ds):
     """Causal with Nq > Nkv: rows without a legal key get dQ = 0 exactly and add nothing to dK/dV."""
     q, k, v, do = W.dense_inputs(1, 2, 2, 100, 30, 320, FP, seed=21)
-    _, _, dq, dk, dv = _run_dense(lib, q, k, v, do, True, None)
+    _, _, dq, dk, dv = _run_dense(lib, q, k, v, do, True, None, store_ds)
     assert torch.all(dq[:, :, :70] == 0)
     do2 = do.clone()
     do2[:, :, :70] = 100.0
-    _, _, dq2, dk2, dv2 = _run_dense(lib, q, k, v, do2, True, None)
+    _, _, dq2, dk2, dv2 = _run_dense(lib, q, k, v, do2, True, None, store_ds)
     assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
     assert torch.all(dq2[:, :, :70] == 0)
 
 
-def test_bwd_deterministic(lib):
+@PATHS
+def test_bwd_deterministic(lib, store_ds):
     q, k, v, do = W.dense_inputs(1, 4, 2, 200, 200, 512, BF, seed=22)
-    r1 = _run_dense(lib, q, k, v, do, True, None)
-    r2 = _run_dense(lib, q, k, v, do, True, None)
+    r1 = _run_dense(lib, q, k, v, do, True, None, store_ds)
+    r2 = _run_dense(lib, q, k, v, do, True, None, store_ds)
     for a, b in zip(r1, r2):
         assert torch.equal(a, b)
 
@@ -109,33 +130,35 @@ VARLEN_CASES = [
 ]
 
 
+@PATHS
 @pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: f"q{c[0]}k{c[1]}h{c[2]}x{c[3]}d{c[4]}{'c' if c[6] else ''}")
-def test_bwd_varlen(lib, case):
+def test_bwd_varlen(lib, case, store_ds):
     lq, lk, hq, hkv, d, dt, causal = case
     q, k, v, do, cu_q, cu_k = W.varlen_inputs(lq, lk, hq, hkv, d, dt, seed=77 + d)
     scale = 1.0 / math.sqrt(d)
     qc, kc, vc, doc, cq, ck = q.cuda(), k.cuda(), v.cuda(), do.cuda(), cu_q.cuda(), cu_k.cuda()
     o, lse = lib.ffpa_varlen_fwd(qc, kc, vc, cq, ck, causal=causal, scale=scale)
-    dq, dk, dv = lib.ffpa_varlen_bwd(qc, kc, vc, o, doc, lse, cq, ck, causal=causal, scale=scale)
+    dq, dk, dv = lib.ffpa_varlen_bwd(qc, kc, vc, o, doc, lse, cq, ck, causal=causal, scale=scale, store_ds=store_ds)
     torch.cuda.synchronize()
     g_ref = ref.varlen_bwd(q, k, v, do, cu_q.numpy(), cu_k.numpy(), scale=np.float64(np.float32(scale)),
                            causal=causal)
     check_grads((dq, dk, dv), g_ref, f"varlen {lq} {lk}")
 
 
-def test_bwd_varlen_equals_dense(lib):
+@PATHS
+def test_bwd_varlen_equals_dense(lib, store_ds):
     """A packed batch gives the same gradients as separate dense calls per sequence."""
     lens = [40, 97, 64]
     q, k, v, do, cu_q, cu_k = W.varlen_inputs(lens, lens, 2, 2, 512, BF, seed=25)
     qc, kc, vc, doc, cq = q.cuda(), k.cuda(), v.cuda(), do.cuda(), cu_q.cuda()
     o, lse = lib.ffpa_varlen_fwd(qc, kc, vc, cq, causal=True)
-    dq, dk, dv = lib.ffpa_varlen_bwd(qc, kc, vc, o, doc, lse, cq, causal=True)
+    dq, dk, dv = lib.ffpa_varlen_bwd(qc, kc, vc, o, doc, lse, cq, causal=True, store_ds=store_ds)
     torch.cuda.synchronize()
     for s, n in enumerate(lens):
         a, b = int(cu_q[s]), int(cu_q[s + 1])
         sl = lambda x: x[a:b].transpose(0, 1).unsqueeze(0).contiguous()
         od, lsed = lib.ffpa_fwd(sl(qc), sl(kc), sl(vc), causal=True)
-        g = lib.ffpa_bwd(sl(qc), sl(kc), sl(vc), od, sl(doc), lsed, causal=True)
+        g = lib.ffpa_bwd(sl(qc), sl(kc), sl(vc), od, sl(doc), lsed, causal=True, store_ds=store_ds)
         torch.cuda.synchronize()
         assert torch.equal(od, sl(o)) and torch.equal(lsed[0], lse[:, a:b])
         for x, y in zip((dq, dk, dv), g):
