@@ -904,8 +904,8 @@ static hipError_t launch_bwd_pp(AttnParams p, hipStream_t st) {
 // x 4 column groups, each wave 64 queries (two 32-row MFMA blocks) x DW columns of fp32
 // accumulators. Per step of 32 keys the K rows of the chunk (32 x 1 KB, swizzled as elsewhere)
 // and the 128 x 32 dS block (64-byte rows, 16-byte chunks XOR-swizzled by bits 2-3 of the row)
-// are copied into LDS, double-buffered, with the next step's copies spread over the current
-// step's MFMAs. acc^T[d][q] += K^T[d][k] dS^T[k][q]: K^T is read transposed (ds_read_b64_tr_b16)
+// are copied into LDS, triple-buffered: the copies of step j + 2 are spread over the MFMAs of
+// step j, so each has a whole step to land. acc^T[d][q] += K^T[d][k] dS^T[k][q]: K^T is read transposed (ds_read_b64_tr_b16)
 // and used for both query blocks; dS^T is one 16-byte row read per query block and k-block.
 // Causal and ragged tiles mask dS to 0 where the key is not legal (those entries were not
 // written by the dK kernel).
@@ -921,7 +921,8 @@ struct DqCfg {
   static constexpr int KTILE = 32 * RS;
   static constexpr int STILE = BQ * 64;        // dS block: BQ rows x 32 keys x 2 bytes
   static constexpr int STAGE = KTILE + STILE;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int NBUF = 3;
+  static constexpr int LDS = NBUF * STAGE;
   static constexpr int KCOPY = KTILE / 1024 / NW;  // K copies per wave per step
   static constexpr int SCOPY = STILE / 1024 / NW;  // dS copies per wave per step
   static_assert(DWG <= 512 && SCOPY >= 1 && LDS <= 160 * 1024, "tile budget");
@@ -1035,15 +1036,21 @@ __global__ void __launch_bounds__(512, 2) ffpa_dq_from_ds_kernel(AttnParams p, i
   if (nsteps > 0) {
 #pragma unroll
     for (int c = 0; c < NCOPY; ++c) copy(0, 0, c);
+#pragma unroll
+    for (int c = 0; c < NCOPY; ++c) copy(min(1, nsteps - 1), 1, c);
   }
   wait_all();
 
+  int buf = 0;  // j % 3
   for (int j = 0; j < nsteps; ++j) {
-    const int buf = j & 1;
-    wait_vmcnt<0>();
+    // In flight: the copies of step j (issued during step j - 2) and then those of step j + 1.
+    wait_vmcnt<NCOPY>();
     lds_barrier();  // step j's tiles are visible; every wave has finished step j - 1
     const uint32_t tile = lds_addr(smem + buf * C::STAGE);
-    const int jn = min(j + 1, nsteps - 1);  // past the end: a harmless re-copy into the free buffer
+    // Step j + 2 goes into the buffer of step j - 1 (released by the barrier above); past the end
+    // the last step is copied again into a buffer that is not read any more.
+    const int jn = min(j + 2, nsteps - 1);
+    const int bn = buf == 0 ? 2 : buf - 1;
 
     // dS^T operands of both query blocks; masked where the key is not legal.
     u32x4_t bs[C::QB][2];
@@ -1082,11 +1089,12 @@ __global__ void __launch_bounds__(512, 2) ffpa_dq_from_ds_kernel(AttnParams p, i
           acc[qb][db] = Elt<T>::mma(a, bs[qb][kb2], acc[qb][db]);
 #pragma unroll
           for (int c = 0; c < NCOPY; ++c)
-            if (mi == spread_at(c)) copy(jn, buf ^ 1, c);
+            if (mi == spread_at(c)) copy(jn, bn, c);
           ++mi;
         }
       }
     }
+    buf = buf == 2 ? 0 : buf + 1;
   }
   // Copies issued during the last step land in LDS that the next workgroup may own.
   wait_vmcnt<0>();
