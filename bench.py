@@ -4,10 +4,10 @@
 Metric: attention TFLOPS (forward, and forward+backward) at D=512, N=8192, bf16, as a fraction
 of the dense bf16 MFMA peak. A step is one pass of the whole path over one batch of synthetic
 inputs already resident in HBM: the forward kernel, then the four backward launches
-(preprocess, dV, dK, dQ). Credited flops per legal (query, key) pair and query head: 4*D forward,
+(preprocess, dK, dV, dQ). Credited flops per legal (query, key) pair and query head: 4*D forward,
 10*D backward (the recomputation inside the backward is not credited). By default the backward
-runs with the library's dS workspace (dK stores dS, dQ multiplies it by K); --no-ds-workspace
-times the recomputing dQ kernel instead.
+runs with the library's P/dS workspace (dK stores P and dS, dV = P^T dO and dQ = dS K are
+products); --no-ds-workspace times the recomputing dV and dQ kernels instead.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line (rank 0).
@@ -31,11 +31,11 @@ METRIC = "attention TFLOPS (fwd, fwd+bwd) at D=512 N=8192 bf16; % of MFMA peak"
 # 256 CUs x 2.4 GHz x 4096 dense bf16/fp16 flop per clock per CU.
 PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
-# Algorithmic flops per legal pair and query head, by kernel (D multiplies these). dQ does 6 D when
-# it recomputes S, P, dP and dS, and 2 D when it multiplies the stored dS by K.
+# Algorithmic flops per legal pair and query head, by kernel (D multiplies these). Recomputing, dV
+# does 4 D (S, P^T dO) and dQ 6 D (S, dP, dS K); with the stored P and dS each is one product, 2 D.
 KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "dv": 4, "dk": 6, "dq": 6}
-DQ_FLOPS_PER_PAIR_D_STORED_DS = 2
-STAGES = ("fwd", "pre", "dv", "dk", "dq")
+STORED_FLOPS_PER_PAIR_D = {"dv": 2, "dq": 2}
+STAGES = ("fwd", "pre", "dk", "dv", "dq")
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "traffic_dense_d512_n8192.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "head_dim_attention_amd", "csrc", f)
                   for f in ("ffpa_device.h", "ffpa_params.h", "ffpa_fwd.hip", "ffpa_bwd.hip")]
@@ -68,7 +68,7 @@ def parse_args(argv=None):
     ap.add_argument("--seed", type=int, default=2024)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-ds-workspace", action="store_true",
-                    help="backward without the dS workspace (dQ recomputes S, P, dP and dS)")
+                    help="backward without the P/dS workspace (dV and dQ recompute)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration under rocprofv3)")
     return ap.parse_args(argv)
@@ -176,7 +176,7 @@ def main(argv=None) -> int:
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
     flops_d = dict(KERNEL_FLOPS_PER_PAIR_D)
     if ws is not None:
-        flops_d["dq"] = DQ_FLOPS_PER_PAIR_D_STORED_DS
+        flops_d.update(STORED_FLOPS_PER_PAIR_D)
     dt = 0 if w.dtype == "bf16" else 1
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -257,8 +257,8 @@ def main(argv=None) -> int:
         "fwdbwd_frac_of_peak": round(value / PEAK_TFLOPS, 4),
         "peak_tflops": PEAK_TFLOPS,
         "event_ms_per_step": round(step_ms, 4),
-        "dq_path": (f"stored dS ({ws_bytes / 2**30:.2f} GiB workspace)" if ws is not None
-                    else "recompute S, P, dP, dS"),
+        "bwd_path": (f"stored P and dS ({ws_bytes / 2**30:.2f} GiB workspace): dV = P^T dO, dQ = dS K"
+                     if ws is not None else "dV and dQ recompute S, P (dP, dS)"),
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic},

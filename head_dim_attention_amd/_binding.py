@@ -146,12 +146,12 @@ def ffpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = F
 
 
 def ffpa_bwd_workspace_bytes(batch: int, hq: int, nq: int, nkv: int) -> int:
-    """Bytes of the optional dS workspace of the dense backward (0: not available)."""
+    """Bytes of the optional P/dS workspace of the dense backward (0: not available)."""
     return int(load_library().ffpa_bwd_workspace_bytes(int(batch), int(hq), int(nq), int(nkv)))
 
 
 def ffpa_varlen_bwd_workspace_bytes(hq: int, total_q: int, max_seqlen_q: int, max_seqlen_k: int) -> int:
-    """Bytes of the optional dS workspace of the varlen backward (0: not available)."""
+    """Bytes of the optional P/dS workspace of the varlen backward (0: not available)."""
     return int(load_library().ffpa_varlen_bwd_workspace_bytes(int(hq), int(total_q), int(max_seqlen_q),
                                                                int(max_seqlen_k)))
 
@@ -166,8 +166,9 @@ def _workspace(nbytes: int, like: torch.Tensor):
 def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float] = None, store_ds: bool = True):
     """Dense backward -> (dq, dk, dv) with the shapes and dtype of q, k, v.
 
-    store_ds: let the dK stage store dS in a temporary workspace of ffpa_bwd_workspace_bytes() bytes so
-    that the dQ stage multiplies it by K instead of recomputing it (False: O(N) memory, recompute).
+    store_ds: let the dK stage store P and dS in a temporary workspace of ffpa_bwd_workspace_bytes()
+    bytes so that dV = P^T dO and dQ = dS K are products instead of recomputations (False: O(N)
+    memory, recompute).
     """
     q, k, v, o, dout = (_dev(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")))
     lse = _dev(lse, "lse")
@@ -190,11 +191,11 @@ def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float]
 
 def ffpa_bwd_stage(stage: int, q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool = False,
                    scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
-    """Run one backward stage (0 preprocess, 1 dV, 2 dK, 3 dQ) into caller-provided buffers.
+    """Run one backward stage (0 preprocess, 1 dK, 2 dV, 3 dQ) into caller-provided buffers.
 
     All tensors must be contiguous GPU tensors with ffpa_bwd's shapes; delta is float32 [B,Hq,Nq].
-    workspace: optional dS workspace (a GPU tensor of at least ffpa_bwd_workspace_bytes() bytes),
-    the same for stages 2 and 3.
+    workspace: optional P/dS workspace (a GPU tensor of at least ffpa_bwd_workspace_bytes() bytes),
+    the same for stages 1, 2 and 3 (stage 1 fills it, stages 2 and 3 read it).
     """
     if workspace is not None and not (isinstance(workspace, torch.Tensor) and workspace.device.type == "cuda"
                                       and workspace.is_contiguous()):

@@ -84,26 +84,29 @@ bool too_big_dense(int batch, int h, int n, int d) {
 
 long long round_up8(long long x) { return (x + 7) & ~7LL; }
 
-// Bytes of one head's stored dS block of nq rows of round_up8(nkv) elements; the dQ pass
-// addresses it with 32-bit byte offsets, so larger blocks use the recomputing dQ kernel.
+// Bytes of one head's stored dS (or P) block of nq rows of round_up8(nkv) elements; the dQ and
+// dV passes address it with 32-bit byte offsets, so larger blocks use the recomputing kernels.
 bool ds_block_ok(long long nq, long long nkv) { return nq * round_up8(nkv) * 2 <= (1LL << 31) - 4096; }
 
+// The workspace holds two equal blocks: dS, then P.
 size_t dense_ds_bytes(int batch, int hq, int nq, int nkv) {
   if (batch < 1 || hq < 1 || nq < 1 || nkv < 1 || !ds_block_ok(nq, nkv)) return 0;
-  return (size_t)batch * hq * nq * round_up8(nkv) * 2;
+  return 2 * (size_t)batch * hq * nq * round_up8(nkv) * 2;
 }
 
 size_t varlen_ds_bytes(int hq, int total_q, int max_q, int max_k) {
   if (hq < 1 || total_q < 1 || max_q < 1 || max_k < 1 || !ds_block_ok(max_q, max_k)) return 0;
-  return (size_t)hq * total_q * round_up8(max_k) * 2;
+  return 2 * (size_t)hq * total_q * round_up8(max_k) * 2;
 }
 
-// Attach a caller workspace for dS. NULL selects the recomputing dQ kernel; a workspace smaller
-// than `need` is an invalid argument; need == 0 (not available for these sizes) ignores it.
+// Attach a caller workspace for dS and P. NULL selects the recomputing dV and dQ kernels; a
+// workspace smaller than `need` is an invalid argument; need == 0 (not available for these sizes)
+// ignores it.
 int attach_ds(AttnParams& p, void* ws, size_t ws_bytes, size_t need) {
   if (ws == nullptr || need == 0) return FFPA_OK;
   if (ws_bytes < need) return FFPA_ERR_INVALID_ARGUMENT;
   p.ds = ws;
+  p.pst = (char*)ws + need / 2;
   return FFPA_OK;
 }
 

@@ -378,7 +378,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
     uint32_t bop[2][4];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      float v2[2];
+      float v2[2], pv2[2] = {0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int rr = r + u;
@@ -391,19 +391,26 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
           const bool legal = ki < sv.lk && qi < sv.lq && (!p.causal || ki <= qi + off);
           pv = legal ? pv : 0.f;
         }
+        if constexpr (MODE == kDK) pv2[u] = pv;
         if constexpr (HAS_DP) pv = pv * (dpacc[rr] - row_val(dlt_lane, rr));
         v2[u] = pv;
       }
       bop[r >> 3][(r & 7) >> 1] = Elt<T>::pack2(v2[0], v2[1]);
       if constexpr (MODE == kDK) {
-        // Optionally store the rounded dS (the value the accumulating product uses) for dQ.
+        // Optionally store the rounded dS and P (the values a product uses) for dQ and dV.
         if (store_ds && oi < sv.lk) {
           const uint32_t pk = bop[r >> 3][(r & 7) >> 1];
-          uint16_t* dsp = (uint16_t*)p.ds + dsv.base + (long long)step_head(st) * dsv.head + oi;
+          const uint32_t pp = Elt<T>::pack2(pv2[0], pv2[1]);
+          const long long hoff = dsv.base + (long long)step_head(st) * dsv.head + oi;
+          uint16_t* dsp = (uint16_t*)p.ds + hoff;
+          uint16_t* psp = (uint16_t*)p.pst + hoff;
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int qi = row0 + c_row(r + u, hh);
-            if (qi < sv.lq) dsp[(long long)qi * dsv.row] = (uint16_t)(u ? pk >> 16 : pk & 0xffff);
+            if (qi < sv.lq) {
+              dsp[(long long)qi * dsv.row] = (uint16_t)(u ? pk >> 16 : pk & 0xffff);
+              psp[(long long)qi * dsv.row] = (uint16_t)(u ? pp >> 16 : pp & 0xffff);
+            }
           }
         }
       }
@@ -495,7 +502,8 @@ struct PpCfg {
   static constexpr int X_OFF = 4 * TILE;         // [cg][3 partner quarters][S, dP] pieces
   static constexpr int G_OFF = X_OFF + NC * 3 * 2 * PIECE;  // [cg] packed dS quarter, 8 B/lane
   static constexpr int ST_OFF = G_OFF + NC * 64 * 8;        // [buffer][LSE, Delta] x 64 floats
-  static constexpr int LDS = ST_OFF + 2 * 2 * 256;
+  static constexpr int P_OFF = ST_OFF + 2 * 2 * 256;        // [cg] packed P quarter (when stored)
+  static constexpr int LDS = P_OFF + NC * 64 * 8;
   static constexpr int NCOPY = TILE / 1024 / 4;  // copies per wave of a tile (one group copies it)
   static constexpr int KSTEPS = 2 * NDB;         // k-steps of the partial products
   static constexpr int KA = (3 * KSTEPS) / 4;    // k-steps in M1a (M1b shares its slot with M2)
@@ -505,7 +513,7 @@ struct PpCfg {
 template <class T, int MODE, int NDB, bool STORE_DS>
 __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
   static_assert(MODE == kDQ || MODE == kDK, "dK and dQ only");
-  static_assert(!STORE_DS || MODE == kDK, "dS is stored by the dK kernel");
+  static_assert(!STORE_DS || MODE == kDK, "dS and P are stored by the dK kernel");
   constexpr bool OWN_Q = MODE == kDQ;
   using C = PpCfg<NDB>;
   constexpr int NC = C::NC;
@@ -717,11 +725,14 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
   };
   // ---- phase V1: reduce this wave's quarter (own part + partners in a fixed order), P and dS
   u32x2_t mine;
-  // dS row piece of this lane, its byte offset and the head block's buffer resource: formed in V1,
-  // stored at the start of M2 (so V1 does not wait for the transposed reads).
-  u32x4_t ds_piece = {0u, 0u, 0u, 0u};
+  // dS and P row pieces of this lane, their byte offset (the same in both blocks) and the head
+  // blocks' buffer resources: formed in V1, stored at the start of M2 (so that V1 does not wait
+  // for the transposed reads).
+  u32x4_t ds_piece = {0u, 0u, 0u, 0u}, p_piece = {0u, 0u, 0u, 0u};
   uint32_t ds_boff = 0xFFFFFFF0u;
   __amdgpu_buffer_rsrc_t ds_rs = __builtin_amdgcn_make_buffer_rsrc(p.dq, 0, 0, 0x00020000);
+  __amdgpu_buffer_rsrc_t p_rs = ds_rs;
+  lds_t* const pbuf = smem + C::P_OFF;
   auto v1 = [&](int st) {
     f32x4_t sq = sq_own, dq = dq_own;
 #pragma unroll
@@ -751,7 +762,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
     } else {
       need_mask = (row0 + 32 > sv.lq) || (p.causal && ow0 + 31 > row0 + off);
     }
-    float ds[4];
+    float ds[4], pq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float pv = fast_exp2(sq[i] * p.scale_log2 - lse2q[i]);
@@ -762,35 +773,44 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
         const bool legal = ki < sv.lk && qi < sv.lq && (!p.causal || ki <= qi + off);
         pv = legal ? pv : 0.f;
       }
+      pq[i] = pv;
       ds[i] = pv * (dq[i] - dltq[i]);
     }
     mine = (u32x2_t){Elt<T>::pack2(ds[0], ds[1]), Elt<T>::pack2(ds[2], ds[3])};
     *(__attribute__((address_space(3))) u32x2_t*)(gbuf + cg * 512 + lane * 8) = mine;
     if constexpr (STORE_DS) {
-      // Store the rounded dS the accumulating product uses, dS[query][key], as 16-byte row pieces.
-      // The wave's quarter, just written to the gather buffer (lane (h, key n): 4 query rows),
-      // is read back transposed: in 16-lane group g (g = 0, 1 <-> h = g) source lane s = t + 4 m
-      // points at key 8 t + m (first read) or 8 t + 4 + m (second), so lane i receives keys
-      // 8 (i/4) + 0..7 of query row qrow(g) + i%4. Lanes 32..63 and pieces outside the sequence
-      // (rows >= Lq, or starting at or past the padded row end) get an offset past the block, which
-      // the buffer range check discards.
+      // Store the rounded dS and P (the values a product uses), [query][key], as 16-byte row
+      // pieces. The wave's quarter, in the buffer as lane (h, key n): 4 query rows, is read back
+      // transposed: in 16-lane group g (g = 0, 1 <-> h = g) source lane s = t + 4 m points at key
+      // 8 t + m (first read) or 8 t + 4 + m (second), so lane i receives keys 8 (i/4) + 0..7 of
+      // query row qrow(g) + i%4. Lanes 32..63 and pieces outside the sequence (rows >= Lq, or
+      // starting at or past the padded row end) get an offset past the block, which the buffer
+      // range check discards.
+      const u32x2_t pmine = {Elt<T>::pack2(pq[0], pq[1]), Elt<T>::pack2(pq[2], pq[3])};
+      *(__attribute__((address_space(3))) u32x2_t*)(pbuf + cg * 512 + lane * 8) = pmine;
       const int g = (lane >> 4) & 1, sl = lane & 15, i16 = lane & 15;
-      const lds_t* gq = gbuf + cg * 512 + (32 * g + 8 * (sl & 3) + (sl >> 2)) * 8;
-      ds_piece = join_tr(lds_read_tr16(gq, 0), lds_read_tr16(gq, 32));
+      const int toff = cg * 512 + (32 * g + 8 * (sl & 3) + (sl >> 2)) * 8;
+      ds_piece = join_tr(lds_read_tr16(gbuf + toff, 0), lds_read_tr16(gbuf + toff, 32));
+      p_piece = join_tr(lds_read_tr16(pbuf + toff, 0), lds_read_tr16(pbuf + toff, 32));
       const int rq = row0 + 16 * (cg >> 1) + 8 * g + 4 * (cg & 1) + (i16 & 3);
       const int key0 = ow0 + 8 * (i16 >> 2);
       const bool ok = lane < 32 && rq < sv.lq && key0 < dsv.row;
       ds_boff = ok ? (uint32_t)((rq * dsv.row + key0) * 2) : 0xFFFFFFF0u;
-      uint16_t* head_blk = (uint16_t*)p.ds + dsv.base + (long long)step_head(st) * dsv.head;
-      ds_rs = __builtin_amdgcn_make_buffer_rsrc(head_blk, 0, (int)((long long)sv.lq * dsv.row * 2), 0x00020000);
+      const long long hoff = dsv.base + (long long)step_head(st) * dsv.head;
+      const int nrec = (int)((long long)sv.lq * dsv.row * 2);
+      ds_rs = __builtin_amdgcn_make_buffer_rsrc((uint16_t*)p.ds + hoff, 0, nrec, 0x00020000);
+      p_rs = __builtin_amdgcn_make_buffer_rsrc((uint16_t*)p.pst + hoff, 0, nrec, 0x00020000);
     }
   };
   // ---- phase M2: all-gather dS (quarter q gives B-operand words 2 (q % 2), +1 of k-block q / 2),
   // then acc^T[d][own] += A[d][streamed] * dS[streamed][own], A read transposed from tile 1
   auto m2 = [&](int st) {
-    if constexpr (STORE_DS)
+    if constexpr (STORE_DS) {
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, ds_piece), ds_rs, (int)ds_boff, 0,
                                              DS_STORE_CPOL);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, p_piece), p_rs, (int)ds_boff, 0,
+                                             DS_STORE_CPOL);
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       u32x2_t v = mine;
@@ -836,8 +856,8 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
         lds_barrier();
         m2(st);
         // Issued since the last wait, in order: the tile copies (M1a), the row statistics (M1b) and,
-        // when dS is stored, its store (M2): that one may stay in flight.
-        wait_vmcnt<STORE_DS ? 1 : 0>();
+        // when dS and P are stored, their two stores (M2): those may stay in flight.
+        wait_vmcnt<STORE_DS ? 2 : 0>();
         lds_barrier();
       }
       lds_barrier();
@@ -1143,6 +1163,262 @@ static hipError_t launch_dq_ds_t(const AttnParams& p, hipStream_t st) {
   return launch_dq_from_ds<T, 4>(p, nchunk, st);
 }
 
+// ------------------------------------------------------------------------------------------------
+// dV from a stored P: dV_j = sum over the query heads h of the group and queries i of P_hij dO_hi
+// (fp32 accumulation, one rounding), the dV stage when the dK kernel has stored P.
+//
+// Same tiling as the dQ pass with keys as the output rows: a workgroup owns 128 keys of one KV head
+// and one chunk of up to 512 head-dim columns; its 8 waves are 2 key groups x 4 column groups, each
+// wave 64 keys (two 32-row MFMA blocks) x DW columns. The streamed side is 32 queries of one query
+// head of the group per step (all the group's heads in turn; causal steps start at the first
+// query that sees a key of the block). acc^T[d][j] += dO^T[d][i] P[i][j]: dO^T is read transposed
+// from the dO rows (as K^T in the dQ pass) and P[i][j] for 8 consecutive queries i of key j is read
+// transposed from the P block in LDS (32 queries x 128 keys, 256-byte rows whose 64-byte blocks are
+// XOR-swizzled by the row index mod 4, which keeps a half-wave's transposed reads on distinct
+// banks). Triple-buffered copies as in the dQ pass. P is masked to 0 for queries at or past Lq
+// (their rows are clamped duplicates) and for keys that are not legal (not written by dK).
+// ------------------------------------------------------------------------------------------------
+template <int NDB>
+struct DvCfg {
+  static constexpr int NW = 8;
+  static constexpr int KB = 2;                 // 32-key MFMA blocks per wave
+  static constexpr int DW = NDB * 32;
+  static constexpr int DWG = 4 * DW;
+  static constexpr int BK = 2 * KB * 32;       // keys per workgroup
+  static constexpr int RS = 1024;              // dO tile row stride (bytes)
+  static constexpr int OTILE = 32 * RS;
+  static constexpr int PROW = BK * 2;          // P block row: 128 keys x 2 bytes
+  static constexpr int PTILE = 32 * PROW;
+  static constexpr int STAGE = OTILE + PTILE;
+  static constexpr int NBUF = 3;
+  static constexpr int LDS = NBUF * STAGE;
+  static constexpr int OCOPY = OTILE / 1024 / NW;
+  static constexpr int PCOPY = PTILE / 1024 / NW;
+  static_assert(DWG <= 512 && PCOPY == 1 && PROW == 256 && LDS <= 160 * 1024, "tile budget");
+};
+
+template <class T, int NDB>
+__global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, int nchunk) {
+  using C = DvCfg<NDB>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
+  lds_t* smem = (lds_t*)smem_raw;
+
+  const int L = blockIdx.x;
+  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  if (item >= p.total) return;
+  const int kt = item % p.ntiles;
+  const int rest = item / p.ntiles;
+  const int chunk = rest % nchunk;
+  const int hs = rest / nchunk;
+  const int kvh = hs % p.hkv;
+  const int s = hs / p.hkv;
+
+  const SeqView sv = seq_view(p, s);
+  const int k0 = kt * C::BK;
+  if (k0 >= sv.lk) return;
+  const DsView dsv = ds_view(p, s, sv);
+  const int d0 = chunk * C::DWG;
+
+  const int w = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int kg = w >> 2;
+  const int dg = w & 3;
+  const int off = sv.lk - sv.lq;
+
+  // Streamed steps: query tiles of each query head of the group.
+  const int qfirst = p.causal ? max(0, k0 - off) : 0;
+  const int qt_first = qfirst >> 5;
+  const int nqt = sv.lq > qfirst ? ((sv.lq + 31) >> 5) - qt_first : 0;
+  const int nsteps = p.group * nqt;
+  auto step_head = [&](int st) { return kvh * p.group + st / nqt; };
+  auto step_row0 = [&](int st) { return (qt_first + st % nqt) * 32; };
+
+  f32x16_t acc[C::KB][NDB];
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[kb][db] = (f32x16_t){};
+
+  // ---- copies. dO rows of the chunk: copy ii of wave w fills tile row i = w + 8 ii (as in dQ).
+  const int orow_bytes = p.q_row * 2;
+  const uint32_t ospan = (uint32_t)min((long long)max(sv.lq, 1) * orow_bytes, (long long)0xFFFFFFF0);
+  const int dch = p.d >> 3;
+  int ovoff[C::OCOPY];
+#pragma unroll
+  for (int ii = 0; ii < C::OCOPY; ++ii) ovoff[ii] = min((d0 >> 3) + (lane ^ swz(w + 8 * ii)), dch - 1) << 4;
+  // P rows: copy of wave w fills block rows 4 w .. 4 w + 3; lane l writes row 4 w + l / 16, physical
+  // chunk l % 16, holding logical chunk (l % 16) ^ (4 (row % 4)) (keys k0 + 8 * logical chunk).
+  // The whole byte offset is per lane (range-checked; the block is a multiple of 16 bytes).
+  const int prow_l = 4 * w + (lane >> 4);
+  const int pchunk = (lane & 15) ^ (4 * (prow_l & 3));
+  const uint32_t pspan = (uint32_t)((long long)sv.lq * dsv.row * 2);
+  struct StepSrc {
+    i32x4_t ors, prs;
+    int row0;
+  };
+  auto step_src = [&](int st) {
+    st = min(st, nsteps - 1);
+    StepSrc x;
+    const int h = step_head(st);
+    x.row0 = step_row0(st);
+    x.ors = make_rsrc((const uint16_t*)p.dout + sv.q_off + (long long)h * p.q_head, ospan);
+    x.prs = make_rsrc((const uint16_t*)p.pst + dsv.base + (long long)h * dsv.head, pspan);
+    return x;
+  };
+  auto copy = [&](const StepSrc& x, int buf, int c) {
+    lds_t* stage = smem + buf * C::STAGE;
+    if (c < C::OCOPY) {
+      const int i = w + 8 * c;
+      dma16_buf(x.ors, ovoff[c], min(x.row0 + i, sv.lq - 1) * orow_bytes, stage + i * 1024);
+    } else {
+      const int qrow = min(x.row0 + prow_l, sv.lq - 1);
+      dma16_buf(x.prs, (qrow * dsv.row + k0 + 8 * pchunk) * 2, 0, stage + C::OTILE + w * 1024);
+    }
+  };
+  constexpr int NCOPY = C::OCOPY + C::PCOPY;
+  constexpr int NMMA = 2 * NDB * C::KB;
+  auto spread_at = [](int c) { return (c * NMMA) / NCOPY; };
+
+  // ---- operand addresses. dO^T (A operand): transposed reads as K^T in the dQ pass.
+  const int g16 = lane >> 4;
+  const int r16 = lane & 15;
+  const int cbase = dg * C::DW >> 3;
+  const int tclo = 2 * (g16 & 1) + ((r16 & 3) >> 1);
+  const int twithin = ((4 * (r16 & 3)) & 7) << 1;
+  constexpr bool kAligned = (C::DW % 128) == 0;
+  uint32_t tlane[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int k = 8 * hh + 4 * half + (r16 >> 2);
+    tlane[half] = k * C::RS + (cbase << 4) + ((tclo ^ swz(k)) << 4) + twithin;
+  }
+  auto t_addr = [&](uint32_t tile, int db, int kb2, int half) -> uint32_t {
+    if constexpr (kAligned)
+      return ((tile + tlane[half]) ^ ((db & 3) << 6)) + ((db >> 2) << 8) + kb2 * 16 * C::RS;
+    const int k = 16 * kb2 + 8 * hh + 4 * half + (r16 >> 2);
+    return tile + k * C::RS + (((cbase + 4 * db + tclo) ^ swz(k)) << 4) + twithin;
+  };
+  // P (B operand): lane (h, key n) needs queries 16 kb2 + 8 h + 0..7 of key 64 kg + 32 kb + n. In
+  // 16-lane group g16 source lane s = t + 4 m points at block row 16 kb2 + 8 h + 4 half + m, keys
+  // 64 kg + 32 kb + 16 (g16 % 2) + 4 t + 0..3, so lane i receives key 16 (g16 % 2) + i of the
+  // 32-key block and queries + 0..3 (half 0) or + 4..7 (half 1).
+  auto p_addr = [&](uint32_t tile, int kb, int kb2, int half) -> uint32_t {
+    const int m = r16 >> 2, t = r16 & 3;
+    const int row = 16 * kb2 + 8 * hh + 4 * half + m;
+    const int byte = (64 * kg + 32 * kb + 16 * (g16 & 1) + 4 * t) * 2;
+    return tile + C::OTILE + row * C::PROW + ((((byte >> 4) ^ (4 * (row & 3))) << 4) | (byte & 15));
+  };
+
+  if (nsteps > 0) {
+    const StepSrc x0 = step_src(0), x1 = step_src(1);
+#pragma unroll
+    for (int c = 0; c < NCOPY; ++c) copy(x0, 0, c);
+#pragma unroll
+    for (int c = 0; c < NCOPY; ++c) copy(x1, 1, c);
+  }
+  wait_all();
+
+  int buf = 0;  // st % 3
+  for (int st = 0; st < nsteps; ++st) {
+    // In flight: the copies of step st (issued during step st - 2) and then those of step st + 1.
+    wait_vmcnt<NCOPY>();
+    lds_barrier();  // step st's tiles are visible; every wave has finished step st - 1
+    const uint32_t tile = lds_addr(smem + buf * C::STAGE);
+    const int bn = buf == 0 ? 2 : buf - 1;  // the buffer of step st - 1
+    const StepSrc xn = step_src(st + 2);
+    const int row0 = step_row0(st);
+
+    u32x4_t bp[C::KB][2];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+        bp[kb][kb2] = join_tr(lds_read_tr16_at(p_addr(tile, kb, kb2, 0)), lds_read_tr16_at(p_addr(tile, kb, kb2, 1)));
+    const int kw0 = k0 + 64 * kg;
+    const bool need_mask = (row0 + 32 > sv.lq) || (kw0 + 64 > sv.lk) || (p.causal && kw0 + 63 > row0 + off);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        const int kj = kw0 + 32 * kb + l32;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int q = row0 + 16 * kb2 + 8 * hh + 2 * e;
+            auto legal = [&](int qi) { return qi < sv.lq && kj < sv.lk && (!p.causal || kj <= qi + off); };
+            uint32_t x = bp[kb][kb2][e];
+            if (!legal(q)) x &= 0xffff0000u;
+            if (!legal(q + 1)) x &= 0x0000ffffu;
+            bp[kb][kb2][e] = x;
+          }
+      }
+    }
+    int mi = 0;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const s16x4_t lo = lds_read_tr16_at(t_addr(tile, db, kb2, 0));
+        const s16x4_t hi = lds_read_tr16_at(t_addr(tile, db, kb2, 1));
+        const u32x4_t a = join_tr(lo, hi);
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+          acc[kb][db] = Elt<T>::mma(a, bp[kb][kb2], acc[kb][db]);
+#pragma unroll
+          for (int c = 0; c < NCOPY; ++c)
+            if (mi == spread_at(c)) copy(xn, bn, c);
+          ++mi;
+        }
+      }
+    }
+    buf = buf == 2 ? 0 : buf + 1;
+  }
+  // Copies issued during the last steps land in LDS that the next workgroup may own.
+  wait_vmcnt<0>();
+
+  // ---- epilogue: round once, store keys < Lk and columns < D
+  uint16_t* dvh = (uint16_t*)p.dv + sv.k_off + (long long)kvh * p.k_head;
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+    const int kj = k0 + 64 * kg + 32 * kb + l32;
+    if (kj < sv.lk) {
+      uint16_t* dst = dvh + (long long)kj * p.k_row;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = d0 + dg * C::DW + 32 * db + 8 * i4 + 4 * hh;
+          if (d < p.d) {
+            const f32x16_t& a = acc[kb][db];
+            const u32x2_t pk = {Elt<T>::pack2(a[4 * i4], a[4 * i4 + 1]), Elt<T>::pack2(a[4 * i4 + 2], a[4 * i4 + 3])};
+            *(u32x2_t*)(dst + d) = pk;
+          }
+        }
+    }
+  }
+}
+
+template <class T, int NDB>
+static hipError_t launch_dv_from_p(AttnParams p, int nchunk, hipStream_t st) {
+  using C = DvCfg<NDB>;
+  p.ntiles = (p.nkv + C::BK - 1) / C::BK;
+  p.total = p.batch * p.hkv * nchunk * p.ntiles;
+  if (p.total == 0) return hipSuccess;
+  const int grid = (p.total + 7) & ~7;
+  hipLaunchKernelGGL((ffpa_dv_from_p_kernel<T, NDB>), dim3(grid), dim3(64 * C::NW), 0, st, p, nchunk);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_dv_p_t(const AttnParams& p, hipStream_t st) {
+  const int nchunk = (p.d + 511) / 512;
+  const int per = (p.d + nchunk - 1) / nchunk;
+  if (per <= 384) return launch_dv_from_p<T, 3>(p, nchunk, st);
+  return launch_dv_from_p<T, 4>(p, nchunk, st);
+}
+
 template <class T, int MODE, int NC, int NDB>
 static hipError_t launch_bwd_cfg(AttnParams p, hipStream_t st) {
   constexpr int NX = MODE != kDV ? 2 : 1;
@@ -1194,13 +1470,14 @@ static hipError_t launch_stage_t(int stage, const AttnParams& p, int nrows, int 
         return hipGetLastError();
       }
       return hipSuccess;
-    case 1: return launch_bwd_mode<T, kDV>(p, st);
-    case 2: return launch_bwd_mode<T, kDK>(p, st);  // also stores dS when p.ds is set
+    // With a workspace, dK also stores dS and P, and dV and dQ are products of them.
+    case 1: return launch_bwd_mode<T, kDK>(p, st);
+    case 2: return p.pst != nullptr ? launch_dv_p_t<T>(p, st) : launch_bwd_mode<T, kDV>(p, st);
     default: return p.ds != nullptr ? launch_dq_ds_t<T>(p, st) : launch_bwd_mode<T, kDQ>(p, st);
   }
 }
 
-// Stage 0 = preprocess, 1 = dV, 2 = dK, 3 = dQ; -1 runs all four in order.
+// Stage 0 = preprocess, 1 = dK, 2 = dV, 3 = dQ; -1 runs all four in order.
 hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total, hipStream_t st, int stage) {
   for (int s = stage < 0 ? 0 : stage; s <= (stage < 0 ? 3 : stage); ++s) {
     const hipError_t e = fp16 ? launch_stage_t<FP16>(s, p, nrows, varlen_total, st)

@@ -26,6 +26,7 @@ struct AttnParams {
   // b * ds_batch + h * ds_head + i * ds_row + j. Varlen: sequence s starts at hq * P_s with
   // P_s = sum over earlier sequences of Lq * round_up(Lk, 8), head h at + h * Lq_s * round_up(Lk_s, 8).
   void* ds;
+  void* pst;  // stored P (same geometry as ds), or NULL
   long long ds_batch, ds_head;
   int ds_row;
   // Dense strides in elements (unused for varlen except row/head strides).

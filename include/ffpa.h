@@ -33,15 +33,17 @@
  *     enqueued; a non-OK status means nothing was launched. FFPA_ERR_HIP reports a failed launch.
  *   - Inputs are assumed finite. Buffers may not alias each other except q/k/v among themselves.
  *
- * Optional dS workspace of the backward entry points (workspace, workspace_bytes)
- *   NULL: the dQ stage recomputes S, P, dP and dS from q, k, v and dout (memory O(N)).
- *   Non-NULL: the dK stage also stores the rounded dS = P * (dP - Delta) (dtype, the value its own
- *     product uses) into the workspace, and the dQ stage computes dq = scale * dS k from it
- *     instead of recomputing: 2 D instead of 6 D flops per (query, key) pair, for
- *     ffpa_bwd_workspace_bytes() bytes of device memory (B * Hq * Nq * round_up(Nkv, 8) * 2).
- *     The workspace is caller-owned device memory; its contents are scratch. A workspace smaller
- *     than the size function's value is FFPA_ERR_INVALID_ARGUMENT. When the size function returns
- *     0 (a head's dS block would exceed 2^31 bytes) the workspace is ignored and dQ recomputes.
+ * Optional P/dS workspace of the backward entry points (workspace, workspace_bytes)
+ *   NULL: the dV and dQ stages recompute S and P (and dP, dS) from q, k, v and dout (memory O(N)).
+ *   Non-NULL: the dK stage also stores the rounded P = exp(scale q k^T - lse) and
+ *     dS = P * (dP - Delta) (dtype, the values the products use) into the workspace, and the dV
+ *     and dQ stages are products of them, dv = P^T dout and dq = scale * dS k, instead of
+ *     recomputations: 2 D flops per (query, key) pair each instead of 4 D and 6 D, for
+ *     ffpa_bwd_workspace_bytes() bytes of device memory (2 * B * Hq * Nq * round_up(Nkv, 8) * 2:
+ *     the dS block, then the P block). The workspace is caller-owned device memory; its contents
+ *     are scratch. A workspace smaller than the size function's value is
+ *     FFPA_ERR_INVALID_ARGUMENT. When the size function returns 0 (a head's block would exceed
+ *     2^31 bytes) the workspace is ignored and the stages recompute.
  *   Both choices give the same result up to the order of fp32 additions.
  */
 #ifndef FFPA_H_
@@ -80,9 +82,9 @@ int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int dtype, float scale, int causal, void* stream);
 
 /*
- * Bytes of the optional dS workspace of ffpa_bwd / ffpa_bwd_stage for these sizes:
- * batch * hq * nq * round_up(nkv, 8) * 2, or 0 when the stored-dS dQ pass is not available
- * (a head's dS block above 2^31 bytes) or a size is < 1. Host function; launches nothing.
+ * Bytes of the optional P/dS workspace of ffpa_bwd / ffpa_bwd_stage for these sizes:
+ * 2 * batch * hq * nq * round_up(nkv, 8) * 2, or 0 when the stored-P/dS passes are not available
+ * (a head's block above 2^31 bytes) or a size is < 1. Host function; launches nothing.
  */
 size_t ffpa_bwd_workspace_bytes(int batch, int hq, int nq, int nkv);
 
@@ -92,7 +94,7 @@ size_t ffpa_bwd_workspace_bytes(int batch, int hq, int nq, int nkv);
  *   delta [batch, hq, nq] fp32   caller-owned workspace, overwritten with rowsum(dout * o)
  *   dq    [batch, hq, nq, d]     out
  *   dk, dv [batch, hkv, nkv, d]  out; sums over the hq/hkv query heads that share a KV head
- *   workspace, workspace_bytes   optional dS workspace (see above), or NULL, 0
+ *   workspace, workspace_bytes   optional P/dS workspace (see above), or NULL, 0
  * Gradients are accumulated in fp32 and rounded to dtype once. Rows with lse = -inf contribute
  * nothing and get dq = 0.
  */
@@ -103,10 +105,12 @@ int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
 
 /*
  * One stage of the dense backward, with exactly the arguments of ffpa_bwd plus `stage`:
- *   0 = preprocess (writes delta), 1 = dV, 2 = dK, 3 = dQ.
- * ffpa_bwd is these four launches in order; stages 2 and 3 read the delta written by stage 0.
- * With a dS workspace, stage 2 writes dS into it and stage 3 reads it: pass the same workspace
- * to both (stage 3 with a workspace that stage 2 did not fill gives undefined dq).
+ *   0 = preprocess (writes delta), 1 = dK, 2 = dV, 3 = dQ.
+ * ffpa_bwd is these four launches in order; stage 1 reads the delta written by stage 0 (and so
+ * does stage 3 without a workspace). With a P/dS workspace, stage 1 writes P and dS into it and
+ * stages 2 and 3 read them: pass the same workspace to all three (stages 2 and 3 with a workspace
+ * that stage 1 did not fill give undefined dv, dq). The pages run dV before dK; the two are
+ * independent without a workspace, and with one dK goes first because it produces P.
  * Lets a caller time or schedule the launches individually ("CuTe-DSL Backend", "Blackwell
  * status": the backward is four launches). Returns FFPA_ERR_INVALID_ARGUMENT for another stage.
  */
@@ -131,17 +135,18 @@ int ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float*
                     int hq, int hkv, int d, int dtype, float scale, int causal, void* stream);
 
 /*
- * Bytes of the optional dS workspace of ffpa_varlen_bwd: hq * total_q * round_up(max_seqlen_k, 8)
- * * 2, a bound on the packed per-sequence layout (sequence by sequence, then head, then
- * query row, keys padded to a multiple of 8) that holds for every cu_seqlens consistent with the
- * max_seqlen values; 0 when not available (see ffpa_bwd_workspace_bytes). Host function.
+ * Bytes of the optional P/dS workspace of ffpa_varlen_bwd:
+ * 2 * hq * total_q * round_up(max_seqlen_k, 8) * 2, two blocks (dS, then P), each bounding the
+ * packed per-sequence layout (sequence by sequence, then head, then query row, keys padded to a
+ * multiple of 8) for every cu_seqlens consistent with the max_seqlen values; 0 when not
+ * available (see ffpa_bwd_workspace_bytes). Host function.
  */
 size_t ffpa_varlen_bwd_workspace_bytes(int hq, int total_q, int max_seqlen_q, int max_seqlen_k);
 
 /*
  * Packed (THD) varlen backward; arguments as ffpa_varlen_fwd plus o, dout [total_q, hq, d],
  * the forward's lse [hq, total_q], a caller-owned fp32 workspace delta [hq, total_q], the
- * outputs dq [total_q, hq, d], dk, dv [total_k, hkv, d], and the optional dS workspace.
+ * outputs dq [total_q, hq, d], dk, dv [total_k, hkv, d], and the optional P/dS workspace.
  */
 int ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, float* delta, void* dq, void* dk, void* dv,

@@ -1,7 +1,7 @@
 """GPU parity of the four-stage backward (preprocess, dV, dK, dQ) against the float64 oracle.
 
-Every parity case runs both dQ paths: with the dS workspace (dK stores dS, dQ multiplies it by K)
-and without it (dQ recomputes S, P, dP and dS).
+Every parity case runs both paths: with the P/dS workspace (dK stores P and dS; dV = P^T dO and
+dQ = dS K are products) and without it (dV and dQ recompute S, P, dP and dS).
 """
 import math
 
@@ -69,14 +69,15 @@ def test_bwd_dense(lib, case, store_ds):
 
 
 def test_bwd_ds_path_matches_recompute(lib):
-    """The two dQ paths: dK and dV are the same launches (bit-identical); dQ agrees to fp32 order."""
+    """The two paths: dK is the same computation (bit-identical); dV and dQ agree to fp32 order."""
     q, k, v, do = W.dense_inputs(1, 4, 2, 161, 203, 512, BF, seed=26)
     for causal in (False, True):
         _, _, dq1, dk1, dv1 = _run_dense(lib, q, k, v, do, causal, None, True)
         _, _, dq2, dk2, dv2 = _run_dense(lib, q, k, v, do, causal, None, False)
-        assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
-        x, y = to64(dq1), to64(dq2)
-        assert np.linalg.norm(x - y) / np.linalg.norm(y) < 5e-3
+        assert torch.equal(dk1, dk2)
+        for a, b in ((dq1, dq2), (dv1, dv2)):
+            x, y = to64(a), to64(b)
+            assert np.linalg.norm(x - y) / np.linalg.norm(y) < 5e-3
 
 
 @PATHS
