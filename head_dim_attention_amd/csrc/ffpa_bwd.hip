@@ -30,9 +30,10 @@ namespace ffpa {
 #ifndef BWD_AHEAD
 #define BWD_AHEAD 2
 #endif
-// Cache policy of the dS stores (written once, read once by the dQ pass).
+// Cache policy of the dS and P stores (written once, read once by the dQ and dV passes):
+// non-temporal, system scope (nt sc1), the fastest of the policies measured for this pattern.
 #ifndef DS_STORE_CPOL
-#define DS_STORE_CPOL 2
+#define DS_STORE_CPOL 18
 #endif
 // Same, for the two-group dK/dQ kernel, whose MFMA phases run one wave per SIMD at a time.
 #ifndef PP_AHEAD_M1
@@ -802,15 +803,19 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
       p_rs = __builtin_amdgcn_make_buffer_rsrc((uint16_t*)p.pst + hoff, 0, nrec, 0x00020000);
     }
   };
-  // ---- phase M2: all-gather dS (quarter q gives B-operand words 2 (q % 2), +1 of k-block q / 2),
-  // then acc^T[d][own] += A[d][streamed] * dS[streamed][own], A read transposed from tile 1
-  auto m2 = [&](int st) {
+  // Stores of the pieces formed in V1, at the start of M2.
+  auto store_pieces = [&]() {
     if constexpr (STORE_DS) {
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, ds_piece), ds_rs, (int)ds_boff, 0,
                                              DS_STORE_CPOL);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, p_piece), p_rs, (int)ds_boff, 0,
                                              DS_STORE_CPOL);
     }
+  };
+  // ---- phase M2: all-gather dS (quarter q gives B-operand words 2 (q % 2), +1 of k-block q / 2),
+  // then acc^T[d][own] += A[d][streamed] * dS[streamed][own], A read transposed from tile 1
+  auto m2 = [&](int st) {
+    store_pieces();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       u32x2_t v = mine;
