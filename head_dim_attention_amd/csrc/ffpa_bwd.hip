@@ -35,6 +35,15 @@ namespace ffpa {
 #ifndef DS_STORE_CPOL
 #define DS_STORE_CPOL 18
 #endif
+// LDS reads requested ahead of the MFMA issuing in the dQ-from-dS and dV-from-P products (each
+// A operand is two transposed reads used by two MFMAs).
+#ifndef PROD_AHEAD
+#define PROD_AHEAD 6
+#endif
+// Depth of the product passes' tile rings (copies are issued PROD_NBUF - 1 steps ahead).
+#ifndef PROD_NBUF
+#define PROD_NBUF 3
+#endif
 // Same, for the two-group dK/dQ kernel, whose MFMA phases run one wave per SIMD at a time.
 #ifndef PP_AHEAD_M1
 #define PP_AHEAD_M1 2
@@ -824,10 +833,13 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
       bop[q >> 1][2 * (q & 1) + 1] = v.y;
     }
     const uint32_t t1 = t1_addr(st);
+    // k-block outer, head-dim block inner: consecutive MFMAs use different accumulators (two
+    // dependent MFMAs in a row issue 44 instead of 32 cycles apart, and here only one wave per
+    // SIMD is multiplying).
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int db = 0; db < NDB; ++db) {
         const s16x4_t lo = lds_read_tr16_at(t_addr(t1, db, kb2, 0));
         const s16x4_t hi = lds_read_tr16_at(t_addr(t1, db, kb2, 1));
         const u32x4_t bv = {bop[kb2][0], bop[kb2][1], bop[kb2][2], bop[kb2][3]};
@@ -946,7 +958,7 @@ struct DqCfg {
   static constexpr int KTILE = 32 * RS;
   static constexpr int STILE = BQ * 64;        // dS block: BQ rows x 32 keys x 2 bytes
   static constexpr int STAGE = KTILE + STILE;
-  static constexpr int NBUF = 3;
+  static constexpr int NBUF = PROD_NBUF;
   static constexpr int LDS = NBUF * STAGE;
   static constexpr int KCOPY = KTILE / 1024 / NW;  // K copies per wave per step
   static constexpr int SCOPY = STILE / 1024 / NW;  // dS copies per wave per step
@@ -1058,24 +1070,26 @@ __global__ void __launch_bounds__(512, 2) ffpa_dq_from_ds_kernel(AttnParams p, i
     return tile + C::KTILE + r * 64 + (((2 * kb2 + hh) ^ ((r >> 2) & 3)) << 4);
   };
 
+  constexpr int NB = C::NBUF;
   if (nsteps > 0) {
 #pragma unroll
-    for (int c = 0; c < NCOPY; ++c) copy(0, 0, c);
+    for (int b = 0; b < NB - 1; ++b)
 #pragma unroll
-    for (int c = 0; c < NCOPY; ++c) copy(min(1, nsteps - 1), 1, c);
+      for (int c = 0; c < NCOPY; ++c) copy(min(b, nsteps - 1), b, c);
   }
   wait_all();
 
-  int buf = 0;  // j % 3
+  int buf = 0;  // j % NB
   for (int j = 0; j < nsteps; ++j) {
-    // In flight: the copies of step j (issued during step j - 2) and then those of step j + 1.
-    wait_vmcnt<NCOPY>();
+    // In flight: the copies of step j (issued during step j - NB + 1) and then those of the NB - 2
+    // steps after it.
+    wait_vmcnt<(NB - 2) * NCOPY>();
     lds_barrier();  // step j's tiles are visible; every wave has finished step j - 1
     const uint32_t tile = lds_addr(smem + buf * C::STAGE);
-    // Step j + 2 goes into the buffer of step j - 1 (released by the barrier above); past the end
-    // the last step is copied again into a buffer that is not read any more.
-    const int jn = min(j + 2, nsteps - 1);
-    const int bn = buf == 0 ? 2 : buf - 1;
+    // Step j + NB - 1 goes into the buffer of step j - 1 (released by the barrier above); past the
+    // end the last step is copied again into a buffer that is not read any more.
+    const int jn = min(j + NB - 1, nsteps - 1);
+    const int bn = buf == 0 ? NB - 1 : buf - 1;
 
     // dS^T operands of both query blocks; masked where the key is not legal.
     u32x4_t bs[C::QB][2];
@@ -1119,7 +1133,8 @@ __global__ void __launch_bounds__(512, 2) ffpa_dq_from_ds_kernel(AttnParams p, i
         }
       }
     }
-    buf = buf == 2 ? 0 : buf + 1;
+    pin_lds_mfma_pipeline<NMMA, PROD_AHEAD, 1>();
+    buf = buf == NB - 1 ? 0 : buf + 1;
   }
   // Copies issued during the last step land in LDS that the next workgroup may own.
   wait_vmcnt<0>();
@@ -1195,7 +1210,7 @@ struct DvCfg {
   static constexpr int PROW = BK * 2;          // P block row: 128 keys x 2 bytes
   static constexpr int PTILE = 32 * PROW;
   static constexpr int STAGE = OTILE + PTILE;
-  static constexpr int NBUF = 3;
+  static constexpr int NBUF = PROD_NBUF;
   static constexpr int LDS = NBUF * STAGE;
   static constexpr int OCOPY = OTILE / 1024 / NW;
   static constexpr int PCOPY = PTILE / 1024 / NW;
@@ -1316,23 +1331,26 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
     return tile + C::OTILE + row * C::PROW + ((((byte >> 4) ^ (4 * (row & 3))) << 4) | (byte & 15));
   };
 
+  constexpr int NB = C::NBUF;
   if (nsteps > 0) {
-    const StepSrc x0 = step_src(0), x1 = step_src(1);
 #pragma unroll
-    for (int c = 0; c < NCOPY; ++c) copy(x0, 0, c);
+    for (int b = 0; b < NB - 1; ++b) {
+      const StepSrc xb = step_src(b);
 #pragma unroll
-    for (int c = 0; c < NCOPY; ++c) copy(x1, 1, c);
+      for (int c = 0; c < NCOPY; ++c) copy(xb, b, c);
+    }
   }
   wait_all();
 
-  int buf = 0;  // st % 3
+  int buf = 0;  // st % NB
   for (int st = 0; st < nsteps; ++st) {
-    // In flight: the copies of step st (issued during step st - 2) and then those of step st + 1.
-    wait_vmcnt<NCOPY>();
+    // In flight: the copies of step st (issued during step st - NB + 1) and then those of the
+    // NB - 2 steps after it.
+    wait_vmcnt<(NB - 2) * NCOPY>();
     lds_barrier();  // step st's tiles are visible; every wave has finished step st - 1
     const uint32_t tile = lds_addr(smem + buf * C::STAGE);
-    const int bn = buf == 0 ? 2 : buf - 1;  // the buffer of step st - 1
-    const StepSrc xn = step_src(st + 2);
+    const int bn = buf == 0 ? NB - 1 : buf - 1;  // the buffer of step st - 1
+    const StepSrc xn = step_src(st + NB - 1);
     const int row0 = step_row0(st);
 
     u32x4_t bp[C::KB][2];
@@ -1378,7 +1396,8 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
         }
       }
     }
-    buf = buf == 2 ? 0 : buf + 1;
+    pin_lds_mfma_pipeline<NMMA, PROD_AHEAD, 1>();
+    buf = buf == NB - 1 ? 0 : buf + 1;
   }
   // Copies issued during the last steps land in LDS that the next workgroup may own.
   wait_vmcnt<0>();
