@@ -78,6 +78,8 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   const int rg = w / NC;
   const int cg = w % NC;
   const int qw0 = qt0 + rg * QB * 32;
+  // Eight waves with double-buffered 1 KB-row tiles run the two-group schedule below.
+  constexpr bool kPingPong = NW == 8 && NBUF == 2 && NC == 2 && C::RS == 1024;
 
   const uint16_t* qh = (const uint16_t*)p.q + sv.q_off + (long long)h * p.q_head;
   const int row_bytes = p.k_row * 2;
@@ -196,8 +198,9 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     }
   };
 
-  // Full S^T (keys x queries) of tile j for this wave's query block, masked.
-  auto scores = [&](int j, f32x16_t (&sacc)[QB]) {
+  // Partial S^T (keys x queries) of tile j over this wave's head-dim columns, written to the
+  // exchange buffer; copy_at(kb) issues the tile copies assigned to k-step kb.
+  auto s_partial = [&](int j, f32x16_t (&sacc)[QB], auto&& copy_at) {
     const lds_t* kt = kbuf(NBUF == 2 ? (j & 1) : 0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) sacc[qb] = (f32x16_t){};
@@ -206,11 +209,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
       const u32x4_t a = lds_read_b128_at(k_addr(lds_addr(kt), kb));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) sacc[qb] = Elt<T>::mma(a, qreg[qb][kb], sacc[qb]);
-      if constexpr (NBUF == 2) {
-#pragma unroll
-        for (int ii = 0; ii < C::NINSTR; ++ii)
-          if (kb == spread_at(2 * NDB, ii)) issue1(krs, j + 1, kbuf((j + 1) & 1), ii);
-      }
+      copy_at(kb);
     }
     if constexpr (QB == 1) pin_lds_mfma_pipeline<2 * NDB, FWD_AHEAD, 1>();
 #pragma unroll
@@ -219,13 +218,10 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
       for (int r4 = 0; r4 < 4; ++r4)
         lds_write_f4(xbuf, (((w * QB + qb) * 4 + r4) * 64 + lane) * 16,
                      (f32x4_t){sacc[qb][4 * r4], sacc[qb][4 * r4 + 1], sacc[qb][4 * r4 + 2], sacc[qb][4 * r4 + 3]});
-    // In flight: V_j (issued during P V of step j - 1), then K_{j+1}. V_j is needed after this
-    // barrier.
-    if constexpr (NBUF == 2) wait_vmcnt<C::NINSTR>();
-    lds_barrier();
-    if constexpr (NBUF == 1) {
-      if (j + 1 < ntk) issue(krs, j + 1, kbuf(0));
-    }
+  };
+
+  // Full S^T of tile j (after the barrier that makes the partners' partial sums visible), masked.
+  auto s_combine = [&](int j, f32x16_t (&sacc)[QB]) {
     // Add the partial sums of the row group's waves in a fixed commutative pattern, so that
     // every wave of the row group ends with bit-identical scores.
 #pragma unroll
@@ -256,6 +252,25 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
           if (j * 32 + c_row(r, hh) > lim) sacc[qb][r] = -INFINITY;
       }
     }
+  };
+
+  // Full S^T of tile j, all eight waves in step (the loop without the two-group schedule).
+  auto scores = [&](int j, f32x16_t (&sacc)[QB]) {
+    s_partial(j, sacc, [&](int kb) {
+      if constexpr (NBUF == 2) {
+#pragma unroll
+        for (int ii = 0; ii < C::NINSTR; ++ii)
+          if (kb == spread_at(2 * NDB, ii)) issue1(krs, j + 1, kbuf((j + 1) & 1), ii);
+      }
+    });
+    // In flight: V_j (issued during P V of step j - 1), then K_{j+1}. V_j is needed after this
+    // barrier.
+    if constexpr (NBUF == 2) wait_vmcnt<C::NINSTR>();
+    lds_barrier();
+    if constexpr (NBUF == 1) {
+      if (j + 1 < ntk) issue(krs, j + 1, kbuf(0));
+    }
+    s_combine(j, sacc);
   };
 
   // P = exp2(S * scale*log2e - mref), l += rowsum P, packed as B operands.
@@ -290,11 +305,8 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     }
   };
 
-  auto pv = [&](int j, const uint32_t (&pb)[QB][2][4]) {
-    if constexpr (NBUF == 1) {
-      if (j + 1 < ntk) wait_vmcnt<C::NINSTR>(); else wait_vmcnt<0>();  // V_j has landed
-      lds_barrier();
-    }
+  // O^T += V^T P^T for tile j; copy_at(m) issues the copies assigned to MFMA m.
+  auto pv_mma = [&](int j, const uint32_t (&pb)[QB][2][4], auto&& copy_at) {
     const lds_t* vt = vbuf(NBUF == 2 ? (j & 1) : 0);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -308,14 +320,23 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
           const u32x4_t bop = {pb[qb][kb2][0], pb[qb][kb2][1], pb[qb][kb2][2], pb[qb][kb2][3]};
           oacc[qb][db] = Elt<T>::mma(a, bop, oacc[qb][db]);
         }
-        if constexpr (NBUF == 2) {
-#pragma unroll
-          for (int ii = 0; ii < C::NINSTR; ++ii)
-            if (2 * db + kb2 == spread_at(2 * NDB, ii)) issue1(vrs, j + 1, vbuf((j + 1) & 1), ii);
-        }
+        copy_at(2 * db + kb2);
       }
     }
     if constexpr (QB == 1) pin_lds_mfma_pipeline<2 * NDB, FWD_AHEAD, 2>();
+  };
+  auto pv = [&](int j, const uint32_t (&pb)[QB][2][4]) {
+    if constexpr (NBUF == 1) {
+      if (j + 1 < ntk) wait_vmcnt<C::NINSTR>(); else wait_vmcnt<0>();  // V_j has landed
+      lds_barrier();
+    }
+    pv_mma(j, pb, [&](int m) {
+      if constexpr (NBUF == 2) {
+#pragma unroll
+        for (int ii = 0; ii < C::NINSTR; ++ii)
+          if (m == spread_at(2 * NDB, ii)) issue1(vrs, j + 1, vbuf((j + 1) & 1), ii);
+      }
+    });
     if constexpr (NBUF == 1) {
       lds_barrier();
       if (j + 1 < ntk) issue(vrs, j + 1, vbuf(0));
@@ -329,11 +350,94 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   // The Q operands (and tile 0) are complete before the loop, so the loop never waits for them.
   wait_all();
 
+  f32x16_t sacc[QB];
+  if constexpr (kPingPong) {
+    // Two-group schedule (eight waves, double-buffered K and V). Waves 0-3 (query row groups 0 and
+    // 1) and waves 4-7 (row groups 2 and 3) form two groups; the two waves of a SIMD belong to
+    // different groups. Each step is two slots separated by barriers:
+    //   slot 0: group 0 forms partial scores of tile j | group 1 finishes tile j - 1 (exchange,
+    //           softmax, P V)
+    //   slot 1: group 0 finishes tile j                 | group 1 forms partial scores of tile j
+    // so in every slot one wave of each SIMD multiplies scores while the other does the softmax
+    // and then multiplies P V. Group 0 copies K of tile j + 1 during its score MFMAs (K_{j-1},
+    // last read in slot 1 of step j - 1, has been released) and completes it before slot 0 of
+    // step j + 1; group 1 copies V of tile j + 1 during its score MFMAs (V_{j-1}, last read in
+    // slot 0 of step j, has been released) and completes it before slot 1 of step j + 1. Every
+    // wave keeps its own exchange slot, which its partner reads in the next slot.
+    const int grp = w >> 2, wg = w & 3;
+    constexpr int GCOPY = 2 * C::NINSTR;  // 1 KB copies per wave of the group's tile
+    int gvoff[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) gvoff[ii] = min(lane ^ swz(wg + 4 * ii), dch - 1) << 4;
+    const i32x4_t grs = grp == 0 ? krs : vrs;
+    auto gcopy = [&](int j, int ii) {
+      const int i = wg + 4 * ii;
+      lds_t* dst = (grp == 0 ? kbuf(j & 1) : vbuf(j & 1)) + i * 1024;
+      dma16_buf(grs, gvoff[ii & 3], min(j * 32 + i, sv.lk - 1) * row_bytes, dst);
+    };
+    auto s_phase = [&](int j) {
+      s_partial(j, sacc, [&](int kb) {
+#pragma unroll
+        for (int ii = 0; ii < GCOPY; ++ii)
+          if (kb == (ii * 2 * NDB) / GCOPY) gcopy(j + 1, ii);
+      });
+    };
+    auto p_phase = [&](int j) {
+      s_combine(j, sacc);
+      // Online softmax with a lazily updated reference max: a row's reference is its first finite
+      // tile max, raised (with the matching rescale of O and l) only when a tile max exceeds it
+      // by more than 2^8; exp2 then stays below 256.
+      float mt[QB];
+      tile_max(sacc, mt);
+      bool grow = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (mref[qb] == -INFINITY) mref[qb] = mt[qb];
+        grow |= mt[qb] > mref[qb] + 8.0f;
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const bool nd = mt[qb] > mref[qb] + 8.0f;
+          const float alpha = nd ? fast_exp2(mref[qb] - mt[qb]) : 1.0f;
+          if (nd) mref[qb] = mt[qb];
+          lsum[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
+        }
+      }
+      uint32_t pb[QB][2][4];
+      make_p(sacc, pb);
+      pv_mma(j, pb, [](int) {});
+    };
+    lds_barrier();
+    if (ntk > 0) {
+      if (grp == 0) {
+        for (int j = 0; j < ntk; ++j) {
+          s_phase(j);
+          lds_barrier();
+          p_phase(j);
+          wait_vmcnt<0>();  // K_{j+1}
+          lds_barrier();
+        }
+        lds_barrier();
+      } else {
+        lds_barrier();
+        for (int j = 0; j < ntk; ++j) {
+          s_phase(j);
+          lds_barrier();
+          p_phase(j);
+          wait_vmcnt<0>();  // V_{j+1}
+          lds_barrier();
+        }
+      }
+    }
+  } else {
+
   // ---- fast loop: the reference max of a row is fixed at its first finite tile max. The loop
   // leaves (per wave) as soon as a tile max exceeds the reference by more than 2^8, so O never
   // needs rescaling here and exp2 stays below 256.
   int j = 0;
-  f32x16_t sacc[QB];
   for (; j < ntk; ++j) {
     top(j);
     scores(j, sacc);
@@ -373,6 +477,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     make_p(sacc, pb);
     pv(j, pb);
   }
+  }  // !kPingPong
 
   // Copies issued during the last step land in LDS that the next workgroup may own.
   wait_vmcnt<0>();
