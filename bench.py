@@ -3,11 +3,12 @@
 
 Metric: attention TFLOPS (forward, and forward+backward) at D=512, N=8192, bf16, as a fraction
 of the dense bf16 MFMA peak. A step is one pass of the whole path over one batch of synthetic
-inputs already resident in HBM: the forward kernel, then the four backward launches
-(preprocess, dK, dV, dQ). Credited flops per legal (query, key) pair and query head: 4*D forward,
+inputs already resident in HBM: the forward kernel, then the backward launches (preprocess,
+P/dS, dK, dV, dQ). Credited flops per legal (query, key) pair and query head: 4*D forward,
 10*D backward (the recomputation inside the backward is not credited). By default the backward
-runs with the library's P/dS workspace (dK stores P and dS, dV = P^T dO and dQ = dS K are
-products); --no-ds-workspace times the recomputing dV and dQ kernels instead.
+runs with the library's P/dS workspace (one kernel forms and stores P and dS; dK = dS^T Q,
+dV = P^T dO and dQ = dS K are products of them); --no-ds-workspace times the recomputing dK, dV
+and dQ kernels instead (the P/dS launch is then empty).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line (rank 0).
@@ -32,10 +33,14 @@ METRIC = "attention TFLOPS (fwd, fwd+bwd) at D=512 N=8192 bf16; % of MFMA peak"
 PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
 # Algorithmic flops per legal pair and query head, by kernel (D multiplies these). Recomputing, dV
-# does 4 D (S, P^T dO) and dQ 6 D (S, dP, dS K); with the stored P and dS each is one product, 2 D.
-KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "dv": 4, "dk": 6, "dq": 6}
-STORED_FLOPS_PER_PAIR_D = {"dv": 2, "dq": 2}
-STAGES = ("fwd", "pre", "dk", "dv", "dq")
+# does 4 D (S, P^T dO), dK and dQ 6 D (S, dP, one product); with the stored P and dS the P/dS
+# kernel does 4 D (S, dP) and dK, dV, dQ are one product each, 2 D.
+KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "pds": 0, "dk": 6, "dv": 4, "dq": 6}
+STORED_FLOPS_PER_PAIR_D = {"pds": 4, "dk": 2, "dv": 2, "dq": 2}
+# (name, ffpa_bwd_stage index) of the timed launches after the forward, in ffpa_bwd's order.
+BWD_STAGES = (("pre", 0), ("pds", 4), ("dk", 1), ("dv", 2), ("dq", 3))
+STAGES = ("fwd",) + tuple(n for n, _ in BWD_STAGES)
+COMPUTE_KERNELS = ("fwd", "pds", "dk", "dv", "dq")
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "traffic_dense_d512_n8192.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "head_dim_attention_amd", "csrc", f)
                   for f in ("ffpa_device.h", "ffpa_params.h", "ffpa_fwd.hip", "ffpa_bwd.hip")]
@@ -177,6 +182,8 @@ def main(argv=None) -> int:
     flops_d = dict(KERNEL_FLOPS_PER_PAIR_D)
     if ws is not None:
         flops_d.update(STORED_FLOPS_PER_PAIR_D)
+        if d > 512:  # the dK kernel recomputes and stores P and dS itself; the P/dS launch is empty
+            flops_d.update({"pds": 0, "dk": 6})
     dt = 0 if w.dtype == "bf16" else 1
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -193,7 +200,7 @@ def main(argv=None) -> int:
         if st:
             raise RuntimeError(F.ffpa_status_string(st))
 
-    launches = [fwd, lambda: bwd_stage(0), lambda: bwd_stage(1), lambda: bwd_stage(2), lambda: bwd_stage(3)]
+    launches = [fwd] + [(lambda i=i: bwd_stage(i)) for _, i in BWD_STAGES]
 
     for _ in range(args.warmup):
         for fn in launches:
@@ -224,12 +231,14 @@ def main(argv=None) -> int:
     fwd_tflops = fwd_flops / (stage_ms["fwd"] * 1e-3) / 1e12
 
     # Dominant kernel: the longest of the compute kernels.
-    dom = max(("fwd", "dv", "dk", "dq"), key=lambda n: stage_ms[n])
+    dom = max((n for n in COMPUTE_KERNELS if flops_d[n] > 0), key=lambda n: stage_ms[n])
     dom_flops = flops_d[dom] * d * pairs
     achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
     traffic = load_traffic(dom)
     kernels = {}
-    for n in ("fwd", "dv", "dk", "dq"):
+    for n in COMPUTE_KERNELS:
+        if flops_d[n] == 0:
+            continue
         fl = flops_d[n] * d * pairs
         kernels[n] = {"ms": round(stage_ms[n], 4), "algorithmic_tflops": round(fl / (stage_ms[n] * 1e-3) / 1e12, 2),
                       "frac": round(fl / (stage_ms[n] * 1e-3) / 1e12 / PEAK_TFLOPS, 4)}
@@ -257,8 +266,8 @@ def main(argv=None) -> int:
         "fwdbwd_frac_of_peak": round(value / PEAK_TFLOPS, 4),
         "peak_tflops": PEAK_TFLOPS,
         "event_ms_per_step": round(step_ms, 4),
-        "bwd_path": (f"stored P and dS ({ws_bytes / 2**30:.2f} GiB workspace): dV = P^T dO, dQ = dS K"
-                     if ws is not None else "dV and dQ recompute S, P (dP, dS)"),
+        "bwd_path": (f"stored P and dS ({ws_bytes / 2**30:.2f} GiB workspace): dK = dS^T Q, dV = P^T dO, dQ = dS K"
+                     if ws is not None else "dK, dV and dQ recompute S, P (dP, dS)"),
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic},

@@ -46,7 +46,7 @@ _SIGNATURES = {
 }
 _SIZE_FUNCTIONS = {
     "ffpa_bwd_workspace_bytes": [_i] * 4,
-    "ffpa_varlen_bwd_workspace_bytes": [_i] * 4,
+    "ffpa_varlen_bwd_workspace_bytes": [_i] * 5,
 }
 
 
@@ -150,10 +150,11 @@ def ffpa_bwd_workspace_bytes(batch: int, hq: int, nq: int, nkv: int) -> int:
     return int(load_library().ffpa_bwd_workspace_bytes(int(batch), int(hq), int(nq), int(nkv)))
 
 
-def ffpa_varlen_bwd_workspace_bytes(hq: int, total_q: int, max_seqlen_q: int, max_seqlen_k: int) -> int:
+def ffpa_varlen_bwd_workspace_bytes(hq: int, total_q: int, total_k: int, max_seqlen_q: int,
+                                    max_seqlen_k: int) -> int:
     """Bytes of the optional P/dS workspace of the varlen backward (0: not available)."""
-    return int(load_library().ffpa_varlen_bwd_workspace_bytes(int(hq), int(total_q), int(max_seqlen_q),
-                                                               int(max_seqlen_k)))
+    return int(load_library().ffpa_varlen_bwd_workspace_bytes(int(hq), int(total_q), int(total_k),
+                                                               int(max_seqlen_q), int(max_seqlen_k)))
 
 
 def _workspace(nbytes: int, like: torch.Tensor):
@@ -166,9 +167,9 @@ def _workspace(nbytes: int, like: torch.Tensor):
 def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float] = None, store_ds: bool = True):
     """Dense backward -> (dq, dk, dv) with the shapes and dtype of q, k, v.
 
-    store_ds: let the dK stage store P and dS in a temporary workspace of ffpa_bwd_workspace_bytes()
-    bytes so that dV = P^T dO and dQ = dS K are products instead of recomputations (False: O(N)
-    memory, recompute).
+    store_ds: store P and dS in a temporary workspace of ffpa_bwd_workspace_bytes() bytes so that
+    dK = scale dS^T Q, dV = P^T dO and dQ = scale dS K are products instead of recomputations
+    (False: O(N) memory, recompute).
     """
     q, k, v, o, dout = (_dev(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")))
     lse = _dev(lse, "lse")
@@ -191,11 +192,13 @@ def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float]
 
 def ffpa_bwd_stage(stage: int, q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool = False,
                    scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
-    """Run one backward stage (0 preprocess, 1 dK, 2 dV, 3 dQ) into caller-provided buffers.
+    """Run one backward stage (0 preprocess, 4 P and dS, 1 dK, 2 dV, 3 dQ) into caller buffers.
 
-    All tensors must be contiguous GPU tensors with ffpa_bwd's shapes; delta is float32 [B,Hq,Nq].
-    workspace: optional P/dS workspace (a GPU tensor of at least ffpa_bwd_workspace_bytes() bytes),
-    the same for stages 1, 2 and 3 (stage 1 fills it, stages 2 and 3 read it).
+    ffpa_bwd runs the stages in the order 0, 4, 1, 2, 3. All tensors must be contiguous GPU tensors
+    with ffpa_bwd's shapes; delta is float32 [B,Hq,Nq]. workspace: optional P/dS workspace (a GPU
+    tensor of at least ffpa_bwd_workspace_bytes() bytes), the same for stages 4, 1, 2 and 3: stage 4
+    fills it (for D > 512 stage 1 does), and stages 1, 2 and 3 read it. Without a workspace stage 4
+    launches nothing and stages 1-3 recompute.
     """
     if workspace is not None and not (isinstance(workspace, torch.Tensor) and workspace.device.type == "cuda"
                                       and workspace.is_contiguous()):
@@ -284,7 +287,7 @@ def ffpa_varlen_bwd(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k=None, max_
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     delta = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
-    ws, nws = _workspace(ffpa_varlen_bwd_workspace_bytes(hq, tq, max_q, max_k) if store_ds else 0, q)
+    ws, nws = _workspace(ffpa_varlen_bwd_workspace_bytes(hq, tq, tk, max_q, max_k) if store_ds else 0, q)
     st = load_library().ffpa_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
                                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_q), _ptr(cu_k), cu_q.numel() - 1,
                                         max_q, max_k, tq, tk, hq, hkv, d, _dtype_code(q), _scale(scale, d),

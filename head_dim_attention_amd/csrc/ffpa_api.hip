@@ -84,19 +84,21 @@ bool too_big_dense(int batch, int h, int n, int d) {
 
 long long round_up8(long long x) { return (x + 7) & ~7LL; }
 
-// Bytes of one head's stored dS (or P) block of nq rows of round_up8(nkv) elements; the dQ and
-// dV passes address it with 32-bit byte offsets, so larger blocks use the recomputing kernels.
-bool ds_block_ok(long long nq, long long nkv) { return nq * round_up8(nkv) * 2 <= (1LL << 31) - 4096; }
+// Bytes of one head's stored dS (or P) block, transposed: nkv rows of round_up8(nq) elements; the
+// kernels address it with 32-bit byte offsets, so larger blocks use the recomputing kernels.
+bool ds_block_ok(long long nq, long long nkv) { return nkv * round_up8(nq) * 2 <= (1LL << 31) - 4096; }
 
 // The workspace holds two equal blocks: dS, then P.
 size_t dense_ds_bytes(int batch, int hq, int nq, int nkv) {
   if (batch < 1 || hq < 1 || nq < 1 || nkv < 1 || !ds_block_ok(nq, nkv)) return 0;
-  return 2 * (size_t)batch * hq * nq * round_up8(nkv) * 2;
+  return 2 * (size_t)batch * hq * nkv * round_up8(nq) * 2;
 }
 
-size_t varlen_ds_bytes(int hq, int total_q, int max_q, int max_k) {
-  if (hq < 1 || total_q < 1 || max_q < 1 || max_k < 1 || !ds_block_ok(max_q, max_k)) return 0;
-  return 2 * (size_t)hq * total_q * round_up8(max_k) * 2;
+// Sequence s needs Lk_s * round_up8(Lq_s) elements per head and block, at most
+// Lk_s * round_up8(max_q); the sum over sequences is at most total_k * round_up8(max_q).
+size_t varlen_ds_bytes(int hq, int total_q, int total_k, int max_q, int max_k) {
+  if (hq < 1 || total_q < 1 || total_k < 1 || max_q < 1 || max_k < 1 || !ds_block_ok(max_q, max_k)) return 0;
+  return 2 * (size_t)hq * total_k * round_up8(max_q) * 2;
 }
 
 // Attach a caller workspace for dS and P. NULL selects the recomputing dV and dQ kernels; a
@@ -156,7 +158,7 @@ static int dense_bwd(int stage, const void* q, const void* k, const void* v, con
                      const float* lse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv,
                      int nq, int nkv, int d, int dtype, float scale, int causal, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  if (stage < -1 || stage > 3) return FFPA_ERR_INVALID_ARGUMENT;
+  if (stage < -1 || stage > 4) return FFPA_ERR_INVALID_ARGUMENT;
   if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
   const int st = check_common(hq, hkv, d, dtype, scale, causal);
@@ -177,16 +179,16 @@ static int dense_bwd(int stage, const void* q, const void* k, const void* v, con
   p.dv = dv;
   const int ws = attach_ds(p, workspace, workspace_bytes, dense_ds_bytes(batch, hq, nq, nkv));
   if (ws != FFPA_OK) return ws;
-  p.ds_row = (int)round_up8(nkv);
-  p.ds_head = (long long)nq * p.ds_row;
+  p.ds_row = (int)round_up8(nq);
+  p.ds_head = (long long)nkv * p.ds_row;
   p.ds_batch = (long long)hq * p.ds_head;
   return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, (int)nrows, 0, (hipStream_t)stream, stage));
 }
 
 size_t ffpa_bwd_workspace_bytes(int batch, int hq, int nq, int nkv) { return dense_ds_bytes(batch, hq, nq, nkv); }
 
-size_t ffpa_varlen_bwd_workspace_bytes(int hq, int total_q, int max_seqlen_q, int max_seqlen_k) {
-  return varlen_ds_bytes(hq, total_q, max_seqlen_q, max_seqlen_k);
+size_t ffpa_varlen_bwd_workspace_bytes(int hq, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k) {
+  return varlen_ds_bytes(hq, total_q, total_k, max_seqlen_q, max_seqlen_k);
 }
 
 int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -200,7 +202,7 @@ int ffpa_bwd_stage(int stage, const void* q, const void* k, const void* v, const
                    const float* lse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq,
                    int nkv, int d, int dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
                    void* stream) {
-  if (stage < 0 || stage > 3) return FFPA_ERR_INVALID_ARGUMENT;
+  if (stage < 0 || stage > 4) return FFPA_ERR_INVALID_ARGUMENT;
   return dense_bwd(stage, q, k, v, o, dout, lse, delta, dq, dk, dv, batch, hq, hkv, nq, nkv, d, dtype, scale, causal,
                    workspace, workspace_bytes, stream);
 }
@@ -239,7 +241,7 @@ int ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, 
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  const int ws = attach_ds(p, workspace, workspace_bytes, varlen_ds_bytes(hq, total_q, max_seqlen_q, max_seqlen_k));
+  const int ws = attach_ds(p, workspace, workspace_bytes, varlen_ds_bytes(hq, total_q, total_k, max_seqlen_q, max_seqlen_k));
   if (ws != FFPA_OK) return ws;
   return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, total_q * hq, total_q, (hipStream_t)stream, -1));
 }

@@ -385,7 +385,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
     } else {
       need_mask = (row0 + 32 > sv.lq) || (p.causal && ow0 + 31 > row0 + off);
     }
-    uint32_t bop[2][4];
+    uint32_t bop[2][4], ppk[2][4];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       float v2[2], pv2[2] = {0.f, 0.f};
@@ -406,22 +406,30 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
         v2[u] = pv;
       }
       bop[r >> 3][(r & 7) >> 1] = Elt<T>::pack2(v2[0], v2[1]);
-      if constexpr (MODE == kDK) {
-        // Optionally store the rounded dS and P (the values a product uses) for dQ and dV.
-        if (store_ds && oi < sv.lk) {
-          const uint32_t pk = bop[r >> 3][(r & 7) >> 1];
-          const uint32_t pp = Elt<T>::pack2(pv2[0], pv2[1]);
-          const long long hoff = dsv.base + (long long)step_head(st) * dsv.head + oi;
-          uint16_t* dsp = (uint16_t*)p.ds + hoff;
-          uint16_t* psp = (uint16_t*)p.pst + hoff;
+      if constexpr (MODE == kDK) ppk[r >> 3][(r & 7) >> 1] = Elt<T>::pack2(pv2[0], pv2[1]);
+    }
+    if constexpr (MODE == kDK) {
+      // Optionally store the rounded dS and P (the values the products use), transposed: registers
+      // 8 kb2 .. 8 kb2 + 7 of key oi are queries row0 + 16 kb2 + 8 h + 0..7, one 16-byte piece of
+      // the key's row. Every wave of the row group holds the same values; piece i (dS or P, kb2)
+      // is stored by the wave with cg = i % NC. Keys at or past Lk and pieces starting at or past
+      // the padded row end get an offset past the block, which the buffer range check discards.
+      if (store_ds) {
+        const long long hoff = dsv.base + (long long)step_head(st) * dsv.head;
+        const int nrec = (int)((long long)sv.lk * dsv.row * 2);
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int qi = row0 + c_row(r + u, hh);
-            if (qi < sv.lq) {
-              dsp[(long long)qi * dsv.row] = (uint16_t)(u ? pk >> 16 : pk & 0xffff);
-              psp[(long long)qi * dsv.row] = (uint16_t)(u ? pp >> 16 : pp & 0xffff);
-            }
-          }
+        for (int pi = 0; pi < 4; ++pi) {
+          if (pi % NC != cg) continue;
+          const int kb2 = pi & 1;
+          const bool is_p = pi >= 2;
+          const __amdgpu_buffer_rsrc_t rs =
+              __builtin_amdgcn_make_buffer_rsrc((uint16_t*)(is_p ? p.pst : p.ds) + hoff, 0, nrec, 0x00020000);
+          const int q8 = row0 + 16 * kb2 + 8 * hh;
+          const bool ok = oi < sv.lk && q8 < dsv.row;
+          const uint32_t boff = ok ? (uint32_t)(((long long)oi * dsv.row + q8) * 2) : 0xFFFFFFF0u;
+          const uint32_t(&src)[4] = is_p ? ppk[kb2] : bop[kb2];
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, (u32x4_t){src[0], src[1], src[2], src[3]}),
+                                                 rs, (int)boff, 0, DS_STORE_CPOL);
         }
       }
     }
@@ -512,18 +520,16 @@ struct PpCfg {
   static constexpr int X_OFF = 4 * TILE;         // [cg][3 partner quarters][S, dP] pieces
   static constexpr int G_OFF = X_OFF + NC * 3 * 2 * PIECE;  // [cg] packed dS quarter, 8 B/lane
   static constexpr int ST_OFF = G_OFF + NC * 64 * 8;        // [buffer][LSE, Delta] x 64 floats
-  static constexpr int P_OFF = ST_OFF + 2 * 2 * 256;        // [cg] packed P quarter (when stored)
-  static constexpr int LDS = P_OFF + NC * 64 * 8;
+  static constexpr int LDS = ST_OFF + 2 * 2 * 256;
   static constexpr int NCOPY = TILE / 1024 / 4;  // copies per wave of a tile (one group copies it)
   static constexpr int KSTEPS = 2 * NDB;         // k-steps of the partial products
   static constexpr int KA = (3 * KSTEPS) / 4;    // k-steps in M1a (M1b shares its slot with M2)
   static_assert(4 * DW <= 512 && LDS <= 160 * 1024, "LDS budget");
 };
 
-template <class T, int MODE, int NDB, bool STORE_DS>
+template <class T, int MODE, int NDB>
 __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
   static_assert(MODE == kDQ || MODE == kDK, "dK and dQ only");
-  static_assert(!STORE_DS || MODE == kDK, "dS and P are stored by the dK kernel");
   constexpr bool OWN_Q = MODE == kDQ;
   using C = PpCfg<NDB>;
   constexpr int NC = C::NC;
@@ -544,9 +550,6 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
   const int own_len = OWN_Q ? sv.lq : sv.lk;
   const int o0 = t * C::BOWN;
   if (o0 >= own_len) return;
-  // dK can also store dS for a dQ pass that multiplies it by K (no recomputation there).
-  DsView dsv{};
-  if constexpr (STORE_DS) dsv = ds_view(p, s, sv);
 
   const int w = wave_id();
   const int lane = threadIdx.x & 63;
@@ -735,14 +738,6 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
   };
   // ---- phase V1: reduce this wave's quarter (own part + partners in a fixed order), P and dS
   u32x2_t mine;
-  // dS and P row pieces of this lane, their byte offset (the same in both blocks) and the head
-  // blocks' buffer resources: formed in V1, stored at the start of M2 (so that V1 does not wait
-  // for the transposed reads).
-  u32x4_t ds_piece = {0u, 0u, 0u, 0u}, p_piece = {0u, 0u, 0u, 0u};
-  uint32_t ds_boff = 0xFFFFFFF0u;
-  __amdgpu_buffer_rsrc_t ds_rs = __builtin_amdgcn_make_buffer_rsrc(p.dq, 0, 0, 0x00020000);
-  __amdgpu_buffer_rsrc_t p_rs = ds_rs;
-  lds_t* const pbuf = smem + C::P_OFF;
   auto v1 = [&](int st) {
     f32x4_t sq = sq_own, dq = dq_own;
 #pragma unroll
@@ -772,7 +767,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
     } else {
       need_mask = (row0 + 32 > sv.lq) || (p.causal && ow0 + 31 > row0 + off);
     }
-    float ds[4], pq[4];
+    float ds[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float pv = fast_exp2(sq[i] * p.scale_log2 - lse2q[i]);
@@ -783,48 +778,14 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
         const bool legal = ki < sv.lk && qi < sv.lq && (!p.causal || ki <= qi + off);
         pv = legal ? pv : 0.f;
       }
-      pq[i] = pv;
       ds[i] = pv * (dq[i] - dltq[i]);
     }
     mine = (u32x2_t){Elt<T>::pack2(ds[0], ds[1]), Elt<T>::pack2(ds[2], ds[3])};
     *(__attribute__((address_space(3))) u32x2_t*)(gbuf + cg * 512 + lane * 8) = mine;
-    if constexpr (STORE_DS) {
-      // Store the rounded dS and P (the values a product uses), [query][key], as 16-byte row
-      // pieces. The wave's quarter, in the buffer as lane (h, key n): 4 query rows, is read back
-      // transposed: in 16-lane group g (g = 0, 1 <-> h = g) source lane s = t + 4 m points at key
-      // 8 t + m (first read) or 8 t + 4 + m (second), so lane i receives keys 8 (i/4) + 0..7 of
-      // query row qrow(g) + i%4. Lanes 32..63 and pieces outside the sequence (rows >= Lq, or
-      // starting at or past the padded row end) get an offset past the block, which the buffer
-      // range check discards.
-      const u32x2_t pmine = {Elt<T>::pack2(pq[0], pq[1]), Elt<T>::pack2(pq[2], pq[3])};
-      *(__attribute__((address_space(3))) u32x2_t*)(pbuf + cg * 512 + lane * 8) = pmine;
-      const int g = (lane >> 4) & 1, sl = lane & 15, i16 = lane & 15;
-      const int toff = cg * 512 + (32 * g + 8 * (sl & 3) + (sl >> 2)) * 8;
-      ds_piece = join_tr(lds_read_tr16(gbuf + toff, 0), lds_read_tr16(gbuf + toff, 32));
-      p_piece = join_tr(lds_read_tr16(pbuf + toff, 0), lds_read_tr16(pbuf + toff, 32));
-      const int rq = row0 + 16 * (cg >> 1) + 8 * g + 4 * (cg & 1) + (i16 & 3);
-      const int key0 = ow0 + 8 * (i16 >> 2);
-      const bool ok = lane < 32 && rq < sv.lq && key0 < dsv.row;
-      ds_boff = ok ? (uint32_t)((rq * dsv.row + key0) * 2) : 0xFFFFFFF0u;
-      const long long hoff = dsv.base + (long long)step_head(st) * dsv.head;
-      const int nrec = (int)((long long)sv.lq * dsv.row * 2);
-      ds_rs = __builtin_amdgcn_make_buffer_rsrc((uint16_t*)p.ds + hoff, 0, nrec, 0x00020000);
-      p_rs = __builtin_amdgcn_make_buffer_rsrc((uint16_t*)p.pst + hoff, 0, nrec, 0x00020000);
-    }
-  };
-  // Stores of the pieces formed in V1, at the start of M2.
-  auto store_pieces = [&]() {
-    if constexpr (STORE_DS) {
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, ds_piece), ds_rs, (int)ds_boff, 0,
-                                             DS_STORE_CPOL);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, p_piece), p_rs, (int)ds_boff, 0,
-                                             DS_STORE_CPOL);
-    }
   };
   // ---- phase M2: all-gather dS (quarter q gives B-operand words 2 (q % 2), +1 of k-block q / 2),
   // then acc^T[d][own] += A[d][streamed] * dS[streamed][own], A read transposed from tile 1
   auto m2 = [&](int st) {
-    store_pieces();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       u32x2_t v = mine;
@@ -872,9 +833,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
         v1(st);
         lds_barrier();
         m2(st);
-        // Issued since the last wait, in order: the tile copies (M1a), the row statistics (M1b) and,
-        // when dS and P are stored, their two stores (M2): those may stay in flight.
-        wait_vmcnt<STORE_DS ? 2 : 0>();
+        wait_vmcnt<0>();  // the tile copies (M1a) and the row statistics (M1b)
         lds_barrier();
       }
       lds_barrier();
@@ -924,28 +883,302 @@ static hipError_t launch_bwd_pp(AttnParams p, hipStream_t st) {
   p.total = p.batch * (MODE == kDQ ? p.hq : p.hkv) * p.ntiles;
   if (p.total == 0) return hipSuccess;
   const int grid = (p.total + 7) & ~7;
-  if (MODE == kDK && p.ds != nullptr)
-    hipLaunchKernelGGL((ffpa_bwd_pp_kernel<T, kDK, NDB, true>), dim3(grid), dim3(64 * C::NW), 0, st, p);
-  else
-    hipLaunchKernelGGL((ffpa_bwd_pp_kernel<T, MODE, NDB, false>), dim3(grid), dim3(64 * C::NW), 0, st, p);
+  hipLaunchKernelGGL((ffpa_bwd_pp_kernel<T, MODE, NDB>), dim3(grid), dim3(64 * C::NW), 0, st, p);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------
+// P and dS for the stored-P/dS backward (D <= 512): P = exp(scale S - LSE) and dS = P (dP - Delta)
+// of every (query, key) pair, rounded to the storage dtype, with dP = dO V^T. No accumulator: the
+// gradients are products of the stored blocks (dK = scale dS^T Q, dV = P^T dO, dQ = scale dS K).
+//
+// The layout is the forward kernel's: a workgroup owns 128 queries of one head as 4 row groups x
+// 2 head-dim halves (8 waves, two per SIMD); each wave keeps its 32 queries' Q and dO columns in
+// registers (B operands) and forms the partial S^T = K Q^T and dP^T = V dO^T over its half from
+// K and V tiles (32 keys x 1 KB, XOR-swizzled) streamed through LDS. The two halves are combined by
+// a reduce-scatter: the A operand rows of the wave with head-dim half c are rotated by 16 c, so
+// its registers 0..7 hold keys 16 c + 8 h + 0..7 of the tile (the keys it finishes) and registers
+// 8..15 the partner's, which go to the exchange buffer. After the exchange, lane (h, query n)
+// holds 8 consecutive keys of its query. P and dS are stored transposed (one row per key, queries
+// contiguous), so that the two waves of a group that share a head-dim half complete whole 128-byte
+// lines of a key row in the same slot: each wave turns its 32 queries x 16 keys into 16-byte pieces
+// of 8 queries of one key with one LDS write and two transposed reads per block. LSE and Delta are
+// per lane (one query per lane).
+//
+// Two-group schedule (as in the forward): waves 0-3 and 4-7 run half a step apart, so in every
+// slot one wave of each SIMD multiplies while the other exchanges, exponentiates and stores.
+//   slot 2j:     group 0 multiplies tile j (and copies K of tile j + 1) | group 1 finishes j - 1
+//                (and copies V of tile j + 1)
+//   slot 2j + 1: group 0 finishes tile j                                | group 1 multiplies j
+// K_{j+1} and V_{j+1} go into the buffer of tile j - 1, which group 1 last read in slot 2j - 1,
+// and each group completes its copies before the barrier that ends slot 2j + 1.
+// ------------------------------------------------------------------------------------------------
+#ifndef PDS_AHEAD
+#define PDS_AHEAD 2
+#endif
+template <int NDB>
+struct PdsCfg {
+  static constexpr int NW = 8;
+  static constexpr int DW = NDB * 32;              // head-dim columns per wave (half the head)
+  static constexpr int KSTEPS = 2 * NDB;           // 16-wide k-steps over them
+  static constexpr int RS = 1024;                  // LDS row stride (bytes)
+  static constexpr int BQ = 4 * 32;                // queries per workgroup
+  static constexpr int TILE = 32 * RS;
+  static constexpr int XWAVE = 4 * 64 * 16;        // per wave: the partner's half of S and dP
+  static constexpr int LDS = 4 * TILE + 8 * XWAVE;  // [buffer][K, V] tiles, exchange
+  static constexpr int GCOPY = TILE / 1024 / 4;    // 1 KB copies per wave of a tile (one group)
+  static_assert(2 * DW <= 512 && LDS <= 160 * 1024, "LDS budget");
+};
+
+template <class T, int NDB>
+__global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
+  using C = PdsCfg<NDB>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
+  lds_t* smem = (lds_t*)smem_raw;
+  auto kbuf = [&](int b) { return smem + (2 * b) * C::TILE; };
+  auto vbuf = [&](int b) { return smem + (2 * b + 1) * C::TILE; };
+  lds_t* const xbuf = smem + 4 * C::TILE;
+
+  const int L = blockIdx.x;
+  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  if (item >= p.total) return;
+  int t = item % p.ntiles;
+  const int hs = item / p.ntiles;
+  const int h = hs % p.hq;
+  const int s = hs / p.hq;
+  if (p.causal) t = p.ntiles - 1 - t;  // heaviest causal tiles first
+
+  const SeqView sv = seq_view(p, s);
+  const int qt0 = t * C::BQ;
+  if (qt0 >= sv.lq) return;
+  const DsView dsv = ds_view(p, s, sv);
+  const int kvh = h / p.group;
+
+  const int w = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int grp = w >> 2;
+  const int wg = w & 3;
+  const int rg = w >> 1;
+  const int cg = w & 1;
+  const int qw0 = qt0 + rg * 32;
+  const int off = sv.lk - sv.lq;
+
+  const int row_bytes = p.k_row * 2;
+  const long long kv_off = sv.k_off + (long long)kvh * p.k_head;
+  const uint32_t span = (uint32_t)min((long long)max(sv.lk, 1) * row_bytes, (long long)0xFFFFFFF0);
+  const i32x4_t krs = make_rsrc((const uint16_t*)p.k + kv_off, span);
+  const i32x4_t vrs = make_rsrc((const uint16_t*)p.v + kv_off, span);
+  int kend = sv.lk;
+  if (p.causal) kend = min(kend, qt0 + C::BQ + off);
+  const int ntk = kend > 0 ? (kend + 31) >> 5 : 0;
+
+  // Q and dO columns of this wave as B operands: lane (h, n) holds query n, dims 16 kb + 8 h + 0..7.
+  const int qi = qw0 + l32;
+  const long long qrow = sv.q_off + (long long)h * p.q_head + (long long)min(qi, sv.lq - 1) * p.q_row;
+  u32x4_t qreg[C::KSTEPS], oreg[C::KSTEPS];
+#pragma unroll
+  for (int kb = 0; kb < C::KSTEPS; ++kb) {
+    const int dim = cg * C::DW + kb * 16 + hh * 8;
+    const bool in = dim < p.d;
+    qreg[kb] = in ? *(const u32x4_t*)((const uint16_t*)p.q + qrow + dim) : (u32x4_t){0u, 0u, 0u, 0u};
+    oreg[kb] = in ? *(const u32x4_t*)((const uint16_t*)p.dout + qrow + dim) : (u32x4_t){0u, 0u, 0u, 0u};
+  }
+  // The query's LSE in log2 units (+inf for a row without a legal key makes P = 0) and Delta.
+  const long long li = sv.lse_off + (long long)h * p.lse_head + min(qi, sv.lq - 1);
+  const float lse_raw = p.lse_in[li];
+  const float lse2 = lse_raw == -INFINITY ? INFINITY : lse_raw * kLog2e;
+  const float dlt = p.delta[li];
+
+  // The head's P and dS blocks (Lk rows of round_up(Lq, 8) queries).
+  const long long hoff = dsv.base + (long long)h * dsv.head;
+  const int nrec = (int)((long long)sv.lk * dsv.row * 2);
+  const __amdgpu_buffer_rsrc_t ds_rs = __builtin_amdgcn_make_buffer_rsrc((uint16_t*)p.ds + hoff, 0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t p_rs = __builtin_amdgcn_make_buffer_rsrc((uint16_t*)p.pst + hoff, 0, nrec, 0x00020000);
+
+  // Copies: instruction ii of a wave of a group fills tile row i = wg + 4 ii of that group's tile.
+  const int dch = p.d >> 3;
+  int gvoff[4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) gvoff[ii] = min(lane ^ swz(wg + 4 * ii), dch - 1) << 4;
+  auto gcopy = [&](const i32x4_t& rs, lds_t* tile, int j, int ii) {
+    const int i = wg + 4 * ii;
+    dma16_buf(rs, gvoff[ii & 3], min(j * 32 + i, sv.lk - 1) * row_bytes, tile + i * 1024);
+  };
+
+  // K and V rows (A operands): MFMA row m reads tile row row_perm(m) ^ 16 cg (see above).
+  const int krow = row_perm(l32) ^ (16 * cg);
+  const int kswz = swz(krow);
+  const int cbase = cg * C::DW >> 3;
+  constexpr bool kAligned = (C::DW % 128) == 0;
+  const uint32_t klane = krow * C::RS + (cbase << 4) + ((hh ^ kswz) << 4);
+  auto a_addr = [&](uint32_t tile, int kb) -> uint32_t {
+    if constexpr (kAligned) return ((tile + klane) ^ ((kb & 7) << 5)) + ((kb >> 3) << 8);
+    return tile + krow * C::RS + (((cbase + 2 * kb + hh) ^ kswz) << 4);
+  };
+
+  f32x16_t sacc, pacc;
+  // Partial S^T and dP^T of tile j over this wave's half; the partner's rows go to the exchange.
+  auto m_phase = [&](int j, auto&& copy_at) {
+    const uint32_t kt = lds_addr(kbuf(j & 1)), vt = lds_addr(vbuf(j & 1));
+    sacc = (f32x16_t){};
+    pacc = (f32x16_t){};
+#pragma unroll
+    for (int kb = 0; kb < C::KSTEPS; ++kb) {
+      sacc = Elt<T>::mma(lds_read_b128_at(a_addr(kt, kb)), qreg[kb], sacc);
+      pacc = Elt<T>::mma(lds_read_b128_at(a_addr(vt, kb)), oreg[kb], pacc);
+      copy_at(kb);
+    }
+    pin_lds_mfma_pipeline<2 * C::KSTEPS, PDS_AHEAD, 1>();
+#pragma unroll
+    for (int r4 = 0; r4 < 2; ++r4) {
+      lds_write_f4(xbuf, ((w * 4 + r4) * 64 + lane) * 16,
+                   (f32x4_t){sacc[8 + 4 * r4], sacc[9 + 4 * r4], sacc[10 + 4 * r4], sacc[11 + 4 * r4]});
+      lds_write_f4(xbuf, ((w * 4 + 2 + r4) * 64 + lane) * 16,
+                   (f32x4_t){pacc[8 + 4 * r4], pacc[9 + 4 * r4], pacc[10 + 4 * r4], pacc[11 + 4 * r4]});
+    }
+  };
+  // Full S and dP of this lane's 8 keys (own half + partner's), then P, dS and their stores.
+  auto e_phase = [&](int j, auto&& copies) {
+    const int pw = w ^ 1;
+    float sf[8], df[8];
+#pragma unroll
+    for (int r4 = 0; r4 < 2; ++r4) {
+      const f32x4_t a = lds_read_f4(xbuf, ((pw * 4 + r4) * 64 + lane) * 16);
+      const f32x4_t b = lds_read_f4(xbuf, ((pw * 4 + 2 + r4) * 64 + lane) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sf[4 * r4 + i] = sacc[4 * r4 + i] + a[i];
+        df[4 * r4 + i] = pacc[4 * r4 + i] + b[i];
+      }
+    }
+    copies();
+    const int key0 = j * 32 + 16 * cg + 8 * hh;
+    const bool need_mask = (j * 32 + 32 > sv.lk) || (p.causal && j * 32 + 31 > qw0 + off);
+    const int lim = p.causal ? min(qi + off, sv.lk - 1) : sv.lk - 1;
+    uint32_t pk[4], dk[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      float pv[2], dv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = 2 * e2 + u;
+        float pe = fast_exp2(sf[e] * p.scale_log2 - lse2);
+        if (need_mask) pe = key0 + e <= lim ? pe : 0.f;
+        pv[u] = pe;
+        dv[u] = pe * (df[e] - dlt);
+      }
+      pk[e2] = Elt<T>::pack2(pv[0], pv[1]);
+      dk[e2] = Elt<T>::pack2(dv[0], dv[1]);
+    }
+    // Transpose through this wave's inbox, free once read: lane (h, n) writes the 16 keys of query
+    // n as a 32-byte row (its half at 16 h); in 16-lane group g, source lane s = 4 e + t points at
+    // query row 8 g + e (+ 4 in the second read), keys 4 t .. 4 t + 3, so lane i receives key i and
+    // queries 8 g + 0..7.
+    lds_t* const tb = xbuf + (w ^ 1) * C::XWAVE;
+    const int wo = l32 * 32 + hh * 16;
+    lds_write_b128(tb, wo, (u32x4_t){pk[0], pk[1], pk[2], pk[3]});
+    lds_write_b128(tb, 1024 + wo, (u32x4_t){dk[0], dk[1], dk[2], dk[3]});
+    const int s16 = lane & 15, g = lane >> 4;
+    const int ro = (8 * g + (s16 >> 2)) * 32 + 8 * (s16 & 3);
+    const u32x4_t pt = join_tr(lds_read_tr16(tb, ro), lds_read_tr16(tb, ro + 128));
+    const u32x4_t dt = join_tr(lds_read_tr16(tb, 1024 + ro), lds_read_tr16(tb, 1024 + ro + 128));
+    // Pieces of keys at or past Lk, or starting at or past the padded row end, get an offset past
+    // the block, which the buffer range check discards.
+    const int key = j * 32 + 16 * cg + s16;
+    const int q8 = qw0 + 8 * g;
+    const bool ok = key < sv.lk && q8 < dsv.row;
+    const uint32_t boff = ok ? (uint32_t)(((long long)key * dsv.row + q8) * 2) : 0xFFFFFFF0u;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, pt), p_rs, (int)boff, 0, DS_STORE_CPOL);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, dt), ds_rs, (int)boff, 0, DS_STORE_CPOL);
+  };
+
+  if (ntk > 0) {
+    // Tile 0 by all waves (rows w + 8 ii of K and V).
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = w + 8 * ii;
+      const int row = min(i, sv.lk - 1) * row_bytes;
+      const int vo = min(lane ^ swz(i), dch - 1) << 4;
+      dma16_buf(krs, vo, row, kbuf(0) + i * 1024);
+      dma16_buf(vrs, vo, row, vbuf(0) + i * 1024);
+    }
+  }
+  wait_all();  // the stationary operands, LSE, Delta and tile 0
+  lds_barrier();
+
+  if (ntk > 0) {
+    if (grp == 0) {
+      for (int j = 0; j < ntk; ++j) {
+        m_phase(j, [&](int kb) {
+#pragma unroll
+          for (int ii = 0; ii < C::GCOPY; ++ii)
+            if (kb == (ii * C::KSTEPS) / C::GCOPY) gcopy(krs, kbuf((j + 1) & 1), j + 1, ii);
+        });
+        lds_barrier();
+        e_phase(j, [] {});
+        wait_vmcnt<2>();  // K_{j+1}; this step's two stores may stay in flight
+        lds_barrier();
+      }
+      lds_barrier();
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < C::GCOPY; ++ii) gcopy(vrs, vbuf(1), 1, ii);
+      lds_barrier();
+      for (int j = 0; j < ntk; ++j) {
+        m_phase(j, [](int) {});
+        wait_vmcnt<0>();  // V_{j+1}
+        lds_barrier();
+        e_phase(j, [&] {
+#pragma unroll
+          for (int ii = 0; ii < C::GCOPY; ++ii) gcopy(vrs, vbuf(j & 1), j + 2, ii);
+        });
+        lds_barrier();
+      }
+    }
+  }
+  // Copies issued during the last steps land in LDS that the next workgroup may own.
+  wait_vmcnt<0>();
+}
+
+template <class T, int NDB>
+static hipError_t launch_pds(AttnParams p, hipStream_t st) {
+  using C = PdsCfg<NDB>;
+  p.ntiles = (p.nq + C::BQ - 1) / C::BQ;
+  p.total = p.batch * p.hq * p.ntiles;
+  if (p.total == 0) return hipSuccess;
+  const int grid = (p.total + 7) & ~7;
+  hipLaunchKernelGGL((ffpa_pds_kernel<T, NDB>), dim3(grid), dim3(64 * C::NW), 0, st, p);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_pds_t(const AttnParams& p, hipStream_t st) {
+  switch ((p.d + 63) / 64) {
+    case 5: return launch_pds<T, 5>(p, st);
+    case 6: return launch_pds<T, 6>(p, st);
+    case 7: return launch_pds<T, 7>(p, st);
+    default: return launch_pds<T, 8>(p, st);
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
 // dQ from a stored dS: dQ_i = scale * sum_j dS_ij K_j (fp32 accumulation, one rounding).
 //
-// With dS written by the dK kernel (same rounding as the value its own product uses), the dQ stage
-// is a plain product instead of a recomputation of S, P, dP and dS: 2 D flops per legal pair
-// instead of 6 D, for dense B * Hq * Nq * Nkv dS elements of HBM workspace. A workgroup owns 128
-// queries of one head and one chunk of up to 512 head-dim columns; its 8 waves are 2 query groups
-// x 4 column groups, each wave 64 queries (two 32-row MFMA blocks) x DW columns of fp32
-// accumulators. Per step of 32 keys the K rows of the chunk (32 x 1 KB, swizzled as elsewhere)
-// and the 128 x 32 dS block (64-byte rows, 16-byte chunks XOR-swizzled by bits 2-3 of the row)
-// are copied into LDS, triple-buffered: the copies of step j + 2 are spread over the MFMAs of
-// step j, so each has a whole step to land. acc^T[d][q] += K^T[d][k] dS^T[k][q]: K^T is read transposed (ds_read_b64_tr_b16)
-// and used for both query blocks; dS^T is one 16-byte row read per query block and k-block.
-// Causal and ragged tiles mask dS to 0 where the key is not legal (those entries were not
-// written by the dK kernel).
+// With dS written by the P/dS kernel (the rounded value the dK product uses too), the dQ stage is
+// a plain product instead of a recomputation of S, P, dP and dS: 2 D flops per legal pair instead
+// of 6 D, for dense B * Hq * Nq * Nkv dS elements of HBM workspace. A workgroup owns 128 queries of
+// one head and one chunk of up to 512 head-dim columns; its 8 waves are 2 query groups x 4 column
+// groups, each wave 64 queries (two 32-row MFMA blocks) x DW columns of fp32 accumulators. Per
+// step of 32 keys the K rows of the chunk (32 x 1 KB, swizzled as elsewhere) and the dS block
+// (stored transposed: 32 keys x 128 queries, 256-byte rows whose 64-byte blocks are XOR-swizzled
+// by the row index mod 4) are copied into LDS, triple-buffered: the copies of step j + 2 are
+// spread over the MFMAs of step j, so each has a whole step to land. acc^T[d][q] += K^T[d][k]
+// dS^T[k][q]: K^T is read transposed (ds_read_b64_tr_b16) and used for both query blocks; dS^T,
+// 8 consecutive keys of one query, is read transposed from the key rows (the swizzle keeps a
+// half-wave's transposed reads on distinct banks). Causal and ragged tiles mask dS to 0 where the
+// key is not legal (those entries were not written by the P/dS kernel).
 // ------------------------------------------------------------------------------------------------
 template <int NDB>
 struct DqCfg {
@@ -956,13 +1189,14 @@ struct DqCfg {
   static constexpr int BQ = 2 * QB * 32;       // queries per workgroup
   static constexpr int RS = 1024;              // K tile row stride (bytes)
   static constexpr int KTILE = 32 * RS;
-  static constexpr int STILE = BQ * 64;        // dS block: BQ rows x 32 keys x 2 bytes
+  static constexpr int STILE = 32 * BQ * 2;    // dS block: 32 key rows x BQ queries x 2 bytes
+  static constexpr int SROW = BQ * 2;
   static constexpr int STAGE = KTILE + STILE;
   static constexpr int NBUF = PROD_NBUF;
   static constexpr int LDS = NBUF * STAGE;
   static constexpr int KCOPY = KTILE / 1024 / NW;  // K copies per wave per step
   static constexpr int SCOPY = STILE / 1024 / NW;  // dS copies per wave per step
-  static_assert(DWG <= 512 && SCOPY >= 1 && LDS <= 160 * 1024, "tile budget");
+  static_assert(DWG <= 512 && SCOPY == 1 && SROW == 256 && LDS <= 160 * 1024, "tile budget");
 };
 
 template <class T, int NDB>
@@ -1015,28 +1249,23 @@ __global__ void __launch_bounds__(512, 2) ffpa_dq_from_ds_kernel(AttnParams p, i
   int kvoff[C::KCOPY];
 #pragma unroll
   for (int ii = 0; ii < C::KCOPY; ++ii) kvoff[ii] = min((d0 >> 3) + (lane ^ swz(w + 8 * ii)), dch - 1) << 4;
-  // dS rows: copy ii of wave w fills block rows 16 i .. 16 i + 15, i = w + 8 ii; lane l writes
-  // row 16 i + l / 4, physical chunk l % 4 = logical chunk (l % 4) ^ ((row >> 2) & 3). The whole
-  // byte offset goes in the per-lane operand, which the buffer range check covers: pieces past the
-  // head's block (the last step's keys beyond the padded row of the last row) read as 0. The
-  // block size is a multiple of 16 bytes, so no piece straddles its end.
+  // dS rows (one per key): the copy of wave w fills block rows 4 w .. 4 w + 3; lane l writes row
+  // 4 w + l / 16 (key 32 j + row, clamped to the last key), physical chunk l % 16, holding logical
+  // chunk (l % 16) ^ (4 (row % 4)) (queries q0 + 8 * logical chunk). The whole byte offset goes in
+  // the per-lane operand, which the buffer range check covers: pieces past the head's block read
+  // as 0. The block size is a multiple of 16 bytes, so no piece straddles its end.
   const uint16_t* dsh = (const uint16_t*)p.ds + dsv.base + (long long)h * dsv.head;
-  const i32x4_t srs = make_rsrc(dsh, (uint32_t)((long long)sv.lq * dsv.row * 2));
-  int svoff[C::SCOPY];
-#pragma unroll
-  for (int ii = 0; ii < C::SCOPY; ++ii) {
-    const int r = 16 * (w + 8 * ii) + (lane >> 2);
-    const int qrow = min(q0 + r, sv.lq - 1);
-    svoff[ii] = qrow * dsv.row * 2 + ((((lane & 3) ^ ((r >> 2) & 3))) << 4);
-  }
+  const i32x4_t srs = make_rsrc(dsh, (uint32_t)((long long)sv.lk * dsv.row * 2));
+  const int srow_l = 4 * w + (lane >> 4);
+  const int sqoff = q0 + 8 * ((lane & 15) ^ (4 * (srow_l & 3)));
   auto copy = [&](int j, int buf, int c) {
     lds_t* stage = smem + buf * C::STAGE;
     if (c < C::KCOPY) {
       const int i = w + 8 * c;
       dma16_buf(krs, kvoff[c], min(j * 32 + i, sv.lk - 1) * krow_bytes, stage + i * 1024);
     } else {
-      const int ii = c - C::KCOPY;
-      dma16_buf(srs, svoff[ii] + j * 64, 0, stage + C::KTILE + (w + 8 * ii) * 1024);
+      const int key = min(j * 32 + srow_l, sv.lk - 1);
+      dma16_buf(srs, (key * dsv.row + sqoff) * 2, 0, stage + C::KTILE + w * 1024);
     }
   };
   constexpr int NCOPY = C::KCOPY + C::SCOPY;
@@ -1063,11 +1292,15 @@ __global__ void __launch_bounds__(512, 2) ffpa_dq_from_ds_kernel(AttnParams p, i
     const int k = 16 * kb2 + 8 * hh + 4 * half + (r16 >> 2);
     return tile + k * C::RS + (((cbase + 4 * db + tclo) ^ swz(k)) << 4) + twithin;
   };
-  // dS^T (B operand): lane (h, n) reads query row r = 64 qg + 32 qb + n, keys 16 kb2 + 8 h + 0..7,
-  // i.e. logical chunk 2 kb2 + h of the row.
-  auto s_addr = [&](uint32_t tile, int qb, int kb2) -> uint32_t {
-    const int r = 64 * qg + 32 * qb + l32;
-    return tile + C::KTILE + r * 64 + (((2 * kb2 + hh) ^ ((r >> 2) & 3)) << 4);
+  // dS^T (B operand): lane (h, query n) needs keys 16 kb2 + 8 h + 0..7 of query 64 qg + 32 qb + n.
+  // In 16-lane group g16 source lane s = t + 4 m points at key row 16 kb2 + 8 h + 4 half + m,
+  // queries 64 qg + 32 qb + 16 (g16 % 2) + 4 t + 0..3, so lane i receives query 16 (g16 % 2) + i
+  // of the 32-query block and keys + 0..3 (half 0) or + 4..7 (half 1).
+  auto s_addr = [&](uint32_t tile, int qb, int kb2, int half) -> uint32_t {
+    const int m = r16 >> 2, t = r16 & 3;
+    const int row = 16 * kb2 + 8 * hh + 4 * half + m;
+    const int byte = (64 * qg + 32 * qb + 16 * (g16 & 1) + 4 * t) * 2;
+    return tile + C::KTILE + row * C::SROW + ((((byte >> 4) ^ (4 * (row & 3))) << 4) | (byte & 15));
   };
 
   constexpr int NB = C::NBUF;
@@ -1096,7 +1329,8 @@ __global__ void __launch_bounds__(512, 2) ffpa_dq_from_ds_kernel(AttnParams p, i
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) bs[qb][kb2] = lds_read_b128_at(s_addr(tile, qb, kb2));
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+        bs[qb][kb2] = join_tr(lds_read_tr16_at(s_addr(tile, qb, kb2, 0)), lds_read_tr16_at(s_addr(tile, qb, kb2, 1)));
     const bool need_mask = (j * 32 + 32 > sv.lk) || (p.causal && j * 32 + 31 > q0 + 64 * qg + off);
     if (need_mask) {
 #pragma unroll
@@ -1184,19 +1418,19 @@ static hipError_t launch_dq_ds_t(const AttnParams& p, hipStream_t st) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// dV from a stored P: dV_j = sum over the query heads h of the group and queries i of P_hij dO_hi
-// (fp32 accumulation, one rounding), the dV stage when the dK kernel has stored P.
+// dV from a stored P: dV_j = sum over the query heads h of the group and queries i of P_hij dO_hi,
+// and with DK the same product dK_j = scale sum dS_hij Q_hi (fp32 accumulation, one rounding).
 //
 // Same tiling as the dQ pass with keys as the output rows: a workgroup owns 128 keys of one KV head
 // and one chunk of up to 512 head-dim columns; its 8 waves are 2 key groups x 4 column groups, each
 // wave 64 keys (two 32-row MFMA blocks) x DW columns. The streamed side is 32 queries of one query
 // head of the group per step (all the group's heads in turn; causal steps start at the first
 // query that sees a key of the block). acc^T[d][j] += dO^T[d][i] P[i][j]: dO^T is read transposed
-// from the dO rows (as K^T in the dQ pass) and P[i][j] for 8 consecutive queries i of key j is read
-// transposed from the P block in LDS (32 queries x 128 keys, 256-byte rows whose 64-byte blocks are
-// XOR-swizzled by the row index mod 4, which keeps a half-wave's transposed reads on distinct
-// banks). Triple-buffered copies as in the dQ pass. P is masked to 0 for queries at or past Lq
-// (their rows are clamped duplicates) and for keys that are not legal (not written by dK).
+// from the dO rows (as K^T in the dQ pass); P is stored transposed (one row per key), so P[i][j]
+// for 8 consecutive queries i of key j is one 16-byte read from the block in LDS (128 keys x 32
+// queries, 64-byte rows whose 16-byte chunks are XOR-swizzled by bits 2-3 of the row).
+// Triple-buffered copies as in the dQ pass. P is masked to 0 for queries at or past Lq (padding or
+// the next row's values) and for pairs that are not legal (not written by the P/dS kernel).
 // ------------------------------------------------------------------------------------------------
 template <int NDB>
 struct DvCfg {
@@ -1207,19 +1441,22 @@ struct DvCfg {
   static constexpr int BK = 2 * KB * 32;       // keys per workgroup
   static constexpr int RS = 1024;              // dO tile row stride (bytes)
   static constexpr int OTILE = 32 * RS;
-  static constexpr int PROW = BK * 2;          // P block row: 128 keys x 2 bytes
-  static constexpr int PTILE = 32 * PROW;
+  static constexpr int PROW = 32 * 2;          // P block row: one key, 32 queries x 2 bytes
+  static constexpr int PTILE = BK * PROW;
   static constexpr int STAGE = OTILE + PTILE;
   static constexpr int NBUF = PROD_NBUF;
   static constexpr int LDS = NBUF * STAGE;
   static constexpr int OCOPY = OTILE / 1024 / NW;
   static constexpr int PCOPY = PTILE / 1024 / NW;
-  static_assert(DWG <= 512 && PCOPY == 1 && PROW == 256 && LDS <= 160 * 1024, "tile budget");
+  static_assert(DWG <= 512 && PCOPY == 1 && PTILE == NW * 1024 && LDS <= 160 * 1024, "tile budget");
 };
 
-template <class T, int NDB>
+template <class T, int NDB, bool DK>
 __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, int nchunk) {
   using C = DvCfg<NDB>;
+  // dV = P^T dO, or (DK) dK = scale dS^T Q: the same product of a stored block and query rows.
+  const void* const rows_src = DK ? p.q : p.dout;
+  const void* const blk_src = DK ? p.ds : p.pst;
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
   lds_t* smem = (lds_t*)smem_raw;
 
@@ -1268,12 +1505,14 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
   int ovoff[C::OCOPY];
 #pragma unroll
   for (int ii = 0; ii < C::OCOPY; ++ii) ovoff[ii] = min((d0 >> 3) + (lane ^ swz(w + 8 * ii)), dch - 1) << 4;
-  // P rows: copy of wave w fills block rows 4 w .. 4 w + 3; lane l writes row 4 w + l / 16, physical
-  // chunk l % 16, holding logical chunk (l % 16) ^ (4 (row % 4)) (keys k0 + 8 * logical chunk).
-  // The whole byte offset is per lane (range-checked; the block is a multiple of 16 bytes).
-  const int prow_l = 4 * w + (lane >> 4);
-  const int pchunk = (lane & 15) ^ (4 * (prow_l & 3));
-  const uint32_t pspan = (uint32_t)((long long)sv.lq * dsv.row * 2);
+  // P rows (one per key): copy of wave w fills block rows 16 w .. 16 w + 15; lane l writes row
+  // 16 w + l / 4 (key k0 + row, clamped to the last key), physical chunk l % 4, holding logical
+  // chunk (l % 4) ^ ((row >> 2) & 3) (queries row0 + 8 * logical chunk). The whole byte offset is
+  // per lane (range-checked; the block is a multiple of 16 bytes).
+  const int prow_l = 16 * w + (lane >> 2);
+  const int pchunk = (lane & 3) ^ ((prow_l >> 2) & 3);
+  const int pkey = min(k0 + prow_l, sv.lk - 1);
+  const uint32_t pspan = (uint32_t)((long long)sv.lk * dsv.row * 2);
   struct StepSrc {
     i32x4_t ors, prs;
     int row0;
@@ -1283,8 +1522,8 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
     StepSrc x;
     const int h = step_head(st);
     x.row0 = step_row0(st);
-    x.ors = make_rsrc((const uint16_t*)p.dout + sv.q_off + (long long)h * p.q_head, ospan);
-    x.prs = make_rsrc((const uint16_t*)p.pst + dsv.base + (long long)h * dsv.head, pspan);
+    x.ors = make_rsrc((const uint16_t*)rows_src + sv.q_off + (long long)h * p.q_head, ospan);
+    x.prs = make_rsrc((const uint16_t*)blk_src + dsv.base + (long long)h * dsv.head, pspan);
     return x;
   };
   auto copy = [&](const StepSrc& x, int buf, int c) {
@@ -1293,8 +1532,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
       const int i = w + 8 * c;
       dma16_buf(x.ors, ovoff[c], min(x.row0 + i, sv.lq - 1) * orow_bytes, stage + i * 1024);
     } else {
-      const int qrow = min(x.row0 + prow_l, sv.lq - 1);
-      dma16_buf(x.prs, (qrow * dsv.row + k0 + 8 * pchunk) * 2, 0, stage + C::OTILE + w * 1024);
+      dma16_buf(x.prs, (pkey * dsv.row + x.row0 + 8 * pchunk) * 2, 0, stage + C::OTILE + w * 1024);
     }
   };
   constexpr int NCOPY = C::OCOPY + C::PCOPY;
@@ -1320,15 +1558,11 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
     const int k = 16 * kb2 + 8 * hh + 4 * half + (r16 >> 2);
     return tile + k * C::RS + (((cbase + 4 * db + tclo) ^ swz(k)) << 4) + twithin;
   };
-  // P (B operand): lane (h, key n) needs queries 16 kb2 + 8 h + 0..7 of key 64 kg + 32 kb + n. In
-  // 16-lane group g16 source lane s = t + 4 m points at block row 16 kb2 + 8 h + 4 half + m, keys
-  // 64 kg + 32 kb + 16 (g16 % 2) + 4 t + 0..3, so lane i receives key 16 (g16 % 2) + i of the
-  // 32-key block and queries + 0..3 (half 0) or + 4..7 (half 1).
-  auto p_addr = [&](uint32_t tile, int kb, int kb2, int half) -> uint32_t {
-    const int m = r16 >> 2, t = r16 & 3;
-    const int row = 16 * kb2 + 8 * hh + 4 * half + m;
-    const int byte = (64 * kg + 32 * kb + 16 * (g16 & 1) + 4 * t) * 2;
-    return tile + C::OTILE + row * C::PROW + ((((byte >> 4) ^ (4 * (row & 3))) << 4) | (byte & 15));
+  // P (B operand): lane (h, key n) reads block row r = 64 kg + 32 kb + n, queries 16 kb2 + 8 h + 0..7,
+  // i.e. logical chunk 2 kb2 + h of the row.
+  auto p_addr = [&](uint32_t tile, int kb, int kb2) -> uint32_t {
+    const int r = 64 * kg + 32 * kb + l32;
+    return tile + C::OTILE + r * C::PROW + (((2 * kb2 + hh) ^ ((r >> 2) & 3)) << 4);
   };
 
   constexpr int NB = C::NBUF;
@@ -1358,7 +1592,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
-        bp[kb][kb2] = join_tr(lds_read_tr16_at(p_addr(tile, kb, kb2, 0)), lds_read_tr16_at(p_addr(tile, kb, kb2, 1)));
+        bp[kb][kb2] = lds_read_b128_at(p_addr(tile, kb, kb2));
     const int kw0 = k0 + 64 * kg;
     const bool need_mask = (row0 + 32 > sv.lq) || (kw0 + 64 > sv.lk) || (p.causal && kw0 + 63 > row0 + off);
     if (need_mask) {
@@ -1403,7 +1637,8 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
   wait_vmcnt<0>();
 
   // ---- epilogue: round once, store keys < Lk and columns < D
-  uint16_t* dvh = (uint16_t*)p.dv + sv.k_off + (long long)kvh * p.k_head;
+  uint16_t* dvh = (uint16_t*)(DK ? p.dk : p.dv) + sv.k_off + (long long)kvh * p.k_head;
+  const float oscale = DK ? p.scale : 1.0f;
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb) {
     const int kj = k0 + 64 * kg + 32 * kb + l32;
@@ -1416,7 +1651,8 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
           const int d = d0 + dg * C::DW + 32 * db + 8 * i4 + 4 * hh;
           if (d < p.d) {
             const f32x16_t& a = acc[kb][db];
-            const u32x2_t pk = {Elt<T>::pack2(a[4 * i4], a[4 * i4 + 1]), Elt<T>::pack2(a[4 * i4 + 2], a[4 * i4 + 3])};
+            const u32x2_t pk = {Elt<T>::pack2(a[4 * i4] * oscale, a[4 * i4 + 1] * oscale),
+                                Elt<T>::pack2(a[4 * i4 + 2] * oscale, a[4 * i4 + 3] * oscale)};
             *(u32x2_t*)(dst + d) = pk;
           }
         }
@@ -1424,23 +1660,23 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
   }
 }
 
-template <class T, int NDB>
+template <class T, int NDB, bool DK>
 static hipError_t launch_dv_from_p(AttnParams p, int nchunk, hipStream_t st) {
   using C = DvCfg<NDB>;
   p.ntiles = (p.nkv + C::BK - 1) / C::BK;
   p.total = p.batch * p.hkv * nchunk * p.ntiles;
   if (p.total == 0) return hipSuccess;
   const int grid = (p.total + 7) & ~7;
-  hipLaunchKernelGGL((ffpa_dv_from_p_kernel<T, NDB>), dim3(grid), dim3(64 * C::NW), 0, st, p, nchunk);
+  hipLaunchKernelGGL((ffpa_dv_from_p_kernel<T, NDB, DK>), dim3(grid), dim3(64 * C::NW), 0, st, p, nchunk);
   return hipGetLastError();
 }
 
-template <class T>
+template <class T, bool DK>
 static hipError_t launch_dv_p_t(const AttnParams& p, hipStream_t st) {
   const int nchunk = (p.d + 511) / 512;
   const int per = (p.d + nchunk - 1) / nchunk;
-  if (per <= 384) return launch_dv_from_p<T, 3>(p, nchunk, st);
-  return launch_dv_from_p<T, 4>(p, nchunk, st);
+  if (per <= 384) return launch_dv_from_p<T, 3, DK>(p, nchunk, st);
+  return launch_dv_from_p<T, 4, DK>(p, nchunk, st);
 }
 
 template <class T, int MODE, int NC, int NDB>
@@ -1494,16 +1730,23 @@ static hipError_t launch_stage_t(int stage, const AttnParams& p, int nrows, int 
         return hipGetLastError();
       }
       return hipSuccess;
-    // With a workspace, dK also stores dS and P, and dV and dQ are products of them.
-    case 1: return launch_bwd_mode<T, kDK>(p, st);
-    case 2: return p.pst != nullptr ? launch_dv_p_t<T>(p, st) : launch_bwd_mode<T, kDV>(p, st);
+    // With a workspace, stage 4 stores P and dS (for D > 512 the dK kernel stores them as it goes)
+    // and dK, dV, dQ are products of them.
+    case 4: return p.ds != nullptr && p.d <= 512 ? launch_pds_t<T>(p, st) : hipSuccess;
+    case 1:
+      if (p.ds != nullptr && p.d <= 512) return launch_dv_p_t<T, true>(p, st);
+      return launch_bwd_mode<T, kDK>(p, st);
+    case 2: return p.pst != nullptr ? launch_dv_p_t<T, false>(p, st) : launch_bwd_mode<T, kDV>(p, st);
     default: return p.ds != nullptr ? launch_dq_ds_t<T>(p, st) : launch_bwd_mode<T, kDQ>(p, st);
   }
 }
 
-// Stage 0 = preprocess, 1 = dK, 2 = dV, 3 = dQ; -1 runs all four in order.
+// Stage 0 = preprocess, 4 = P and dS, 1 = dK, 2 = dV, 3 = dQ; -1 runs all five in that order.
 hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total, hipStream_t st, int stage) {
-  for (int s = stage < 0 ? 0 : stage; s <= (stage < 0 ? 3 : stage); ++s) {
+  static const int kOrder[5] = {0, 4, 1, 2, 3};
+  for (int i = 0; i < 5; ++i) {
+    const int s = kOrder[i];
+    if (stage >= 0 && s != stage) continue;
     const hipError_t e = fp16 ? launch_stage_t<FP16>(s, p, nrows, varlen_total, st)
                               : launch_stage_t<BF16>(s, p, nrows, varlen_total, st);
     if (e != hipSuccess) return e;

@@ -268,8 +268,9 @@ __device__ __forceinline__ SeqView seq_view(const AttnParams& p, int s) {
   return v;
 }
 
-// Stored-dS geometry of slice s: element offset of (s, head 0, row 0, key 0), the head stride and
-// the row stride (keys padded to a multiple of 8 elements, so 16-byte pieces stay aligned).
+// Stored P/dS geometry of slice s (blocks stored transposed, one row per key): element offset of
+// (s, head 0, key 0, query 0), the head stride and the row stride (queries padded to a multiple of
+// 8 elements, so 16-byte pieces stay aligned).
 struct DsView {
   long long base, head;
   int row;
@@ -281,9 +282,9 @@ __device__ __forceinline__ DsView ds_view(const AttnParams& p, int s, const SeqV
   DsView v;
   if (p.cu_q != nullptr) {
     long long pre = 0;
-    for (int t = 0; t < s; ++t) pre += (long long)(p.cu_q[t + 1] - p.cu_q[t]) * round_up8(p.cu_k[t + 1] - p.cu_k[t]);
-    v.row = round_up8(sv.lk);
-    v.head = (long long)sv.lq * v.row;
+    for (int t = 0; t < s; ++t) pre += (long long)(p.cu_k[t + 1] - p.cu_k[t]) * round_up8(p.cu_q[t + 1] - p.cu_q[t]);
+    v.row = round_up8(sv.lq);
+    v.head = (long long)sv.lk * v.row;
     v.base = pre * p.hq;
   } else {
     v.row = p.ds_row;

@@ -21,10 +21,10 @@ struct AttnParams {
   void* dv;
   const int32_t* cu_q;  // varlen: [batch+1]; NULL for dense
   const int32_t* cu_k;
-  // Stored dS (same dtype as q), or NULL. Row (b or sequence s, query head h, query i) holds keys
-  // 0..nkv-1 padded to ds_row = round_up(nkv, 8) elements. Dense: element offset
-  // b * ds_batch + h * ds_head + i * ds_row + j. Varlen: sequence s starts at hq * P_s with
-  // P_s = sum over earlier sequences of Lq * round_up(Lk, 8), head h at + h * Lq_s * round_up(Lk_s, 8).
+  // Stored dS (same dtype as q), or NULL, transposed: row (b or sequence s, query head h, key j)
+  // holds queries 0..nq-1 padded to ds_row = round_up(nq, 8) elements. Dense: element offset
+  // b * ds_batch + h * ds_head + j * ds_row + i. Varlen: sequence s starts at hq * P_s with
+  // P_s = sum over earlier sequences of Lk * round_up(Lq, 8), head h at + h * Lk_s * round_up(Lq_s, 8).
   void* ds;
   void* pst;  // stored P (same geometry as ds), or NULL
   long long ds_batch, ds_head;

@@ -34,17 +34,22 @@
  *   - Inputs are assumed finite. Buffers may not alias each other except q/k/v among themselves.
  *
  * Optional P/dS workspace of the backward entry points (workspace, workspace_bytes)
- *   NULL: the dV and dQ stages recompute S and P (and dP, dS) from q, k, v and dout (memory O(N)).
- *   Non-NULL: the dK stage also stores the rounded P = exp(scale q k^T - lse) and
- *     dS = P * (dP - Delta) (dtype, the values the products use) into the workspace, and the dV
- *     and dQ stages are products of them, dv = P^T dout and dq = scale * dS k, instead of
- *     recomputations: 2 D flops per (query, key) pair each instead of 4 D and 6 D, for
- *     ffpa_bwd_workspace_bytes() bytes of device memory (2 * B * Hq * Nq * round_up(Nkv, 8) * 2:
- *     the dS block, then the P block). The workspace is caller-owned device memory; its contents
- *     are scratch. A workspace smaller than the size function's value is
- *     FFPA_ERR_INVALID_ARGUMENT. When the size function returns 0 (a head's block would exceed
- *     2^31 bytes) the workspace is ignored and the stages recompute.
- *   Both choices give the same result up to the order of fp32 additions.
+ *   NULL: the dK, dV and dQ stages recompute S and P (and dP, dS) from q, k, v and dout (memory
+ *     O(N)).
+ *   Non-NULL: a P/dS stage stores the rounded P = exp(scale q k^T - lse) and
+ *     dS = P * (dP - Delta) (dtype, the values the products use) into the workspace, and the dK,
+ *     dV and dQ stages are products of them, dk = scale * dS^T q, dv = P^T dout and
+ *     dq = scale * dS k, instead of recomputations: 4 D flops per (query, key) pair to form P and
+ *     dS, then 2 D per product, instead of 6 D, 4 D and 6 D. (For D > 512 the dK stage forms and
+ *     stores P and dS itself, recomputing, and the P/dS stage launches nothing.) It takes
+ *     ffpa_bwd_workspace_bytes() bytes of device memory: 2 * B * Hq * Nkv * round_up(Nq, 8) * 2,
+ *     the dS block, then the P block, each stored transposed (one row of round_up(Nq, 8) queries
+ *     per key). The workspace is caller-owned device memory; its contents are scratch. A workspace
+ *     smaller than the size function's value is FFPA_ERR_INVALID_ARGUMENT. When the size function
+ *     returns 0 (a head's block would exceed 2^31 bytes) the workspace is ignored and the stages
+ *     recompute.
+ *   Both choices give the same result up to the order of fp32 additions and the rounding of P and
+ *   dS to dtype.
  */
 #ifndef FFPA_H_
 #define FFPA_H_
@@ -83,7 +88,7 @@ int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of the optional P/dS workspace of ffpa_bwd / ffpa_bwd_stage for these sizes:
- * 2 * batch * hq * nq * round_up(nkv, 8) * 2, or 0 when the stored-P/dS passes are not available
+ * 2 * batch * hq * nkv * round_up(nq, 8) * 2, or 0 when the stored-P/dS passes are not available
  * (a head's block above 2^31 bytes) or a size is < 1. Host function; launches nothing.
  */
 size_t ffpa_bwd_workspace_bytes(int batch, int hq, int nq, int nkv);
@@ -105,14 +110,16 @@ int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
 
 /*
  * One stage of the dense backward, with exactly the arguments of ffpa_bwd plus `stage`:
- *   0 = preprocess (writes delta), 1 = dK, 2 = dV, 3 = dQ.
- * ffpa_bwd is these four launches in order; stage 1 reads the delta written by stage 0 (and so
- * does stage 3 without a workspace). With a P/dS workspace, stage 1 writes P and dS into it and
- * stages 2 and 3 read them: pass the same workspace to all three (stages 2 and 3 with a workspace
- * that stage 1 did not fill give undefined dv, dq). The pages run dV before dK; the two are
- * independent without a workspace, and with one dK goes first because it produces P.
+ *   0 = preprocess (writes delta), 4 = P and dS, 1 = dK, 2 = dV, 3 = dQ.
+ * ffpa_bwd is these launches in the order 0, 4, 1, 2, 3. Stages 4 and 1 read the delta written by
+ * stage 0 (and so does stage 3 without a workspace). With a P/dS workspace, stage 4 writes P and
+ * dS into it (for D > 512, stage 1 does) and stages 1, 2 and 3 read them: pass the same workspace
+ * to all of them (a stage that reads a workspace that was not filled gives undefined results).
+ * Without a workspace stage 4 launches nothing and stages 1, 2 and 3 are independent. The pages
+ * run dV before dK; the order of the products does not matter.
  * Lets a caller time or schedule the launches individually ("CuTe-DSL Backend", "Blackwell
- * status": the backward is four launches). Returns FFPA_ERR_INVALID_ARGUMENT for another stage.
+ * status": the backward is separate launches). Returns FFPA_ERR_INVALID_ARGUMENT for another
+ * stage.
  */
 int ffpa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, float* delta, void* dq, void* dk, void* dv,
@@ -136,12 +143,12 @@ int ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float*
 
 /*
  * Bytes of the optional P/dS workspace of ffpa_varlen_bwd:
- * 2 * hq * total_q * round_up(max_seqlen_k, 8) * 2, two blocks (dS, then P), each bounding the
- * packed per-sequence layout (sequence by sequence, then head, then query row, keys padded to a
- * multiple of 8) for every cu_seqlens consistent with the max_seqlen values; 0 when not
+ * 2 * hq * total_k * round_up(max_seqlen_q, 8) * 2, two blocks (dS, then P), each bounding the
+ * packed per-sequence layout (sequence by sequence, then head, then key row of round_up(Lq, 8)
+ * queries) for every cu_seqlens consistent with the totals and max_seqlen values; 0 when not
  * available (see ffpa_bwd_workspace_bytes). Host function.
  */
-size_t ffpa_varlen_bwd_workspace_bytes(int hq, int total_q, int max_seqlen_q, int max_seqlen_k);
+size_t ffpa_varlen_bwd_workspace_bytes(int hq, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k);
 
 /*
  * Packed (THD) varlen backward; arguments as ffpa_varlen_fwd plus o, dout [total_q, hq, d],

@@ -84,7 +84,7 @@ def _bwd(lib, stage=None, b=1, hq=2, hkv=1, nq=64, nkv=64, d=640, dtype=1, scale
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(b=0), 1), (dict(hq=3, hkv=2), 1), (dict(d=300), 2), (dict(dtype=5), 1), (dict(scale=0.0), 1),
-    (dict(stage=4), 1), (dict(stage=-1), 1), (dict(stage=2, d=2048), 2),
+    (dict(stage=5), 1), (dict(stage=-1), 1), (dict(stage=2, d=2048), 2),
     # a workspace smaller than ffpa_bwd_workspace_bytes() is rejected before any launch
     (dict(ws=P, ws_bytes=2 * 2 * 64 * 64 * 2 - 1), 1), (dict(stage=3, ws=P, ws_bytes=16), 1),
 ])
@@ -94,15 +94,16 @@ def test_bwd_validation(lib, kw, expect):
 
 def test_workspace_sizes(lib):
     from head_dim_attention_amd import _binding as B
-    # two blocks (dS, P) of B * Hq * Nq * round_up(Nkv, 8) dtype-sized elements
+    # two blocks (dS, P), stored transposed: B * Hq * Nkv * round_up(Nq, 8) dtype-sized elements
     assert B.ffpa_bwd_workspace_bytes(1, 32, 8192, 8192) == 2 * 32 * 8192 * 8192 * 2
-    assert B.ffpa_bwd_workspace_bytes(2, 3, 5, 13) == 2 * 2 * 3 * 5 * 16 * 2
-    assert B.ffpa_bwd_workspace_bytes(1, 1, 7, 8) == 2 * 7 * 8 * 2
+    assert B.ffpa_bwd_workspace_bytes(2, 3, 13, 5) == 2 * 2 * 3 * 5 * 16 * 2
+    assert B.ffpa_bwd_workspace_bytes(1, 1, 8, 7) == 2 * 7 * 8 * 2
     assert B.ffpa_bwd_workspace_bytes(0, 1, 7, 8) == 0
-    # a head's block above 2^31 bytes: not available (the library then recomputes dQ)
+    # a head's block above 2^31 bytes: not available (the library then recomputes)
     assert B.ffpa_bwd_workspace_bytes(1, 1, 40000, 40000) == 0
-    assert B.ffpa_varlen_bwd_workspace_bytes(4, 100, 60, 41) == 2 * 4 * 100 * 48 * 2
-    assert B.ffpa_varlen_bwd_workspace_bytes(4, 0, 0, 41) == 0
+    # varlen: bounded by total_k * round_up(max_seqlen_q, 8) per head and block
+    assert B.ffpa_varlen_bwd_workspace_bytes(4, 100, 90, 41, 60) == 2 * 4 * 90 * 48 * 2
+    assert B.ffpa_varlen_bwd_workspace_bytes(4, 0, 0, 0, 41) == 0
 
 
 def test_bwd_null_pointers(lib):
