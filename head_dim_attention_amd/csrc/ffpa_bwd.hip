@@ -907,11 +907,11 @@ static hipError_t launch_bwd_pp(AttnParams p, hipStream_t st) {
 //
 // Two-group schedule (as in the forward): waves 0-3 and 4-7 run half a step apart, so in every
 // slot one wave of each SIMD multiplies while the other exchanges, exponentiates and stores.
-//   slot 2j:     group 0 multiplies tile j (and copies K of tile j + 1) | group 1 finishes j - 1
-//                (and copies V of tile j + 1)
-//   slot 2j + 1: group 0 finishes tile j                                | group 1 multiplies j
-// K_{j+1} and V_{j+1} go into the buffer of tile j - 1, which group 1 last read in slot 2j - 1,
-// and each group completes its copies before the barrier that ends slot 2j + 1.
+//   slot 2j:     group 0 multiplies tile j   | group 1 finishes tile j - 1 and copies tile j + 1
+//   slot 2j + 1: group 0 finishes tile j     | group 1 multiplies tile j
+// Tile j + 1 goes into the buffer of tile j - 1, which group 1 last read in slot 2j - 1, and group
+// 1 completes the copies before the barrier that ends slot 2j + 1. All copies are issued by the
+// finishing group: the multiplying waves issue nothing but LDS reads and MFMAs.
 // ------------------------------------------------------------------------------------------------
 #ifndef PDS_AHEAD
 #define PDS_AHEAD 2
@@ -1020,7 +1020,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
 
   f32x16_t sacc, pacc;
   // Partial S^T and dP^T of tile j over this wave's half; the partner's rows go to the exchange.
-  auto m_phase = [&](int j, auto&& copy_at) {
+  auto m_phase = [&](int j) {
     const uint32_t kt = lds_addr(kbuf(j & 1)), vt = lds_addr(vbuf(j & 1));
     sacc = (f32x16_t){};
     pacc = (f32x16_t){};
@@ -1028,7 +1028,6 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
     for (int kb = 0; kb < C::KSTEPS; ++kb) {
       sacc = Elt<T>::mma(lds_read_b128_at(a_addr(kt, kb)), qreg[kb], sacc);
       pacc = Elt<T>::mma(lds_read_b128_at(a_addr(vt, kb)), oreg[kb], pacc);
-      copy_at(kb);
     }
     pin_lds_mfma_pipeline<2 * C::KSTEPS, PDS_AHEAD, 1>();
 #pragma unroll
@@ -1110,29 +1109,33 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
 
   if (ntk > 0) {
     if (grp == 0) {
+      // Only stores leave this group's waves inside the loop; they are not waited for.
       for (int j = 0; j < ntk; ++j) {
-        m_phase(j, [&](int kb) {
-#pragma unroll
-          for (int ii = 0; ii < C::GCOPY; ++ii)
-            if (kb == (ii * C::KSTEPS) / C::GCOPY) gcopy(krs, kbuf((j + 1) & 1), j + 1, ii);
-        });
+        m_phase(j);
         lds_barrier();
         e_phase(j, [] {});
-        wait_vmcnt<2>();  // K_{j+1}; this step's two stores may stay in flight
         lds_barrier();
       }
       lds_barrier();
     } else {
 #pragma unroll
-      for (int ii = 0; ii < C::GCOPY; ++ii) gcopy(vrs, vbuf(1), 1, ii);
+      for (int ii = 0; ii < C::GCOPY; ++ii) {
+        gcopy(krs, kbuf(1), 1, ii);
+        gcopy(vrs, vbuf(1), 1, ii);
+      }
       lds_barrier();
       for (int j = 0; j < ntk; ++j) {
-        m_phase(j, [](int) {});
-        wait_vmcnt<0>();  // V_{j+1}
+        m_phase(j);
+        // Tile j + 1 (copied in the prologue, or in the finishing phase of step j - 1, followed
+        // there by that step's two stores, which may stay in flight).
+        if (j == 0) wait_vmcnt<0>(); else wait_vmcnt<2>();
         lds_barrier();
         e_phase(j, [&] {
 #pragma unroll
-          for (int ii = 0; ii < C::GCOPY; ++ii) gcopy(vrs, vbuf(j & 1), j + 2, ii);
+          for (int ii = 0; ii < C::GCOPY; ++ii) {
+            gcopy(krs, kbuf(j & 1), j + 2, ii);
+            gcopy(vrs, vbuf(j & 1), j + 2, ii);
+          }
         });
         lds_barrier();
       }
