@@ -74,6 +74,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-ds-workspace", action="store_true",
                     help="backward without the P/dS workspace (dV and dQ recompute)")
+    ap.add_argument("--decode-workload", default="decode_gqa_d512_k65536",
+                    help="workload of the split-KV decode leg ('none' skips it)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration under rocprofv3)")
     return ap.parse_args(argv)
@@ -92,6 +94,54 @@ def load_traffic(kernel: str):
     if not k:
         return None
     return k.get("hbm_bytes_per_launch")
+
+
+def decode_leg(F, W, w, seed: int, steps: int, warmup: int) -> dict:
+    """Time ffpa_decode_fwd (split-KV pass + combine pass) on a decode workload, inputs resident in
+    HBM. The pass is HBM-bound: algorithmic bytes are K and V read once plus Q and O, LSE, and the
+    partial results written and read back once by the combine."""
+    import torch
+    q, k, v, _ = W.workload_inputs(w, seed)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    b, hq, nq, d = qd.shape
+    hkv, nkv = kd.shape[1], kd.shape[2]
+    o = torch.empty_like(qd)
+    lse = torch.empty((b, hq, nq), dtype=torch.float32, device=dev)
+    nws = F.ffpa_decode_workspace_bytes(b, hq, hkv, nq, nkv, d)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    lib = F.load_library()
+    stream = torch.cuda.current_stream(dev)
+    P = F._binding._ptr
+    dt = 0 if w.dtype == "bf16" else 1
+
+    def run():
+        st = lib.ffpa_decode_fwd(P(qd), P(kd), P(vd), P(o), P(lse), b, hq, hkv, nq, nkv, d, dt,
+                                 1.0 / math.sqrt(d), int(w.causal), P(ws), nws, stream.cuda_stream)
+        if st:
+            raise RuntimeError(F.ffpa_status_string(st))
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        run()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps
+    el = qd.element_size()
+    kv_bytes = 2.0 * b * hkv * nkv * d * el
+    part_bytes = 2.0 * nws  # partial O and LSE written once, read once
+    alg_bytes = kv_bytes + 2.0 * b * hq * nq * d * el + 4.0 * b * hq * nq + part_bytes
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "batch": b, "heads": hq, "kv_heads": hkv, "seq_len_q": nq, "seq_len_kv": nkv,
+            "head_dim": d, "causal": w.causal, "dtype": w.dtype, "ms": round(ms, 4),
+            "nsplit": nws // (b * hq * nq * (d + 1) * 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes": alg_bytes, "kv_bytes": kv_bytes}}
 
 
 def cpu_baseline(q, k, v, do, scale, causal, dq, dk, dv, o, lse, tol_o, budget_s=10.0):
@@ -272,6 +322,10 @@ def main(argv=None) -> int:
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic},
     }
+
+    if args.decode_workload != "none":
+        print(f"bench: timing the split-KV decode pass on {args.decode_workload}", file=sys.stderr, flush=True)
+        out["decode"] = decode_leg(F, W, W.get(args.decode_workload), args.seed, max(args.steps, 10), args.warmup)
 
     if args.calib_copy_mib > 0:
         nbytes = args.calib_copy_mib << 20

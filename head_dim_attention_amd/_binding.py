@@ -20,7 +20,8 @@ __all__ = [
     "FFPA_OK", "FFPA_ERR_INVALID_ARGUMENT", "FFPA_ERR_NOT_SUPPORTED", "FFPA_ERR_HIP",
     "library_path", "load_library", "ffpa_status_string",
     "ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd",
-    "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes",
+    "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes", "ffpa_decode_fwd",
+    "ffpa_decode_workspace_bytes",
 ]
 
 FFPA_OK = 0
@@ -39,6 +40,7 @@ _sz = ctypes.c_size_t
 
 _SIGNATURES = {
     "ffpa_fwd": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp],
+    "ffpa_decode_fwd": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp],
     "ffpa_bwd": [_vp] * 10 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "ffpa_bwd_stage": [_i] + [_vp] * 10 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "ffpa_varlen_fwd": [_vp] * 7 + [_i] * 9 + [_f, _i, _vp],
@@ -47,6 +49,7 @@ _SIGNATURES = {
 _SIZE_FUNCTIONS = {
     "ffpa_bwd_workspace_bytes": [_i] * 4,
     "ffpa_varlen_bwd_workspace_bytes": [_i] * 5,
+    "ffpa_decode_workspace_bytes": [_i] * 6,
 }
 
 
@@ -142,6 +145,32 @@ def ffpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = F
     st = load_library().ffpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv, d,
                                  _dtype_code(q), _scale(scale, d), int(bool(causal)), _stream(q))
     _raise_for(st, "ffpa_fwd")
+    return o, lse
+
+
+def ffpa_decode_workspace_bytes(batch: int, hq: int, hkv: int, nq: int, nkv: int, d: int) -> int:
+    """Bytes of the split-KV decode workspace (partial O and LSE per key range)."""
+    return int(load_library().ffpa_decode_workspace_bytes(int(batch), int(hq), int(hkv), int(nq), int(nkv), int(d)))
+
+
+def ffpa_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                    scale: Optional[float] = None):
+    """Split-KV decode forward (meant for Nq in [1, 8)); same shapes and results as ffpa_fwd."""
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    _same(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,Hq,Nq,D] and k, v [B,Hkv,Nkv,D]")
+    b, hq, nq, d = q.shape
+    _, hkv, nkv, dk = k.shape
+    if k.shape[0] != b or dk != d:
+        raise ValueError("batch and head dim of q, k, v must match")
+    o = torch.empty_like(q)
+    lse = torch.empty((b, hq, nq), dtype=torch.float32, device=q.device)
+    ws, nws = _workspace(ffpa_decode_workspace_bytes(b, hq, hkv, nq, nkv, d), q)
+    st = load_library().ffpa_decode_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv, d,
+                                        _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(ws), nws,
+                                        _stream(q))
+    _raise_for(st, "ffpa_decode_fwd")
     return o, lse
 
 

@@ -17,10 +17,16 @@ from . import _binding as B
 __all__ = ["ffpa_attn_func", "ffpa_attn_varlen_func"]
 
 
+# Queries per head below which the forward takes the split-KV decode path ("Backends Overview",
+# "Automatic SDPA fallback": Nq in [1, 8) uses the native decode path).
+DECODE_MAX_NQ = 8
+
+
 class _FFPAAttn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, causal, scale):
-        o, lse = B.ffpa_fwd(q, k, v, causal=causal, scale=scale)
+        fwd = B.ffpa_decode_fwd if q.shape[2] < DECODE_MAX_NQ else B.ffpa_fwd
+        o, lse = fwd(q, k, v, causal=causal, scale=scale)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.causal, ctx.scale = causal, scale
         return o, lse

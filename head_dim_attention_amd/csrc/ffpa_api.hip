@@ -1,6 +1,7 @@
 // Host side of libffpa.so: argument validation, launch geometry and the C ABI (include/ffpa.h).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -9,6 +10,7 @@
 
 namespace ffpa {
 hipError_t launch_fwd(const AttnParams& p, int fp16, hipStream_t st);
+hipError_t launch_decode(const AttnParams& p, int fp16, hipStream_t st);
 hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total, hipStream_t st, int stage);
 }  // namespace ffpa
 
@@ -101,6 +103,34 @@ size_t varlen_ds_bytes(int hq, int total_q, int total_k, int max_q, int max_k) {
   return 2 * (size_t)hq * total_k * round_up8(max_q) * 2;
 }
 
+// Split-KV decode geometry: rows = G * nq rows per KV head in blocks of 32, and the key ranges.
+// About two workgroups per compute unit (256 CUs), at least four 32-key tiles per range, at most
+// 256 ranges; the tile count per range is then evened out so that no range is empty.
+struct DecodeGeom {
+  int rows, nrb, nsplit, split_tiles;
+};
+
+DecodeGeom decode_geom(int batch, int hq, int hkv, int nq, int nkv) {
+  DecodeGeom g{};
+  g.rows = (hq / hkv) * nq;
+  g.nrb = (g.rows + 31) / 32;
+  const long long ntk = ((long long)nkv + 31) / 32;
+  const long long base = (long long)batch * hkv * g.nrb;
+  long long want = (512 + base - 1) / base;
+  const long long cap = std::max(1LL, std::min(256LL, ntk / 4));
+  want = std::max(1LL, std::min(want, cap));
+  g.split_tiles = (int)((ntk + want - 1) / want);
+  g.nsplit = (int)((ntk + g.split_tiles - 1) / g.split_tiles);
+  return g;
+}
+
+// Workspace of the decode path: per (b, h, query, range) a normalised fp32 O row, then the LSEs.
+size_t decode_ws_bytes(int batch, int hq, int hkv, int nq, int nkv, int d) {
+  if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || nq < 1 || nkv < 1 || d < 1) return 0;
+  const DecodeGeom g = decode_geom(batch, hq, hkv, nq, nkv);
+  return (size_t)batch * hq * nq * g.nsplit * ((size_t)d + 1) * 4;
+}
+
 // Attach a caller workspace for dS and P. NULL selects the recomputing dV and dQ kernels; a
 // workspace smaller than `need` is an invalid argument; need == 0 (not available for these sizes)
 // ignores it.
@@ -186,6 +216,37 @@ static int dense_bwd(int stage, const void* q, const void* k, const void* v, con
 }
 
 size_t ffpa_bwd_workspace_bytes(int batch, int hq, int nq, int nkv) { return dense_ds_bytes(batch, hq, nq, nkv); }
+
+size_t ffpa_decode_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, int d) {
+  return decode_ws_bytes(batch, hq, hkv, nq, nkv, d);
+}
+
+int ffpa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                    int nq, int nkv, int d, int dtype, float scale, int causal, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return FFPA_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
+  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  if (st != FFPA_OK) return st;
+  if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
+  if ((long long)batch * hq * nq > (1LL << 31) - 1) return FFPA_ERR_INVALID_ARGUMENT;
+  const size_t need = decode_ws_bytes(batch, hq, hkv, nq, nkv, d);
+  if (workspace_bytes < need) return FFPA_ERR_INVALID_ARGUMENT;
+  AttnParams p = dense_params(batch, hq, hkv, nq, nkv, d, scale, causal);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  const DecodeGeom g = decode_geom(batch, hq, hkv, nq, nkv);
+  p.rows = g.rows;
+  p.nrb = g.nrb;
+  p.nsplit = g.nsplit;
+  p.split_tiles = g.split_tiles;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)workspace + (size_t)batch * hq * nq * g.nsplit * d;
+  return to_status(ffpa::launch_decode(p, dtype == FFPA_DTYPE_FP16, (hipStream_t)stream));
+}
 
 size_t ffpa_varlen_bwd_workspace_bytes(int hq, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k) {
   return varlen_ds_bytes(hq, total_q, total_k, max_seqlen_q, max_seqlen_k);

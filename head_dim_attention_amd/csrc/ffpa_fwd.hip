@@ -45,9 +45,12 @@ struct FwdCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <class T, int NC, int NDB, int QB, int NBUF, int NW>
+// DEC selects the split-KV decode form (one 32-row block of (query head, query) rows of a KV
+// group, one range of key tiles, partial results to a workspace); see the decode section below.
+template <class T, int NC, int NDB, int QB, int NBUF, int NW, bool DEC = false>
 __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p) {
   using C = FwdCfg<NC, NDB, QB, NBUF, NW>;
+  static_assert(!DEC || (QB == 1 && NW == NC), "decode: one 32-row block per workgroup");
   __shared__ __attribute__((aligned(1024))) char k0_raw[C::TILE], v0_raw[C::TILE];
   __shared__ __attribute__((aligned(1024))) char k1_raw[NBUF == 2 ? C::TILE : 16], v1_raw[NBUF == 2 ? C::TILE : 16];
   __shared__ __attribute__((aligned(1024))) char x_raw[C::XBYTES];
@@ -60,16 +63,29 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   const int L = blockIdx.x;
   const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
   if (item >= p.total) return;
-  int t = item % p.ntiles;
-  const int hs = item / p.ntiles;
-  const int h = hs % p.hq;
-  const int s = hs / p.hq;
-  if (p.causal) t = p.ntiles - 1 - t;  // heaviest causal tiles first
+  int t, h, s, kvh, split = 0;
+  if constexpr (DEC) {
+    // item = ((s * Hkv + kvh) * nsplit + split) * nrb + row block: the row blocks of one key range
+    // are neighbours (same XCD, shared K/V lines in its L2).
+    t = item % p.nrb;
+    int rest = item / p.nrb;
+    split = rest % p.nsplit;
+    rest /= p.nsplit;
+    kvh = rest % p.hkv;
+    s = rest / p.hkv;
+    h = kvh * p.group;
+  } else {
+    t = item % p.ntiles;
+    const int hs = item / p.ntiles;
+    h = hs % p.hq;
+    s = hs / p.hq;
+    if (p.causal) t = p.ntiles - 1 - t;  // heaviest causal tiles first
+    kvh = h / p.group;
+  }
 
   const SeqView sv = seq_view(p, s);
-  const int qt0 = t * C::BQ;
+  const int qt0 = DEC ? 0 : t * C::BQ;
   if (qt0 >= sv.lq) return;
-  const int kvh = h / p.group;
 
   const int w = wave_id();
   const int lane = threadIdx.x & 63;
@@ -78,10 +94,23 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   const int rg = w / NC;
   const int cg = w % NC;
   const int qw0 = qt0 + rg * QB * 32;
+  // Head and query of this lane's row (query column n of the MFMA blocks). Decode: row
+  // R = 32 t + n of the block is query R % Nq of query head kvh * G + R / Nq (rows at or past
+  // G * Nq repeat the last row and are not stored).
+  int hl = h, qi_l = qw0 + l32;
+  bool row_ok = true;
+  if constexpr (DEC) {
+    const int r = t * 32 + l32;
+    row_ok = r < p.rows;
+    const int rc = min(r, p.rows - 1);
+    hl = h + rc / sv.lq;
+    qi_l = rc % sv.lq;
+  }
+  const int q_lo = DEC ? 0 : qw0;  // smallest query index of the wave's rows
   // Eight waves with double-buffered 1 KB-row tiles run the two-group schedule below.
   constexpr bool kPingPong = NW == 8 && NBUF == 2 && NC == 2 && C::RS == 1024;
 
-  const uint16_t* qh = (const uint16_t*)p.q + sv.q_off + (long long)h * p.q_head;
+  const uint16_t* qh = (const uint16_t*)p.q + sv.q_off + (long long)hl * p.q_head;
   const int row_bytes = p.k_row * 2;
   const char* kbase = (const char*)p.k + 2 * (sv.k_off + (long long)kvh * p.k_head);
   const char* vbase = (const char*)p.v + 2 * (sv.k_off + (long long)kvh * p.k_head);
@@ -91,14 +120,20 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
 
   const int off = sv.lk - sv.lq;  // tail alignment of the causal mask
   int kend = sv.lk;
-  if (p.causal) kend = min(kend, qt0 + C::BQ + off);
+  if (p.causal && !DEC) kend = min(kend, qt0 + C::BQ + off);
   const int ntk = kend > 0 ? (kend + 31) >> 5 : 0;
+  // Key tiles of this workgroup: all of them, or (decode) this split's range.
+  int jbeg = 0, jend = ntk;
+  if constexpr (DEC) {
+    jbeg = split * p.split_tiles;
+    jend = min(jbeg + p.split_tiles, ntk);
+  }
 
   // Q block of this wave as B operands: lane (h, n) holds query n, dims 16 kb + 8 h + 0..7.
   u32x4_t qreg[QB][2 * NDB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int qi = min(qw0 + qb * 32 + l32, sv.lq - 1);
+    const int qi = DEC ? qi_l : min(qw0 + qb * 32 + l32, sv.lq - 1);
     const uint16_t* qrow = qh + (long long)qi * p.q_row;
 #pragma unroll
     for (int kb = 0; kb < 2 * NDB; ++kb) {
@@ -241,11 +276,11 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
       }
     }
     // Mask tail keys and the causal diagonal (only on tiles that need it).
-    const bool need_mask = (j * 32 + 32 > sv.lk) || (p.causal && j * 32 + 31 > qw0 + off);
+    const bool need_mask = (j * 32 + 32 > sv.lk) || (p.causal && j * 32 + 31 > q_lo + off);
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int qi = qw0 + qb * 32 + l32;
+        const int qi = DEC ? qi_l : qw0 + qb * 32 + l32;
         const int lim = p.causal ? min(qi + off, sv.lk - 1) : sv.lk - 1;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -268,7 +303,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     if constexpr (NBUF == 2) wait_vmcnt<C::NINSTR>();
     lds_barrier();
     if constexpr (NBUF == 1) {
-      if (j + 1 < ntk) issue(krs, j + 1, kbuf(0));
+      if (j + 1 < jend) issue(krs, j + 1, kbuf(0));
     }
     s_combine(j, sacc);
   };
@@ -327,7 +362,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   };
   auto pv = [&](int j, const uint32_t (&pb)[QB][2][4]) {
     if constexpr (NBUF == 1) {
-      if (j + 1 < ntk) wait_vmcnt<C::NINSTR>(); else wait_vmcnt<0>();  // V_j has landed
+      if (j + 1 < jend) wait_vmcnt<C::NINSTR>(); else wait_vmcnt<0>();  // V_j has landed
       lds_barrier();
     }
     pv_mma(j, pb, [&](int m) {
@@ -339,13 +374,13 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     });
     if constexpr (NBUF == 1) {
       lds_barrier();
-      if (j + 1 < ntk) issue(vrs, j + 1, vbuf(0));
+      if (j + 1 < jend) issue(vrs, j + 1, vbuf(0));
     }
   };
 
-  if (ntk > 0) {
-    issue(krs, 0, kbuf(0));
-    issue(vrs, 0, vbuf(0));
+  if (jend > jbeg) {
+    issue(krs, jbeg, kbuf(NBUF == 2 ? (jbeg & 1) : 0));
+    issue(vrs, jbeg, vbuf(NBUF == 2 ? (jbeg & 1) : 0));
   }
   // The Q operands (and tile 0) are complete before the loop, so the loop never waits for them.
   wait_all();
@@ -437,8 +472,8 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   // ---- fast loop: the reference max of a row is fixed at its first finite tile max. The loop
   // leaves (per wave) as soon as a tile max exceeds the reference by more than 2^8, so O never
   // needs rescaling here and exp2 stays below 256.
-  int j = 0;
-  for (; j < ntk; ++j) {
+  int j = jbeg;
+  for (; j < jend; ++j) {
     top(j);
     scores(j, sacc);
     float mt[QB];
@@ -457,7 +492,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
 
   // ---- rescaling loop (entered only after a large growth of a row max): standard online
   // softmax with a lazily updated reference. Tile j's scores are already in sacc.
-  for (bool fresh = false; j < ntk; ++j, fresh = true) {
+  for (bool fresh = false; j < jend; ++j, fresh = true) {
     if (fresh) {
       top(j);
       scores(j, sacc);
@@ -481,6 +516,30 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
 
   // Copies issued during the last step land in LDS that the next workgroup may own.
   wait_vmcnt<0>();
+
+  if constexpr (DEC) {
+    // ---- decode epilogue: this key range's normalised O (fp32) and its LSE in log2 units
+    // (-inf and 0 when no key of the range is legal for the row), for the combine pass.
+    const float lt = half_sum(lsum[0]);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    if (row_ok) {
+      const long long prow = ((long long)s * p.hq + hl) * sv.lq + qi_l;
+      float* orow = p.part_o + (prow * p.nsplit + split) * p.d;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = cg * C::DW + 32 * db + 8 * i4 + 4 * hh;
+          if (d < p.d) {
+            const f32x16_t& o = oacc[0][db];
+            *(f32x4_t*)(orow + d) = (f32x4_t){o[4 * i4] * inv, o[4 * i4 + 1] * inv, o[4 * i4 + 2] * inv,
+                                              o[4 * i4 + 3] * inv};
+          }
+        }
+      if (cg == 0 && hh == 0) p.part_lse[prow * p.nsplit + split] = lt > 0.f ? mref[0] + fast_log2(lt) : -INFINITY;
+    }
+    return;
+  }
 
   // ---- epilogue: O = O^T / l, LSE = ln(2) * (mref + log2 l); empty rows give 0 and -inf
 #pragma unroll
@@ -545,6 +604,95 @@ static hipError_t launch_fwd_t(const AttnParams& p, hipStream_t st) {
 
 hipError_t launch_fwd(const AttnParams& p, int fp16, hipStream_t st) {
   return fp16 ? launch_fwd_t<FP16>(p, st) : launch_fwd_t<BF16>(p, st);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Split-KV decode ("Triton Backend", "Feature support": decode as a two-stage split-KV path;
+// "Backends Overview", "Automatic SDPA fallback": the native decode path serves Nq in [1, 8)).
+//
+// With a handful of queries the forward grid above has one small workgroup per (head, 128
+// queries) that streams all of K and V: a few dozen workgroups for the whole GPU, and each KV
+// head read once per query head of its group. The decode form instead gives every workgroup one
+// KV head, one 32-row block of (query head of the group, query) rows -- all G * Nq rows of the
+// group share each K/V tile -- and one range of key tiles; the key ranges of a row are
+// independent (partial O normalised by its own sum, plus its LSE) and a second pass merges them:
+//   LSE = log sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s,
+// which is exactly the softmax over the union of the ranges. The work is HBM-bound (each K/V
+// byte is read once per row block): the split count fills the GPU with about two workgroups per
+// compute unit while keeping at least four tiles per range. Four waves split the head dim
+// (NC = 4); K and V tiles are double-buffered for D <= 512.
+// ------------------------------------------------------------------------------------------------
+template <class T>
+__global__ void __launch_bounds__(256) ffpa_decode_combine_kernel(AttnParams p, int nrows) {
+  // One wave per output row (b, h, i) = ((b * Hq + h) * Nq + i); lane l covers head-dim elements
+  // 4 (l + 64 k) .. + 3.
+  const int row = blockIdx.x * 4 + wave_id();
+  if (row >= nrows) return;
+  const int lane = threadIdx.x & 63;
+  const int i = row % p.nq;
+  const int bh = row / p.nq;
+  const int h = bh % p.hq;
+  const int b = bh / p.hq;
+  const float* lp = p.part_lse + (long long)row * p.nsplit;
+  const float* po = p.part_o + (long long)row * p.nsplit * p.d;
+  float m = -INFINITY;
+  for (int sp = 0; sp < p.nsplit; ++sp) m = fmaxf(m, lp[sp]);
+  f32x4_t acc[4] = {};
+  float l = 0.f;
+  if (m != -INFINITY) {
+    for (int sp = 0; sp < p.nsplit; ++sp) {
+      const float wgt = fast_exp2(lp[sp] - m);  // 0 for a range without a legal key
+      l += wgt;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int d = 4 * (lane + 64 * k);
+        if (d < p.d) acc[k] += wgt * *(const f32x4_t*)(po + (long long)sp * p.d + d);
+      }
+    }
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  uint16_t* orow = (uint16_t*)p.o + (long long)b * p.q_batch + (long long)h * p.q_head + (long long)i * p.q_row;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int d = 4 * (lane + 64 * k);
+    if (d < p.d)
+      *(u32x2_t*)(orow + d) = (u32x2_t){Elt<T>::pack2(acc[k].x * inv, acc[k].y * inv),
+                                        Elt<T>::pack2(acc[k].z * inv, acc[k].w * inv)};
+  }
+  if (lane == 0)
+    p.lse[(long long)b * p.lse_batch + (long long)h * p.lse_head + i] = l > 0.f ? (m + fast_log2(l)) * kLn2 : -INFINITY;
+}
+
+template <class T, int NDB>
+static hipError_t launch_decode_cfg(AttnParams p, hipStream_t st) {
+  constexpr int NC = 4, NW = 4, QB = 1;
+  using C1 = FwdCfg<NC, NDB, QB, 1, NW>;
+  constexpr int NBUF = (2 * 2 * C1::TILE + C1::XBYTES) <= 160 * 1024 ? 2 : 1;
+  p.total = p.batch * p.hkv * p.nsplit * p.nrb;
+  if (p.total == 0) return hipSuccess;
+  const int grid = (p.total + 7) & ~7;
+  hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF, NW, true>), dim3(grid), dim3(64 * NW), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nrows = p.batch * p.hq * p.nq;
+  hipLaunchKernelGGL(ffpa_decode_combine_kernel<T>, dim3((nrows + 3) / 4), dim3(256), 0, st, p, nrows);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_decode_t(const AttnParams& p, hipStream_t st) {
+  switch ((p.d + 127) / 128) {
+    case 3: return launch_decode_cfg<T, 3>(p, st);
+    case 4: return launch_decode_cfg<T, 4>(p, st);
+    case 5: return launch_decode_cfg<T, 5>(p, st);
+    case 6: return launch_decode_cfg<T, 6>(p, st);
+    case 7: return launch_decode_cfg<T, 7>(p, st);
+    default: return launch_decode_cfg<T, 8>(p, st);
+  }
+}
+
+hipError_t launch_decode(const AttnParams& p, int fp16, hipStream_t st) {
+  return fp16 ? launch_decode_t<FP16>(p, st) : launch_decode_t<BF16>(p, st);
 }
 
 }  // namespace ffpa

@@ -41,6 +41,12 @@ struct AttnParams {
   // Grid decode.
   int ntiles;  // row tiles per (sequence, head)
   int total;   // work items = batch * heads * ntiles
+  // Split-KV decode: rows = G * nq (query head in group, query) rows per KV head in nrb blocks of
+  // 32; nsplit key ranges of split_tiles 32-key tiles; per (row, range) a normalised fp32 O
+  // (part_o [B, Hq, Nq, nsplit, D]) and its log2-domain LSE (part_lse [B, Hq, Nq, nsplit]).
+  int rows, nrb, nsplit, split_tiles;
+  float* part_o;
+  float* part_lse;
 };
 
 }  // namespace ffpa

@@ -87,6 +87,28 @@ int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int dtype, float scale, int causal, void* stream);
 
 /*
+ * Split-KV decode forward ("Triton Backend", "Feature support": decode as a two-stage split-KV
+ * path; "Backends Overview", "Automatic SDPA fallback": the native decode path serves Nq in
+ * [1, 8)). Same arguments, layouts and results as ffpa_fwd (o, lse), plus a caller-owned device
+ * workspace of at least ffpa_decode_workspace_bytes() bytes (scratch: partial results per key
+ * range). The keys are cut into ranges processed by separate workgroups, each over all
+ * (query head of the KV group, query) rows, and the partial results are merged by a second
+ * launch; the result equals ffpa_fwd's up to the order of fp32 additions. Meant for few queries
+ * (it is correct for any nq, but each workgroup holds 32 rows). A NULL or too-small workspace is
+ * FFPA_ERR_INVALID_ARGUMENT.
+ */
+int ffpa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int batch, int hq, int hkv, int nq, int nkv, int d,
+                    int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of the ffpa_decode_fwd workspace for these sizes: batch * hq * nq * nsplit * (d + 1) * 4,
+ * where nsplit (the number of key ranges, 1..256) is the library's choice for these sizes; 0 for
+ * invalid sizes. Host function; launches nothing.
+ */
+size_t ffpa_decode_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, int d);
+
+/*
  * Bytes of the optional P/dS workspace of ffpa_bwd / ffpa_bwd_stage for these sizes:
  * 2 * batch * hq * nkv * round_up(nq, 8) * 2, or 0 when the stored-P/dS passes are not available
  * (a head's block above 2^31 bytes) or a size is < 1. Host function; launches nothing.

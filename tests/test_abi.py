@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_expected_entry_points():
     names = _declared()
     for n in ("ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd", "ffpa_status_string",
-              "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes"):
+              "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes", "ffpa_decode_fwd",
+              "ffpa_decode_workspace_bytes"):
         assert n in names
 
 
@@ -182,3 +183,23 @@ def test_bench_legal_pair_count():
     assert bench.legal_pairs(3, 5, True) == 3 + 4 + 5
     n = 8192
     assert bench.legal_pairs(n, n, True) == n * (n + 1) // 2
+
+
+def test_decode_workspace_sizes(lib):
+    from head_dim_attention_amd import _binding as B
+    # batch * hq * nq * nsplit * (d + 1) * 4 bytes: one fp32 O row and one LSE per key range
+    n = B.ffpa_decode_workspace_bytes(1, 32, 8, 1, 65536, 512)
+    assert n > 0 and n % (32 * 513 * 4) == 0
+    nsplit = n // (32 * 513 * 4)
+    assert 1 <= nsplit <= 256 and 2048 // nsplit >= 4  # at least four 32-key tiles per range
+    assert B.ffpa_decode_workspace_bytes(1, 2, 2, 1, 40, 512) == 2 * 1 * 513 * 4  # two tiles: one range
+    assert B.ffpa_decode_workspace_bytes(0, 2, 2, 1, 40, 512) == 0
+    assert B.ffpa_decode_workspace_bytes(1, 3, 2, 1, 40, 512) == 0  # hq % hkv != 0
+
+
+def test_decode_validation(lib):
+    args = [P] * 5 + [1, 2, 2, 1, 64, 512, 0, 0.04, 0]
+    assert lib.ffpa_decode_fwd(*args, N, 1 << 20, S) == 1            # NULL workspace
+    assert lib.ffpa_decode_fwd(*args, P, 16, S) == 1                 # too small
+    bad_d = [P] * 5 + [1, 2, 2, 1, 64, 300, 0, 0.04, 0]
+    assert lib.ffpa_decode_fwd(*bad_d, P, 1 << 20, S) == 2          # unsupported head dim

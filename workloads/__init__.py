@@ -27,13 +27,18 @@ class Workload:
     batch: int          # dense batch, or number of sequences for varlen
     hq: int
     hkv: int
-    n: int              # Nq = Nkv for dense workloads; unused for varlen
+    n: int              # Nkv (and Nq unless nq is set) for dense workloads; unused for varlen
     d: int
     dtype: str          # "bf16" | "fp16"
     causal: bool
     backward: bool
     varlen: bool = False
     input_scale: float = 1.0
+    nq: int = 0         # Nq when it differs from n (decode: a few queries against a long cache)
+
+    @property
+    def n_q(self) -> int:
+        return self.nq if self.nq > 0 else self.n
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -47,6 +52,8 @@ WORKLOADS = {
     "gqa_causal_d1024_n8192": Workload("gqa_causal_d1024_n8192", 1, 32, 8, 8192, 1024, "fp16", True, True,
                                        input_scale=0.5),
     "varlen_causal_d512": Workload("varlen_causal_d512", 8, 32, 32, 0, 512, "bf16", True, True, varlen=True),
+    # Split-KV decode: one new query per head against a 64K-key cache, 4 query heads per KV head.
+    "decode_gqa_d512_k65536": Workload("decode_gqa_d512_k65536", 1, 32, 8, 65536, 512, "bf16", True, False, nq=1),
 }
 
 
@@ -111,4 +118,4 @@ def workload_inputs(w: Workload, seed: int, varlen_lengths_override: Optional[li
     if w.varlen:
         lens = varlen_lengths_override if varlen_lengths_override is not None else varlen_lengths(w.batch, seed)
         return varlen_inputs(lens, lens, w.hq, w.hkv, w.d, w.torch_dtype, seed, w.input_scale, w.backward)
-    return dense_inputs(w.batch, w.hq, w.hkv, w.n, w.n, w.d, w.torch_dtype, seed, w.input_scale, w.backward)
+    return dense_inputs(w.batch, w.hq, w.hkv, w.n_q, w.n, w.d, w.torch_dtype, seed, w.input_scale, w.backward)
