@@ -24,6 +24,8 @@ __all__ = [
     "ffpa_decode_workspace_bytes",
 ]
 
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
 FFPA_OK = 0
 FFPA_ERR_INVALID_ARGUMENT = 1
 FFPA_ERR_NOT_SUPPORTED = 2
@@ -41,6 +43,8 @@ _sz = ctypes.c_size_t
 _SIGNATURES = {
     "ffpa_fwd": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp],
     "ffpa_decode_fwd": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp],
+    "ffpa_fwd_strided": [_vp] * 5 + [_i] * 6 + [_i64p, _i, _f, _i, _vp],
+    "ffpa_decode_fwd_strided": [_vp] * 5 + [_i] * 6 + [_i64p, _i, _f, _i, _vp, _sz, _vp],
     "ffpa_bwd": [_vp] * 10 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "ffpa_bwd_stage": [_i] + [_vp] * 10 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "ffpa_varlen_fwd": [_vp] * 7 + [_i] * 9 + [_f, _i, _vp],
@@ -129,10 +133,35 @@ def _same(ref: torch.Tensor, *ts):
             raise ValueError("q, k, v (and o, dout) must share dtype and device")
 
 
-def ffpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
-             scale: Optional[float] = None):
-    """Dense forward. q [B,Hq,Nq,D], k/v [B,Hkv,Nkv,D] -> (o [B,Hq,Nq,D], lse fp32 [B,Hq,Nq])."""
-    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+def _view(t: torch.Tensor, what: str) -> torch.Tensor:
+    """A [B, H, N, D] GPU tensor the forward kernels can read in place (unit last stride, 16-byte
+    aligned, other strides multiples of 8 elements, e.g. a [B, N, H, D] tensor transposed to
+    [B, H, N, D] or a slice of a fused QKV tensor); anything else is copied to packed layout."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a GPU tensor (got {t.device})")
+    if t.dim() == 4 and t.stride(-1) == 1 and t.data_ptr() % 16 == 0 and \
+            all(st % 8 == 0 and st >= 0 for sz, st in zip(t.shape[:-1], t.stride()[:-1]) if sz > 1):
+        return t
+    return t.contiguous()
+
+
+def _strides(*ts) -> Optional[ctypes.Array]:
+    """(batch, head, row) strides of each tensor for the strided entry points, or None when all
+    are packed [B, H, N, D] (size-1 dims do not count)."""
+    out = []
+    packed = True
+    for t in ts:
+        for i in range(3):
+            st = t.stride(i) if t.shape[i] > 1 else 0
+            out.append(st)
+        packed = packed and t.is_contiguous()
+    return None if packed else (ctypes.c_int64 * 12)(*out)
+
+
+def _fwd_prep(q, k, v):
+    q, k, v = _view(q, "q"), _view(k, "k"), _view(v, "v")
     _same(q, k, v)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("expected q [B,Hq,Nq,D] and k, v [B,Hkv,Nkv,D]")
@@ -140,10 +169,30 @@ def ffpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = F
     _, hkv, nkv, dk = k.shape
     if k.shape[0] != b or dk != d:
         raise ValueError("batch and head dim of q, k, v must match")
+    # O takes q's layout when q is a dense permutation (e.g. [B, N, H, D] viewed as [B, H, N, D]).
     o = torch.empty_like(q)
+    if _view(o, "o") is not o:
+        o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     lse = torch.empty((b, hq, nq), dtype=torch.float32, device=q.device)
-    st = load_library().ffpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv, d,
-                                 _dtype_code(q), _scale(scale, d), int(bool(causal)), _stream(q))
+    return q, k, v, o, lse, (b, hq, hkv, nq, nkv, d)
+
+
+def ffpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+             scale: Optional[float] = None):
+    """Dense forward. q [B,Hq,Nq,D], k/v [B,Hkv,Nkv,D] -> (o [B,Hq,Nq,D], lse fp32 [B,Hq,Nq]).
+
+    Strided views (for example [B, N, H, D] tensors transposed to [B, H, N, D], or the q, k, v
+    slices of one fused QKV tensor) are read in place through ffpa_fwd_strided; o then takes q's
+    layout when q is a dense permutation of [B, H, N, D]."""
+    q, k, v, o, lse, (b, hq, hkv, nq, nkv, d) = _fwd_prep(q, k, v)
+    strides = _strides(q, k, v, o)
+    L = load_library()
+    if strides is None:
+        st = L.ffpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv, d,
+                        _dtype_code(q), _scale(scale, d), int(bool(causal)), _stream(q))
+    else:
+        st = L.ffpa_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv, d, strides,
+                                _dtype_code(q), _scale(scale, d), int(bool(causal)), _stream(q))
     _raise_for(st, "ffpa_fwd")
     return o, lse
 
@@ -155,21 +204,19 @@ def ffpa_decode_workspace_bytes(batch: int, hq: int, hkv: int, nq: int, nkv: int
 
 def ffpa_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
                     scale: Optional[float] = None):
-    """Split-KV decode forward (meant for Nq in [1, 8)); same shapes and results as ffpa_fwd."""
-    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
-    _same(q, k, v)
-    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
-        raise ValueError("expected q [B,Hq,Nq,D] and k, v [B,Hkv,Nkv,D]")
-    b, hq, nq, d = q.shape
-    _, hkv, nkv, dk = k.shape
-    if k.shape[0] != b or dk != d:
-        raise ValueError("batch and head dim of q, k, v must match")
-    o = torch.empty_like(q)
-    lse = torch.empty((b, hq, nq), dtype=torch.float32, device=q.device)
+    """Split-KV decode forward (meant for Nq in [1, 8)); same shapes, results and strided views as
+    ffpa_fwd."""
+    q, k, v, o, lse, (b, hq, hkv, nq, nkv, d) = _fwd_prep(q, k, v)
+    strides = _strides(q, k, v, o)
     ws, nws = _workspace(ffpa_decode_workspace_bytes(b, hq, hkv, nq, nkv, d), q)
-    st = load_library().ffpa_decode_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv, d,
-                                        _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(ws), nws,
-                                        _stream(q))
+    L = load_library()
+    if strides is None:
+        st = L.ffpa_decode_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv, d,
+                               _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(ws), nws, _stream(q))
+    else:
+        st = L.ffpa_decode_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv, d,
+                                       strides, _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(ws),
+                                       nws, _stream(q))
     _raise_for(st, "ffpa_decode_fwd")
     return o, lse
 

@@ -40,6 +40,12 @@ AttnParams dense_params(int batch, int hq, int hkv, int nq, int nkv, int d, floa
   p.k_batch = (long long)hkv * nkv * d;
   p.lse_head = nq;
   p.lse_batch = (long long)hq * nq;
+  p.v_row = p.k_row;
+  p.v_head = p.k_head;
+  p.v_batch = p.k_batch;
+  p.o_row = p.q_row;
+  p.o_head = p.q_head;
+  p.o_batch = p.q_batch;
   p.batch = batch;
   p.hq = hq;
   p.hkv = hkv;
@@ -61,6 +67,10 @@ AttnParams varlen_params(int batch, int max_q, int max_k, int total_q, int hq, i
   p.k_row = hkv * d;
   p.k_head = d;
   p.lse_head = total_q;
+  p.v_row = p.k_row;
+  p.v_head = p.k_head;
+  p.o_row = p.q_row;
+  p.o_head = p.q_head;
   p.cu_q = cu_q;
   p.cu_k = cu_k != nullptr ? cu_k : cu_q;
   p.batch = batch;
@@ -101,6 +111,41 @@ size_t dense_ds_bytes(int batch, int hq, int nq, int nkv) {
 size_t varlen_ds_bytes(int hq, int total_q, int total_k, int max_q, int max_k) {
   if (hq < 1 || total_q < 1 || total_k < 1 || max_q < 1 || max_k < 1 || !ds_block_ok(max_q, max_k)) return 0;
   return 2 * (size_t)hq * total_k * round_up8(max_q) * 2;
+}
+
+// Strided forward layouts: strides[12] = {q, k, v, o} x {batch, head, row} in elements (the head
+// dim is contiguous). Rows must stay 16-byte aligned (strides multiples of 8 elements, 16-byte
+// aligned base pointers), strides non-negative, and one head's rows addressable with the kernels'
+// 32-bit row arithmetic.
+int apply_strides(AttnParams& p, const int64_t* st, const void* q, const void* k, const void* v, const void* o,
+                  int nq, int nkv, int d) {
+  if (st == nullptr) return FFPA_ERR_INVALID_ARGUMENT;
+  for (const void* ptr : {q, k, v, o})
+    if ((uintptr_t)ptr % 16 != 0) return FFPA_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < 12; ++i)
+    if (st[i] < 0 || st[i] % 8 != 0) return FFPA_ERR_INVALID_ARGUMENT;
+  const long long lim = (1LL << 31) - 1;
+  // {q, k, v, o}: rows per head and the row/head strides must fit the int fields; the last row of a
+  // head must end below 2^31 bytes from the head's first row.
+  const int rows[4] = {nq, nkv, nkv, nq};
+  for (int t = 0; t < 4; ++t) {
+    const long long hs = st[3 * t + 1], rs = st[3 * t + 2];
+    if (hs > lim || rs > lim) return FFPA_ERR_INVALID_ARGUMENT;
+    if (((long long)(rows[t] - 1) * rs + d) * 2 > lim) return FFPA_ERR_INVALID_ARGUMENT;
+  }
+  p.q_batch = st[0];
+  p.q_head = (int)st[1];
+  p.q_row = (int)st[2];
+  p.k_batch = st[3];
+  p.k_head = (int)st[4];
+  p.k_row = (int)st[5];
+  p.v_batch = st[6];
+  p.v_head = (int)st[7];
+  p.v_row = (int)st[8];
+  p.o_batch = st[9];
+  p.o_head = (int)st[10];
+  p.o_row = (int)st[11];
+  return FFPA_OK;
 }
 
 // Split-KV decode geometry: rows = G * nq rows per KV head in blocks of 32, and the key ranges.
@@ -146,20 +191,37 @@ int attach_ds(AttnParams& p, void* ws, size_t ws_bytes, size_t need) {
 
 extern "C" {
 
-int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
-             int nq, int nkv, int d, int dtype, float scale, int causal, void* stream) {
+static int dense_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                     int nq, int nkv, int d, const int64_t* strides, int dtype, float scale, int causal,
+                     void* stream) {
   if (!q || !k || !v || !o || !lse) return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
   const int st = check_common(hq, hkv, d, dtype, scale, causal);
   if (st != FFPA_OK) return st;
   if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
   AttnParams p = dense_params(batch, hq, hkv, nq, nkv, d, scale, causal);
+  if (strides != nullptr) {
+    const int sst = apply_strides(p, strides, q, k, v, o, nq, nkv, d);
+    if (sst != FFPA_OK) return sst;
+  }
   p.q = q;
   p.k = k;
   p.v = v;
   p.o = o;
   p.lse = lse;
   return to_status(ffpa::launch_fwd(p, dtype == FFPA_DTYPE_FP16, (hipStream_t)stream));
+}
+
+int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+             int nq, int nkv, int d, int dtype, float scale, int causal, void* stream) {
+  return dense_fwd(q, k, v, o, lse, batch, hq, hkv, nq, nkv, d, nullptr, dtype, scale, causal, stream);
+}
+
+int ffpa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                     int nq, int nkv, int d, const int64_t* strides, int dtype, float scale, int causal,
+                     void* stream) {
+  if (strides == nullptr) return FFPA_ERR_INVALID_ARGUMENT;
+  return dense_fwd(q, k, v, o, lse, batch, hq, hkv, nq, nkv, d, strides, dtype, scale, causal, stream);
 }
 
 int ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
@@ -221,9 +283,9 @@ size_t ffpa_decode_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, 
   return decode_ws_bytes(batch, hq, hkv, nq, nkv, d);
 }
 
-int ffpa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
-                    int nq, int nkv, int d, int dtype, float scale, int causal, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+static int decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                      int nq, int nkv, int d, const int64_t* strides, int dtype, float scale, int causal,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !lse || !workspace) return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
   const int st = check_common(hq, hkv, d, dtype, scale, causal);
@@ -233,6 +295,10 @@ int ffpa_decode_fwd(const void* q, const void* k, const void* v, void* o, float*
   const size_t need = decode_ws_bytes(batch, hq, hkv, nq, nkv, d);
   if (workspace_bytes < need) return FFPA_ERR_INVALID_ARGUMENT;
   AttnParams p = dense_params(batch, hq, hkv, nq, nkv, d, scale, causal);
+  if (strides != nullptr) {
+    const int sst = apply_strides(p, strides, q, k, v, o, nq, nkv, d);
+    if (sst != FFPA_OK) return sst;
+  }
   p.q = q;
   p.k = k;
   p.v = v;
@@ -246,6 +312,21 @@ int ffpa_decode_fwd(const void* q, const void* k, const void* v, void* o, float*
   p.part_o = (float*)workspace;
   p.part_lse = (float*)workspace + (size_t)batch * hq * nq * g.nsplit * d;
   return to_status(ffpa::launch_decode(p, dtype == FFPA_DTYPE_FP16, (hipStream_t)stream));
+}
+
+int ffpa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                    int nq, int nkv, int d, int dtype, float scale, int causal, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return decode_fwd(q, k, v, o, lse, batch, hq, hkv, nq, nkv, d, nullptr, dtype, scale, causal, workspace,
+                    workspace_bytes, stream);
+}
+
+int ffpa_decode_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq,
+                            int hkv, int nq, int nkv, int d, const int64_t* strides, int dtype, float scale,
+                            int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  if (strides == nullptr) return FFPA_ERR_INVALID_ARGUMENT;
+  return decode_fwd(q, k, v, o, lse, batch, hq, hkv, nq, nkv, d, strides, dtype, scale, causal, workspace,
+                    workspace_bytes, stream);
 }
 
 size_t ffpa_varlen_bwd_workspace_bytes(int hq, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k) {

@@ -244,7 +244,7 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 
 // Geometry of one (batch or sequence) slice, resolved from dense strides or cu_seqlens.
 struct SeqView {
-  long long q_off, k_off, lse_off;
+  long long q_off, k_off, lse_off, v_off, o_off;
   int lq, lk;
 };
 
@@ -257,12 +257,16 @@ __device__ __forceinline__ SeqView seq_view(const AttnParams& p, int s) {
     v.lk = p.cu_k[s + 1] - k0;
     v.q_off = (long long)q0 * p.q_row;
     v.k_off = (long long)k0 * p.k_row;
+    v.v_off = (long long)k0 * p.v_row;
+    v.o_off = (long long)q0 * p.o_row;
     v.lse_off = q0;
   } else {
     v.lq = p.nq;
     v.lk = p.nkv;
     v.q_off = (long long)s * p.q_batch;
     v.k_off = (long long)s * p.k_batch;
+    v.v_off = (long long)s * p.v_batch;
+    v.o_off = (long long)s * p.o_batch;
     v.lse_off = (long long)s * p.lse_batch;
   }
   return v;

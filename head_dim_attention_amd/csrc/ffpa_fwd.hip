@@ -111,12 +111,19 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   constexpr bool kPingPong = NW == 8 && NBUF == 2 && NC == 2 && C::RS == 1024;
 
   const uint16_t* qh = (const uint16_t*)p.q + sv.q_off + (long long)hl * p.q_head;
-  const int row_bytes = p.k_row * 2;
-  const char* kbase = (const char*)p.k + 2 * (sv.k_off + (long long)kvh * p.k_head);
-  const char* vbase = (const char*)p.v + 2 * (sv.k_off + (long long)kvh * p.k_head);
-  const uint32_t span = (uint32_t)min((long long)max(sv.lk, 1) * row_bytes, (long long)0xFFFFFFF0);
-  const i32x4_t krs = make_rsrc(kbase, span);
-  const i32x4_t vrs = make_rsrc(vbase, span);
+  // K and V of the KV head: buffer resource over the head's rows and the row stride in bytes
+  // (K and V may have different strides, e.g. slices of one fused QKV tensor).
+  struct Src {
+    i32x4_t rs;
+    int rb;
+  };
+  auto stream_src = [&](const void* base, long long off, int row) {
+    const int rb = row * 2;
+    const uint32_t span = (uint32_t)min((long long)max(sv.lk, 1) * rb, (long long)0xFFFFFFF0);
+    return Src{make_rsrc((const uint16_t*)base + off, span), rb};
+  };
+  const Src ksrc = stream_src(p.k, sv.k_off + (long long)kvh * p.k_head, p.k_row);
+  const Src vsrc = stream_src(p.v, sv.v_off + (long long)kvh * p.v_head, p.v_row);
 
   const int off = sv.lk - sv.lq;  // tail alignment of the causal mask
   int kend = sv.lk;
@@ -169,14 +176,14 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     const int pc = (i % IPR) * 64 + lane;
     voff[ii] = min(pc ^ swz(R), dch - 1) << 4;
   }
-  auto issue1 = [&](i32x4_t rs, int j, lds_t* dst, int ii) {
+  auto issue1 = [&](const Src& x, int j, lds_t* dst, int ii) {
     const int i = w + NW * ii;
     const int row = min(j * 32 + i / IPR, sv.lk - 1);
-    dma16_buf(rs, voff[ii], row * row_bytes, dst + i * 1024);
+    dma16_buf(x.rs, voff[ii], row * x.rb, dst + i * 1024);
   };
-  auto issue = [&](i32x4_t rs, int j, lds_t* dst) {
+  auto issue = [&](const Src& x, int j, lds_t* dst) {
 #pragma unroll
-    for (int ii = 0; ii < C::NINSTR; ++ii) issue1(rs, j, dst, ii);
+    for (int ii = 0; ii < C::NINSTR; ++ii) issue1(x, j, dst, ii);
   };
   // With two buffers, the copies of tile j + 1 are spread over the MFMAs of step j (K during the
   // scores, V during P V): the copy path moves about 64 B per clock per CU, so a whole tile issued
@@ -295,7 +302,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
       if constexpr (NBUF == 2) {
 #pragma unroll
         for (int ii = 0; ii < C::NINSTR; ++ii)
-          if (kb == spread_at(2 * NDB, ii)) issue1(krs, j + 1, kbuf((j + 1) & 1), ii);
+          if (kb == spread_at(2 * NDB, ii)) issue1(ksrc, j + 1, kbuf((j + 1) & 1), ii);
       }
     });
     // In flight: V_j (issued during P V of step j - 1), then K_{j+1}. V_j is needed after this
@@ -303,7 +310,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     if constexpr (NBUF == 2) wait_vmcnt<C::NINSTR>();
     lds_barrier();
     if constexpr (NBUF == 1) {
-      if (j + 1 < jend) issue(krs, j + 1, kbuf(0));
+      if (j + 1 < jend) issue(ksrc, j + 1, kbuf(0));
     }
     s_combine(j, sacc);
   };
@@ -369,18 +376,18 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
       if constexpr (NBUF == 2) {
 #pragma unroll
         for (int ii = 0; ii < C::NINSTR; ++ii)
-          if (m == spread_at(2 * NDB, ii)) issue1(vrs, j + 1, vbuf((j + 1) & 1), ii);
+          if (m == spread_at(2 * NDB, ii)) issue1(vsrc, j + 1, vbuf((j + 1) & 1), ii);
       }
     });
     if constexpr (NBUF == 1) {
       lds_barrier();
-      if (j + 1 < jend) issue(vrs, j + 1, vbuf(0));
+      if (j + 1 < jend) issue(vsrc, j + 1, vbuf(0));
     }
   };
 
   if (jend > jbeg) {
-    issue(krs, jbeg, kbuf(NBUF == 2 ? (jbeg & 1) : 0));
-    issue(vrs, jbeg, vbuf(NBUF == 2 ? (jbeg & 1) : 0));
+    issue(ksrc, jbeg, kbuf(NBUF == 2 ? (jbeg & 1) : 0));
+    issue(vsrc, jbeg, vbuf(NBUF == 2 ? (jbeg & 1) : 0));
   }
   // The Q operands (and tile 0) are complete before the loop, so the loop never waits for them.
   wait_all();
@@ -404,11 +411,11 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     int gvoff[4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) gvoff[ii] = min(lane ^ swz(wg + 4 * ii), dch - 1) << 4;
-    const i32x4_t grs = grp == 0 ? krs : vrs;
+    const Src gsrc = grp == 0 ? ksrc : vsrc;
     auto gcopy = [&](int j, int ii) {
       const int i = wg + 4 * ii;
       lds_t* dst = (grp == 0 ? kbuf(j & 1) : vbuf(j & 1)) + i * 1024;
-      dma16_buf(grs, gvoff[ii & 3], min(j * 32 + i, sv.lk - 1) * row_bytes, dst);
+      dma16_buf(gsrc.rs, gvoff[ii & 3], min(j * 32 + i, sv.lk - 1) * gsrc.rb, dst);
     };
     auto s_phase = [&](int j) {
       s_partial(j, sacc, [&](int kb) {
@@ -548,7 +555,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const int qi = qw0 + qb * 32 + l32;
     if (qi < sv.lq) {
-      uint16_t* orow = (uint16_t*)p.o + sv.q_off + (long long)h * p.q_head + (long long)qi * p.q_row;
+      uint16_t* orow = (uint16_t*)p.o + sv.o_off + (long long)h * p.o_head + (long long)qi * p.o_row;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -651,7 +658,7 @@ __global__ void __launch_bounds__(256) ffpa_decode_combine_kernel(AttnParams p, 
     }
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  uint16_t* orow = (uint16_t*)p.o + (long long)b * p.q_batch + (long long)h * p.q_head + (long long)i * p.q_row;
+  uint16_t* orow = (uint16_t*)p.o + (long long)b * p.o_batch + (long long)h * p.o_head + (long long)i * p.o_row;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int d = 4 * (lane + 64 * k);

@@ -29,9 +29,11 @@ struct AttnParams {
   void* pst;  // stored P (same geometry as ds), or NULL
   long long ds_batch, ds_head;
   int ds_row;
-  // Dense strides in elements (unused for varlen except row/head strides).
-  long long q_batch, k_batch, lse_batch;
-  int q_row, q_head, k_row, k_head, lse_head;
+  // Dense strides in elements (unused for varlen except row/head strides). The forward reads V
+  // and writes O with their own strides (v_*, o_*); every other kernel uses q's strides for
+  // o/dout/dq and k's for v/dk/dv, and the backward entry points set v_* = k_*, o_* = q_*.
+  long long q_batch, k_batch, lse_batch, v_batch, o_batch;
+  int q_row, q_head, k_row, k_head, lse_head, v_row, v_head, o_row, o_head;
   // Problem.
   int batch, hq, hkv, group;  // group = hq / hkv
   int nq, nkv;                // dense lengths, or max lengths for varlen

@@ -87,6 +87,23 @@ int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int dtype, float scale, int causal, void* stream);
 
 /*
+ * Strided (zero-copy) dense forward ("Backends Overview", backend table notes: NHD zero-copy
+ * consumes [B, N, H, D] or fused-QKV chunk views without a packed copy, an inference-path
+ * feature). Same as ffpa_fwd, but q, k, v and o are addressed through strides instead of the
+ * packed [B, H, N, D] layout: element (b, h, n, d) of tensor t sits at
+ *   b * strides[3t] + h * strides[3t + 1] + n * strides[3t + 2] + d,    t = 0 q, 1 k, 2 v, 3 o,
+ * with strides in elements (so [B, N, H, D] is {N H D, D, H D} and a fused [B, N, 3, H, D] tensor
+ * gives q, k, v views with {3 N H D, D, 3 H D} at offsets 0, H D, 2 H D). lse stays packed
+ * [batch, hq, nq]. Requirements (else FFPA_ERR_INVALID_ARGUMENT): strides non-NULL, non-negative
+ * and multiples of 8; q, k, v, o 16-byte aligned; for every tensor, (rows - 1) * row stride + d
+ * below 2^30 elements and head and row strides below 2^31. o must not overlap the inputs or
+ * itself.
+ */
+int ffpa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int batch, int hq, int hkv, int nq, int nkv, int d, const int64_t* strides,
+                     int dtype, float scale, int causal, void* stream);
+
+/*
  * Split-KV decode forward ("Triton Backend", "Feature support": decode as a two-stage split-KV
  * path; "Backends Overview", "Automatic SDPA fallback": the native decode path serves Nq in
  * [1, 8)). Same arguments, layouts and results as ffpa_fwd (o, lse), plus a caller-owned device
@@ -100,6 +117,12 @@ int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int ffpa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                     int batch, int hq, int hkv, int nq, int nkv, int d,
                     int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ffpa_decode_fwd with the strided layouts of ffpa_fwd_strided (same strides[12] and rules). */
+int ffpa_decode_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int batch, int hq, int hkv, int nq, int nkv, int d, const int64_t* strides,
+                            int dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * Bytes of the ffpa_decode_fwd workspace for these sizes: batch * hq * nq * nsplit * (d + 1) * 4,

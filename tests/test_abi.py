@@ -203,3 +203,28 @@ def test_decode_validation(lib):
     assert lib.ffpa_decode_fwd(*args, P, 16, S) == 1                 # too small
     bad_d = [P] * 5 + [1, 2, 2, 1, 64, 300, 0, 0.04, 0]
     assert lib.ffpa_decode_fwd(*bad_d, P, 1 << 20, S) == 2          # unsupported head dim
+
+
+def _strided_args(strides, ptrs=None):
+    ptrs = ptrs or [P] * 5
+    return (*ptrs, 1, 2, 2, 64, 64, 512, strides, 0, 0.04, 0, S)
+
+
+def test_strided_validation(lib):
+    ok = [64 * 2 * 512, 512, 2 * 512] * 4          # [B, N, H, D] viewed as [B, H, N, D]
+    arr = lambda xs: (ctypes.c_int64 * 12)(*xs)
+    assert lib.ffpa_fwd_strided(*_strided_args(None)) == 1                     # NULL strides
+    for i in range(12):
+        bad = list(ok)
+        bad[i] = 4                                                              # not a multiple of 8
+        assert lib.ffpa_fwd_strided(*_strided_args(arr(bad))) == 1
+        bad[i] = -8                                                             # negative
+        assert lib.ffpa_fwd_strided(*_strided_args(arr(bad))) == 1
+    huge = list(ok)
+    huge[5] = 1 << 26                                                           # K rows beyond 2^31 bytes
+    assert lib.ffpa_fwd_strided(*_strided_args(arr(huge))) == 1
+    mis = [P, ctypes.c_void_p(0x1008), P, P, P]                                 # k not 16-byte aligned
+    assert lib.ffpa_fwd_strided(*_strided_args(arr(ok), mis)) == 1
+    args = (P, P, P, P, P, 1, 2, 2, 1, 64, 512, arr(ok), 0, 0.04, 0)
+    assert lib.ffpa_decode_fwd_strided(*args, N, 1 << 20, S) == 1             # NULL workspace
+    assert lib.ffpa_decode_fwd_strided(P, P, P, P, P, 1, 2, 2, 1, 64, 512, None, 0, 0.04, 0, P, 1 << 20, S) == 1
