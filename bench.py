@@ -140,7 +140,7 @@ def decode_leg(F, W, w, seed: int, steps: int, warmup: int) -> dict:
             "head_dim": d, "causal": w.causal, "dtype": w.dtype, "ms": round(ms, 4),
             "nsplit": nws // (b * hq * nq * (d + 1) * 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic("decode"),
                          "algorithmic_bytes": alg_bytes, "kv_bytes": kv_bytes}}
 
 
