@@ -25,6 +25,12 @@ What is computed, and where the ffpa-attn user guide fixes it:
   Delta = rowsum(dO * O), dV = P^T dO, dP = dO V^T, dS = P * (dP - Delta), dK = scale dS^T Q,
   dQ = scale dS K. These are the exact gradients of L = sum(dO * O); the oracle writes the
   definition out and leaves the split into kernels to the GPU side.
+* attn_mask ("Triton Backend", "Feature support"): an additive bias broadcastable to
+  [B, Hq, Nq, Nkv] is added to the scaled scores (SDPA semantics); a boolean mask is the bias
+  0 where it keeps a key and -inf where it drops one. An entry whose score is -inf is not a legal
+  key, so a row with no finite score is an empty row (O = 0, LSE = -inf, zero gradient, as for
+  the causal mask). The bias gradient is dS (the gradient of L with respect to the scores)
+  summed over the dimensions the bias broadcasts.
 
 Everything is the plain definition in float64 NumPy: S is materialised per (batch, KV group).
 Queries are independent rows, so they are processed in row blocks to bound memory; that changes
@@ -38,7 +44,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 __all__ = [
-    "legal_mask", "softmax_rows", "group_forward", "group_backward",
+    "legal_mask", "softmax_rows", "group_forward", "group_backward", "mask_to_bias", "reduce_to_shape",
     "attn_fwd", "attn_bwd", "varlen_fwd", "varlen_bwd", "preprocess_delta", "fwd_rows",
 ]
 
@@ -71,8 +77,19 @@ def softmax_rows(s: np.ndarray, legal: np.ndarray):
     return p, lse
 
 
-def group_forward(qg: np.ndarray, kg: np.ndarray, vg: np.ndarray, scale: float, causal: bool):
-    """One KV group. qg [G, Nq, D]; kg, vg [Nkv, D]. Returns O [G, Nq, D], LSE [G, Nq]."""
+def _scores(q_b, kg, scale, rows, nq, nkv, causal, bias_b):
+    """Scaled scores of a row block (plus the bias rows, if any) and their legal entries."""
+    s = scale * (q_b @ kg.T)
+    legal = legal_mask(rows, nq, nkv, causal)
+    if bias_b is not None:
+        s = s + bias_b
+        legal = legal & (s > -np.inf)
+    return s, legal
+
+
+def group_forward(qg: np.ndarray, kg: np.ndarray, vg: np.ndarray, scale: float, causal: bool, bias_g=None):
+    """One KV group. qg [G, Nq, D]; kg, vg [Nkv, D]; bias_g None or [G, Nq, Nkv].
+    Returns O [G, Nq, D], LSE [G, Nq]."""
     g_, nq, d = qg.shape
     nkv = kg.shape[0]
     o = np.zeros((g_, nq, d), dtype=np.float64)
@@ -82,18 +99,20 @@ def group_forward(qg: np.ndarray, kg: np.ndarray, vg: np.ndarray, scale: float, 
     for h in range(g_):
         for r0 in range(0, nq, _ROW_BLOCK):
             rows = np.arange(r0, min(nq, r0 + _ROW_BLOCK))
-            s = scale * (qg[h, rows] @ kg.T)
-            p, l_ = softmax_rows(s, legal_mask(rows, nq, nkv, causal))
+            s, legal = _scores(qg[h, rows], kg, scale, rows, nq, nkv, causal,
+                               None if bias_g is None else bias_g[h, rows])
+            p, l_ = softmax_rows(s, legal)
             o[h, rows] = p @ vg
             lse[h, rows] = l_
     return o, lse
 
 
-def group_backward(qg, kg, vg, dog, scale: float, causal: bool):
+def group_backward(qg, kg, vg, dog, scale: float, causal: bool, bias_g=None):
     """Gradients of L = sum(dO * O) for one KV group.
 
-    qg, dog [G, Nq, D]; kg, vg [Nkv, D]. Returns dQ [G, Nq, D], dK [Nkv, D], dV [Nkv, D], and the
-    forward's O [G, Nq, D], LSE [G, Nq] and Delta [G, Nq] (float64).
+    qg, dog [G, Nq, D]; kg, vg [Nkv, D]; bias_g None or [G, Nq, Nkv]. Returns dQ [G, Nq, D],
+    dK [Nkv, D], dV [Nkv, D], the forward's O [G, Nq, D], LSE [G, Nq] and Delta [G, Nq], and dS
+    [G, Nq, Nkv] (the gradient with respect to the scores; None without a bias), all float64.
     """
     g_, nq, d = qg.shape
     nkv = kg.shape[0]
@@ -103,15 +122,17 @@ def group_backward(qg, kg, vg, dog, scale: float, causal: bool):
     o = np.zeros((g_, nq, d), dtype=np.float64)
     lse = np.full((g_, nq), -np.inf, dtype=np.float64)
     delta = np.zeros((g_, nq), dtype=np.float64)
+    ds_all = None if bias_g is None else np.zeros((g_, nq, nkv), dtype=np.float64)
     if nq == 0 or nkv == 0:
-        return dq, dk, dv, o, lse, delta
+        return dq, dk, dv, o, lse, delta, ds_all
     for h in range(g_):
         for r0 in range(0, nq, _ROW_BLOCK):
             rows = np.arange(r0, min(nq, r0 + _ROW_BLOCK))
             q_b = qg[h, rows]
             do_b = dog[h, rows]
-            s = scale * (q_b @ kg.T)
-            p, l_ = softmax_rows(s, legal_mask(rows, nq, nkv, causal))
+            s, legal = _scores(q_b, kg, scale, rows, nq, nkv, causal,
+                               None if bias_g is None else bias_g[h, rows])
+            p, l_ = softmax_rows(s, legal)
             o_b = p @ vg
             # Stage 1 (preprocess): Delta_i = sum_d dO_id * O_id.
             dlt = np.sum(do_b * o_b, axis=1)
@@ -127,7 +148,9 @@ def group_backward(qg, kg, vg, dog, scale: float, causal: bool):
             o[h, rows] = o_b
             lse[h, rows] = l_
             delta[h, rows] = dlt
-    return dq, dk, dv, o, lse, delta
+            if ds_all is not None:
+                ds_all[h, rows] = ds
+    return dq, dk, dv, o, lse, delta, ds_all
 
 
 def _threads() -> int:
@@ -154,20 +177,43 @@ def _map_groups(fn, items):
         return list(ex.map(fn, items))
 
 
-def attn_fwd(q, k, v, *, scale: float, causal: bool):
-    """Dense forward. q [B,Hq,Nq,D]; k, v [B,Hkv,Nkv,D]. Returns (O [B,Hq,Nq,D], LSE [B,Hq,Nq])."""
+def mask_to_bias(mask) -> np.ndarray:
+    """A boolean attn_mask (True keeps the key) as the equivalent additive bias (0 / -inf)."""
+    m = np.asarray(mask.detach().cpu().numpy() if hasattr(mask, "detach") else mask, dtype=bool)
+    return np.where(m, 0.0, -np.inf)
+
+
+def _full_bias(bias, b, hq, nq, nkv):
+    return None if bias is None else np.broadcast_to(_f64(bias), (b, hq, nq, nkv))
+
+
+def reduce_to_shape(full: np.ndarray, shape) -> np.ndarray:
+    """Sum a [B, Hq, Nq, Nkv] array over the dimensions a bias of ``shape`` broadcasts."""
+    shape = tuple(shape)
+    lead = full.ndim - len(shape)
+    out = full.sum(axis=tuple(range(lead))) if lead > 0 else full
+    axes = tuple(i for i, n in enumerate(shape) if n == 1 and out.shape[i] != 1)
+    return out.sum(axis=axes, keepdims=True) if axes else out
+
+
+def attn_fwd(q, k, v, *, scale: float, causal: bool, bias=None):
+    """Dense forward. q [B,Hq,Nq,D]; k, v [B,Hkv,Nkv,D]; bias None or broadcastable to
+    [B,Hq,Nq,Nkv] (use mask_to_bias for a boolean mask). Returns (O [B,Hq,Nq,D], LSE [B,Hq,Nq])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     b, hq, nq, d = q.shape
     hkv = k.shape[1]
     assert hq % hkv == 0, "Hq must be a multiple of Hkv"
     gsz = hq // hkv
+    nkv = k.shape[2]
+    fb = _full_bias(bias, b, hq, nq, nkv)
     o = np.zeros((b, hq, nq, d))
     lse = np.zeros((b, hq, nq))
     items = [(bi, g) for bi in range(b) for g in range(hkv)]
 
     def run(it):
         bi, g = it
-        return group_forward(q[bi, g * gsz:(g + 1) * gsz], k[bi, g], v[bi, g], scale, causal)
+        sl = slice(g * gsz, (g + 1) * gsz)
+        return group_forward(q[bi, sl], k[bi, g], v[bi, g], scale, causal, None if fb is None else fb[bi, sl])
 
     for (bi, g), (og, lg) in zip(items, _map_groups(run, items)):
         o[bi, g * gsz:(g + 1) * gsz] = og
@@ -175,27 +221,37 @@ def attn_fwd(q, k, v, *, scale: float, causal: bool):
     return o, lse
 
 
-def attn_bwd(q, k, v, do, *, scale: float, causal: bool):
-    """Dense backward of L = sum(dO * O). Returns (dQ, dK, dV) float64 with the input shapes."""
+def attn_bwd(q, k, v, do, *, scale: float, causal: bool, bias=None):
+    """Dense backward of L = sum(dO * O). Returns (dQ, dK, dV) float64 with the input shapes, and
+    with a bias also dBias with the bias's shape (dS summed over its broadcast dimensions)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     b, hq, nq, d = q.shape
     hkv = k.shape[1]
     gsz = hq // hkv
+    nkv = k.shape[2]
+    fb = _full_bias(bias, b, hq, nq, nkv)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    ds = None if fb is None else np.zeros((b, hq, nq, nkv))
     items = [(bi, g) for bi in range(b) for g in range(hkv)]
 
     def run(it):
         bi, g = it
         sl = slice(g * gsz, (g + 1) * gsz)
-        return group_backward(q[bi, sl], k[bi, g], v[bi, g], do[bi, sl], scale, causal)[:3]
+        r = group_backward(q[bi, sl], k[bi, g], v[bi, g], do[bi, sl], scale, causal,
+                           None if fb is None else fb[bi, sl])
+        return r[:3] + (r[6],)
 
-    for (bi, g), (dqg, dkg, dvg) in zip(items, _map_groups(run, items)):
+    for (bi, g), (dqg, dkg, dvg, dsg) in zip(items, _map_groups(run, items)):
         dq[bi, g * gsz:(g + 1) * gsz] = dqg
         dk[bi, g] = dkg
         dv[bi, g] = dvg
-    return dq, dk, dv
+        if ds is not None:
+            ds[bi, g * gsz:(g + 1) * gsz] = dsg
+    if ds is None:
+        return dq, dk, dv
+    return dq, dk, dv, reduce_to_shape(ds, np.shape(bias))
 
 
 def preprocess_delta(o, do) -> np.ndarray:

@@ -369,3 +369,115 @@ def test_fwd_rows_matches_full():
         orow, lrow = ref.fwd_rows(q[0, 0], k[0, 0], v[0, 0], rows, scale=0.3, causal=causal)
         np.testing.assert_allclose(orow, o[0, 0, rows], atol=1e-14)
         np.testing.assert_allclose(lrow, lse[0, 0, rows], atol=1e-14)
+
+
+# ----------------------------------------------------------------------------------------------
+# P-m: attn_mask. An additive bias is added to the scaled scores and a boolean mask is the bias
+# 0 / -inf ("Triton Backend", "Feature support": boolean and additive masks broadcast in any
+# dimension, the bias gradient reduced to the mask's shape).
+# ----------------------------------------------------------------------------------------------
+def test_bias_row_constant_shifts_lse_only():
+    """Adding c_i to every score of row i leaves P and O unchanged and adds c_i to LSE_i."""
+    r = rng(21)
+    q = r.standard_normal((1, 2, 5, 8))
+    k = r.standard_normal((1, 1, 7, 8))
+    v = r.standard_normal((1, 1, 7, 8))
+    c = r.standard_normal((1, 2, 5, 1))
+    for causal in (False, True):
+        o0, l0 = ref.attn_fwd(q, k, v, scale=0.3, causal=causal)
+        o1, l1 = ref.attn_fwd(q, k, v, scale=0.3, causal=causal, bias=c)
+        np.testing.assert_allclose(o1, o0, atol=1e-13)
+        np.testing.assert_allclose(l1, l0 + c[..., 0], atol=1e-13)
+
+
+def test_mask_equals_causal_and_empty_rows():
+    """A boolean mask with the bottom-right causal pattern gives exactly the causal results;
+    a row the mask empties is O = 0, LSE = -inf with zero gradient."""
+    r = rng(22)
+    nq, nkv = 6, 4
+    q = r.standard_normal((2, 2, nq, 8))
+    k = r.standard_normal((2, 2, nkv, 8))
+    v = r.standard_normal((2, 2, nkv, 8))
+    do = r.standard_normal((2, 2, nq, 8))
+    keep = np.arange(nkv)[None, :] <= np.arange(nq)[:, None] + (nkv - nq)
+    bias = ref.mask_to_bias(keep)
+    o0, l0 = ref.attn_fwd(q, k, v, scale=0.5, causal=True)
+    o1, l1 = ref.attn_fwd(q, k, v, scale=0.5, causal=False, bias=bias)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    g0 = ref.attn_bwd(q, k, v, do, scale=0.5, causal=True)
+    g1 = ref.attn_bwd(q, k, v, do, scale=0.5, causal=False, bias=bias)
+    for a, b in zip(g0, g1[:3]):
+        assert np.array_equal(a, b)
+    assert np.all(l1[:, :, :2] == -np.inf) and np.all(o1[:, :, :2] == 0)
+    assert np.all(g1[3][:2] == 0) and g1[3].shape == bias.shape
+
+
+@pytest.mark.parametrize("shape", [(2, 4, 5, 6), (1, 4, 5, 6), (2, 1, 5, 6), (1, 1, 5, 6), (2, 4, 1, 6),
+                                   (1, 4, 5, 1), (5, 6)])
+def test_fd_bias_gradient(shape):
+    """dBias against central finite differences of L = sum(dO * O), for full and broadcast
+    biases (the gradient of a broadcast bias is the sum over the dimensions it broadcasts)."""
+    r = rng(23)
+    q = r.standard_normal((2, 4, 5, 8))
+    k = r.standard_normal((2, 2, 6, 8))
+    v = r.standard_normal((2, 2, 6, 8))
+    do = r.standard_normal((2, 4, 5, 8))
+    bias = r.standard_normal(shape)
+    for causal in (False, True):
+        g = ref.attn_bwd(q, k, v, do, scale=0.4, causal=causal, bias=bias)
+        assert g[3].shape == bias.shape
+        num = np.zeros_like(bias)
+        eps = 1e-6
+        for idx in np.ndindex(bias.shape):
+            bp, bm = bias.copy(), bias.copy()
+            bp[idx] += eps
+            bm[idx] -= eps
+            lp = float(np.sum(do * ref.attn_fwd(q, k, v, scale=0.4, causal=causal, bias=bp)[0]))
+            lm = float(np.sum(do * ref.attn_fwd(q, k, v, scale=0.4, causal=causal, bias=bm)[0]))
+            num[idx] = (lp - lm) / (2 * eps)
+        # (a bias constant along the keys has a zero gradient: rows of dS sum to zero)
+        assert np.linalg.norm(num - g[3]) <= 1e-6 * max(np.linalg.norm(num), 1.0)
+
+
+def test_bias_gradient_rows_sum_to_zero():
+    """Each row of the full bias gradient (dS) sums to zero: sum_j P_ij (dP_ij - Delta_i) = 0."""
+    r = rng(24)
+    q = r.standard_normal((1, 2, 6, 8))
+    k = r.standard_normal((1, 2, 9, 8))
+    v = r.standard_normal((1, 2, 9, 8))
+    do = r.standard_normal((1, 2, 6, 8))
+    bias = r.standard_normal((1, 2, 6, 9))
+    db = ref.attn_bwd(q, k, v, do, scale=0.5, causal=True, bias=bias)[3]
+    np.testing.assert_allclose(db.sum(axis=-1), 0.0, atol=1e-13)
+
+
+@pytest.mark.parametrize("kind", ["additive", "boolean"])
+def test_bias_against_torch_sdpa(kind):
+    """PyTorch float64 SDPA with the same attn_mask (and autograd for the bias gradient)."""
+    r = rng(25)
+    b, hq, hkv, nq, nkv, d = 2, 4, 2, 5, 7, 16
+    q = r.standard_normal((b, hq, nq, d))
+    k = r.standard_normal((b, hkv, nkv, d))
+    v = r.standard_normal((b, hkv, nkv, d))
+    do = r.standard_normal((b, hq, nq, d))
+    scale = 1.0 / math.sqrt(d)
+    if kind == "additive":
+        mask_np = r.standard_normal((1, hq, nq, nkv))
+        bias = mask_np
+        tm = torch.tensor(mask_np, requires_grad=True)
+    else:
+        mask_np = r.random((b, 1, nq, nkv)) > 0.3
+        mask_np[..., 0] = True  # SDPA gives NaN for a fully masked row; keep one key per row
+        bias = ref.mask_to_bias(mask_np)
+        tm = torch.tensor(mask_np)
+    o, lse = ref.attn_fwd(q, k, v, scale=scale, causal=False, bias=bias)
+    g = ref.attn_bwd(q, k, v, do, scale=scale, causal=False, bias=bias)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(2, dim=1), tv.repeat_interleave(2, dim=1), attn_mask=tm, scale=scale)
+    to.backward(torch.tensor(do))
+    np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-12)
+    for a, t in zip(g[:3], (tq, tk, tv)):
+        np.testing.assert_allclose(a, t.grad.numpy(), atol=1e-12)
+    if kind == "additive":
+        np.testing.assert_allclose(g[3], tm.grad.numpy(), atol=1e-12)
