@@ -44,6 +44,8 @@ _SIGNATURES = {
     "ffpa_fwd": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp],
     "ffpa_decode_fwd": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp],
     "ffpa_fwd_strided": [_vp] * 5 + [_i] * 6 + [_i64p, _i, _f, _i, _vp],
+    "ffpa_fwd_masked": [_vp] * 5 + [_i] * 6 + [_vp, _i, _i64p, _i, _f, _i, _vp],
+    "ffpa_bwd_masked": [_vp] * 10 + [_i] * 6 + [_vp, _i, _i64p, _vp, _i, _f, _i, _vp, _sz, _vp],
     "ffpa_decode_fwd_strided": [_vp] * 5 + [_i] * 6 + [_i64p, _i, _f, _i, _vp, _sz, _vp],
     "ffpa_bwd": [_vp] * 10 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "ffpa_bwd_stage": [_i] + [_vp] * 10 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
@@ -177,14 +179,66 @@ def _fwd_prep(q, k, v):
     return q, k, v, o, lse, (b, hq, hkv, nq, nkv, d)
 
 
+MASK_ADDITIVE = 1
+MASK_BOOL = 2
+
+
+class _Mask:
+    """An attn_mask prepared for the C ABI: a 4-d view (batch, head, query, key) whose dims are
+    1 (broadcast, stride 0) or full, with unit key stride and rows of a multiple of 8 elements
+    (copied into such a layout when the given tensor is not)."""
+
+    def __init__(self, mask: torch.Tensor, q: torch.Tensor, nkv: int):
+        if not isinstance(mask, torch.Tensor) or mask.device != q.device:
+            raise ValueError("attn_mask must be a tensor on q's device")
+        if mask.dtype == torch.bool:
+            self.kind = MASK_BOOL
+        elif mask.dtype == q.dtype:
+            self.kind = MASK_ADDITIVE
+        else:
+            raise TypeError("attn_mask must be bool or have q's dtype")
+        b, hq, nq, _ = q.shape
+        full = (b, hq, nq, nkv)
+        if mask.dim() > 4:
+            raise ValueError("attn_mask must broadcast to [B, Hq, Nq, Nkv]")
+        self.orig_shape = tuple(mask.shape)
+        m = mask.reshape((1,) * (4 - mask.dim()) + self.orig_shape)
+        for n, f in zip(m.shape, full):
+            if n != 1 and n != f:
+                raise ValueError(f"attn_mask of shape {self.orig_shape} does not broadcast to {full}")
+        self.shape4 = tuple(m.shape)
+        es = m.element_size()
+        ok = (m.shape[3] == 1 or m.stride(3) == 1) and m.data_ptr() % (16 if es == 2 else 8) == 0 and \
+            all(m.stride(i) % 8 == 0 for i in range(3) if m.shape[i] > 1)
+        if not ok:
+            kp = ((m.shape[3] + 7) // 8) * 8 if m.shape[3] > 1 else 1
+            buf = torch.empty(self.shape4[:3] + (kp,), dtype=m.dtype, device=m.device)
+            buf[..., :m.shape[3]] = m
+            m = buf[..., :m.shape[3]]
+        self.tensor = m
+        self.strides = (ctypes.c_int64 * 4)(*[m.stride(i) if m.shape[i] > 1 else 0 for i in range(4)])
+
+
 def ffpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
-             scale: Optional[float] = None):
+             scale: Optional[float] = None, attn_mask: Optional[torch.Tensor] = None):
     """Dense forward. q [B,Hq,Nq,D], k/v [B,Hkv,Nkv,D] -> (o [B,Hq,Nq,D], lse fp32 [B,Hq,Nq]).
 
     Strided views (for example [B, N, H, D] tensors transposed to [B, H, N, D], or the q, k, v
     slices of one fused QKV tensor) are read in place through ffpa_fwd_strided; o then takes q's
-    layout when q is a dense permutation of [B, H, N, D]."""
+    layout when q is a dense permutation of [B, H, N, D].
+
+    attn_mask: None, a bool tensor (True keeps the key) or an additive bias in q's dtype,
+    broadcastable to [B, Hq, Nq, Nkv] (ffpa_fwd_masked; q, k, v then packed)."""
+    if attn_mask is not None:
+        q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
     q, k, v, o, lse, (b, hq, hkv, nq, nkv, d) = _fwd_prep(q, k, v)
+    if attn_mask is not None:
+        m = _Mask(attn_mask, q, nkv)
+        st = load_library().ffpa_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv, d,
+                                            _ptr(m.tensor), m.kind, m.strides, _dtype_code(q), _scale(scale, d),
+                                            int(bool(causal)), _stream(q))
+        _raise_for(st, "ffpa_fwd_masked")
+        return o, lse
     strides = _strides(q, k, v, o)
     L = load_library()
     if strides is None:
@@ -240,13 +294,18 @@ def _workspace(nbytes: int, like: torch.Tensor):
     return torch.empty(nbytes, dtype=torch.uint8, device=like.device), nbytes
 
 
-def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float] = None, store_ds: bool = True):
+def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float] = None, store_ds: bool = True,
+             attn_mask: Optional[torch.Tensor] = None, mask_grad: bool = False):
     """Dense backward -> (dq, dk, dv) with the shapes and dtype of q, k, v.
 
     store_ds: store P and dS in a temporary workspace of ffpa_bwd_workspace_bytes() bytes so that
     dK = scale dS^T Q, dV = P^T dO and dQ = scale dS K are products instead of recomputations
     (False: O(N) memory, recompute).
+    attn_mask: the forward's mask (ffpa_bwd_masked, always with the workspace); with mask_grad
+    (additive masks) the result is (dq, dk, dv, dmask), dmask with the mask's shape.
     """
+    if attn_mask is not None:
+        return _bwd_masked(q, k, v, o, dout, lse, causal, scale, attn_mask, mask_grad)
     q, k, v, o, dout = (_dev(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")))
     lse = _dev(lse, "lse")
     _same(q, k, v, o, dout)
@@ -264,6 +323,31 @@ def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float]
                                  _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(ws), nws, _stream(q))
     _raise_for(st, "ffpa_bwd")
     return dq, dk, dv
+
+
+def _bwd_masked(q, k, v, o, dout, lse, causal, scale, attn_mask, mask_grad):
+    q, k, v, o, dout = (_dev(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")))
+    lse = _dev(lse, "lse")
+    _same(q, k, v, o, dout)
+    b, hq, nq, d = q.shape
+    _, hkv, nkv, _ = k.shape
+    if o.shape != q.shape or dout.shape != q.shape or lse.shape != (b, hq, nq) or lse.dtype != torch.float32:
+        raise ValueError("o and dout must match q; lse must be float32 [B,Hq,Nq]")
+    m = _Mask(attn_mask, q, nkv)
+    if mask_grad and m.kind != MASK_ADDITIVE:
+        raise ValueError("only an additive attn_mask has a gradient")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((b, hq, nq), dtype=torch.float32, device=q.device)
+    dm = torch.empty(m.shape4, dtype=q.dtype, device=q.device) if mask_grad else None
+    ws, nws = _workspace(ffpa_bwd_workspace_bytes(b, hq, nq, nkv), q)
+    st = load_library().ffpa_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
+                                        _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, nq, nkv, d, _ptr(m.tensor),
+                                        m.kind, m.strides, _ptr(dm), _dtype_code(q), _scale(scale, d),
+                                        int(bool(causal)), _ptr(ws), nws, _stream(q))
+    _raise_for(st, "ffpa_bwd_masked")
+    if not mask_grad:
+        return dq, dk, dv
+    return dq, dk, dv, dm.reshape(m.orig_shape)
 
 
 def ffpa_bwd_stage(stage: int, q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool = False,

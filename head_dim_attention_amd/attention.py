@@ -24,18 +24,25 @@ DECODE_MAX_NQ = 8
 
 class _FFPAAttn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, causal, scale):
-        fwd = B.ffpa_decode_fwd if q.shape[2] < DECODE_MAX_NQ else B.ffpa_fwd
-        o, lse = fwd(q, k, v, causal=causal, scale=scale)
-        ctx.save_for_backward(q, k, v, o, lse)
+    def forward(ctx, q, k, v, causal, scale, mask):
+        if mask is not None:
+            o, lse = B.ffpa_fwd(q, k, v, causal=causal, scale=scale, attn_mask=mask)
+        else:
+            fwd = B.ffpa_decode_fwd if q.shape[2] < DECODE_MAX_NQ else B.ffpa_fwd
+            o, lse = fwd(q, k, v, causal=causal, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse, mask)
         ctx.causal, ctx.scale = causal, scale
         return o, lse
 
     @staticmethod
     def backward(ctx, do, dlse):
-        q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = B.ffpa_bwd(q, k, v, o, do, lse, causal=ctx.causal, scale=ctx.scale)
-        return dq, dk, dv, None, None
+        q, k, v, o, lse, mask = ctx.saved_tensors
+        if mask is None:
+            dq, dk, dv = B.ffpa_bwd(q, k, v, o, do, lse, causal=ctx.causal, scale=ctx.scale)
+            return dq, dk, dv, None, None, None
+        want = ctx.needs_input_grad[5] and mask.dtype != torch.bool
+        g = B.ffpa_bwd(q, k, v, o, do, lse, causal=ctx.causal, scale=ctx.scale, attn_mask=mask, mask_grad=want)
+        return g[0], g[1], g[2], None, None, (g[3] if want else None)
 
 
 class _FFPAVarlen(torch.autograd.Function):
@@ -55,13 +62,16 @@ class _FFPAVarlen(torch.autograd.Function):
         return dq, dk, dv, None, None, None, None, None, None
 
 
-def ffpa_attn_func(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool = False,
-                   scale: Optional[float] = None, return_lse: bool = False):
+def ffpa_attn_func(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[torch.Tensor] = None,
+                   is_causal: bool = False, scale: Optional[float] = None, return_lse: bool = False):
     """Attention over dense [B, H, N, D] tensors (fp16/bf16, D in 320..1024, D % 32 == 0).
 
-    Causal masking is bottom-right aligned; Hq may be any multiple of Hkv (GQA/MQA).
+    Causal masking is bottom-right aligned; Hq may be any multiple of Hkv (GQA/MQA). attn_mask:
+    None, a bool mask (True keeps the key) or an additive bias in q's dtype, broadcastable to
+    [B, Hq, Nq, Nkv] ("Triton Backend", "Feature support"); an additive mask that requires grad
+    gets its gradient reduced to its own shape.
     """
-    o, lse = _FFPAAttn.apply(q, k, v, bool(is_causal), scale)
+    o, lse = _FFPAAttn.apply(q, k, v, bool(is_causal), scale, attn_mask)
     return (o, lse) if return_lse else o
 
 

@@ -148,6 +148,31 @@ int apply_strides(AttnParams& p, const int64_t* st, const void* q, const void* k
   return FFPA_OK;
 }
 
+// attn_mask arguments: kind 1 additive (2-byte elements), 2 boolean (1 byte); strides[4] =
+// (batch, head, query, key) in elements, non-negative, key stride 0 or 1; with a contiguous key
+// dim the other strides are multiples of 8 and the pointer is 16-byte (additive) or 8-byte
+// (boolean) aligned, so that 8 keys are one aligned load.
+int apply_mask(AttnParams& p, const void* mask, int kind, const int64_t* st, float scale) {
+  if (mask == nullptr || st == nullptr || (kind != FFPA_MASK_ADDITIVE && kind != FFPA_MASK_BOOL))
+    return FFPA_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < 4; ++i)
+    if (st[i] < 0) return FFPA_ERR_INVALID_ARGUMENT;
+  if (st[3] != 0 && st[3] != 1) return FFPA_ERR_INVALID_ARGUMENT;
+  if (st[3] == 1) {
+    if (st[0] % 8 != 0 || st[1] % 8 != 0 || st[2] % 8 != 0) return FFPA_ERR_INVALID_ARGUMENT;
+    if ((uintptr_t)mask % (kind == FFPA_MASK_ADDITIVE ? 16 : 8) != 0) return FFPA_ERR_INVALID_ARGUMENT;
+  }
+  if (st[2] > (1LL << 31) - 1) return FFPA_ERR_INVALID_ARGUMENT;
+  p.mask = mask;
+  p.mask_kind = kind;
+  p.m_batch = st[0];
+  p.m_head = st[1];
+  p.m_row = (int)st[2];
+  p.m_key = (int)st[3];
+  p.inv_scale = 1.0f / scale;
+  return FFPA_OK;
+}
+
 // Split-KV decode geometry: rows = G * nq rows per KV head in blocks of 32, and the key ranges.
 // About two workgroups per compute unit (256 CUs), at least four 32-key tiles per range, at most
 // 256 ranges; the tile count per range is then evened out so that no range is empty.
@@ -217,6 +242,25 @@ int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return dense_fwd(q, k, v, o, lse, batch, hq, hkv, nq, nkv, d, nullptr, dtype, scale, causal, stream);
 }
 
+int ffpa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                    int nq, int nkv, int d, const void* mask, int mask_kind, const int64_t* mask_strides,
+                    int dtype, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FFPA_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
+  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  if (st != FFPA_OK) return st;
+  if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
+  AttnParams p = dense_params(batch, hq, hkv, nq, nkv, d, scale, causal);
+  const int ms = apply_mask(p, mask, mask_kind, mask_strides, scale);
+  if (ms != FFPA_OK) return ms;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  return to_status(ffpa::launch_fwd(p, dtype == FFPA_DTYPE_FP16, (hipStream_t)stream));
+}
+
 int ffpa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
                      int nq, int nkv, int d, const int64_t* strides, int dtype, float scale, int causal,
                      void* stream) {
@@ -249,7 +293,8 @@ int ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float*
 static int dense_bwd(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
                      const float* lse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv,
                      int nq, int nkv, int d, int dtype, float scale, int causal, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     size_t workspace_bytes, void* stream, const void* mask = nullptr, int mask_kind = 0,
+                     const int64_t* mask_strides = nullptr, void* dmask = nullptr) {
   if (stage < -1 || stage > 4) return FFPA_ERR_INVALID_ARGUMENT;
   if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
@@ -271,6 +316,11 @@ static int dense_bwd(int stage, const void* q, const void* k, const void* v, con
   p.dv = dv;
   const int ws = attach_ds(p, workspace, workspace_bytes, dense_ds_bytes(batch, hq, nq, nkv));
   if (ws != FFPA_OK) return ws;
+  if (mask != nullptr || mask_kind != 0) {
+    const int ms = apply_mask(p, mask, mask_kind, mask_strides, scale);
+    if (ms != FFPA_OK) return ms;
+    p.dmask = dmask;
+  }
   p.ds_row = (int)round_up8(nq);
   p.ds_head = (long long)nkv * p.ds_row;
   p.ds_batch = (long long)hq * p.ds_head;
@@ -331,6 +381,18 @@ int ffpa_decode_fwd_strided(const void* q, const void* k, const void* v, void* o
 
 size_t ffpa_varlen_bwd_workspace_bytes(int hq, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k) {
   return varlen_ds_bytes(hq, total_q, total_k, max_seqlen_q, max_seqlen_k);
+}
+
+int ffpa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq, int nkv, int d,
+                    const void* mask, int mask_kind, const int64_t* mask_strides, void* dmask, int dtype,
+                    float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr) return FFPA_ERR_INVALID_ARGUMENT;
+  if (dense_ds_bytes(batch, hq, nq, nkv) == 0 && batch >= 1 && hq >= 1 && nq >= 1 && nkv >= 1)
+    return FFPA_ERR_NOT_SUPPORTED;  // a head's P/dS block is too large for the stored path
+  if (dmask != nullptr && mask_kind != FFPA_MASK_ADDITIVE) return FFPA_ERR_INVALID_ARGUMENT;
+  return dense_bwd(-1, q, k, v, o, dout, lse, delta, dq, dk, dv, batch, hq, hkv, nq, nkv, d, dtype, scale, causal,
+                   workspace, workspace_bytes, stream, mask, mask_kind, mask_strides, dmask);
 }
 
 int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,

@@ -119,8 +119,11 @@ struct BwdCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <class T, int MODE, int NC, int NDB, int NBUF, int NW>
+// MASK (dK with the P/dS workspace only): the attn_mask term of each (query, key) pair is added to
+// the scores before P, as in the forward.
+template <class T, int MODE, int NC, int NDB, int NBUF, int NW, bool MASK = false>
 __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p) {
+  static_assert(!MASK || MODE == kDK, "the mask is applied where P and dS are stored");
   constexpr bool OWN_Q = MODE == kDQ;   // stationary rows are queries (dQ) or keys (dK, dV)
   constexpr bool HAS_DP = MODE != kDV;  // dK and dQ need dP = dO V^T
   constexpr int NX = HAS_DP ? 2 : 1;
@@ -385,6 +388,19 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
     } else {
       need_mask = (row0 + 32 > sv.lq) || (p.causal && ow0 + 31 > row0 + off);
     }
+    // attn_mask term of (query row0 + c_row(r, h), key oi) per register: one element each.
+    float mterm[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mterm[r] = 0.f;
+    if constexpr (MASK) {
+      if (oi < sv.lk) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const long long mr = mask_row(p, s, step_head(st), min(row0 + c_row(r, hh), sv.lq - 1));
+          mterm[r] = mask1<T>(p, mr, oi);
+        }
+      }
+    }
     uint32_t bop[2][4], ppk[2][4];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
@@ -393,7 +409,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
       for (int u = 0; u < 2; ++u) {
         const int rr = r + u;
         const float lse2 = row_val(lse2_lane, rr);
-        float pv = fast_exp2(sacc[rr] * p.scale_log2 - lse2);
+        float pv = fast_exp2((sacc[rr] + mterm[rr]) * p.scale_log2 - lse2);
         if (need_mask) {
           const int si = row0 + c_row(rr, hh);
           const int qi = OWN_Q ? oi : si;
@@ -930,7 +946,7 @@ struct PdsCfg {
   static_assert(2 * DW <= 512 && LDS <= 160 * 1024, "LDS budget");
 };
 
-template <class T, int NDB>
+template <class T, int NDB, bool MASK>
 __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
   using C = PdsCfg<NDB>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
@@ -1052,6 +1068,17 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
         df[4 * r4 + i] = pacc[4 * r4 + i] + b[i];
       }
     }
+    if constexpr (MASK) {
+      // attn_mask terms of this lane's 8 keys (added to the scores before P). The empty asm keeps
+      // the sums, and so the wait for the mask loads, ahead of the copies issued next.
+      float mb[8];
+      mask8<T>(p, mask_row(p, s, h, min(qi, sv.lq - 1)), j * 32 + 16 * cg + 8 * hh, sv.lk, mb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sf[e] += mb[e];
+        asm volatile("" ::"v"(sf[e]));
+      }
+    }
     copies();
     const int key0 = j * 32 + 16 * cg + 8 * hh;
     const bool need_mask = (j * 32 + 32 > sv.lk) || (p.causal && j * 32 + 31 > qw0 + off);
@@ -1152,7 +1179,10 @@ static hipError_t launch_pds(AttnParams p, hipStream_t st) {
   p.total = p.batch * p.hq * p.ntiles;
   if (p.total == 0) return hipSuccess;
   const int grid = (p.total + 7) & ~7;
-  hipLaunchKernelGGL((ffpa_pds_kernel<T, NDB>), dim3(grid), dim3(64 * C::NW), 0, st, p);
+  if (p.mask_kind != 0)
+    hipLaunchKernelGGL((ffpa_pds_kernel<T, NDB, true>), dim3(grid), dim3(64 * C::NW), 0, st, p);
+  else
+    hipLaunchKernelGGL((ffpa_pds_kernel<T, NDB, false>), dim3(grid), dim3(64 * C::NW), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1682,6 +1712,123 @@ static hipError_t launch_dv_p_t(const AttnParams& p, hipStream_t st) {
   return launch_dv_from_p<T, 4, DK>(p, nchunk, st);
 }
 
+// ------------------------------------------------------------------------------------------------
+// attn_mask gradient ("Triton Backend", "Feature support": the backward reduces the bias gradient
+// back to the mask's original shape): dBias = dS summed over the dimensions the bias broadcasts,
+// read from the stored (transposed) dS block. Pairs that are not legal (causal, or queries past Lq)
+// are not all written there and count as 0. The output has dims DB, DH, DQ, DK (1 where the bias
+// broadcasts), packed row-major in q's dtype, summed in fp32 and rounded once.
+//
+// Full query and key dims (the bias may broadcast over batch and heads): a workgroup owns a 64-key
+// x 64-query tile of one output (b', h'), adds the stored 16-byte pieces of every (batch, head) of
+// its set (4 lanes per key row, so each row's 128 bytes are one coalesced read), transposes
+// through LDS and writes 64 consecutive keys per instruction. A bias broadcast over queries or
+// keys uses one thread per output element looping over its whole set.
+// ------------------------------------------------------------------------------------------------
+struct DbiasDims {
+  int db, dh, dq, dk;
+};
+
+template <class T>
+__global__ void __launch_bounds__(256) ffpa_dbias_tile_kernel(AttnParams p, DbiasDims od) {
+  __shared__ float tile[64][65];
+  const int nit = (p.nq + 63) / 64, njt = (p.nkv + 63) / 64;
+  int item = blockIdx.x;
+  const int jt = item % njt;
+  item /= njt;
+  const int it = item % nit;
+  item /= nit;
+  const int ho = item % od.dh;
+  const int bo = item / od.dh;
+  const int i0 = it * 64, j0 = jt * 64;
+  const int tid = threadIdx.x;
+  const int off = p.nkv - p.nq;
+
+  // Phase A: thread (key row jr, query chunk c) sums queries i0 + 16 c + 0..15 of key j0 + jr.
+  const int jr = tid >> 2, c = tid & 3;
+  const int key = j0 + jr;
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  if (key < p.nkv) {
+    for (int b = od.db == 1 ? 0 : bo; b < (od.db == 1 ? p.batch : bo + 1); ++b)
+      for (int h = od.dh == 1 ? 0 : ho; h < (od.dh == 1 ? p.hq : ho + 1); ++h) {
+        const uint16_t* row = (const uint16_t*)p.ds + (long long)b * p.ds_batch + (long long)h * p.ds_head +
+                              (long long)key * p.ds_row;
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc) {
+          const int q8 = i0 + 16 * c + 8 * pc;
+          if (q8 < p.ds_row) {
+            const u32x4_t v = *(const u32x4_t*)(row + q8);
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              float lo, hi;
+              Elt<T>::unpack2(v[e2], lo, hi);
+              const int qa = q8 + 2 * e2;
+              const bool la = qa < p.nq && (!p.causal || key <= qa + off);
+              const bool lb = qa + 1 < p.nq && (!p.causal || key <= qa + 1 + off);
+              acc[8 * pc + 2 * e2] += la ? lo : 0.f;
+              acc[8 * pc + 2 * e2 + 1] += lb ? hi : 0.f;
+            }
+          }
+        }
+      }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) tile[16 * c + e][jr] = acc[e];
+  __syncthreads();
+  // Phase B: thread (key j, row group g) writes rows 16 g + 0..15 of the tile at key j0 + j.
+  const int j = tid & 63, g = tid >> 6;
+  if (j0 + j < p.nkv) {
+    uint16_t* out = (uint16_t*)p.dmask + ((long long)bo * od.dh + ho) * od.dq * (long long)od.dk + j0 + j;
+#pragma unroll 4
+    for (int r = 0; r < 16; ++r) {
+      const int qi = i0 + 16 * g + r;
+      if (qi < p.nq) {
+        const uint32_t pk = Elt<T>::pack2(tile[16 * g + r][j], 0.f);
+        out[(long long)qi * od.dk] = (uint16_t)(pk & 0xffffu);
+      }
+    }
+  }
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) ffpa_dbias_any_kernel(AttnParams p, DbiasDims od, long long total) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  long long r = idx;
+  const int jo = (int)(r % od.dk);
+  r /= od.dk;
+  const int io = (int)(r % od.dq);
+  r /= od.dq;
+  const int ho = (int)(r % od.dh);
+  const int bo = (int)(r / od.dh);
+  const int off = p.nkv - p.nq;
+  float acc = 0.f;
+  for (int b = od.db == 1 ? 0 : bo; b < (od.db == 1 ? p.batch : bo + 1); ++b)
+    for (int h = od.dh == 1 ? 0 : ho; h < (od.dh == 1 ? p.hq : ho + 1); ++h) {
+      const uint16_t* blk = (const uint16_t*)p.ds + (long long)b * p.ds_batch + (long long)h * p.ds_head;
+      for (int j = od.dk == 1 ? 0 : jo; j < (od.dk == 1 ? p.nkv : jo + 1); ++j)
+        for (int i = od.dq == 1 ? 0 : io; i < (od.dq == 1 ? p.nq : io + 1); ++i)
+          if (!p.causal || j <= i + off) acc += Elt<T>::to_f32(blk[(long long)j * p.ds_row + i]);
+    }
+  ((uint16_t*)p.dmask)[idx] = (uint16_t)(Elt<T>::pack2(acc, 0.f) & 0xffffu);
+}
+
+template <class T>
+static hipError_t launch_dbias_t(const AttnParams& p, hipStream_t st) {
+  const DbiasDims od{p.m_batch ? p.batch : 1, p.m_head ? p.hq : 1, p.m_row ? p.nq : 1, p.m_key ? p.nkv : 1};
+  if (od.dq == p.nq && od.dk == p.nkv && p.nq > 1 && p.nkv > 1) {
+    const long long blocks = (long long)od.db * od.dh * ((p.nq + 63) / 64) * ((p.nkv + 63) / 64);
+    hipLaunchKernelGGL(ffpa_dbias_tile_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st, p, od);
+  } else {
+    const long long total = (long long)od.db * od.dh * od.dq * od.dk;
+    hipLaunchKernelGGL(ffpa_dbias_any_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, p, od,
+                       total);
+  }
+  return hipGetLastError();
+}
+
 template <class T, int MODE, int NC, int NDB>
 static hipError_t launch_bwd_cfg(AttnParams p, hipStream_t st) {
   constexpr int NX = MODE != kDV ? 2 : 1;
@@ -1695,6 +1842,12 @@ static hipError_t launch_bwd_cfg(AttnParams p, hipStream_t st) {
   p.total = p.batch * (own_q ? p.hq : p.hkv) * p.ntiles;
   if (p.total == 0) return hipSuccess;
   const int grid = (p.total + 7) & ~7;
+  if constexpr (MODE == kDK) {
+    if (p.mask_kind != 0) {
+      hipLaunchKernelGGL((ffpa_bwd_kernel<T, kDK, NC, NDB, NBUF, NW, true>), dim3(grid), dim3(64 * NW), 0, st, p);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((ffpa_bwd_kernel<T, MODE, NC, NDB, NBUF, NW>), dim3(grid), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
@@ -1736,9 +1889,12 @@ static hipError_t launch_stage_t(int stage, const AttnParams& p, int nrows, int 
     // With a workspace, stage 4 stores P and dS (for D > 512 the dK kernel stores them as it goes)
     // and dK, dV, dQ are products of them.
     case 4: return p.ds != nullptr && p.d <= 512 ? launch_pds_t<T>(p, st) : hipSuccess;
-    case 1:
-      if (p.ds != nullptr && p.d <= 512) return launch_dv_p_t<T, true>(p, st);
-      return launch_bwd_mode<T, kDK>(p, st);
+    case 1: {
+      const hipError_t e = p.ds != nullptr && p.d <= 512 ? launch_dv_p_t<T, true>(p, st) : launch_bwd_mode<T, kDK>(p, st);
+      // The attn_mask gradient, once dS is stored (stage 4 for D <= 512, the dK kernel above otherwise).
+      if (e != hipSuccess || p.dmask == nullptr) return e;
+      return launch_dbias_t<T>(p, st);
+    }
     case 2: return p.pst != nullptr ? launch_dv_p_t<T, false>(p, st) : launch_bwd_mode<T, kDV>(p, st);
     default: return p.ds != nullptr ? launch_dq_ds_t<T>(p, st) : launch_bwd_mode<T, kDQ>(p, st);
   }

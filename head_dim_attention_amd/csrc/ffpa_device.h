@@ -298,4 +298,60 @@ __device__ __forceinline__ DsView ds_view(const AttnParams& p, int s, const SeqV
   return v;
 }
 
+// attn_mask terms of 8 consecutive keys key0 .. key0 + 7 of the mask row at element offset rowoff,
+// in units of the raw scores: bias / scale for an additive mask, 0 (kept) or -inf (dropped) for a
+// boolean one. Keys at or past lk give 0 (the caller masks them). With a contiguous key dim the
+// row offset and key0 are multiples of 8, so a whole piece is one aligned 16-byte (bias) or
+// 8-byte (boolean) load; the last, partial piece of a row is read element by element.
+template <class T>
+__device__ __forceinline__ void mask8(const AttnParams& p, long long rowoff, int key0, int lk, float (&out)[8]) {
+  if (p.mask_kind == 1) {
+    const uint16_t* m = (const uint16_t*)p.mask + rowoff;
+    if (p.m_key == 0) {
+      const float x = Elt<T>::to_f32(m[0]) * p.inv_scale;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = x;
+    } else if (key0 + 8 <= lk) {
+      const u32x4_t v = *(const u32x4_t*)(m + key0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float lo, hi;
+        Elt<T>::unpack2(v[e], lo, hi);
+        out[2 * e] = lo * p.inv_scale;
+        out[2 * e + 1] = hi * p.inv_scale;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = key0 + e < lk ? Elt<T>::to_f32(m[key0 + e]) * p.inv_scale : 0.f;
+    }
+  } else {
+    const uint8_t* m = (const uint8_t*)p.mask + rowoff;
+    if (p.m_key == 0) {
+      const float x = m[0] != 0 ? 0.f : -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = x;
+    } else if (key0 + 8 <= lk) {
+      const u32x2_t v = *(const u32x2_t*)(m + key0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = ((e < 4 ? v.x : v.y) >> (8 * (e & 3))) & 0xffu ? 0.f : -INFINITY;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = key0 + e < lk && m[key0 + e] == 0 ? -INFINITY : 0.f;
+    }
+  }
+}
+
+// attn_mask term of one key (< lk) of the mask row at element offset rowoff.
+template <class T>
+__device__ __forceinline__ float mask1(const AttnParams& p, long long rowoff, int key) {
+  const long long o = rowoff + (long long)key * p.m_key;
+  if (p.mask_kind == 1) return Elt<T>::to_f32(((const uint16_t*)p.mask)[o]) * p.inv_scale;
+  return ((const uint8_t*)p.mask)[o] != 0 ? 0.f : -INFINITY;
+}
+
+// Element offset of the attn_mask row of (slice s, query head h, query i).
+__device__ __forceinline__ long long mask_row(const AttnParams& p, int s, int h, int i) {
+  return (long long)s * p.m_batch + (long long)h * p.m_head + (long long)i * p.m_row;
+}
+
 }  // namespace ffpa

@@ -47,7 +47,10 @@ struct FwdCfg {
 
 // DEC selects the split-KV decode form (one 32-row block of (query head, query) rows of a KV
 // group, one range of key tiles, partial results to a workspace); see the decode section below.
-template <class T, int NC, int NDB, int QB, int NBUF, int NW, bool DEC = false>
+// MASK adds an attn_mask to the scores ("Triton Backend", "Feature support": boolean or additive,
+// broadcast in any dimension): the combined scores of each tile get bias / scale, or -inf where a
+// boolean mask drops the key, before the row max; a row that ends with no finite score is empty.
+template <class T, int NC, int NDB, int QB, int NBUF, int NW, bool DEC = false, bool MASK = false>
 __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p) {
   using C = FwdCfg<NC, NDB, QB, NBUF, NW>;
   static_assert(!DEC || (QB == 1 && NW == NC), "decode: one 32-row block per workgroup");
@@ -280,6 +283,21 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
         }
         sacc[qb][4 * r4] = mine.x; sacc[qb][4 * r4 + 1] = mine.y;
         sacc[qb][4 * r4 + 2] = mine.z; sacc[qb][4 * r4 + 3] = mine.w;
+      }
+    }
+    if constexpr (MASK) {
+      // Registers 0..7 hold keys 8 h + 0..7 of the tile, registers 8..15 keys 16 + 8 h + 0..7.
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qi = DEC ? qi_l : min(qw0 + qb * 32 + l32, sv.lq - 1);
+        const long long mr = mask_row(p, s, hl, qi);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float mb[8];
+          mask8<T>(p, mr, j * 32 + 16 * half + 8 * hh, sv.lk, mb);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sacc[qb][8 * half + e] += mb[e];
+        }
       }
     }
     // Mask tail keys and the causal diagonal (only on tiles that need it).
@@ -577,6 +595,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
 
 template <class T, int NC, int NDB>
 static hipError_t launch_fwd_cfg(AttnParams p, hipStream_t st) {
+  static_assert(NC == 2 || NC == 4, "head-dim split");
   constexpr int QB = 1;
   // Two waves per SIMD where the per-wave state fits 256 registers (D <= 512), else one.
   constexpr int NW = NC == 2 ? 8 : 4;
@@ -587,7 +606,10 @@ static hipError_t launch_fwd_cfg(AttnParams p, hipStream_t st) {
   p.total = p.batch * p.hq * p.ntiles;
   if (p.total == 0) return hipSuccess;
   const int grid = (p.total + 7) & ~7;
-  hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF, NW>), dim3(grid), dim3(64 * NW), 0, st, p);
+  if (p.mask_kind != 0)
+    hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF, NW, false, true>), dim3(grid), dim3(64 * NW), 0, st, p);
+  else
+    hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF, NW>), dim3(grid), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
 
@@ -678,7 +700,10 @@ static hipError_t launch_decode_cfg(AttnParams p, hipStream_t st) {
   p.total = p.batch * p.hkv * p.nsplit * p.nrb;
   if (p.total == 0) return hipSuccess;
   const int grid = (p.total + 7) & ~7;
-  hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF, NW, true>), dim3(grid), dim3(64 * NW), 0, st, p);
+  if (p.mask_kind != 0)
+    hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF, NW, true, true>), dim3(grid), dim3(64 * NW), 0, st, p);
+  else
+    hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF, NW, true>), dim3(grid), dim3(64 * NW), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nrows = p.batch * p.hq * p.nq;

@@ -49,6 +49,16 @@ struct AttnParams {
   int rows, nrb, nsplit, split_tiles;
   float* part_o;
   float* part_lse;
+  // attn_mask (dense entry points): kind 0 none, 1 additive bias (q's dtype, added to the scaled
+  // scores), 2 boolean (one byte per element, nonzero keeps the key). Element (b, h, i, j) sits at
+  // b * m_batch + h * m_head + i * m_row + j * m_key (stride 0 broadcasts; m_key is 0 or 1).
+  // dmask: the bias gradient (q's dtype), packed in the shape with a 1 for every 0-stride dim.
+  const void* mask;
+  void* dmask;
+  int mask_kind;
+  long long m_batch, m_head;
+  int m_row, m_key;
+  float inv_scale;  // 1 / scale: the bias in units of the raw scores
 };
 
 }  // namespace ffpa

@@ -66,6 +66,12 @@ typedef enum {
   FFPA_DTYPE_FP16 = 1
 } ffpa_dtype_t;
 
+/* attn_mask kinds ("Triton Backend", "Feature support": boolean and additive masks). */
+typedef enum {
+  FFPA_MASK_ADDITIVE = 1, /* a bias in q's dtype added to the scaled scores */
+  FFPA_MASK_BOOL = 2      /* one byte per element: nonzero keeps the key, 0 drops it (score -inf) */
+} ffpa_mask_kind_t;
+
 typedef enum {
   FFPA_OK = 0,
   FFPA_ERR_INVALID_ARGUMENT = 1, /* null pointer, size < 1, Hq % Hkv != 0, bad enum, causal not 0/1, scale <= 0 */
@@ -85,6 +91,25 @@ typedef enum {
 int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int batch, int hq, int hkv, int nq, int nkv, int d,
              int dtype, float scale, int causal, void* stream);
+
+/*
+ * Dense forward with an attn_mask ("Triton Backend", "Feature support": boolean and additive
+ * masks, broadcast in any of the four dimensions). Arguments as ffpa_fwd plus:
+ *   mask          device pointer to the mask (FFPA_MASK_ADDITIVE: q's dtype; FFPA_MASK_BOOL: one
+ *                 byte per element, nonzero keeps the key)
+ *   mask_kind     FFPA_MASK_ADDITIVE or FFPA_MASK_BOOL
+ *   mask_strides  host int64[4]: element (b, h, i, j) of the mask, for query head h, query i and
+ *                 key j, sits at b*s[0] + h*s[1] + i*s[2] + j*s[3]; a stride of 0 broadcasts that
+ *                 dimension. s[3] must be 0 or 1; with s[3] == 1, s[0..2] are multiples of 8 and
+ *                 the mask pointer is 16-byte (additive) / 8-byte (boolean) aligned.
+ * The scores are scale * q k^T + bias (or -inf where a boolean mask drops the key), combined with
+ * the causal mask when causal = 1; a row whose scores are all -inf is empty (O = 0, LSE = -inf).
+ * Invalid mask arguments are FFPA_ERR_INVALID_ARGUMENT.
+ */
+int ffpa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int batch, int hq, int hkv, int nq, int nkv, int d,
+                    const void* mask, int mask_kind, const int64_t* mask_strides,
+                    int dtype, float scale, int causal, void* stream);
 
 /*
  * Strided (zero-copy) dense forward ("Backends Overview", backend table notes: NHD zero-copy
@@ -152,6 +177,21 @@ int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, float* delta, void* dq, void* dk, void* dv,
              int batch, int hq, int hkv, int nq, int nkv, int d,
              int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dense backward with the attn_mask of ffpa_fwd_masked (same mask arguments), through the P/dS
+ * workspace, which is required here (NULL: FFPA_ERR_INVALID_ARGUMENT; sizes whose workspace is
+ * not available: FFPA_ERR_NOT_SUPPORTED). The mask enters P exactly as in the forward.
+ *   dmask  NULL, or (additive masks only) the bias gradient out: dS = P * (dP - Delta), the
+ *          gradient with respect to the scores, summed over the broadcast dimensions (those with
+ *          a 0 stride), written packed row-major in the shape [s0 ? batch : 1, s1 ? hq : 1,
+ *          s2 ? nq : 1, s3 ? nkv : 1] in q's dtype (fp32 sums, one rounding).
+ */
+int ffpa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, float* delta, void* dq, void* dk, void* dv,
+                    int batch, int hq, int hkv, int nq, int nkv, int d,
+                    const void* mask, int mask_kind, const int64_t* mask_strides, void* dmask,
+                    int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One stage of the dense backward, with exactly the arguments of ffpa_bwd plus `stage`:

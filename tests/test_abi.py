@@ -228,3 +228,20 @@ def test_strided_validation(lib):
     args = (P, P, P, P, P, 1, 2, 2, 1, 64, 512, arr(ok), 0, 0.04, 0)
     assert lib.ffpa_decode_fwd_strided(*args, N, 1 << 20, S) == 1             # NULL workspace
     assert lib.ffpa_decode_fwd_strided(P, P, P, P, P, 1, 2, 2, 1, 64, 512, None, 0, 0.04, 0, P, 1 << 20, S) == 1
+
+
+def test_mask_validation(lib):
+    arr = lambda *xs: (ctypes.c_int64 * 4)(*xs)
+    base = (P, P, P, P, P, 1, 2, 2, 64, 64, 512)
+    tail = (0, 0.04, 0, S)
+    good = arr(0, 64 * 64, 64, 1)
+    assert lib.ffpa_fwd_masked(*base, N, 1, good, *tail) == 1                 # NULL mask
+    assert lib.ffpa_fwd_masked(*base, P, 3, good, *tail) == 1                 # unknown kind
+    assert lib.ffpa_fwd_masked(*base, P, 1, None, *tail) == 1                 # NULL strides
+    assert lib.ffpa_fwd_masked(*base, P, 1, arr(0, 64 * 64, 64, 2), *tail) == 1   # key stride 2
+    assert lib.ffpa_fwd_masked(*base, P, 1, arr(0, 64 * 64, 60, 1), *tail) == 1  # row stride % 8
+    assert lib.ffpa_fwd_masked(*base, P, 1, arr(-8, 0, 64, 1), *tail) == 1       # negative
+    assert lib.ffpa_fwd_masked(*base, ctypes.c_void_p(0x1008), 1, good, *tail) == 1  # 8-byte aligned bias
+    bw = (P,) * 10 + (1, 2, 2, 64, 64, 512)
+    assert lib.ffpa_bwd_masked(*bw, P, 1, good, N, 0, 0.04, 0, N, 0, S) == 1       # no workspace
+    assert lib.ffpa_bwd_masked(*bw, P, 2, good, P, 0, 0.04, 0, P, 1 << 30, S) == 1  # gradient of a bool mask
