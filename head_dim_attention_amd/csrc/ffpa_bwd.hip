@@ -1465,23 +1465,34 @@ static hipError_t launch_dq_ds_t(const AttnParams& p, hipStream_t st) {
 // Triple-buffered copies as in the dQ pass. P is masked to 0 for queries at or past Lq (padding or
 // the next row's values) and for pairs that are not legal (not written by the P/dS kernel).
 // ------------------------------------------------------------------------------------------------
-template <int NDB>
+// SQ = queries per step: 32 (triple-buffered) or 64 (double-buffered), i.e. block rows of 64 or
+// 128 bytes per key; whole 128-byte rows keep the stored blocks' HBM reads at full lines.
+#ifndef DV_SQ
+#define DV_SQ 64
+#endif
+template <int NDB, int SQ = DV_SQ>
 struct DvCfg {
   static constexpr int NW = 8;
   static constexpr int KB = 2;                 // 32-key MFMA blocks per wave
+  static constexpr int KB2 = SQ / 16;          // 16-query k-steps per step
   static constexpr int DW = NDB * 32;
   static constexpr int DWG = 4 * DW;
   static constexpr int BK = 2 * KB * 32;       // keys per workgroup
   static constexpr int RS = 1024;              // dO tile row stride (bytes)
-  static constexpr int OTILE = 32 * RS;
-  static constexpr int PROW = 32 * 2;          // P block row: one key, 32 queries x 2 bytes
+  static constexpr int OTILE = SQ * RS;
+  static constexpr int PROW = SQ * 2;          // P block row: one key, SQ queries x 2 bytes
+  static constexpr int PCH = PROW / 16;        // 16-byte chunks per P row
   static constexpr int PTILE = BK * PROW;
   static constexpr int STAGE = OTILE + PTILE;
-  static constexpr int NBUF = PROD_NBUF;
+  static constexpr int NBUF = SQ == 32 ? PROD_NBUF : 2;
   static constexpr int LDS = NBUF * STAGE;
   static constexpr int OCOPY = OTILE / 1024 / NW;
   static constexpr int PCOPY = PTILE / 1024 / NW;
-  static_assert(DWG <= 512 && PCOPY == 1 && PTILE == NW * 1024 && LDS <= 160 * 1024, "tile budget");
+  static_assert((SQ == 32 || SQ == 64) && DWG <= 512 && PCOPY * NW * 1024 == PTILE && LDS <= 160 * 1024,
+                "tile budget");
+  // XOR on the chunk index of P row r: 16 consecutive rows read by a half-wave at one logical
+  // chunk land on 16 distinct 16-byte bank groups.
+  static __device__ __forceinline__ int pswz(int r) { return PCH == 4 ? (r >> 2) & 3 : (r >> 1) & 7; }
 };
 
 template <class T, int NDB, bool DK>
@@ -1517,13 +1528,14 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
   const int dg = w & 3;
   const int off = sv.lk - sv.lq;
 
-  // Streamed steps: query tiles of each query head of the group.
+  // Streamed steps: SQ-query tiles of each query head of the group.
+  constexpr int SQ = C::KB2 * 16;
   const int qfirst = p.causal ? max(0, k0 - off) : 0;
-  const int qt_first = qfirst >> 5;
-  const int nqt = sv.lq > qfirst ? ((sv.lq + 31) >> 5) - qt_first : 0;
+  const int qt_first = qfirst / SQ;
+  const int nqt = sv.lq > qfirst ? (sv.lq + SQ - 1) / SQ - qt_first : 0;
   const int nsteps = p.group * nqt;
   auto step_head = [&](int st) { return kvh * p.group + st / nqt; };
-  auto step_row0 = [&](int st) { return (qt_first + st % nqt) * 32; };
+  auto step_row0 = [&](int st) { return (qt_first + st % nqt) * SQ; };
 
   f32x16_t acc[C::KB][NDB];
 #pragma unroll
@@ -1538,13 +1550,17 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
   int ovoff[C::OCOPY];
 #pragma unroll
   for (int ii = 0; ii < C::OCOPY; ++ii) ovoff[ii] = min((d0 >> 3) + (lane ^ swz(w + 8 * ii)), dch - 1) << 4;
-  // P rows (one per key): copy of wave w fills block rows 16 w .. 16 w + 15; lane l writes row
-  // 16 w + l / 4 (key k0 + row, clamped to the last key), physical chunk l % 4, holding logical
-  // chunk (l % 4) ^ ((row >> 2) & 3) (queries row0 + 8 * logical chunk). The whole byte offset is
-  // per lane (range-checked; the block is a multiple of 16 bytes).
-  const int prow_l = 16 * w + (lane >> 2);
-  const int pchunk = (lane & 3) ^ ((prow_l >> 2) & 3);
-  const int pkey = min(k0 + prow_l, sv.lk - 1);
+  // P rows (one per key): copy c of wave w fills 1 KB of the block, rows (PCOPY w + c) * 1024 /
+  // PROW + l / PCH for lane l (key k0 + row, clamped to the last key), physical chunk l % PCH,
+  // holding logical chunk (l % PCH) ^ pswz(row) (queries row0 + 8 * logical chunk). The whole
+  // byte offset is per lane (range-checked; the block is a multiple of 16 bytes).
+  int pkey[C::PCOPY], pchunk[C::PCOPY];
+#pragma unroll
+  for (int c = 0; c < C::PCOPY; ++c) {
+    const int r = (C::PCOPY * w + c) * (1024 / C::PROW) + lane / C::PCH;
+    pkey[c] = min(k0 + r, sv.lk - 1);
+    pchunk[c] = (lane % C::PCH) ^ C::pswz(r);
+  }
   const uint32_t pspan = (uint32_t)((long long)sv.lk * dsv.row * 2);
   struct StepSrc {
     i32x4_t ors, prs;
@@ -1565,11 +1581,13 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
       const int i = w + 8 * c;
       dma16_buf(x.ors, ovoff[c], min(x.row0 + i, sv.lq - 1) * orow_bytes, stage + i * 1024);
     } else {
-      dma16_buf(x.prs, (pkey * dsv.row + x.row0 + 8 * pchunk) * 2, 0, stage + C::OTILE + w * 1024);
+      const int pc = c - C::OCOPY;
+      dma16_buf(x.prs, (pkey[pc] * dsv.row + x.row0 + 8 * pchunk[pc]) * 2, 0,
+                stage + C::OTILE + (C::PCOPY * w + pc) * 1024);
     }
   };
   constexpr int NCOPY = C::OCOPY + C::PCOPY;
-  constexpr int NMMA = 2 * NDB * C::KB;
+  constexpr int NMMA = C::KB2 * NDB * C::KB;
   auto spread_at = [](int c) { return (c * NMMA) / NCOPY; };
 
   // ---- operand addresses. dO^T (A operand): transposed reads as K^T in the dQ pass.
@@ -1595,7 +1613,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
   // i.e. logical chunk 2 kb2 + h of the row.
   auto p_addr = [&](uint32_t tile, int kb, int kb2) -> uint32_t {
     const int r = 64 * kg + 32 * kb + l32;
-    return tile + C::OTILE + r * C::PROW + (((2 * kb2 + hh) ^ ((r >> 2) & 3)) << 4);
+    return tile + C::OTILE + r * C::PROW + (((2 * kb2 + hh) ^ C::pswz(r)) << 4);
   };
 
   constexpr int NB = C::NBUF;
@@ -1620,20 +1638,20 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
     const StepSrc xn = step_src(st + NB - 1);
     const int row0 = step_row0(st);
 
-    u32x4_t bp[C::KB][2];
+    u32x4_t bp[C::KB][C::KB2];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < C::KB2; ++kb2)
         bp[kb][kb2] = lds_read_b128_at(p_addr(tile, kb, kb2));
     const int kw0 = k0 + 64 * kg;
-    const bool need_mask = (row0 + 32 > sv.lq) || (kw0 + 64 > sv.lk) || (p.causal && kw0 + 63 > row0 + off);
+    const bool need_mask = (row0 + SQ > sv.lq) || (kw0 + 64 > sv.lk) || (p.causal && kw0 + 63 > row0 + off);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         const int kj = kw0 + 32 * kb + l32;
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < C::KB2; ++kb2)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int q = row0 + 16 * kb2 + 8 * hh + 2 * e;
@@ -1647,7 +1665,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
     }
     int mi = 0;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb2 = 0; kb2 < C::KB2; ++kb2) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const s16x4_t lo = lds_read_tr16_at(t_addr(tile, db, kb2, 0));
