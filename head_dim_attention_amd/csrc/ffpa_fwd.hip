@@ -646,17 +646,23 @@ hipError_t launch_fwd(const AttnParams& p, int fp16, hipStream_t st) {
 // group share each K/V tile -- and one range of key tiles; the key ranges of a row are
 // independent (partial O normalised by its own sum, plus its LSE) and a second pass merges them:
 //   LSE = log sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s,
-// which is exactly the softmax over the union of the ranges. The work is HBM-bound (each K/V
+// which is exactly the softmax over the union of the ranges (the merge: one workgroup per output
+// row and 256 columns, its four waves taking every fourth range). The work is HBM-bound (each K/V
 // byte is read once per row block): the split count fills the GPU with about two workgroups per
 // compute unit while keeping at least four tiles per range. Four waves split the head dim
 // (NC = 4); K and V tiles are double-buffered for D <= 512.
 // ------------------------------------------------------------------------------------------------
 template <class T>
 __global__ void __launch_bounds__(256) ffpa_decode_combine_kernel(AttnParams p, int nrows) {
-  // One wave per output row (b, h, i) = ((b * Hq + h) * Nq + i); lane l covers head-dim elements
-  // 4 (l + 64 k) .. + 3.
-  const int row = blockIdx.x * 4 + wave_id();
+  // Workgroup = (output row (b, h, i) = ((b * Hq + h) * Nq + i), 256-column chunk); lane l covers
+  // columns 256 chunk + 4 l .. + 3, and wave w the key ranges w, w + 4, ...; the four partial sums
+  // are added through LDS in a fixed order. Every wave forms the same max and weight sum.
+  __shared__ f32x4_t part[3][64];
+  const int nchunk = (p.d + 255) / 256;
+  const int row = blockIdx.x / nchunk;
+  const int chunk = blockIdx.x % nchunk;
   if (row >= nrows) return;
+  const int w = wave_id();
   const int lane = threadIdx.x & 63;
   const int i = row % p.nq;
   const int bh = row / p.nq;
@@ -666,29 +672,22 @@ __global__ void __launch_bounds__(256) ffpa_decode_combine_kernel(AttnParams p, 
   const float* po = p.part_o + (long long)row * p.nsplit * p.d;
   float m = -INFINITY;
   for (int sp = 0; sp < p.nsplit; ++sp) m = fmaxf(m, lp[sp]);
-  f32x4_t acc[4] = {};
   float l = 0.f;
-  if (m != -INFINITY) {
-    for (int sp = 0; sp < p.nsplit; ++sp) {
-      const float wgt = fast_exp2(lp[sp] - m);  // 0 for a range without a legal key
-      l += wgt;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int d = 4 * (lane + 64 * k);
-        if (d < p.d) acc[k] += wgt * *(const f32x4_t*)(po + (long long)sp * p.d + d);
-      }
-    }
-  }
+  if (m != -INFINITY)
+    for (int sp = 0; sp < p.nsplit; ++sp) l += fast_exp2(lp[sp] - m);  // 0 for a range without a legal key
+  const int d = 256 * chunk + 4 * lane;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (m != -INFINITY && d < p.d)
+    for (int sp = w; sp < p.nsplit; sp += 4) acc += fast_exp2(lp[sp] - m) * *(const f32x4_t*)(po + (long long)sp * p.d + d);
+  if (w > 0) part[w - 1][lane] = acc;
+  __syncthreads();
+  if (w != 0) return;
+  acc = ((acc + part[0][lane]) + part[1][lane]) + part[2][lane];
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   uint16_t* orow = (uint16_t*)p.o + (long long)b * p.o_batch + (long long)h * p.o_head + (long long)i * p.o_row;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int d = 4 * (lane + 64 * k);
-    if (d < p.d)
-      *(u32x2_t*)(orow + d) = (u32x2_t){Elt<T>::pack2(acc[k].x * inv, acc[k].y * inv),
-                                        Elt<T>::pack2(acc[k].z * inv, acc[k].w * inv)};
-  }
-  if (lane == 0)
+  if (d < p.d)
+    *(u32x2_t*)(orow + d) = (u32x2_t){Elt<T>::pack2(acc.x * inv, acc.y * inv), Elt<T>::pack2(acc.z * inv, acc.w * inv)};
+  if (lane == 0 && chunk == 0)
     p.lse[(long long)b * p.lse_batch + (long long)h * p.lse_head + i] = l > 0.f ? (m + fast_log2(l)) * kLn2 : -INFINITY;
 }
 
@@ -707,7 +706,7 @@ static hipError_t launch_decode_cfg(AttnParams p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nrows = p.batch * p.hq * p.nq;
-  hipLaunchKernelGGL(ffpa_decode_combine_kernel<T>, dim3((nrows + 3) / 4), dim3(256), 0, st, p, nrows);
+  hipLaunchKernelGGL(ffpa_decode_combine_kernel<T>, dim3(nrows * ((p.d + 255) / 256)), dim3(256), 0, st, p, nrows);
   return hipGetLastError();
 }
 
