@@ -46,6 +46,7 @@ import numpy as np
 __all__ = [
     "legal_mask", "softmax_rows", "group_forward", "group_backward", "mask_to_bias", "reduce_to_shape",
     "attn_fwd", "attn_bwd", "varlen_fwd", "varlen_bwd", "preprocess_delta", "fwd_rows",
+    "e4m3", "fp8_quantize", "attn_fwd_fp8",
 ]
 
 # Query rows per block when S is materialised: 2048 rows x 8192 keys x 8 B = 128 MiB per array.
@@ -332,3 +333,66 @@ def fwd_rows(q_head, k_head, v_head, rows, *, scale: float, causal: bool):
     s = scale * (qh[rows] @ kh.T)
     p, lse = softmax_rows(s, legal_mask(rows, nq, nkv, causal))
     return p @ vh, lse
+
+
+# ------------------------------------------------------------------------------------------------
+# FP8 forward ("Backends Overview", backend table and notes: FP8 attention quantizes fp16/bf16
+# Q, K, V inside the kernel; forward only). The guide's FP8 page is not among the pages, so the
+# scale granularity below is a reading: OCP e4m3, one scale per (batch, head) and tensor
+# (448 / amax, applied in fp32), P = exp(S - row max) quantized as e4m3(P * 448), and
+# O = (P8 V8) / l with l the unquantized row sum. The quantized tensors are exact (both sides take
+# the rounding decision on the same fp32 value); P8 is taken against the final row max here and
+# against a running max on the GPU, so O agrees to the e4m3 rounding of P only.
+# ------------------------------------------------------------------------------------------------
+def e4m3(x) -> np.ndarray:
+    """float64 values of fp32 inputs rounded to OCP e4m3 (float8_e4m3fn), nearest even, saturating
+    at 448 (PyTorch's cast)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).to(
+        torch.float64).numpy()
+
+
+def fp8_quantize(x: np.ndarray):
+    """Per-(batch, head) e4m3 quantization of x [B, H, N, D]: returns (x8 [B,H,N,D] float64 e4m3
+    values, amax [B,H] float64). x8 = e4m3(fp32(x) * fp32(448 / amax)) (0 for a zero head)."""
+    x = _f64(x)
+    amax = np.abs(x).max(axis=(2, 3))
+    f = np.where(amax > 0, np.float32(448.0) / amax.astype(np.float32), np.float32(0.0)).astype(np.float32)
+    x8 = e4m3(x.astype(np.float32) * f[:, :, None, None])
+    return x8, amax
+
+
+def attn_fwd_fp8(q, k, v, *, scale: float, causal: bool, parts: bool = False):
+    """FP8 forward as read above. Returns (O [B,Hq,Nq,D], LSE [B,Hq,Nq]) float64; with
+    ``parts`` also a dict of the unquantized P [B,Hq,Nq,Nkv] (against the final row max, 0 for
+    illegal keys), its row sums l [B,Hq,Nq] and the dequantized V8 [B,Hkv,Nkv,D] (V8 * amax / 448),
+    from which a caller can bound any other placement of the P rounding."""
+    q8, aq = fp8_quantize(q)
+    k8, ak = fp8_quantize(k)
+    v8, av = fp8_quantize(v)
+    b, hq, nq, d = q8.shape
+    hkv, nkv = k8.shape[1], k8.shape[2]
+    gsz = hq // hkv
+    o = np.zeros((b, hq, nq, d))
+    lse = np.full((b, hq, nq), -np.inf)
+    p_all = np.zeros((b, hq, nq, nkv)) if parts else None
+    l_all = np.zeros((b, hq, nq)) if parts else None
+    legal = legal_mask(np.arange(nq), nq, nkv, causal)
+    for bi in range(b):
+        for h in range(hq):
+            g = h // gsz
+            s = scale * (q8[bi, h] @ k8[bi, g].T) * (aq[bi, h] / 448.0) * (ak[bi, g] / 448.0)
+            s = np.where(legal, s, -np.inf)
+            has = legal.any(axis=1)
+            m = np.where(has, s.max(axis=1, initial=-np.inf), 0.0)
+            p = np.where(legal, np.exp(s - m[:, None]), 0.0)
+            l_ = p.sum(axis=1)
+            p8 = e4m3(p * 448.0)
+            safe = np.where(l_ > 0, l_, 1.0)
+            o[bi, h] = np.where((l_ > 0)[:, None], (p8 @ v8[bi, g]) * (av[bi, g] / 448.0 / 448.0) / safe[:, None], 0.0)
+            lse[bi, h] = np.where(l_ > 0, m + np.log(safe), -np.inf)
+            if parts:
+                p_all[bi, h], l_all[bi, h] = p, l_
+    if parts:
+        return o, lse, {"p": p_all, "l": l_all, "v": v8 * (av / 448.0)[:, :, None, None]}
+    return o, lse

@@ -481,3 +481,82 @@ def test_bias_against_torch_sdpa(kind):
         np.testing.assert_allclose(a, t.grad.numpy(), atol=1e-12)
     if kind == "additive":
         np.testing.assert_allclose(g[3], tm.grad.numpy(), atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------------
+# P-n: the FP8 forward's emulation. e4m3 rounding is pinned to the format's definition (3 mantissa
+# bits, exponent bias 7, subnormals below 2^-6, nearest even, 448 the largest finite value).
+# ----------------------------------------------------------------------------------------------
+def _e4m3_by_definition(x: float) -> float:
+    if x == 0:
+        return 0.0
+    sgn = -1.0 if x < 0 else 1.0
+    a = abs(x)
+    e = max(math.floor(math.log2(a)), -6)      # subnormals share the exponent -6
+    q = 2.0 ** (e - 3)                          # spacing with 3 mantissa bits
+    n = a / q
+    r = math.floor(n)
+    frac = n - r
+    if frac > 0.5 or (frac == 0.5 and r % 2 == 1):
+        r += 1
+    return sgn * min(r * q, 448.0)
+
+
+def test_e4m3_matches_definition():
+    r = rng(31)
+    xs = np.concatenate([r.standard_normal(3000) * s for s in (1e-3, 0.1, 3.0, 100.0)]).astype(np.float32)
+    xs = np.concatenate([xs, np.float32([1.0625, 1.1875, 0.00146484375, 0.0009765625, 448.0, 463.9, -3.3, 0.0])])
+    got = ref.e4m3(xs)
+    want = np.array([_e4m3_by_definition(float(x)) for x in xs])
+    assert np.array_equal(got, want)
+
+
+def test_fp8_oracle_exact_when_representable():
+    """e4m3-representable inputs whose head amax is 448 quantize to themselves; with one key, P = 1
+    and P8 = 448, so the FP8 forward gives exactly V (and LSE = S)."""
+    r = rng(32)
+    grid = np.array([_e4m3_by_definition(x) for x in np.linspace(-448, 448, 301)])
+    q = r.choice(grid, size=(1, 2, 3, 32))
+    k = r.choice(grid, size=(1, 2, 1, 32))
+    v = r.choice(grid, size=(1, 2, 1, 32))
+    for t in (q, k, v):
+        t[..., 0, 0] = 448.0
+    q8, aq = ref.fp8_quantize(q)
+    assert np.array_equal(q8, q) and np.all(aq == 448.0)
+    o, lse = ref.attn_fwd_fp8(q, k, v, scale=1e-4, causal=False)
+    np.testing.assert_array_equal(o, np.broadcast_to(v, o.shape))
+    o_ex, lse_ex = ref.attn_fwd(q, k, v, scale=1e-4, causal=False)
+    np.testing.assert_allclose(lse, lse_ex, rtol=1e-14)
+
+
+def test_fp8_oracle_close_to_exact():
+    """The FP8 reading stays within e4m3's relative precision (2^-4) of exact attention."""
+    r = rng(33)
+    q = r.standard_normal((1, 2, 40, 64))
+    k = r.standard_normal((1, 1, 50, 64))
+    v = r.standard_normal((1, 1, 50, 64))
+    for causal in (False, True):
+        o8, l8 = ref.attn_fwd_fp8(q, k, v, scale=0.125, causal=causal)
+        o, l_ = ref.attn_fwd(q, k, v, scale=0.125, causal=causal)
+        assert np.linalg.norm(o8 - o) / np.linalg.norm(o) < 2.0 ** -4
+        fin = np.isfinite(l_)
+        assert np.max(np.abs(l8[fin] - l_[fin])) < 0.1
+
+
+def test_fp8_oracle_parts():
+    """The intermediates the FP8 oracle hands out: every row of P with a legal key peaks at exactly
+    1 (the final max) and sums to l, and V's dequantized values lie within e4m3's half-step of V
+    (2^-4 relative for normals, 2^-10 of the scale below 2^-6)."""
+    r = rng(34)
+    q = r.standard_normal((1, 2, 9, 64))
+    k = r.standard_normal((1, 1, 7, 64))
+    v = r.standard_normal((1, 1, 7, 64))
+    o8, lse8, parts = ref.attn_fwd_fp8(q, k, v, scale=0.125, causal=True, parts=True)
+    o8b, lse8b = ref.attn_fwd_fp8(q, k, v, scale=0.125, causal=True)
+    assert np.array_equal(o8, o8b) and np.array_equal(lse8, lse8b)
+    p, l_ = parts["p"], parts["l"]
+    has = np.isfinite(lse8)
+    assert np.all(p[~has] == 0) and np.allclose(p.max(axis=-1)[has], 1.0)
+    assert np.allclose(p.sum(axis=-1), l_)
+    step = 2.0 ** -10 * np.abs(v).max() / 448.0  # half the subnormal spacing, in V's units
+    assert np.all(np.abs(parts["v"] - v) <= np.maximum(2.0 ** -4 * np.abs(v), step) * (1 + 1e-6))
