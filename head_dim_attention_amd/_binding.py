@@ -21,7 +21,7 @@ __all__ = [
     "library_path", "load_library", "ffpa_status_string",
     "ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd",
     "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes", "ffpa_decode_fwd",
-    "ffpa_decode_workspace_bytes",
+    "ffpa_decode_workspace_bytes", "ffpa_fwd_fp8", "ffpa_fwd_fp8_workspace_bytes",
 ]
 
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -45,6 +45,7 @@ _SIGNATURES = {
     "ffpa_decode_fwd": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp],
     "ffpa_fwd_strided": [_vp] * 5 + [_i] * 6 + [_i64p, _i, _f, _i, _vp],
     "ffpa_fwd_masked": [_vp] * 5 + [_i] * 6 + [_vp, _i, _i64p, _i, _f, _i, _vp],
+    "ffpa_fwd_fp8": [_vp] * 5 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "ffpa_bwd_masked": [_vp] * 10 + [_i] * 6 + [_vp, _i, _i64p, _vp, _i, _f, _i, _vp, _sz, _vp],
     "ffpa_decode_fwd_strided": [_vp] * 5 + [_i] * 6 + [_i64p, _i, _f, _i, _vp, _sz, _vp],
     "ffpa_bwd": [_vp] * 10 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
@@ -56,6 +57,7 @@ _SIZE_FUNCTIONS = {
     "ffpa_bwd_workspace_bytes": [_i] * 4,
     "ffpa_varlen_bwd_workspace_bytes": [_i] * 5,
     "ffpa_decode_workspace_bytes": [_i] * 6,
+    "ffpa_fwd_fp8_workspace_bytes": [_i] * 6,
 }
 
 
@@ -273,6 +275,53 @@ def ffpa_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: b
                                        nws, _stream(q))
     _raise_for(st, "ffpa_decode_fwd")
     return o, lse
+
+
+def ffpa_fwd_fp8_workspace_bytes(batch: int, hq: int, hkv: int, nq: int, nkv: int, d: int) -> int:
+    """Bytes of the FP8 forward's workspace (per-head amax, K8, transposed V8); 0: not available."""
+    return int(load_library().ffpa_fwd_fp8_workspace_bytes(int(batch), int(hq), int(hkv), int(nq), int(nkv), int(d)))
+
+
+def ffpa_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                 scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+    """FP8 forward (D <= 512): fp16/bf16 q [B,Hq,Nq,D], k/v [B,Hkv,Nkv,D] quantized to e4m3 inside
+    the library with one scale per head and tensor -> (o, lse) as ffpa_fwd. ``workspace`` (a byte
+    tensor of at least ffpa_fwd_fp8_workspace_bytes()) keeps the quantized K8, V8^T and amax
+    values for inspection; by default a temporary one is allocated."""
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    _same(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,Hq,Nq,D] and k, v [B,Hkv,Nkv,D]")
+    b, hq, nq, d = q.shape
+    _, hkv, nkv, dk = k.shape
+    if k.shape[0] != b or dk != d:
+        raise ValueError("batch and head dim of q, k, v must match")
+    o = torch.empty_like(q)
+    lse = torch.empty((b, hq, nq), dtype=torch.float32, device=q.device)
+    need = ffpa_fwd_fp8_workspace_bytes(b, hq, hkv, nq, nkv, d)
+    if workspace is None:
+        workspace, nws = _workspace(need, q)
+    else:
+        workspace = _dev(workspace, "workspace")
+        nws = workspace.numel() * workspace.element_size()
+    st = load_library().ffpa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv, d,
+                                     _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(workspace), nws,
+                                     _stream(q))
+    _raise_for(st, "ffpa_fwd_fp8")
+    return o, lse
+
+
+def fp8_workspace_views(ws: torch.Tensor, b: int, hq: int, hkv: int, nkv: int, d: int):
+    """(amax_q [B,Hq], amax_k [B,Hkv], amax_v [B,Hkv], K8 [B,Hkv,Nkv,D] uint8, V8T [B,Hkv,D,np] uint8)
+    views of a filled FP8 workspace (the layout documented with ffpa_fwd_fp8 in include/ffpa.h)."""
+    al = lambda x: (x + 255) // 256 * 256
+    np_ = (nkv + 63) // 64 * 64
+    k8_off = al((b * hq + 2 * b * hkv) * 4)
+    v8_off = k8_off + al(b * hkv * nkv * d)
+    am = ws[: (b * hq + 2 * b * hkv) * 4].view(torch.float32)
+    return (am[: b * hq].view(b, hq), am[b * hq: b * hq + b * hkv].view(b, hkv), am[b * hq + b * hkv:].view(b, hkv),
+            ws[k8_off: k8_off + b * hkv * nkv * d].view(b, hkv, nkv, d),
+            ws[v8_off: v8_off + b * hkv * d * np_].view(b, hkv, d, np_))
 
 
 def ffpa_bwd_workspace_bytes(batch: int, hq: int, nq: int, nkv: int) -> int:

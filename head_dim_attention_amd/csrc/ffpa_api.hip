@@ -11,6 +11,8 @@
 namespace ffpa {
 hipError_t launch_fwd(const AttnParams& p, int fp16, hipStream_t st);
 hipError_t launch_decode(const AttnParams& p, int fp16, hipStream_t st);
+hipError_t launch_fwd_fp8(const AttnParams& p, int fp16, void* ws, hipStream_t st);
+size_t fp8_workspace_bytes(int batch, int hq, int hkv, int nkv, int d);
 hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total, hipStream_t st, int stage);
 }  // namespace ffpa
 
@@ -259,6 +261,33 @@ int ffpa_fwd_masked(const void* q, const void* k, const void* v, void* o, float*
   p.o = o;
   p.lse = lse;
   return to_status(ffpa::launch_fwd(p, dtype == FFPA_DTYPE_FP16, (hipStream_t)stream));
+}
+
+size_t ffpa_fwd_fp8_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, int d) {
+  if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || nq < 1 || nkv < 1 || d < 320 || d > 512 || d % 32 != 0)
+    return 0;
+  return ffpa::fp8_workspace_bytes(batch, hq, hkv, nkv, d);
+}
+
+int ffpa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                 int nq, int nkv, int d, int dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return FFPA_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
+  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  if (st != FFPA_OK) return st;
+  if (d > 512) return FFPA_ERR_NOT_SUPPORTED;
+  if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
+  // The fp8 copies of one head (K8 rows, V8^T rows of nkv rounded up to 64) use 32-bit offsets.
+  if ((long long)(nkv + 63) / 64 * 64 * d > (1LL << 31) - 1) return FFPA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < ffpa::fp8_workspace_bytes(batch, hq, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
+  AttnParams p = dense_params(batch, hq, hkv, nq, nkv, d, scale, causal);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  return to_status(ffpa::launch_fwd_fp8(p, dtype == FFPA_DTYPE_FP16, workspace, (hipStream_t)stream));
 }
 
 int ffpa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,

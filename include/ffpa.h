@@ -112,6 +112,28 @@ int ffpa_fwd_masked(const void* q, const void* k, const void* v, void* o, float*
                     int dtype, float scale, int causal, void* stream);
 
 /*
+ * FP8 dense forward ("Backends Overview", backend table and notes: FP8 attention takes fp16/bf16
+ * activations and quantizes Q, K and V inside the kernel; forward only). Arguments as ffpa_fwd
+ * plus a caller-owned device workspace of at least ffpa_fwd_fp8_workspace_bytes() bytes. D <= 512
+ * (else FFPA_ERR_NOT_SUPPORTED). The guide's FP8 page is not available; the semantics implemented:
+ *   - OCP e4m3 (max 448) for Q, K, V and P, rounded to nearest even from fp32;
+ *   - one scale per (batch, head) and tensor: x8 = e4m3(x * (448 / amax)), amax = max |x| over the
+ *     head (a zero head stays zero);
+ *   - S = scale * (Q8 K8^T) * amax_q * amax_k / 448^2; P = exp(S - running row max) in [0, 1],
+ *     P8 = e4m3(P * 448); O = (P8 V8) * amax_v / 448^2 / l with l = sum P (fp32), LSE = ln-sum-exp
+ *     of S as in ffpa_fwd; causal, GQA and empty rows as in ffpa_fwd.
+ * Workspace layout (each part 256-byte aligned): fp32 amax of Q [batch, hq], K [batch, hkv],
+ * V [batch, hkv]; K8 [batch, hkv, nkv, d] bytes; V8 transposed [batch, hkv, d, np] bytes with np =
+ * nkv rounded up to 64 (zero padding). It is left filled after the call.
+ */
+int ffpa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int batch, int hq, int hkv, int nq, int nkv, int d,
+                 int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the ffpa_fwd_fp8 workspace; 0 for invalid sizes or d outside 320..512. Host function. */
+size_t ffpa_fwd_fp8_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, int d);
+
+/*
  * Strided (zero-copy) dense forward ("Backends Overview", backend table notes: NHD zero-copy
  * consumes [B, N, H, D] or fused-QKV chunk views without a packed copy, an inference-path
  * feature). Same as ffpa_fwd, but q, k, v and o are addressed through strides instead of the
