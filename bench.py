@@ -10,6 +10,10 @@ runs with the library's P/dS workspace (one kernel forms and stores P and dS; dK
 dV = P^T dO and dQ = dS K are products of them); --no-ds-workspace times the recomputing dK, dV
 and dQ kernels instead (the P/dS launch is then empty).
 
+Two side legs follow the step, each reported in its own object of the JSON line: the split-KV
+decode pass on a decode workload ("decode", HBM-bound) and the FP8 forward on the step's inputs
+("fp8_fwd", quantizing pre-pass included, against the fp8 MFMA peak).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line (rank 0).
 """
@@ -32,6 +36,8 @@ METRIC = "attention TFLOPS (fwd, fwd+bwd) at D=512 N=8192 bf16; % of MFMA peak"
 # 256 CUs x 2.4 GHz x 4096 dense bf16/fp16 flop per clock per CU.
 PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
+# Dense fp8 (e4m3) MFMA: twice the bf16 rate.
+FP8_PEAK_TFLOPS = 5033.2
 # Algorithmic flops per legal pair and query head, by kernel (D multiplies these). Recomputing, dV
 # does 4 D (S, P^T dO), dK and dQ 6 D (S, dP, one product); with the stored P and dS the P/dS
 # kernel does 4 D (S, dP) and dK, dV, dQ are one product each, 2 D.
@@ -76,6 +82,7 @@ def parse_args(argv=None):
                     help="backward without the P/dS workspace (dV and dQ recompute)")
     ap.add_argument("--decode-workload", default="decode_gqa_d512_k65536",
                     help="workload of the split-KV decode leg ('none' skips it)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward leg")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration under rocprofv3)")
     return ap.parse_args(argv)
@@ -142,6 +149,47 @@ def decode_leg(F, W, w, seed: int, steps: int, warmup: int) -> dict:
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic("decode"),
                          "algorithmic_bytes": alg_bytes, "kv_bytes": kv_bytes}}
+
+
+def fp8_leg(F, qd, kd, vd, causal: bool, pairs: int, steps: int, warmup: int) -> dict:
+    """Time ffpa_fwd_fp8 (the quantizing pre-pass and the FP8 MFMA forward, one call) on the
+    measured workload's Q, K, V, inputs resident in HBM; flops as the forward's, against the dense
+    fp8 MFMA peak."""
+    import torch
+    b, hq, nq, d = qd.shape
+    hkv, nkv = kd.shape[1], kd.shape[2]
+    o = torch.empty_like(qd)
+    lse = torch.empty((b, hq, nq), dtype=torch.float32, device=qd.device)
+    nws = F.ffpa_fwd_fp8_workspace_bytes(b, hq, hkv, nq, nkv, d)
+    if nws == 0:
+        return {"skipped": f"no FP8 forward at D={d}"}
+    ws = torch.empty(nws, dtype=torch.uint8, device=qd.device)
+    lib = F.load_library()
+    stream = torch.cuda.current_stream(qd.device)
+    P = F._binding._ptr
+    dt = 0 if qd.dtype == torch.bfloat16 else 1
+
+    def run():
+        st = lib.ffpa_fwd_fp8(P(qd), P(kd), P(vd), P(o), P(lse), b, hq, hkv, nq, nkv, d, dt, 1.0 / math.sqrt(d),
+                              int(causal), P(ws), nws, stream.cuda_stream)
+        if st:
+            raise RuntimeError(F.ffpa_status_string(st))
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        run()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps
+    tf = 4.0 * d * pairs / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "includes": "amax and quantization pre-pass + FP8 forward kernel",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / FP8_PEAK_TFLOPS, 4)},
+            "vs_bf16_fwd": None}
 
 
 def cpu_baseline(q, k, v, do, scale, causal, dq, dk, dv, o, lse, tol_o, budget_s=10.0):
@@ -326,6 +374,13 @@ def main(argv=None) -> int:
     if args.decode_workload != "none":
         print(f"bench: timing the split-KV decode pass on {args.decode_workload}", file=sys.stderr, flush=True)
         out["decode"] = decode_leg(F, W, W.get(args.decode_workload), args.seed, max(args.steps, 10), args.warmup)
+
+    if not args.no_fp8:
+        print("bench: timing the FP8 forward on the same inputs", file=sys.stderr, flush=True)
+        f8 = fp8_leg(F, qd, kd, vd, causal, pairs, max(args.steps, 10), args.warmup)
+        if "ms" in f8:
+            f8["vs_bf16_fwd"] = round(stage_ms["fwd"] / f8["ms"], 3)
+        out["fp8_fwd"] = f8
 
     if args.calib_copy_mib > 0:
         nbytes = args.calib_copy_mib << 20
