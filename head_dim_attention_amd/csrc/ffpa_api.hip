@@ -276,7 +276,8 @@ int ffpa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
   if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
   const int st = check_common(hq, hkv, d, dtype, scale, causal);
   if (st != FFPA_OK) return st;
-  if (d > 512) return FFPA_ERR_NOT_SUPPORTED;
+  // (the quantizing passes put batch x heads in one grid dimension)
+  if (d > 512 || (long long)batch * hq > 65535) return FFPA_ERR_NOT_SUPPORTED;
   if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
   // The fp8 copies of one head (K8 rows, V8^T rows of nkv rounded up to 64) use 32-bit offsets.
   if ((long long)(nkv + 63) / 64 * 64 * d > (1LL << 31) - 1) return FFPA_ERR_INVALID_ARGUMENT;

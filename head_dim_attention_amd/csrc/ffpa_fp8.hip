@@ -21,7 +21,8 @@
 // queries' Q8 for the whole head dim in registers (64 VGPRs at D = 512) and forms S for one
 // 32-key half of the tile with no partial-sum exchange; the pair shares the tile max (one float
 // per query through LDS) and its P8 halves (1 KB per wave), and each wave then multiplies P V for
-// its half of the head dim.
+// its half of the head dim. Waves 0-3 and 4-7 run one slot apart (one multiplies while the other
+// does the softmax), as in the bf16/fp16 forward.
 #include "ffpa_device.h"
 #include "ffpa_params.h"
 
@@ -43,31 +44,39 @@ __global__ void __launch_bounds__(256) ffpa_fp8_amax_init_kernel(float* amax, in
   if (i < n) amax[i] = 0.f;
 }
 
-// amax[head] = max |x| over the head's rows: grid (heads, row blocks of 64 rows); 8 bf16/fp16
-// values per thread and step.
+// amax[head] = max |x| over a head's n * d values: grid (chunks of 256K values, heads); each thread
+// keeps four 16-byte loads in flight, then one atomic max per workgroup (the fp32 bits of
+// non-negative values order like the values).
+constexpr int kAmaxChunk = 1 << 18;
 template <class T>
-__global__ void __launch_bounds__(256) ffpa_fp8_amax_kernel(const uint16_t* x, long long head_elems, int rows,
-                                                            int d, float* amax) {
-  const int head = blockIdx.x;
-  const int r0 = blockIdx.y * 64;
+__global__ void __launch_bounds__(256) ffpa_fp8_amax_kernel(const uint16_t* x, long long head_elems, float* amax) {
+  __shared__ float wmax[4];
+  const int head = blockIdx.y;
+  const long long beg = (long long)blockIdx.x * kAmaxChunk;
+  const long long end = min(beg + kAmaxChunk, head_elems);
   const uint16_t* base = x + (long long)head * head_elems;
-  const int per_row = d >> 3;
   float m = 0.f;
-  for (int idx = threadIdx.x; idx < 64 * per_row; idx += 256) {
-    const int r = r0 + idx / per_row;
-    if (r < rows) {
-      const u32x4_t v = *(const u32x4_t*)(base + (long long)r * d + 8 * (idx % per_row));
+  for (long long i = beg + 8 * threadIdx.x; i < end; i += 4 * 8 * 256) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const long long iu = i + (long long)u * 8 * 256;
+      v[u] = iu < end ? *(const u32x4_t*)(base + iu) : (u32x4_t){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float lo, hi;
-        Elt<T>::unpack2(v[e], lo, hi);
+        Elt<T>::unpack2(v[u][e], lo, hi);
         m = fmaxf(m, fmaxf(fabsf(lo), fabsf(hi)));
       }
-    }
   }
-  // wave max, then one atomic per wave (the fp32 bits of non-negative values order like them)
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)(amax + head), __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax((unsigned int*)(amax + head), __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
 }
 
 __device__ __forceinline__ float quant_factor(float amax) { return amax > 0.f ? 448.0f / amax : 0.f; }
@@ -150,15 +159,40 @@ struct Fp8Cfg {
   static constexpr int KT = 64;                // keys per tile
   static constexpr int KROW = 512;             // K8 tile row stride in LDS (bytes)
   static constexpr int KTILE = KT * KROW;      // 32 KB
-  static constexpr int VROWS = (DPAD + 127) / 128 * 128;  // V8^T tile rows (copies of 16 rows x 8 waves)
+  static constexpr int VROWS = DPAD;           // V8^T tile rows (copies of 16 rows x 4 waves)
   static constexpr int VTILE = VROWS * KT;     // V8^T tile: VROWS rows x 64 keys
   static constexpr int P8_OFF = 2 * KTILE + 2 * VTILE;
   static constexpr int XM_OFF = P8_OFF + NW * 1024;  // per wave: 32 queries x 32 keys of P8
   static constexpr int LDS = XM_OFF + NW * 32 * 4;   // per wave: tile max, then l, per query
-  static constexpr int KCOPY = KTILE / 1024 / NW;
-  static constexpr int VCOPY = VTILE / 1024 / NW;
-  static_assert(DPAD <= 512 && LDS <= 160 * 1024 && VTILE % (1024 * NW) == 0, "LDS budget");
+  static constexpr int KCOPY4 = KTILE / 1024 / 4;  // 1 KB copies per wave of the copying group
+  static constexpr int VCOPY4 = VTILE / 1024 / 4;
+  static_assert(DPAD <= 512 && LDS <= 160 * 1024 && VTILE % 4096 == 0, "LDS budget");
 };
+
+// Scheduling pin for N MFMAs with R LDS reads each, after PRE other LDS reads: the PRE reads and
+// those of the first AHEAD MFMAs, then one MFMA and the reads of a later one alternately, then the
+// last AHEAD MFMAs (mask bits: 0x008 MFMA, 0x100 LDS read).
+template <int N, int AHEAD, int R, int PRE>
+__device__ __forceinline__ void pin_fp8_pipeline() {
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE + AHEAD * R, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
+// LDS operand reads issued ahead of their MFMA in the product runs.
+constexpr int FP8_AHEAD = 2;
+
+// Opaque register uses and definitions (empty asm): a value is materialised here, or is not known
+// to the compiler past this point (so nothing derived from it is hoisted out of the loop).
+__device__ __forceinline__ void keep_here(const f32x16_t& x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ int opaque_v(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 __device__ __forceinline__ f32x16_t mma_fp8(i32x8_t a, i32x8_t b, f32x16_t c) {
   // unit block scales (E8M0 127 = 2^0); A and B in OCP e4m3 (format 0)
@@ -232,37 +266,33 @@ __global__ void __launch_bounds__(512, 2) ffpa_fwd_fp8_kernel(AttnParams p, cons
     }
   }
 
-  // ---- copies of tile j: K8 rows (64 x D bytes into 512-byte LDS rows; 16-byte chunk c of row r
-  // at physical chunk c ^ (r & 15), chunks past the head dim clamped) and V8^T rows (DPAD x 64
-  // bytes; chunk c of row r at c ^ ((r >> 2) & 3), rows past the head dim clamped).
+  // ---- copies. K8 tile: 64 rows x D bytes into 512-byte LDS rows, 16-byte chunk c of row r at
+  // physical chunk c ^ (r & 15) (chunks past the head dim clamped); one 1 KB copy = two rows.
+  // V8^T tile: VROWS rows x 64 keys, chunk c of row r at c ^ ((r >> 2) & 3) (rows past the head
+  // dim clamped); one copy = 16 rows. Each copy is split over the four waves of one group.
+  const int grp = w >> 2, wg = w & 3;
   const int dch = p.d >> 4;
   const long long k8_head = (long long)hk_flat * p.nkv * p.d;
   const long long v8_head = (long long)hk_flat * p.d * np;
   const i32x4_t krs = make_rsrc(k8 + k8_head, (uint32_t)min((long long)p.nkv * p.d, (long long)0xFFFFFFF0));
   const i32x4_t vrs = make_rsrc(v8t + v8_head, (uint32_t)min((long long)p.d * np, (long long)0xFFFFFFF0));
-  int kvoff[C::KCOPY], vvoff[C::VCOPY], vrow[C::VCOPY];
-#pragma unroll
-  for (int c = 0; c < C::KCOPY; ++c) {
-    const int r = 2 * (w + C::NW * c) + hh;  // 2 rows per 1 KB copy
-    kvoff[c] = min(l32 ^ (r & 15), dch - 1) << 4;
-  }
-#pragma unroll
-  for (int c = 0; c < C::VCOPY; ++c) {
-    const int r = 16 * (w + C::NW * c) + (lane >> 2);  // 16 rows per copy
-    vrow[c] = min(r, p.d - 1);
-    vvoff[c] = vrow[c] * np + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
-  }
-  auto copy_tile = [&](int j, int b) {
-#pragma unroll
-    for (int c = 0; c < C::KCOPY; ++c) {
-      const int r = 2 * (w + C::NW * c);
-      const int key = min(j * C::KT + r + hh, p.nkv - 1);
-      // the row offset is per lane here (two rows per instruction): fold it into voffset
-      dma16_buf(krs, key * p.d + kvoff[c], 0, kbuf(b) + r * C::KROW);
-    }
-#pragma unroll
-    for (int c = 0; c < C::VCOPY; ++c)
-      dma16_buf(vrs, vvoff[c] + j * C::KT, 0, vbuf(b) + (16 * (w + C::NW * c)) * C::KT);
+  // rows 2 (wg + 4 c) + h: the swizzle (row & 15) takes two values, for even and odd c
+  const int kch0 = min(l32 ^ (2 * wg + hh), dch - 1) << 4;
+  const int kch1 = min(l32 ^ (2 * wg + hh + 8), dch - 1) << 4;
+  // copy tile j into the buffer of tile jb
+  // (kb0/kb1 are laundered per slot by the caller, so the compiler does not keep one offset per
+  // copy live across the loop)
+  auto copy_k = [&](int j, int jb, int c, int kb0, int kb1) {
+    const int r0 = 2 * (wg + 4 * c);
+    const int key = min(j * C::KT + r0 + hh, p.nkv - 1);
+    dma16_buf(krs, key * p.d + ((c & 1) ? kb1 : kb0), 0, kbuf(jb & 1) + r0 * C::KROW);
+  };
+  // rows 16 (wg + 4 c) + lane / 4: the swizzle ((row >> 2) & 3) is (lane >> 4) & 3 for every c
+  const int vch = ((lane & 3) ^ ((lane >> 4) & 3)) << 4;
+  auto copy_v = [&](int j, int jb, int c, int vr, int vc) {
+    const int r0 = 16 * (wg + 4 * c);
+    const int row = min(r0 + vr, p.d - 1);
+    dma16_buf(vrs, row * np + vc + j * C::KT, 0, vbuf(jb & 1) + r0 * C::KT);
   };
 
   // ---- operand addresses
@@ -270,59 +300,98 @@ __global__ void __launch_bounds__(512, 2) ffpa_fwd_fp8_kernel(AttnParams p, cons
   // 32 cg + c_row(r, h); lane reads 32 bytes = chunks 4 kb + 2 h, + 1 of its key row.
   // The row base is a multiple of 512, so the swizzled chunk is one per-lane base XOR a constant.
   const int krow = 32 * cg + row_perm(l32);
-  const uint32_t klane = krow * C::KROW + ((krow & 15) << 4);
-  auto k_addr = [&](uint32_t tile, int kb, int part) -> uint32_t {
-    return (tile + klane) ^ ((4 * kb + 2 * hh + part) << 4);
+  // (the lane half's chunk offset 2 h is folded into the lane base; the tile base is a multiple of
+  // 512, so adding it and XOR-ing the chunk commute, and the per-read XOR is an immediate)
+  const uint32_t klane = krow * C::KROW + (((krow & 15) ^ (2 * hh)) << 4);
+  auto k_addr = [&](uint32_t tile_lane, int kb, int part) -> uint32_t {
+    return tile_lane ^ ((4 * kb + part) << 4);
   };
   // V8^T (A of O^T += V^T P^T): row d = cg DW + 32 db + n, keys 32 h .. + 31 = chunks 2 h, + 1; the
   // swizzle depends on n only.
-  const uint32_t vlane = (cg * C::DW + l32) * C::KT;
+  // Per lane two byte offsets (part 0 and 1); the column block adds an immediate.
   const int vsw = (l32 >> 2) & 3;
-  auto v_addr = [&](uint32_t tile, int db, int part) -> uint32_t {
-    return tile + vlane + 32 * db * C::KT + (((2 * hh + part) ^ vsw) << 4);
-  };
+  const int vlane0 = (cg * C::DW + l32) * C::KT + (((2 * hh) ^ vsw) << 4);
+  const int vlane1 = (cg * C::DW + l32) * C::KT + (((2 * hh + 1) ^ vsw) << 4);
   // P8 of wave (rg, c): [query n][32 keys], 32-byte rows whose two chunks swap for n & 8.
   auto p8_off = [&](int wave, int n, int key) -> int {
     return wave * 1024 + n * 32 + ((((key >> 4) ^ ((n >> 3) & 1))) << 4) + (key & 15);
+  };
+  auto rd8 = [&](uint32_t a0, uint32_t a1) -> i32x8_t {
+    const u32x4_t x = lds_read_b128_at(a0), y = lds_read_b128_at(a1);
+    return (i32x8_t){(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
   };
 
   f32x16_t oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = (f32x16_t){};
-  float mref = -INFINITY, lsum = 0.f;
-
-  if (ntk > 0) copy_tile(0, 0);
-  wait_all();
+  f32x16_t sacc = (f32x16_t){};
+  float mref = -INFINITY, lsum = 0.f, mw = -INFINITY;
   const int qi = qw0 + l32;
-  for (int j = 0; j < ntk; ++j) {
-    wait_vmcnt<0>();
-    lds_barrier();  // tile j visible; every wave has finished tile j - 1
-    const uint32_t kt = lds_addr(kbuf(j & 1)), vt = lds_addr(vbuf(j & 1));
-    if (j + 1 < ntk) copy_tile(j + 1, (j + 1) & 1);
+  const int lim_row = p.causal ? min(qi + off, p.nkv - 1) : p.nkv - 1;
 
-    // S^T for this wave's 32 keys over the whole head dim
-    f32x16_t sacc = (f32x16_t){};
+  // Multiply slot of step j: S^T of tile j and O^T += V8^T P8^T of tile j - 1, alternating so that
+  // no two dependent MFMAs are adjacent; then (group 0) the copy of K of tile j + 1, and the scale,
+  // mask and tile max of this wave's 32 keys, written for the partner. At j = 0 the P8 slots and
+  // the second V buffer hold zeros, so the P V product adds exact zeros; at j = ntk the scores are
+  // formed (on a stale tile) but not used.
+  auto m_slot = [&](int j) {
+    // opaque per slot, so the per-read addresses are formed at their use instead of being kept
+    // live across the loop
+    const uint32_t kt = (uint32_t)opaque_v((int)(lds_addr(kbuf(j & 1)) + klane));
+    const lds_t* const vt0 = vbuf((j + 1) & 1) + opaque_v(vlane0);
+    const lds_t* const vt1 = vbuf((j + 1) & 1) + opaque_v(vlane1);
+    // P8^T B operand: lane (h, n) = query n, keys 32 h .. + 31 of tile j - 1, i.e. the P8 row of
+    // wave (rg, h); the V8^T A operand holds the same keys in the same byte order.
+    const uint32_t pb = lds_addr(p8buf) + p8_off(2 * rg + hh, l32, 0);
+    const i32x8_t bop = rd8(pb, pb ^ 16);
 #pragma unroll
-    for (int kb = 0; kb < C::KS; ++kb) {
-      const u32x4_t a0 = lds_read_b128_at(k_addr(kt, kb, 0));
-      const u32x4_t a1 = lds_read_b128_at(k_addr(kt, kb, 1));
-      const i32x8_t a = (i32x8_t){(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      sacc = mma_fp8(a, q8[kb], sacc);
+    for (int i = 0; i < NDB; ++i) {
+      const u32x4_t x = lds_read_b128(vt0, 32 * i * C::KT), y = lds_read_b128(vt1, 32 * i * C::KT);
+      const i32x8_t a = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      oacc[i] = mma_fp8(a, bop, oacc[i]);
     }
-    // log2-domain scores, masked; tile max of this wave's keys per query
-    const int key0 = j * C::KT + 32 * cg;
-    const int lim = p.causal ? min(qi + off, p.nkv - 1) : p.nkv - 1;
-    float mw = -INFINITY;
+    pin_fp8_pipeline<NDB, FP8_AHEAD, 2, 2>();
+    // opaque uses: the products stay in this slot (otherwise they are sunk towards their next use,
+    // past the barrier, where their operands occupy registers the softmax needs)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) keep_here(oacc[i]);
+    __builtin_amdgcn_sched_barrier(0);
+    sacc = (f32x16_t){};
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) sacc = mma_fp8(rd8(k_addr(kt, i, 0), k_addr(kt, i, 1)), q8[i], sacc);
+    pin_fp8_pipeline<NDB, FP8_AHEAD, 2, 0>();
+    keep_here(sacc);
+    if (grp == 0) {
+      const int jn = min(j + 1, ntk - 1);
+      const int kb0 = opaque_v(kch0), kb1 = opaque_v(kch1);
+#pragma unroll
+      for (int c = 0; c < C::KCOPY4; ++c) copy_k(jn, j + 1, c, kb0, kb1);
+    }
+    // key of register r: j KT + 32 cg + c_row(r, h), and c_row(r, h) = c_row(r, 0) + 8 h, so one
+    // per-lane bound against immediates
+    const int klim = lim_row - (j * C::KT + 32 * cg + 8 * hh);
+    mw = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float v = sacc[r] * sdq;
-      if (key0 + c_row(r, hh) > lim) v = -INFINITY;
+      if (c_row(r, 0) > klim) v = -INFINITY;
       sacc[r] = v;
       mw = fmaxf(mw, v);
     }
     mw = half_max(mw);
     if (hh == 0) *(__attribute__((address_space(3))) float*)(xmbuf + (w * 32 + l32) * 4) = mw;
-    lds_barrier();
+  };
+
+  // Softmax slot of step j: (group 1) the copy of V of tile j + 1; the pair's tile max, the exact
+  // running max (rescaling O and l when it grows), P = exp2(S - max) in [0, 1] and
+  // P8 = e4m3(448 P) for the partner.
+  auto e_slot = [&](int j) {
+    if (grp == 1) {
+      const int jn = min(j + 1, ntk - 1);
+      const int vr = opaque_v(lane >> 2), vc = opaque_v(vch);
+#pragma unroll
+      for (int c = 0; c < C::VCOPY4; ++c) copy_v(jn, j + 1, c, vr, vc);
+    }
     const float mpart = *(const __attribute__((address_space(3))) float*)(xmbuf + ((w ^ 1) * 32 + l32) * 4);
     // the pair's tile max: the same commutative max in both waves
     const float mt = cg == 0 ? fmaxf(mw, mpart) : fmaxf(mpart, mw);
@@ -334,7 +403,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_fwd_fp8_kernel(AttnParams p, cons
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
       mref = mnew;
     }
-    // P in [0, 1] against the running max (a row with no finite score yet keeps P = 0), P8
+    // a row with no finite score yet keeps P = 0
     const float mu = mref == -INFINITY ? 0.f : mref;
     // keys 8 h + 0..7 (registers 0..7) and 16 + 8 h + 0..7 (8..15) of this wave's 32 as bytes
 #pragma unroll
@@ -353,25 +422,61 @@ __global__ void __launch_bounds__(512, 2) ffpa_fwd_fp8_kernel(AttnParams p, cons
       *(__attribute__((address_space(3))) u32x2_t*)(p8buf + p8_off(w, l32, 16 * half + 8 * hh)) =
           (u32x2_t){wd[0], wd[1]};
     }
-    lds_barrier();
-    // P8^T B operand: lane (h, n) = query n, keys 32 h .. + 31 of the tile, i.e. the P8 row of wave
-    // (rg, h); the V8^T A operand holds the same keys in the same byte order.
-    const int pw = 2 * rg + hh;
-    const u32x4_t b0 = lds_read_b128(p8buf, p8_off(pw, l32, 0));
-    const u32x4_t b1 = lds_read_b128(p8buf, p8_off(pw, l32, 16));
-    const i32x8_t bop = (i32x8_t){(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  };
+
+  // Two-group schedule. Waves 0-3 (row groups 0, 1) and 4-7 (row groups 2, 3) run one slot apart,
+  // so in every slot one wave of each SIMD multiplies while the other does the softmax:
+  //   slot 2j:     group 0 multiplies (S_j, P_{j-1} V_{j-1}) | group 1 softmax of tile j - 1
+  //   slot 2j + 1: group 0 softmax of tile j                  | group 1 multiplies (S_j, P_{j-1} V_{j-1})
+  // for j = 0 .. ntk (group 1's slot 0 only copies). Buffers (two each): K_{j+1} replaces K_{j-1}
+  // (last read in slot 2j - 1) and is copied by group 0 in slot 2j; V_j replaces V_{j-2} (last read
+  // in slot 2j - 1) and is copied by group 1 in slot 2j. The copying waves complete their copies
+  // before the barrier that ends slot 2j + 1. Past the last tile the copies repeat tile ntk - 1
+  // into the free buffer, so every slot has the same shape. A wave's tile max and P8 are read by
+  // its partner (same group) in the next slot and rewritten two slots later.
+  if (ntk > 0) {
+    // zero P8 slots and the second V buffer (read by the first multiply slot), then K_0
+    {
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      for (int o = threadIdx.x * 16; o < C::VTILE; o += 512 * 16) lds_write_b128(vbuf(1), o, z);
+      lds_write_b128(p8buf, threadIdx.x * 16, z);
+    }
+    if (grp == 0) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const u32x4_t a0 = lds_read_b128_at(v_addr(vt, db, 0));
-      const u32x4_t a1 = lds_read_b128_at(v_addr(vt, db, 1));
-      const i32x8_t a = (i32x8_t){(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      oacc[db] = mma_fp8(a, bop, oacc[db]);
+      for (int c = 0; c < C::KCOPY4; ++c) copy_k(0, 0, c, kch0, kch1);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (grp == 1) {
+#pragma unroll
+      for (int c = 0; c < C::VCOPY4; ++c) copy_v(0, 0, c, lane >> 2, vch);
+      lds_barrier();
+    }
+    // (the scheduling barriers keep each slot's MFMAs on its side of the workgroup barrier)
+    for (int j = 0; j < ntk; ++j) {
+      m_slot(j);
+      if (grp == 1) wait_vmcnt<0>();  // V_j
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      e_slot(j);
+      if (grp == 0) wait_vmcnt<0>();  // K_{j+1}
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    m_slot(ntk);
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (grp == 0) {
+      wait_vmcnt<0>();
+      lds_barrier();
     }
   }
-  wait_vmcnt<0>();
 
-  // ---- epilogue: the pair's l (each wave summed its own keys), O = O^T * amax_v / 448^2 / l
-  lds_barrier();
+  // ---- epilogue: the pair's l (each wave summed its own keys), O = O^T * amax_v / 448^2 / l.
+  // Both groups have passed the same number of barriers; the partner read this wave's exchange
+  // slot (its last tile max) before the last one.
   const float lw = half_sum(lsum);
   if (hh == 0) *(__attribute__((address_space(3))) float*)(xmbuf + (w * 32 + l32) * 4) = lw;
   lds_barrier();
@@ -427,15 +532,15 @@ static hipError_t launch_fp8_cfg(AttnParams p, char* ws, hipStream_t st) {
   uint8_t* v8t = (uint8_t*)(ws + lay.v8t);
   const int nam = p.batch * (p.hq + 2 * p.hkv);
   hipLaunchKernelGGL(ffpa_fp8_amax_init_kernel, dim3((nam + 255) / 256), dim3(256), 0, st, amax_q, nam);
-  hipLaunchKernelGGL(ffpa_fp8_amax_kernel<T>, dim3(p.batch * p.hq, (p.nq + 63) / 64), dim3(256), 0, st,
-                     (const uint16_t*)p.q, (long long)p.nq * p.d, p.nq, p.d, amax_q);
-  hipLaunchKernelGGL(ffpa_fp8_amax_kernel<T>, dim3(p.batch * p.hkv, (p.nkv + 63) / 64), dim3(256), 0, st,
-                     (const uint16_t*)p.k, (long long)p.nkv * p.d, p.nkv, p.d, amax_k);
-  hipLaunchKernelGGL(ffpa_fp8_amax_kernel<T>, dim3(p.batch * p.hkv, (p.nkv + 63) / 64), dim3(256), 0, st,
-                     (const uint16_t*)p.v, (long long)p.nkv * p.d, p.nkv, p.d, amax_v);
-  const long long kelems = (long long)p.nkv * p.d;
-  hipLaunchKernelGGL(ffpa_fp8_quant_rows_kernel<T>, dim3((unsigned)((kelems / 16 + 255) / 256), p.batch * p.hkv),
-                     dim3(256), 0, st, (const uint16_t*)p.k, k8, amax_k, kelems, p.d);
+  const long long qelems = (long long)p.nq * p.d, kvelems = (long long)p.nkv * p.d;
+  hipLaunchKernelGGL(ffpa_fp8_amax_kernel<T>, dim3((unsigned)((qelems + kAmaxChunk - 1) / kAmaxChunk), p.batch * p.hq),
+                     dim3(256), 0, st, (const uint16_t*)p.q, qelems, amax_q);
+  hipLaunchKernelGGL(ffpa_fp8_amax_kernel<T>, dim3((unsigned)((kvelems + kAmaxChunk - 1) / kAmaxChunk), p.batch * p.hkv),
+                     dim3(256), 0, st, (const uint16_t*)p.k, kvelems, amax_k);
+  hipLaunchKernelGGL(ffpa_fp8_amax_kernel<T>, dim3((unsigned)((kvelems + kAmaxChunk - 1) / kAmaxChunk), p.batch * p.hkv),
+                     dim3(256), 0, st, (const uint16_t*)p.v, kvelems, amax_v);
+  hipLaunchKernelGGL(ffpa_fp8_quant_rows_kernel<T>, dim3((unsigned)((kvelems / 16 + 255) / 256), p.batch * p.hkv),
+                     dim3(256), 0, st, (const uint16_t*)p.k, k8, amax_k, kvelems, p.d);
   hipLaunchKernelGGL(ffpa_fp8_quant_vt_kernel<T>, dim3(lay.np / 64, (p.d + 63) / 64, p.batch * p.hkv), dim3(256), 0,
                      st, (const uint16_t*)p.v, v8t, amax_v, p.nkv, p.d, lay.np);
   p.ntiles = (p.nq + 127) / 128;

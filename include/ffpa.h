@@ -115,7 +115,8 @@ int ffpa_fwd_masked(const void* q, const void* k, const void* v, void* o, float*
  * FP8 dense forward ("Backends Overview", backend table and notes: FP8 attention takes fp16/bf16
  * activations and quantizes Q, K and V inside the kernel; forward only). Arguments as ffpa_fwd
  * plus a caller-owned device workspace of at least ffpa_fwd_fp8_workspace_bytes() bytes. D <= 512
- * (else FFPA_ERR_NOT_SUPPORTED). The guide's FP8 page is not available; the semantics implemented:
+ * and batch * hq <= 65535 (else FFPA_ERR_NOT_SUPPORTED); a workspace that is NULL or too small is
+ * FFPA_ERR_INVALID_ARGUMENT. The guide's FP8 page is not available; the semantics implemented:
  *   - OCP e4m3 (max 448) for Q, K, V and P, rounded to nearest even from fp32;
  *   - one scale per (batch, head) and tensor: x8 = e4m3(x * (448 / amax)), amax = max |x| over the
  *     head (a zero head stays zero);

@@ -37,6 +37,9 @@ CASES = [
     (1, 4, 1, 70, 333, 448, BF, False),
     (1, 2, 2, 1, 200, 512, FP, True),
     (1, 3, 3, 257, 200, 384, BF, True),
+    (1, 2, 1, 64, 40, 512, BF, False),     # one key tile
+    (1, 2, 2, 100, 30, 448, FP, True),     # causal Nq > Nkv: rows without a legal key
+    (1, 4, 2, 300, 1000, 512, BF, True),   # many tiles, ragged tails
 ]
 
 
