@@ -49,7 +49,7 @@ STAGES = ("fwd",) + tuple(n for n, _ in BWD_STAGES)
 COMPUTE_KERNELS = ("fwd", "pds", "dk", "dv", "dq")
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "traffic_dense_d512_n8192.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "head_dim_attention_amd", "csrc", f)
-                  for f in ("ffpa_device.h", "ffpa_params.h", "ffpa_fwd.hip", "ffpa_bwd.hip")]
+                  for f in ("ffpa_device.h", "ffpa_params.h", "ffpa_fwd.hip", "ffpa_bwd.hip", "ffpa_fp8.hip")]
 
 
 def kernel_source_hash() -> str:
@@ -188,7 +188,7 @@ def fp8_leg(F, qd, kd, vd, causal: bool, pairs: int, steps: int, warmup: int) ->
     tf = 4.0 * d * pairs / (ms * 1e-3) / 1e12
     return {"ms": round(ms, 4), "includes": "amax and quantization pre-pass + FP8 forward kernel",
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / FP8_PEAK_TFLOPS, 4)},
+                         "frac": round(tf / FP8_PEAK_TFLOPS, 4), "traffic": load_traffic("fp8_fwd")},
             "vs_bf16_fwd": None}
 
 
