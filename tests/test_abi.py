@@ -30,7 +30,8 @@ def test_header_declares_expected_entry_points():
     names = _declared()
     for n in ("ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd", "ffpa_status_string",
               "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes", "ffpa_decode_fwd",
-              "ffpa_decode_workspace_bytes"):
+              "ffpa_decode_workspace_bytes", "ffpa_decode_fwd_strided", "ffpa_fwd_strided", "ffpa_fwd_masked",
+              "ffpa_bwd_masked", "ffpa_fwd_fp8", "ffpa_fwd_fp8_workspace_bytes"):
         assert n in names
 
 
@@ -245,3 +246,33 @@ def test_mask_validation(lib):
     bw = (P,) * 10 + (1, 2, 2, 64, 64, 512)
     assert lib.ffpa_bwd_masked(*bw, P, 1, good, N, 0, 0.04, 0, N, 0, S) == 1       # no workspace
     assert lib.ffpa_bwd_masked(*bw, P, 2, good, P, 0, 0.04, 0, P, 1 << 30, S) == 1  # gradient of a bool mask
+
+
+def test_fp8_workspace_sizes(lib):
+    """ffpa_fwd_fp8_workspace_bytes: amax of Q, K, V (fp32), K8 (one byte per element) and V8^T with
+    the key count padded to 64, each part 256-byte aligned; 0 outside the supported sizes."""
+    lib.ffpa_fwd_fp8_workspace_bytes.restype = ctypes.c_size_t
+    al = lambda x: (x + 255) // 256 * 256
+    for b, hq, hkv, nkv, d in ((1, 32, 32, 8192, 512), (2, 4, 2, 150, 320), (1, 4, 1, 333, 448), (3, 6, 3, 1, 384)):
+        want = al(4 * (b * hq + 2 * b * hkv)) + al(b * hkv * nkv * d) + al(b * hkv * d * ((nkv + 63) // 64 * 64))
+        assert lib.ffpa_fwd_fp8_workspace_bytes(b, hq, hkv, 7, nkv, d) == want
+    for bad in ((1, 2, 2, 8, 8, 640), (1, 2, 2, 8, 8, 300), (1, 3, 2, 8, 8, 512), (0, 2, 2, 8, 8, 512),
+                (1, 2, 2, 0, 8, 512), (1, 2, 2, 8, 0, 512)):
+        assert lib.ffpa_fwd_fp8_workspace_bytes(*bad) == 0
+
+
+def test_fp8_validation(lib):
+    """Host checks of ffpa_fwd_fp8 (no launch happens for any of these)."""
+    def call(b=1, hq=2, hkv=2, nq=64, nkv=64, d=512, dtype=0, scale=0.04, causal=0, ptrs=None, ws=P, nws=1 << 30):
+        ptrs = ptrs or [P] * 5
+        return lib.ffpa_fwd_fp8(*ptrs, b, hq, hkv, nq, nkv, d, dtype, ctypes.c_float(scale), causal, ws, nws, S)
+    assert call(ws=N) == 1                                   # no workspace
+    assert call(nws=1024) == 1                               # workspace too small
+    assert call(d=640) == 2 and call(d=300) == 2             # head dims the FP8 path does not cover
+    assert call(b=2048, hq=64, hkv=64, nq=1, nkv=1) == 2     # batch x heads beyond one grid dimension
+    assert call(hq=3, hkv=2) == 1 and call(dtype=7) == 1 and call(scale=-1.0) == 1 and call(causal=2) == 1
+    assert call(nq=0) == 1 and call(nkv=0) == 1
+    for i in range(5):
+        ptrs = [P] * 5
+        ptrs[i] = N
+        assert call(ptrs=ptrs) == 1
