@@ -258,8 +258,8 @@ def main(argv=None) -> int:
 
     F.load_library()
     w = W.get(args.workload)
-    if w.varlen:
-        print("bench.py: choose a dense workload", file=sys.stderr)
+    if w.varlen or not w.backward:
+        print(f"bench.py: {w.name} is not a dense forward+backward workload; choose one that is", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -132,9 +132,9 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
   lds_t* smem = (lds_t*)smem_raw;
 
   const int L = blockIdx.x;
-  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
-  if (item >= p.total) return;
   const int heads = OWN_Q ? p.hq : p.hkv;
+  const int item = xcd_item(L, gridDim.x, p.cu_q != nullptr, heads, p.ntiles);
+  if (item >= p.total) return;
   int t = item % p.ntiles;
   const int hs = item / p.ntiles;
   const int hd = hs % heads;
@@ -553,9 +553,9 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
   lds_t* smem = (lds_t*)smem_raw;
 
   const int L = blockIdx.x;
-  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
-  if (item >= p.total) return;
   const int heads = OWN_Q ? p.hq : p.hkv;
+  const int item = xcd_item(L, gridDim.x, p.cu_q != nullptr, heads, p.ntiles);
+  if (item >= p.total) return;
   int t = item % p.ntiles;
   const int hs = item / p.ntiles;
   const int hd = hs % heads;
@@ -956,7 +956,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
   lds_t* const xbuf = smem + 4 * C::TILE;
 
   const int L = blockIdx.x;
-  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  const int item = xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hq, p.ntiles);
   if (item >= p.total) return;
   int t = item % p.ntiles;
   const int hs = item / p.ntiles;
@@ -1239,7 +1239,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_dq_from_ds_kernel(AttnParams p, i
   lds_t* smem = (lds_t*)smem_raw;
 
   const int L = blockIdx.x;
-  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  const int item = xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hq, nchunk * p.ntiles);
   if (item >= p.total) return;
   const int qt = item % p.ntiles;
   const int rest = item / p.ntiles;
@@ -1505,7 +1505,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
   lds_t* smem = (lds_t*)smem_raw;
 
   const int L = blockIdx.x;
-  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  const int item = xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hkv, nchunk * p.ntiles);
   if (item >= p.total) return;
   const int kt = item % p.ntiles;
   const int rest = item / p.ntiles;

@@ -242,6 +242,21 @@ __device__ __forceinline__ float half_sum(float x) { return x + other_half(x); }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Work item of workgroup L among items ordered (sequence, head, inner index), `inner` items per
+// head. Workgroup ids go round-robin over the 8 XCDs (L mod 8). Dense: XCD x takes the contiguous
+// eighth [x grid / 8, (x + 1) grid / 8) of the list -- whole heads, so a head's K/V tiles are
+// shared in one XCD's L2. Varlen sequences differ in length and contiguous eighths would hand
+// whole sequences to one XCD; there XCD x takes heads x, x + 8, ... of every sequence (each XCD
+// the same share of every sequence, a head's items still on one XCD) when the head count is a
+// multiple of 8, else the items round-robin. Needs grid = total rounded up to a multiple of 8.
+__device__ __forceinline__ int xcd_item(int L, int grid, bool varlen, int heads, int inner) {
+  if (!varlen) return (L & 7) * (grid >> 3) + (L >> 3);
+  if ((heads & 7) != 0) return L;
+  const int r = L >> 3, hpx = heads >> 3;
+  const int t = r % inner, q = r / inner;
+  return ((q / hpx) * heads + (L & 7) + 8 * (q % hpx)) * inner + t;
+}
+
 // Geometry of one (batch or sequence) slice, resolved from dense strides or cu_seqlens.
 struct SeqView {
   long long q_off, k_off, lse_off, v_off, o_off;

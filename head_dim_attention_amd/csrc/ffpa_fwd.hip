@@ -60,11 +60,11 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   auto kbuf = [&](int b) { return b ? (lds_t*)k1_raw : (lds_t*)k0_raw; };
   auto vbuf = [&](int b) { return b ? (lds_t*)v1_raw : (lds_t*)v0_raw; };
 
-  // Work item: XCD-aware decode. Consecutive workgroup ids go round-robin over the 8 XCDs, so
-  // item = (id % 8) * (grid / 8) + id / 8 gives each XCD a contiguous run of (head, tile) items
-  // and the tiles of one KV head share that XCD's L2.
+  // Work item: XCD-aware decode (xcd_item): each XCD runs whole heads, so the tiles of one KV head
+  // share that XCD's L2.
   const int L = blockIdx.x;
-  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  const int item = DEC ? xcd_item(L, gridDim.x, false, p.hkv, p.nsplit * p.nrb)
+                       : xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hq, p.ntiles);
   if (item >= p.total) return;
   int t, h, s, kvh, split = 0;
   if constexpr (DEC) {

@@ -176,6 +176,14 @@ def test_bench_refuses_multi_gpu():
     assert bench.main(["--gpus", "2"]) == 2
 
 
+def test_bench_refuses_workloads_it_cannot_step():
+    """A step is forward + backward on a dense batch: forward-only and varlen workloads are refused
+    before any device work."""
+    import bench
+    assert bench.main(["--workload", "fwd_d320_n512"]) == 2
+    assert bench.main(["--workload", "varlen_causal_d512"]) == 2
+
+
 def test_bench_legal_pair_count():
     import bench
     assert bench.legal_pairs(4, 4, False) == 16
