@@ -148,6 +148,9 @@ VARLEN_CASES = [
     ([0, 33, 130, 64], [5, 0, 64, 130], 4, 2, 320, FP, True),
     ([50, 7, 129], [80, 200, 3], 2, 1, 1024, BF, False),
     ([64, 64], [64, 64], 2, 2, 704, FP, True),
+    # head counts that are multiples of 8 take the per-XCD head interleave of the varlen grid
+    ([0, 45, 300, 129, 64], [10, 45, 280, 0, 64], 8, 2, 512, BF, True),
+    ([33, 150, 7], [33, 150, 7], 16, 8, 384, FP, False),
 ]
 
 
