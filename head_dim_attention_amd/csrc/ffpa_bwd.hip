@@ -22,6 +22,8 @@
 // accumulating product's A operand read transposed from the streamed tile (ds_read_b64_tr_b16).
 // For D <= 512, dV runs 8 waves (NC = 2) and dK/dQ run the 8-wave reduce-scatter variant below
 // (NC = 4), both at two waves per SIMD; larger head dims use 4 waves (NC = 4), one per SIMD.
+#include <algorithm>
+
 #include "ffpa_device.h"
 #include "ffpa_params.h"
 
@@ -955,11 +957,14 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
   auto vbuf = [&](int b) { return smem + (2 * b + 1) * C::TILE; };
   lds_t* const xbuf = smem + 4 * C::TILE;
 
+  // Work item (sequence, query head, query tile, key range): grids too small to fill the GPU
+  // split each tile's key tiles into p.nsplit ranges (P and dS of different keys are independent).
   const int L = blockIdx.x;
-  const int item = xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hq, p.ntiles);
+  const int item = xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hq, p.ntiles * p.nsplit);
   if (item >= p.total) return;
-  int t = item % p.ntiles;
-  const int hs = item / p.ntiles;
+  const int split = item % p.nsplit;
+  int t = (item / p.nsplit) % p.ntiles;
+  const int hs = item / p.nsplit / p.ntiles;
   const int h = hs % p.hq;
   const int s = hs / p.hq;
   if (p.causal) t = p.ntiles - 1 - t;  // heaviest causal tiles first
@@ -989,6 +994,10 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
   int kend = sv.lk;
   if (p.causal) kend = min(kend, qt0 + C::BQ + off);
   const int ntk = kend > 0 ? (kend + 31) >> 5 : 0;
+  // This item's key tiles [jb, je): an equal share of the query tile's own range.
+  const int per = (ntk + p.nsplit - 1) / p.nsplit;
+  const int jb = min(split * per, ntk), je = min(jb + per, ntk);
+  if (jb >= je && split > 0) return;
 
   // Q and dO columns of this wave as B operands: lane (h, n) holds query n, dims 16 kb + 8 h + 0..7.
   const int qi = qw0 + l32;
@@ -1120,24 +1129,24 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, dt), ds_rs, (int)boff, 0, DS_STORE_CPOL);
   };
 
-  if (ntk > 0) {
-    // Tile 0 by all waves (rows w + 8 ii of K and V).
+  if (je > jb) {
+    // Tile jb by all waves (rows w + 8 ii of K and V).
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int i = w + 8 * ii;
-      const int row = min(i, sv.lk - 1) * row_bytes;
+      const int row = min(jb * 32 + i, sv.lk - 1) * row_bytes;
       const int vo = min(lane ^ swz(i), dch - 1) << 4;
-      dma16_buf(krs, vo, row, kbuf(0) + i * 1024);
-      dma16_buf(vrs, vo, row, vbuf(0) + i * 1024);
+      dma16_buf(krs, vo, row, kbuf(jb & 1) + i * 1024);
+      dma16_buf(vrs, vo, row, vbuf(jb & 1) + i * 1024);
     }
   }
   wait_all();  // the stationary operands, LSE, Delta and tile 0
   lds_barrier();
 
-  if (ntk > 0) {
+  if (je > jb) {
     if (grp == 0) {
       // Only stores leave this group's waves inside the loop; they are not waited for.
-      for (int j = 0; j < ntk; ++j) {
+      for (int j = jb; j < je; ++j) {
         m_phase(j);
         lds_barrier();
         e_phase(j, [] {});
@@ -1147,15 +1156,15 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
     } else {
 #pragma unroll
       for (int ii = 0; ii < C::GCOPY; ++ii) {
-        gcopy(krs, kbuf(1), 1, ii);
-        gcopy(vrs, vbuf(1), 1, ii);
+        gcopy(krs, kbuf((jb + 1) & 1), jb + 1, ii);
+        gcopy(vrs, vbuf((jb + 1) & 1), jb + 1, ii);
       }
       lds_barrier();
-      for (int j = 0; j < ntk; ++j) {
+      for (int j = jb; j < je; ++j) {
         m_phase(j);
         // Tile j + 1 (copied in the prologue, or in the finishing phase of step j - 1, followed
         // there by that step's two stores, which may stay in flight).
-        if (j == 0) wait_vmcnt<0>(); else wait_vmcnt<2>();
+        if (j == jb) wait_vmcnt<0>(); else wait_vmcnt<2>();
         lds_barrier();
         e_phase(j, [&] {
 #pragma unroll
@@ -1176,7 +1185,12 @@ template <class T, int NDB>
 static hipError_t launch_pds(AttnParams p, hipStream_t st) {
   using C = PdsCfg<NDB>;
   p.ntiles = (p.nq + C::BQ - 1) / C::BQ;
-  p.total = p.batch * p.hq * p.ntiles;
+  // Fewer than two workgroups per compute unit (of 256): split the key tiles of each query tile
+  // into up to 8 ranges of at least 4 tiles, which also spreads the heavy tiles of a causal grid.
+  const long long base = (long long)p.batch * p.hq * p.ntiles;
+  const int ktiles = (p.nkv + 31) / 32;
+  p.nsplit = (int)std::max(1LL, std::min({8LL, (512 + base - 1) / std::max(base, 1LL), (long long)ktiles / 4}));
+  p.total = p.batch * p.hq * p.ntiles * p.nsplit;
   if (p.total == 0) return hipSuccess;
   const int grid = (p.total + 7) & ~7;
   if (p.mask_kind != 0)
