@@ -287,8 +287,17 @@ def main(argv=None) -> int:
     sp = stream.cuda_stream
     P = F._binding._ptr
 
+    # Grids too small to fill the GPU take the key-range split forward (its workspace allocated
+    # here, outside the timed region); the headline grid needs none.
+    fws_bytes = F.ffpa_fwd_split_workspace_bytes(b, hq, hkv, nq, nkv, d)
+    fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev) if fws_bytes > 0 else None
+
     def fwd():
-        st = lib.ffpa_fwd(P(qd), P(kd), P(vd), P(o), P(lse), b, hq, hkv, nq, nkv, d, dt, scale, int(causal), sp)
+        if fws is None:
+            st = lib.ffpa_fwd(P(qd), P(kd), P(vd), P(o), P(lse), b, hq, hkv, nq, nkv, d, dt, scale, int(causal), sp)
+        else:
+            st = lib.ffpa_fwd_split(P(qd), P(kd), P(vd), P(o), P(lse), b, hq, hkv, nq, nkv, d, dt, scale, int(causal),
+                                    P(fws), fws_bytes, sp)
         if st:
             raise RuntimeError(F.ffpa_status_string(st))
 

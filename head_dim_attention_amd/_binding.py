@@ -21,7 +21,7 @@ __all__ = [
     "library_path", "load_library", "ffpa_status_string",
     "ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd",
     "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes", "ffpa_decode_fwd",
-    "ffpa_decode_workspace_bytes", "ffpa_fwd_fp8", "ffpa_fwd_fp8_workspace_bytes",
+    "ffpa_decode_workspace_bytes", "ffpa_fwd_fp8", "ffpa_fwd_fp8_workspace_bytes", "ffpa_fwd_split_workspace_bytes",
 ]
 
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -46,6 +46,7 @@ _SIGNATURES = {
     "ffpa_fwd_strided": [_vp] * 5 + [_i] * 6 + [_i64p, _i, _f, _i, _vp],
     "ffpa_fwd_masked": [_vp] * 5 + [_i] * 6 + [_vp, _i, _i64p, _i, _f, _i, _vp],
     "ffpa_fwd_fp8": [_vp] * 5 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
+    "ffpa_fwd_split": [_vp] * 5 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "ffpa_bwd_masked": [_vp] * 10 + [_i] * 6 + [_vp, _i, _i64p, _vp, _i, _f, _i, _vp, _sz, _vp],
     "ffpa_decode_fwd_strided": [_vp] * 5 + [_i] * 6 + [_i64p, _i, _f, _i, _vp, _sz, _vp],
     "ffpa_bwd": [_vp] * 10 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
@@ -58,6 +59,7 @@ _SIZE_FUNCTIONS = {
     "ffpa_varlen_bwd_workspace_bytes": [_i] * 5,
     "ffpa_decode_workspace_bytes": [_i] * 6,
     "ffpa_fwd_fp8_workspace_bytes": [_i] * 6,
+    "ffpa_fwd_split_workspace_bytes": [_i] * 6,
 }
 
 
@@ -222,7 +224,7 @@ class _Mask:
 
 
 def ffpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
-             scale: Optional[float] = None, attn_mask: Optional[torch.Tensor] = None):
+             scale: Optional[float] = None, attn_mask: Optional[torch.Tensor] = None, split: Optional[bool] = None):
     """Dense forward. q [B,Hq,Nq,D], k/v [B,Hkv,Nkv,D] -> (o [B,Hq,Nq,D], lse fp32 [B,Hq,Nq]).
 
     Strided views (for example [B, N, H, D] tensors transposed to [B, H, N, D], or the q, k, v
@@ -230,7 +232,11 @@ def ffpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = F
     layout when q is a dense permutation of [B, H, N, D].
 
     attn_mask: None, a bool tensor (True keeps the key) or an additive bias in q's dtype,
-    broadcastable to [B, Hq, Nq, Nkv] (ffpa_fwd_masked; q, k, v then packed)."""
+    broadcastable to [B, Hq, Nq, Nkv] (ffpa_fwd_masked; q, k, v then packed).
+
+    split: packed inputs without a mask go through ffpa_fwd_split (key ranges merged by LSE, with a
+    temporary workspace) when the library reports that the grid is too small to fill the GPU
+    (None, the default) or never (False); the results agree up to fp32 summation order."""
     if attn_mask is not None:
         q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
     q, k, v, o, lse, (b, hq, hkv, nq, nkv, d) = _fwd_prep(q, k, v)
@@ -243,7 +249,12 @@ def ffpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = F
         return o, lse
     strides = _strides(q, k, v, o)
     L = load_library()
-    if strides is None:
+    need = L.ffpa_fwd_split_workspace_bytes(b, hq, hkv, nq, nkv, d) if strides is None and split is not False else 0
+    if need > 0:
+        ws, nws = _workspace(need, q)
+        st = L.ffpa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv, d,
+                              _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(ws), nws, _stream(q))
+    elif strides is None:
         st = L.ffpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv, d,
                         _dtype_code(q), _scale(scale, d), int(bool(causal)), _stream(q))
     else:
@@ -251,6 +262,11 @@ def ffpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = F
                                 _dtype_code(q), _scale(scale, d), int(bool(causal)), _stream(q))
     _raise_for(st, "ffpa_fwd")
     return o, lse
+
+
+def ffpa_fwd_split_workspace_bytes(batch: int, hq: int, hkv: int, nq: int, nkv: int, d: int) -> int:
+    """Bytes of the key-range split forward's workspace; 0 when the grid needs no split."""
+    return int(load_library().ffpa_fwd_split_workspace_bytes(int(batch), int(hq), int(hkv), int(nq), int(nkv), int(d)))
 
 
 def ffpa_decode_workspace_bytes(batch: int, hq: int, hkv: int, nq: int, nkv: int, d: int) -> int:

@@ -12,6 +12,8 @@ namespace ffpa {
 hipError_t launch_fwd(const AttnParams& p, int fp16, hipStream_t st);
 hipError_t launch_decode(const AttnParams& p, int fp16, hipStream_t st);
 hipError_t launch_fwd_fp8(const AttnParams& p, int fp16, void* ws, hipStream_t st);
+hipError_t launch_fwd_split(const AttnParams& p, int fp16, int nsplit, void* ws, hipStream_t st);
+int fwd_split_count(int batch, int hq, int nq, int nkv, int d);
 size_t fp8_workspace_bytes(int batch, int hq, int hkv, int nkv, int d);
 hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total, hipStream_t st, int stage);
 }  // namespace ffpa
@@ -242,6 +244,40 @@ static int dense_fwd(const void* q, const void* k, const void* v, void* o, float
 int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
              int nq, int nkv, int d, int dtype, float scale, int causal, void* stream) {
   return dense_fwd(q, k, v, o, lse, batch, hq, hkv, nq, nkv, d, nullptr, dtype, scale, causal, stream);
+}
+
+// Workspace of the key-range split forward: per row and range a normalised fp32 O and a log2 LSE;
+// 0 when the grid fills the GPU without a split (or the sizes are invalid).
+static size_t fwd_split_ws_bytes(int batch, int hq, int hkv, int nq, int nkv, int d) {
+  if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || nq < 1 || nkv < 1 || d < 320 || d > 1024 || d % 32 != 0)
+    return 0;
+  const int ns = ffpa::fwd_split_count(batch, hq, nq, nkv, d);
+  return ns > 1 ? (size_t)batch * hq * nq * ns * ((size_t)d + 1) * 4 : 0;
+}
+
+size_t ffpa_fwd_split_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, int d) {
+  return fwd_split_ws_bytes(batch, hq, hkv, nq, nkv, d);
+}
+
+int ffpa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                   int nq, int nkv, int d, int dtype, float scale, int causal, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  const size_t need = fwd_split_ws_bytes(batch, hq, hkv, nq, nkv, d);
+  if (need == 0) return dense_fwd(q, k, v, o, lse, batch, hq, hkv, nq, nkv, d, nullptr, dtype, scale, causal, stream);
+  if (!q || !k || !v || !o || !lse || !workspace) return FFPA_ERR_INVALID_ARGUMENT;
+  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  if (st != FFPA_OK) return st;
+  if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
+  if ((long long)batch * hq * nq > (1LL << 31) - 1) return FFPA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return FFPA_ERR_INVALID_ARGUMENT;
+  AttnParams p = dense_params(batch, hq, hkv, nq, nkv, d, scale, causal);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  return to_status(ffpa::launch_fwd_split(p, dtype == FFPA_DTYPE_FP16,
+                                          ffpa::fwd_split_count(batch, hq, nq, nkv, d), workspace, (hipStream_t)stream));
 }
 
 int ffpa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,

@@ -22,6 +22,8 @@
 //  * Softmax runs in the exp2 domain with a lazily updated reference max: O and l are rescaled
 //    only when a row max grows by more than 2^8, which leaves the result unchanged (the same
 //    reference is used for numerator and denominator) and removes the per-tile O rescale.
+#include <algorithm>
+
 #include "ffpa_device.h"
 #include "ffpa_params.h"
 
@@ -50,10 +52,15 @@ struct FwdCfg {
 // MASK adds an attn_mask to the scores ("Triton Backend", "Feature support": boolean or additive,
 // broadcast in any dimension): the combined scores of each tile get bias / scale, or -inf where a
 // boolean mask drops the key, before the row max; a row that ends with no finite score is empty.
-template <class T, int NC, int NDB, int QB, int NBUF, int NW, bool DEC = false, bool MASK = false>
+// SPL splits the key tiles of each query tile into p.nsplit ranges (work item = (sequence, head,
+// query tile, range)) and writes, per row and range, the normalised fp32 O and the log2-domain
+// LSE to part_o / part_lse as the decode form does; the same merge pass combines them. It serves
+// grids too small to fill the GPU (a causal grid's heavy tiles are split as well).
+template <class T, int NC, int NDB, int QB, int NBUF, int NW, bool DEC = false, bool MASK = false, bool SPL = false>
 __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p) {
   using C = FwdCfg<NC, NDB, QB, NBUF, NW>;
   static_assert(!DEC || (QB == 1 && NW == NC), "decode: one 32-row block per workgroup");
+  static_assert(!SPL || (QB == 1 && !DEC), "key-range split: one query block per wave, prefill form");
   __shared__ __attribute__((aligned(1024))) char k0_raw[C::TILE], v0_raw[C::TILE];
   __shared__ __attribute__((aligned(1024))) char k1_raw[NBUF == 2 ? C::TILE : 16], v1_raw[NBUF == 2 ? C::TILE : 16];
   __shared__ __attribute__((aligned(1024))) char x_raw[C::XBYTES];
@@ -64,7 +71,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   // share that XCD's L2.
   const int L = blockIdx.x;
   const int item = DEC ? xcd_item(L, gridDim.x, false, p.hkv, p.nsplit * p.nrb)
-                       : xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hq, p.ntiles);
+                       : xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hq, SPL ? p.ntiles * p.nsplit : p.ntiles);
   if (item >= p.total) return;
   int t, h, s, kvh, split = 0;
   if constexpr (DEC) {
@@ -78,8 +85,10 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     s = rest / p.hkv;
     h = kvh * p.group;
   } else {
-    t = item % p.ntiles;
-    const int hs = item / p.ntiles;
+    const int tile_item = SPL ? item / p.nsplit : item;
+    if constexpr (SPL) split = item % p.nsplit;
+    t = tile_item % p.ntiles;
+    const int hs = tile_item / p.ntiles;
     h = hs % p.hq;
     s = hs / p.hq;
     if (p.causal) t = p.ntiles - 1 - t;  // heaviest causal tiles first
@@ -102,6 +111,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   // G * Nq repeat the last row and are not stored).
   int hl = h, qi_l = qw0 + l32;
   bool row_ok = true;
+  if constexpr (SPL) row_ok = qi_l < sv.lq;
   if constexpr (DEC) {
     const int r = t * 32 + l32;
     row_ok = r < p.rows;
@@ -137,6 +147,12 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   if constexpr (DEC) {
     jbeg = split * p.split_tiles;
     jend = min(jbeg + p.split_tiles, ntk);
+  }
+  if constexpr (SPL) {
+    // an equal share of this query tile's own key tiles (empty ranges give O = 0, LSE = -inf)
+    const int per = (ntk + p.nsplit - 1) / p.nsplit;
+    jbeg = min(split * per, ntk);
+    jend = min(jbeg + per, ntk);
   }
 
   // Q block of this wave as B operands: lane (h, n) holds query n, dims 16 kb + 8 h + 0..7.
@@ -471,9 +487,9 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
       pv_mma(j, pb, [](int) {});
     };
     lds_barrier();
-    if (ntk > 0) {
+    if (jend > jbeg) {
       if (grp == 0) {
-        for (int j = 0; j < ntk; ++j) {
+        for (int j = jbeg; j < jend; ++j) {
           s_phase(j);
           lds_barrier();
           p_phase(j);
@@ -483,7 +499,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
         lds_barrier();
       } else {
         lds_barrier();
-        for (int j = 0; j < ntk; ++j) {
+        for (int j = jbeg; j < jend; ++j) {
           s_phase(j);
           lds_barrier();
           p_phase(j);
@@ -542,8 +558,8 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   // Copies issued during the last step land in LDS that the next workgroup may own.
   wait_vmcnt<0>();
 
-  if constexpr (DEC) {
-    // ---- decode epilogue: this key range's normalised O (fp32) and its LSE in log2 units
+  if constexpr (DEC || SPL) {
+    // ---- decode / split epilogue: this key range's normalised O (fp32) and its LSE in log2 units
     // (-inf and 0 when no key of the range is legal for the row), for the combine pass.
     const float lt = half_sum(lsum[0]);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
@@ -611,6 +627,99 @@ static hipError_t launch_fwd_cfg(AttnParams p, hipStream_t st) {
   else
     hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF, NW>), dim3(grid), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
+}
+
+// Merge of the key-range split forward: many rows, few ranges. One wave per output row (four rows
+// per workgroup); lane l covers columns 8 l .. + 7 of each 512-column chunk and loops over the
+// ranges in order: LSE = log2 sum_s exp2(LSE_s), O = sum_s exp2(LSE_s - LSE) O_s, the same formula
+// as the decode merge in a fixed order.
+template <class T>
+__global__ void __launch_bounds__(256) ffpa_split_combine_kernel(AttnParams p, int nrows) {
+  const int row = blockIdx.x * 4 + wave_id();
+  if (row >= nrows) return;
+  const int lane = threadIdx.x & 63;
+  const int i = row % p.nq;
+  const int bh = row / p.nq;
+  const int h = bh % p.hq;
+  const int b = bh / p.hq;
+  const float* lp = p.part_lse + (long long)row * p.nsplit;
+  const float* po = p.part_o + (long long)row * p.nsplit * p.d;
+  float m = -INFINITY;
+  for (int sp = 0; sp < p.nsplit; ++sp) m = fmaxf(m, lp[sp]);
+  float l = 0.f;
+  if (m != -INFINITY)
+    for (int sp = 0; sp < p.nsplit; ++sp) l += fast_exp2(lp[sp] - m);  // 0 for a range without a legal key
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  uint16_t* orow = (uint16_t*)p.o + (long long)b * p.o_batch + (long long)h * p.o_head + (long long)i * p.o_row;
+  for (int d0 = 8 * lane; d0 < p.d; d0 += 512) {
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    if (m != -INFINITY)
+      for (int sp = 0; sp < p.nsplit; ++sp) {
+        const float wgt = fast_exp2(lp[sp] - m);
+        const float* src = po + (long long)sp * p.d + d0;
+        a0 += wgt * *(const f32x4_t*)src;
+        a1 += wgt * *(const f32x4_t*)(src + 4);
+      }
+    *(u32x4_t*)(orow + d0) = (u32x4_t){Elt<T>::pack2(a0.x * inv, a0.y * inv), Elt<T>::pack2(a0.z * inv, a0.w * inv),
+                                       Elt<T>::pack2(a1.x * inv, a1.y * inv), Elt<T>::pack2(a1.z * inv, a1.w * inv)};
+  }
+  if (lane == 0)
+    p.lse[(long long)b * p.lse_batch + (long long)h * p.lse_head + i] = l > 0.f ? (m + fast_log2(l)) * kLn2 : -INFINITY;
+}
+
+// Key-range split count of a dense forward: 1 when the grid gives at least two workgroups per
+// compute unit (of 256), else enough ranges for that, up to 8 and with at least 4 key tiles each.
+int fwd_split_count(int batch, int hq, int nq, int nkv, int d) {
+  const int bq = d <= 512 ? 128 : 32;  // queries per workgroup of the forward configurations
+  const long long base = (long long)batch * hq * ((nq + bq - 1) / bq);
+  const long long ktiles = (nkv + 31) / 32;
+  if (base <= 0 || base >= 512) return 1;
+  return (int)std::max(1LL, std::min({8LL, (512 + base - 1) / base, ktiles / 4}));
+}
+
+template <class T, int NC, int NDB>
+static hipError_t launch_fwd_split_cfg(AttnParams p, int nsplit, float* ws, hipStream_t st) {
+  constexpr int QB = 1;
+  constexpr int NW = NC == 2 ? 8 : 4;
+  using C1 = FwdCfg<NC, NDB, QB, 1, NW>;
+  constexpr int NBUF = (2 * 2 * C1::TILE + C1::XBYTES) <= 160 * 1024 ? 2 : 1;
+  using C = FwdCfg<NC, NDB, QB, NBUF, NW>;
+  p.ntiles = (p.nq + C::BQ - 1) / C::BQ;
+  p.nsplit = nsplit;
+  const long long nrows = (long long)p.batch * p.hq * p.nq;
+  p.part_o = ws;
+  p.part_lse = ws + nrows * nsplit * p.d;
+  p.total = p.batch * p.hq * p.ntiles * nsplit;
+  if (p.total == 0) return hipSuccess;
+  const int grid = (p.total + 7) & ~7;
+  hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF, NW, false, false, true>), dim3(grid), dim3(64 * NW), 0, st,
+                     p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ffpa_split_combine_kernel<T>, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st, p, (int)nrows);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_fwd_split_t(const AttnParams& p, int nsplit, float* ws, hipStream_t st) {
+  if (p.d <= 512) {
+    switch ((p.d + 63) / 64) {
+      case 5: return launch_fwd_split_cfg<T, 2, 5>(p, nsplit, ws, st);
+      case 6: return launch_fwd_split_cfg<T, 2, 6>(p, nsplit, ws, st);
+      case 7: return launch_fwd_split_cfg<T, 2, 7>(p, nsplit, ws, st);
+      default: return launch_fwd_split_cfg<T, 2, 8>(p, nsplit, ws, st);
+    }
+  }
+  switch ((p.d + 127) / 128) {
+    case 5: return launch_fwd_split_cfg<T, 4, 5>(p, nsplit, ws, st);
+    case 6: return launch_fwd_split_cfg<T, 4, 6>(p, nsplit, ws, st);
+    case 7: return launch_fwd_split_cfg<T, 4, 7>(p, nsplit, ws, st);
+    default: return launch_fwd_split_cfg<T, 4, 8>(p, nsplit, ws, st);
+  }
+}
+
+hipError_t launch_fwd_split(const AttnParams& p, int fp16, int nsplit, void* ws, hipStream_t st) {
+  return fp16 ? launch_fwd_split_t<FP16>(p, nsplit, (float*)ws, st) : launch_fwd_split_t<BF16>(p, nsplit, (float*)ws, st);
 }
 
 template <class T>

@@ -93,6 +93,25 @@ int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int dtype, float scale, int causal, void* stream);
 
 /*
+ * Dense forward for grids too small to fill the GPU: same arguments and results as ffpa_fwd
+ * (O and LSE equal up to fp32 summation order), plus a caller-owned device workspace of at least
+ * ffpa_fwd_split_workspace_bytes() bytes. The key tiles of every query tile are split into ranges
+ * (an equal share of the tile's own, causal, range each: the heavy tiles of a causal grid are
+ * split too); each range writes a normalised fp32 O and its log2 LSE per row to the workspace and
+ * a second pass merges them by LSE weights ("Triton Backend", "Feature support": the split-KV
+ * two-stage merge). When the size function returns 0 no split helps: the call is ffpa_fwd and
+ * the workspace is ignored (may be NULL). Otherwise a NULL or smaller workspace is
+ * FFPA_ERR_INVALID_ARGUMENT. Workspace layout: fp32 O [batch, hq, nq, nsplit, d] then fp32 LSE
+ * [batch, hq, nq, nsplit]; its contents are scratch.
+ */
+int ffpa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int batch, int hq, int hkv, int nq, int nkv, int d,
+                   int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the ffpa_fwd_split workspace; 0 when the grid needs no split or the sizes are invalid. */
+size_t ffpa_fwd_split_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, int d);
+
+/*
  * Dense forward with an attn_mask ("Triton Backend", "Feature support": boolean and additive
  * masks, broadcast in any of the four dimensions). Arguments as ffpa_fwd plus:
  *   mask          device pointer to the mask (FFPA_MASK_ADDITIVE: q's dtype; FFPA_MASK_BOOL: one

@@ -31,7 +31,8 @@ def test_header_declares_expected_entry_points():
     for n in ("ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd", "ffpa_status_string",
               "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes", "ffpa_decode_fwd",
               "ffpa_decode_workspace_bytes", "ffpa_decode_fwd_strided", "ffpa_fwd_strided", "ffpa_fwd_masked",
-              "ffpa_bwd_masked", "ffpa_fwd_fp8", "ffpa_fwd_fp8_workspace_bytes"):
+              "ffpa_bwd_masked", "ffpa_fwd_fp8", "ffpa_fwd_fp8_workspace_bytes", "ffpa_fwd_split",
+              "ffpa_fwd_split_workspace_bytes"):
         assert n in names
 
 
@@ -284,3 +285,21 @@ def test_fp8_validation(lib):
         ptrs = [P] * 5
         ptrs[i] = N
         assert call(ptrs=ptrs) == 1
+
+
+def test_fwd_split_workspace_and_validation(lib):
+    """ffpa_fwd_split_workspace_bytes: B Hq Nq nsplit (D + 1) fp32 values when the grid has fewer
+    than two workgroups per compute unit (128 queries per workgroup for D <= 512, 32 above), else 0;
+    ffpa_fwd_split then needs a workspace of that size, and is ffpa_fwd when it is 0."""
+    lib.ffpa_fwd_split_workspace_bytes.restype = ctypes.c_size_t
+    f = lib.ffpa_fwd_split_workspace_bytes
+    assert f(1, 32, 32, 8192, 8192, 512) == 0                      # 2048 workgroups: no split
+    assert f(1, 2, 2, 128, 128, 512) == 0                          # 4 key tiles: too short to split
+    # 8 heads x 32 tiles = 256 workgroups -> 2 ranges
+    assert f(1, 8, 8, 4096, 4096, 512) == 1 * 8 * 4096 * 2 * 513 * 4
+    assert f(1, 2, 2, 300, 4096, 768) == 2 * 300 * 8 * 769 * 4    # 20 workgroups -> 8 ranges
+    assert f(1, 2, 2, 300, 4096, 300) == 0 and f(1, 3, 2, 300, 4096, 512) == 0
+    def call(b=1, hq=8, hkv=8, nq=4096, nkv=4096, d=512, ws=P, nws=1 << 30):
+        return lib.ffpa_fwd_split(P, P, P, P, P, b, hq, hkv, nq, nkv, d, 0, ctypes.c_float(0.04), 1, ws, nws, S)
+    assert call(ws=N) == 1 and call(nws=1024) == 1
+    assert call(hq=3, hkv=2, ws=N) == 1       # no split for invalid sizes: ffpa_fwd's checks apply

@@ -7,7 +7,7 @@ import torch
 
 import workloads as W
 from oracle import ref
-from tests.gpu_helpers import check_o_lse
+from tests.gpu_helpers import check_o_lse, rel_l2, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -87,6 +87,41 @@ def test_fwd_zero_query_prefix_means(lib):
         assert torch.max(torch.abs(o[0, :, i].cpu().double() - exp)) < 2e-2
         assert torch.allclose(lse[0, :, i].cpu().double(), torch.full((2,), math.log(last + 1), dtype=torch.float64),
                               atol=1e-3)
+
+
+SPLIT_CASES = [
+    # (B, Hq, Hkv, Nq, Nkv, D, dtype, causal): grids below two workgroups per compute unit, which
+    # the binding sends through ffpa_fwd_split
+    (1, 8, 8, 2048, 2048, 512, BF, True),
+    (1, 4, 2, 1000, 1500, 384, FP, False),
+    (2, 2, 1, 700, 520, 320, BF, True),     # causal Nq > Nkv: rows without a legal key
+    (1, 2, 2, 300, 4096, 768, FP, True),    # D > 512 form
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: f"b{c[0]}h{c[1]}x{c[2]}q{c[3]}k{c[4]}d{c[5]}{'c' if c[7] else ''}")
+def test_fwd_split(lib, case):
+    """Key-range split forward: parity with the oracle, agreement with the unsplit forward up to
+    fp32 summation order (O within 1e-2 relative L2, LSE within 1e-4, -inf rows identical) and
+    run-to-run bit equality."""
+    from head_dim_attention_amd import _binding as B
+    b, hq, hkv, nq, nkv, d, dt, causal = case
+    assert B.ffpa_fwd_split_workspace_bytes(b, hq, hkv, nq, nkv, d) > 0
+    q, k, v, _ = W.dense_inputs(b, hq, hkv, nq, nkv, d, dt, seed=300 + d + nq, with_grad=False)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    scale = 1.0 / math.sqrt(d)
+    print(f"split case {case}", flush=True)
+    o, lse = lib.ffpa_fwd(qc, kc, vc, causal=causal, scale=scale)
+    o3, l3 = lib.ffpa_fwd(qc, kc, vc, causal=causal, scale=scale)
+    o2, l2 = lib.ffpa_fwd(qc, kc, vc, causal=causal, scale=scale, split=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o3) and torch.equal(lse, l3)
+    assert torch.equal(torch.isneginf(lse), torch.isneginf(l2))
+    fin = torch.isfinite(l2)
+    assert float((lse[fin] - l2[fin]).abs().max()) < 1e-4
+    assert rel_l2(to64(o), to64(o2)) < 1e-2
+    o_ref, lse_ref = ref.attn_fwd(q, k, v, scale=np.float64(np.float32(scale)), causal=causal)
+    check_o_lse(o, lse, o_ref, lse_ref, dt, f"split {case}")
 
 
 def test_fwd_gqa_equals_repeated(lib):

@@ -5,6 +5,7 @@ fused-QKV chunk views without materializing a packed copy).
 The strided path runs the same kernels with different addressing, so its results must equal the
 packed path's bit for bit; one case per layout is also checked against the oracle.
 """
+import functools
 import math
 
 import numpy as np
@@ -48,7 +49,8 @@ def test_nhd_views_equal_packed(lib, case):
     qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
     qn, kn, vn = _nhd(qc), _nhd(kc), _nhd(vc)
     assert not (qn.is_contiguous() and kn.is_contiguous()), "at least one input is a strided view"
-    for fwd in (lib.ffpa_fwd, lib.ffpa_decode_fwd):
+    # (strided views take no key-range split, so the packed call is made without one)
+    for fwd in (functools.partial(lib.ffpa_fwd, split=False), lib.ffpa_decode_fwd):
         o1, l1 = fwd(qc, kc, vc, causal=causal)
         o2, l2 = fwd(qn, kn, vn, causal=causal)
         torch.cuda.synchronize()
@@ -69,7 +71,8 @@ def test_fused_qkv_slices(lib, nq):
     qkv = torch.randn(b, n, 3, h, d, generator=g).to(BF).cuda()
     q, k, v = (qkv[:, :, i].transpose(1, 2) for i in range(3))
     assert q.stride() == (n * 3 * h * d, d, 3 * h * d, 1)
-    for fwd in (lib.ffpa_fwd, lib.ffpa_decode_fwd):
+    # (strided views take no key-range split, so the packed call is made without one)
+    for fwd in (functools.partial(lib.ffpa_fwd, split=False), lib.ffpa_decode_fwd):
         o1, l1 = fwd(q.contiguous(), k.contiguous(), v.contiguous(), causal=True)
         o2, l2 = fwd(q, k, v, causal=True)
         torch.cuda.synchronize()
