@@ -247,7 +247,7 @@ def cpu_baseline(q, k, v, do, scale, causal, dq, dk, dv, o, lse, tol_o, budget_s
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: times a single GPU only; --gpus {args.gpus} is not supported "
               "(heads are independent, so more GPUs would each run a share of the heads)", file=sys.stderr)
         return 2
 
