@@ -132,12 +132,6 @@ __device__ __forceinline__ u32x4_t join_tr(s16x4_t lo, s16x4_t hi) {
   return (u32x4_t){a.x, a.y, b.x, b.y};
 }
 
-// Asynchronous 16-byte global -> LDS copy: lane l writes LDS bytes [lds + 16 l, lds + 16 l + 16).
-// `lds` must be wave-uniform.
-__device__ __forceinline__ void dma16(const void* gptr, lds_t* lds) {
-  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
-
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 // Buffer resource descriptor over [base, base + bytes) for raw (unformatted) 32-bit accesses:
