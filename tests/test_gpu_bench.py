@@ -1,0 +1,36 @@
+"""bench.py's output contract on the GPU: one JSON line with the metric, the whole-step value, the
+dominant kernel's roofline object, and the decode and FP8 legs with their own rooflines (a short
+run: two timed steps, no CPU baseline)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_json_line():
+    print("bench.py --steps 2 --warmup 1 --no-cpu-baseline", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "2", "--warmup", "1",
+                        "--no-cpu-baseline"], capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+                "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1 and d["value"] > 0 and d["dtype"] == "bf16"
+    assert d["config"]["workload"] == "dense_d512_n8192"
+    roof = d["roofline"]
+    assert set(roof) >= {"bound", "achieved", "peak", "unit", "frac", "traffic"}
+    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and 0 < roof["frac"] < 1
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    dec = d["decode"]["roofline"]
+    assert dec["bound"] == "hbm" and dec["unit"] == "GB/s" and 0 < dec["frac"] < 1
+    f8 = d["fp8_fwd"]["roofline"]
+    assert f8["bound"] == "mfma" and 0 < f8["frac"] < 1 and f8["peak"] > roof["peak"]
