@@ -99,3 +99,30 @@ def test_fp8_forward(lib, case):
     print(f"O |err| / bound max {ratio:.3f}, rel-L2 vs emulation {e_em:.3e}, vs exact {e_ex:.3e}; "
           f"LSE {err_l:.3e}")
     assert ratio <= 1.0 and err_l <= 1e-3 and e_ex <= 0.1
+
+
+def test_fp8_full_size_sampled_head(lib):
+    """The measured shape (B=1, H=32, N=8192, D=512, bf16, as bench.py times it): every head's amax
+    exactly, and one whole head's O against the emulation within the same bound, LSE within 1e-3."""
+    from head_dim_attention_amd import _binding as B
+    w = W.get("dense_d512_n8192")
+    q, k, v, _ = W.workload_inputs(w, seed=2024)
+    b, hq, nq, d = q.shape
+    hkv, nkv = k.shape[1], k.shape[2]
+    nws = B.ffpa_fwd_fp8_workspace_bytes(b, hq, hkv, nq, nkv, d)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    print("fp8 full size", flush=True)
+    o, lse = lib.ffpa_fwd_fp8(q.cuda(), k.cuda(), v.cuda(), causal=False, scale=scale, workspace=ws)
+    torch.cuda.synchronize()
+    aq, ak, av, _, _ = B.fp8_workspace_views(ws, b, hq, hkv, nkv, d)
+    for x, a in ((q, aq), (k, ak), (v, av)):
+        assert np.array_equal(a.cpu().double().numpy(), ref.fp8_quantize(x)[1])
+    h = 7
+    qs, ks, vs = q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1]
+    o_r, lse_r, parts = ref.attn_fwd_fp8(qs, ks, vs, scale=float(np.float32(scale)), causal=False, parts=True)
+    og = to64(o[:, h:h + 1])
+    ratio = float(np.max(np.abs(og - o_r) / fp8_o_bound(parts, o_r, 1, BF)))
+    err_l = float(np.max(np.abs(lse[:, h:h + 1].double().cpu().numpy() - lse_r)))
+    print(f"full size head {h}: O |err| / bound max {ratio:.3f}, LSE {err_l:.3e}")
+    assert ratio <= 1.0 and err_l <= 1e-3
