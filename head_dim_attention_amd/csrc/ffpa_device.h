@@ -234,6 +234,22 @@ __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32);
 __device__ __forceinline__ float half_max(float x) { return fmaxf(x, other_half(x)); }
 __device__ __forceinline__ float half_sum(float x) { return x + other_half(x); }
 
+// Opaque register definition (empty asm): the value is not known to the compiler past this point,
+// so nothing derived from it is hoisted out of a loop (it is recomputed where it is used instead
+// of holding registers across the loop).
+__device__ __forceinline__ int opaque_v(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// This lane's index in its wave, read from the hardware at this point (not a value the compiler
+// may keep in a register across a loop).
+__device__ __forceinline__ int fresh_lane_id() {
+  int x;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+  return x;
+}
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Work item of workgroup L among items ordered (sequence, head, inner index), `inner` items per
@@ -307,47 +323,61 @@ __device__ __forceinline__ DsView ds_view(const AttnParams& p, int s, const SeqV
   return v;
 }
 
-// attn_mask terms of 8 consecutive keys key0 .. key0 + 7 of the mask row at element offset rowoff,
-// in units of the raw scores: bias / scale for an additive mask, 0 (kept) or -inf (dropped) for a
-// boolean one. Keys at or past lk give 0 (the caller masks them). With a contiguous key dim the
-// row offset and key0 are multiples of 8, so a whole piece is one aligned 16-byte (bias) or
-// 8-byte (boolean) load; the last, partial piece of a row is read element by element.
+// attn_mask of 8 consecutive keys key0 .. key0 + 7 (key0 a multiple of 8) of the mask row at
+// element offset rowoff, in two steps so that the load can be issued well before its use.
+// mask_raw8 returns the raw bits: additive, eight 16-bit values (all four words); boolean, eight
+// bytes (.x, .y); a key-broadcast mask (m_key == 0), its one element in .x. With a contiguous key
+// dim the row offset is a multiple of 8 and the base is aligned, so a piece is one aligned 16-byte
+// (bias) or 8-byte (boolean) load. A piece that reaches past the row's last key lk - 1 is read
+// as the row's last whole aligned piece instead (the one holding key lk - 1: an aligned piece
+// never crosses a memory page, so the read stays in mapped memory); the terms of keys at or past
+// lk are then meaningless and the caller drops those keys by the key bound. lk >= 1.
 template <class T>
-__device__ __forceinline__ void mask8(const AttnParams& p, long long rowoff, int key0, int lk, float (&out)[8]) {
+__device__ __forceinline__ u32x4_t mask_raw8(const AttnParams& p, long long rowoff, int key0, int lk) {
+  const int k = p.m_key == 0 ? 0 : min(key0, max(lk - 1, 0) & ~7);
   if (p.mask_kind == 1) {
-    const uint16_t* m = (const uint16_t*)p.mask + rowoff;
+    const uint16_t* m = (const uint16_t*)p.mask + rowoff + k;
+    if (p.m_key == 0) return (u32x4_t){(uint32_t)m[0], 0u, 0u, 0u};
+    return *(const u32x4_t*)m;
+  }
+  const uint8_t* m = (const uint8_t*)p.mask + rowoff + k;
+  if (p.m_key == 0) return (u32x4_t){(uint32_t)m[0], 0u, 0u, 0u};
+  const u32x2_t v = *(const u32x2_t*)m;
+  return (u32x4_t){v.x, v.y, 0u, 0u};
+}
+
+// The mask terms of those eight keys, in units of the raw scores: bias / scale for an additive
+// mask, 0 (kept) or -inf (dropped) for a boolean one.
+template <class T>
+__device__ __forceinline__ void mask_apply8(const AttnParams& p, u32x4_t raw, float (&out)[8]) {
+  if (p.mask_kind == 1) {
     if (p.m_key == 0) {
-      const float x = Elt<T>::to_f32(m[0]) * p.inv_scale;
+      const float x = Elt<T>::to_f32((uint16_t)raw.x) * p.inv_scale;
 #pragma unroll
       for (int e = 0; e < 8; ++e) out[e] = x;
-    } else if (key0 + 8 <= lk) {
-      const u32x4_t v = *(const u32x4_t*)(m + key0);
+    } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float lo, hi;
-        Elt<T>::unpack2(v[e], lo, hi);
+        Elt<T>::unpack2(raw[e], lo, hi);
         out[2 * e] = lo * p.inv_scale;
         out[2 * e + 1] = hi * p.inv_scale;
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = key0 + e < lk ? Elt<T>::to_f32(m[key0 + e]) * p.inv_scale : 0.f;
     }
+  } else if (p.m_key == 0) {
+    const float x = (raw.x & 0xffu) != 0 ? 0.f : -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = x;
   } else {
-    const uint8_t* m = (const uint8_t*)p.mask + rowoff;
-    if (p.m_key == 0) {
-      const float x = m[0] != 0 ? 0.f : -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = x;
-    } else if (key0 + 8 <= lk) {
-      const u32x2_t v = *(const u32x2_t*)(m + key0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = ((e < 4 ? v.x : v.y) >> (8 * (e & 3))) & 0xffu ? 0.f : -INFINITY;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = key0 + e < lk && m[key0 + e] == 0 ? -INFINITY : 0.f;
-    }
+    for (int e = 0; e < 8; ++e) out[e] = ((e < 4 ? raw.x : raw.y) >> (8 * (e & 3))) & 0xffu ? 0.f : -INFINITY;
   }
+}
+
+// Both steps at once.
+template <class T>
+__device__ __forceinline__ void mask8(const AttnParams& p, long long rowoff, int key0, int lk, float (&out)[8]) {
+  mask_apply8<T>(p, mask_raw8<T>(p, rowoff, key0, lk), out);
 }
 
 // attn_mask term of one key (< lk) of the mask row at element offset rowoff.

@@ -186,13 +186,9 @@ __device__ __forceinline__ void pin_fp8_pipeline() {
 // LDS operand reads issued ahead of their MFMA in the product runs.
 constexpr int FP8_AHEAD = 2;
 
-// Opaque register uses and definitions (empty asm): a value is materialised here, or is not known
-// to the compiler past this point (so nothing derived from it is hoisted out of the loop).
+// Opaque register use (empty asm): the value is materialised here (see opaque_v for the other
+// direction).
 __device__ __forceinline__ void keep_here(const f32x16_t& x) { asm volatile("" ::"v"(x)); }
-__device__ __forceinline__ int opaque_v(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
 
 __device__ __forceinline__ f32x16_t mma_fp8(i32x8_t a, i32x8_t b, f32x16_t c) {
   // unit block scales (E8M0 127 = 2^0); A and B in OCP e4m3 (format 0)

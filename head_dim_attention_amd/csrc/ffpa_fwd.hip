@@ -33,12 +33,20 @@ namespace ffpa {
 #define FWD_AHEAD 2
 #endif
 
+
 template <int NC, int NDB, int QB, int NBUF, int NW>
 struct FwdCfg {
   static constexpr int NR = NW / NC;                     // query row groups
   static constexpr int DW = NDB * 32;                    // head-dim columns per wave
   static constexpr int DPAD = NC * DW;                   // padded head dim
   static constexpr int RS = DPAD <= 512 ? 1024 : 2048;   // LDS row stride (bytes), power of two
+  // An LDS row gives each wave's head-dim columns a slot of SLOT 16-byte chunks, of which the
+  // first WCH hold its columns; the rest are padding. Every wave's operands then start on a
+  // 16-chunk boundary, where the row swizzle (an XOR on the low 4 bits of the chunk index) makes
+  // each operand address one per-lane base XOR a constant.
+  static constexpr int WCH = NDB * 4;                    // 16-byte chunks of one wave's columns
+  static constexpr int SLOT = RS / 16 / NC;              // chunks per wave slot
+  static_assert(WCH <= SLOT && SLOT % 16 == 0, "one 16-chunk-aligned slot per wave in an LDS row");
   static constexpr int BQ = NR * QB * 32;                // queries per workgroup
   static constexpr int TILE = 32 * RS;                   // one 32-row K or V tile in LDS
   static constexpr int XBYTES = NW * QB * 16 * 64 * 4;   // partial scores of all waves
@@ -182,18 +190,20 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
 
   // DMA: instruction ii of this wave fills LDS bytes [1024 i, 1024 i + 1024) of a tile, i = w + 4 ii,
   // i.e. tile row R = i / (RS / 1024) (uniform per instruction). Lane l writes physical chunk
-  // pc = (i % (RS/1024)) * 64 + l, holding logical chunk pc ^ swz(R) (clamped into the head dim:
-  // padded chunks hold finite duplicates that never reach a result). The column offset is
+  // pc = (i % (RS/1024)) * 64 + l; un-swizzled, u = pc ^ swz(R) is chunk u % SLOT of wave slot
+  // u / SLOT, i.e. head-dim chunk (u / SLOT) WCH + u % SLOT. Padding chunks and chunks past the head dim
+  // hold finite duplicates (clamped indices) that never reach a result. The column offset is
   // loop-invariant (VGPR); the row offset, clamped to the last key, is scalar.
   constexpr int IPR = C::RS / 1024;  // DMA instructions per LDS row
   const int dch = p.d >> 3;
+  auto src_chunk = [&](int u) { return min((u / C::SLOT) * C::WCH + min(u % C::SLOT, C::WCH - 1), dch - 1); };
   int voff[C::NINSTR];
 #pragma unroll
   for (int ii = 0; ii < C::NINSTR; ++ii) {
     const int i = w + NW * ii;
     const int R = i / IPR;
     const int pc = (i % IPR) * 64 + lane;
-    voff[ii] = min(pc ^ swz(R), dch - 1) << 4;
+    voff[ii] = src_chunk(pc ^ swz(R)) << 4;
   }
   auto issue1 = [&](const Src& x, int j, lds_t* dst, int ii) {
     const int i = w + NW * ii;
@@ -216,18 +226,16 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   const int kswz = swz(krow);
   const int g16 = lane >> 4;
   const int r16 = lane & 15;
-  const int cbase = cg * C::DW >> 3;  // first 16-byte chunk of this wave's head-dim columns
+  const int cbase = cg * C::SLOT;  // first physical 16-byte chunk of this wave's slot
 
-  // LDS byte addresses of this lane's operands in a tile at LDS address `tile`. When the wave's
-  // first chunk is a multiple of 16, the swizzle (an XOR on the low 4 bits of the 16-byte chunk
-  // index) touches only address bits 4-7, which are zero in the row, column-group and tile bases:
-  // every operand address is then one per-lane base XOR a compile-time constant, plus a constant.
-  constexpr bool kAligned = (C::DW % 128) == 0;
+  // LDS byte addresses of this lane's operands in a tile at LDS address `tile`. The wave's slot
+  // starts on a multiple of 16 chunks, so the swizzle (an XOR on the low 4 bits of the 16-byte
+  // chunk index) touches only address bits 4-7, which are zero in the row, slot and tile bases:
+  // every operand address is one per-lane base XOR a compile-time constant, plus a constant.
   // K rows (A operand of S^T): tile row row_perm(m), chunk cbase + 2 kb + h.
   const uint32_t klane = krow * C::RS + (cbase << 4) + ((hh ^ kswz) << 4);
   auto k_addr = [&](uint32_t tile, int kb) -> uint32_t {
-    if constexpr (kAligned) return ((tile + klane) ^ ((kb & 7) << 5)) + ((kb >> 3) << 8);
-    return tile + krow * C::RS + (((cbase + 2 * kb + hh) ^ kswz) << 4);
+    return ((tile + klane) ^ ((kb & 7) << 5)) + ((kb >> 3) << 8);
   };
   // V^T (A operand of O^T += V^T P^T) via transposed reads: key row
   // k = 16 kb2 + 8 h + 4 half + r16/4, head-dim column d = cg DW + 32 db + 16 (g16 % 2) + 4 (r16 % 4),
@@ -241,10 +249,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     vlane[half] = k * C::RS + (cbase << 4) + ((vclo ^ swz(k)) << 4) + vwithin;
   }
   auto v_addr = [&](uint32_t tile, int db, int kb2, int half) -> uint32_t {
-    if constexpr (kAligned)
-      return ((tile + vlane[half]) ^ ((db & 3) << 6)) + ((db >> 2) << 8) + kb2 * 16 * C::RS;
-    const int k = 16 * kb2 + 8 * hh + 4 * half + (r16 >> 2);
-    return tile + k * C::RS + (((cbase + 4 * db + vclo) ^ swz(k)) << 4) + vwithin;
+    return ((tile + vlane[half]) ^ ((db & 3) << 6)) + ((db >> 2) << 8) + kb2 * 16 * C::RS;
   };
 
   // ---- pipeline pieces (each runs the same barriers in every wave) --------------------------
@@ -259,12 +264,59 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     }
   };
 
+  // attn_mask: this lane's mask rows and the raw bits of one tile (mask_fetch). The two-group
+  // schedule requests tile j + 1's bits during the P V products of tile j (no copies are issued
+  // there, and the score registers are free) and starts the scores of one wave of each row group
+  // from the mask terms, so that the combined sum holds them once; the other schedules request
+  // them when a tile's score products start and add them to the combined scores.
+  // The row address is rebuilt at each fetch from the lane index (a few ALU operations) rather
+  // than held in registers across the loop.
+  u32x4_t mraw[QB][2];
+  auto mask_fetch = [&](int j) {
+    const int ln = fresh_lane_id();
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      int hm = h, qm = min(qw0 + qb * 32 + (ln & 31), sv.lq - 1);
+      if constexpr (DEC) {
+        const int rc = min(t * 32 + (ln & 31), p.rows - 1);
+        hm = h + rc / sv.lq;
+        qm = rc % sv.lq;
+      }
+      const long long row = mask_row(p, s, hm, qm);
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        mraw[qb][half] = mask_raw8<T>(p, row, j * 32 + 16 * half + 8 * (ln >> 5), sv.lk);
+    }
+  };
+  // Registers 0..7 of a score block hold keys 8 h + 0..7 of the tile, registers 8..15 keys
+  // 16 + 8 h + 0..7.
+  auto mask_terms = [&](int qb, f32x16_t& acc, bool add) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float mb[8];
+      mask_apply8<T>(p, mraw[qb][half], mb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[8 * half + e] = add ? acc[8 * half + e] + mb[e] : mb[e];
+    }
+  };
+
   // Partial S^T (keys x queries) of tile j over this wave's head-dim columns, written to the
   // exchange buffer; copy_at(kb) issues the tile copies assigned to k-step kb.
   auto s_partial = [&](int j, f32x16_t (&sacc)[QB], auto&& copy_at) {
     const lds_t* kt = kbuf(NBUF == 2 ? (j & 1) : 0);
+    if constexpr (MASK && kPingPong) {
+      if (cg == 0) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) sacc[qb] = (f32x16_t){};
+        for (int qb = 0; qb < QB; ++qb) mask_terms(qb, sacc[qb], false);
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb] = (f32x16_t){};
+      }
+    } else {
+      if constexpr (MASK) mask_fetch(j);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb] = (f32x16_t){};
+    }
 #pragma unroll
     for (int kb = 0; kb < 2 * NDB; ++kb) {
       const u32x4_t a = lds_read_b128_at(k_addr(lds_addr(kt), kb));
@@ -301,20 +353,9 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
         sacc[qb][4 * r4 + 2] = mine.z; sacc[qb][4 * r4 + 3] = mine.w;
       }
     }
-    if constexpr (MASK) {
-      // Registers 0..7 hold keys 8 h + 0..7 of the tile, registers 8..15 keys 16 + 8 h + 0..7.
+    if constexpr (MASK && !kPingPong) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qi = DEC ? qi_l : min(qw0 + qb * 32 + l32, sv.lq - 1);
-        const long long mr = mask_row(p, s, hl, qi);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float mb[8];
-          mask8<T>(p, mr, j * 32 + 16 * half + 8 * hh, sv.lk, mb);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sacc[qb][8 * half + e] += mb[e];
-        }
-      }
+      for (int qb = 0; qb < QB; ++qb) mask_terms(qb, sacc[qb], true);
     }
     // Mask tail keys and the causal diagonal (only on tiles that need it).
     const bool need_mask = (j * 32 + 32 > sv.lk) || (p.causal && j * 32 + 31 > q_lo + off);
@@ -444,7 +485,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     constexpr int GCOPY = 2 * C::NINSTR;  // 1 KB copies per wave of the group's tile
     int gvoff[4];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) gvoff[ii] = min(lane ^ swz(wg + 4 * ii), dch - 1) << 4;
+    for (int ii = 0; ii < 4; ++ii) gvoff[ii] = src_chunk(lane ^ swz(wg + 4 * ii)) << 4;
     const Src gsrc = grp == 0 ? ksrc : vsrc;
     auto gcopy = [&](int j, int ii) {
       const int i = wg + 4 * ii;
@@ -484,8 +525,14 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
       }
       uint32_t pb[QB][2][4];
       make_p(sacc, pb);
+      if constexpr (MASK) {
+        if (cg == 0) mask_fetch(j + 1);  // past the last tile: clamped to the row, unused
+      }
       pv_mma(j, pb, [](int) {});
     };
+    if constexpr (MASK) {
+      if (cg == 0) mask_fetch(jbeg);
+    }
     lds_barrier();
     if (jend > jbeg) {
       if (grp == 0) {

@@ -120,7 +120,10 @@ size_t ffpa_fwd_split_workspace_bytes(int batch, int hq, int hkv, int nq, int nk
  *   mask_strides  host int64[4]: element (b, h, i, j) of the mask, for query head h, query i and
  *                 key j, sits at b*s[0] + h*s[1] + i*s[2] + j*s[3]; a stride of 0 broadcasts that
  *                 dimension. s[3] must be 0 or 1; with s[3] == 1, s[0..2] are multiples of 8 and
- *                 the mask pointer is 16-byte (additive) / 8-byte (boolean) aligned.
+ *                 the mask pointer is 16-byte (additive) / 8-byte (boolean) aligned. The mask is
+ *                 read in aligned 8-key pieces: the piece holding a row's last key is read whole,
+ *                 so up to 7 elements past that key (never past its aligned 16- or 8-byte piece)
+ *                 are loaded and ignored.
  * The scores are scale * q k^T + bias (or -inf where a boolean mask drops the key), combined with
  * the causal mask when causal = 1; a row whose scores are all -inf is empty (O = 0, LSE = -inf).
  * Invalid mask arguments are FFPA_ERR_INVALID_ARGUMENT.

@@ -53,6 +53,8 @@ CASES = [
     (1, 3, 3, 33, 200, 448, BF, True, "11QK", "bool"),
     (2, 2, 2, 64, 64, 512, BF, False, "B1QK", "add"),
     (1, 2, 1, 50, 70, 512, BF, True, "1H1K", "add"),
+    (1, 2, 2, 70, 91, 384, BF, True, "BHQ1", "add"),
+    (2, 2, 1, 45, 203, 512, FP, False, "BHQK", "bool"),
 ]
 
 
