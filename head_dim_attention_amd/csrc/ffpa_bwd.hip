@@ -1044,9 +1044,17 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
   };
 
   f32x16_t sacc, pacc;
+  // attn_mask bits of this lane's 8 keys of tile j: requested when the tile's products start (the
+  // multiplying phase issues no copies), used after the exchange.
+  const long long mrow = MASK ? mask_row(p, s, h, min(qi, sv.lq - 1)) : 0;
+  u32x4_t mraw;
   // Partial S^T and dP^T of tile j over this wave's half; the partner's rows go to the exchange.
   auto m_phase = [&](int j) {
     const uint32_t kt = lds_addr(kbuf(j & 1)), vt = lds_addr(vbuf(j & 1));
+    if constexpr (MASK) {
+      mraw = mask_block(p, mrow, j * 32 + 16 * cg + 8 * hh, sv.lk);
+      __builtin_amdgcn_sched_barrier(0);  // issued here, not sunk behind the products
+    }
     sacc = (f32x16_t){};
     pacc = (f32x16_t){};
 #pragma unroll
@@ -1079,9 +1087,9 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
     }
     if constexpr (MASK) {
       // attn_mask terms of this lane's 8 keys (added to the scores before P). The empty asm keeps
-      // the sums, and so the wait for the mask loads, ahead of the copies issued next.
+      // the sums, and so the wait for the mask load, ahead of the copies issued next.
       float mb[8];
-      mask8<T>(p, mask_row(p, s, h, min(qi, sv.lq - 1)), j * 32 + 16 * cg + 8 * hh, sv.lk, mb);
+      mask_apply8_block<T>(p, mraw, mrow, j * 32 + 16 * cg + 8 * hh, sv.lk, mb);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         sf[e] += mb[e];
@@ -1163,8 +1171,9 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
       for (int j = jb; j < je; ++j) {
         m_phase(j);
         // Tile j + 1 (copied in the prologue, or in the finishing phase of step j - 1, followed
-        // there by that step's two stores, which may stay in flight).
-        if (j == jb) wait_vmcnt<0>(); else wait_vmcnt<2>();
+        // there by that step's two stores and then this step's mask load, which may stay in
+        // flight).
+        if (j == jb) wait_vmcnt<0>(); else wait_vmcnt<MASK ? 3 : 2>();
         lds_barrier();
         e_phase(j, [&] {
 #pragma unroll

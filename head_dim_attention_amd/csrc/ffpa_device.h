@@ -374,10 +374,52 @@ __device__ __forceinline__ void mask_apply8(const AttnParams& p, u32x4_t raw, fl
   }
 }
 
-// Both steps at once.
+// The same 8 keys as one load in every form (used where the load is issued long before its use
+// and copies are issued in between: a form that also writes zero words after its load makes the
+// compiler wait for that load, and so for the copies, before the registers are reused).
+// mask_block loads the aligned 16-byte block that holds the first needed element: with a
+// contiguous key dim the row offset is a multiple of 8 and the base is aligned, so an additive
+// piece is the whole block and a boolean piece one half of it; a key-broadcast mask (m_key == 0)
+// has its one element somewhere in the block. An aligned block never crosses a memory page, so the
+// read stays in mapped memory. A piece that reaches past the row's last key lk - 1 is read as the
+// row's last whole aligned piece instead (the one holding key lk - 1); the terms of keys at or
+// past lk are then meaningless and the caller drops those keys by the key bound. lk >= 1.
+// (Pointer arithmetic on the mask pointer throughout, so that the loads stay global loads.)
+__device__ __forceinline__ const char* mask_addr(const AttnParams& p, long long rowoff, int key0, int lk) {
+  const int k = p.m_key == 0 ? 0 : min(key0, max(lk - 1, 0) & ~7);
+  return (const char*)p.mask + ((rowoff + k) << (p.mask_kind == 1 ? 1 : 0));
+}
+__device__ __forceinline__ u32x4_t mask_block(const AttnParams& p, long long rowoff, int key0, int lk) {
+  const char* a = mask_addr(p, rowoff, key0, lk);
+  return *(const u32x4_t*)(a - ((uintptr_t)a & 15));
+}
+
+// The mask terms of those eight keys from mask_block's bits (same rowoff, key0, lk), in units of
+// the raw scores: bias / scale for an additive mask, 0 (kept) or -inf (dropped) for a boolean one.
 template <class T>
-__device__ __forceinline__ void mask8(const AttnParams& p, long long rowoff, int key0, int lk, float (&out)[8]) {
-  mask_apply8<T>(p, mask_raw8<T>(p, rowoff, key0, lk), out);
+__device__ __forceinline__ void mask_apply8_block(const AttnParams& p, u32x4_t blk, long long rowoff, int key0,
+                                                  int lk, float (&out)[8]) {
+  if (p.m_key == 0) {
+    const int at = (int)((uintptr_t)mask_addr(p, rowoff, key0, lk) & 15);  // byte offset of the element
+    const uint32_t word = at < 8 ? (at < 4 ? blk.x : blk.y) : (at < 12 ? blk.z : blk.w);
+    const uint32_t e = word >> (8 * (at & 3));
+    const float x = p.mask_kind == 1 ? Elt<T>::to_f32((uint16_t)e) * p.inv_scale : ((e & 0xffu) != 0 ? 0.f : -INFINITY);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = x;
+  } else if (p.mask_kind == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float lo, hi;
+      Elt<T>::unpack2(blk[i], lo, hi);
+      out[2 * i] = lo * p.inv_scale;
+      out[2 * i + 1] = hi * p.inv_scale;
+    }
+  } else {
+    const bool upper = ((uintptr_t)mask_addr(p, rowoff, key0, lk) & 8) != 0;
+    const uint32_t w0 = upper ? blk.z : blk.x, w1 = upper ? blk.w : blk.y;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = ((i < 4 ? w0 : w1) >> (8 * (i & 3))) & 0xffu ? 0.f : -INFINITY;
+  }
 }
 
 // attn_mask term of one key (< lk) of the mask row at element offset rowoff.
