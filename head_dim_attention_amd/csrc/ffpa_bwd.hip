@@ -945,7 +945,12 @@ struct PdsCfg {
   static constexpr int XWAVE = 4 * 64 * 16;        // per wave: the partner's half of S and dP
   static constexpr int LDS = 4 * TILE + 8 * XWAVE;  // [buffer][K, V] tiles, exchange
   static constexpr int GCOPY = TILE / 1024 / 4;    // 1 KB copies per wave of a tile (one group)
-  static_assert(2 * DW <= 512 && LDS <= 160 * 1024, "LDS budget");
+  // Each head-dim half owns a 32-chunk (512-byte) slot of an LDS row, its WCH chunks first, so its
+  // operands start on a 16-chunk boundary and every operand address is one per-lane base XOR a
+  // constant (the row swizzle flips only address bits 4-7).
+  static constexpr int WCH = NDB * 4;
+  static constexpr int SLOT = 32;
+  static_assert(2 * DW <= 512 && LDS <= 160 * 1024 && WCH <= SLOT && 2 * SLOT * 16 == RS, "LDS budget");
 };
 
 template <class T, int NDB, bool MASK>
@@ -1022,11 +1027,14 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
   const __amdgpu_buffer_rsrc_t ds_rs = __builtin_amdgcn_make_buffer_rsrc((uint16_t*)p.ds + hoff, 0, nrec, 0x00020000);
   const __amdgpu_buffer_rsrc_t p_rs = __builtin_amdgcn_make_buffer_rsrc((uint16_t*)p.pst + hoff, 0, nrec, 0x00020000);
 
-  // Copies: instruction ii of a wave of a group fills tile row i = wg + 4 ii of that group's tile.
+  // Copies: instruction ii of a wave of a group fills tile row i = wg + 4 ii of that group's tile;
+  // lane l writes physical chunk l, whose un-swizzled index u = l ^ swz(i) is chunk u % SLOT of
+  // half u / SLOT (padding and chunks past the head dim hold clamped, finite duplicates).
   const int dch = p.d >> 3;
+  auto src_chunk = [&](int u) { return min((u / C::SLOT) * C::WCH + min(u % C::SLOT, C::WCH - 1), dch - 1); };
   int gvoff[4];
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii) gvoff[ii] = min(lane ^ swz(wg + 4 * ii), dch - 1) << 4;
+  for (int ii = 0; ii < 4; ++ii) gvoff[ii] = src_chunk(lane ^ swz(wg + 4 * ii)) << 4;
   auto gcopy = [&](const i32x4_t& rs, lds_t* tile, int j, int ii) {
     const int i = wg + 4 * ii;
     dma16_buf(rs, gvoff[ii & 3], min(j * 32 + i, sv.lk - 1) * row_bytes, tile + i * 1024);
@@ -1035,12 +1043,10 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
   // K and V rows (A operands): MFMA row m reads tile row row_perm(m) ^ 16 cg (see above).
   const int krow = row_perm(l32) ^ (16 * cg);
   const int kswz = swz(krow);
-  const int cbase = cg * C::DW >> 3;
-  constexpr bool kAligned = (C::DW % 128) == 0;
+  const int cbase = cg * C::SLOT;
   const uint32_t klane = krow * C::RS + (cbase << 4) + ((hh ^ kswz) << 4);
   auto a_addr = [&](uint32_t tile, int kb) -> uint32_t {
-    if constexpr (kAligned) return ((tile + klane) ^ ((kb & 7) << 5)) + ((kb >> 3) << 8);
-    return tile + krow * C::RS + (((cbase + 2 * kb + hh) ^ kswz) << 4);
+    return ((tile + klane) ^ ((kb & 7) << 5)) + ((kb >> 3) << 8);
   };
 
   f32x16_t sacc, pacc;
@@ -1143,7 +1149,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
     for (int ii = 0; ii < 4; ++ii) {
       const int i = w + 8 * ii;
       const int row = min(jb * 32 + i, sv.lk - 1) * row_bytes;
-      const int vo = min(lane ^ swz(i), dch - 1) << 4;
+      const int vo = src_chunk(lane ^ swz(i)) << 4;
       dma16_buf(krs, vo, row, kbuf(jb & 1) + i * 1024);
       dma16_buf(vrs, vo, row, vbuf(jb & 1) + i * 1024);
     }
