@@ -142,3 +142,29 @@ def test_autograd_mask_grad(lib):
     g_ref = ref.attn_bwd(q, k, v, do, scale=s64, causal=True, bias=bias.double().numpy())
     check_grads((qc.grad, kc.grad, vc.grad), g_ref[:3], "autograd mask")
     assert rel_l2(to64(bc.grad), g_ref[3]) <= GRAD_RTOL
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("d,kind", [(512, "add"), (448, "bool")])
+def test_mask_full_size(lib, d, kind):
+    """The masked forward and backward at the benchmark's sequence length (N = 8192: 256 key tiles
+    per row through the two-group schedule, the mask fetched a tile ahead) with one [1, 1, N, N]
+    mask shared by all heads; whole heads 0 and 3 against the oracle."""
+    b, h, n = 1, 4, 8192
+    q, k, v, do = W.dense_inputs(b, h, h, n, n, d, BF, seed=900 + d)
+    m = _bias((1, 1, n, n), BF, 901, kind)
+    scale = 1.0 / math.sqrt(d)
+    s64 = np.float64(np.float32(scale))
+    print(f"full-size masked d{d} {kind}: running on the GPU", flush=True)
+    qc, kc, vc, doc, mc = q.cuda(), k.cuda(), v.cuda(), do.cuda(), m.cuda()
+    o, lse = lib.ffpa_fwd(qc, kc, vc, scale=scale, attn_mask=mc)
+    dq, dk, dv = lib.ffpa_bwd(qc, kc, vc, o, doc, lse, scale=scale, attn_mask=mc)[:3]
+    torch.cuda.synchronize()
+    rb = _ref_bias(m)
+    for hd in (0, 3):
+        sl = slice(hd, hd + 1)
+        tag = f"full-size masked d{d} {kind} head {hd}"
+        o_ref, lse_ref = ref.attn_fwd(q[:, sl], k[:, sl], v[:, sl], scale=s64, causal=False, bias=rb)
+        check_o_lse(o[:, sl], lse[:, sl], o_ref, lse_ref, BF, tag)
+        g_ref = ref.attn_bwd(q[:, sl], k[:, sl], v[:, sl], do[:, sl], scale=s64, causal=False, bias=rb)
+        check_grads((dq[:, sl], dk[:, sl], dv[:, sl]), g_ref[:3], tag)
