@@ -704,8 +704,11 @@ __global__ void __launch_bounds__(256) ffpa_split_combine_kernel(AttnParams p, i
       for (int sp = 0; sp < p.nsplit; ++sp) {
         const float wgt = fast_exp2(lp[sp] - m);
         const float* src = po + (long long)sp * p.d + d0;
-        a0 += wgt * *(const f32x4_t*)src;
-        a1 += wgt * *(const f32x4_t*)(src + 4);
+        // Read once: non-temporal loads, so that the partials do not stay in the caches at the
+        // expense of the next launch's operands (the P/dS pass after a split forward ran about 35%
+        // slower with ordinary loads here).
+        a0 += wgt * __builtin_nontemporal_load((const f32x4_t*)src);
+        a1 += wgt * __builtin_nontemporal_load((const f32x4_t*)(src + 4));
       }
     *(u32x4_t*)(orow + d0) = (u32x4_t){Elt<T>::pack2(a0.x * inv, a0.y * inv), Elt<T>::pack2(a0.z * inv, a0.w * inv),
                                        Elt<T>::pack2(a1.x * inv, a1.y * inv), Elt<T>::pack2(a1.z * inv, a1.w * inv)};
