@@ -28,10 +28,11 @@
 #include "ffpa_params.h"
 
 namespace ffpa {
-// MFMAs whose LDS operands are requested ahead of the one issuing (see pin_lds_mfma_pipeline).
-#ifndef FWD_AHEAD
-#define FWD_AHEAD 2
-#endif
+// MFMAs whose LDS operands are requested ahead of the one issuing (see pin_lds_mfma_pipeline):
+// three for the two-wave head-dim split at D = 384 and 448 (1-2% faster there), two otherwise
+// (three is 3.5% slower at D = 512 and no faster at D = 320).
+template <int NC, int NDB>
+constexpr int fwd_ahead() { return NC == 2 && (NDB == 6 || NDB == 7) ? 3 : 2; }
 
 
 template <int NC, int NDB, int QB, int NBUF, int NW>
@@ -324,7 +325,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
       for (int qb = 0; qb < QB; ++qb) sacc[qb] = Elt<T>::mma(a, qreg[qb][kb], sacc[qb]);
       copy_at(kb);
     }
-    if constexpr (QB == 1) pin_lds_mfma_pipeline<2 * NDB, FWD_AHEAD, 1>();
+    if constexpr (QB == 1) pin_lds_mfma_pipeline<2 * NDB, fwd_ahead<NC, NDB>(), 1>();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -440,7 +441,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
         copy_at(2 * db + kb2);
       }
     }
-    if constexpr (QB == 1) pin_lds_mfma_pipeline<2 * NDB, FWD_AHEAD, 2>();
+    if constexpr (QB == 1) pin_lds_mfma_pipeline<2 * NDB, fwd_ahead<NC, NDB>(), 2>();
   };
   auto pv = [&](int j, const uint32_t (&pb)[QB][2][4]) {
     if constexpr (NBUF == 1) {
