@@ -25,6 +25,11 @@ What is computed, and where the ffpa-attn user guide fixes it:
   Delta = rowsum(dO * O), dV = P^T dO, dP = dO V^T, dS = P * (dP - Delta), dK = scale dS^T Q,
   dQ = scale dS K. These are the exact gradients of L = sum(dO * O); the oracle writes the
   definition out and leaves the split into kernels to the GPU side.
+* The LSE is an output the caller may use ("CuTe-DSL Backend", "Varlen (packed THD) API":
+  return_lse=True hands it back), so it can carry a gradient dLSE of its own. With
+  L = sum(dO * O) + sum(dLSE * LSE), the chain rule adds, for every legal entry, dLSE_i times
+  d LSE_i / d S_ij = P_ij to the gradient with respect to the scores: dS = P * (dP - Delta) +
+  P * dLSE. Empty rows have a constant LSE (-inf), so their dLSE contributes nothing.
 * attn_mask ("Triton Backend", "Feature support"): an additive bias broadcastable to
   [B, Hq, Nq, Nkv] is added to the scaled scores (SDPA semantics); a boolean mask is the bias
   0 where it keeps a key and -inf where it drops one. An entry whose score is -inf is not a legal
@@ -108,10 +113,11 @@ def group_forward(qg: np.ndarray, kg: np.ndarray, vg: np.ndarray, scale: float, 
     return o, lse
 
 
-def group_backward(qg, kg, vg, dog, scale: float, causal: bool, bias_g=None):
-    """Gradients of L = sum(dO * O) for one KV group.
+def group_backward(qg, kg, vg, dog, scale: float, causal: bool, bias_g=None, dlse_g=None):
+    """Gradients of L = sum(dO * O) (+ sum(dLSE * LSE) with dlse_g) for one KV group.
 
-    qg, dog [G, Nq, D]; kg, vg [Nkv, D]; bias_g None or [G, Nq, Nkv]. Returns dQ [G, Nq, D],
+    qg, dog [G, Nq, D]; kg, vg [Nkv, D]; bias_g None or [G, Nq, Nkv]; dlse_g None or [G, Nq], the
+    gradient of the loss with respect to the LSE. Returns dQ [G, Nq, D],
     dK [Nkv, D], dV [Nkv, D], the forward's O [G, Nq, D], LSE [G, Nq] and Delta [G, Nq], and dS
     [G, Nq, Nkv] (the gradient with respect to the scores; None without a bias), all float64.
     """
@@ -142,6 +148,9 @@ def group_backward(qg, kg, vg, dog, scale: float, causal: bool, bias_g=None):
             # dP = dO V^T ; dS = P * (dP - Delta).
             dp = do_b @ vg.T
             ds = p * (dp - dlt[:, None])
+            if dlse_g is not None:
+                # The LSE's own gradient: d LSE_i / d S_ij = P_ij on the legal entries.
+                ds = ds + p * dlse_g[h, rows][:, None]
             # Stage 3 (dK): dK += scale dS^T Q.
             dk += scale * (ds.T @ q_b)
             # Stage 4 (dQ): dQ = scale dS K.
@@ -222,10 +231,12 @@ def attn_fwd(q, k, v, *, scale: float, causal: bool, bias=None):
     return o, lse
 
 
-def attn_bwd(q, k, v, do, *, scale: float, causal: bool, bias=None):
-    """Dense backward of L = sum(dO * O). Returns (dQ, dK, dV) float64 with the input shapes, and
-    with a bias also dBias with the bias's shape (dS summed over its broadcast dimensions)."""
+def attn_bwd(q, k, v, do, *, scale: float, causal: bool, bias=None, dlse=None):
+    """Dense backward of L = sum(dO * O) (+ sum(dLSE * LSE) when ``dlse`` [B,Hq,Nq] is given).
+    Returns (dQ, dK, dV) float64 with the input shapes, and with a bias also dBias with the bias's
+    shape (dS summed over its broadcast dimensions)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    dl = None if dlse is None else _f64(dlse)
     b, hq, nq, d = q.shape
     hkv = k.shape[1]
     gsz = hq // hkv
@@ -241,7 +252,7 @@ def attn_bwd(q, k, v, do, *, scale: float, causal: bool, bias=None):
         bi, g = it
         sl = slice(g * gsz, (g + 1) * gsz)
         r = group_backward(q[bi, sl], k[bi, g], v[bi, g], do[bi, sl], scale, causal,
-                           None if fb is None else fb[bi, sl])
+                           None if fb is None else fb[bi, sl], None if dl is None else dl[bi, sl])
         return r[:3] + (r[6],)
 
     for (bi, g), (dqg, dkg, dvg, dsg) in zip(items, _map_groups(run, items)):
@@ -293,9 +304,11 @@ def varlen_fwd(q, k, v, cu_q, cu_k, *, scale: float, causal: bool):
     return o, lse
 
 
-def varlen_bwd(q, k, v, do, cu_q, cu_k, *, scale: float, causal: bool):
-    """Packed backward. Returns (dQ [Tq,Hq,D], dK [Tk,Hkv,D], dV [Tk,Hkv,D]) float64."""
+def varlen_bwd(q, k, v, do, cu_q, cu_k, *, scale: float, causal: bool, dlse=None):
+    """Packed backward (``dlse`` None or [Hq,Tq], the LSE's gradient, as in attn_bwd).
+    Returns (dQ [Tq,Hq,D], dK [Tk,Hkv,D], dV [Tk,Hkv,D]) float64."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    dl = None if dlse is None else _f64(dlse)
     tq, hq, d = q.shape
     hkv = k.shape[1]
     gsz = hq // hkv
@@ -311,7 +324,8 @@ def varlen_bwd(q, k, v, do, cu_q, cu_k, *, scale: float, causal: bool):
         sl = slice(g * gsz, (g + 1) * gsz)
         qg = np.transpose(q[q0:q1, sl], (1, 0, 2))
         dog = np.transpose(do[q0:q1, sl], (1, 0, 2))
-        return group_backward(qg, k[k0:k1, g], v[k0:k1, g], dog, scale, causal)[:3]
+        return group_backward(qg, k[k0:k1, g], v[k0:k1, g], dog, scale, causal, None,
+                              None if dl is None else dl[sl, q0:q1])[:3]
 
     for (s, g), (dqg, dkg, dvg) in zip(items, _map_groups(run, items)):
         (q0, q1), (k0, k1) = sq[s], sk[s]

@@ -159,20 +159,26 @@ def test_single_key():
 # ----------------------------------------------------------------------------------------------
 # P-e: gradients against central finite differences of L = sum(dO * O).
 # ----------------------------------------------------------------------------------------------
-def _fd_check(q, k, v, do, scale, causal, varlen=None):
+def _fd_check(q, k, v, do, scale, causal, varlen=None, dlse=None):
+    """Central differences of L = sum(dO * O), plus sum(dLSE * LSE) over the rows with a finite
+    LSE when dlse is given (an empty row's LSE is the constant -inf)."""
     eps = 1e-6
 
     def loss(qq, kk, vv):
         if varlen is None:
-            o, _ = ref.attn_fwd(qq, kk, vv, scale=scale, causal=causal)
+            o, lse = ref.attn_fwd(qq, kk, vv, scale=scale, causal=causal)
         else:
-            o, _ = ref.varlen_fwd(qq, kk, vv, varlen[0], varlen[1], scale=scale, causal=causal)
-        return float(np.sum(do * o))
+            o, lse = ref.varlen_fwd(qq, kk, vv, varlen[0], varlen[1], scale=scale, causal=causal)
+        total = float(np.sum(do * o))
+        if dlse is not None:
+            fin = np.isfinite(lse)
+            total += float(np.sum(dlse[fin] * lse[fin]))
+        return total
 
     if varlen is None:
-        grads = ref.attn_bwd(q, k, v, do, scale=scale, causal=causal)
+        grads = ref.attn_bwd(q, k, v, do, scale=scale, causal=causal, dlse=dlse)
     else:
-        grads = ref.varlen_bwd(q, k, v, do, varlen[0], varlen[1], scale=scale, causal=causal)
+        grads = ref.varlen_bwd(q, k, v, do, varlen[0], varlen[1], scale=scale, causal=causal, dlse=dlse)
     for which, (x, g) in enumerate(zip((q, k, v), grads)):
         num = np.zeros_like(x)
         it = np.nditer(x, flags=["multi_index"])
@@ -219,6 +225,74 @@ def test_fd_varlen():
     do = r.standard_normal((8, 2, 6))
     for causal in (False, True):
         _fd_check(q, k, v, do, 0.6, causal, varlen=(cu_q, cu_k))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fd_lse_gradient_dense(causal):
+    """The returned LSE carries its own gradient: finite differences of sum(dO*O) + sum(g*LSE) on
+    GQA with empty rows (causal, Nq > Nkv)."""
+    r = rng(31)
+    q = r.standard_normal((1, 4, 7, 6))
+    k = r.standard_normal((1, 2, 5, 6))
+    v = r.standard_normal((1, 2, 5, 6))
+    do = r.standard_normal((1, 4, 7, 6))
+    g = r.standard_normal((1, 4, 7))
+    _fd_check(q, k, v, do, 0.45, causal, dlse=g)
+    # With dO = 0 the loss is sum(g * LSE) alone: dV is exactly zero (LSE does not depend on V).
+    _, _, dv = ref.attn_bwd(q, k, v, np.zeros_like(do), scale=0.45, causal=causal, dlse=g)
+    assert np.all(dv == 0.0)
+
+
+def test_fd_lse_gradient_varlen():
+    r = rng(32)
+    cu_q = np.array([0, 3, 3, 8])
+    cu_k = np.array([0, 4, 6, 6])
+    q = r.standard_normal((8, 2, 6))
+    k = r.standard_normal((6, 1, 6))
+    v = r.standard_normal((6, 1, 6))
+    do = r.standard_normal((8, 2, 6))
+    g = r.standard_normal((2, 8))
+    for causal in (False, True):
+        _fd_check(q, k, v, do, 0.6, causal, varlen=(cu_q, cu_k), dlse=g)
+
+
+def test_lse_gradient_closed_form():
+    """dLSE alone on one query: dQ = scale * g * sum_j P_j k_j - which with Q = 0 (uniform P) is
+    scale * g * mean(k); dK_j = scale * g * P_j q = scale * g * q / Nkv."""
+    r = rng(33)
+    nkv, d, scale, g = 5, 4, 0.7, 1.3
+    q = np.zeros((1, 1, 1, d))
+    k = r.standard_normal((1, 1, nkv, d))
+    v = r.standard_normal((1, 1, nkv, d))
+    dq, dk, dv = ref.attn_bwd(q, k, v, np.zeros((1, 1, 1, d)), scale=scale, causal=False,
+                              dlse=np.full((1, 1, 1), g))
+    np.testing.assert_allclose(dq[0, 0, 0], scale * g * k[0, 0].mean(axis=0), atol=1e-14)
+    np.testing.assert_allclose(dk[0, 0], np.zeros((nkv, d)), atol=1e-15)   # q = 0
+    q2 = r.standard_normal((1, 1, 1, d))
+    _, dk2, _ = ref.attn_bwd(q2, np.zeros_like(k), v, np.zeros((1, 1, 1, d)), scale=scale, causal=False,
+                             dlse=np.full((1, 1, 1), g))
+    np.testing.assert_allclose(dk2[0, 0], np.broadcast_to(scale * g * q2[0, 0, 0] / nkv, (nkv, d)), atol=1e-14)
+
+
+def test_lse_gradient_against_torch_autograd():
+    """PyTorch float64 autograd of sum(dO*O) + sum(g*logsumexp(S)) with an explicit bottom-right mask."""
+    r = rng(34)
+    nq, nkv, d, scale = 6, 9, 5, 0.5
+    q = r.standard_normal((1, 2, nq, d))
+    k = r.standard_normal((1, 2, nkv, d))
+    v = r.standard_normal((1, 2, nkv, d))
+    do = r.standard_normal((1, 2, nq, d))
+    g = r.standard_normal((1, 2, nq))
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    legal = torch.tensor(ref.legal_mask(np.arange(nq), nq, nkv, True))
+    s = scale * qt @ kt.transpose(-1, -2)
+    s = s.masked_fill(~legal, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    o = torch.softmax(s, dim=-1) @ vt
+    (torch.sum(torch.tensor(do) * o) + torch.sum(torch.tensor(g) * lse)).backward()
+    got = ref.attn_bwd(q, k, v, do, scale=scale, causal=True, dlse=g)
+    for x, t in zip(got, (qt, kt, vt)):
+        np.testing.assert_allclose(x, t.grad.numpy(), rtol=1e-10, atol=1e-12)
 
 
 # ----------------------------------------------------------------------------------------------
