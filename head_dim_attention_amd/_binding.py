@@ -20,7 +20,8 @@ __all__ = [
     "FFPA_OK", "FFPA_ERR_INVALID_ARGUMENT", "FFPA_ERR_NOT_SUPPORTED", "FFPA_ERR_HIP",
     "library_path", "load_library", "ffpa_status_string",
     "ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd",
-    "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes", "ffpa_decode_fwd",
+    "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes_exact",
+    "ffpa_decode_fwd", "choose_store_ds",
     "ffpa_decode_workspace_bytes", "ffpa_fwd_fp8", "ffpa_fwd_fp8_workspace_bytes", "ffpa_fwd_split_workspace_bytes",
 ]
 
@@ -47,16 +48,17 @@ _SIGNATURES = {
     "ffpa_fwd_masked": [_vp] * 5 + [_i] * 6 + [_vp, _i, _i64p, _i, _f, _i, _vp],
     "ffpa_fwd_fp8": [_vp] * 5 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "ffpa_fwd_split": [_vp] * 5 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
-    "ffpa_bwd_masked": [_vp] * 10 + [_i] * 6 + [_vp, _i, _i64p, _vp, _i, _f, _i, _vp, _sz, _vp],
+    "ffpa_bwd_masked": [_vp] * 11 + [_i] * 6 + [_vp, _i, _i64p, _vp, _i, _f, _i, _vp, _sz, _vp],
     "ffpa_decode_fwd_strided": [_vp] * 5 + [_i] * 6 + [_i64p, _i, _f, _i, _vp, _sz, _vp],
-    "ffpa_bwd": [_vp] * 10 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
-    "ffpa_bwd_stage": [_i] + [_vp] * 10 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
+    "ffpa_bwd": [_vp] * 11 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
+    "ffpa_bwd_stage": [_i] + [_vp] * 11 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "ffpa_varlen_fwd": [_vp] * 7 + [_i] * 9 + [_f, _i, _vp],
-    "ffpa_varlen_bwd": [_vp] * 12 + [_i] * 9 + [_f, _i, _vp, _sz, _vp],
+    "ffpa_varlen_bwd": [_vp] * 15 + [_i] * 9 + [_f, _i, _vp, _sz, _vp],
 }
 _SIZE_FUNCTIONS = {
     "ffpa_bwd_workspace_bytes": [_i] * 4,
     "ffpa_varlen_bwd_workspace_bytes": [_i] * 5,
+    "ffpa_varlen_bwd_workspace_bytes_exact": [_i, _i, _vp, _vp, _i, _i, _i, _i],
     "ffpa_decode_workspace_bytes": [_i] * 6,
     "ffpa_fwd_fp8_workspace_bytes": [_i] * 6,
     "ffpa_fwd_split_workspace_bytes": [_i] * 6,
@@ -352,6 +354,36 @@ def ffpa_varlen_bwd_workspace_bytes(hq: int, total_q: int, total_k: int, max_seq
                                                                int(max_seqlen_q), int(max_seqlen_k)))
 
 
+def ffpa_varlen_bwd_workspace_bytes_exact(hq: int, cu_seqlens_q_host, cu_seqlens_k_host, total_q: int, total_k: int,
+                                          max_seqlen_q: int, max_seqlen_k: int) -> int:
+    """Exact bytes of the varlen P/dS workspace for these (host) cu_seqlens lists (k None: the q
+    ones); 0 when they are invalid or the workspace is not available."""
+    cq = (ctypes.c_int32 * len(cu_seqlens_q_host))(*cu_seqlens_q_host)
+    ck = (ctypes.c_int32 * len(cu_seqlens_k_host))(*cu_seqlens_k_host) if cu_seqlens_k_host is not None else None
+    return int(load_library().ffpa_varlen_bwd_workspace_bytes_exact(
+        int(hq), len(cu_seqlens_q_host) - 1, ctypes.cast(cq, ctypes.c_void_p),
+        ctypes.cast(ck, ctypes.c_void_p) if ck is not None else None, int(total_q), int(total_k),
+        int(max_seqlen_q), int(max_seqlen_k)))
+
+
+# Memory kept free beside a P/dS workspace when the backward decides whether to store P and dS.
+DS_HEADROOM_BYTES = 1 << 30
+
+
+def choose_store_ds(need: int, available: int, headroom: int = DS_HEADROOM_BYTES) -> bool:
+    """Whether the backward stores P and dS: the workspace exists for these sizes (need > 0) and
+    fits in the device memory available to the caller with `headroom` bytes to spare; otherwise
+    the O(N)-memory recomputing kernels run."""
+    return 0 < need and need + headroom <= available
+
+
+def _available_bytes(dev: torch.device) -> int:
+    """Device memory a new allocation can use: free on the device plus what PyTorch's caching
+    allocator holds unused."""
+    free, _ = torch.cuda.mem_get_info(dev)
+    return int(free) + int(torch.cuda.memory_reserved(dev) - torch.cuda.memory_allocated(dev))
+
+
 def _workspace(nbytes: int, like: torch.Tensor):
     """Device workspace of nbytes (None when nbytes is 0), and its size to pass."""
     if nbytes <= 0:
@@ -359,20 +391,36 @@ def _workspace(nbytes: int, like: torch.Tensor):
     return torch.empty(nbytes, dtype=torch.uint8, device=like.device), nbytes
 
 
-def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float] = None, store_ds: bool = True,
-             attn_mask: Optional[torch.Tensor] = None, mask_grad: bool = False):
+def _dlse_arg(dlse, lse):
+    """The LSE gradient as a contiguous float32 tensor shaped like lse, or None."""
+    if dlse is None:
+        return None
+    dlse = _dev(dlse, "dlse")
+    if dlse.shape != lse.shape:
+        raise ValueError(f"dlse must have lse's shape {tuple(lse.shape)}")
+    return dlse.float().contiguous()
+
+
+def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float] = None,
+             store_ds: Optional[bool] = None, attn_mask: Optional[torch.Tensor] = None, mask_grad: bool = False,
+             dlse: Optional[torch.Tensor] = None):
     """Dense backward -> (dq, dk, dv) with the shapes and dtype of q, k, v.
 
-    store_ds: store P and dS in a temporary workspace of ffpa_bwd_workspace_bytes() bytes so that
-    dK = scale dS^T Q, dV = P^T dO and dQ = scale dS K are products instead of recomputations
-    (False: O(N) memory, recompute).
-    attn_mask: the forward's mask (ffpa_bwd_masked, always with the workspace); with mask_grad
-    (additive masks) the result is (dq, dk, dv, dmask), dmask with the mask's shape.
+    store_ds: True stores P and dS in a temporary workspace of ffpa_bwd_workspace_bytes() bytes so
+    that dK = scale dS^T Q, dV = P^T dO and dQ = scale dS K are products instead of
+    recomputations; False recomputes (O(N) memory); None (default) stores them when the workspace
+    fits in the free device memory with DS_HEADROOM_BYTES to spare (choose_store_ds).
+    attn_mask: the forward's mask (ffpa_bwd_masked, always with the workspace: a MemoryError when it
+    does not fit); with mask_grad (additive masks) the result is (dq, dk, dv, dmask), dmask with the
+    mask's shape.
+    dlse: the gradient of the returned LSE (float32, lse's shape) or None; the loss is then
+    sum(dout * o) + sum(dlse * lse).
     """
     if attn_mask is not None:
-        return _bwd_masked(q, k, v, o, dout, lse, causal, scale, attn_mask, mask_grad)
+        return _bwd_masked(q, k, v, o, dout, lse, causal, scale, attn_mask, mask_grad, dlse)
     q, k, v, o, dout = (_dev(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")))
     lse = _dev(lse, "lse")
+    dlse = _dlse_arg(dlse, lse)
     _same(q, k, v, o, dout)
     b, hq, nq, d = q.shape
     _, hkv, nkv, _ = k.shape
@@ -382,17 +430,36 @@ def ffpa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: Optional[float]
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     delta = torch.empty((b, hq, nq), dtype=torch.float32, device=q.device)
-    ws, nws = _workspace(ffpa_bwd_workspace_bytes(b, hq, nq, nkv) if store_ds else 0, q)
-    st = load_library().ffpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
+    need = ffpa_bwd_workspace_bytes(b, hq, nq, nkv)
+    if store_ds is None:
+        store_ds = choose_store_ds(need, _available_bytes(q.device))
+    ws, nws = _workspace(need if store_ds else 0, q)
+    st = load_library().ffpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dlse), _ptr(delta),
                                  _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, nq, nkv, d,
                                  _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(ws), nws, _stream(q))
     _raise_for(st, "ffpa_bwd")
     return dq, dk, dv
 
 
-def _bwd_masked(q, k, v, o, dout, lse, causal, scale, attn_mask, mask_grad):
+def masked_bwd_workspace_check(b: int, hq: int, nq: int, nkv: int, dev: torch.device, available: Optional[int] = None):
+    """The masked backward always stores P and dS: raise MemoryError (before anything is launched
+    or allocated) when its workspace does not fit in the device memory (`available` bytes, default
+    the free memory now)."""
+    need = ffpa_bwd_workspace_bytes(b, hq, nq, nkv)
+    if need == 0:
+        raise NotImplementedError("the attn_mask backward needs a P/dS workspace, which is not available for "
+                                  f"nq={nq}, nkv={nkv} (a head's block above 2^31 bytes)")
+    have = _available_bytes(dev) if available is None else int(available)
+    if need > have:
+        raise MemoryError(f"the attn_mask backward needs a {need / 2**30:.2f} GiB P/dS workspace; "
+                          f"only {have / 2**30:.2f} GiB of device memory is available")
+    return need
+
+
+def _bwd_masked(q, k, v, o, dout, lse, causal, scale, attn_mask, mask_grad, dlse=None):
     q, k, v, o, dout = (_dev(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")))
     lse = _dev(lse, "lse")
+    dlse = _dlse_arg(dlse, lse)
     _same(q, k, v, o, dout)
     b, hq, nq, d = q.shape
     _, hkv, nkv, _ = k.shape
@@ -404,8 +471,9 @@ def _bwd_masked(q, k, v, o, dout, lse, causal, scale, attn_mask, mask_grad):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((b, hq, nq), dtype=torch.float32, device=q.device)
     dm = torch.empty(m.shape4, dtype=q.dtype, device=q.device) if mask_grad else None
-    ws, nws = _workspace(ffpa_bwd_workspace_bytes(b, hq, nq, nkv), q)
-    st = load_library().ffpa_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
+    ws, nws = _workspace(masked_bwd_workspace_check(b, hq, nq, nkv, q.device), q)
+    st = load_library().ffpa_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dlse),
+                                        _ptr(delta),
                                         _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, nq, nkv, d, _ptr(m.tensor),
                                         m.kind, m.strides, _ptr(dm), _dtype_code(q), _scale(scale, d),
                                         int(bool(causal)), _ptr(ws), nws, _stream(q))
@@ -416,15 +484,18 @@ def _bwd_masked(q, k, v, o, dout, lse, causal, scale, attn_mask, mask_grad):
 
 
 def ffpa_bwd_stage(stage: int, q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool = False,
-                   scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+                   scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                   dlse: Optional[torch.Tensor] = None):
     """Run one backward stage (0 preprocess, 4 P and dS, 1 dK, 2 dV, 3 dQ) into caller buffers.
 
     ffpa_bwd runs the stages in the order 0, 4, 1, 2, 3. All tensors must be contiguous GPU tensors
     with ffpa_bwd's shapes; delta is float32 [B,Hq,Nq]. workspace: optional P/dS workspace (a GPU
     tensor of at least ffpa_bwd_workspace_bytes() bytes), the same for stages 4, 1, 2 and 3: stage 4
     fills it (for D > 512 stage 1 does), and stages 1, 2 and 3 read it. Without a workspace stage 4
-    launches nothing and stages 1-3 recompute.
+    launches nothing and stages 1-3 recompute. dlse (stage 0 only reads it): as in ffpa_bwd.
     """
+    if dlse is not None:
+        dlse = _dlse_arg(dlse, lse)
     if workspace is not None and not (isinstance(workspace, torch.Tensor) and workspace.device.type == "cuda"
                                       and workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous GPU tensor")
@@ -436,7 +507,7 @@ def ffpa_bwd_stage(stage: int, q, k, v, o, dout, lse, delta, dq, dk, dv, causal:
     _, hkv, nkv, _ = k.shape
     nws = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load_library().ffpa_bwd_stage(int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                                       _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, nq, nkv, d,
+                                       _ptr(dlse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, nq, nkv, d,
                                        _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(workspace), nws,
                                        _stream(q))
     _raise_for(st, "ffpa_bwd_stage")
@@ -451,11 +522,15 @@ def _check_cu(cu: torch.Tensor, total: int, what: str) -> list[int]:
     return host
 
 
-def _varlen_meta(q, k, cu_q, cu_k, max_q, max_k, validate):
+def _varlen_meta(q, k, cu_q, cu_k, max_q, max_k, validate, host=None):
+    """(cu_k, max_q, max_k, host lists or None). With validate the host copies of cu_seqlens are
+    checked (and returned); ``host`` passes lists the caller already checked."""
     if q.dim() != 3 or k.dim() != 3:
         raise ValueError("varlen expects packed q [Tq,Hq,D] and k, v [Tk,Hkv,D]")
     tq, tk = q.shape[0], k.shape[0]
     if cu_k is None:
+        if tk != tq:
+            raise ValueError("cu_seqlens_k is required when k and q have different total lengths")
         cu_k = cu_q
     if validate:
         hq_ = _check_cu(cu_q, tq, "cu_seqlens_q")
@@ -470,9 +545,10 @@ def _varlen_meta(q, k, cu_q, cu_k, max_q, max_k, validate):
             max_k = max(lk)
         if max(lq) > max_q or max(lk) > max_k:
             raise ValueError("max_seqlen_q / max_seqlen_k smaller than a sequence length")
+        host = (hq_, hk_)
     if max_q is None or max_k is None:
         raise ValueError("max_seqlen_q and max_seqlen_k are required when validate=False")
-    return cu_k, int(max_q), int(max_k)
+    return cu_k, int(max_q), int(max_k), host
 
 
 def ffpa_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
@@ -482,7 +558,7 @@ def ffpa_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None,
     _same(q, k, v)
     cu_q = _dev(cu_seqlens_q, "cu_seqlens_q")
     cu_k = _dev(cu_seqlens_k, "cu_seqlens_k") if cu_seqlens_k is not None else None
-    cu_k, max_q, max_k = _varlen_meta(q, k, cu_q, cu_k, max_seqlen_q, max_seqlen_k, validate)
+    cu_k, max_q, max_k, _ = _varlen_meta(q, k, cu_q, cu_k, max_seqlen_q, max_seqlen_k, validate)
     tq, hq, d = q.shape
     tk, hkv, _ = k.shape
     o = torch.empty_like(q)
@@ -496,26 +572,43 @@ def ffpa_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None,
 
 def ffpa_varlen_bwd(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None,
                     max_seqlen_k=None, causal: bool = False, scale: Optional[float] = None,
-                    validate: bool = True, store_ds: bool = True):
-    """Packed backward -> (dq [Tq,Hq,D], dk [Tk,Hkv,D], dv [Tk,Hkv,D]). store_ds as in ffpa_bwd."""
+                    validate: bool = True, store_ds: Optional[bool] = None, dlse: Optional[torch.Tensor] = None,
+                    cu_seqlens_host=None):
+    """Packed backward -> (dq [Tq,Hq,D], dk [Tk,Hkv,D], dv [Tk,Hkv,D]). store_ds and dlse ([Hq,Tq])
+    as in ffpa_bwd. With host copies of cu_seqlens (validate=True makes them, or pass
+    cu_seqlens_host=(list_q, list_k) already checked) the P/dS workspace has the exact size of these
+    sequences (ffpa_varlen_bwd_workspace_bytes_exact) instead of the bound for any lengths."""
     q, k, v, o, dout = (_dev(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")))
     lse = _dev(lse, "lse")
     _same(q, k, v, o, dout)
     cu_q = _dev(cu_seqlens_q, "cu_seqlens_q")
     cu_k = _dev(cu_seqlens_k, "cu_seqlens_k") if cu_seqlens_k is not None else None
-    cu_k, max_q, max_k = _varlen_meta(q, k, cu_q, cu_k, max_seqlen_q, max_seqlen_k, validate)
+    cu_k, max_q, max_k, host = _varlen_meta(q, k, cu_q, cu_k, max_seqlen_q, max_seqlen_k, validate,
+                                            cu_seqlens_host)
     tq, hq, d = q.shape
     tk, hkv, _ = k.shape
     if o.shape != q.shape or dout.shape != q.shape or lse.shape != (hq, tq) or lse.dtype != torch.float32:
         raise ValueError("o and dout must match q; lse must be float32 [Hq,Tq]")
+    dlse = _dlse_arg(dlse, lse)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     delta = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
-    ws, nws = _workspace(ffpa_varlen_bwd_workspace_bytes(hq, tq, tk, max_q, max_k) if store_ds else 0, q)
-    st = load_library().ffpa_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
-                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_q), _ptr(cu_k), cu_q.numel() - 1,
-                                        max_q, max_k, tq, tk, hq, hkv, d, _dtype_code(q), _scale(scale, d),
-                                        int(bool(causal)), _ptr(ws), nws, _stream(q))
+    hq_arr = hk_arr = None
+    if host is not None:
+        hq_arr = (ctypes.c_int32 * len(host[0]))(*host[0])
+        hk_arr = (ctypes.c_int32 * len(host[1]))(*host[1])
+        need = ffpa_varlen_bwd_workspace_bytes_exact(hq, host[0], host[1], tq, tk, max_q, max_k)
+    else:
+        need = ffpa_varlen_bwd_workspace_bytes(hq, tq, tk, max_q, max_k)
+    if store_ds is None:
+        store_ds = choose_store_ds(need, _available_bytes(q.device))
+    ws, nws = _workspace(need if store_ds else 0, q)
+    vp = lambda a: ctypes.cast(a, ctypes.c_void_p) if a is not None else ctypes.c_void_p(0)
+    st = load_library().ffpa_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dlse),
+                                        _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_q), _ptr(cu_k),
+                                        vp(hq_arr), vp(hk_arr), cu_q.numel() - 1, max_q, max_k, tq, tk, hq, hkv,
+                                        d, _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(ws), nws,
+                                        _stream(q))
     _raise_for(st, "ffpa_varlen_bwd")
     return dq, dk, dv

@@ -25,7 +25,13 @@ DECODE_MAX_NQ = 8
 class _FFPAAttn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, causal, scale, mask):
+        ctx.set_materialize_grads(False)  # an unused O or LSE gets None, not a zero tensor
         if mask is not None:
+            if any(ctx.needs_input_grad[:3]):
+                # The masked backward stores P and dS: fail before the forward when its workspace
+                # can never fit on this device.
+                total = torch.cuda.get_device_properties(q.device).total_memory
+                B.masked_bwd_workspace_check(q.shape[0], q.shape[1], q.shape[2], k.shape[2], q.device, total)
             o, lse = B.ffpa_fwd(q, k, v, causal=causal, scale=scale, attn_mask=mask)
         else:
             fwd = B.ffpa_decode_fwd if q.shape[2] < DECODE_MAX_NQ else B.ffpa_fwd
@@ -36,29 +42,40 @@ class _FFPAAttn(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, do, dlse):
+        # The returned LSE is differentiable: its gradient enters the preprocess stage
+        # (delta = rowsum(dO * O) - dLSE) inside the library.
         q, k, v, o, lse, mask = ctx.saved_tensors
+        if do is None:
+            do = torch.zeros_like(o)
         if mask is None:
-            dq, dk, dv = B.ffpa_bwd(q, k, v, o, do, lse, causal=ctx.causal, scale=ctx.scale)
+            dq, dk, dv = B.ffpa_bwd(q, k, v, o, do, lse, causal=ctx.causal, scale=ctx.scale, dlse=dlse)
             return dq, dk, dv, None, None, None
         want = ctx.needs_input_grad[5] and mask.dtype != torch.bool
-        g = B.ffpa_bwd(q, k, v, o, do, lse, causal=ctx.causal, scale=ctx.scale, attn_mask=mask, mask_grad=want)
+        g = B.ffpa_bwd(q, k, v, o, do, lse, causal=ctx.causal, scale=ctx.scale, attn_mask=mask, mask_grad=want,
+                       dlse=dlse)
         return g[0], g[1], g[2], None, None, (g[3] if want else None)
 
 
 class _FFPAVarlen(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, cu_q, cu_k, max_q, max_k, causal, scale):
+        ctx.set_materialize_grads(False)
         o, lse = B.ffpa_varlen_fwd(q, k, v, cu_q, cu_k, max_q, max_k, causal=causal, scale=scale)
         ctx.save_for_backward(q, k, v, o, lse, cu_q, cu_k)
-        ctx.meta = (max_q, max_k, causal, scale)
+        # Host copies of the (validated) lengths size the backward's P/dS workspace exactly.
+        host = (cu_q.detach().to("cpu").tolist(), cu_k.detach().to("cpu").tolist()) if any(ctx.needs_input_grad[:3]) \
+            else None
+        ctx.meta = (max_q, max_k, causal, scale, host)
         return o, lse
 
     @staticmethod
     def backward(ctx, do, dlse):
         q, k, v, o, lse, cu_q, cu_k = ctx.saved_tensors
-        max_q, max_k, causal, scale = ctx.meta
+        max_q, max_k, causal, scale, host = ctx.meta
+        if do is None:
+            do = torch.zeros_like(o)
         dq, dk, dv = B.ffpa_varlen_bwd(q, k, v, o, do, lse, cu_q, cu_k, max_q, max_k, causal=causal,
-                                       scale=scale, validate=False)
+                                       scale=scale, validate=False, dlse=dlse, cu_seqlens_host=host)
         return dq, dk, dv, None, None, None, None, None, None
 
 

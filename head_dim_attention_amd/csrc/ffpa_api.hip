@@ -25,7 +25,7 @@ namespace {
 bool bad_dtype(int dtype) { return dtype != FFPA_DTYPE_BF16 && dtype != FFPA_DTYPE_FP16; }
 
 // Shared checks of every entry point; NOT_SUPPORTED is reported only for otherwise valid calls.
-int check_common(int hq, int hkv, int d, int dtype, float scale, int causal) {
+ffpa_status_t check_common(int hq, int hkv, int d, int dtype, float scale, int causal) {
   if (hq < 1 || hkv < 1 || hq % hkv != 0) return FFPA_ERR_INVALID_ARGUMENT;
   if (bad_dtype(dtype)) return FFPA_ERR_INVALID_ARGUMENT;
   if (causal != 0 && causal != 1) return FFPA_ERR_INVALID_ARGUMENT;
@@ -90,7 +90,7 @@ AttnParams varlen_params(int batch, int max_q, int max_k, int total_q, int hq, i
   return p;
 }
 
-int to_status(hipError_t e) { return e == hipSuccess ? FFPA_OK : FFPA_ERR_HIP; }
+ffpa_status_t to_status(hipError_t e) { return e == hipSuccess ? FFPA_OK : FFPA_ERR_HIP; }
 
 // Sizes in elements must stay addressable with the kernels' 32-bit row/head arithmetic.
 bool too_big_dense(int batch, int h, int n, int d) {
@@ -117,11 +117,34 @@ size_t varlen_ds_bytes(int hq, int total_q, int total_k, int max_q, int max_k) {
   return 2 * (size_t)hq * total_k * round_up8(max_q) * 2;
 }
 
+// Host copies of cu_seqlens (k NULL: the q ones) that follow the rules of the varlen entry points
+// for these totals and max lengths: batch + 1 entries from 0, non-decreasing, ending at the totals,
+// every length at most the max length.
+bool host_cu_ok(int batch, const int32_t* cu, int total, int max_len) {
+  if (cu == nullptr || batch < 1 || cu[0] != 0 || cu[batch] != total) return false;
+  for (int s = 0; s < batch; ++s)
+    if (cu[s + 1] < cu[s] || cu[s + 1] - cu[s] > max_len) return false;
+  return true;
+}
+
+// Exact P/dS workspace of these sequences: two blocks of hq * sum_s Lk_s * round_up8(Lq_s)
+// elements (the layout the kernels address, sequence by sequence), or 0 when not available.
+size_t varlen_ds_bytes_exact(int hq, int batch, const int32_t* cu_q, const int32_t* cu_k, int total_q, int total_k,
+                             int max_q, int max_k) {
+  if (cu_k == nullptr) cu_k = cu_q;
+  if (hq < 1 || total_q < 1 || total_k < 1 || max_q < 1 || max_k < 1 || !ds_block_ok(max_q, max_k)) return 0;
+  if (!host_cu_ok(batch, cu_q, total_q, max_q) || !host_cu_ok(batch, cu_k, total_k, max_k)) return 0;
+  if (cu_k == cu_q && total_k != total_q) return 0;
+  long long elems = 0;
+  for (int s = 0; s < batch; ++s) elems += (long long)(cu_k[s + 1] - cu_k[s]) * round_up8(cu_q[s + 1] - cu_q[s]);
+  return elems == 0 ? 0 : 2 * (size_t)hq * (size_t)elems * 2;
+}
+
 // Strided forward layouts: strides[12] = {q, k, v, o} x {batch, head, row} in elements (the head
 // dim is contiguous). Rows must stay 16-byte aligned (strides multiples of 8 elements, 16-byte
 // aligned base pointers), strides non-negative, and one head's rows addressable with the kernels'
 // 32-bit row arithmetic.
-int apply_strides(AttnParams& p, const int64_t* st, const void* q, const void* k, const void* v, const void* o,
+ffpa_status_t apply_strides(AttnParams& p, const int64_t* st, const void* q, const void* k, const void* v, const void* o,
                   int nq, int nkv, int d) {
   if (st == nullptr) return FFPA_ERR_INVALID_ARGUMENT;
   for (const void* ptr : {q, k, v, o})
@@ -156,7 +179,7 @@ int apply_strides(AttnParams& p, const int64_t* st, const void* q, const void* k
 // (batch, head, query, key) in elements, non-negative, key stride 0 or 1; with a contiguous key
 // dim the other strides are multiples of 8 and the pointer is 16-byte (additive) or 8-byte
 // (boolean) aligned, so that 8 keys are one aligned load.
-int apply_mask(AttnParams& p, const void* mask, int kind, const int64_t* st, float scale) {
+ffpa_status_t apply_mask(AttnParams& p, const void* mask, int kind, const int64_t* st, float scale) {
   if (mask == nullptr || st == nullptr || (kind != FFPA_MASK_ADDITIVE && kind != FFPA_MASK_BOOL))
     return FFPA_ERR_INVALID_ARGUMENT;
   for (int i = 0; i < 4; ++i)
@@ -208,7 +231,7 @@ size_t decode_ws_bytes(int batch, int hq, int hkv, int nq, int nkv, int d) {
 // Attach a caller workspace for dS and P. NULL selects the recomputing dV and dQ kernels; a
 // workspace smaller than `need` is an invalid argument; need == 0 (not available for these sizes)
 // ignores it.
-int attach_ds(AttnParams& p, void* ws, size_t ws_bytes, size_t need) {
+ffpa_status_t attach_ds(AttnParams& p, void* ws, size_t ws_bytes, size_t need) {
   if (ws == nullptr || need == 0) return FFPA_OK;
   if (ws_bytes < need) return FFPA_ERR_INVALID_ARGUMENT;
   p.ds = ws;
@@ -220,17 +243,17 @@ int attach_ds(AttnParams& p, void* ws, size_t ws_bytes, size_t need) {
 
 extern "C" {
 
-static int dense_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+static ffpa_status_t dense_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
                      int nq, int nkv, int d, const int64_t* strides, int dtype, float scale, int causal,
-                     void* stream) {
+                     hipStream_t stream) {
   if (!q || !k || !v || !o || !lse) return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
-  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  const ffpa_status_t st = check_common(hq, hkv, d, dtype, scale, causal);
   if (st != FFPA_OK) return st;
   if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
   AttnParams p = dense_params(batch, hq, hkv, nq, nkv, d, scale, causal);
   if (strides != nullptr) {
-    const int sst = apply_strides(p, strides, q, k, v, o, nq, nkv, d);
+    const ffpa_status_t sst = apply_strides(p, strides, q, k, v, o, nq, nkv, d);
     if (sst != FFPA_OK) return sst;
   }
   p.q = q;
@@ -238,11 +261,11 @@ static int dense_fwd(const void* q, const void* k, const void* v, void* o, float
   p.v = v;
   p.o = o;
   p.lse = lse;
-  return to_status(ffpa::launch_fwd(p, dtype == FFPA_DTYPE_FP16, (hipStream_t)stream));
+  return to_status(ffpa::launch_fwd(p, dtype == FFPA_DTYPE_FP16, stream));
 }
 
-int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
-             int nq, int nkv, int d, int dtype, float scale, int causal, void* stream) {
+ffpa_status_t ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+             int nq, int nkv, int d, ffpa_dtype_t dtype, float scale, int causal, hipStream_t stream) {
   return dense_fwd(q, k, v, o, lse, batch, hq, hkv, nq, nkv, d, nullptr, dtype, scale, causal, stream);
 }
 
@@ -259,13 +282,13 @@ size_t ffpa_fwd_split_workspace_bytes(int batch, int hq, int hkv, int nq, int nk
   return fwd_split_ws_bytes(batch, hq, hkv, nq, nkv, d);
 }
 
-int ffpa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
-                   int nq, int nkv, int d, int dtype, float scale, int causal, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+ffpa_status_t ffpa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                   int nq, int nkv, int d, ffpa_dtype_t dtype, float scale, int causal, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
   const size_t need = fwd_split_ws_bytes(batch, hq, hkv, nq, nkv, d);
   if (need == 0) return dense_fwd(q, k, v, o, lse, batch, hq, hkv, nq, nkv, d, nullptr, dtype, scale, causal, stream);
   if (!q || !k || !v || !o || !lse || !workspace) return FFPA_ERR_INVALID_ARGUMENT;
-  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  const ffpa_status_t st = check_common(hq, hkv, d, dtype, scale, causal);
   if (st != FFPA_OK) return st;
   if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
   if ((long long)batch * hq * nq > (1LL << 31) - 1) return FFPA_ERR_INVALID_ARGUMENT;
@@ -277,26 +300,26 @@ int ffpa_fwd_split(const void* q, const void* k, const void* v, void* o, float* 
   p.o = o;
   p.lse = lse;
   return to_status(ffpa::launch_fwd_split(p, dtype == FFPA_DTYPE_FP16,
-                                          ffpa::fwd_split_count(batch, hq, nq, nkv, d), workspace, (hipStream_t)stream));
+                                          ffpa::fwd_split_count(batch, hq, nq, nkv, d), workspace, stream));
 }
 
-int ffpa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
-                    int nq, int nkv, int d, const void* mask, int mask_kind, const int64_t* mask_strides,
-                    int dtype, float scale, int causal, void* stream) {
+ffpa_status_t ffpa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                    int nq, int nkv, int d, const void* mask, ffpa_mask_kind_t mask_kind, const int64_t* mask_strides,
+                    ffpa_dtype_t dtype, float scale, int causal, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse) return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
-  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  const ffpa_status_t st = check_common(hq, hkv, d, dtype, scale, causal);
   if (st != FFPA_OK) return st;
   if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
   AttnParams p = dense_params(batch, hq, hkv, nq, nkv, d, scale, causal);
-  const int ms = apply_mask(p, mask, mask_kind, mask_strides, scale);
+  const ffpa_status_t ms = apply_mask(p, mask, mask_kind, mask_strides, scale);
   if (ms != FFPA_OK) return ms;
   p.q = q;
   p.k = k;
   p.v = v;
   p.o = o;
   p.lse = lse;
-  return to_status(ffpa::launch_fwd(p, dtype == FFPA_DTYPE_FP16, (hipStream_t)stream));
+  return to_status(ffpa::launch_fwd(p, dtype == FFPA_DTYPE_FP16, stream));
 }
 
 size_t ffpa_fwd_fp8_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, int d) {
@@ -305,12 +328,12 @@ size_t ffpa_fwd_fp8_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv,
   return ffpa::fp8_workspace_bytes(batch, hq, hkv, nkv, d);
 }
 
-int ffpa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
-                 int nq, int nkv, int d, int dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+ffpa_status_t ffpa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                 int nq, int nkv, int d, ffpa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !workspace) return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
-  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  const ffpa_status_t st = check_common(hq, hkv, d, dtype, scale, causal);
   if (st != FFPA_OK) return st;
   // (the quantizing passes put batch x heads in one grid dimension)
   if (d > 512 || (long long)batch * hq > 65535) return FFPA_ERR_NOT_SUPPORTED;
@@ -324,24 +347,26 @@ int ffpa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
   p.v = v;
   p.o = o;
   p.lse = lse;
-  return to_status(ffpa::launch_fwd_fp8(p, dtype == FFPA_DTYPE_FP16, workspace, (hipStream_t)stream));
+  return to_status(ffpa::launch_fwd_fp8(p, dtype == FFPA_DTYPE_FP16, workspace, stream));
 }
 
-int ffpa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
-                     int nq, int nkv, int d, const int64_t* strides, int dtype, float scale, int causal,
-                     void* stream) {
+ffpa_status_t ffpa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                     int nq, int nkv, int d, const int64_t* strides, ffpa_dtype_t dtype, float scale, int causal,
+                     hipStream_t stream) {
   if (strides == nullptr) return FFPA_ERR_INVALID_ARGUMENT;
   return dense_fwd(q, k, v, o, lse, batch, hq, hkv, nq, nkv, d, strides, dtype, scale, causal, stream);
 }
 
-int ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
+ffpa_status_t ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
                     const int32_t* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k, int total_q,
-                    int total_k, int hq, int hkv, int d, int dtype, float scale, int causal, void* stream) {
+                    int total_k, int hq, int hkv, int d, ffpa_dtype_t dtype, float scale, int causal, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !cu_seqlens_q) return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
     return FFPA_ERR_INVALID_ARGUMENT;
   if (max_seqlen_q > total_q || max_seqlen_k > total_k) return FFPA_ERR_INVALID_ARGUMENT;
-  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  // Keys share the query offsets: both sides must have the same total.
+  if (cu_seqlens_k == nullptr && total_k != total_q) return FFPA_ERR_INVALID_ARGUMENT;
+  const ffpa_status_t st = check_common(hq, hkv, d, dtype, scale, causal);
   if (st != FFPA_OK) return st;
   if ((long long)total_q * hq * d > (1LL << 31) - 1 || (long long)total_k * hkv * d > (1LL << 31) - 1)
     return FFPA_ERR_INVALID_ARGUMENT;
@@ -353,18 +378,18 @@ int ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float*
   p.v = v;
   p.o = o;
   p.lse = lse;
-  return to_status(ffpa::launch_fwd(p, dtype == FFPA_DTYPE_FP16, (hipStream_t)stream));
+  return to_status(ffpa::launch_fwd(p, dtype == FFPA_DTYPE_FP16, stream));
 }
 
-static int dense_bwd(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
-                     const float* lse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv,
+static ffpa_status_t dense_bwd(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, const float* dlse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv,
                      int nq, int nkv, int d, int dtype, float scale, int causal, void* workspace,
-                     size_t workspace_bytes, void* stream, const void* mask = nullptr, int mask_kind = 0,
+                     size_t workspace_bytes, hipStream_t stream, const void* mask = nullptr, int mask_kind = 0,
                      const int64_t* mask_strides = nullptr, void* dmask = nullptr) {
   if (stage < -1 || stage > 4) return FFPA_ERR_INVALID_ARGUMENT;
   if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
-  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  const ffpa_status_t st = check_common(hq, hkv, d, dtype, scale, causal);
   if (st != FFPA_OK) return st;
   if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
   const long long nrows = (long long)batch * hq * nq;
@@ -376,21 +401,22 @@ static int dense_bwd(int stage, const void* q, const void* k, const void* v, con
   p.o_in = o;
   p.dout = dout;
   p.lse_in = lse;
+  p.dlse = dlse;
   p.delta = delta;
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  const int ws = attach_ds(p, workspace, workspace_bytes, dense_ds_bytes(batch, hq, nq, nkv));
+  const ffpa_status_t ws = attach_ds(p, workspace, workspace_bytes, dense_ds_bytes(batch, hq, nq, nkv));
   if (ws != FFPA_OK) return ws;
   if (mask != nullptr || mask_kind != 0) {
-    const int ms = apply_mask(p, mask, mask_kind, mask_strides, scale);
+    const ffpa_status_t ms = apply_mask(p, mask, mask_kind, mask_strides, scale);
     if (ms != FFPA_OK) return ms;
     p.dmask = dmask;
   }
   p.ds_row = (int)round_up8(nq);
   p.ds_head = (long long)nkv * p.ds_row;
   p.ds_batch = (long long)hq * p.ds_head;
-  return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, (int)nrows, 0, (hipStream_t)stream, stage));
+  return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, (int)nrows, 0, stream, stage));
 }
 
 size_t ffpa_bwd_workspace_bytes(int batch, int hq, int nq, int nkv) { return dense_ds_bytes(batch, hq, nq, nkv); }
@@ -399,12 +425,12 @@ size_t ffpa_decode_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, 
   return decode_ws_bytes(batch, hq, hkv, nq, nkv, d);
 }
 
-static int decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+static ffpa_status_t decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
                       int nq, int nkv, int d, const int64_t* strides, int dtype, float scale, int causal,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !workspace) return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
-  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  const ffpa_status_t st = check_common(hq, hkv, d, dtype, scale, causal);
   if (st != FFPA_OK) return st;
   if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
   if ((long long)batch * hq * nq > (1LL << 31) - 1) return FFPA_ERR_INVALID_ARGUMENT;
@@ -412,7 +438,7 @@ static int decode_fwd(const void* q, const void* k, const void* v, void* o, floa
   if (workspace_bytes < need) return FFPA_ERR_INVALID_ARGUMENT;
   AttnParams p = dense_params(batch, hq, hkv, nq, nkv, d, scale, causal);
   if (strides != nullptr) {
-    const int sst = apply_strides(p, strides, q, k, v, o, nq, nkv, d);
+    const ffpa_status_t sst = apply_strides(p, strides, q, k, v, o, nq, nkv, d);
     if (sst != FFPA_OK) return sst;
   }
   p.q = q;
@@ -427,19 +453,19 @@ static int decode_fwd(const void* q, const void* k, const void* v, void* o, floa
   p.split_tiles = g.split_tiles;
   p.part_o = (float*)workspace;
   p.part_lse = (float*)workspace + (size_t)batch * hq * nq * g.nsplit * d;
-  return to_status(ffpa::launch_decode(p, dtype == FFPA_DTYPE_FP16, (hipStream_t)stream));
+  return to_status(ffpa::launch_decode(p, dtype == FFPA_DTYPE_FP16, stream));
 }
 
-int ffpa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
-                    int nq, int nkv, int d, int dtype, float scale, int causal, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+ffpa_status_t ffpa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                    int nq, int nkv, int d, ffpa_dtype_t dtype, float scale, int causal, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
   return decode_fwd(q, k, v, o, lse, batch, hq, hkv, nq, nkv, d, nullptr, dtype, scale, causal, workspace,
                     workspace_bytes, stream);
 }
 
-int ffpa_decode_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq,
-                            int hkv, int nq, int nkv, int d, const int64_t* strides, int dtype, float scale,
-                            int causal, void* workspace, size_t workspace_bytes, void* stream) {
+ffpa_status_t ffpa_decode_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq,
+                            int hkv, int nq, int nkv, int d, const int64_t* strides, ffpa_dtype_t dtype, float scale,
+                            int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (strides == nullptr) return FFPA_ERR_INVALID_ARGUMENT;
   return decode_fwd(q, k, v, o, lse, batch, hq, hkv, nq, nkv, d, strides, dtype, scale, causal, workspace,
                     workspace_bytes, stream);
@@ -449,52 +475,70 @@ size_t ffpa_varlen_bwd_workspace_bytes(int hq, int total_q, int total_k, int max
   return varlen_ds_bytes(hq, total_q, total_k, max_seqlen_q, max_seqlen_k);
 }
 
-int ffpa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                    float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq, int nkv, int d,
-                    const void* mask, int mask_kind, const int64_t* mask_strides, void* dmask, int dtype,
-                    float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+ffpa_status_t ffpa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    const float* dlse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq, int nkv, int d,
+                    const void* mask, ffpa_mask_kind_t mask_kind, const int64_t* mask_strides, void* dmask, ffpa_dtype_t dtype,
+                    float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (workspace == nullptr) return FFPA_ERR_INVALID_ARGUMENT;
   if (dense_ds_bytes(batch, hq, nq, nkv) == 0 && batch >= 1 && hq >= 1 && nq >= 1 && nkv >= 1)
     return FFPA_ERR_NOT_SUPPORTED;  // a head's P/dS block is too large for the stored path
   if (dmask != nullptr && mask_kind != FFPA_MASK_ADDITIVE) return FFPA_ERR_INVALID_ARGUMENT;
-  return dense_bwd(-1, q, k, v, o, dout, lse, delta, dq, dk, dv, batch, hq, hkv, nq, nkv, d, dtype, scale, causal,
-                   workspace, workspace_bytes, stream, mask, mask_kind, mask_strides, dmask);
+  return dense_bwd(-1, q, k, v, o, dout, lse, dlse, delta, dq, dk, dv, batch, hq, hkv, nq, nkv, d, dtype, scale,
+                   causal, workspace, workspace_bytes, stream, mask, mask_kind, mask_strides, dmask);
 }
 
-int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-             float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq, int nkv, int d,
-             int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
-  return dense_bwd(-1, q, k, v, o, dout, lse, delta, dq, dk, dv, batch, hq, hkv, nq, nkv, d, dtype, scale, causal,
-                   workspace, workspace_bytes, stream);
+ffpa_status_t ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             const float* dlse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq, int nkv, int d,
+             ffpa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return dense_bwd(-1, q, k, v, o, dout, lse, dlse, delta, dq, dk, dv, batch, hq, hkv, nq, nkv, d, dtype, scale,
+                   causal, workspace, workspace_bytes, stream);
 }
 
-int ffpa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
-                   const float* lse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq,
-                   int nkv, int d, int dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+ffpa_status_t ffpa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, const float* dlse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq,
+                   int nkv, int d, ffpa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
   if (stage < 0 || stage > 4) return FFPA_ERR_INVALID_ARGUMENT;
-  return dense_bwd(stage, q, k, v, o, dout, lse, delta, dq, dk, dv, batch, hq, hkv, nq, nkv, d, dtype, scale, causal,
-                   workspace, workspace_bytes, stream);
+  return dense_bwd(stage, q, k, v, o, dout, lse, dlse, delta, dq, dk, dv, batch, hq, hkv, nq, nkv, d, dtype, scale,
+                   causal, workspace, workspace_bytes, stream);
 }
 
-int ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                    float* delta, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
-                    const int32_t* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k, int total_q,
-                    int total_k, int hq, int hkv, int d, int dtype, float scale, int causal, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+size_t ffpa_varlen_bwd_workspace_bytes_exact(int hq, int batch, const int32_t* cu_seqlens_q_host,
+                                             const int32_t* cu_seqlens_k_host, int total_q, int total_k,
+                                             int max_seqlen_q, int max_seqlen_k) {
+  return varlen_ds_bytes_exact(hq, batch, cu_seqlens_q_host, cu_seqlens_k_host, total_q, total_k, max_seqlen_q,
+                               max_seqlen_k);
+}
+
+ffpa_status_t ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, const float* dlse, float* delta, void* dq, void* dk, void* dv,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_k_host, int batch,
+                              int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int hq, int hkv, int d,
+                              ffpa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
   if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv || !cu_seqlens_q)
     return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
     return FFPA_ERR_INVALID_ARGUMENT;
   if (max_seqlen_q > total_q || max_seqlen_k > total_k) return FFPA_ERR_INVALID_ARGUMENT;
-  const int st = check_common(hq, hkv, d, dtype, scale, causal);
+  if (cu_seqlens_k == nullptr && total_k != total_q) return FFPA_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens_k_host != nullptr && cu_seqlens_q_host == nullptr) return FFPA_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens_q_host != nullptr) {
+    // Host copies are checked here; the device contents must equal them.
+    if (!host_cu_ok(batch, cu_seqlens_q_host, total_q, max_seqlen_q)) return FFPA_ERR_INVALID_ARGUMENT;
+    if (!host_cu_ok(batch, cu_seqlens_k_host != nullptr ? cu_seqlens_k_host : cu_seqlens_q_host, total_k,
+                    max_seqlen_k))
+      return FFPA_ERR_INVALID_ARGUMENT;
+  }
+  const ffpa_status_t st = check_common(hq, hkv, d, dtype, scale, causal);
   if (st != FFPA_OK) return st;
   if ((long long)total_q * hq * d > (1LL << 31) - 1 || (long long)total_k * hkv * d > (1LL << 31) - 1)
     return FFPA_ERR_INVALID_ARGUMENT;
   if (total_k == 0 || max_seqlen_k == 0) {
     // No keys at all: dK and dV are empty, every query row is empty and gets dQ = 0.
     if (total_q > 0) {
-      const hipError_t e = hipMemsetAsync(dq, 0, (size_t)total_q * hq * d * 2, (hipStream_t)stream);
+      const hipError_t e = hipMemsetAsync(dq, 0, (size_t)total_q * hq * d * 2, stream);
       if (e != hipSuccess) return FFPA_ERR_HIP;
     }
     return FFPA_OK;
@@ -507,16 +551,23 @@ int ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, 
   p.o_in = o;
   p.dout = dout;
   p.lse_in = lse;
+  p.dlse = dlse;
   p.delta = delta;
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  const int ws = attach_ds(p, workspace, workspace_bytes, varlen_ds_bytes(hq, total_q, total_k, max_seqlen_q, max_seqlen_k));
+  // With host copies the workspace needs only the exact size of these sequences; the P block
+  // then starts at half of that size (both blocks are equal).
+  const size_t need = cu_seqlens_q_host != nullptr
+                          ? varlen_ds_bytes_exact(hq, batch, cu_seqlens_q_host, cu_seqlens_k_host, total_q, total_k,
+                                                  max_seqlen_q, max_seqlen_k)
+                          : varlen_ds_bytes(hq, total_q, total_k, max_seqlen_q, max_seqlen_k);
+  const ffpa_status_t ws = attach_ds(p, workspace, workspace_bytes, need);
   if (ws != FFPA_OK) return ws;
-  return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, total_q * hq, total_q, (hipStream_t)stream, -1));
+  return to_status(ffpa::launch_bwd(p, dtype == FFPA_DTYPE_FP16, total_q * hq, total_q, stream, -1));
 }
 
-const char* ffpa_status_string(int status) {
+const char* ffpa_status_string(ffpa_status_t status) {
   switch (status) {
     case FFPA_OK: return "FFPA_OK";
     case FFPA_ERR_INVALID_ARGUMENT: return "FFPA_ERR_INVALID_ARGUMENT: invalid argument";

@@ -28,34 +28,26 @@
 #include "ffpa_params.h"
 
 namespace ffpa {
+// Fixed pipelining and cache-policy constants of the backward kernels (measured choices).
 // MFMAs whose LDS operands are requested ahead of the one issuing (see pin_lds_mfma_pipeline).
-#ifndef BWD_AHEAD
-#define BWD_AHEAD 2
-#endif
+constexpr int kBwdAhead = 2;
 // Cache policy of the dS and P stores (written once, read once by the dQ and dV passes):
 // non-temporal, system scope (nt sc1), the fastest of the policies measured for this pattern.
-#ifndef DS_STORE_CPOL
-#define DS_STORE_CPOL 18
-#endif
+constexpr int kDsStoreCpol = 18;
 // LDS reads requested ahead of the MFMA issuing in the dQ-from-dS and dV-from-P products (each
 // A operand is two transposed reads used by two MFMAs).
-#ifndef PROD_AHEAD
-#define PROD_AHEAD 6
-#endif
-// Depth of the product passes' tile rings (copies are issued PROD_NBUF - 1 steps ahead).
-#ifndef PROD_NBUF
-#define PROD_NBUF 3
-#endif
-// Same, for the two-group dK/dQ kernel, whose MFMA phases run one wave per SIMD at a time.
-#ifndef PP_AHEAD_M1
-#define PP_AHEAD_M1 2
-#endif
-#ifndef PP_AHEAD_M2
-#define PP_AHEAD_M2 2
-#endif
+constexpr int kProdAhead = 6;
+// Depth of the product passes' tile rings (copies are issued kProdNbuf - 1 steps ahead).
+constexpr int kProdNbuf = 3;
+// Same as kBwdAhead, for the two MFMA phases of the two-group dK/dQ kernel, whose MFMA phases run
+// one wave per SIMD at a time.
+constexpr int kPpAheadM1 = 2;
+constexpr int kPpAheadM2 = 2;
 
 // ------------------------------------------------------------------------------------------------
-// Stage 1: Delta = rowsum(dO * O) in fp32 from the stored (rounded) O.
+// Stage 1: Delta = rowsum(dO * O) in fp32 from the stored (rounded) O, minus the gradient of the
+// returned LSE when there is one: d LSE_i / d S_ij = P_ij, so a loss term g_i LSE_i adds g_i P_ij to
+// dS = P (dP - Delta), which is the same as Delta_i - g_i in place of Delta_i.
 // One wave per row, 8 elements (16 bytes) per lane per step, 4 rows per wave.
 // ------------------------------------------------------------------------------------------------
 template <class T>
@@ -97,7 +89,7 @@ __global__ void __launch_bounds__(256) ffpa_bwd_preprocess_kernel(AttnParams p, 
     if (lane == 0 && row < nrows) {
       // Dense rows are ordered (b, h, n) like Delta; packed rows are (t, h) and Delta is [H, T].
       const long long idx = varlen_total > 0 ? (row % p.hq) * varlen_total + row / p.hq : row;
-      p.delta[idx] = acc[r];
+      p.delta[idx] = p.dlse != nullptr ? acc[r] - p.dlse[idx] : acc[r];
     }
   }
 }
@@ -343,7 +335,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
           if (kb == spread_at(KSTEPS, c)) copy1(xn, buf ^ 1, 1 + (c & 1), c >> 1);
       }
     }
-    pin_lds_mfma_pipeline<KSTEPS * (HAS_DP ? 2 : 1), BWD_AHEAD, 1>();
+    pin_lds_mfma_pipeline<KSTEPS * (HAS_DP ? 2 : 1), kBwdAhead, 1>();
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       lds_write_f4(xbuf, (((w * NX + 0) * 4 + r4) * 64 + lane) * 16,
@@ -447,7 +439,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
           const uint32_t boff = ok ? (uint32_t)(((long long)oi * dsv.row + q8) * 2) : 0xFFFFFFF0u;
           const uint32_t(&src)[4] = is_p ? ppk[kb2] : bop[kb2];
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, (u32x4_t){src[0], src[1], src[2], src[3]}),
-                                                 rs, (int)boff, 0, DS_STORE_CPOL);
+                                                 rs, (int)boff, 0, kDsStoreCpol);
         }
       }
     }
@@ -464,7 +456,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
         acc[db] = Elt<T>::mma(join_tr(lo, hi), bv, acc[db]);
       }
     }
-    pin_lds_mfma_pipeline<2 * NDB, BWD_AHEAD, 2>();
+    pin_lds_mfma_pipeline<2 * NDB, kBwdAhead, 2>();
 
     if constexpr (NBUF == 1) {
       lds_barrier();
@@ -730,7 +722,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
       for (int ii = 0; ii < C::NCOPY; ++ii)
         if (kb == spread_at(C::KA, ii)) copy_tile(xn, nb, ii);
     }
-    pin_lds_mfma_pipeline<2 * C::KA, PP_AHEAD_M1, 1>();
+    pin_lds_mfma_pipeline<2 * C::KA, kPpAheadM1, 1>();
   };
   // ---- phase M1b: remaining k-steps, then the partner quarters to the exchange buffer
   auto m1b = [&](int st) {
@@ -741,7 +733,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
       sacc = Elt<T>::mma(lds_read_b128_at(a_addr(t1, kb)), r1[kb], sacc);
       dpacc = Elt<T>::mma(lds_read_b128_at(a_addr(t2, kb)), r2[kb], dpacc);
     }
-    pin_lds_mfma_pipeline<2 * (C::KSTEPS - C::KA), (PP_AHEAD_M1 < 2 * (C::KSTEPS - C::KA) ? PP_AHEAD_M1 : 2 * (C::KSTEPS - C::KA)), 1>();
+    pin_lds_mfma_pipeline<2 * (C::KSTEPS - C::KA), (kPpAheadM1 < 2 * (C::KSTEPS - C::KA) ? kPpAheadM1 : 2 * (C::KSTEPS - C::KA)), 1>();
     // Slot j holds register quarter j + 1, i.e. quarter (cg + 1 + j) % 4.
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -825,7 +817,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
         acc[db] = Elt<T>::mma(join_tr(lo, hi), bv, acc[db]);
       }
     }
-    pin_lds_mfma_pipeline<2 * NDB, PP_AHEAD_M2, 2>();
+    pin_lds_mfma_pipeline<2 * NDB, kPpAheadM2, 2>();
   };
 
   if (nsteps > 0) {
@@ -931,9 +923,8 @@ static hipError_t launch_bwd_pp(AttnParams p, hipStream_t st) {
 // 1 completes the copies before the barrier that ends slot 2j + 1. All copies are issued by the
 // finishing group: the multiplying waves issue nothing but LDS reads and MFMAs.
 // ------------------------------------------------------------------------------------------------
-#ifndef PDS_AHEAD
-#define PDS_AHEAD 2
-#endif
+// LDS operands requested ahead in the P/dS kernel's score products.
+constexpr int kPdsAhead = 2;
 template <int NDB>
 struct PdsCfg {
   static constexpr int NW = 8;
@@ -1068,7 +1059,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
       sacc = Elt<T>::mma(lds_read_b128_at(a_addr(kt, kb)), qreg[kb], sacc);
       pacc = Elt<T>::mma(lds_read_b128_at(a_addr(vt, kb)), oreg[kb], pacc);
     }
-    pin_lds_mfma_pipeline<2 * C::KSTEPS, PDS_AHEAD, 1>();
+    pin_lds_mfma_pipeline<2 * C::KSTEPS, kPdsAhead, 1>();
 #pragma unroll
     for (int r4 = 0; r4 < 2; ++r4) {
       lds_write_f4(xbuf, ((w * 4 + r4) * 64 + lane) * 16,
@@ -1139,8 +1130,8 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
     const int q8 = qw0 + 8 * g;
     const bool ok = key < sv.lk && q8 < dsv.row;
     const uint32_t boff = ok ? (uint32_t)(((long long)key * dsv.row + q8) * 2) : 0xFFFFFFF0u;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, pt), p_rs, (int)boff, 0, DS_STORE_CPOL);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, dt), ds_rs, (int)boff, 0, DS_STORE_CPOL);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, pt), p_rs, (int)boff, 0, kDsStoreCpol);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, dt), ds_rs, (int)boff, 0, kDsStoreCpol);
   };
 
   if (je > jb) {
@@ -1254,7 +1245,7 @@ struct DqCfg {
   static constexpr int STILE = 32 * BQ * 2;    // dS block: 32 key rows x BQ queries x 2 bytes
   static constexpr int SROW = BQ * 2;
   static constexpr int STAGE = KTILE + STILE;
-  static constexpr int NBUF = PROD_NBUF;
+  static constexpr int NBUF = kProdNbuf;
   static constexpr int LDS = NBUF * STAGE;
   static constexpr int KCOPY = KTILE / 1024 / NW;  // K copies per wave per step
   static constexpr int SCOPY = STILE / 1024 / NW;  // dS copies per wave per step
@@ -1429,7 +1420,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_dq_from_ds_kernel(AttnParams p, i
         }
       }
     }
-    pin_lds_mfma_pipeline<NMMA, PROD_AHEAD, 1>();
+    pin_lds_mfma_pipeline<NMMA, kProdAhead, 1>();
     buf = buf == NB - 1 ? 0 : buf + 1;
   }
   // Copies issued during the last step land in LDS that the next workgroup may own.
@@ -1496,10 +1487,8 @@ static hipError_t launch_dq_ds_t(const AttnParams& p, hipStream_t st) {
 // ------------------------------------------------------------------------------------------------
 // SQ = queries per step: 32 (triple-buffered) or 64 (double-buffered), i.e. block rows of 64 or
 // 128 bytes per key; whole 128-byte rows keep the stored blocks' HBM reads at full lines.
-#ifndef DV_SQ
-#define DV_SQ 64
-#endif
-template <int NDB, int SQ = DV_SQ>
+constexpr int kDvSq = 64;
+template <int NDB, int SQ = kDvSq>
 struct DvCfg {
   static constexpr int NW = 8;
   static constexpr int KB = 2;                 // 32-key MFMA blocks per wave
@@ -1513,7 +1502,7 @@ struct DvCfg {
   static constexpr int PCH = PROW / 16;        // 16-byte chunks per P row
   static constexpr int PTILE = BK * PROW;
   static constexpr int STAGE = OTILE + PTILE;
-  static constexpr int NBUF = SQ == 32 ? PROD_NBUF : 2;
+  static constexpr int NBUF = SQ == 32 ? kProdNbuf : 2;
   static constexpr int LDS = NBUF * STAGE;
   static constexpr int OCOPY = OTILE / 1024 / NW;
   static constexpr int PCOPY = PTILE / 1024 / NW;
@@ -1710,7 +1699,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
         }
       }
     }
-    pin_lds_mfma_pipeline<NMMA, PROD_AHEAD, 1>();
+    pin_lds_mfma_pipeline<NMMA, kProdAhead, 1>();
     buf = buf == NB - 1 ? 0 : buf + 1;
   }
   // Copies issued during the last steps land in LDS that the next workgroup may own.

@@ -1,7 +1,8 @@
 // Device-side building blocks shared by the gfx950 attention kernels.
 //
 // Conventions used by every kernel in this library:
-//  * A workgroup is 4 wave64s. Waves are arranged NR x NC: NR row groups of stationary rows
+//  * A workgroup is 4 or 8 wave64s (8, two per SIMD, where a wave's state fits 256 registers).
+//    Waves are arranged NR x NC: NR row groups of stationary rows
 //    (queries in the forward and dQ kernels, keys in the dK/dV kernel) and NC column groups that
 //    each own DW = NDB*32 of the (padded) head dim. Partial sums over the head dim are combined
 //    across the NC waves of a row group through LDS.

@@ -15,6 +15,7 @@ struct AttnParams {
   void* o;              // forward output
   float* lse;           // forward output
   const float* lse_in;  // backward input
+  const float* dlse;    // backward: gradient of the returned LSE (lse layout), or NULL for zero
   float* delta;         // backward: Delta = rowsum(dO * O)
   void* dq;
   void* dk;

@@ -54,6 +54,7 @@
 #ifndef FFPA_H_
 #define FFPA_H_
 
+#include <hip/hip_runtime_api.h> /* hipStream_t */
 #include <stddef.h>
 #include <stdint.h>
 
@@ -88,9 +89,9 @@ typedef enum {
  *   lse  [batch, hq,  nq] fp32  out, natural-log log-sum-exp of the scaled scores; -inf for empty rows
  * Requires batch, hq, hkv, nq, nkv >= 1 and hq % hkv == 0.
  */
-int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-             int batch, int hq, int hkv, int nq, int nkv, int d,
-             int dtype, float scale, int causal, void* stream);
+ffpa_status_t ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+    int batch, int hq, int hkv, int nq, int nkv, int d,
+    ffpa_dtype_t dtype, float scale, int causal, hipStream_t stream);
 
 /*
  * Dense forward for grids too small to fill the GPU: same arguments and results as ffpa_fwd
@@ -104,9 +105,10 @@ int ffpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * FFPA_ERR_INVALID_ARGUMENT. Workspace layout: fp32 O [batch, hq, nq, nsplit, d] then fp32 LSE
  * [batch, hq, nq, nsplit]; its contents are scratch.
  */
-int ffpa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
-                   int batch, int hq, int hkv, int nq, int nkv, int d,
-                   int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+ffpa_status_t ffpa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+    int batch, int hq, int hkv, int nq, int nkv, int d,
+    ffpa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+    hipStream_t stream);
 
 /* Bytes of the ffpa_fwd_split workspace; 0 when the grid needs no split or the sizes are invalid. */
 size_t ffpa_fwd_split_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, int d);
@@ -128,10 +130,10 @@ size_t ffpa_fwd_split_workspace_bytes(int batch, int hq, int hkv, int nq, int nk
  * the causal mask when causal = 1; a row whose scores are all -inf is empty (O = 0, LSE = -inf).
  * Invalid mask arguments are FFPA_ERR_INVALID_ARGUMENT.
  */
-int ffpa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
-                    int batch, int hq, int hkv, int nq, int nkv, int d,
-                    const void* mask, int mask_kind, const int64_t* mask_strides,
-                    int dtype, float scale, int causal, void* stream);
+ffpa_status_t ffpa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+    int batch, int hq, int hkv, int nq, int nkv, int d,
+    const void* mask, ffpa_mask_kind_t mask_kind, const int64_t* mask_strides,
+    ffpa_dtype_t dtype, float scale, int causal, hipStream_t stream);
 
 /*
  * FP8 dense forward ("Backends Overview", backend table and notes: FP8 attention takes fp16/bf16
@@ -149,9 +151,10 @@ int ffpa_fwd_masked(const void* q, const void* k, const void* v, void* o, float*
  * V [batch, hkv]; K8 [batch, hkv, nkv, d] bytes; V8 transposed [batch, hkv, d, np] bytes with np =
  * nkv rounded up to 64 (zero padding). It is left filled after the call.
  */
-int ffpa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
-                 int batch, int hq, int hkv, int nq, int nkv, int d,
-                 int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+ffpa_status_t ffpa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+    int batch, int hq, int hkv, int nq, int nkv, int d,
+    ffpa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+    hipStream_t stream);
 
 /* Bytes of the ffpa_fwd_fp8 workspace; 0 for invalid sizes or d outside 320..512. Host function. */
 size_t ffpa_fwd_fp8_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, int d);
@@ -169,9 +172,9 @@ size_t ffpa_fwd_fp8_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv,
  * below 2^30 elements and head and row strides below 2^31. o must not overlap the inputs or
  * itself.
  */
-int ffpa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
-                     int batch, int hq, int hkv, int nq, int nkv, int d, const int64_t* strides,
-                     int dtype, float scale, int causal, void* stream);
+ffpa_status_t ffpa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+    int batch, int hq, int hkv, int nq, int nkv, int d, const int64_t* strides,
+    ffpa_dtype_t dtype, float scale, int causal, hipStream_t stream);
 
 /*
  * Split-KV decode forward ("Triton Backend", "Feature support": decode as a two-stage split-KV
@@ -184,15 +187,16 @@ int ffpa_fwd_strided(const void* q, const void* k, const void* v, void* o, float
  * (it is correct for any nq, but each workgroup holds 32 rows). A NULL or too-small workspace is
  * FFPA_ERR_INVALID_ARGUMENT.
  */
-int ffpa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                    int batch, int hq, int hkv, int nq, int nkv, int d,
-                    int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+ffpa_status_t ffpa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+    int batch, int hq, int hkv, int nq, int nkv, int d,
+    ffpa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+    hipStream_t stream);
 
 /* ffpa_decode_fwd with the strided layouts of ffpa_fwd_strided (same strides[12] and rules). */
-int ffpa_decode_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
-                            int batch, int hq, int hkv, int nq, int nkv, int d, const int64_t* strides,
-                            int dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
-                            void* stream);
+ffpa_status_t ffpa_decode_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+    int batch, int hq, int hkv, int nq, int nkv, int d, const int64_t* strides,
+    ffpa_dtype_t dtype, float scale, int causal, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Bytes of the ffpa_decode_fwd workspace for these sizes: batch * hq * nq * nsplit * (d + 1) * 4,
@@ -209,91 +213,117 @@ size_t ffpa_decode_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, 
 size_t ffpa_bwd_workspace_bytes(int batch, int hq, int nq, int nkv);
 
 /*
- * Dense backward of L = sum(dout * o) ("CuTe-DSL Backend", "Blackwell status": preprocess, dV,
- * dK, dQ). Takes the forward's inputs, its outputs o and lse, and dout [batch, hq, nq, d].
- *   delta [batch, hq, nq] fp32   caller-owned workspace, overwritten with rowsum(dout * o)
+ * Dense backward ("CuTe-DSL Backend", "Blackwell status": preprocess, dV, dK, dQ) of
+ * L = sum(dout * o) + sum(dlse * lse). Takes the forward's inputs, its outputs o and lse,
+ * dout [batch, hq, nq, d] and optionally the gradient of the returned LSE ("CuTe-DSL Backend",
+ * "Varlen (packed THD) API": the LSE is handed back to the caller, return_lse=True, so a loss may
+ * use it).
+ *   dlse  [batch, hq, nq] fp32   in, or NULL for zero. Since d lse_i / d s_ij = P_ij, it enters
+ *                                as delta_i = rowsum(dout * o)_i - dlse_i (dS = P * (dP - delta));
+ *                                ignored on rows with lse = -inf
+ *   delta [batch, hq, nq] fp32   caller-owned workspace, overwritten with that delta
  *   dq    [batch, hq, nq, d]     out
  *   dk, dv [batch, hkv, nkv, d]  out; sums over the hq/hkv query heads that share a KV head
  *   workspace, workspace_bytes   optional P/dS workspace (see above), or NULL, 0
  * Gradients are accumulated in fp32 and rounded to dtype once. Rows with lse = -inf contribute
  * nothing and get dq = 0.
  */
-int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-             const float* lse, float* delta, void* dq, void* dk, void* dv,
-             int batch, int hq, int hkv, int nq, int nkv, int d,
-             int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+ffpa_status_t ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+    const float* lse, const float* dlse, float* delta, void* dq, void* dk, void* dv,
+    int batch, int hq, int hkv, int nq, int nkv, int d,
+    ffpa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Dense backward with the attn_mask of ffpa_fwd_masked (same mask arguments), through the P/dS
+ * Dense backward with the attn_mask of ffpa_fwd_masked (same mask arguments; "Triton Backend",
+ * "Feature support": additive masks get a gradient reduced to their shape), through the P/dS
  * workspace, which is required here (NULL: FFPA_ERR_INVALID_ARGUMENT; sizes whose workspace is
- * not available: FFPA_ERR_NOT_SUPPORTED). The mask enters P exactly as in the forward.
- *   dmask  NULL, or (additive masks only) the bias gradient out: dS = P * (dP - Delta), the
+ * not available: FFPA_ERR_NOT_SUPPORTED). The mask enters P exactly as in the forward; dlse as in
+ * ffpa_bwd.
+ *   dmask  NULL, or (additive masks only) the bias gradient out: dS = P * (dP - delta), the
  *          gradient with respect to the scores, summed over the broadcast dimensions (those with
  *          a 0 stride), written packed row-major in the shape [s0 ? batch : 1, s1 ? hq : 1,
  *          s2 ? nq : 1, s3 ? nkv : 1] in q's dtype (fp32 sums, one rounding).
  */
-int ffpa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                    const float* lse, float* delta, void* dq, void* dk, void* dv,
-                    int batch, int hq, int hkv, int nq, int nkv, int d,
-                    const void* mask, int mask_kind, const int64_t* mask_strides, void* dmask,
-                    int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+ffpa_status_t ffpa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout,
+    const float* lse, const float* dlse, float* delta, void* dq, void* dk, void* dv,
+    int batch, int hq, int hkv, int nq, int nkv, int d,
+    const void* mask, ffpa_mask_kind_t mask_kind, const int64_t* mask_strides, void* dmask,
+    ffpa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * One stage of the dense backward, with exactly the arguments of ffpa_bwd plus `stage`:
  *   0 = preprocess (writes delta), 4 = P and dS, 1 = dK, 2 = dV, 3 = dQ.
  * ffpa_bwd is these launches in the order 0, 4, 1, 2, 3. Stages 4 and 1 read the delta written by
- * stage 0 (and so does stage 3 without a workspace). With a P/dS workspace, stage 4 writes P and
- * dS into it (for D > 512, stage 1 does) and stages 1, 2 and 3 read them: pass the same workspace
- * to all of them (a stage that reads a workspace that was not filled gives undefined results).
- * Without a workspace stage 4 launches nothing and stages 1, 2 and 3 are independent. The pages
- * run dV before dK; the order of the products does not matter.
+ * stage 0 (and so does stage 3 without a workspace); only stage 0 reads dlse. With a P/dS
+ * workspace, stage 4 writes P and dS into it (for D > 512, stage 1 does) and stages 1, 2 and 3
+ * read them: pass the same workspace to all of them (a stage that reads a workspace that was not
+ * filled gives undefined results). Without a workspace stage 4 launches nothing and stages 1, 2
+ * and 3 are independent. The pages run dV before dK; the order of the products does not matter.
  * Lets a caller time or schedule the launches individually ("CuTe-DSL Backend", "Blackwell
  * status": the backward is separate launches). Returns FFPA_ERR_INVALID_ARGUMENT for another
  * stage.
  */
-int ffpa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
-                   const float* lse, float* delta, void* dq, void* dk, void* dv,
-                   int batch, int hq, int hkv, int nq, int nkv, int d,
-                   int dtype, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+ffpa_status_t ffpa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+    const void* dout, const float* lse, const float* dlse, float* delta, void* dq, void* dk, void* dv,
+    int batch, int hq, int hkv, int nq, int nkv, int d,
+    ffpa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Packed (THD) varlen forward ("CuTe-DSL Backend", "Varlen (packed THD) API").
  *   q [total_q, hq, d]; k, v [total_k, hkv, d]; o [total_q, hq, d]; lse [hq, total_q] fp32.
  *   cu_seqlens_q [batch+1], cu_seqlens_k [batch+1]: device int32, start at 0, non-decreasing,
- *     end at total_q / total_k. cu_seqlens_k == NULL means cu_seqlens_k = cu_seqlens_q.
+ *     end at total_q / total_k. cu_seqlens_k == NULL means cu_seqlens_k = cu_seqlens_q (then
+ *     total_k must equal total_q, else FFPA_ERR_INVALID_ARGUMENT).
  *   max_seqlen_q / max_seqlen_k bound every sequence length (they size the launch grid).
  * Sequence s attends queries [cu_q[s], cu_q[s+1]) to keys [cu_k[s], cu_k[s+1]); sequences of
  * length 0 are allowed. The device contents of cu_seqlens are not read on the host: contents
  * that break the rules above are undefined behaviour.
  */
-int ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                    int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
-                    int hq, int hkv, int d, int dtype, float scale, int causal, void* stream);
+ffpa_status_t ffpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+    int hq, int hkv, int d, ffpa_dtype_t dtype, float scale, int causal, hipStream_t stream);
 
 /*
- * Bytes of the optional P/dS workspace of ffpa_varlen_bwd:
- * 2 * hq * total_k * round_up(max_seqlen_q, 8) * 2, two blocks (dS, then P), each bounding the
- * packed per-sequence layout (sequence by sequence, then head, then key row of round_up(Lq, 8)
- * queries) for every cu_seqlens consistent with the totals and max_seqlen values; 0 when not
- * available (see ffpa_bwd_workspace_bytes). Host function.
+ * Bytes of the optional P/dS workspace of ffpa_varlen_bwd for any cu_seqlens consistent with the
+ * totals and max_seqlen values: 2 * hq * total_k * round_up(max_seqlen_q, 8) * 2, two blocks
+ * (dS, then P), each bounding the packed per-sequence layout (sequence by sequence, then head,
+ * then key row of round_up(Lq, 8) queries); 0 when not available (see ffpa_bwd_workspace_bytes).
+ * Host function.
  */
 size_t ffpa_varlen_bwd_workspace_bytes(int hq, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k);
 
 /*
- * Packed (THD) varlen backward; arguments as ffpa_varlen_fwd plus o, dout [total_q, hq, d],
- * the forward's lse [hq, total_q], a caller-owned fp32 workspace delta [hq, total_q], the
- * outputs dq [total_q, hq, d], dk, dv [total_k, hkv, d], and the optional P/dS workspace.
+ * Exact bytes of the same workspace for the given sequence lengths: 2 * hq * sum_s Lk_s *
+ * round_up(Lq_s, 8) * 2, from HOST copies of cu_seqlens (cu_seqlens_k_host NULL: the q ones).
+ * 0 when the copies break the cu_seqlens rules of ffpa_varlen_fwd for these totals and max
+ * lengths, or when the workspace is not available. Host function.
  */
-int ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                    const float* lse, float* delta, void* dq, void* dk, void* dv,
-                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                    int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
-                    int hq, int hkv, int d, int dtype, float scale, int causal,
-                    void* workspace, size_t workspace_bytes, void* stream);
+size_t ffpa_varlen_bwd_workspace_bytes_exact(int hq, int batch, const int32_t* cu_seqlens_q_host,
+    const int32_t* cu_seqlens_k_host, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k);
+
+/*
+ * Packed (THD) varlen backward ("CuTe-DSL Backend", "Varlen (packed THD) API": the packed call
+ * with autograd; "Blackwell status": preprocess, dV, dK, dQ). Arguments as ffpa_varlen_fwd plus
+ * o, dout [total_q, hq, d], the forward's lse [hq, total_q], dlse [hq, total_q] fp32 or NULL (as
+ * in ffpa_bwd), a caller-owned fp32 workspace delta [hq, total_q], the outputs dq [total_q, hq, d],
+ * dk, dv [total_k, hkv, d], and the optional P/dS workspace.
+ *   cu_seqlens_q_host, cu_seqlens_k_host: NULL, or host copies of the device cu_seqlens (k NULL:
+ *     the q ones). With them the P/dS workspace needs only the exact size
+ *     (ffpa_varlen_bwd_workspace_bytes_exact), the copies are checked on the host (a bad copy is
+ *     FFPA_ERR_INVALID_ARGUMENT) and must equal the device contents (else undefined behaviour);
+ *     without them it needs ffpa_varlen_bwd_workspace_bytes.
+ */
+ffpa_status_t ffpa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+    const float* lse, const float* dlse, float* delta, void* dq, void* dk, void* dv,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_k_host,
+    int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+    int hq, int hkv, int d, ffpa_dtype_t dtype, float scale, int causal,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable name of a status code; never NULL. */
-const char* ffpa_status_string(int status);
+const char* ffpa_status_string(ffpa_status_t status);
 
 #ifdef __cplusplus
 }

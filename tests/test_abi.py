@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "ffpa.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(ffpa_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:ffpa_status_t|size_t|const char\*)\s+(ffpa_\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -32,8 +32,26 @@ def test_header_declares_expected_entry_points():
               "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes", "ffpa_decode_fwd",
               "ffpa_decode_workspace_bytes", "ffpa_decode_fwd_strided", "ffpa_fwd_strided", "ffpa_fwd_masked",
               "ffpa_bwd_masked", "ffpa_fwd_fp8", "ffpa_fwd_fp8_workspace_bytes", "ffpa_fwd_split",
-              "ffpa_fwd_split_workspace_bytes"):
+              "ffpa_fwd_split_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes_exact"):
         assert n in names
+
+
+def test_header_is_valid_c_and_cxx():
+    """include/ffpa.h compiles as C11 and as C++17 (declarations only, no library needed)."""
+    import shutil
+    import subprocess
+    import tempfile
+    for cc, std, ext in (("gcc", "-std=c11", "c"), ("g++", "-std=c++17", "cpp")):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not available")
+        with tempfile.TemporaryDirectory() as td:
+            src = os.path.join(td, f"t.{ext}")
+            with open(src, "w") as f:
+                f.write('#include "ffpa.h"\nint main(void) { ffpa_status_t s = FFPA_OK; ffpa_dtype_t t = '
+                        'FFPA_DTYPE_BF16; hipStream_t st = 0; (void)st; return (int)s + (int)t; }\n')
+            r = subprocess.run([cc, std, "-fsyntax-only", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                                "-I", "/opt/rocm/include", src], capture_output=True, text=True)
+            assert r.returncode == 0, r.stderr
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -78,9 +96,14 @@ def test_fwd_null_pointers(lib):
         assert _fwd(lib, ptrs=ptrs) == 1
 
 
+# q, k, v, o, dout, lse, dlse, delta, dq, dk, dv; dlse (index 6) may be NULL.
+BWD_PTRS = 11
+DLSE = 6
+
+
 def _bwd(lib, stage=None, b=1, hq=2, hkv=1, nq=64, nkv=64, d=640, dtype=1, scale=0.04, causal=1, ptrs=None,
          ws=N, ws_bytes=0):
-    ptrs = ptrs or [P] * 10
+    ptrs = ptrs or [P] * BWD_PTRS
     args = (*ptrs, b, hq, hkv, nq, nkv, d, dtype, scale, causal, ws, ws_bytes, S)
     return lib.ffpa_bwd(*args) if stage is None else lib.ffpa_bwd_stage(stage, *args)
 
@@ -107,11 +130,45 @@ def test_workspace_sizes(lib):
     # varlen: bounded by total_k * round_up(max_seqlen_q, 8) per head and block
     assert B.ffpa_varlen_bwd_workspace_bytes(4, 100, 90, 41, 60) == 2 * 4 * 90 * 48 * 2
     assert B.ffpa_varlen_bwd_workspace_bytes(4, 0, 0, 0, 41) == 0
+    # exact: sum over sequences of Lk * round_up(Lq, 8) per head and block
+    cq, ck = [0, 41, 41, 100], [0, 30, 60, 90]
+    assert B.ffpa_varlen_bwd_workspace_bytes_exact(4, cq, ck, 100, 90, 59, 30) == \
+        2 * 4 * (30 * 48 + 30 * 0 + 30 * 64) * 2
+    assert B.ffpa_varlen_bwd_workspace_bytes_exact(4, cq, None, 100, 100, 59, 59) == \
+        2 * 4 * (41 * 48 + 0 + 59 * 64) * 2
+    assert B.ffpa_varlen_bwd_workspace_bytes_exact(4, cq, ck, 100, 90, 40, 30) == 0   # max_seqlen_q too small
+    assert B.ffpa_varlen_bwd_workspace_bytes_exact(4, cq, ck, 101, 90, 59, 30) == 0   # wrong total
+
+
+def test_store_ds_policy():
+    """The backward stores P and dS only when the workspace exists and fits with headroom."""
+    from head_dim_attention_amd import _binding as B
+    gib = 1 << 30
+    assert B.choose_store_ds(8 * gib, 200 * gib)
+    assert not B.choose_store_ds(8 * gib, 8 * gib)                  # no headroom left
+    assert B.choose_store_ds(8 * gib, 9 * gib)
+    assert not B.choose_store_ds(0, 200 * gib)                      # not available for these sizes
+    assert not B.choose_store_ds(275 * gib, 280 * gib, headroom=8 * gib)
+    assert B.choose_store_ds(100, 200, headroom=0)
+
+
+def test_masked_backward_workspace_check():
+    """The masked backward needs the P/dS workspace: a clear error when it cannot fit."""
+    from head_dim_attention_amd import _binding as B
+    dev = torch.device("cpu")
+    need = B.ffpa_bwd_workspace_bytes(8, 32, 16384, 16384)
+    assert B.masked_bwd_workspace_check(8, 32, 16384, 16384, dev, available=need) == need
+    with pytest.raises(MemoryError):
+        B.masked_bwd_workspace_check(8, 32, 16384, 16384, dev, available=need - 1)
+    with pytest.raises(NotImplementedError):
+        B.masked_bwd_workspace_check(1, 1, 40000, 40000, dev, available=1 << 40)
 
 
 def test_bwd_null_pointers(lib):
-    for i in range(10):
-        ptrs = [P] * 10
+    for i in range(BWD_PTRS):
+        if i == DLSE:
+            continue
+        ptrs = [P] * BWD_PTRS
         ptrs[i] = N
         assert _bwd(lib, ptrs=ptrs) == 1
 
@@ -135,11 +192,44 @@ def test_varlen_null_pointers(lib):
         ptrs = [P] * 7
         ptrs[i] = N
         assert _vfwd(lib, ptrs=ptrs) == 1
-    args = [P] * 12
+    # q, k, v, o, dout, lse, dlse, delta, dq, dk, dv, cu_q, cu_k, then the two host copies (NULL)
+    args = [P] * 13 + [N, N]
     args[3] = N
     assert lib.ffpa_varlen_bwd(*args, 2, 64, 64, 128, 128, 4, 2, 512, 0, 0.04, 1, N, 0, S) == 1
     # too small a dS workspace
-    assert lib.ffpa_varlen_bwd(*([P] * 12), 2, 64, 64, 128, 128, 4, 2, 512, 0, 0.04, 1, P, 1024, S) == 1
+    assert lib.ffpa_varlen_bwd(*([P] * 13), N, N, 2, 64, 64, 128, 128, 4, 2, 512, 0, 0.04, 1, P, 1024, S) == 1
+
+
+def test_varlen_null_cu_seqlens_k_needs_equal_totals(lib):
+    """cu_seqlens_k = NULL reuses the query offsets for the keys: total_k != total_q would index K
+    and V out of range, so it is an invalid argument (forward and backward)."""
+    ptrs = [P] * 7
+    ptrs[6] = N
+    assert _vfwd(lib, ptrs=ptrs, tq=128, tk=96, mk=64) == 1
+    bargs = [P] * 12 + [N, N, N]
+    assert lib.ffpa_varlen_bwd(*bargs, 2, 64, 64, 128, 96, 4, 2, 512, 0, 0.04, 1, N, 0, S) == 1
+    # host copy of k without one of q is rejected
+    cu = (ctypes.c_int32 * 3)(0, 64, 128)
+    hargs = [P] * 13 + [N, ctypes.cast(cu, ctypes.c_void_p)]
+    assert lib.ffpa_varlen_bwd(*hargs, 2, 64, 64, 128, 128, 4, 2, 512, 0, 0.04, 1, N, 0, S) == 1
+
+
+def test_varlen_host_cu_seqlens_checked(lib):
+    """Host copies of cu_seqlens are validated before anything is launched."""
+    def call(cq, ck, tq=128, tk=128, mq=64, mk=64, ws=N, nws=0):
+        aq = (ctypes.c_int32 * len(cq))(*cq)
+        ak = (ctypes.c_int32 * len(ck))(*ck)
+        args = [P] * 13 + [ctypes.cast(aq, ctypes.c_void_p), ctypes.cast(ak, ctypes.c_void_p)]
+        return lib.ffpa_varlen_bwd(*args, len(cq) - 1, mq, mk, tq, tk, 4, 2, 512, 0, 0.04, 1, ws, nws, S)
+    assert call([1, 64, 128], [0, 64, 128]) == 1        # does not start at 0
+    assert call([0, 70, 128], [0, 64, 128]) == 1        # a length above max_seqlen_q
+    assert call([0, 64, 120], [0, 64, 128]) == 1        # does not end at total_q
+    assert call([0, 64, 128], [0, 80, 60]) == 1         # decreasing
+    # a workspace of the exact size passes validation only when it is large enough
+    from head_dim_attention_amd import _binding as B
+    need = B.ffpa_varlen_bwd_workspace_bytes_exact(4, [0, 64, 128], [0, 64, 128], 128, 128, 64, 64)
+    assert need == 2 * 4 * (64 * 64 + 64 * 64) * 2
+    assert call([0, 64, 128], [0, 64, 128], ws=P, nws=need - 1) == 1
 
 
 def test_varlen_empty_batch_is_a_noop(lib):
@@ -252,7 +342,7 @@ def test_mask_validation(lib):
     assert lib.ffpa_fwd_masked(*base, P, 1, arr(0, 64 * 64, 60, 1), *tail) == 1  # row stride % 8
     assert lib.ffpa_fwd_masked(*base, P, 1, arr(-8, 0, 64, 1), *tail) == 1       # negative
     assert lib.ffpa_fwd_masked(*base, ctypes.c_void_p(0x1008), 1, good, *tail) == 1  # 8-byte aligned bias
-    bw = (P,) * 10 + (1, 2, 2, 64, 64, 512)
+    bw = (P,) * 11 + (1, 2, 2, 64, 64, 512)
     assert lib.ffpa_bwd_masked(*bw, P, 1, good, N, 0, 0.04, 0, N, 0, S) == 1       # no workspace
     assert lib.ffpa_bwd_masked(*bw, P, 2, good, P, 0, 0.04, 0, P, 1 << 30, S) == 1  # gradient of a bool mask
 

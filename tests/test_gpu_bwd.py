@@ -187,3 +187,112 @@ def test_bwd_varlen_equals_dense(lib, store_ds):
         assert torch.equal(od, sl(o)) and torch.equal(lsed[0], lse[:, a:b])
         for x, y in zip((dq, dk, dv), g):
             assert torch.equal(sl(x), y)
+
+
+# ----------------------------------------------------------------------------------------------
+# The returned LSE is differentiable: loss = sum(dO * O) + sum(g * LSE).
+# ----------------------------------------------------------------------------------------------
+DLSE_CASES = [
+    (1, 4, 2, 100, 60, 512, BF, True),     # causal Nq > Nkv: 40 empty rows per head
+    (1, 2, 2, 130, 130, 384, FP, False),
+    (1, 4, 1, 96, 200, 768, BF, True),
+]
+
+
+@PATHS
+@pytest.mark.parametrize("case", DLSE_CASES, ids=_ids)
+def test_bwd_dlse(lib, case, store_ds):
+    b, hq, hkv, nq, nkv, d, dt, causal = case
+    q, k, v, do = W.dense_inputs(b, hq, hkv, nq, nkv, d, dt, seed=601 + d)
+    g = torch.randn((b, hq, nq), generator=torch.Generator().manual_seed(602 + d), dtype=torch.float32)
+    scale = 1.0 / math.sqrt(d)
+    print(f"case {_ids(case)} dlse store_ds={store_ds}", flush=True)
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = lib.ffpa_fwd(qc, kc, vc, causal=causal, scale=scale)
+    dq, dk, dv = lib.ffpa_bwd(qc, kc, vc, o, doc, lse, causal=causal, scale=scale, store_ds=store_ds, dlse=g.cuda())
+    torch.cuda.synchronize()
+    g_ref = ref.attn_bwd(q, k, v, do, scale=np.float64(np.float32(scale)), causal=causal, dlse=g.double().numpy())
+    check_grads((dq, dk, dv), g_ref, _ids(case) + " dlse")
+    if causal and nq > nkv:
+        assert torch.all(dq[:, :, :nq - nkv] == 0)
+
+
+def test_bwd_dlse_only(lib):
+    """dO = 0 leaves only the LSE term: dV is exactly zero and dQ/dK match the oracle."""
+    q, k, v, do = W.dense_inputs(1, 2, 2, 80, 80, 512, BF, seed=603)
+    g = torch.randn((1, 2, 80), generator=torch.Generator().manual_seed(604))
+    do = torch.zeros_like(do)
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = lib.ffpa_fwd(qc, kc, vc, causal=True)
+    dq, dk, dv = lib.ffpa_bwd(qc, kc, vc, o, doc, lse, causal=True, dlse=g.cuda())
+    torch.cuda.synchronize()
+    assert torch.all(dv == 0)
+    g_ref = ref.attn_bwd(q, k, v, do, scale=np.float64(np.float32(1 / math.sqrt(512))), causal=True,
+                         dlse=g.double().numpy())
+    for x, r in ((dq, g_ref[0]), (dk, g_ref[1])):
+        assert np.linalg.norm(to64(x) - r) / np.linalg.norm(r) <= 2e-2
+
+
+def test_autograd_return_lse_is_differentiable(lib):
+    """ffpa_attn_func(return_lse=True): a loss that uses the LSE gets the LSE's gradient."""
+    q, k, v, do = W.dense_inputs(1, 4, 2, 90, 120, 512, BF, seed=605)
+    g = torch.randn((1, 4, 90), generator=torch.Generator().manual_seed(606))
+    qc, kc, vc = (x.cuda().requires_grad_(True) for x in (q, k, v))
+    o, lse = lib.ffpa_attn_func(qc, kc, vc, is_causal=True, return_lse=True)
+    ((o.float() * do.cuda().float()).sum() + (lse * g.cuda()).sum()).backward()
+    g_ref = ref.attn_bwd(q, k, v, do, scale=np.float64(np.float32(1 / math.sqrt(512))), causal=True,
+                         dlse=g.double().numpy())
+    check_grads((qc.grad, kc.grad, vc.grad), g_ref, "autograd lse")
+    # LSE alone: the output O is unused (its gradient is None inside the wrapper)
+    qc.grad = kc.grad = vc.grad = None
+    _, lse2 = lib.ffpa_attn_func(qc, kc, vc, is_causal=True, return_lse=True)
+    (lse2 * g.cuda()).sum().backward()
+    g_ref2 = ref.attn_bwd(q, k, v, np.zeros(do.shape), scale=np.float64(np.float32(1 / math.sqrt(512))),
+                          causal=True, dlse=g.double().numpy())
+    assert torch.all(vc.grad == 0)
+    for x, r in ((qc.grad, g_ref2[0]), (kc.grad, g_ref2[1])):
+        assert np.linalg.norm(to64(x) - r) / np.linalg.norm(r) <= 2e-2
+
+
+@PATHS
+def test_bwd_varlen_dlse(lib, store_ds):
+    lq, lk = [0, 33, 130, 64], [5, 0, 64, 130]
+    q, k, v, do, cu_q, cu_k = W.varlen_inputs(lq, lk, 4, 2, 512, BF, seed=607)
+    g = torch.randn((4, sum(lq)), generator=torch.Generator().manual_seed(608))
+    qc, kc, vc, doc, cq, ck = q.cuda(), k.cuda(), v.cuda(), do.cuda(), cu_q.cuda(), cu_k.cuda()
+    o, lse = lib.ffpa_varlen_fwd(qc, kc, vc, cq, ck, causal=True)
+    dq, dk, dv = lib.ffpa_varlen_bwd(qc, kc, vc, o, doc, lse, cq, ck, causal=True, store_ds=store_ds, dlse=g.cuda())
+    torch.cuda.synchronize()
+    g_ref = ref.varlen_bwd(q, k, v, do, cu_q.numpy(), cu_k.numpy(), scale=np.float64(np.float32(1 / math.sqrt(512))),
+                           causal=True, dlse=g.double().numpy())
+    check_grads((dq, dk, dv), g_ref, "varlen dlse")
+
+
+def test_varlen_autograd_return_lse(lib):
+    lens = [40, 97, 64]
+    q, k, v, do, cu_q, cu_k = W.varlen_inputs(lens, lens, 2, 2, 512, BF, seed=609)
+    g = torch.randn((2, sum(lens)), generator=torch.Generator().manual_seed(610))
+    qc, kc, vc = (x.cuda().requires_grad_(True) for x in (q, k, v))
+    o, lse = lib.ffpa_attn_varlen_func(qc, kc, vc, cu_q.cuda(), causal=True, return_lse=True)
+    ((o.float() * do.cuda().float()).sum() + (lse * g.cuda()).sum()).backward()
+    g_ref = ref.varlen_bwd(q, k, v, do, cu_q.numpy(), cu_q.numpy(), scale=np.float64(np.float32(1 / math.sqrt(512))),
+                           causal=True, dlse=g.double().numpy())
+    check_grads((qc.grad, kc.grad, vc.grad), g_ref, "varlen autograd lse")
+
+
+def test_varlen_exact_workspace_equals_bound(lib):
+    """The exact-size P/dS workspace (host copies of cu_seqlens) gives bit-identical gradients to
+    the bound-sized one."""
+    lq, lk = [0, 45, 300, 129, 64], [10, 45, 280, 0, 64]
+    q, k, v, do, cu_q, cu_k = W.varlen_inputs(lq, lk, 8, 2, 512, BF, seed=611)
+    qc, kc, vc, doc, cq, ck = q.cuda(), k.cuda(), v.cuda(), do.cuda(), cu_q.cuda(), cu_k.cuda()
+    o, lse = lib.ffpa_varlen_fwd(qc, kc, vc, cq, ck, causal=True)
+    mq, mk = max(lq), max(lk)
+    exact = lib.ffpa_varlen_bwd(qc, kc, vc, o, doc, lse, cq, ck, mq, mk, causal=True, store_ds=True)
+    bound = lib.ffpa_varlen_bwd(qc, kc, vc, o, doc, lse, cq, ck, mq, mk, causal=True, store_ds=True, validate=False)
+    torch.cuda.synchronize()
+    from head_dim_attention_amd import _binding as B
+    assert B.ffpa_varlen_bwd_workspace_bytes_exact(8, cu_q.tolist(), cu_k.tolist(), sum(lq), sum(lk), mq, mk) < \
+        B.ffpa_varlen_bwd_workspace_bytes(8, sum(lq), sum(lk), mq, mk)
+    for x, y in zip(exact, bound):
+        assert torch.equal(x, y)

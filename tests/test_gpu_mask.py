@@ -168,3 +168,21 @@ def test_mask_full_size(lib, d, kind):
         check_o_lse(o[:, sl], lse[:, sl], o_ref, lse_ref, BF, tag)
         g_ref = ref.attn_bwd(q[:, sl], k[:, sl], v[:, sl], do[:, sl], scale=s64, causal=False, bias=rb)
         check_grads((dq[:, sl], dk[:, sl], dv[:, sl]), g_ref[:3], tag)
+
+
+@pytest.mark.parametrize("d", [512, 768])
+def test_mask_dlse(lib, d):
+    """The LSE's gradient through the masked backward (and into the bias gradient)."""
+    q, k, v, do = W.dense_inputs(1, 4, 2, 70, 90, d, BF, seed=620 + d)
+    m = _bias((1, 4, 70, 90), BF, 621, "add")
+    g = torch.randn((1, 4, 70), generator=torch.Generator().manual_seed(622))
+    scale = 1.0 / math.sqrt(d)
+    qc, kc, vc, doc, mc = q.cuda(), k.cuda(), v.cuda(), do.cuda(), m.cuda()
+    o, lse = lib.ffpa_fwd(qc, kc, vc, causal=True, scale=scale, attn_mask=mc)
+    dq, dk, dv, dm = lib.ffpa_bwd(qc, kc, vc, o, doc, lse, causal=True, scale=scale, attn_mask=mc, mask_grad=True,
+                                  dlse=g.cuda())
+    torch.cuda.synchronize()
+    r = ref.attn_bwd(q, k, v, do, scale=np.float64(np.float32(scale)), causal=True, bias=_ref_bias(m),
+                     dlse=g.double().numpy())
+    check_grads((dq, dk, dv), r[:3], f"mask dlse d{d}")
+    assert rel_l2(to64(dm), r[3]) <= GRAD_RTOL
