@@ -10,9 +10,18 @@ runs with the library's P/dS workspace (one kernel forms and stores P and dS; dK
 dV = P^T dO and dQ = dS K are products of them); --no-ds-workspace times the recomputing dK, dV
 and dQ kernels instead (the P/dS launch is then empty).
 
-Two side legs follow the step, each reported in its own object of the JSON line: the split-KV
-decode pass on a decode workload ("decode", HBM-bound) and the FP8 forward on the step's inputs
-("fp8_fwd", quantizing pre-pass included, against the fp8 MFMA peak).
+Legs that follow the timed step, each in its own object of the JSON line (none of them changes
+the step's timed region):
+  configs        every other configuration of the benchmark set: the forward-only latency case
+                 (B=1, H=2, N=512, D=320), the causal H=8 N=4096 D=512 step, the causal GQA
+                 D=1024 fp16 step and the packed varlen causal step (forward, backward, per kernel)
+  recompute_bwd  the O(N)-memory backward (no P/dS workspace) on the headline shape and on the
+                 varlen set, beside the stored-P/dS path's time
+  decode         the split-KV decode pass (HBM-bound)
+  fp8_fwd        the FP8 forward on the step's inputs (quantizing pre-pass included)
+  cpu_baseline   the float64 oracle on whole KV groups of the same inputs, on the host's cores
+The side legs draw their inputs on the GPU with a seeded device generator (same distribution as
+the CPU recipe, other values) so that large inputs need no host round trip.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line (rank 0).
@@ -50,6 +59,8 @@ COMPUTE_KERNELS = ("fwd", "pds", "dk", "dv", "dq")
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "traffic_dense_d512_n8192.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "head_dim_attention_amd", "csrc", f)
                   for f in ("ffpa_device.h", "ffpa_params.h", "ffpa_fwd.hip", "ffpa_bwd.hip", "ffpa_fp8.hip")]
+# The other configurations reported beside the headline step (forward-only, causal, GQA, varlen).
+CONFIG_LEGS = ("fwd_d320_n512", "causal_d512_n4096", "gqa_causal_d1024_n8192", "varlen_causal_d512")
 
 
 def kernel_source_hash() -> str:
@@ -83,6 +94,9 @@ def parse_args(argv=None):
     ap.add_argument("--decode-workload", default="decode_gqa_d512_k65536",
                     help="workload of the split-KV decode leg ('none' skips it)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward leg")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other configurations and the recompute leg")
+    ap.add_argument("--only-legs", default="",
+                    help="comma-separated config legs to run instead of the headline step (profiling)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration under rocprofv3)")
     return ap.parse_args(argv)
@@ -101,6 +115,218 @@ def load_traffic(kernel: str):
     if not k:
         return None
     return k.get("hbm_bytes_per_launch")
+
+
+def _tf(flops: float, ms: float) -> float:
+    return flops / (ms * 1e-3) / 1e12
+
+
+def _check(F, st):
+    if st:
+        raise RuntimeError(F.ffpa_status_string(st))
+
+
+class DenseStep:
+    """The launches of one dense forward + backward step on resident inputs, through the C ABI:
+    forward (split when the grid is small), then backward stages 0, 4, 1, 2, 3."""
+
+    def __init__(self, F, qd, kd, vd, dod, causal: bool, store_ds: bool):
+        import torch
+        self.F, self.lib = F, F.load_library()
+        self.qd, self.kd, self.vd, self.dod = qd, kd, vd, dod
+        b, hq, nq, d = qd.shape
+        hkv, nkv = kd.shape[1], kd.shape[2]
+        self.dims = (b, hq, hkv, nq, nkv, d)
+        self.causal, self.scale = causal, 1.0 / math.sqrt(d)
+        dev = qd.device
+        self.o = torch.empty_like(qd)
+        self.lse = torch.empty((b, hq, nq), dtype=torch.float32, device=dev)
+        self.delta = torch.empty_like(self.lse)
+        self.dq, self.dk, self.dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        self.ws_bytes = F.ffpa_bwd_workspace_bytes(b, hq, nq, nkv) if store_ds else 0
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev) if self.ws_bytes > 0 else None
+        # Grids too small to fill the GPU take the key-range split forward (workspace allocated
+        # here, outside any timed region); the headline grid needs none.
+        self.fws_bytes = F.ffpa_fwd_split_workspace_bytes(b, hq, hkv, nq, nkv, d)
+        self.fws = torch.empty(self.fws_bytes, dtype=torch.uint8, device=dev) if self.fws_bytes > 0 else None
+        self.dt = 0 if qd.dtype == torch.bfloat16 else 1
+        self.stream = torch.cuda.current_stream(dev)
+        self.flops_d = dict(KERNEL_FLOPS_PER_PAIR_D)
+        if self.ws is not None:
+            self.flops_d.update(STORED_FLOPS_PER_PAIR_D)
+            if d > 512:  # the dK kernel recomputes and stores P and dS itself; the P/dS launch is empty
+                self.flops_d.update({"pds": 0, "dk": 6})
+        self.pairs = legal_pairs(nq, nkv, causal) * b * hq
+        self.launches = [self.fwd] + [(lambda i=i: self.bwd_stage(i)) for _, i in BWD_STAGES]
+
+    def fwd(self):
+        P, (b, hq, hkv, nq, nkv, d) = self.F._binding._ptr, self.dims
+        sp = self.stream.cuda_stream
+        if self.fws is None:
+            st = self.lib.ffpa_fwd(P(self.qd), P(self.kd), P(self.vd), P(self.o), P(self.lse), b, hq, hkv, nq, nkv, d,
+                                   self.dt, self.scale, int(self.causal), sp)
+        else:
+            st = self.lib.ffpa_fwd_split(P(self.qd), P(self.kd), P(self.vd), P(self.o), P(self.lse), b, hq, hkv, nq,
+                                         nkv, d, self.dt, self.scale, int(self.causal), P(self.fws), self.fws_bytes, sp)
+        _check(self.F, st)
+
+    def bwd_stage(self, i):
+        P, (b, hq, hkv, nq, nkv, d) = self.F._binding._ptr, self.dims
+        st = self.lib.ffpa_bwd_stage(i, P(self.qd), P(self.kd), P(self.vd), P(self.o), P(self.dod), P(self.lse), None,
+                                     P(self.delta), P(self.dq), P(self.dk), P(self.dv), b, hq, hkv, nq, nkv, d,
+                                     self.dt, self.scale, int(self.causal), P(self.ws), self.ws_bytes,
+                                     self.stream.cuda_stream)
+        _check(self.F, st)
+
+    def time(self, steps: int, warmup: int):
+        """HIP events on the launch stream around every launch of every step; returns (mean ms per
+        stage, host wall ms per step)."""
+        import torch
+        for _ in range(warmup):
+            for fn in self.launches:
+                fn()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.launches) + 1)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            ev[s][0].record(self.stream)
+            for i, fn in enumerate(self.launches):
+                fn()
+                ev[s][i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        stage_ms = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+                    for i, name in enumerate(STAGES)}
+        return stage_ms, wall_ms
+
+    def kernel_table(self, stage_ms):
+        d = self.dims[5]
+        kernels = {}
+        for n in COMPUTE_KERNELS:
+            if self.flops_d[n] == 0:
+                continue
+            fl = self.flops_d[n] * d * self.pairs
+            kernels[n] = {"ms": round(stage_ms[n], 4), "algorithmic_tflops": round(_tf(fl, stage_ms[n]), 2),
+                          "frac": round(_tf(fl, stage_ms[n]) / PEAK_TFLOPS, 4)}
+        b, hq, _, nq, _, _ = self.dims
+        pre_bytes = 2.0 * b * hq * nq * d * self.qd.element_size() + 4.0 * b * hq * nq
+        gbs = pre_bytes / (stage_ms["pre"] * 1e-3) / 1e9
+        kernels["pre"] = {"ms": round(stage_ms["pre"], 4), "algorithmic_gbs": round(gbs, 1),
+                          "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        return kernels
+
+
+def _timed(fn, steps: int, warmup: int, stream) -> float:
+    """Mean HIP-event ms of fn() over `steps` calls on `stream` after `warmup` calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps
+
+
+def dense_config_leg(F, W, w, seed: int, steps: int, warmup: int, store_ds: bool = True) -> dict:
+    """Forward (+ backward) of a dense workload: times, credited TFLOPS and fractions of peak."""
+    import torch
+    dev = torch.device("cuda:0")
+    q, k, v, do = W.workload_inputs(w, seed, device="cuda")
+    if do is None:
+        do = torch.zeros_like(q)
+    step = DenseStep(F, q, k, v, do, w.causal, store_ds)
+    b, hq, hkv, nq, nkv, d = step.dims
+    fwd_flops = 4.0 * d * step.pairs
+    out = {"workload": w.name, "batch": b, "heads": hq, "kv_heads": hkv, "seq_len_q": nq, "seq_len_kv": nkv,
+           "head_dim": d, "causal": w.causal, "dtype": w.dtype, "credited_fwd_flops": fwd_flops}
+    if not w.backward:
+        n = max(steps, 200)
+        ms = _timed(step.fwd, n, max(warmup, 10), step.stream)
+        out.update({"fwd_ms": round(ms, 5), "fwd_tflops": round(_tf(fwd_flops, ms), 2),
+                    "fwd_frac": round(_tf(fwd_flops, ms) / PEAK_TFLOPS, 4), "timed_calls": n,
+                    "note": "latency-bound (grid of a few workgroups); warm caches"})
+        del step
+        torch.cuda.empty_cache()
+        return out
+    stage_ms, _ = step.time(steps, warmup)
+    ms_fwd = stage_ms["fwd"]
+    ms_step = sum(stage_ms.values())
+    out.update({"fwd_ms": round(ms_fwd, 4), "fwd_tflops": round(_tf(fwd_flops, ms_fwd), 2),
+                "fwd_frac": round(_tf(fwd_flops, ms_fwd) / PEAK_TFLOPS, 4),
+                "bwd_ms": round(ms_step - ms_fwd, 4), "fwdbwd_ms": round(ms_step, 4),
+                "fwdbwd_tflops": round(_tf(3.5 * fwd_flops, ms_step), 2),
+                "fwdbwd_frac": round(_tf(3.5 * fwd_flops, ms_step) / PEAK_TFLOPS, 4),
+                "bwd_path": "stored P and dS" if step.ws is not None else "recompute (O(N) memory)",
+                "workspace_gib": round(step.ws_bytes / 2**30, 3),
+                "forward_kernel": "key-range split + merge" if step.fws is not None else "one launch",
+                "kernels": step.kernel_table(stage_ms)})
+    del step
+    torch.cuda.empty_cache()
+    return out
+
+
+def varlen_config_leg(F, W, w, seed: int, steps: int, warmup: int, store_ds_modes=(True, False)) -> dict:
+    """Packed varlen forward and backward through ffpa_varlen_fwd / ffpa_varlen_bwd (workspaces
+    allocated outside the timed region), for each backward path in store_ds_modes."""
+    import torch
+    dev = torch.device("cuda:0")
+    lens = W.varlen_lengths(w.batch, seed)
+    q, k, v, do, cu_q, cu_k = W.workload_inputs(w, seed, device="cuda")
+    cq, ck = cu_q.to(dev), cu_k.to(dev)
+    cu_host = cu_q.tolist()
+    tq, hq, d = q.shape
+    hkv = k.shape[1]
+    mx = max(lens)
+    lib = F.load_library()
+    P = F._binding._ptr
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    dt = 0 if q.dtype == torch.bfloat16 else 1
+    scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, tq), dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    pairs = hq * sum(n * (n + 1) // 2 for n in lens)
+    fwd_flops = 4.0 * d * pairs
+
+    def fwd():
+        _check(F, lib.ffpa_varlen_fwd(P(q), P(k), P(v), P(o), P(lse), P(cq), P(ck), w.batch, mx, mx, tq, tq, hq, hkv,
+                                      d, dt, scale, 1, sp))
+
+    ms_fwd = _timed(fwd, steps, warmup, stream)
+    out = {"workload": w.name, "sequences": w.batch, "lengths": lens, "total_tokens": tq, "heads": hq,
+           "head_dim": d, "causal": True, "dtype": w.dtype, "credited_fwd_flops": fwd_flops,
+           "fwd_ms": round(ms_fwd, 4), "fwd_tflops": round(_tf(fwd_flops, ms_fwd), 2),
+           "fwd_frac": round(_tf(fwd_flops, ms_fwd) / PEAK_TFLOPS, 4)}
+    import ctypes
+    host = (ctypes.c_int32 * len(cu_host))(*cu_host)
+    hp = ctypes.cast(host, ctypes.c_void_p)
+    for store_ds in store_ds_modes:
+        nws = F.ffpa_varlen_bwd_workspace_bytes_exact(hq, cu_host, cu_host, tq, tq, mx, mx) if store_ds else 0
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws > 0 else None
+
+        def bwd():
+            _check(F, lib.ffpa_varlen_bwd(P(q), P(k), P(v), P(o), P(do), P(lse), None, P(delta), P(dq), P(dk), P(dv),
+                                          P(cq), P(ck), hp, hp, w.batch, mx, mx, tq, tq, hq, hkv, d, dt, scale, 1,
+                                          P(ws), nws, sp))
+
+        ms_bwd = _timed(bwd, steps, warmup, stream)
+        key = "" if store_ds else "recompute_"
+        tot = ms_fwd + ms_bwd
+        out.update({f"{key}bwd_ms": round(ms_bwd, 4), f"{key}fwdbwd_ms": round(tot, 4),
+                    f"{key}fwdbwd_tflops": round(_tf(3.5 * fwd_flops, tot), 2),
+                    f"{key}fwdbwd_frac": round(_tf(3.5 * fwd_flops, tot) / PEAK_TFLOPS, 4),
+                    f"{key}workspace_gib": round(nws / 2**30, 3)})
+        del ws
+        torch.cuda.empty_cache()
+    out["workspace_bound_gib"] = round(F.ffpa_varlen_bwd_workspace_bytes(hq, tq, tq, mx, mx) / 2**30, 3)
+    return out
 
 
 def decode_leg(F, W, w, seed: int, steps: int, warmup: int) -> dict:
@@ -123,21 +349,10 @@ def decode_leg(F, W, w, seed: int, steps: int, warmup: int) -> dict:
     dt = 0 if w.dtype == "bf16" else 1
 
     def run():
-        st = lib.ffpa_decode_fwd(P(qd), P(kd), P(vd), P(o), P(lse), b, hq, hkv, nq, nkv, d, dt,
-                                 1.0 / math.sqrt(d), int(w.causal), P(ws), nws, stream.cuda_stream)
-        if st:
-            raise RuntimeError(F.ffpa_status_string(st))
+        _check(F, lib.ffpa_decode_fwd(P(qd), P(kd), P(vd), P(o), P(lse), b, hq, hkv, nq, nkv, d, dt,
+                                      1.0 / math.sqrt(d), int(w.causal), P(ws), nws, stream.cuda_stream))
 
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    ev[0].record(stream)
-    for i in range(steps):
-        run()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps
+    ms = _timed(run, steps, warmup, stream)
     el = qd.element_size()
     kv_bytes = 2.0 * b * hkv * nkv * d * el
     part_bytes = 2.0 * nws  # partial O and LSE written once, read once
@@ -170,31 +385,45 @@ def fp8_leg(F, qd, kd, vd, causal: bool, pairs: int, steps: int, warmup: int) ->
     dt = 0 if qd.dtype == torch.bfloat16 else 1
 
     def run():
-        st = lib.ffpa_fwd_fp8(P(qd), P(kd), P(vd), P(o), P(lse), b, hq, hkv, nq, nkv, d, dt, 1.0 / math.sqrt(d),
-                              int(causal), P(ws), nws, stream.cuda_stream)
-        if st:
-            raise RuntimeError(F.ffpa_status_string(st))
+        _check(F, lib.ffpa_fwd_fp8(P(qd), P(kd), P(vd), P(o), P(lse), b, hq, hkv, nq, nkv, d, dt, 1.0 / math.sqrt(d),
+                                   int(causal), P(ws), nws, stream.cuda_stream))
 
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    ev[0].record(stream)
-    for i in range(steps):
-        run()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps
-    tf = 4.0 * d * pairs / (ms * 1e-3) / 1e12
+    ms = _timed(run, steps, warmup, stream)
+    tf = _tf(4.0 * d * pairs, ms)
     return {"ms": round(ms, 4), "includes": "amax and quantization pre-pass + FP8 forward kernel",
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / FP8_PEAK_TFLOPS, 4), "traffic": load_traffic("fp8_fwd")},
             "vs_bf16_fwd": None}
 
 
+def host_description() -> dict:
+    """CPU model (/proc/cpuinfo), the CPUs this process may run on, and NumPy's BLAS build."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        import threadpoolctl
+        infos = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            i = infos[0]
+            blas = f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', 'n/a')} threads, " \
+                   f"{i.get('architecture', 'n/a')})"
+    except Exception:  # noqa: BLE001 - description only
+        pass
+    return {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)), "blas": blas}
+
+
 def cpu_baseline(q, k, v, do, scale, causal, dq, dk, dv, o, lse, tol_o, budget_s=10.0):
     """Time the float64 oracle on whole KV groups of the same inputs (batch 0, KV heads 0, 1, ...)
-    until about `budget_s` seconds of CPU work have run.
+    until about `budget_s` seconds of CPU work have run, with BLAS limited to the CPUs this
+    process may use (len(os.sched_getaffinity(0)) threads).
 
     Returns (baseline dict, parity dict): the same runs check the GPU's O, LSE, dQ, dK, dV for those
     groups in full.
@@ -207,7 +436,7 @@ def cpu_baseline(q, k, v, do, scale, causal, dq, dk, dv, o, lse, tol_o, budget_s
     hkv = k.shape[1]
     g = q.shape[1] // hkv
     nq, nkv, d = q.shape[2], k.shape[2], q.shape[3]
-    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    cores = len(os.sched_getaffinity(0))
     s64 = float(np.float32(scale))
 
     def relerr(x, y):
@@ -215,33 +444,51 @@ def cpu_baseline(q, k, v, do, scale, causal, dq, dk, dv, o, lse, tol_o, budget_s
 
     par = {"o_max_abs": 0.0, "lse_max_abs": 0.0, "dq_rel_l2": 0.0, "dk_rel_l2": 0.0, "dv_rel_l2": 0.0}
     elapsed, groups = 0.0, 0
-    while groups < hkv and (groups == 0 or elapsed < budget_s):
-        kv = groups
-        hs = slice(kv * g, (kv + 1) * g)
-        qg, dog = q[0, hs].double().numpy(), do[0, hs].double().numpy()
-        kg, vg = k[0, kv].double().numpy(), v[0, kv].double().numpy()
-        t0 = time.perf_counter()
-        dq_r, dk_r, dv_r, o_r, lse_r = ref.group_backward(qg, kg, vg, dog, s64, causal)[:5]
-        elapsed += time.perf_counter() - t0
-        groups += 1
-        fin = np.isfinite(lse_r)
-        lg = lse[0, hs].double().cpu().numpy()
-        par["o_max_abs"] = max(par["o_max_abs"], float(np.max(np.abs(o[0, hs].double().cpu().numpy() - o_r))))
-        if fin.any():
-            par["lse_max_abs"] = max(par["lse_max_abs"], float(np.max(np.abs(lg[fin] - lse_r[fin]))))
-        par["dq_rel_l2"] = max(par["dq_rel_l2"], relerr(dq[0, hs].double().cpu().numpy(), dq_r))
-        par["dk_rel_l2"] = max(par["dk_rel_l2"], relerr(dk[0, kv].double().cpu().numpy(), dk_r))
-        par["dv_rel_l2"] = max(par["dv_rel_l2"], relerr(dv[0, kv].double().cpu().numpy(), dv_r))
+    with threadpoolctl.threadpool_limits(limits=cores, user_api="blas"):
+        used = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+                   or [1])
+        while groups < hkv and (groups == 0 or elapsed < budget_s):
+            kv = groups
+            hs = slice(kv * g, (kv + 1) * g)
+            qg, dog = q[0, hs].double().numpy(), do[0, hs].double().numpy()
+            kg, vg = k[0, kv].double().numpy(), v[0, kv].double().numpy()
+            t0 = time.perf_counter()
+            dq_r, dk_r, dv_r, o_r, lse_r = ref.group_backward(qg, kg, vg, dog, s64, causal)[:5]
+            elapsed += time.perf_counter() - t0
+            groups += 1
+            fin = np.isfinite(lse_r)
+            lg = lse[0, hs].double().cpu().numpy()
+            par["o_max_abs"] = max(par["o_max_abs"], float(np.max(np.abs(o[0, hs].double().cpu().numpy() - o_r))))
+            if fin.any():
+                par["lse_max_abs"] = max(par["lse_max_abs"], float(np.max(np.abs(lg[fin] - lse_r[fin]))))
+            par["dq_rel_l2"] = max(par["dq_rel_l2"], relerr(dq[0, hs].double().cpu().numpy(), dq_r))
+            par["dk_rel_l2"] = max(par["dk_rel_l2"], relerr(dk[0, kv].double().cpu().numpy(), dk_r))
+            par["dv_rel_l2"] = max(par["dv_rel_l2"], relerr(dv[0, kv].double().cpu().numpy(), dv_r))
     flops = 14.0 * d * legal_pairs(nq, nkv, causal) * g * groups
-    base = {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+    host = host_description()
+    base = {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOPS", "cores": int(min(used, cores)),
+            "kind": "oracle",
             "sample": f"float64 NumPy oracle forward+backward of {groups} of {hkv} KV groups "
                       f"({groups * g} of {q.shape[1]} query heads, batch 0) of the same inputs: "
                       f"{elapsed:.2f} s, credited {flops:.3e} flops",
-            "seconds": round(elapsed, 3), "cpu": platform.processor() or platform.machine()}
+            "seconds": round(elapsed, 3), "cpu": host["cpu_model"], "affinity_cpus": host["affinity_cpus"],
+            "blas_threads": int(used), "blas": host["blas"]}
     par["sample"] = f"KV groups 0..{groups - 1} of batch 0, all rows"
     par["pass"] = bool(par["o_max_abs"] <= tol_o and par["lse_max_abs"] <= 1e-3 and
                        max(par["dq_rel_l2"], par["dk_rel_l2"], par["dv_rel_l2"]) <= 2e-2)
     return base, par
+
+
+def run_legs(F, W, names, seed: int, steps: int, warmup: int) -> dict:
+    legs = {}
+    for name in names:
+        w = W.get(name)
+        print(f"bench: timing configuration {name}", file=sys.stderr, flush=True)
+        if w.varlen:
+            legs[name] = varlen_config_leg(F, W, w, seed, steps, warmup)
+        else:
+            legs[name] = dense_config_leg(F, W, w, seed, steps, warmup)
+    return legs
 
 
 def main(argv=None) -> int:
@@ -251,107 +498,53 @@ def main(argv=None) -> int:
               "(heads are independent, so more GPUs would each run a share of the heads)", file=sys.stderr)
         return 2
 
-    import torch
-
     import head_dim_attention_amd as F
     import workloads as W
 
+    if args.only_legs:
+        names = [n for n in args.only_legs.split(",") if n]
+        for n in names:
+            if n not in W.WORKLOADS:
+                print(f"bench.py: unknown workload {n}", file=sys.stderr)
+                return 2
+    else:
+        w = W.get(args.workload)
+        if w.varlen or not w.backward:
+            print(f"bench.py: the step needs a dense forward+backward workload; {w.name} is timed as a "
+                  "configuration leg (--only-legs)", file=sys.stderr)
+            return 2
+
+    import torch
+
     F.load_library()
-    w = W.get(args.workload)
-    if w.varlen or not w.backward:
-        print(f"bench.py: {w.name} is not a dense forward+backward workload; choose one that is", file=sys.stderr)
-        return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.only_legs:
+        print(json.dumps({"configs": run_legs(F, W, names, args.seed, max(args.steps, 5), args.warmup)}), flush=True)
+        return 0
+
     q, k, v, do = W.workload_inputs(w, args.seed)
     qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
-    b, hq, nq, d = qd.shape
-    hkv, nkv = kd.shape[1], kd.shape[2]
-    scale = 1.0 / math.sqrt(d)
+    step = DenseStep(F, qd, kd, vd, dod, w.causal, not args.no_ds_workspace)
+    b, hq, hkv, nq, nkv, d = step.dims
     causal = w.causal
 
-    o = torch.empty_like(qd)
-    lse = torch.empty((b, hq, nq), dtype=torch.float32, device=dev)
-    delta = torch.empty_like(lse)
-    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-    lib = F.load_library()
-    ws_bytes = 0 if args.no_ds_workspace else F.ffpa_bwd_workspace_bytes(b, hq, nq, nkv)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
-    flops_d = dict(KERNEL_FLOPS_PER_PAIR_D)
-    if ws is not None:
-        flops_d.update(STORED_FLOPS_PER_PAIR_D)
-        if d > 512:  # the dK kernel recomputes and stores P and dS itself; the P/dS launch is empty
-            flops_d.update({"pds": 0, "dk": 6})
-    dt = 0 if w.dtype == "bf16" else 1
-    stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
-    P = F._binding._ptr
-
-    # Grids too small to fill the GPU take the key-range split forward (its workspace allocated
-    # here, outside the timed region); the headline grid needs none.
-    fws_bytes = F.ffpa_fwd_split_workspace_bytes(b, hq, hkv, nq, nkv, d)
-    fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev) if fws_bytes > 0 else None
-
-    def fwd():
-        if fws is None:
-            st = lib.ffpa_fwd(P(qd), P(kd), P(vd), P(o), P(lse), b, hq, hkv, nq, nkv, d, dt, scale, int(causal), sp)
-        else:
-            st = lib.ffpa_fwd_split(P(qd), P(kd), P(vd), P(o), P(lse), b, hq, hkv, nq, nkv, d, dt, scale, int(causal),
-                                    P(fws), fws_bytes, sp)
-        if st:
-            raise RuntimeError(F.ffpa_status_string(st))
-
-    def bwd_stage(i):
-        st = lib.ffpa_bwd_stage(i, P(qd), P(kd), P(vd), P(o), P(dod), P(lse), P(delta), P(dq), P(dk), P(dv),
-                                b, hq, hkv, nq, nkv, d, dt, scale, int(causal), P(ws), ws_bytes, sp)
-        if st:
-            raise RuntimeError(F.ffpa_status_string(st))
-
-    launches = [fwd] + [(lambda i=i: bwd_stage(i)) for _, i in BWD_STAGES]
-
-    for _ in range(args.warmup):
-        for fn in launches:
-            fn()
-    torch.cuda.synchronize()
-    print(f"bench: warmup done ({args.warmup} steps), timing {args.steps} steps of {w.name}", file=sys.stderr,
-          flush=True)
-
-    # Events on the stream the kernels are launched on, between every launch of every step.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        ev[s][0].record(stream)
-        for i, fn in enumerate(launches):
-            fn()
-            ev[s][i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    stage_ms = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
-                for i, name in enumerate(STAGES)}
+    for fn in step.launches:  # one untimed pass before the warmup message
+        fn()
+    print(f"bench: warmup ({args.warmup} steps), timing {args.steps} steps of {w.name}", file=sys.stderr, flush=True)
+    stage_ms, wall_ms = step.time(args.steps, args.warmup)
     step_ms = sum(stage_ms.values())
 
-    pairs = legal_pairs(nq, nkv, causal) * b * hq
+    pairs = step.pairs
     fwd_flops = 4.0 * d * pairs
     fb_flops = 14.0 * d * pairs
-    value = fb_flops / (wall_ms * 1e-3) / 1e12
-    fwd_tflops = fwd_flops / (stage_ms["fwd"] * 1e-3) / 1e12
+    value = _tf(fb_flops, wall_ms)
+    fwd_tflops = _tf(fwd_flops, stage_ms["fwd"])
 
     # Dominant kernel: the longest of the compute kernels.
-    dom = max((n for n in COMPUTE_KERNELS if flops_d[n] > 0), key=lambda n: stage_ms[n])
-    dom_flops = flops_d[dom] * d * pairs
-    achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
-    traffic = load_traffic(dom)
-    kernels = {}
-    for n in COMPUTE_KERNELS:
-        if flops_d[n] == 0:
-            continue
-        fl = flops_d[n] * d * pairs
-        kernels[n] = {"ms": round(stage_ms[n], 4), "algorithmic_tflops": round(fl / (stage_ms[n] * 1e-3) / 1e12, 2),
-                      "frac": round(fl / (stage_ms[n] * 1e-3) / 1e12 / PEAK_TFLOPS, 4)}
-    pre_bytes = 2.0 * b * hq * nq * d * qd.element_size() + 4.0 * b * hq * nq
-    kernels["pre"] = {"ms": round(stage_ms["pre"], 4), "algorithmic_gbs": round(pre_bytes / (stage_ms["pre"] * 1e-3) / 1e9, 1),
-                      "frac": round(pre_bytes / (stage_ms["pre"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    dom = max((n for n in COMPUTE_KERNELS if step.flops_d[n] > 0), key=lambda n: stage_ms[n])
+    achieved = _tf(step.flops_d[dom] * d * pairs, stage_ms[dom])
 
     out = {
         "metric": METRIC,
@@ -373,16 +566,12 @@ def main(argv=None) -> int:
         "fwdbwd_frac_of_peak": round(value / PEAK_TFLOPS, 4),
         "peak_tflops": PEAK_TFLOPS,
         "event_ms_per_step": round(step_ms, 4),
-        "bwd_path": (f"stored P and dS ({ws_bytes / 2**30:.2f} GiB workspace): dK = dS^T Q, dV = P^T dO, dQ = dS K"
-                     if ws is not None else "dK, dV and dQ recompute S, P (dP, dS)"),
-        "kernels": kernels,
+        "bwd_path": (f"stored P and dS ({step.ws_bytes / 2**30:.2f} GiB workspace): dK = dS^T Q, dV = P^T dO, "
+                     "dQ = dS K" if step.ws is not None else "dK, dV and dQ recompute S, P (dP, dS)"),
+        "kernels": step.kernel_table(stage_ms),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic},
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": load_traffic(dom)},
     }
-
-    if args.decode_workload != "none":
-        print(f"bench: timing the split-KV decode pass on {args.decode_workload}", file=sys.stderr, flush=True)
-        out["decode"] = decode_leg(F, W, W.get(args.decode_workload), args.seed, max(args.steps, 10), args.warmup)
 
     if not args.no_fp8:
         print("bench: timing the FP8 forward on the same inputs", file=sys.stderr, flush=True)
@@ -390,6 +579,45 @@ def main(argv=None) -> int:
         if "ms" in f8:
             f8["vs_bf16_fwd"] = round(stage_ms["fwd"] / f8["ms"], 3)
         out["fp8_fwd"] = f8
+
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on whole KV groups", file=sys.stderr, flush=True)
+        base, par = cpu_baseline(q, k, v, do, 1.0 / math.sqrt(d), causal, step.dq, step.dk, step.dv, step.o,
+                                 step.lse, 2e-2 if w.dtype == "bf16" else 4e-3)
+        out["cpu_baseline"] = base
+        out["parity"] = par
+    else:
+        out["cpu_baseline"] = None
+
+    if not args.no_configs:
+        # The O(N)-memory backward of the same shape, beside the stored-P/dS one.
+        ws_keep = step.ws
+        step.ws, step.ws_bytes = None, 0
+        step.flops_d = dict(KERNEL_FLOPS_PER_PAIR_D)
+        print("bench: timing the recomputing backward on the same inputs", file=sys.stderr, flush=True)
+        rs_ms, _ = step.time(max(args.steps // 2, 5), 1)
+        bwd_rec = sum(rs_ms[n] for n, _ in BWD_STAGES)
+        rec = {"workload": w.name, "bwd_ms": round(bwd_rec, 4),
+               "fwdbwd_tflops": round(_tf(fb_flops, rs_ms["fwd"] + bwd_rec), 2),
+               "fwdbwd_frac": round(_tf(fb_flops, rs_ms["fwd"] + bwd_rec) / PEAK_TFLOPS, 4),
+               "stored_ds_bwd_ms": round(step_ms - stage_ms["fwd"], 4),
+               "stored_ds_workspace_gib": round((ws_keep.numel() if ws_keep is not None else 0) / 2**30, 3),
+               "kernels": step.kernel_table(rs_ms)}
+        del ws_keep, step
+        del qd, kd, vd, dod
+        torch.cuda.empty_cache()
+        out["configs"] = run_legs(F, W, CONFIG_LEGS, args.seed, max(args.steps // 2, 5), args.warmup)
+        vl = out["configs"].get("varlen_causal_d512", {})
+        out["recompute_bwd"] = {w.name: rec}
+        if "recompute_bwd_ms" in vl:
+            out["recompute_bwd"]["varlen_causal_d512"] = {
+                "bwd_ms": vl["recompute_bwd_ms"], "fwdbwd_tflops": vl["recompute_fwdbwd_tflops"],
+                "fwdbwd_frac": vl["recompute_fwdbwd_frac"], "stored_ds_bwd_ms": vl["bwd_ms"],
+                "stored_ds_workspace_gib": vl["workspace_gib"]}
+
+    if args.decode_workload != "none":
+        print(f"bench: timing the split-KV decode pass on {args.decode_workload}", file=sys.stderr, flush=True)
+        out["decode"] = decode_leg(F, W, W.get(args.decode_workload), args.seed, max(args.steps, 10), args.warmup)
 
     if args.calib_copy_mib > 0:
         nbytes = args.calib_copy_mib << 20
@@ -399,13 +627,6 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    if not args.no_cpu_baseline:
-        print("bench: timing the CPU oracle on one KV group", file=sys.stderr, flush=True)
-        base, par = cpu_baseline(q, k, v, do, scale, causal, dq, dk, dv, o, lse, 2e-2 if w.dtype == "bf16" else 4e-3)
-        out["cpu_baseline"] = base
-        out["parity"] = par
-    else:
-        out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
     return 0
 

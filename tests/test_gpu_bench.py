@@ -1,5 +1,6 @@
 """bench.py's output contract on the GPU: one JSON line with the metric, the whole-step value, the
-dominant kernel's roofline object, and the decode and FP8 legs with their own rooflines (a short
+dominant kernel's roofline object, the decode and FP8 legs with their own rooflines, the other
+configurations and the recomputing backward (a short
 run: two timed steps, no CPU baseline)."""
 import json
 import os
@@ -34,3 +35,15 @@ def test_bench_json_line():
     assert dec["bound"] == "hbm" and dec["unit"] == "GB/s" and 0 < dec["frac"] < 1
     f8 = d["fp8_fwd"]["roofline"]
     assert f8["bound"] == "mfma" and 0 < f8["frac"] < 1 and f8["peak"] > roof["peak"]
+    # every other configuration of the benchmark set, and the recomputing backward beside the stored one
+    cfg = d["configs"]
+    assert set(cfg) == {"fwd_d320_n512", "causal_d512_n4096", "gqa_causal_d1024_n8192", "varlen_causal_d512"}
+    assert cfg["fwd_d320_n512"]["fwd_ms"] > 0 and "bwd_ms" not in cfg["fwd_d320_n512"]
+    for name in ("causal_d512_n4096", "gqa_causal_d1024_n8192", "varlen_causal_d512"):
+        c = cfg[name]
+        assert 0 < c["fwd_frac"] < 1 and 0 < c["fwdbwd_frac"] < 1, name
+        assert c["fwdbwd_ms"] > c["fwd_ms"] > 0, name
+    assert cfg["gqa_causal_d1024_n8192"]["kernels"]["dk"]["ms"] > 0
+    assert cfg["varlen_causal_d512"]["workspace_gib"] <= cfg["varlen_causal_d512"]["workspace_bound_gib"]
+    rec = d["recompute_bwd"]
+    assert rec["dense_d512_n8192"]["bwd_ms"] > 0 and rec["varlen_causal_d512"]["bwd_ms"] > 0

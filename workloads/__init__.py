@@ -61,23 +61,25 @@ def get(name: str) -> Workload:
     return WORKLOADS[name]
 
 
-def _gen(seed: int) -> torch.Generator:
-    g = torch.Generator(device="cpu")
+def _gen(seed: int, device: str = "cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     return g
 
 
 def _draw(g: torch.Generator, shape, dtype: torch.dtype, scale: float) -> torch.Tensor:
-    x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    x = torch.randn(*shape, generator=g, dtype=torch.float32, device=g.device)
     if scale != 1.0:
         x = x * scale
     return x.to(dtype)
 
 
 def dense_inputs(b: int, hq: int, hkv: int, nq: int, nkv: int, d: int, dtype: torch.dtype, seed: int,
-                 input_scale: float = 1.0, with_grad: bool = True):
-    """Return (q, k, v, do) CPU tensors: q/do [b,hq,nq,d], k/v [b,hkv,nkv,d]."""
-    g = _gen(seed)
+                 input_scale: float = 1.0, with_grad: bool = True, device: str = "cpu"):
+    """Return (q, k, v, do) tensors: q/do [b,hq,nq,d], k/v [b,hkv,nkv,d]. ``device`` other than the
+    CPU draws the same distribution with that device's generator (different values; for timing
+    large inputs without a host round trip)."""
+    g = _gen(seed, device)
     q = _draw(g, (b, hq, nq, d), dtype, input_scale)
     k = _draw(g, (b, hkv, nkv, d), dtype, input_scale)
     v = _draw(g, (b, hkv, nkv, d), dtype, input_scale)
@@ -100,12 +102,13 @@ def cu_from_lengths(lengths) -> torch.Tensor:
 
 
 def varlen_inputs(lengths_q, lengths_k, hq: int, hkv: int, d: int, dtype: torch.dtype, seed: int,
-                  input_scale: float = 1.0, with_grad: bool = True):
-    """Return (q, k, v, do, cu_q, cu_k): packed [T, H, D] tensors and int32 cumulative lengths."""
+                  input_scale: float = 1.0, with_grad: bool = True, device: str = "cpu"):
+    """Return (q, k, v, do, cu_q, cu_k): packed [T, H, D] tensors and int32 cumulative lengths (CPU;
+    ``device`` as in dense_inputs for the packed tensors)."""
     cu_q = cu_from_lengths(lengths_q)
     cu_k = cu_from_lengths(lengths_k)
     tq, tk = int(cu_q[-1]), int(cu_k[-1])
-    g = _gen(seed + 1)
+    g = _gen(seed + 1, device)
     q = _draw(g, (tq, hq, d), dtype, input_scale)
     k = _draw(g, (tk, hkv, d), dtype, input_scale)
     v = _draw(g, (tk, hkv, d), dtype, input_scale)
@@ -113,9 +116,11 @@ def varlen_inputs(lengths_q, lengths_k, hq: int, hkv: int, d: int, dtype: torch.
     return q, k, v, do, cu_q, cu_k
 
 
-def workload_inputs(w: Workload, seed: int, varlen_lengths_override: Optional[list] = None):
-    """Inputs for a named workload. Varlen lengths come from ``varlen_lengths(w.batch, seed)``."""
+def workload_inputs(w: Workload, seed: int, varlen_lengths_override: Optional[list] = None, device: str = "cpu"):
+    """Inputs for a named workload. Varlen lengths come from ``varlen_lengths(w.batch, seed)`` (always
+    the CPU generator, so they do not depend on ``device``)."""
     if w.varlen:
         lens = varlen_lengths_override if varlen_lengths_override is not None else varlen_lengths(w.batch, seed)
-        return varlen_inputs(lens, lens, w.hq, w.hkv, w.d, w.torch_dtype, seed, w.input_scale, w.backward)
-    return dense_inputs(w.batch, w.hq, w.hkv, w.n_q, w.n, w.d, w.torch_dtype, seed, w.input_scale, w.backward)
+        return varlen_inputs(lens, lens, w.hq, w.hkv, w.d, w.torch_dtype, seed, w.input_scale, w.backward, device)
+    return dense_inputs(w.batch, w.hq, w.hkv, w.n_q, w.n, w.d, w.torch_dtype, seed, w.input_scale, w.backward,
+                        device)
