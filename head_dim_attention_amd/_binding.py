@@ -21,7 +21,7 @@ __all__ = [
     "library_path", "load_library", "ffpa_status_string",
     "ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd",
     "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes_exact",
-    "ffpa_decode_fwd", "choose_store_ds",
+    "ffpa_decode_fwd", "ffpa_decode_fwd_noalloc", "choose_store_ds",
     "ffpa_decode_workspace_bytes", "ffpa_fwd_fp8", "ffpa_fwd_fp8_workspace_bytes", "ffpa_fwd_split_workspace_bytes",
 ]
 
@@ -31,6 +31,9 @@ FFPA_OK = 0
 FFPA_ERR_INVALID_ARGUMENT = 1
 FFPA_ERR_NOT_SUPPORTED = 2
 FFPA_ERR_HIP = 3
+FFPA_ERR_TOO_LARGE = 4
+# Fixed device scratch of ffpa_decode_fwd_noalloc (FFPA_NOALLOC_SCRATCH_BYTES in include/ffpa.h).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _DTYPES = {torch.bfloat16: 0, torch.float16: 1}
 _LIB = None
@@ -50,6 +53,7 @@ _SIGNATURES = {
     "ffpa_fwd_split": [_vp] * 5 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "ffpa_bwd_masked": [_vp] * 11 + [_i] * 6 + [_vp, _i, _i64p, _vp, _i, _f, _i, _vp, _sz, _vp],
     "ffpa_decode_fwd_strided": [_vp] * 5 + [_i] * 6 + [_i64p, _i, _f, _i, _vp, _sz, _vp],
+    "ffpa_decode_fwd_noalloc": [_vp] * 5 + [_i] * 7 + [_f, _i, _vp],
     "ffpa_bwd": [_vp] * 11 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "ffpa_bwd_stage": [_i] + [_vp] * 11 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "ffpa_varlen_fwd": [_vp] * 7 + [_i] * 9 + [_f, _i, _vp],
@@ -102,7 +106,7 @@ def _raise_for(status: int, name: str) -> None:
     if status == FFPA_OK:
         return
     msg = f"{name}: {ffpa_status_string(status)}"
-    if status == FFPA_ERR_INVALID_ARGUMENT:
+    if status in (FFPA_ERR_INVALID_ARGUMENT, FFPA_ERR_TOO_LARGE):
         raise ValueError(msg)
     if status == FFPA_ERR_NOT_SUPPORTED:
         raise NotImplementedError(msg)
@@ -292,6 +296,32 @@ def ffpa_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: b
                                        strides, _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(ws),
                                        nws, _stream(q))
     _raise_for(st, "ffpa_decode_fwd")
+    return o, lse
+
+
+def ffpa_decode_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                            scale: Optional[float] = None, out=None):
+    """ffpa_decode_fwd through the library's fixed scratch (no workspace allocation). Packed
+    [B, H, N, D] inputs; ``out`` = (o, lse) preallocated outputs (then this call allocates nothing
+    at all), else they are allocated here. Sizes whose decode workspace exceeds
+    NOALLOC_SCRATCH_BYTES raise ValueError. Calls that overlap on one GPU race on the scratch."""
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    _same(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,Hq,Nq,D] and k, v [B,Hkv,Nkv,D]")
+    b, hq, nq, d = q.shape
+    _, hkv, nkv, _ = k.shape
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((b, hq, nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        if not (o.is_contiguous() and o.shape == q.shape and o.dtype == q.dtype and lse.is_contiguous()
+                and lse.shape == (b, hq, nq) and lse.dtype == torch.float32):
+            raise ValueError("out must be contiguous (o like q, lse float32 [B,Hq,Nq])")
+    st = load_library().ffpa_decode_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, hq, hkv, nq, nkv,
+                                                d, _dtype_code(q), _scale(scale, d), int(bool(causal)), _stream(q))
+    _raise_for(st, "ffpa_decode_fwd_noalloc")
     return o, lse
 
 

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/ffpa.h"
 #include "ffpa_params.h"
@@ -20,7 +21,30 @@ hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total
 
 using ffpa::AttnParams;
 
+// Fixed device scratch of ffpa_decode_fwd_noalloc (partial O and LSE of the split-KV decode). In
+// host code `scratch` is only a stand-in for the symbol: its device address, per device, comes
+// from hipGetSymbolAddress and is the only form passed to kernels.
+static __device__ __align__(256) char scratch[FFPA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device (with that device
+// current); NULL on failure.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 bool bad_dtype(int dtype) { return dtype != FFPA_DTYPE_BF16 && dtype != FFPA_DTYPE_FP16; }
 
@@ -471,6 +495,24 @@ ffpa_status_t ffpa_decode_fwd_strided(const void* q, const void* k, const void* 
                     workspace_bytes, stream);
 }
 
+ffpa_status_t ffpa_decode_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                                      int hq, int hkv, int nq, int nkv, int d, ffpa_dtype_t dtype, float scale,
+                                      int causal, hipStream_t stream) {
+  // Every argument check of ffpa_decode_fwd first (a stand-in workspace pointer that is never
+  // dereferenced), then the size against the fixed scratch; only then the scratch address.
+  if (!q || !k || !v || !o || !lse) return FFPA_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
+  const ffpa_status_t st = check_common(hq, hkv, d, dtype, scale, causal);
+  if (st != FFPA_OK) return st;
+  if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
+  if ((long long)batch * hq * nq > (1LL << 31) - 1) return FFPA_ERR_INVALID_ARGUMENT;
+  if (decode_ws_bytes(batch, hq, hkv, nq, nkv, d) > FFPA_NOALLOC_SCRATCH_BYTES) return FFPA_ERR_TOO_LARGE;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return FFPA_ERR_HIP;
+  return decode_fwd(q, k, v, o, lse, batch, hq, hkv, nq, nkv, d, nullptr, dtype, scale, causal, ws,
+                    FFPA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 size_t ffpa_varlen_bwd_workspace_bytes(int hq, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k) {
   return varlen_ds_bytes(hq, total_q, total_k, max_seqlen_q, max_seqlen_k);
 }
@@ -573,6 +615,8 @@ const char* ffpa_status_string(ffpa_status_t status) {
     case FFPA_ERR_INVALID_ARGUMENT: return "FFPA_ERR_INVALID_ARGUMENT: invalid argument";
     case FFPA_ERR_NOT_SUPPORTED: return "FFPA_ERR_NOT_SUPPORTED: head dim must be a multiple of 32 in [320, 1024]";
     case FFPA_ERR_HIP: return "FFPA_ERR_HIP: a HIP launch or runtime call failed";
+    case FFPA_ERR_TOO_LARGE:
+      return "FFPA_ERR_TOO_LARGE: the sizes need more than the fixed decode scratch (use ffpa_decode_fwd with a workspace)";
     default: return "FFPA_ERR_UNKNOWN: unknown status code";
   }
 }

@@ -77,7 +77,8 @@ typedef enum {
   FFPA_OK = 0,
   FFPA_ERR_INVALID_ARGUMENT = 1, /* null pointer, size < 1, Hq % Hkv != 0, bad enum, causal not 0/1, scale <= 0 */
   FFPA_ERR_NOT_SUPPORTED = 2,    /* D outside [320, 1024] or D % 32 != 0 */
-  FFPA_ERR_HIP = 3               /* a HIP launch or runtime call failed */
+  FFPA_ERR_HIP = 3,              /* a HIP launch or runtime call failed */
+  FFPA_ERR_TOO_LARGE = 4         /* ffpa_decode_fwd_noalloc: the call needs more than the fixed scratch */
 } ffpa_status_t;
 
 /*
@@ -204,6 +205,27 @@ ffpa_status_t ffpa_decode_fwd_strided(const void* q, const void* k, const void* 
  * invalid sizes. Host function; launches nothing.
  */
 size_t ffpa_decode_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, int d);
+
+/* Bytes of the library's fixed device scratch used by ffpa_decode_fwd_noalloc (32 MiB per GPU). */
+#define FFPA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * ffpa_decode_fwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments (minus the workspace), checks and results as ffpa_decode_fwd; the partial results go
+ * to a fixed device array of FFPA_NOALLOC_SCRATCH_BYTES inside the library instead of a caller
+ * workspace. It calls no hipMalloc/hipFree: each GPU the library runs on holds its own copy of the
+ * array from the first call on that device until the process ends.
+ *   - Sizes whose ffpa_decode_workspace_bytes() exceeds FFPA_NOALLOC_SCRATCH_BYTES return
+ *     FFPA_ERR_TOO_LARGE (nothing launched); use ffpa_decode_fwd with a workspace for them.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's contents (every
+ *     entry a call reads is written earlier in the same call, so no clearing is needed). Calls
+ *     that overlap on one GPU (on different streams, or from different threads without ordering)
+ *     race on it and give undefined results: serialize them on one stream.
+ */
+ffpa_status_t ffpa_decode_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+    int batch, int hq, int hkv, int nq, int nkv, int d,
+    ffpa_dtype_t dtype, float scale, int causal, hipStream_t stream);
 
 /*
  * Bytes of the optional P/dS workspace of ffpa_bwd / ffpa_bwd_stage for these sizes:

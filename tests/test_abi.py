@@ -393,3 +393,18 @@ def test_fwd_split_workspace_and_validation(lib):
         return lib.ffpa_fwd_split(P, P, P, P, P, b, hq, hkv, nq, nkv, d, 0, ctypes.c_float(0.04), 1, ws, nws, S)
     assert call(ws=N) == 1 and call(nws=1024) == 1
     assert call(hq=3, hkv=2, ws=N) == 1       # no split for invalid sizes: ffpa_fwd's checks apply
+
+
+def test_decode_noalloc_validation(lib):
+    """ffpa_decode_fwd_noalloc checks every argument, then its sizes against the fixed scratch,
+    before it touches the device (fake pointers: nothing is dereferenced)."""
+    from head_dim_attention_amd import _binding as B
+    args = lambda b, hq, hkv, nq, nkv, d, dt=0, scale=0.04, causal=1: (P, P, P, P, P, b, hq, hkv, nq, nkv, d, dt,
+                                                                         scale, causal, S)
+    assert lib.ffpa_decode_fwd_noalloc(*args(0, 32, 8, 1, 4096, 512)) == 1
+    assert lib.ffpa_decode_fwd_noalloc(*args(1, 32, 8, 1, 4096, 300)) == 2
+    assert lib.ffpa_decode_fwd_noalloc(*args(1, 32, 8, 1, 4096, 512, dt=3)) == 1
+    assert lib.ffpa_decode_fwd_noalloc(N, P, P, P, P, 1, 32, 8, 1, 4096, 512, 0, 0.04, 1, S) == 1
+    assert B.ffpa_decode_workspace_bytes(64, 32, 8, 7, 4096, 1024) > B.NOALLOC_SCRATCH_BYTES
+    assert lib.ffpa_decode_fwd_noalloc(*args(64, 32, 8, 7, 4096, 1024)) == B.FFPA_ERR_TOO_LARGE
+    assert "TOO_LARGE" in B.ffpa_status_string(B.FFPA_ERR_TOO_LARGE)
