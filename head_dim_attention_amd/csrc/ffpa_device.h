@@ -243,6 +243,12 @@ __device__ __forceinline__ int opaque_v(int x) {
   return x;
 }
 
+// Opaque scalar (wave-uniform) value: like opaque_v, for values kept in scalar registers.
+__device__ __forceinline__ uint32_t opaque_s(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
 // This lane's index in its wave, read from the hardware at this point (not a value the compiler
 // may keep in a register across a loop).
 __device__ __forceinline__ int fresh_lane_id() {

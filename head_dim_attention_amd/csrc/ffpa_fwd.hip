@@ -206,10 +206,16 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     const int pc = (i % IPR) * 64 + lane;
     voff[ii] = src_chunk(pc ^ swz(R)) << 4;
   }
+  // Single-buffered eight-wave tiles: the column offsets are rebuilt from the hardware lane index
+  // at each copy instead of holding NINSTR registers across the loop.
+  constexpr bool kFreshOff = NBUF == 1 && NW == 8;
   auto issue1 = [&](const Src& x, int j, lds_t* dst, int ii) {
     const int i = w + NW * ii;
     const int row = min(j * 32 + i / IPR, sv.lk - 1);
-    dma16_buf(x.rs, voff[ii], row * x.rb, dst + i * 1024);
+    const int vo = kFreshOff ? src_chunk(((i % IPR) * 64 + fresh_lane_id()) ^ swz(i / IPR)) << 4 : voff[ii];
+    lds_t* d = dst + i * 1024;
+    if constexpr (kFreshOff) d = (lds_t*)(uintptr_t)opaque_s((uint32_t)(uintptr_t)d);
+    dma16_buf(x.rs, vo, row * x.rb, d);
   };
   auto issue = [&](const Src& x, int j, lds_t* dst) {
 #pragma unroll
@@ -305,6 +311,9 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   // exchange buffer; copy_at(kb) issues the tile copies assigned to k-step kb.
   auto s_partial = [&](int j, f32x16_t (&sacc)[QB], auto&& copy_at) {
     const lds_t* kt = kbuf(NBUF == 2 ? (j & 1) : 0);
+    // (single-buffered eight waves: an opaque base, so that the constant operand addresses are
+    // formed at each use instead of held in registers across the loop)
+    const uint32_t kta = kFreshOff ? (uint32_t)opaque_v((int)lds_addr(kt)) : lds_addr(kt);
     if constexpr (MASK && kPingPong) {
       if (cg == 0) {
 #pragma unroll
@@ -320,7 +329,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     }
 #pragma unroll
     for (int kb = 0; kb < 2 * NDB; ++kb) {
-      const u32x4_t a = lds_read_b128_at(k_addr(lds_addr(kt), kb));
+      const u32x4_t a = lds_read_b128_at(k_addr(kta, kb));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) sacc[qb] = Elt<T>::mma(a, qreg[qb][kb], sacc[qb]);
       copy_at(kb);
@@ -349,6 +358,12 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
         if constexpr (NC == 4) {
           const int o0 = base + ((cg & 2) ^ 2);
           mine = mine + (rd(o0) + rd(o0 + 1));
+        }
+        // Eight single-buffered waves: the sums of each half of the block are complete before
+        // the next half's partner reads are issued (all twelve reads at once would need 48
+        // registers the wave does not have).
+        if constexpr (kFreshOff) {
+          if (r4 & 1) asm volatile("" : "+v"(mine) : : "memory");
         }
         sacc[qb][4 * r4] = mine.x; sacc[qb][4 * r4 + 1] = mine.y;
         sacc[qb][4 * r4 + 2] = mine.z; sacc[qb][4 * r4 + 3] = mine.w;
@@ -426,12 +441,13 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   // O^T += V^T P^T for tile j; copy_at(m) issues the copies assigned to MFMA m.
   auto pv_mma = [&](int j, const uint32_t (&pb)[QB][2][4], auto&& copy_at) {
     const lds_t* vt = vbuf(NBUF == 2 ? (j & 1) : 0);
+    const uint32_t vta = kFreshOff ? (uint32_t)opaque_v((int)lds_addr(vt)) : lds_addr(vt);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const s16x4_t lo = lds_read_tr16_at(v_addr(lds_addr(vt), db, kb2, 0));
-        const s16x4_t hi = lds_read_tr16_at(v_addr(lds_addr(vt), db, kb2, 1));
+        const s16x4_t lo = lds_read_tr16_at(v_addr(vta, db, kb2, 0));
+        const s16x4_t hi = lds_read_tr16_at(v_addr(vta, db, kb2, 1));
         const u32x4_t a = join_tr(lo, hi);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -558,6 +574,36 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     }
   } else {
 
+  if constexpr (kFreshOff) {
+    // Eight waves, single-buffered: one loop with the lazily updated reference max (rescale only
+    // when a tile max exceeds the reference by more than 2^8), as in the two-group schedule.
+    for (int j = jbeg; j < jend; ++j) {
+      top(j);
+      scores(j, sacc);
+      float mt[QB];
+      tile_max(sacc, mt);
+      bool grow = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (mref[qb] == -INFINITY) mref[qb] = mt[qb];
+        grow |= mt[qb] > mref[qb] + 8.0f;
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const bool nd = mt[qb] > mref[qb] + 8.0f;
+          const float alpha = nd ? fast_exp2(mref[qb] - mt[qb]) : 1.0f;
+          if (nd) mref[qb] = mt[qb];
+          lsum[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
+        }
+      }
+      uint32_t pb[QB][2][4];
+      make_p(sacc, pb);
+      pv(j, pb);
+    }
+  } else {
   // ---- fast loop: the reference max of a row is fixed at its first finite tile max. The loop
   // leaves (per wave) as soon as a tile max exceeds the reference by more than 2^8, so O never
   // needs rescaling here and exp2 stays below 256.
@@ -601,6 +647,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     make_p(sacc, pb);
     pv(j, pb);
   }
+  }  // !kFreshOff
   }  // !kPingPong
 
   // Copies issued during the last step land in LDS that the next workgroup may own.
@@ -657,12 +704,9 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   }
 }
 
-template <class T, int NC, int NDB>
-static hipError_t launch_fwd_cfg(AttnParams p, hipStream_t st) {
-  static_assert(NC == 2 || NC == 4, "head-dim split");
+template <class T, int NC, int NDB, int NW, bool MASK>
+static hipError_t launch_fwd_nw(AttnParams p, hipStream_t st) {
   constexpr int QB = 1;
-  // Two waves per SIMD where the per-wave state fits 256 registers (D <= 512), else one.
-  constexpr int NW = NC == 2 ? 8 : 4;
   using C1 = FwdCfg<NC, NDB, QB, 1, NW>;
   constexpr int NBUF = (2 * 2 * C1::TILE + C1::XBYTES) <= 160 * 1024 ? 2 : 1;
   using C = FwdCfg<NC, NDB, QB, NBUF, NW>;
@@ -670,11 +714,20 @@ static hipError_t launch_fwd_cfg(AttnParams p, hipStream_t st) {
   p.total = p.batch * p.hq * p.ntiles;
   if (p.total == 0) return hipSuccess;
   const int grid = (p.total + 7) & ~7;
-  if (p.mask_kind != 0)
-    hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF, NW, false, true>), dim3(grid), dim3(64 * NW), 0, st, p);
-  else
-    hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF, NW>), dim3(grid), dim3(64 * NW), 0, st, p);
+  hipLaunchKernelGGL((ffpa_fwd_kernel<T, NC, NDB, QB, NBUF, NW, false, MASK>), dim3(grid), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
+}
+
+// Eight waves (two per SIMD): 128 queries per workgroup for D <= 512 (two head-dim halves,
+// double-buffered 32 KB tiles), 64 for D > 512 (four head-dim quarters, single-buffered 64 KB K and
+// V tiles: each copied K/V byte then feeds twice the queries of a four-wave workgroup). The masked
+// form above D = 896 keeps four waves (32 queries): its mask registers do not fit beside the
+// 256-column operands in the 256 registers of a two-wave SIMD.
+template <class T, int NC, int NDB>
+static hipError_t launch_fwd_cfg(AttnParams p, hipStream_t st) {
+  static_assert(NC == 2 || NC == 4, "head-dim split");
+  if (p.mask_kind != 0) return launch_fwd_nw<T, NC, NDB, (NC == 4 && NDB == 8) ? 4 : 8, true>(p, st);
+  return launch_fwd_nw<T, NC, NDB, 8, false>(p, st);
 }
 
 // Merge of the key-range split forward: many rows, few ranges. One wave per output row (four rows
@@ -721,7 +774,7 @@ __global__ void __launch_bounds__(256) ffpa_split_combine_kernel(AttnParams p, i
 // Key-range split count of a dense forward: 1 when the grid gives at least two workgroups per
 // compute unit (of 256), else enough ranges for that, up to 8 and with at least 4 key tiles each.
 int fwd_split_count(int batch, int hq, int nq, int nkv, int d) {
-  const int bq = d <= 512 ? 128 : 32;  // queries per workgroup of the forward configurations
+  const int bq = d <= 512 ? 128 : 64;  // queries per workgroup of the forward configurations
   const long long base = (long long)batch * hq * ((nq + bq - 1) / bq);
   const long long ktiles = (nkv + 31) / 32;
   if (base <= 0 || base >= 512) return 1;
@@ -731,7 +784,7 @@ int fwd_split_count(int batch, int hq, int nq, int nkv, int d) {
 template <class T, int NC, int NDB>
 static hipError_t launch_fwd_split_cfg(AttnParams p, int nsplit, float* ws, hipStream_t st) {
   constexpr int QB = 1;
-  constexpr int NW = NC == 2 ? 8 : 4;
+  constexpr int NW = 8;
   using C1 = FwdCfg<NC, NDB, QB, 1, NW>;
   constexpr int NBUF = (2 * 2 * C1::TILE + C1::XBYTES) <= 160 * 1024 ? 2 : 1;
   using C = FwdCfg<NC, NDB, QB, NBUF, NW>;
