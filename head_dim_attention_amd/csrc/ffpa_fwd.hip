@@ -479,7 +479,8 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
 
   if (jend > jbeg) {
     issue(ksrc, jbeg, kbuf(NBUF == 2 ? (jbeg & 1) : 0));
-    issue(vsrc, jbeg, vbuf(NBUF == 2 ? (jbeg & 1) : 0));
+    // (single-buffered eight waves copy V_j during the step's score products)
+    if constexpr (!kFreshOff) issue(vsrc, jbeg, vbuf(NBUF == 2 ? (jbeg & 1) : 0));
   }
   // The Q operands (and tile 0) are complete before the loop, so the loop never waits for them.
   wait_all();
@@ -575,11 +576,24 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   } else {
 
   if constexpr (kFreshOff) {
-    // Eight waves, single-buffered: one loop with the lazily updated reference max (rescale only
-    // when a tile max exceeds the reference by more than 2^8), as in the two-group schedule.
+    // Eight waves, single-buffered K and V tiles (64 KB each). The copies are spread over the
+    // MFMAs (a burst of them would hold every wave at the copy issue, which drains at about 64
+    // bytes per clock per CU): V_j during the score products of step j (V_{j-1} was last read
+    // before the barrier that opens the step) and K_{j+1} during the P V products of step j (K_j
+    // was last read before the exchange barrier). K_{j+1} is issued on the last step too (rows
+    // clamped, into a buffer no longer read) so that no branch splits the MFMA sequence. One loop
+    // with the lazily updated reference max (rescale only when a tile max exceeds the reference
+    // by more than 2^8), as in the two-group schedule.
     for (int j = jbeg; j < jend; ++j) {
-      top(j);
-      scores(j, sacc);
+      wait_vmcnt<0>();  // K_j: the only copies in flight
+      lds_barrier();
+      s_partial(j, sacc, [&](int kb) {
+#pragma unroll
+        for (int ii = 0; ii < C::NINSTR; ++ii)
+          if (kb == spread_at(2 * NDB, ii)) issue1(vsrc, j, vbuf(0), ii);
+      });
+      lds_barrier();  // partial sums visible; K_j released
+      s_combine(j, sacc);
       float mt[QB];
       tile_max(sacc, mt);
       bool grow = false;
@@ -601,7 +615,13 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
       }
       uint32_t pb[QB][2][4];
       make_p(sacc, pb);
-      pv(j, pb);
+      wait_vmcnt<0>();  // V_j (and any mask bits of the tile)
+      lds_barrier();
+      pv_mma(j, pb, [&](int m) {
+#pragma unroll
+        for (int ii = 0; ii < C::NINSTR; ++ii)
+          if (m == spread_at(2 * NDB, ii)) issue1(ksrc, j + 1, kbuf(0), ii);
+      });
     }
   } else {
   // ---- fast loop: the reference max of a row is fixed at its first finite tile max. The loop
