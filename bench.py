@@ -154,8 +154,6 @@ class DenseStep:
         self.flops_d = dict(KERNEL_FLOPS_PER_PAIR_D)
         if self.ws is not None:
             self.flops_d.update(STORED_FLOPS_PER_PAIR_D)
-            if d > 512:  # the dK kernel recomputes and stores P and dS itself; the P/dS launch is empty
-                self.flops_d.update({"pds": 0, "dk": 6})
         self.pairs = legal_pairs(nq, nkv, causal) * b * hq
         self.launches = [self.fwd] + [(lambda i=i: self.bwd_stage(i)) for _, i in BWD_STAGES]
 

@@ -1206,8 +1206,284 @@ static hipError_t launch_pds(AttnParams p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------------------
+// P and dS for D > 512 (the stored-P/dS backward's P/dS stage at large head dims).
+//
+// The forward's D > 512 layout: a workgroup owns 64 queries of one head as 2 row groups x 4
+// head-dim quarters (8 waves, two per SIMD); each wave keeps its 32 queries' Q and dO columns of
+// its quarter in registers (B operands, 2 x 64 registers at D = 1024) and forms partial
+// S^T = K Q^T and dP^T = V dO^T from K and V tiles (32 keys x 2 KB, single-buffered: 64 KB each)
+// streamed through LDS. The four quarters are combined by a reduce-scatter: register group
+// r4 = c of a C block (4 registers: keys 16 (c / 2) + 8 h + 4 (c % 2) + 0..3 of lane half h)
+// belongs to the wave with quarter c, which receives the three partners' partial sums of it
+// through its LDS inbox, forms P = exp(scale S - LSE) and dS = P (dP - Delta) for those 8 keys x 32
+// queries, and stores them transposed (one row per key, 8 queries per 16-byte piece) after a
+// transposition through its own inbox slot. Per step (32 keys):
+//   wait K_j | S products (V_j copies spread over them) | S partials out | wait V_j, barrier |
+//   S partials in | dP products (K_{j+1} copies spread over them) | P | barrier | dP partials out |
+//   barrier | dP partials in, dS, transposition, stores
+// so each tile copy overlaps the other tile's products, and the exchange moves 3 register groups
+// per wave instead of the forward's all-reduce of 4 x 3.
+// ------------------------------------------------------------------------------------------------
+template <int NDB>
+struct PdsWideCfg {
+  static constexpr int NW = 8;
+  static constexpr int NC = 4;                      // head-dim quarters
+  static constexpr int DW = NDB * 32;               // head-dim columns per wave
+  static constexpr int KSTEPS = 2 * NDB;            // 16-wide k-steps over them
+  static constexpr int RS = 2048;                   // LDS row stride (bytes)
+  static constexpr int BQ = 2 * 32;                 // queries per workgroup
+  static constexpr int TILE = 32 * RS;              // one 32-key K or V tile
+  static constexpr int WCH = NDB * 4;               // 16-byte chunks of one wave's columns
+  static constexpr int SLOT = RS / 16 / NC;         // chunks per wave slot of an LDS row
+  static constexpr int XSLOT = 64 * 16;             // one register group of one wave
+  static constexpr int XBYTES = NW * NC * XSLOT;    // inbox[wave][source quarter]
+  static constexpr int LDS = 2 * TILE + XBYTES;
+  static constexpr int NINSTR = TILE / 1024 / NW;   // 1 KB copies per wave per tile
+  static_assert(NC * DW <= 1024 && WCH <= SLOT && SLOT % 16 == 0 && LDS <= 160 * 1024, "LDS budget");
+};
+
+// MASK adds the attn_mask term of each owned (query, key) pair to its score before P, as in the
+// forward (the tile's mask bits are requested when its score products start).
+template <class T, int NDB, bool MASK>
+__global__ void __launch_bounds__(512, 2) ffpa_pds_wide_kernel(AttnParams p) {
+  using C = PdsWideCfg<NDB>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
+  lds_t* const kbuf = (lds_t*)smem_raw;
+  lds_t* const vbuf = kbuf + C::TILE;
+  lds_t* const xbuf = kbuf + 2 * C::TILE;
+
+  const int L = blockIdx.x;
+  const int item = xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hq, p.ntiles * p.nsplit);
+  if (item >= p.total) return;
+  const int split = item % p.nsplit;
+  int t = (item / p.nsplit) % p.ntiles;
+  const int hs = item / p.nsplit / p.ntiles;
+  const int h = hs % p.hq;
+  const int s = hs / p.hq;
+  if (p.causal) t = p.ntiles - 1 - t;  // heaviest causal tiles first
+
+  const SeqView sv = seq_view(p, s);
+  const int qt0 = t * C::BQ;
+  if (qt0 >= sv.lq) return;
+  const DsView dsv = ds_view(p, s, sv);
+  const int kvh = h / p.group;
+
+  const int w = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int rg = w / C::NC;
+  const int cg = w % C::NC;
+  const int qw0 = qt0 + rg * 32;
+  const int off = sv.lk - sv.lq;
+
+  const int row_bytes = p.k_row * 2;
+  const long long kv_off = sv.k_off + (long long)kvh * p.k_head;
+  const uint32_t span = (uint32_t)min((long long)max(sv.lk, 1) * row_bytes, (long long)0xFFFFFFF0);
+  const i32x4_t krs = make_rsrc((const uint16_t*)p.k + kv_off, span);
+  const i32x4_t vrs = make_rsrc((const uint16_t*)p.v + kv_off, span);
+  int kend = sv.lk;
+  if (p.causal) kend = min(kend, qt0 + C::BQ + off);
+  const int ntk = kend > 0 ? (kend + 31) >> 5 : 0;
+  // This item's key tiles [jb, je): an equal share of the query tile's own range.
+  const int per = (ntk + p.nsplit - 1) / p.nsplit;
+  const int jb = min(split * per, ntk), je = min(jb + per, ntk);
+  if (jb >= je && split > 0) return;
+
+  // Q and dO columns of this wave's quarter as B operands: lane (h, n) holds query n, dims
+  // 16 kb + 8 h + 0..7 of the quarter.
+  const int qi = qw0 + l32;
+  const long long qrow = sv.q_off + (long long)h * p.q_head + (long long)min(qi, sv.lq - 1) * p.q_row;
+  u32x4_t qreg[C::KSTEPS], oreg[C::KSTEPS];
+#pragma unroll
+  for (int kb = 0; kb < C::KSTEPS; ++kb) {
+    const int dim = cg * C::DW + kb * 16 + hh * 8;
+    const bool in = dim < p.d;
+    qreg[kb] = in ? *(const u32x4_t*)((const uint16_t*)p.q + qrow + dim) : (u32x4_t){0u, 0u, 0u, 0u};
+    oreg[kb] = in ? *(const u32x4_t*)((const uint16_t*)p.dout + qrow + dim) : (u32x4_t){0u, 0u, 0u, 0u};
+  }
+  // The query's LSE in log2 units (+inf for a row without a legal key makes P = 0) and Delta.
+  const long long li = sv.lse_off + (long long)h * p.lse_head + min(qi, sv.lq - 1);
+  const float lse_raw = p.lse_in[li];
+  const float lse2 = lse_raw == -INFINITY ? INFINITY : lse_raw * kLog2e;
+  const float dlt = p.delta[li];
+
+  // The head's P and dS blocks (Lk rows of round_up(Lq, 8) queries).
+  const long long hoff = dsv.base + (long long)h * dsv.head;
+  const int nrec = (int)((long long)sv.lk * dsv.row * 2);
+  const __amdgpu_buffer_rsrc_t ds_rs = __builtin_amdgcn_make_buffer_rsrc((uint16_t*)p.ds + hoff, 0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t p_rs = __builtin_amdgcn_make_buffer_rsrc((uint16_t*)p.pst + hoff, 0, nrec, 0x00020000);
+
+  // Copies: instruction ii of wave w fills LDS bytes [1024 i, 1024 i + 1024) of a tile,
+  // i = w + 8 ii, i.e. tile row R = i / 2; lane l writes physical chunk pc = (i % 2) 64 + l, whose
+  // un-swizzled index u = pc ^ swz(R) is chunk u % SLOT of quarter u / SLOT (padding and chunks
+  // past the head dim hold clamped, finite duplicates). Offsets and LDS addresses are rebuilt at
+  // each copy (no registers held across the loop for them).
+  const int dch = p.d >> 3;
+  auto src_chunk = [&](int u) { return min((u / C::SLOT) * C::WCH + min(u % C::SLOT, C::WCH - 1), dch - 1); };
+  auto copy1 = [&](const i32x4_t& rs, lds_t* tile, int j, int ii) {
+    const int i = w + C::NW * ii;
+    const int row = min(j * 32 + (i >> 1), sv.lk - 1);
+    const int vo = src_chunk((((i & 1) << 6) + fresh_lane_id()) ^ swz(i >> 1)) << 4;
+    lds_t* d = (lds_t*)(uintptr_t)opaque_s((uint32_t)(uintptr_t)(tile + i * 1024));
+    dma16_buf(rs, vo, row * row_bytes, d);
+  };
+  auto spread_at = [](int n, int ii) { return (ii * n) / C::NINSTR; };
+
+  // K and V rows (A operands): MFMA row m reads tile row row_perm(m), chunk cbase + 2 kb + h.
+  const int krow = row_perm(l32);
+  const int kswz = swz(krow);
+  const uint32_t klane = krow * C::RS + ((cg * C::SLOT) << 4) + ((hh ^ kswz) << 4);
+  auto a_addr = [&](uint32_t tile, int kb) -> uint32_t {
+    return ((tile + klane) ^ ((kb & 7) << 5)) + ((kb >> 3) << 8);
+  };
+  // Inbox slot of wave `dst` for partial sums from quarter `src`; a wave's own slot (src = its
+  // quarter) holds its P and dS transposition.
+  auto inbox = [&](int dst, int src) { return xbuf + (dst * C::NC + src) * C::XSLOT; };
+  const int w0 = rg * C::NC;
+  // Owned keys: register group cg, keys 16 (cg / 2) + 4 (cg % 2) + 8 h + 0..3 of the tile.
+  const int kown = 16 * (cg >> 1) + 4 * (cg & 1);
+
+  auto send = [&](const f32x16_t& acc) {
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c)
+      if (c != cg)
+        lds_write_f4(inbox(w0 + c, cg), lane * 16, (f32x4_t){acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]});
+  };
+  // Own register group plus the three partners' partial sums, in quarter order (deterministic).
+  auto receive = [&](const f32x16_t& acc) {
+    f32x4_t r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+      const f32x4_t x = c == cg ? (f32x4_t){acc[4 * cg], acc[4 * cg + 1], acc[4 * cg + 2], acc[4 * cg + 3]}
+                                : lds_read_f4(inbox(w, c), lane * 16);
+      r = c == 0 ? x : r + x;
+    }
+    return r;
+  };
+
+  if (je > jb) {
+#pragma unroll
+    for (int ii = 0; ii < C::NINSTR; ++ii) copy1(krs, kbuf, jb, ii);
+  }
+  wait_all();  // the stationary operands, LSE, Delta and K_jb
+  lds_barrier();
+
+  f32x16_t sacc, pacc;
+  // attn_mask: the aligned 8-key block that holds this lane's 4 owned keys of the tile.
+  const long long mrow = MASK ? mask_row(p, s, h, min(qi, sv.lq - 1)) : 0;
+  u32x4_t mraw;
+  for (int j = jb; j < je; ++j) {
+    // K_j landed (copied during the dP products of step j - 1; the two stores of that step may
+    // still be in flight).
+    if (j > jb) {
+      wait_vmcnt<2>();
+      lds_barrier();
+    }
+    if constexpr (MASK) {
+      mraw = mask_block(p, mrow, j * 32 + 16 * (cg >> 1) + 8 * hh, sv.lk);
+      __builtin_amdgcn_sched_barrier(0);  // issued here, not sunk behind the products
+    }
+    const uint32_t kt = (uint32_t)opaque_v((int)lds_addr(kbuf)), vt = (uint32_t)opaque_v((int)lds_addr(vbuf));
+    sacc = (f32x16_t){};
+#pragma unroll
+    for (int kb = 0; kb < C::KSTEPS; ++kb) {
+      sacc = Elt<T>::mma(lds_read_b128_at(a_addr(kt, kb)), qreg[kb], sacc);
+#pragma unroll
+      for (int ii = 0; ii < C::NINSTR; ++ii)
+        if (kb == spread_at(C::KSTEPS, ii)) copy1(vrs, vbuf, j, ii);
+    }
+    pin_lds_mfma_pipeline<C::KSTEPS, kPdsAhead, 1>();
+    send(sacc);
+    wait_vmcnt<0>();  // V_j (and the stores of step j - 1)
+    lds_barrier();    // S partials visible; K_j released
+    const f32x4_t s4 = receive(sacc);
+    pacc = (f32x16_t){};
+#pragma unroll
+    for (int kb = 0; kb < C::KSTEPS; ++kb) {
+      pacc = Elt<T>::mma(lds_read_b128_at(a_addr(vt, kb)), oreg[kb], pacc);
+#pragma unroll
+      for (int ii = 0; ii < C::NINSTR; ++ii)
+        if (kb == spread_at(C::KSTEPS, ii)) copy1(krs, kbuf, j + 1, ii);  // past the last tile: clamped, unused
+    }
+    pin_lds_mfma_pipeline<C::KSTEPS, kPdsAhead, 1>();
+    // P of the owned keys (0 past the key bound and, on diagonal tiles, above the causal limit).
+    const int key0 = j * 32 + kown + 8 * hh;
+    const bool need_mask = (j * 32 + 32 > sv.lk) || (p.causal && j * 32 + 31 > qw0 + off);
+    const int lim = p.causal ? min(qi + off, sv.lk - 1) : sv.lk - 1;
+    float sown[4] = {s4[0], s4[1], s4[2], s4[3]};
+    if constexpr (MASK) {
+      float mb[8];
+      mask_apply8_block<T>(p, mraw, mrow, j * 32 + 16 * (cg >> 1) + 8 * hh, sv.lk, mb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sown[e] += mb[4 * (cg & 1) + e];
+    }
+    float pe[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = fast_exp2(sown[e] * p.scale_log2 - lse2);
+      pe[e] = need_mask && key0 + e > lim ? 0.f : x;
+    }
+    lds_barrier();  // every wave has read its S partials: the inboxes take the dP partials
+    send(pacc);
+    lds_barrier();
+    const f32x4_t d4 = receive(pacc);
+    // Transposition through the own slot: P at [key kk][query n] (8 rows of 64 bytes), dS 512
+    // bytes further; lane (h, n) owns keys kk = 4 h + e.
+    lds_t* const tb = inbox(w, cg);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t pk = Elt<T>::pack2(pe[e], pe[e] * (d4[e] - dlt));
+      const int o = (4 * hh + e) * 64 + 2 * l32;
+      *(__attribute__((address_space(3))) uint16_t*)(tb + o) = (uint16_t)(pk & 0xffffu);
+      *(__attribute__((address_space(3))) uint16_t*)(tb + 512 + o) = (uint16_t)(pk >> 16);
+    }
+    // Lane l stores one 16-byte piece: P for l < 32, dS for l >= 32; key kk = (l % 32) / 4,
+    // queries qw0 + 8 ((l % 4)) + 0..7. Pieces of keys at or past Lk, or starting at or past the
+    // padded row end, get an offset past the block, which the buffer range check discards.
+    const int kk = l32 >> 2, g = l32 & 3;
+    const u32x4_t piece = lds_read_b128(tb, hh * 512 + kk * 64 + g * 16);
+    const int key = j * 32 + 16 * (cg >> 1) + 4 * (cg & 1) + 8 * (kk >> 2) + (kk & 3);
+    const int q8 = qw0 + 8 * g;
+    const bool ok = key < sv.lk && q8 < dsv.row;
+    const uint32_t boff = ok ? (uint32_t)(((long long)key * dsv.row + q8) * 2) : 0xFFFFFFF0u;
+    if (hh == 0)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, piece), p_rs, (int)boff, 0, kDsStoreCpol);
+    else
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, piece), ds_rs, (int)boff, 0, kDsStoreCpol);
+  }
+  // Copies issued during the last step land in LDS that the next workgroup may own.
+  wait_vmcnt<0>();
+}
+
+template <class T, int NDB>
+static hipError_t launch_pds_wide(AttnParams p, hipStream_t st) {
+  using C = PdsWideCfg<NDB>;
+  p.ntiles = (p.nq + C::BQ - 1) / C::BQ;
+  const long long base = (long long)p.batch * p.hq * p.ntiles;
+  const int ktiles = (p.nkv + 31) / 32;
+  p.nsplit = (int)std::max(1LL, std::min({8LL, (512 + base - 1) / std::max(base, 1LL), (long long)ktiles / 4}));
+  p.total = p.batch * p.hq * p.ntiles * p.nsplit;
+  if (p.total == 0) return hipSuccess;
+  const int grid = (p.total + 7) & ~7;
+  if (p.mask_kind != 0)
+    hipLaunchKernelGGL((ffpa_pds_wide_kernel<T, NDB, true>), dim3(grid), dim3(64 * C::NW), 0, st, p);
+  else
+    hipLaunchKernelGGL((ffpa_pds_wide_kernel<T, NDB, false>), dim3(grid), dim3(64 * C::NW), 0, st, p);
+  return hipGetLastError();
+}
+
 template <class T>
 static hipError_t launch_pds_t(const AttnParams& p, hipStream_t st) {
+  if (p.d > 512) {
+    switch ((p.d + 127) / 128) {
+      case 5: return launch_pds_wide<T, 5>(p, st);
+      case 6: return launch_pds_wide<T, 6>(p, st);
+      case 7: return launch_pds_wide<T, 7>(p, st);
+      default: return launch_pds_wide<T, 8>(p, st);
+    }
+  }
   switch ((p.d + 63) / 64) {
     case 5: return launch_pds<T, 5>(p, st);
     case 6: return launch_pds<T, 6>(p, st);
@@ -1922,11 +2198,10 @@ static hipError_t launch_stage_t(int stage, const AttnParams& p, int nrows, int 
         return hipGetLastError();
       }
       return hipSuccess;
-    // With a workspace, stage 4 stores P and dS (for D > 512 the dK kernel stores them as it goes)
-    // and dK, dV, dQ are products of them.
-    case 4: return p.ds != nullptr && p.d <= 512 ? launch_pds_t<T>(p, st) : hipSuccess;
+    // With a workspace, stage 4 stores P and dS and dK, dV, dQ are products of them.
+    case 4: return p.ds != nullptr ? launch_pds_t<T>(p, st) : hipSuccess;
     case 1: {
-      const hipError_t e = p.ds != nullptr && p.d <= 512 ? launch_dv_p_t<T, true>(p, st) : launch_bwd_mode<T, kDK>(p, st);
+      const hipError_t e = p.ds != nullptr ? launch_dv_p_t<T, true>(p, st) : launch_bwd_mode<T, kDK>(p, st);
       // The attn_mask gradient, once dS is stored (stage 4 for D <= 512, the dK kernel above otherwise).
       if (e != hipSuccess || p.dmask == nullptr) return e;
       return launch_dbias_t<T>(p, st);
