@@ -51,11 +51,12 @@ FP8_PEAK_TFLOPS = 5033.2
 # does 4 D (S, P^T dO), dK and dQ 6 D (S, dP, one product); with the stored P and dS the P/dS
 # kernel does 4 D (S, dP) and dK, dV, dQ are one product each, 2 D.
 KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "pds": 0, "dk": 6, "dv": 4, "dq": 6}
-STORED_FLOPS_PER_PAIR_D = {"pds": 4, "dk": 2, "dv": 2, "dq": 2}
-# (name, ffpa_bwd_stage index) of the timed launches after the forward, in ffpa_bwd's order.
+STORED_FLOPS_PER_PAIR_D = {"pds": 4, "dk": 2, "dv": 2, "dq": 2, "products": 6}
+# (name, ffpa_bwd_stage index) of the timed launches after the forward, in ffpa_bwd's order; for
+# small dense grids ffpa_bwd forms dK, dV and dQ in one launch (stage 5, "products").
 BWD_STAGES = (("pre", 0), ("pds", 4), ("dk", 1), ("dv", 2), ("dq", 3))
-STAGES = ("fwd",) + tuple(n for n, _ in BWD_STAGES)
-COMPUTE_KERNELS = ("fwd", "pds", "dk", "dv", "dq")
+BWD_STAGES_FUSED = (("pre", 0), ("pds", 4), ("products", 5))
+COMPUTE_KERNELS = ("fwd", "pds", "dk", "dv", "dq", "products")
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "traffic_dense_d512_n8192.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "head_dim_attention_amd", "csrc", f)
                   for f in ("ffpa_device.h", "ffpa_params.h", "ffpa_fwd.hip", "ffpa_bwd.hip", "ffpa_fp8.hip")]
@@ -151,11 +152,19 @@ class DenseStep:
         self.fws = torch.empty(self.fws_bytes, dtype=torch.uint8, device=dev) if self.fws_bytes > 0 else None
         self.dt = 0 if qd.dtype == torch.bfloat16 else 1
         self.stream = torch.cuda.current_stream(dev)
-        self.flops_d = dict(KERNEL_FLOPS_PER_PAIR_D)
+        self.pairs = legal_pairs(nq, nkv, causal) * b * hq
+        self.configure()
+
+    def configure(self):
+        """Launch list and per-kernel flops for the current workspace (as ffpa_bwd runs them)."""
+        b, hq, hkv, nq, nkv, d = self.dims
+        self.fused = self.ws is not None and self.F.ffpa_bwd_fused_products(b, hq, hkv, nq, nkv, d)
+        self.bwd_stages = BWD_STAGES_FUSED if self.fused else BWD_STAGES
+        self.stages = ("fwd",) + tuple(n for n, _ in self.bwd_stages)
+        self.flops_d = dict(KERNEL_FLOPS_PER_PAIR_D, products=0)
         if self.ws is not None:
             self.flops_d.update(STORED_FLOPS_PER_PAIR_D)
-        self.pairs = legal_pairs(nq, nkv, causal) * b * hq
-        self.launches = [self.fwd] + [(lambda i=i: self.bwd_stage(i)) for _, i in BWD_STAGES]
+        self.launches = [self.fwd] + [(lambda i=i: self.bwd_stage(i)) for _, i in self.bwd_stages]
 
     def fwd(self):
         P, (b, hq, hkv, nq, nkv, d) = self.F._binding._ptr, self.dims
@@ -195,14 +204,14 @@ class DenseStep:
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / steps
         stage_ms = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
-                    for i, name in enumerate(STAGES)}
+                    for i, name in enumerate(self.stages)}
         return stage_ms, wall_ms
 
     def kernel_table(self, stage_ms):
         d = self.dims[5]
         kernels = {}
         for n in COMPUTE_KERNELS:
-            if self.flops_d[n] == 0:
+            if self.flops_d[n] == 0 or n not in stage_ms:
                 continue
             fl = self.flops_d[n] * d * self.pairs
             kernels[n] = {"ms": round(stage_ms[n], 4), "algorithmic_tflops": round(_tf(fl, stage_ms[n]), 2),
@@ -259,7 +268,8 @@ def dense_config_leg(F, W, w, seed: int, steps: int, warmup: int, store_ds: bool
                 "bwd_ms": round(ms_step - ms_fwd, 4), "fwdbwd_ms": round(ms_step, 4),
                 "fwdbwd_tflops": round(_tf(3.5 * fwd_flops, ms_step), 2),
                 "fwdbwd_frac": round(_tf(3.5 * fwd_flops, ms_step) / PEAK_TFLOPS, 4),
-                "bwd_path": "stored P and dS" if step.ws is not None else "recompute (O(N) memory)",
+                "bwd_path": ("stored P and dS" + (", dK + dV + dQ in one launch" if step.fused else "")
+                             if step.ws is not None else "recompute (O(N) memory)"),
                 "workspace_gib": round(step.ws_bytes / 2**30, 3),
                 "forward_kernel": "key-range split + merge" if step.fws is not None else "one launch",
                 "kernels": step.kernel_table(stage_ms)})
@@ -541,7 +551,7 @@ def main(argv=None) -> int:
     fwd_tflops = _tf(fwd_flops, stage_ms["fwd"])
 
     # Dominant kernel: the longest of the compute kernels.
-    dom = max((n for n in COMPUTE_KERNELS if step.flops_d[n] > 0), key=lambda n: stage_ms[n])
+    dom = max((n for n in COMPUTE_KERNELS if step.flops_d[n] > 0 and n in stage_ms), key=lambda n: stage_ms[n])
     achieved = _tf(step.flops_d[dom] * d * pairs, stage_ms[dom])
 
     out = {
@@ -591,10 +601,10 @@ def main(argv=None) -> int:
         # The O(N)-memory backward of the same shape, beside the stored-P/dS one.
         ws_keep = step.ws
         step.ws, step.ws_bytes = None, 0
-        step.flops_d = dict(KERNEL_FLOPS_PER_PAIR_D)
+        step.configure()
         print("bench: timing the recomputing backward on the same inputs", file=sys.stderr, flush=True)
         rs_ms, _ = step.time(max(args.steps // 2, 5), 1)
-        bwd_rec = sum(rs_ms[n] for n, _ in BWD_STAGES)
+        bwd_rec = sum(rs_ms[n] for n, _ in step.bwd_stages)
         rec = {"workload": w.name, "bwd_ms": round(bwd_rec, 4),
                "fwdbwd_tflops": round(_tf(fb_flops, rs_ms["fwd"] + bwd_rec), 2),
                "fwdbwd_frac": round(_tf(fb_flops, rs_ms["fwd"] + bwd_rec) / PEAK_TFLOPS, 4),

@@ -6,7 +6,8 @@ streams only.
 """
 from ._binding import (  # noqa: F401
     FFPA_ERR_HIP, FFPA_ERR_INVALID_ARGUMENT, FFPA_ERR_NOT_SUPPORTED, FFPA_ERR_TOO_LARGE, FFPA_OK,
-    NOALLOC_SCRATCH_BYTES, choose_store_ds, ffpa_bwd, ffpa_bwd_stage, ffpa_bwd_workspace_bytes, ffpa_decode_fwd,
+    NOALLOC_SCRATCH_BYTES, choose_store_ds, ffpa_bwd, ffpa_bwd_fused_products, ffpa_bwd_stage, ffpa_bwd_workspace_bytes,
+    ffpa_decode_fwd,
     ffpa_decode_fwd_noalloc, ffpa_decode_workspace_bytes, ffpa_fwd, ffpa_fwd_fp8, ffpa_fwd_fp8_workspace_bytes,
     ffpa_fwd_split_workspace_bytes, ffpa_status_string, ffpa_varlen_bwd, ffpa_varlen_bwd_workspace_bytes,
     ffpa_varlen_bwd_workspace_bytes_exact, ffpa_varlen_fwd, library_path, load_library,

@@ -20,7 +20,7 @@ __all__ = [
     "FFPA_OK", "FFPA_ERR_INVALID_ARGUMENT", "FFPA_ERR_NOT_SUPPORTED", "FFPA_ERR_HIP",
     "library_path", "load_library", "ffpa_status_string",
     "ffpa_fwd", "ffpa_bwd", "ffpa_bwd_stage", "ffpa_varlen_fwd", "ffpa_varlen_bwd",
-    "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes_exact",
+    "ffpa_bwd_workspace_bytes", "ffpa_bwd_fused_products", "ffpa_varlen_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes_exact",
     "ffpa_decode_fwd", "ffpa_decode_fwd_noalloc", "choose_store_ds",
     "ffpa_decode_workspace_bytes", "ffpa_fwd_fp8", "ffpa_fwd_fp8_workspace_bytes", "ffpa_fwd_split_workspace_bytes",
 ]
@@ -92,6 +92,8 @@ def load_library():
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = _sz
+        lib.ffpa_bwd_fused_products.argtypes = [_i] * 6
+        lib.ffpa_bwd_fused_products.restype = ctypes.c_int
         lib.ffpa_status_string.argtypes = [ctypes.c_int]
         lib.ffpa_status_string.restype = ctypes.c_char_p
         _LIB = lib
@@ -372,6 +374,11 @@ def fp8_workspace_views(ws: torch.Tensor, b: int, hq: int, hkv: int, nkv: int, d
             ws[v8_off: v8_off + b * hkv * d * np_].view(b, hkv, d, np_))
 
 
+def ffpa_bwd_fused_products(batch: int, hq: int, hkv: int, nq: int, nkv: int, d: int) -> bool:
+    """Whether ffpa_bwd with a P/dS workspace forms dK, dV and dQ in one launch (stage 5)."""
+    return bool(load_library().ffpa_bwd_fused_products(int(batch), int(hq), int(hkv), int(nq), int(nkv), int(d)))
+
+
 def ffpa_bwd_workspace_bytes(batch: int, hq: int, nq: int, nkv: int) -> int:
     """Bytes of the optional P/dS workspace of the dense backward (0: not available)."""
     return int(load_library().ffpa_bwd_workspace_bytes(int(batch), int(hq), int(nq), int(nkv)))
@@ -516,12 +523,13 @@ def _bwd_masked(q, k, v, o, dout, lse, causal, scale, attn_mask, mask_grad, dlse
 def ffpa_bwd_stage(stage: int, q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool = False,
                    scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
                    dlse: Optional[torch.Tensor] = None):
-    """Run one backward stage (0 preprocess, 4 P and dS, 1 dK, 2 dV, 3 dQ) into caller buffers.
+    """Run one backward stage (0 preprocess, 4 P and dS, 1 dK, 2 dV, 3 dQ, 5 dK + dV + dQ in one
+    launch, workspace only) into caller buffers.
 
-    ffpa_bwd runs the stages in the order 0, 4, 1, 2, 3. All tensors must be contiguous GPU tensors
+    ffpa_bwd runs the stages in the order 0, 4, 1, 2, 3 (0, 4, 5 when ffpa_bwd_fused_products()). All tensors must be contiguous GPU tensors
     with ffpa_bwd's shapes; delta is float32 [B,Hq,Nq]. workspace: optional P/dS workspace (a GPU
     tensor of at least ffpa_bwd_workspace_bytes() bytes), the same for stages 4, 1, 2 and 3: stage 4
-    fills it (for D > 512 stage 1 does), and stages 1, 2 and 3 read it. Without a workspace stage 4
+    fills it, and stages 1, 2 and 3 read it. Without a workspace stage 4
     launches nothing and stages 1-3 recompute. dlse (stage 0 only reads it): as in ffpa_bwd.
     """
     if dlse is not None:

@@ -17,6 +17,7 @@ hipError_t launch_fwd_split(const AttnParams& p, int fp16, int nsplit, void* ws,
 int fwd_split_count(int batch, int hq, int nq, int nkv, int d);
 size_t fp8_workspace_bytes(int batch, int hq, int hkv, int nkv, int d);
 hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total, hipStream_t st, int stage);
+bool fused_products(const AttnParams& p);
 }  // namespace ffpa
 
 using ffpa::AttnParams;
@@ -410,7 +411,7 @@ static ffpa_status_t dense_bwd(int stage, const void* q, const void* k, const vo
                      int nq, int nkv, int d, int dtype, float scale, int causal, void* workspace,
                      size_t workspace_bytes, hipStream_t stream, const void* mask = nullptr, int mask_kind = 0,
                      const int64_t* mask_strides = nullptr, void* dmask = nullptr) {
-  if (stage < -1 || stage > 4) return FFPA_ERR_INVALID_ARGUMENT;
+  if (stage < -1 || stage > 5) return FFPA_ERR_INVALID_ARGUMENT;
   if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FFPA_ERR_INVALID_ARGUMENT;
   if (batch < 1 || nq < 1 || nkv < 1) return FFPA_ERR_INVALID_ARGUMENT;
   const ffpa_status_t st = check_common(hq, hkv, d, dtype, scale, causal);
@@ -437,6 +438,7 @@ static ffpa_status_t dense_bwd(int stage, const void* q, const void* k, const vo
     if (ms != FFPA_OK) return ms;
     p.dmask = dmask;
   }
+  if (stage == 5 && p.ds == nullptr) return FFPA_ERR_INVALID_ARGUMENT;  // the one-launch products need P and dS
   p.ds_row = (int)round_up8(nq);
   p.ds_head = (long long)nkv * p.ds_row;
   p.ds_batch = (long long)hq * p.ds_head;
@@ -444,6 +446,13 @@ static ffpa_status_t dense_bwd(int stage, const void* q, const void* k, const vo
 }
 
 size_t ffpa_bwd_workspace_bytes(int batch, int hq, int nq, int nkv) { return dense_ds_bytes(batch, hq, nq, nkv); }
+
+int ffpa_bwd_fused_products(int batch, int hq, int hkv, int nq, int nkv, int d) {
+  if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || nq < 1 || nkv < 1 || d < 320 || d > 1024 || d % 32 != 0)
+    return 0;
+  if (dense_ds_bytes(batch, hq, nq, nkv) == 0) return 0;
+  return ffpa::fused_products(dense_params(batch, hq, hkv, nq, nkv, d, 1.0f, 0)) ? 1 : 0;
+}
 
 size_t ffpa_decode_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, int d) {
   return decode_ws_bytes(batch, hq, hkv, nq, nkv, d);
@@ -540,7 +549,7 @@ ffpa_status_t ffpa_bwd_stage(int stage, const void* q, const void* k, const void
                    const float* lse, const float* dlse, float* delta, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int nq,
                    int nkv, int d, ffpa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
                    hipStream_t stream) {
-  if (stage < 0 || stage > 4) return FFPA_ERR_INVALID_ARGUMENT;
+  if (stage < 0 || stage > 5) return FFPA_ERR_INVALID_ARGUMENT;
   return dense_bwd(stage, q, k, v, o, dout, lse, dlse, delta, dq, dk, dv, batch, hq, hkv, nq, nkv, d, dtype, scale,
                    causal, workspace, workspace_bytes, stream);
 }

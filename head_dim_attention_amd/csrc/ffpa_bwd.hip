@@ -113,11 +113,9 @@ struct BwdCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// MASK (dK with the P/dS workspace only): the attn_mask term of each (query, key) pair is added to
-// the scores before P, as in the forward.
-template <class T, int MODE, int NC, int NDB, int NBUF, int NW, bool MASK = false>
+// The O(N)-memory form (no P/dS workspace; the attn_mask backward always uses the workspace).
+template <class T, int MODE, int NC, int NDB, int NBUF, int NW>
 __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p) {
-  static_assert(!MASK || MODE == kDK, "the mask is applied where P and dS are stored");
   constexpr bool OWN_Q = MODE == kDQ;   // stationary rows are queries (dQ) or keys (dK, dV)
   constexpr bool HAS_DP = MODE != kDV;  // dK and dQ need dP = dO V^T
   constexpr int NX = HAS_DP ? 2 : 1;
@@ -148,9 +146,6 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
   const int cg = w % NC;
   const int ow0 = o0 + rg * 32;
   const int off = sv.lk - sv.lq;
-  const bool store_ds = MODE == kDK && p.ds != nullptr;
-  DsView dsv{};
-  if (store_ds) dsv = ds_view(p, s, sv);
 
   // ---- stationary operands: lane (h, n) holds own row n, dims 16 kb + 8 h + 0..7
   const int own_row = OWN_Q ? p.q_row : p.k_row;
@@ -382,28 +377,15 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
     } else {
       need_mask = (row0 + 32 > sv.lq) || (p.causal && ow0 + 31 > row0 + off);
     }
-    // attn_mask term of (query row0 + c_row(r, h), key oi) per register: one element each.
-    float mterm[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mterm[r] = 0.f;
-    if constexpr (MASK) {
-      if (oi < sv.lk) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const long long mr = mask_row(p, s, step_head(st), min(row0 + c_row(r, hh), sv.lq - 1));
-          mterm[r] = mask1<T>(p, mr, oi);
-        }
-      }
-    }
-    uint32_t bop[2][4], ppk[2][4];
+    uint32_t bop[2][4];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      float v2[2], pv2[2] = {0.f, 0.f};
+      float v2[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int rr = r + u;
         const float lse2 = row_val(lse2_lane, rr);
-        float pv = fast_exp2((sacc[rr] + mterm[rr]) * p.scale_log2 - lse2);
+        float pv = fast_exp2(sacc[rr] * p.scale_log2 - lse2);
         if (need_mask) {
           const int si = row0 + c_row(rr, hh);
           const int qi = OWN_Q ? oi : si;
@@ -411,39 +393,11 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
           const bool legal = ki < sv.lk && qi < sv.lq && (!p.causal || ki <= qi + off);
           pv = legal ? pv : 0.f;
         }
-        if constexpr (MODE == kDK) pv2[u] = pv;
         if constexpr (HAS_DP) pv = pv * (dpacc[rr] - row_val(dlt_lane, rr));
         v2[u] = pv;
       }
       bop[r >> 3][(r & 7) >> 1] = Elt<T>::pack2(v2[0], v2[1]);
-      if constexpr (MODE == kDK) ppk[r >> 3][(r & 7) >> 1] = Elt<T>::pack2(pv2[0], pv2[1]);
     }
-    if constexpr (MODE == kDK) {
-      // Optionally store the rounded dS and P (the values the products use), transposed: registers
-      // 8 kb2 .. 8 kb2 + 7 of key oi are queries row0 + 16 kb2 + 8 h + 0..7, one 16-byte piece of
-      // the key's row. Every wave of the row group holds the same values; piece i (dS or P, kb2)
-      // is stored by the wave with cg = i % NC. Keys at or past Lk and pieces starting at or past
-      // the padded row end get an offset past the block, which the buffer range check discards.
-      if (store_ds) {
-        const long long hoff = dsv.base + (long long)step_head(st) * dsv.head;
-        const int nrec = (int)((long long)sv.lk * dsv.row * 2);
-#pragma unroll
-        for (int pi = 0; pi < 4; ++pi) {
-          if (pi % NC != cg) continue;
-          const int kb2 = pi & 1;
-          const bool is_p = pi >= 2;
-          const __amdgpu_buffer_rsrc_t rs =
-              __builtin_amdgcn_make_buffer_rsrc((uint16_t*)(is_p ? p.pst : p.ds) + hoff, 0, nrec, 0x00020000);
-          const int q8 = row0 + 16 * kb2 + 8 * hh;
-          const bool ok = oi < sv.lk && q8 < dsv.row;
-          const uint32_t boff = ok ? (uint32_t)(((long long)oi * dsv.row + q8) * 2) : 0xFFFFFFF0u;
-          const uint32_t(&src)[4] = is_p ? ppk[kb2] : bop[kb2];
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, (u32x4_t){src[0], src[1], src[2], src[3]}),
-                                                 rs, (int)boff, 0, kDsStoreCpol);
-        }
-      }
-    }
-
     // ---- acc^T[d][own] += A[d][streamed] * B[streamed][own], A read transposed from the tile
     const lds_t* tt = MODE == kDV ? t2 : t1;
 #pragma unroll
@@ -1528,21 +1482,18 @@ struct DqCfg {
   static_assert(DWG <= 512 && SCOPY == 1 && SROW == 256 && LDS <= 160 * 1024, "tile budget");
 };
 
+// Work item `item` of the dQ pass: ((sequence, query head), chunk, query tile), `ntiles` query
+// tiles per head; a causal grid takes its heaviest tiles (the last queries) first.
 template <class T, int NDB>
-__global__ void __launch_bounds__(512, 2) ffpa_dq_from_ds_kernel(AttnParams p, int nchunk) {
+__device__ __forceinline__ void dq_from_ds_body(const AttnParams& p, int nchunk, int ntiles, int item, lds_t* smem) {
   using C = DqCfg<NDB>;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
-  lds_t* smem = (lds_t*)smem_raw;
-
-  const int L = blockIdx.x;
-  const int item = xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hq, nchunk * p.ntiles);
-  if (item >= p.total) return;
-  const int qt = item % p.ntiles;
-  const int rest = item / p.ntiles;
+  int qt = item % ntiles;
+  const int rest = item / ntiles;
   const int chunk = rest % nchunk;
   const int hs = rest / nchunk;
   const int h = hs % p.hq;
   const int s = hs / p.hq;
+  if (p.causal) qt = ntiles - 1 - qt;
 
   const SeqView sv = seq_view(p, s);
   const int q0 = qt * C::BQ;
@@ -1726,6 +1677,14 @@ __global__ void __launch_bounds__(512, 2) ffpa_dq_from_ds_kernel(AttnParams p, i
 }
 
 template <class T, int NDB>
+__global__ void __launch_bounds__(512, 2) ffpa_dq_from_ds_kernel(AttnParams p, int nchunk) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[DqCfg<NDB>::LDS];
+  const int item = xcd_item(blockIdx.x, gridDim.x, p.cu_q != nullptr, p.hq, nchunk * p.ntiles);
+  if (item >= p.total) return;
+  dq_from_ds_body<T, NDB>(p, nchunk, p.ntiles, item, (lds_t*)smem_raw);
+}
+
+template <class T, int NDB>
 static hipError_t launch_dq_from_ds(AttnParams p, int nchunk, hipStream_t st) {
   using C = DqCfg<NDB>;
   p.ntiles = (p.nq + C::BQ - 1) / C::BQ;
@@ -1789,20 +1748,16 @@ struct DvCfg {
   static __device__ __forceinline__ int pswz(int r) { return PCH == 4 ? (r >> 2) & 3 : (r >> 1) & 7; }
 };
 
+// Work item `item` of the dV (or dK) pass: ((sequence, KV head), chunk, key tile), `ntiles` key
+// tiles per head (the first keys, the heaviest of a causal grid, first).
 template <class T, int NDB, bool DK>
-__global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, int nchunk) {
+__device__ __forceinline__ void dv_from_p_body(const AttnParams& p, int nchunk, int ntiles, int item, lds_t* smem) {
   using C = DvCfg<NDB>;
   // dV = P^T dO, or (DK) dK = scale dS^T Q: the same product of a stored block and query rows.
   const void* const rows_src = DK ? p.q : p.dout;
   const void* const blk_src = DK ? p.ds : p.pst;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
-  lds_t* smem = (lds_t*)smem_raw;
-
-  const int L = blockIdx.x;
-  const int item = xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hkv, nchunk * p.ntiles);
-  if (item >= p.total) return;
-  const int kt = item % p.ntiles;
-  const int rest = item / p.ntiles;
+  const int kt = item % ntiles;
+  const int rest = item / ntiles;
   const int chunk = rest % nchunk;
   const int hs = rest / nchunk;
   const int kvh = hs % p.hkv;
@@ -2006,6 +1961,14 @@ __global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, in
 }
 
 template <class T, int NDB, bool DK>
+__global__ void __launch_bounds__(512, 2) ffpa_dv_from_p_kernel(AttnParams p, int nchunk) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[DvCfg<NDB>::LDS];
+  const int item = xcd_item(blockIdx.x, gridDim.x, p.cu_q != nullptr, p.hkv, nchunk * p.ntiles);
+  if (item >= p.total) return;
+  dv_from_p_body<T, NDB, DK>(p, nchunk, p.ntiles, item, (lds_t*)smem_raw);
+}
+
+template <class T, int NDB, bool DK>
 static hipError_t launch_dv_from_p(AttnParams p, int nchunk, hipStream_t st) {
   using C = DvCfg<NDB>;
   p.ntiles = (p.nkv + C::BK - 1) / C::BK;
@@ -2154,12 +2117,6 @@ static hipError_t launch_bwd_cfg(AttnParams p, hipStream_t st) {
   p.total = p.batch * (own_q ? p.hq : p.hkv) * p.ntiles;
   if (p.total == 0) return hipSuccess;
   const int grid = (p.total + 7) & ~7;
-  if constexpr (MODE == kDK) {
-    if (p.mask_kind != 0) {
-      hipLaunchKernelGGL((ffpa_bwd_kernel<T, kDK, NC, NDB, NBUF, NW, true>), dim3(grid), dim3(64 * NW), 0, st, p);
-      return hipGetLastError();
-    }
-  }
   hipLaunchKernelGGL((ffpa_bwd_kernel<T, MODE, NC, NDB, NBUF, NW>), dim3(grid), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
@@ -2188,6 +2145,66 @@ static hipError_t launch_bwd_mode(const AttnParams& p, hipStream_t st) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// dK, dV and dQ from the stored blocks in one launch, for dense grids too small to fill the GPU.
+// Each product pass alone runs one workgroup per compute unit or fewer, and a causal grid's
+// heaviest tile (first keys for dK/dV, last queries for dQ) takes about twice the average tile's
+// time; with the three passes' work items in one grid (dK, then dV, then dQ, heaviest tiles of
+// each head first) the compute units that finish light tiles take the next items, so the launch
+// takes about the sum of the average times instead of the sum of the heaviest.
+// ------------------------------------------------------------------------------------------------
+struct ProductsGrid {
+  int nchunk, ktiles, qtiles, nk, nq;  // nk: dK (and dV) items, nq: dQ items
+};
+
+template <int NDB>
+constexpr int products_lds() { return DvCfg<NDB>::LDS > DqCfg<NDB>::LDS ? DvCfg<NDB>::LDS : DqCfg<NDB>::LDS; }
+
+template <class T, int NDB>
+__global__ void __launch_bounds__(512, 2) ffpa_products_kernel(AttnParams p, ProductsGrid g) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[products_lds<NDB>()];
+  lds_t* const smem = (lds_t*)smem_raw;
+  const int item = xcd_item(blockIdx.x, gridDim.x, false, 0, 0);
+  if (item < g.nk)
+    dv_from_p_body<T, NDB, true>(p, g.nchunk, g.ktiles, item, smem);
+  else if (item < 2 * g.nk)
+    dv_from_p_body<T, NDB, false>(p, g.nchunk, g.ktiles, item - g.nk, smem);
+  else if (item < 2 * g.nk + g.nq)
+    dq_from_ds_body<T, NDB>(p, g.nchunk, g.qtiles, item - 2 * g.nk, smem);
+}
+
+static ProductsGrid products_grid(const AttnParams& p) {
+  ProductsGrid g{};
+  g.nchunk = (p.d + 511) / 512;
+  g.ktiles = (p.nkv + DvCfg<4>::BK - 1) / DvCfg<4>::BK;
+  g.qtiles = (p.nq + DqCfg<4>::BQ - 1) / DqCfg<4>::BQ;
+  g.nk = p.batch * p.hkv * g.nchunk * g.ktiles;
+  g.nq = p.batch * p.hq * g.nchunk * g.qtiles;
+  return g;
+}
+
+// Dense grids whose product passes would each give fewer than two workgroups per compute unit (of
+// 256) take the one-launch form.
+bool fused_products(const AttnParams& p) {
+  if (p.cu_q != nullptr) return false;
+  const ProductsGrid g = products_grid(p);
+  return std::max(g.nk, g.nq) < 512;
+}
+
+template <class T>
+static hipError_t launch_products_t(const AttnParams& p, hipStream_t st) {
+  const ProductsGrid g = products_grid(p);
+  const long long total = 2LL * g.nk + g.nq;
+  if (total == 0) return hipSuccess;
+  const int grid = (int)((total + 7) & ~7LL);
+  const int per = (p.d + g.nchunk - 1) / g.nchunk;
+  if (per <= 384)
+    hipLaunchKernelGGL((ffpa_products_kernel<T, 3>), dim3(grid), dim3(512), 0, st, p, g);
+  else
+    hipLaunchKernelGGL((ffpa_products_kernel<T, 4>), dim3(grid), dim3(512), 0, st, p, g);
+  return hipGetLastError();
+}
+
 template <class T>
 static hipError_t launch_stage_t(int stage, const AttnParams& p, int nrows, int varlen_total, hipStream_t st) {
   switch (stage) {
@@ -2207,18 +2224,32 @@ static hipError_t launch_stage_t(int stage, const AttnParams& p, int nrows, int 
       return launch_dbias_t<T>(p, st);
     }
     case 2: return p.pst != nullptr ? launch_dv_p_t<T, false>(p, st) : launch_bwd_mode<T, kDV>(p, st);
+    case 5: {
+      // dK, dV and dQ in one launch (needs the workspace), then the attn_mask gradient.
+      if (p.ds == nullptr) return hipErrorInvalidValue;
+      const hipError_t e = launch_products_t<T>(p, st);
+      if (e != hipSuccess || p.dmask == nullptr) return e;
+      return launch_dbias_t<T>(p, st);
+    }
     default: return p.ds != nullptr ? launch_dq_ds_t<T>(p, st) : launch_bwd_mode<T, kDQ>(p, st);
   }
 }
 
-// Stage 0 = preprocess, 4 = P and dS, 1 = dK, 2 = dV, 3 = dQ; -1 runs all five in that order.
+// Stage 0 = preprocess, 4 = P and dS, 1 = dK, 2 = dV, 3 = dQ, 5 = dK, dV and dQ in one launch
+// (workspace only). -1 runs 0, 4, 1, 2, 3, or 0, 4, 5 when the workspace is there and the dense grid
+// is small (fused_products).
 hipError_t launch_bwd(const AttnParams& p, int fp16, int nrows, int varlen_total, hipStream_t st, int stage) {
+  auto run = [&](int s) {
+    return fp16 ? launch_stage_t<FP16>(s, p, nrows, varlen_total, st) : launch_stage_t<BF16>(s, p, nrows, varlen_total, st);
+  };
+  if (stage >= 0) return run(stage);
   static const int kOrder[5] = {0, 4, 1, 2, 3};
-  for (int i = 0; i < 5; ++i) {
-    const int s = kOrder[i];
-    if (stage >= 0 && s != stage) continue;
-    const hipError_t e = fp16 ? launch_stage_t<FP16>(s, p, nrows, varlen_total, st)
-                              : launch_stage_t<BF16>(s, p, nrows, varlen_total, st);
+  static const int kFused[3] = {0, 4, 5};
+  const bool fused = p.ds != nullptr && fused_products(p);
+  const int* order = fused ? kFused : kOrder;
+  const int n = fused ? 3 : 5;
+  for (int i = 0; i < n; ++i) {
+    const hipError_t e = run(order[i]);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -429,14 +429,6 @@ __device__ __forceinline__ void mask_apply8_block(const AttnParams& p, u32x4_t b
   }
 }
 
-// attn_mask term of one key (< lk) of the mask row at element offset rowoff.
-template <class T>
-__device__ __forceinline__ float mask1(const AttnParams& p, long long rowoff, int key) {
-  const long long o = rowoff + (long long)key * p.m_key;
-  if (p.mask_kind == 1) return Elt<T>::to_f32(((const uint16_t*)p.mask)[o]) * p.inv_scale;
-  return ((const uint8_t*)p.mask)[o] != 0 ? 0.f : -INFINITY;
-}
-
 // Element offset of the attn_mask row of (slice s, query head h, query i).
 __device__ __forceinline__ long long mask_row(const AttnParams& p, int s, int h, int i) {
   return (long long)s * p.m_batch + (long long)h * p.m_head + (long long)i * p.m_row;

@@ -40,8 +40,7 @@
  *     dS = P * (dP - Delta) (dtype, the values the products use) into the workspace, and the dK,
  *     dV and dQ stages are products of them, dk = scale * dS^T q, dv = P^T dout and
  *     dq = scale * dS k, instead of recomputations: 4 D flops per (query, key) pair to form P and
- *     dS, then 2 D per product, instead of 6 D, 4 D and 6 D. (For D > 512 the dK stage forms and
- *     stores P and dS itself, recomputing, and the P/dS stage launches nothing.) It takes
+ *     dS, then 2 D per product, instead of 6 D, 4 D and 6 D. It takes
  *     ffpa_bwd_workspace_bytes() bytes of device memory: 2 * B * Hq * Nkv * round_up(Nq, 8) * 2,
  *     the dS block, then the P block, each stored transposed (one row of round_up(Nq, 8) queries
  *     per key). The workspace is caller-owned device memory; its contents are scratch. A workspace
@@ -274,12 +273,14 @@ ffpa_status_t ffpa_bwd_masked(const void* q, const void* k, const void* v, const
 
 /*
  * One stage of the dense backward, with exactly the arguments of ffpa_bwd plus `stage`:
- *   0 = preprocess (writes delta), 4 = P and dS, 1 = dK, 2 = dV, 3 = dQ.
- * ffpa_bwd is these launches in the order 0, 4, 1, 2, 3. Stages 4 and 1 read the delta written by
+ *   0 = preprocess (writes delta), 4 = P and dS, 1 = dK, 2 = dV, 3 = dQ,
+ *   5 = dK, dV and dQ in one launch (P/dS workspace required, else FFPA_ERR_INVALID_ARGUMENT).
+ * ffpa_bwd is these launches in the order 0, 4, 1, 2, 3, or 0, 4, 5 when ffpa_bwd_fused_products()
+ * is 1 for its sizes and it has a workspace. Stages 4 and 1 read the delta written by
  * stage 0 (and so does stage 3 without a workspace); only stage 0 reads dlse. With a P/dS
- * workspace, stage 4 writes P and dS into it (for D > 512, stage 1 does) and stages 1, 2 and 3
- * read them: pass the same workspace to all of them (a stage that reads a workspace that was not
- * filled gives undefined results). Without a workspace stage 4 launches nothing and stages 1, 2
+ * workspace, stage 4 writes P and dS into it and stages 1, 2 and 3 read them: pass the same
+ * workspace to all of them (a stage that reads a workspace that was not filled gives undefined
+ * results). Without a workspace stage 4 launches nothing and stages 1, 2
  * and 3 are independent. The pages run dV before dK; the order of the products does not matter.
  * Lets a caller time or schedule the launches individually ("CuTe-DSL Backend", "Blackwell
  * status": the backward is separate launches). Returns FFPA_ERR_INVALID_ARGUMENT for another
@@ -289,6 +290,16 @@ ffpa_status_t ffpa_bwd_stage(int stage, const void* q, const void* k, const void
     const void* dout, const float* lse, const float* dlse, float* delta, void* dq, void* dk, void* dv,
     int batch, int hq, int hkv, int nq, int nkv, int d,
     ffpa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * 1 when ffpa_bwd with a P/dS workspace forms dK, dV and dQ in one launch (stage 5) for these dense
+ * sizes, else 0. That is the case when each product pass alone would give fewer than two
+ * workgroups per compute unit: a causal grid's heaviest tiles then set each pass's time, and one
+ * combined grid lets the light tiles of one pass run beside the heavy tiles of another ("CuTe-DSL
+ * Backend", "Blackwell status": the dV, dK and dQ stages are independent once dS is known). The
+ * result is the same as stages 1, 2 and 3 bit for bit. Host function.
+ */
+int ffpa_bwd_fused_products(int batch, int hq, int hkv, int nq, int nkv, int d);
 
 /*
  * Packed (THD) varlen forward ("CuTe-DSL Backend", "Varlen (packed THD) API").

@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "ffpa.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:ffpa_status_t|size_t|const char\*)\s+(ffpa_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:ffpa_status_t|size_t|int|const char\*)\s+(ffpa_\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +32,7 @@ def test_header_declares_expected_entry_points():
               "ffpa_bwd_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes", "ffpa_decode_fwd",
               "ffpa_decode_workspace_bytes", "ffpa_decode_fwd_strided", "ffpa_fwd_strided", "ffpa_fwd_masked",
               "ffpa_bwd_masked", "ffpa_fwd_fp8", "ffpa_fwd_fp8_workspace_bytes", "ffpa_fwd_split",
-              "ffpa_fwd_split_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes_exact"):
+              "ffpa_fwd_split_workspace_bytes", "ffpa_varlen_bwd_workspace_bytes_exact", "ffpa_bwd_fused_products"):
         assert n in names
 
 
@@ -408,3 +408,16 @@ def test_decode_noalloc_validation(lib):
     assert B.ffpa_decode_workspace_bytes(64, 32, 8, 7, 4096, 1024) > B.NOALLOC_SCRATCH_BYTES
     assert lib.ffpa_decode_fwd_noalloc(*args(64, 32, 8, 7, 4096, 1024)) == B.FFPA_ERR_TOO_LARGE
     assert "TOO_LARGE" in B.ffpa_status_string(B.FFPA_ERR_TOO_LARGE)
+
+
+def test_fused_products_decision(lib):
+    """One-launch dK/dV/dQ for dense grids below two workgroups per CU per pass, with a workspace."""
+    from head_dim_attention_amd import _binding as B
+    assert B.ffpa_bwd_fused_products(1, 8, 8, 4096, 4096, 512)          # 256 items per pass
+    assert not B.ffpa_bwd_fused_products(1, 32, 32, 8192, 8192, 512)    # 2048 items per pass
+    assert not B.ffpa_bwd_fused_products(1, 32, 8, 8192, 8192, 1024)
+    assert not B.ffpa_bwd_fused_products(1, 1, 1, 40000, 40000, 512)    # no workspace for these sizes
+    assert not B.ffpa_bwd_fused_products(1, 8, 8, 4096, 4096, 300)      # unsupported head dim
+    # stage 5 without a workspace is an invalid argument (nothing launched)
+    args = [P] * 11 + [1, 2, 2, 64, 64, 512, 0, 0.04, 1, N, 0, S]
+    assert lib.ffpa_bwd_stage(5, *args) == 1

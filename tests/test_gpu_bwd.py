@@ -296,3 +296,27 @@ def test_varlen_exact_workspace_equals_bound(lib):
         B.ffpa_varlen_bwd_workspace_bytes(8, sum(lq), sum(lk), mq, mk)
     for x, y in zip(exact, bound):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("d,causal", [(512, True), (768, False), (384, True)])
+def test_bwd_fused_products_equal_stages(lib, d, causal):
+    """Stage 5 (dK, dV and dQ in one launch, which ffpa_bwd uses for small dense grids) equals
+    stages 1, 2 and 3 bit for bit."""
+    q, k, v, do = W.dense_inputs(1, 4, 2, 300, 260, d, BF, seed=29 + d)
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    assert lib.ffpa_bwd_fused_products(1, 4, 2, 300, 260, d)
+    o, lse = lib.ffpa_fwd(qc, kc, vc, causal=causal)
+    ws = torch.empty(lib.ffpa_bwd_workspace_bytes(1, 4, 300, 260), dtype=torch.uint8, device="cuda")
+    delta = torch.empty_like(lse)
+    outs = []
+    for stages in ((0, 4, 1, 2, 3), (0, 4, 5)):
+        dq, dk, dv = torch.empty_like(qc), torch.empty_like(kc), torch.empty_like(vc)
+        for stage in stages:
+            lib.ffpa_bwd_stage(stage, qc, kc, vc, o, doc, lse, delta, dq, dk, dv, causal=causal, workspace=ws)
+        outs.append((dq, dk, dv))
+    torch.cuda.synchronize()
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+    g = lib.ffpa_bwd(qc, kc, vc, o, doc, lse, causal=causal, store_ds=True)
+    for x, y in zip(outs[1], g):
+        assert torch.equal(x, y)
