@@ -273,6 +273,12 @@ def dense_config_leg(F, W, w, seed: int, steps: int, warmup: int, store_ds: bool
                 "workspace_gib": round(step.ws_bytes / 2**30, 3),
                 "forward_kernel": "key-range split + merge" if step.fws is not None else "one launch",
                 "kernels": step.kernel_table(stage_ms)})
+    if d > 512:
+        # the FP8 forward above D = 512 (at D <= 512 the main step times it)
+        f8 = fp8_leg(F, q, k, v, w.causal, step.pairs, max(steps, 10), warmup)
+        if "ms" in f8:
+            f8["vs_bf16_fwd"] = round(ms_fwd / f8["ms"], 3)
+        out["fp8_fwd"] = f8
     del step
     torch.cuda.empty_cache()
     return out

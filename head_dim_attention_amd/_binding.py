@@ -334,7 +334,7 @@ def ffpa_fwd_fp8_workspace_bytes(batch: int, hq: int, hkv: int, nq: int, nkv: in
 
 def ffpa_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
                  scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
-    """FP8 forward (D <= 512): fp16/bf16 q [B,Hq,Nq,D], k/v [B,Hkv,Nkv,D] quantized to e4m3 inside
+    """FP8 forward (D 320..1024): fp16/bf16 q [B,Hq,Nq,D], k/v [B,Hkv,Nkv,D] quantized to e4m3 inside
     the library with one scale per head and tensor -> (o, lse) as ffpa_fwd. ``workspace`` (a byte
     tensor of at least ffpa_fwd_fp8_workspace_bytes()) keeps the quantized K8, V8^T and amax
     values for inspection; by default a temporary one is allocated."""

@@ -348,7 +348,7 @@ ffpa_status_t ffpa_fwd_masked(const void* q, const void* k, const void* v, void*
 }
 
 size_t ffpa_fwd_fp8_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, int d) {
-  if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || nq < 1 || nkv < 1 || d < 320 || d > 512 || d % 32 != 0)
+  if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || nq < 1 || nkv < 1 || d < 320 || d > 1024 || d % 32 != 0)
     return 0;
   return ffpa::fp8_workspace_bytes(batch, hq, hkv, nkv, d);
 }
@@ -361,7 +361,7 @@ ffpa_status_t ffpa_fwd_fp8(const void* q, const void* k, const void* v, void* o,
   const ffpa_status_t st = check_common(hq, hkv, d, dtype, scale, causal);
   if (st != FFPA_OK) return st;
   // (the quantizing passes put batch x heads in one grid dimension)
-  if (d > 512 || (long long)batch * hq > 65535) return FFPA_ERR_NOT_SUPPORTED;
+  if ((long long)batch * hq > 65535) return FFPA_ERR_NOT_SUPPORTED;
   if (too_big_dense(batch, hq, nq, d) || too_big_dense(batch, hkv, nkv, d)) return FFPA_ERR_INVALID_ARGUMENT;
   // The fp8 copies of one head (K8 rows, V8^T rows of nkv rounded up to 64) use 32-bit offsets.
   if ((long long)(nkv + 63) / 64 * 64 * d > (1LL << 31) - 1) return FFPA_ERR_INVALID_ARGUMENT;

@@ -22,7 +22,8 @@
 // 32-key half of the tile with no partial-sum exchange; the pair shares the tile max (one float
 // per query through LDS) and its P8 halves (1 KB per wave), and each wave then multiplies P V for
 // its half of the head dim. Waves 0-3 and 4-7 run one slot apart (one multiplies while the other
-// does the softmax), as in the bf16/fp16 forward.
+// does the softmax), as in the bf16/fp16 forward. Above D = 512 Q8 of the whole head dim no longer
+// fits beside a wave's share of O, and a second kernel (below) splits S over head-dim halves.
 #include "ffpa_device.h"
 #include "ffpa_params.h"
 
@@ -498,6 +499,279 @@ __global__ void __launch_bounds__(512, 2) ffpa_fwd_fp8_kernel(AttnParams p, cons
   }
 }
 
+// ---- forward kernel for D > 512 --------------------------------------------------------------
+// The same FP8 algorithm at head dims 544..1024, where a wave can no longer hold Q8 for the whole
+// head dim beside half of O. Eight waves (two per SIMD) own 64 queries as 2 row groups x 4; within
+// a row group, wave (kb, dh) forms the partial S^T of key block kb (32 of the tile's 64 keys) over
+// head-dim half dh (Q8 of that half in registers: 64 registers at D = 1024) and owns a quarter of
+// O^T (128 registers). The two halves of a key block are combined by a reduce-scatter (the A rows
+// of half dh are rotated by 16 dh, so registers 0..7 hold the 16 keys the wave finishes), the four
+// waves share their 16-key maxima for the exact running max, and each writes the e4m3 P of its keys
+// into the row group's P8 block, from which every wave multiplies its quarter: O^T += V8^T P8^T
+// over all 64 keys. K8 (64 keys x 1 KB rows, the two head-dim halves at 0 and 512 bytes) and V8^T
+// (D rows x 64 keys) tiles are 64 KB each and single-buffered; every step runs, all waves in step:
+//   S partials (V_j copies spread over them) | partner's keys out | barrier | own keys in, maxima
+//   out | barrier | running max, P8 out | wait V_j, barrier | O^T += V8^T P8^T (K_{j+1} copies)
+template <int NQ>
+struct Fp8WideCfg {
+  static constexpr int NW = 8;
+  static constexpr int DQW = NQ * 32;          // head-dim columns of O per wave (a quarter)
+  static constexpr int DPAD = 4 * DQW;         // padded head dim (multiple of 128)
+  static constexpr int DH = DPAD / 2;          // head-dim half of the S partials
+  static constexpr int KSH = DH / 64;          // 64-wide k-steps over a half (= NQ)
+  static constexpr int KT = 64;                // keys per tile
+  static constexpr int KROW = 1024;            // K8 row in LDS: half 0 at byte 0, half 1 at 512
+  static constexpr int KTILE = KT * KROW;      // 64 KB
+  static constexpr int VTILE = DPAD * KT;      // V8^T tile: DPAD rows x 64 keys
+  static constexpr int XS_OFF = KTILE + VTILE;       // S partials: per wave 2 KB (the partner's keys)
+  static constexpr int P8_OFF = XS_OFF + NW * 2048;  // per row group: 32 queries x 64 keys of P8
+  static constexpr int XM_OFF = P8_OFF + 2 * 2048;   // per wave: 16-key maximum, then l, per query
+  static constexpr int LDS = XM_OFF + NW * 32 * 4;
+  static constexpr int KCOPY = KTILE / 1024 / NW;    // 1 KB copies per wave of a K8 tile (one row each)
+  static constexpr int VCOPY = VTILE / 1024 / NW;    // of a V8^T tile (16 rows each)
+  static_assert(DPAD > 512 && DPAD <= 1024 && DH <= 512 && LDS <= 160 * 1024 && KSH == NQ, "LDS budget");
+};
+
+template <class T, int NQ>
+__global__ void __launch_bounds__(512, 2) ffpa_fwd_fp8_wide_kernel(AttnParams p, const float* amax_q,
+                                                                   const float* amax_k, const float* amax_v,
+                                                                   const uint8_t* k8, const uint8_t* v8t, int np) {
+  using C = Fp8WideCfg<NQ>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
+  lds_t* smem = (lds_t*)smem_raw;
+  lds_t* const kbuf = smem;
+  lds_t* const vbuf = smem + C::KTILE;
+  lds_t* const xsbuf = smem + C::XS_OFF;
+  lds_t* const p8buf = smem + C::P8_OFF;
+  lds_t* const xmbuf = smem + C::XM_OFF;
+
+  const int L = blockIdx.x;
+  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  if (item >= p.total) return;
+  int t = item % p.ntiles;
+  const int hs = item / p.ntiles;
+  const int h = hs % p.hq;
+  const int s = hs / p.hq;
+  if (p.causal) t = p.ntiles - 1 - t;
+  const int qt0 = t * 64;
+  if (qt0 >= p.nq) return;
+  const int kvh = h / p.group;
+  const int hq_flat = s * p.hq + h, hk_flat = s * p.hkv + kvh;
+
+  const int w = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int rg = w >> 2;
+  const int kb = (w >> 1) & 1;  // key block of the tile
+  const int dh = w & 1;         // head-dim half of the S partials
+  const int oq = w & 3;         // O quarter
+  const int qw0 = qt0 + rg * 32;
+  const int off = p.nkv - p.nq;
+  int kend = p.nkv;
+  if (p.causal) kend = min(kend, qt0 + 64 + off);
+  const int ntk = kend > 0 ? (kend + C::KT - 1) / C::KT : 0;
+
+  const float fq = quant_factor(amax_q[hq_flat]);
+  const float av = amax_v[hk_flat];
+  const float sdq = p.scale_log2 * (amax_q[hq_flat] / 448.0f) * (amax_k[hk_flat] / 448.0f);
+
+  // Q8 of this lane's query over head-dim half dh: k-step kk, lane half h holds dims
+  // dh DH + 64 kk + 32 h .. + 31.
+  i32x8_t q8[C::KSH];
+  {
+    const int qi = min(qw0 + l32, p.nq - 1);
+    const uint16_t* qrow = (const uint16_t*)p.q + ((long long)s * p.hq + h) * p.q_head + (long long)qi * p.q_row;
+#pragma unroll
+    for (int kk = 0; kk < C::KSH; ++kk) {
+      uint32_t wv[8];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = dh * C::DH + 64 * kk + 32 * hh + 8 * g;
+        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (dim < p.d) {
+          const u32x4_t x = *(const u32x4_t*)(qrow + dim);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Elt<T>::unpack2(x[e], a[2 * e], a[2 * e + 1]);
+        }
+        wv[2 * g] = e4m3x4(a[0] * fq, a[1] * fq, a[2] * fq, a[3] * fq);
+        wv[2 * g + 1] = e4m3x4(a[4] * fq, a[5] * fq, a[6] * fq, a[7] * fq);
+      }
+      q8[kk] = (i32x8_t){(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3], (int)wv[4], (int)wv[5], (int)wv[6], (int)wv[7]};
+    }
+  }
+
+  // ---- copies. K8 row r: 64 physical 16-byte chunks; physical chunk pc holds logical chunk
+  // u = pc ^ (r & 15), i.e. chunk u % 32 of head-dim half u / 32 (padding and chunks past the head
+  // dim hold clamped duplicates); copy c of wave w is row w + 8 c. V8^T rows r0 .. r0 + 15
+  // (r0 = 16 (w + 8 c)), chunk c of row r at c ^ ((r >> 2) & 3), rows past the head dim clamped.
+  const int dch = p.d >> 4;
+  const long long k8_head = (long long)hk_flat * p.nkv * p.d;
+  const long long v8_head = (long long)hk_flat * p.d * np;
+  const i32x4_t krs = make_rsrc(k8 + k8_head, (uint32_t)min((long long)p.nkv * p.d, (long long)0xFFFFFFF0));
+  const i32x4_t vrs = make_rsrc(v8t + v8_head, (uint32_t)min((long long)p.d * np, (long long)0xFFFFFFF0));
+  auto copy_k = [&](int j, int c) {
+    const int r = w + C::NW * c;
+    const int key = min(j * C::KT + r, p.nkv - 1);
+    const int u = fresh_lane_id() ^ (r & 15);
+    const int ch = min((u >> 5) * (C::DH / 16) + min(u & 31, C::DH / 16 - 1), dch - 1) << 4;
+    lds_t* d = (lds_t*)(uintptr_t)opaque_s((uint32_t)(uintptr_t)(kbuf + r * C::KROW));
+    dma16_buf(krs, key * p.d + ch, 0, d);
+  };
+  auto copy_v = [&](int j, int c) {
+    const int r0 = 16 * (w + C::NW * c);
+    const int ln = fresh_lane_id();
+    const int row = min(r0 + (ln >> 2), p.d - 1);
+    const int vc = ((ln & 3) ^ ((ln >> 4) & 3)) << 4;
+    lds_t* d = (lds_t*)(uintptr_t)opaque_s((uint32_t)(uintptr_t)(vbuf + r0 * C::KT));
+    dma16_buf(vrs, row * np + vc + j * C::KT, 0, d);
+  };
+  auto spread_k = [](int n, int c) { return (c * n) / C::KCOPY; };
+  auto spread_v = [](int n, int c) { return (c * n) / C::VCOPY; };
+
+  // ---- operand addresses. S^T A rows: tile row 32 kb + (row_perm(n) ^ 16 dh); lane reads 32
+  // bytes of its half's chunks 32 dh + 4 kk + 2 h, + 1 (the half's base is 16-chunk aligned, so
+  // the swizzle is one per-lane base XOR a constant).
+  const int krow = 32 * kb + (row_perm(l32) ^ (16 * dh));
+  const uint32_t klane = krow * C::KROW + ((32 * dh) << 4) + (((krow & 15) ^ (2 * hh)) << 4);
+  auto k_addr = [&](uint32_t tile_lane, int kk, int part) -> uint32_t { return tile_lane ^ ((4 * kk + part) << 4); };
+  // V8^T (A of O^T += V8^T P8^T): row d = oq DQW + 32 i + n, keys 32 h .. + 31 = chunks 2 h, + 1.
+  const int vsw = (l32 >> 2) & 3;
+  const int vlane0 = (oq * C::DQW + l32) * C::KT + (((2 * hh) ^ vsw) << 4);
+  const int vlane1 = (oq * C::DQW + l32) * C::KT + (((2 * hh + 1) ^ vsw) << 4);
+  // P8 block of the row group: [query n][64 keys], the 16-byte chunk index XOR-ed with (n >> 1) & 3.
+  auto p8_off = [&](int n, int key) -> int { return rg * 2048 + n * 64 + ((((key >> 4) ^ (n >> 1)) & 3) << 4) + (key & 15); };
+  auto rd8 = [&](uint32_t a0, uint32_t a1) -> i32x8_t {
+    const u32x4_t x = lds_read_b128_at(a0), y = lds_read_b128_at(a1);
+    return (i32x8_t){(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+  };
+
+  f32x16_t oacc[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) oacc[i] = (f32x16_t){};
+  float mref = -INFINITY, lsum = 0.f;
+  const int qi = qw0 + l32;
+  const int lim_row = p.causal ? min(qi + off, p.nkv - 1) : p.nkv - 1;
+  // This lane's 8 keys of the tile: 32 kb + 16 dh + 8 h + 0..7.
+  const int kown = 32 * kb + 16 * dh + 8 * hh;
+
+  if (ntk > 0) {
+#pragma unroll
+    for (int c = 0; c < C::KCOPY; ++c) copy_k(0, c);
+  }
+  wait_all();  // Q8's loads and K_0
+  lds_barrier();
+
+  for (int j = 0; j < ntk; ++j) {
+    if (j > 0) {
+      wait_vmcnt<0>();  // K_j (copied during the products of step j - 1)
+      lds_barrier();    // every wave has finished step j - 1 (V_{j-1}, the P8 and exchange slots are free)
+    }
+    const uint32_t kt = (uint32_t)opaque_v((int)(lds_addr(kbuf) + klane));
+    f32x16_t sacc = (f32x16_t){};
+#pragma unroll
+    for (int kk = 0; kk < C::KSH; ++kk) {
+      sacc = mma_fp8(rd8(k_addr(kt, kk, 0), k_addr(kt, kk, 1)), q8[kk], sacc);
+#pragma unroll
+      for (int c = 0; c < C::VCOPY; ++c)
+        if (kk == spread_v(C::KSH, c)) copy_v(j, c);
+    }
+    pin_fp8_pipeline<C::KSH, FP8_AHEAD, 2, 0>();
+    // The partner's keys (registers 8..15) to its slot.
+    lds_t* const xs_partner = xsbuf + (w ^ 1) * 2048;
+    lds_write_f4(xs_partner, lane * 16, (f32x4_t){sacc[8], sacc[9], sacc[10], sacc[11]});
+    lds_write_f4(xs_partner, 1024 + lane * 16, (f32x4_t){sacc[12], sacc[13], sacc[14], sacc[15]});
+    lds_barrier();  // partial sums visible; K_j released
+    const lds_t* const xs_mine = xsbuf + w * 2048;
+    const f32x4_t pa = lds_read_f4(xs_mine, lane * 16), pb4 = lds_read_f4(xs_mine, 1024 + lane * 16);
+    float sv[8];
+    const int klim = lim_row - (j * C::KT + kown);
+    float mw = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = (sacc[e] + (e < 4 ? pa[e] : pb4[e - 4])) * sdq;
+      if (e > klim) v = -INFINITY;
+      sv[e] = v;
+      mw = fmaxf(mw, v);
+    }
+    mw = half_max(mw);
+    if (hh == 0) *(__attribute__((address_space(3))) float*)(xmbuf + (w * 32 + l32) * 4) = mw;
+    lds_barrier();  // the row group's 16-key maxima visible
+    // Tile max over the four waves of the row group, in wave order (bit-identical in all four), the
+    // exact running max (rescaling O and l when it grows), P = exp2(S - max) and P8 = e4m3(448 P).
+    float mt = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mt = fmaxf(mt, *(const __attribute__((address_space(3))) float*)(xmbuf + ((4 * rg + c) * 32 + l32) * 4));
+    const float mnew = fmaxf(mref, mt);
+    if (__any(mnew > mref)) {
+      const float alpha = mnew > mref ? (mref == -INFINITY ? 0.f : fast_exp2(mref - mnew)) : 1.0f;
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) oacc[i] *= alpha;
+      mref = mnew;
+    }
+    const float mu = mref == -INFINITY ? 0.f : mref;
+    uint32_t wd[2];
+#pragma unroll
+    for (int q4 = 0; q4 < 2; ++q4) {
+      float e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        e[u] = fast_exp2(sv[4 * q4 + u] - mu);
+        lsum += e[u];
+      }
+      wd[q4] = e4m3x4(e[0] * 448.f, e[1] * 448.f, e[2] * 448.f, e[3] * 448.f);
+    }
+    *(__attribute__((address_space(3))) u32x2_t*)(p8buf + p8_off(l32, kown)) = (u32x2_t){wd[0], wd[1]};
+    wait_vmcnt<0>();  // V_j
+    lds_barrier();    // the row group's P8 visible
+    // O^T += V8^T P8^T over the tile's 64 keys (lane half h: keys 32 h .. + 31), K_{j+1} copies
+    // spread over the products (past the last tile: clamped, into a buffer no longer read).
+    const uint32_t pbase = lds_addr(p8buf);
+    const i32x8_t bop = rd8(pbase + p8_off(l32, 32 * hh), pbase + p8_off(l32, 32 * hh + 16));
+    const lds_t* const vt0 = vbuf + opaque_v(vlane0);
+    const lds_t* const vt1 = vbuf + opaque_v(vlane1);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const u32x4_t x = lds_read_b128(vt0, 32 * i * C::KT), y = lds_read_b128(vt1, 32 * i * C::KT);
+      const i32x8_t a = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      oacc[i] = mma_fp8(a, bop, oacc[i]);
+#pragma unroll
+      for (int c = 0; c < C::KCOPY; ++c)
+        if (i == spread_k(NQ, c)) copy_k(j + 1, c);
+    }
+    pin_fp8_pipeline<NQ, FP8_AHEAD, 2, 2>();
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue: l = the row group's four per-wave sums (wave order), O = O^T * amax_v / 448^2 / l.
+  lds_barrier();  // every wave has read the row group's last maxima
+  const float lw = half_sum(lsum);
+  if (hh == 0) *(__attribute__((address_space(3))) float*)(xmbuf + (w * 32 + l32) * 4) = lw;
+  lds_barrier();
+  float lt = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) lt += *(const __attribute__((address_space(3))) float*)(xmbuf + ((4 * rg + c) * 32 + l32) * 4);
+  const float inv = lt > 0.f ? (av / (448.0f * 448.0f)) / lt : 0.f;
+  if (qi < p.nq) {
+    uint16_t* orow = (uint16_t*)p.o + ((long long)s * p.hq + h) * p.o_head + (long long)qi * p.o_row;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = oq * C::DQW + 32 * i + 8 * i4 + 4 * hh;
+        if (d < p.d) {
+          const f32x16_t& o = oacc[i];
+          *(u32x2_t*)(orow + d) = (u32x2_t){Elt<T>::pack2(o[4 * i4] * inv, o[4 * i4 + 1] * inv),
+                                            Elt<T>::pack2(o[4 * i4 + 2] * inv, o[4 * i4 + 3] * inv)};
+        }
+      }
+    if (oq == 0 && hh == 0)
+      p.lse[(long long)s * p.lse_batch + (long long)h * p.lse_head + qi] =
+          lt > 0.f ? (mref + fast_log2(lt)) * kLn2 : -INFINITY;
+  }
+}
+
 // Workspace: amax of Q (B Hq floats), K and V (B Hkv each), then K8 (B Hkv Nkv D bytes), then V8^T
 // (B Hkv D np bytes, np = Nkv rounded up to 64); each part 256-byte aligned.
 struct Fp8Layout {
@@ -519,7 +793,6 @@ Fp8Layout fp8_layout(int batch, int hq, int hkv, int nkv, int d) {
 
 template <class T, int NDB>
 static hipError_t launch_fp8_cfg(AttnParams p, char* ws, hipStream_t st) {
-  using C = Fp8Cfg<NDB>;
   const Fp8Layout lay = fp8_layout(p.batch, p.hq, p.hkv, p.nkv, p.d);
   float* amax_q = (float*)(ws + lay.amax);
   float* amax_k = amax_q + p.batch * p.hq;
@@ -539,11 +812,23 @@ static hipError_t launch_fp8_cfg(AttnParams p, char* ws, hipStream_t st) {
                      dim3(256), 0, st, (const uint16_t*)p.k, k8, amax_k, kvelems, p.d);
   hipLaunchKernelGGL(ffpa_fp8_quant_vt_kernel<T>, dim3(lay.np / 64, (p.d + 63) / 64, p.batch * p.hkv), dim3(256), 0,
                      st, (const uint16_t*)p.v, v8t, amax_v, p.nkv, p.d, lay.np);
-  p.ntiles = (p.nq + 127) / 128;
-  p.total = p.batch * p.hq * p.ntiles;
-  const int grid = (p.total + 7) & ~7;
-  hipLaunchKernelGGL((ffpa_fwd_fp8_kernel<T, NDB>), dim3(grid), dim3(64 * C::NW), 0, st, p, amax_q, amax_k, amax_v,
-                     k8, v8t, lay.np);
+  if constexpr (NDB <= 8) {
+    p.ntiles = (p.nq + 127) / 128;
+    p.total = p.batch * p.hq * p.ntiles;
+    const int grid = (p.total + 7) & ~7;
+    hipLaunchKernelGGL((ffpa_fwd_fp8_kernel<T, NDB>), dim3(grid), dim3(64 * Fp8Cfg<NDB>::NW), 0, st, p, amax_q, amax_k,
+                       amax_v, k8, v8t, lay.np);
+  } else {
+    // D in 544..1024 (NDB = ceil(D / 64) rounded up to even): each wave owns a quarter of the
+    // padded head dim, NQ = NDB / 2 blocks of 32 columns
+    static_assert(NDB % 2 == 0, "D > 512 takes even block counts");
+    constexpr int NQ = NDB / 2;
+    p.ntiles = (p.nq + 63) / 64;
+    p.total = p.batch * p.hq * p.ntiles;
+    const int grid = (p.total + 7) & ~7;
+    hipLaunchKernelGGL((ffpa_fwd_fp8_wide_kernel<T, NQ>), dim3(grid), dim3(64 * Fp8WideCfg<NQ>::NW), 0, st, p, amax_q,
+                       amax_k, amax_v, k8, v8t, lay.np);
+  }
   return hipGetLastError();
 }
 
@@ -553,7 +838,14 @@ static hipError_t launch_fp8_t(const AttnParams& p, char* ws, hipStream_t st) {
     case 5: return launch_fp8_cfg<T, 5>(p, ws, st);
     case 6: return launch_fp8_cfg<T, 6>(p, ws, st);
     case 7: return launch_fp8_cfg<T, 7>(p, ws, st);
-    default: return launch_fp8_cfg<T, 8>(p, ws, st);
+    case 8: return launch_fp8_cfg<T, 8>(p, ws, st);
+    case 9:
+    case 10: return launch_fp8_cfg<T, 10>(p, ws, st);
+    case 11:
+    case 12: return launch_fp8_cfg<T, 12>(p, ws, st);
+    case 13:
+    case 14: return launch_fp8_cfg<T, 14>(p, ws, st);
+    default: return launch_fp8_cfg<T, 16>(p, ws, st);
   }
 }
 

@@ -138,8 +138,9 @@ ffpa_status_t ffpa_fwd_masked(const void* q, const void* k, const void* v, void*
 /*
  * FP8 dense forward ("Backends Overview", backend table and notes: FP8 attention takes fp16/bf16
  * activations and quantizes Q, K and V inside the kernel; forward only). Arguments as ffpa_fwd
- * plus a caller-owned device workspace of at least ffpa_fwd_fp8_workspace_bytes() bytes. D <= 512
- * and batch * hq <= 65535 (else FFPA_ERR_NOT_SUPPORTED); a workspace that is NULL or too small is
+ * plus a caller-owned device workspace of at least ffpa_fwd_fp8_workspace_bytes() bytes. Head dims
+ * as ffpa_fwd (320..1024, multiples of 32) and batch * hq <= 65535 (else FFPA_ERR_NOT_SUPPORTED);
+ * a workspace that is NULL or too small is
  * FFPA_ERR_INVALID_ARGUMENT. The guide's FP8 page is not available; the semantics implemented:
  *   - OCP e4m3 (max 448) for Q, K, V and P, rounded to nearest even from fp32;
  *   - one scale per (batch, head) and tensor: x8 = e4m3(x * (448 / amax)), amax = max |x| over the
@@ -156,7 +157,7 @@ ffpa_status_t ffpa_fwd_fp8(const void* q, const void* k, const void* v, void* o,
     ffpa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
     hipStream_t stream);
 
-/* Bytes of the ffpa_fwd_fp8 workspace; 0 for invalid sizes or d outside 320..512. Host function. */
+/* Bytes of the ffpa_fwd_fp8 workspace; 0 for invalid sizes or d outside 320..1024. Host function. */
 size_t ffpa_fwd_fp8_workspace_bytes(int batch, int hq, int hkv, int nq, int nkv, int d);
 
 /*

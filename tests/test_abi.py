@@ -352,10 +352,11 @@ def test_fp8_workspace_sizes(lib):
     the key count padded to 64, each part 256-byte aligned; 0 outside the supported sizes."""
     lib.ffpa_fwd_fp8_workspace_bytes.restype = ctypes.c_size_t
     al = lambda x: (x + 255) // 256 * 256
-    for b, hq, hkv, nkv, d in ((1, 32, 32, 8192, 512), (2, 4, 2, 150, 320), (1, 4, 1, 333, 448), (3, 6, 3, 1, 384)):
+    for b, hq, hkv, nkv, d in ((1, 32, 32, 8192, 512), (2, 4, 2, 150, 320), (1, 4, 1, 333, 448), (3, 6, 3, 1, 384),
+                               (1, 32, 8, 8192, 1024), (2, 4, 2, 150, 544)):
         want = al(4 * (b * hq + 2 * b * hkv)) + al(b * hkv * nkv * d) + al(b * hkv * d * ((nkv + 63) // 64 * 64))
         assert lib.ffpa_fwd_fp8_workspace_bytes(b, hq, hkv, 7, nkv, d) == want
-    for bad in ((1, 2, 2, 8, 8, 640), (1, 2, 2, 8, 8, 300), (1, 3, 2, 8, 8, 512), (0, 2, 2, 8, 8, 512),
+    for bad in ((1, 2, 2, 8, 8, 1056), (1, 2, 2, 8, 8, 300), (1, 3, 2, 8, 8, 512), (0, 2, 2, 8, 8, 512),
                 (1, 2, 2, 0, 8, 512), (1, 2, 2, 8, 0, 512)):
         assert lib.ffpa_fwd_fp8_workspace_bytes(*bad) == 0
 
@@ -367,7 +368,8 @@ def test_fp8_validation(lib):
         return lib.ffpa_fwd_fp8(*ptrs, b, hq, hkv, nq, nkv, d, dtype, ctypes.c_float(scale), causal, ws, nws, S)
     assert call(ws=N) == 1                                   # no workspace
     assert call(nws=1024) == 1                               # workspace too small
-    assert call(d=640) == 2 and call(d=300) == 2             # head dims the FP8 path does not cover
+    assert call(d=1056) == 2 and call(d=300) == 2            # head dims the FP8 path does not cover
+    assert call(d=1024, nkv=8192, nws=1 << 20) == 1          # workspace too small at D = 1024
     assert call(b=2048, hq=64, hkv=64, nq=1, nkv=1) == 2     # batch x heads beyond one grid dimension
     assert call(hq=3, hkv=2) == 1 and call(dtype=7) == 1 and call(scale=-1.0) == 1 and call(causal=2) == 1
     assert call(nq=0) == 1 and call(nkv=0) == 1
@@ -379,7 +381,7 @@ def test_fp8_validation(lib):
 
 def test_fwd_split_workspace_and_validation(lib):
     """ffpa_fwd_split_workspace_bytes: B Hq Nq nsplit (D + 1) fp32 values when the grid has fewer
-    than two workgroups per compute unit (128 queries per workgroup for D <= 512, 32 above), else 0;
+    than two workgroups per compute unit (128 queries per workgroup for D <= 512, 64 above), else 0;
     ffpa_fwd_split then needs a workspace of that size, and is ffpa_fwd when it is 0."""
     lib.ffpa_fwd_split_workspace_bytes.restype = ctypes.c_size_t
     f = lib.ffpa_fwd_split_workspace_bytes
@@ -387,7 +389,7 @@ def test_fwd_split_workspace_and_validation(lib):
     assert f(1, 2, 2, 128, 128, 512) == 0                          # 4 key tiles: too short to split
     # 8 heads x 32 tiles = 256 workgroups -> 2 ranges
     assert f(1, 8, 8, 4096, 4096, 512) == 1 * 8 * 4096 * 2 * 513 * 4
-    assert f(1, 2, 2, 300, 4096, 768) == 2 * 300 * 8 * 769 * 4    # 20 workgroups -> 8 ranges
+    assert f(1, 2, 2, 300, 4096, 768) == 2 * 300 * 8 * 769 * 4    # 10 workgroups -> 8 ranges
     assert f(1, 2, 2, 300, 4096, 300) == 0 and f(1, 3, 2, 300, 4096, 512) == 0
     def call(b=1, hq=8, hkv=8, nq=4096, nkv=4096, d=512, ws=P, nws=1 << 30):
         return lib.ffpa_fwd_split(P, P, P, P, P, b, hq, hkv, nq, nkv, d, 0, ctypes.c_float(0.04), 1, ws, nws, S)

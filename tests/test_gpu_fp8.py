@@ -40,6 +40,14 @@ CASES = [
     (1, 2, 1, 64, 40, 512, BF, False),     # one key tile
     (1, 2, 2, 100, 30, 448, FP, True),     # causal Nq > Nkv: rows without a legal key
     (1, 4, 2, 300, 1000, 512, BF, True),   # many tiles, ragged tails
+    # D > 512: S over two head-dim halves, O in quarters
+    (1, 2, 2, 128, 128, 768, BF, False),
+    (1, 4, 2, 100, 150, 1024, FP, True),
+    (1, 2, 1, 70, 333, 544, BF, False),    # head dim padded to 640
+    (1, 2, 2, 1, 200, 768, FP, True),
+    (1, 3, 3, 65, 64, 896, BF, True),      # one key tile, one query past a 64-query tile
+    (1, 2, 2, 100, 30, 640, FP, True),     # causal Nq > Nkv: rows without a legal key
+    (1, 4, 2, 300, 700, 1024, BF, True),   # many tiles, ragged tails
 ]
 
 
@@ -126,3 +134,32 @@ def test_fp8_full_size_sampled_head(lib):
     err_l = float(np.max(np.abs(lse[:, h:h + 1].double().cpu().numpy() - lse_r)))
     print(f"full size head {h}: O |err| / bound max {ratio:.3f}, LSE {err_l:.3e}")
     assert ratio <= 1.0 and err_l <= 1e-3
+
+
+def test_fp8_full_size_d1024_sampled_heads(lib):
+    """The grouped causal D = 1024 shape (B=1, Hq=32, Hkv=8, N=8192, fp16): every head's amax
+    exactly, and two whole heads (different KV groups) against the emulation within the bound,
+    LSE within 1e-3."""
+    from head_dim_attention_amd import _binding as B
+    w = W.get("gqa_causal_d1024_n8192")
+    q, k, v, _ = W.workload_inputs(w, seed=2025)
+    b, hq, nq, d = q.shape
+    hkv, nkv = k.shape[1], k.shape[2]
+    g = hq // hkv
+    nws = B.ffpa_fwd_fp8_workspace_bytes(b, hq, hkv, nq, nkv, d)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    print("fp8 full size d1024", flush=True)
+    o, lse = lib.ffpa_fwd_fp8(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=scale, workspace=ws)
+    torch.cuda.synchronize()
+    aq, ak, av, _, _ = B.fp8_workspace_views(ws, b, hq, hkv, nkv, d)
+    for x, a in ((q, aq), (k, ak), (v, av)):
+        assert np.array_equal(a.cpu().double().numpy(), ref.fp8_quantize(x)[1])
+    for h in (3, 29):
+        qs, ks, vs = q[:, h:h + 1], k[:, h // g:h // g + 1], v[:, h // g:h // g + 1]
+        o_r, lse_r, parts = ref.attn_fwd_fp8(qs, ks, vs, scale=float(np.float32(scale)), causal=True, parts=True)
+        og = to64(o[:, h:h + 1])
+        ratio = float(np.max(np.abs(og - o_r) / fp8_o_bound(parts, o_r, 1, w.torch_dtype)))
+        err_l = float(np.max(np.abs(lse[:, h:h + 1].double().cpu().numpy() - lse_r)))
+        print(f"full size d1024 head {h}: O |err| / bound max {ratio:.3f}, LSE {err_l:.3e}", flush=True)
+        assert ratio <= 1.0 and err_l <= 1e-3
