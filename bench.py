@@ -493,6 +493,19 @@ def cpu_baseline(q, k, v, do, scale, causal, dq, dk, dv, o, lse, tol_o, budget_s
     return base, par
 
 
+def calibration_copy(mib: int, dev) -> None:
+    """One device-to-device copy of `mib` MiB: its FETCH_SIZE / WRITE_SIZE readings under a
+    counter run give the scale from those counters to bytes."""
+    if mib <= 0:
+        return
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def run_legs(F, W, names, seed: int, steps: int, warmup: int) -> dict:
     legs = {}
     for name in names:
@@ -535,7 +548,9 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
 
     if args.only_legs:
-        print(json.dumps({"configs": run_legs(F, W, names, args.seed, max(args.steps, 5), args.warmup)}), flush=True)
+        legs = run_legs(F, W, names, args.seed, max(args.steps, 5), args.warmup)
+        calibration_copy(args.calib_copy_mib, dev)
+        print(json.dumps({"configs": legs}), flush=True)
         return 0
 
     q, k, v, do = W.workload_inputs(w, args.seed)
@@ -633,14 +648,7 @@ def main(argv=None) -> int:
         print(f"bench: timing the split-KV decode pass on {args.decode_workload}", file=sys.stderr, flush=True)
         out["decode"] = decode_leg(F, W, W.get(args.decode_workload), args.seed, max(args.steps, 10), args.warmup)
 
-    if args.calib_copy_mib > 0:
-        nbytes = args.calib_copy_mib << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
+    calibration_copy(args.calib_copy_mib, dev)
     print(json.dumps(out), flush=True)
     return 0
 

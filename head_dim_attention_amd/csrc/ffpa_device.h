@@ -266,7 +266,13 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // whole sequences to one XCD; there XCD x takes heads x, x + 8, ... of every sequence (each XCD
 // the same share of every sequence, a head's items still on one XCD) when the head count is a
 // multiple of 8, else the items round-robin. Needs grid = total rounded up to a multiple of 8.
+// Building with -DFFPA_XCD_ORDER=0 hands out items in launch order instead (workgroup L takes
+// item L), which is only useful to measure what the mapping saves in L2 traffic.
+#ifndef FFPA_XCD_ORDER
+#define FFPA_XCD_ORDER 1
+#endif
 __device__ __forceinline__ int xcd_item(int L, int grid, bool varlen, int heads, int inner) {
+  if (!FFPA_XCD_ORDER) return L;
   if (!varlen) return (L & 7) * (grid >> 3) + (L >> 3);
   if ((heads & 7) != 0) return L;
   const int r = L >> 3, hpx = heads >> 3;

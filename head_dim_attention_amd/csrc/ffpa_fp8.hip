@@ -209,7 +209,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_fwd_fp8_kernel(AttnParams p, cons
   lds_t* const xmbuf = smem + C::XM_OFF;
 
   const int L = blockIdx.x;
-  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  const int item = xcd_item(L, gridDim.x, false, 0, 0);
   if (item >= p.total) return;
   int t = item % p.ntiles;
   const int hs = item / p.ntiles;
@@ -546,7 +546,7 @@ __global__ void __launch_bounds__(512, 2) ffpa_fwd_fp8_wide_kernel(AttnParams p,
   lds_t* const xmbuf = smem + C::XM_OFF;
 
   const int L = blockIdx.x;
-  const int item = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  const int item = xcd_item(L, gridDim.x, false, 0, 0);
   if (item >= p.total) return;
   int t = item % p.ntiles;
   const int hs = item / p.ntiles;
