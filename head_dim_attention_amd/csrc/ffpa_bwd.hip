@@ -913,10 +913,10 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
   const int item = xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hq, p.ntiles * p.nsplit);
   if (item >= p.total) return;
   const int split = item % p.nsplit;
-  int t = (item / p.nsplit) % p.ntiles;
-  const int hs = item / p.nsplit / p.ntiles;
-  const int h = hs % p.hq;
-  const int s = hs / p.hq;
+  const HeadTile ht = head_tile(item / p.nsplit, p.ntiles, p.hq, p.group, p.cu_q == nullptr);
+  int t = ht.t;
+  const int h = ht.h;
+  const int s = ht.s;
   if (p.causal) t = p.ntiles - 1 - t;  // heaviest causal tiles first
 
   const SeqView sv = seq_view(p, s);
@@ -1211,10 +1211,10 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_wide_kernel(AttnParams p) {
   const int item = xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hq, p.ntiles * p.nsplit);
   if (item >= p.total) return;
   const int split = item % p.nsplit;
-  int t = (item / p.nsplit) % p.ntiles;
-  const int hs = item / p.nsplit / p.ntiles;
-  const int h = hs % p.hq;
-  const int s = hs / p.hq;
+  const HeadTile ht = head_tile(item / p.nsplit, p.ntiles, p.hq, p.group, p.cu_q == nullptr);
+  int t = ht.t;
+  const int h = ht.h;
+  const int s = ht.s;
   if (p.causal) t = p.ntiles - 1 - t;  // heaviest causal tiles first
 
   const SeqView sv = seq_view(p, s);
@@ -1487,12 +1487,17 @@ struct DqCfg {
 template <class T, int NDB>
 __device__ __forceinline__ void dq_from_ds_body(const AttnParams& p, int nchunk, int ntiles, int item, lds_t* smem) {
   using C = DqCfg<NDB>;
-  int qt = item % ntiles;
-  const int rest = item / ntiles;
-  const int chunk = rest % nchunk;
-  const int hs = rest / nchunk;
-  const int h = hs % p.hq;
-  const int s = hs / p.hq;
+  // item = (head-tile slice * nchunk + chunk) * (ntiles G) + head_tile's index within the slice:
+  // dense, the G query heads of a KV head side by side (head_tile); varlen, item = ((s Hq + h)
+  // nchunk + chunk) ntiles + t.
+  const bool dense = p.cu_q == nullptr;
+  const int per_chunk = dense ? ntiles * p.group : ntiles;
+  const int chunk = (item / per_chunk) % nchunk;
+  const HeadTile ht = head_tile((item / (per_chunk * nchunk)) * per_chunk + item % per_chunk, ntiles, p.hq,
+                                p.group, dense);
+  int qt = ht.t;
+  const int h = ht.h;
+  const int s = ht.s;
   if (p.causal) qt = ntiles - 1 - qt;
 
   const SeqView sv = seq_view(p, s);

@@ -280,6 +280,32 @@ __device__ __forceinline__ int xcd_item(int L, int grid, bool varlen, int heads,
   return ((q / hpx) * heads + (L & 7) + 8 * (q % hpx)) * inner + t;
 }
 
+// Tile item -> (sequence or batch s, query head h, tile t). Dense grids put the G query heads of
+// a KV head side by side, item = ((s Hkv + kvh) ntiles + t) G + (h - kvh G): they sweep the same
+// keys at the same time, so a tile's K/V lines serve all of them from L2. Varlen keeps
+// item = (s Hq + h) ntiles + t (its XCD mapping hands out whole heads by index).
+struct HeadTile {
+  int s, h, t;
+};
+__device__ __forceinline__ HeadTile head_tile(int item, int ntiles, int hq, int group, bool dense) {
+  HeadTile r;
+  if (dense) {
+    const int hg = item % group;
+    const int rest = item / group;
+    r.t = rest % ntiles;
+    const int ks = rest / ntiles;
+    const int hkv = hq / group;
+    r.h = (ks % hkv) * group + hg;
+    r.s = ks / hkv;
+  } else {
+    r.t = item % ntiles;
+    const int hs = item / ntiles;
+    r.h = hs % hq;
+    r.s = hs / hq;
+  }
+  return r;
+}
+
 // Geometry of one (batch or sequence) slice, resolved from dense strides or cu_seqlens.
 struct SeqView {
   long long q_off, k_off, lse_off, v_off, o_off;

@@ -211,10 +211,10 @@ __global__ void __launch_bounds__(512, 2) ffpa_fwd_fp8_kernel(AttnParams p, cons
   const int L = blockIdx.x;
   const int item = xcd_item(L, gridDim.x, false, 0, 0);
   if (item >= p.total) return;
-  int t = item % p.ntiles;
-  const int hs = item / p.ntiles;
-  const int h = hs % p.hq;
-  const int s = hs / p.hq;
+  const HeadTile ht = head_tile(item, p.ntiles, p.hq, p.group, true);
+  int t = ht.t;
+  const int h = ht.h;
+  const int s = ht.s;
   if (p.causal) t = p.ntiles - 1 - t;
   const int qt0 = t * 128;
   if (qt0 >= p.nq) return;
@@ -548,10 +548,10 @@ __global__ void __launch_bounds__(512, 2) ffpa_fwd_fp8_wide_kernel(AttnParams p,
   const int L = blockIdx.x;
   const int item = xcd_item(L, gridDim.x, false, 0, 0);
   if (item >= p.total) return;
-  int t = item % p.ntiles;
-  const int hs = item / p.ntiles;
-  const int h = hs % p.hq;
-  const int s = hs / p.hq;
+  const HeadTile ht = head_tile(item, p.ntiles, p.hq, p.group, true);
+  int t = ht.t;
+  const int h = ht.h;
+  const int s = ht.s;
   if (p.causal) t = p.ntiles - 1 - t;
   const int qt0 = t * 64;
   if (qt0 >= p.nq) return;

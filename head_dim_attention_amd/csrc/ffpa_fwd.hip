@@ -96,12 +96,12 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   } else {
     const int tile_item = SPL ? item / p.nsplit : item;
     if constexpr (SPL) split = item % p.nsplit;
-    t = tile_item % p.ntiles;
-    const int hs = tile_item / p.ntiles;
-    h = hs % p.hq;
-    s = hs / p.hq;
-    if (p.causal) t = p.ntiles - 1 - t;  // heaviest causal tiles first
+    const HeadTile ht = head_tile(tile_item, p.ntiles, p.hq, p.group, p.cu_q == nullptr);
+    t = ht.t;
+    h = ht.h;
+    s = ht.s;
     kvh = h / p.group;
+    if (p.causal) t = p.ntiles - 1 - t;  // heaviest causal tiles first
   }
 
   const SeqView sv = seq_view(p, s);
