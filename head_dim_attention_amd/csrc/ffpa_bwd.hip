@@ -1550,7 +1550,7 @@ __device__ __forceinline__ void dq_from_ds_body(const AttnParams& p, int nchunk,
       dma16_buf(krs, kvoff[c], min(j * 32 + i, sv.lk - 1) * krow_bytes, stage + i * 1024);
     } else {
       const int key = min(j * 32 + srow_l, sv.lk - 1);
-      dma16_buf(srs, (key * dsv.row + sqoff) * 2, 0, stage + C::KTILE + w * 1024);
+      dma16_buf_nt(srs, (key * dsv.row + sqoff) * 2, 0, stage + C::KTILE + w * 1024);
     }
   };
   constexpr int NCOPY = C::KCOPY + C::SCOPY;
@@ -1782,14 +1782,18 @@ __device__ __forceinline__ void dv_from_p_body(const AttnParams& p, int nchunk, 
   const int dg = w & 3;
   const int off = sv.lk - sv.lq;
 
-  // Streamed steps: SQ-query tiles of each query head of the group.
+  // Streamed steps: SQ-query tiles, from the last one down to the first that sees a key of the
+  // block, each for every query head of the group in turn. Every workgroup of a causal grid then
+  // starts at the same (last) tile and the workgroups sweep the same query rows at the same time,
+  // whatever their key block, so the rows they read are shared in L2 (in ascending order each
+  // would start at its own first query and the sweeps would drift apart).
   constexpr int SQ = C::KB2 * 16;
   const int qfirst = p.causal ? max(0, k0 - off) : 0;
   const int qt_first = qfirst / SQ;
   const int nqt = sv.lq > qfirst ? (sv.lq + SQ - 1) / SQ - qt_first : 0;
   const int nsteps = p.group * nqt;
-  auto step_head = [&](int st) { return kvh * p.group + st / nqt; };
-  auto step_row0 = [&](int st) { return (qt_first + st % nqt) * SQ; };
+  auto step_head = [&](int st) { return kvh * p.group + st % p.group; };
+  auto step_row0 = [&](int st) { return (qt_first + nqt - 1 - st / p.group) * SQ; };
 
   f32x16_t acc[C::KB][NDB];
 #pragma unroll
@@ -1836,7 +1840,7 @@ __device__ __forceinline__ void dv_from_p_body(const AttnParams& p, int nchunk, 
       dma16_buf(x.ors, ovoff[c], min(x.row0 + i, sv.lq - 1) * orow_bytes, stage + i * 1024);
     } else {
       const int pc = c - C::OCOPY;
-      dma16_buf(x.prs, (pkey[pc] * dsv.row + x.row0 + 8 * pchunk[pc]) * 2, 0,
+      dma16_buf_nt(x.prs, (pkey[pc] * dsv.row + x.row0 + 8 * pchunk[pc]) * 2, 0,
                 stage + C::OTILE + (C::PCOPY * w + pc) * 1024);
     }
   };

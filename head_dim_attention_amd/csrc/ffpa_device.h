@@ -167,6 +167,22 @@ __device__ __forceinline__ void dma16_buf(i32x4_t r, int voff, int soff, lds_t* 
       : "memory");
 }
 
+// dma16_buf with the non-temporal hint, for blocks each workgroup reads once: they are not kept
+// in L2 at the expense of the rows that neighbouring workgroups read again.
+__device__ __forceinline__ void dma16_buf_nt(i32x4_t r, int voff, int soff, lds_t* lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(r), "s"(soff), "s"(m)
+      : "memory");
+}
+
 // Scheduling pin for a run of N MFMAs fed by LDS reads in the current scheduling region: the
 // reads of the first AHEAD MFMAs first, then alternately one MFMA and the reads of a later one,
 // then the last AHEAD MFMAs. Each MFMA then finds its operand already loaded instead of waiting
