@@ -875,7 +875,8 @@ static hipError_t launch_bwd_pp(AttnParams p, hipStream_t st) {
 //   slot 2j + 1: group 0 finishes tile j     | group 1 multiplies tile j
 // Tile j + 1 goes into the buffer of tile j - 1, which group 1 last read in slot 2j - 1, and group
 // 1 completes the copies before the barrier that ends slot 2j + 1. All copies are issued by the
-// finishing group: the multiplying waves issue nothing but LDS reads and MFMAs.
+// finishing group: the multiplying waves issue nothing but LDS reads and MFMAs. (j counts the
+// item's steps; with a key-range split, step j covers key tile split + j nsplit.)
 // ------------------------------------------------------------------------------------------------
 // LDS operands requested ahead in the P/dS kernel's score products.
 constexpr int kPdsAhead = 2;
@@ -908,7 +909,8 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
   lds_t* const xbuf = smem + 4 * C::TILE;
 
   // Work item (sequence, query head, query tile, key range): grids too small to fill the GPU
-  // split each tile's key tiles into p.nsplit ranges (P and dS of different keys are independent).
+  // split each tile's key tiles into p.nsplit interleaved sets (P and dS of different keys are
+  // independent).
   const int L = blockIdx.x;
   const int item = xcd_item(L, gridDim.x, p.cu_q != nullptr, p.hq, p.ntiles * p.nsplit);
   if (item >= p.total) return;
@@ -944,10 +946,13 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
   int kend = sv.lk;
   if (p.causal) kend = min(kend, qt0 + C::BQ + off);
   const int ntk = kend > 0 ? (kend + 31) >> 5 : 0;
-  // This item's key tiles [jb, je): an equal share of the query tile's own range.
-  const int per = (ntk + p.nsplit - 1) / p.nsplit;
-  const int jb = min(split * per, ntk), je = min(jb + per, ntk);
-  if (jb >= je && split > 0) return;
+  // This item's key tiles: every nsplit-th of the query tile's own range, from tile `split` on
+  // (step jj covers key tile split + jj nsplit). Interleaved, not contiguous, so that the ranges
+  // of all the grid's items start at the first key tiles and sweep the keys together (shared K/V
+  // lines in L2).
+  const int nsteps = split < ntk ? (ntk - split + p.nsplit - 1) / p.nsplit : 0;
+  auto tile_of = [&](int jj) { return split + jj * p.nsplit; };
+  if (nsteps == 0 && split > 0) return;
 
   // Q and dO columns of this wave as B operands: lane (h, n) holds query n, dims 16 kb + 8 h + 0..7.
   const int qi = qw0 + l32;
@@ -999,9 +1004,11 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
   // multiplying phase issues no copies), used after the exchange.
   const long long mrow = MASK ? mask_row(p, s, h, min(qi, sv.lq - 1)) : 0;
   u32x4_t mraw;
-  // Partial S^T and dP^T of tile j over this wave's half; the partner's rows go to the exchange.
-  auto m_phase = [&](int j) {
-    const uint32_t kt = lds_addr(kbuf(j & 1)), vt = lds_addr(vbuf(j & 1));
+  // Partial S^T and dP^T of step jj (key tile j) over this wave's half; the partner's rows go to
+  // the exchange.
+  auto m_phase = [&](int jj) {
+    const int j = tile_of(jj);
+    const uint32_t kt = lds_addr(kbuf(jj & 1)), vt = lds_addr(vbuf(jj & 1));
     if constexpr (MASK) {
       mraw = mask_block(p, mrow, j * 32 + 16 * cg + 8 * hh, sv.lk);
       __builtin_amdgcn_sched_barrier(0);  // issued here, not sunk behind the products
@@ -1023,7 +1030,8 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
     }
   };
   // Full S and dP of this lane's 8 keys (own half + partner's), then P, dS and their stores.
-  auto e_phase = [&](int j, auto&& copies) {
+  auto e_phase = [&](int jj, auto&& copies) {
+    const int j = tile_of(jj);
     const int pw = w ^ 1;
     float sf[8], df[8];
 #pragma unroll
@@ -1088,49 +1096,49 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, dt), ds_rs, (int)boff, 0, kDsStoreCpol);
   };
 
-  if (je > jb) {
-    // Tile jb by all waves (rows w + 8 ii of K and V).
+  if (nsteps > 0) {
+    // The first step's tile by all waves (rows w + 8 ii of K and V).
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int i = w + 8 * ii;
-      const int row = min(jb * 32 + i, sv.lk - 1) * row_bytes;
+      const int row = min(tile_of(0) * 32 + i, sv.lk - 1) * row_bytes;
       const int vo = src_chunk(lane ^ swz(i)) << 4;
-      dma16_buf(krs, vo, row, kbuf(jb & 1) + i * 1024);
-      dma16_buf(vrs, vo, row, vbuf(jb & 1) + i * 1024);
+      dma16_buf(krs, vo, row, kbuf(0) + i * 1024);
+      dma16_buf(vrs, vo, row, vbuf(0) + i * 1024);
     }
   }
   wait_all();  // the stationary operands, LSE, Delta and tile 0
   lds_barrier();
 
-  if (je > jb) {
+  if (nsteps > 0) {
     if (grp == 0) {
       // Only stores leave this group's waves inside the loop; they are not waited for.
-      for (int j = jb; j < je; ++j) {
-        m_phase(j);
+      for (int jj = 0; jj < nsteps; ++jj) {
+        m_phase(jj);
         lds_barrier();
-        e_phase(j, [] {});
+        e_phase(jj, [] {});
         lds_barrier();
       }
       lds_barrier();
     } else {
 #pragma unroll
       for (int ii = 0; ii < C::GCOPY; ++ii) {
-        gcopy(krs, kbuf((jb + 1) & 1), jb + 1, ii);
-        gcopy(vrs, vbuf((jb + 1) & 1), jb + 1, ii);
+        gcopy(krs, kbuf(1), tile_of(1), ii);
+        gcopy(vrs, vbuf(1), tile_of(1), ii);
       }
       lds_barrier();
-      for (int j = jb; j < je; ++j) {
-        m_phase(j);
-        // Tile j + 1 (copied in the prologue, or in the finishing phase of step j - 1, followed
-        // there by that step's two stores and then this step's mask load, which may stay in
-        // flight).
-        if (j == jb) wait_vmcnt<0>(); else wait_vmcnt<MASK ? 3 : 2>();
+      for (int jj = 0; jj < nsteps; ++jj) {
+        m_phase(jj);
+        // The next step's tile (copied in the prologue, or in the finishing phase of the step
+        // before, followed there by that step's two stores and then this step's mask load, which
+        // may stay in flight).
+        if (jj == 0) wait_vmcnt<0>(); else wait_vmcnt<MASK ? 3 : 2>();
         lds_barrier();
-        e_phase(j, [&] {
+        e_phase(jj, [&] {
 #pragma unroll
           for (int ii = 0; ii < C::GCOPY; ++ii) {
-            gcopy(krs, kbuf(j & 1), j + 2, ii);
-            gcopy(vrs, vbuf(j & 1), j + 2, ii);
+            gcopy(krs, kbuf(jj & 1), tile_of(jj + 2), ii);
+            gcopy(vrs, vbuf(jj & 1), tile_of(jj + 2), ii);
           }
         });
         lds_barrier();
@@ -1146,7 +1154,7 @@ static hipError_t launch_pds(AttnParams p, hipStream_t st) {
   using C = PdsCfg<NDB>;
   p.ntiles = (p.nq + C::BQ - 1) / C::BQ;
   // Fewer than two workgroups per compute unit (of 256): split the key tiles of each query tile
-  // into up to 8 ranges of at least 4 tiles, which also spreads the heavy tiles of a causal grid.
+  // into up to 8 interleaved sets of at least 4 tiles, which also spreads the heavy tiles of a causal grid.
   const long long base = (long long)p.batch * p.hq * p.ntiles;
   const int ktiles = (p.nkv + 31) / 32;
   p.nsplit = (int)std::max(1LL, std::min({8LL, (512 + base - 1) / std::max(base, 1LL), (long long)ktiles / 4}));
