@@ -19,7 +19,8 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers to contiguous buffers owned by the caller. The
- *     library allocates no memory and keeps no state between calls.
+ *     library allocates no memory and keeps no state between calls, except the fixed per-device
+ *     scratch array that ffpa_decode_fwd_noalloc uses in place of a workspace.
  *   - Element (b, h, n, d) of a dense [B, H, N, D] tensor sits at ((b*H + h)*N + n)*D + d;
  *     element (t, h, d) of a packed [T, H, D] tensor sits at (t*H + h)*D + d.
  *   - Query head h reads KV head h / (Hq / Hkv).
