@@ -194,8 +194,11 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_bwd_kernel(AttnParams p)
     nqt = sv.lq > qfirst ? ((sv.lq + 31) >> 5) - qt_first : 0;
     nsteps = p.group * nqt;
   }
-  auto step_head = [&](int st) { return OWN_Q ? hd / p.group : hd * p.group + st / nqt; };
-  auto step_row0 = [&](int st) { return OWN_Q ? st * 32 : (qt_first + st % nqt) * 32; };
+  // dK/dV: query tiles from the last down, each for every head of the group (the workgroups of a
+  // causal grid then start at the same tile and sweep the same query rows together, as in the
+  // products from the stored blocks).
+  auto step_head = [&](int st) { return OWN_Q ? hd / p.group : hd * p.group + st % p.group; };
+  auto step_row0 = [&](int st) { return OWN_Q ? st * 32 : (qt_first + nqt - 1 - st / p.group) * 32; };
   auto str_base = [&](int head) {
     return OWN_Q ? sv.k_off + (long long)head * p.k_head : sv.q_off + (long long)head * p.q_head;
   };
@@ -567,8 +570,11 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
     nqt = sv.lq > qfirst ? ((sv.lq + 31) >> 5) - qt_first : 0;
     nsteps = p.group * nqt;
   }
-  auto step_head = [&](int st) { return OWN_Q ? hd / p.group : hd * p.group + st / nqt; };
-  auto step_row0 = [&](int st) { return OWN_Q ? st * 32 : (qt_first + st % nqt) * 32; };
+  // dK/dV: query tiles from the last down, each for every head of the group (the workgroups of a
+  // causal grid then start at the same tile and sweep the same query rows together, as in the
+  // products from the stored blocks).
+  auto step_head = [&](int st) { return OWN_Q ? hd / p.group : hd * p.group + st % p.group; };
+  auto step_row0 = [&](int st) { return OWN_Q ? st * 32 : (qt_first + nqt - 1 - st / p.group) * 32; };
   auto str_base = [&](int head) {
     return OWN_Q ? sv.k_off + (long long)head * p.k_head : sv.q_off + (long long)head * p.q_head;
   };
