@@ -20,8 +20,12 @@
 // in 32-row tiles (buffer_load...lds), partial head-dim products combined through LDS, scores in a
 // C-block layout whose registers feed the accumulating product directly as B operands, and the
 // accumulating product's A operand read transposed from the streamed tile (ds_read_b64_tr_b16).
-// For D <= 512, dV runs 8 waves (NC = 2) and dK/dQ run the 8-wave reduce-scatter variant below
-// (NC = 4), both at two waves per SIMD; larger head dims use 4 waves (NC = 4), one per SIMD.
+// Two paths. With a caller's P/dS workspace, one kernel forms P and dS for every (query, key) pair
+// and stores them (8 waves; D <= 512 in two head-dim halves, above in four quarters), and dK, dV
+// and dQ become plain products of the stored blocks (8 waves each, or one launch of all three for
+// small grids). Without it, the stages recompute: for D <= 512 dV runs 8 waves (NC = 2) and dK/dQ
+// the 8-wave reduce-scatter variant (NC = 4), at two waves per SIMD; larger head dims use 4 waves
+// (NC = 4), one per SIMD.
 #include <algorithm>
 
 #include "ffpa_device.h"
