@@ -10,8 +10,9 @@
 //  * One workgroup of NW = 8 wave64s (two per SIMD) owns BQ = NR*QB*32 queries of one head: 128
 //    for D <= 512 (4 row groups x 2 head-dim halves), 64 above (2 x 4 quarters; the masked form
 //    above D = 896 keeps 4 waves and 32 queries), so each K/V tile copied into LDS serves that
-//    many queries. Each wave keeps QB*32 queries x DW head-dim columns of Q in registers (B operand of S^T = K Q^T) and
-//    the matching O^T block as fp32 MFMA accumulators ("O accumulator held per D chunk").
+//    many queries. Each wave keeps QB*32 queries x DW head-dim columns of Q in registers (B
+//    operand of S^T = K Q^T) and the matching O^T block as fp32 MFMA accumulators ("O
+//    accumulator held per D chunk").
 //  * K and V stream through LDS in 32-key tiles, copied straight from global memory with 16-byte
 //    global_load_lds (no VGPR staging), double-buffered when a tile pair fits twice in the 160 KB.
 //  * Scores are formed transposed (keys x queries): each lane owns one query column, so the row
