@@ -1676,27 +1676,11 @@ __device__ __forceinline__ void dq_from_ds_body(const AttnParams& p, int nchunk,
   // Copies issued during the last step land in LDS that the next workgroup may own.
   wait_vmcnt<0>();
 
-  // ---- epilogue: scale, round once, store rows < lq and columns < D
+  // ---- epilogue: scale, round once, store rows < lq and columns < D (whole rows, through LDS)
   uint16_t* dqh = (uint16_t*)p.dq + sv.q_off + (long long)h * p.q_head;
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    const int qi = q0 + 64 * qg + 32 * qb + l32;
-    if (qi < sv.lq) {
-      uint16_t* dst = dqh + (long long)qi * p.q_row;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = d0 + dg * C::DW + 32 * db + 8 * i4 + 4 * hh;
-          if (d < p.d) {
-            const f32x16_t& a = acc[qb][db];
-            const u32x2_t pk = {Elt<T>::pack2(a[4 * i4] * p.scale, a[4 * i4 + 1] * p.scale),
-                                Elt<T>::pack2(a[4 * i4 + 2] * p.scale, a[4 * i4 + 3] * p.scale)};
-            *(u32x2_t*)(dst + d) = pk;
-          }
-        }
-    }
-  }
+  static_assert(C::LDS >= 64 * 1024, "epilogue stage");
+  store_block_rows<T, 2, 4, C::QB, NDB>(smem, acc, p.scale, dqh + (long long)q0 * p.q_row + d0, p.q_row, sv.lq - q0,
+                                        min(C::DWG, p.d - d0));
 }
 
 template <class T, int NDB>
@@ -1963,28 +1947,11 @@ __device__ __forceinline__ void dv_from_p_body(const AttnParams& p, int nchunk, 
   // Copies issued during the last steps land in LDS that the next workgroup may own.
   wait_vmcnt<0>();
 
-  // ---- epilogue: round once, store keys < Lk and columns < D
+  // ---- epilogue: round once, store keys < Lk and columns < D (whole rows, through LDS)
   uint16_t* dvh = (uint16_t*)(DK ? p.dk : p.dv) + sv.k_off + (long long)kvh * p.k_head;
-  const float oscale = DK ? p.scale : 1.0f;
-#pragma unroll
-  for (int kb = 0; kb < C::KB; ++kb) {
-    const int kj = k0 + 64 * kg + 32 * kb + l32;
-    if (kj < sv.lk) {
-      uint16_t* dst = dvh + (long long)kj * p.k_row;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = d0 + dg * C::DW + 32 * db + 8 * i4 + 4 * hh;
-          if (d < p.d) {
-            const f32x16_t& a = acc[kb][db];
-            const u32x2_t pk = {Elt<T>::pack2(a[4 * i4] * oscale, a[4 * i4 + 1] * oscale),
-                                Elt<T>::pack2(a[4 * i4 + 2] * oscale, a[4 * i4 + 3] * oscale)};
-            *(u32x2_t*)(dst + d) = pk;
-          }
-        }
-    }
-  }
+  static_assert(C::LDS >= 64 * 1024, "epilogue stage");
+  store_block_rows<T, 2, 4, C::KB, NDB>(smem, acc, DK ? p.scale : 1.0f, dvh + (long long)k0 * p.k_row + d0, p.k_row,
+                                        sv.lk - k0, min(C::DWG, p.d - d0));
 }
 
 template <class T, int NDB, bool DK>
@@ -2176,12 +2143,20 @@ static hipError_t launch_bwd_mode(const AttnParams& p, hipStream_t st) {
 // dK, dV and dQ from the stored blocks in one launch, for dense grids too small to fill the GPU.
 // Each product pass alone runs one workgroup per compute unit or fewer, and a causal grid's
 // heaviest tile (first keys for dK/dV, last queries for dQ) takes about twice the average tile's
-// time; with the three passes' work items in one grid (dK, then dV, then dQ, heaviest tiles of
-// each head first) the compute units that finish light tiles take the next items, so the launch
-// takes about the sum of the average times instead of the sum of the heaviest.
+// time. The three passes' items share one grid, in an order that lets the dispatcher balance
+// them: a slice is one (batch, KV head, head-dim chunk) with its dK and dV key tiles and its
+// dQ query tiles (G heads); rank r of a slice is its r-th heaviest dK, dV and dQ tiles; the list
+// runs rank by rank (r = 0 first), and within a rank slice by slice. Every compute unit that
+// finishes early then takes the heaviest item left (longest-processing-time order), so the
+// launch ends close to the average load instead of a heavy item started last.
+// XCDs: with a multiple of 8 slices, XCD x runs the ranks of its own slices (one slice's rows in
+// one L2); otherwise the whole list goes round-robin over the XCDs (L mod 8), which still hands
+// each XCD a heaviest-first sequence.
 // ------------------------------------------------------------------------------------------------
 struct ProductsGrid {
   int nchunk, ktiles, qtiles, nk, nq;  // nk: dK (and dV) items, nq: dQ items
+  int nslice;                          // (batch, KV head, chunk) slices
+  int per_xcd;                         // slices per XCD (nslice % 8 == 0), else 0
 };
 
 template <int NDB>
@@ -2191,13 +2166,41 @@ template <class T, int NDB>
 __global__ void __launch_bounds__(512, 2) ffpa_products_kernel(AttnParams p, ProductsGrid g) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[products_lds<NDB>()];
   lds_t* const smem = (lds_t*)smem_raw;
-  const int item = xcd_item(blockIdx.x, gridDim.x, false, 0, 0);
-  if (item < g.nk)
-    dv_from_p_body<T, NDB, true>(p, g.nchunk, g.ktiles, item, smem);
-  else if (item < 2 * g.nk)
-    dv_from_p_body<T, NDB, false>(p, g.nchunk, g.ktiles, item - g.nk, smem);
-  else if (item < 2 * g.nk + g.nq)
-    dq_from_ds_body<T, NDB>(p, g.nchunk, g.qtiles, item - 2 * g.nk, smem);
+  const int L = blockIdx.x;
+  // i: position in the rank-ordered list of nsl slices starting at slice sl0
+  int i = L, nsl = g.nslice, sl0 = 0;
+  if (g.per_xcd > 0) {
+    i = L >> 3;
+    nsl = g.per_xcd;
+    sl0 = (L & 7) * g.per_xcd;
+  }
+  // Ranks below min(ktiles, qtiles) hold 2 + G items per slice (dK, dV, then dQ of each query
+  // head); past it only the longer side's items remain (2 or G per slice).
+  const int m = min(g.ktiles, g.qtiles);
+  const int gs = 2 + p.group;
+  int r, sl, j;  // j = 0: dK, 1: dV, 2 + hg: dQ of query head hg of the group
+  if (i < m * nsl * gs) {
+    r = i / (nsl * gs);
+    const int rem = i % (nsl * gs);
+    sl = rem / gs;
+    j = rem % gs;
+  } else {
+    const bool keys = g.ktiles > g.qtiles;
+    const int gs2 = keys ? 2 : p.group;
+    const int i2 = i - m * nsl * gs;
+    r = m + i2 / (nsl * gs2);
+    const int rem = i2 % (nsl * gs2);
+    sl = rem / gs2;
+    j = rem % gs2 + (keys ? 0 : 2);
+  }
+  if (r >= max(g.ktiles, g.qtiles)) return;  // padding of the grid to a multiple of 8
+  sl += sl0;
+  if (j == 0)
+    dv_from_p_body<T, NDB, true>(p, g.nchunk, g.ktiles, sl * g.ktiles + r, smem);
+  else if (j == 1)
+    dv_from_p_body<T, NDB, false>(p, g.nchunk, g.ktiles, sl * g.ktiles + r, smem);
+  else
+    dq_from_ds_body<T, NDB>(p, g.nchunk, g.qtiles, (sl * g.qtiles + r) * p.group + (j - 2), smem);
 }
 
 static ProductsGrid products_grid(const AttnParams& p) {
@@ -2205,8 +2208,10 @@ static ProductsGrid products_grid(const AttnParams& p) {
   g.nchunk = (p.d + 511) / 512;
   g.ktiles = (p.nkv + DvCfg<4>::BK - 1) / DvCfg<4>::BK;
   g.qtiles = (p.nq + DqCfg<4>::BQ - 1) / DqCfg<4>::BQ;
-  g.nk = p.batch * p.hkv * g.nchunk * g.ktiles;
-  g.nq = p.batch * p.hq * g.nchunk * g.qtiles;
+  g.nslice = p.batch * p.hkv * g.nchunk;
+  g.nk = g.nslice * g.ktiles;
+  g.nq = g.nslice * p.group * g.qtiles;
+  g.per_xcd = g.nslice % 8 == 0 ? g.nslice / 8 : 0;
   return g;
 }
 

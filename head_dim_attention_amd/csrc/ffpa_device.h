@@ -245,11 +245,25 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Combine the values of lanes l and l ^ 32 (the two halves of a wave). Both lanes of a pair
-// add/compare the same two operands (commutative), so they get bit-identical results.
-__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32); }
-__device__ __forceinline__ float half_max(float x) { return fmaxf(x, other_half(x)); }
-__device__ __forceinline__ float half_sum(float x) { return x + other_half(x); }
+// Combine the values of lanes l and l ^ 32 (the two halves of a wave). v_permlane32_swap
+// exchanges the upper half of one register with the lower half of another in the VALU (no LDS
+// round trip); applied to two copies of x it leaves lane l with x of lanes l % 32 and 32 + l % 32,
+// so every lane combines the same two operands in the same order and gets the same bits.
+__device__ __forceinline__ void wave_halves(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float half_max(float x) {
+  float lo, hi;
+  wave_halves(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  float lo, hi;
+  wave_halves(x, lo, hi);
+  return lo + hi;
+}
 
 // Opaque register definition (empty asm): the value is not known to the compiler past this point,
 // so nothing derived from it is hoisted out of a loop (it is recomputed where it is used instead
@@ -294,6 +308,58 @@ __device__ __forceinline__ int xcd_item(int L, int grid, bool varlen, int heads,
   const int r = L >> 3, hpx = heads >> 3;
   const int t = r % inner, q = r / inner;
   return ((q / hpx) * heads + (L & 7) + 8 * (q % hpx)) * inner + t;
+}
+
+// Epilogue store of a workgroup's output block through LDS, so that each global store writes 1 KB
+// of one row (64 lanes x 16 bytes) rather than 16-byte pieces of 32 rows; the store path takes a
+// piece per cache line and cycle, so the scattered form costs about 32 cycles an instruction.
+// The 8 waves hold the block as NRG row groups x NCG column groups: wave (rg, cg) has RB x NDB fp32
+// C blocks, block (b, db) covering rows 32 (RB rg + b) + (lane % 32) and columns
+// 32 (NDB cg + db) + 8 i4 + 4 h + 0..3 in registers 4 i4 .. 4 i4 + 3 of lane half h. Per pass (one
+// b) every wave rounds its values times `scale` to T into an LDS stage of 32 NRG rows of 1 KB
+// (16-byte chunk c of stage row s at chunk c ^ (s % 16)), and after a barrier each wave copies
+// 4 NRG stage rows to dst (block row 0, column 0; row stride in elements). Rows at or past `rows`
+// and columns at or past `cols` (a multiple of 8) are not stored. Called by all 8 waves after
+// their last LDS read and DMA wait of the main loop; uses 32 NRG KB of LDS at `stage`.
+template <class T, int NRG, int NCG, int RB, int NDB>
+__device__ __forceinline__ void store_block_rows(lds_t* stage, const f32x16_t (&acc)[RB][NDB], float scale,
+                                                 uint16_t* dst, long long row_stride, int rows, int cols) {
+  static_assert(NRG * NCG == 8 && NCG * NDB * 32 <= 512, "8 waves, at most 512 columns");
+  const int w = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int rg = w / NCG;
+  const int cg = w % NCG;
+  lds_barrier();  // every wave is past its last read of the streamed tiles
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    {
+      const int srow = 32 * rg + l32;
+      const int base = srow * 1024 + 8 * hh;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int chunk = (NDB * cg + db) * 4 + i4;
+          const f32x16_t& a = acc[b][db];
+          const u32x2_t pk = {Elt<T>::pack2(a[4 * i4] * scale, a[4 * i4 + 1] * scale),
+                              Elt<T>::pack2(a[4 * i4 + 2] * scale, a[4 * i4 + 3] * scale)};
+          *(__attribute__((address_space(3))) u32x2_t*)(stage + base + ((chunk ^ (srow & 15)) << 4)) = pk;
+        }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int rr = 0; rr < 4 * NRG; ++rr) {
+      const int srow = 4 * NRG * w + rr;
+      const int brow = 32 * (RB * (srow >> 5) + b) + (srow & 31);
+      if (brow < rows && 8 * lane < cols) {
+        const u32x4_t x = lds_read_b128(stage, srow * 1024 + ((lane ^ (srow & 15)) << 4));
+        *(u32x4_t*)(dst + brow * row_stride + 8 * lane) = x;
+      }
+    }
+    if (b + 1 < RB) lds_barrier();  // the stage is rewritten by the next pass
+  }
 }
 
 // Tile item -> (sequence or batch s, query head h, tile t). Dense grids put the G query heads of

@@ -298,15 +298,21 @@ def test_varlen_exact_workspace_equals_bound(lib):
         assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("d,causal", [(512, True), (768, False), (384, True)])
-def test_bwd_fused_products_equal_stages(lib, d, causal):
+# (batch, hq, hkv, nq, nkv, d, causal): slice counts (batch x KV heads x head-dim chunks) of 2 and
+# 4 take the round-robin order of the one-launch products, 8 the per-XCD order, with more key
+# tiles than query tiles, fewer, or as many.
+@pytest.mark.parametrize("b,hq,hkv,nq,nkv,d,causal", [
+    (1, 4, 2, 300, 260, 512, True), (1, 4, 2, 300, 260, 768, False), (1, 4, 2, 300, 260, 384, True),
+    (1, 16, 8, 300, 420, 512, True), (2, 8, 4, 420, 260, 384, True), (1, 8, 8, 200, 200, 320, False)])
+def test_bwd_fused_products_equal_stages(lib, b, hq, hkv, nq, nkv, d, causal):
     """Stage 5 (dK, dV and dQ in one launch, which ffpa_bwd uses for small dense grids) equals
     stages 1, 2 and 3 bit for bit."""
-    q, k, v, do = W.dense_inputs(1, 4, 2, 300, 260, d, BF, seed=29 + d)
+    print(f"fused products b={b} hq={hq} hkv={hkv} nq={nq} nkv={nkv} d={d} causal={causal}", flush=True)
+    q, k, v, do = W.dense_inputs(b, hq, hkv, nq, nkv, d, BF, seed=29 + d + hq)
     qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
-    assert lib.ffpa_bwd_fused_products(1, 4, 2, 300, 260, d)
+    assert lib.ffpa_bwd_fused_products(b, hq, hkv, nq, nkv, d)
     o, lse = lib.ffpa_fwd(qc, kc, vc, causal=causal)
-    ws = torch.empty(lib.ffpa_bwd_workspace_bytes(1, 4, 300, 260), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(lib.ffpa_bwd_workspace_bytes(b, hq, nq, nkv), dtype=torch.uint8, device="cuda")
     delta = torch.empty_like(lse)
     outs = []
     for stages in ((0, 4, 1, 2, 3), (0, 4, 5)):
