@@ -311,20 +311,38 @@ __device__ __forceinline__ int xcd_item(int L, int grid, bool varlen, int heads,
 }
 
 // Epilogue store of a workgroup's output block through LDS, so that each global store writes 1 KB
-// of one row (64 lanes x 16 bytes) rather than 16-byte pieces of 32 rows; the store path takes a
-// piece per cache line and cycle, so the scattered form costs about 32 cycles an instruction.
-// The 8 waves hold the block as NRG row groups x NCG column groups: wave (rg, cg) has RB x NDB fp32
-// C blocks, block (b, db) covering rows 32 (RB rg + b) + (lane % 32) and columns
-// 32 (NDB cg + db) + 8 i4 + 4 h + 0..3 in registers 4 i4 .. 4 i4 + 3 of lane half h. Per pass (one
-// b) every wave rounds its values times `scale` to T into an LDS stage of 32 NRG rows of 1 KB
-// (16-byte chunk c of stage row s at chunk c ^ (s % 16)), and after a barrier each wave copies
-// 4 NRG stage rows to dst (block row 0, column 0; row stride in elements). Rows at or past `rows`
-// and columns at or past `cols` (a multiple of 8) are not stored. Called by all 8 waves after
-// their last LDS read and DMA wait of the main loop; uses 32 NRG KB of LDS at `stage`.
-template <class T, int NRG, int NCG, int RB, int NDB>
+// of one row (64 lanes x 16 bytes) rather than 8- or 16-byte pieces of 32 rows; the store path
+// takes a piece per cache line and cycle, so the scattered form costs about 32 cycles an
+// instruction. The 8 waves hold the block as NRG row groups x NCG column groups: wave (rg, cg)
+// has RB x NDB fp32 C blocks, block (b, db) covering rows 32 (RB rg + b) + (lane % 32) and columns
+// 32 (NDB cg + db) + 8 i4 + 4 h + 0..3 in registers 4 i4 .. 4 i4 + 3 of lane half h. The values
+// (times the lane's `scale`) go out as T (rounded once) or, with F32, as fp32. A pass stages the
+// rows of RGP row groups for one b in LDS rows of RS bytes (16-byte chunk c of stage row s at
+// chunk c ^ (s % 16)); after a barrier the 8 waves copy them to dst (block row 0, column 0; row
+// stride in elements). Rows at or past `rows` and columns at or past `cols` (a multiple of 8)
+// are not stored. Called by all 8 waves after their last LDS read and DMA wait of the main loop;
+// uses store_block_lds() bytes of LDS at `stage`.
+template <bool F32, int NCG, int NDB>
+struct BlockStore {
+  static constexpr int ES = F32 ? 4 : 2;                 // bytes per stored element
+  static constexpr int ROWB = NCG * NDB * 32 * ES;       // bytes of a block row
+  static constexpr int RS = ROWB <= 1024 ? 1024 : ROWB <= 2048 ? 2048 : 4096;
+  static constexpr int RGP_MAX = 4096 / RS;              // row groups per pass (128 KB of LDS)
+};
+template <bool F32, int NRG, int NCG, int NDB>
+constexpr int store_block_lds() {
+  using S = BlockStore<F32, NCG, NDB>;
+  return 32 * (NRG < S::RGP_MAX ? NRG : S::RGP_MAX) * S::RS;
+}
+template <class T, bool F32, int NRG, int NCG, int RB, int NDB>
 __device__ __forceinline__ void store_block_rows(lds_t* stage, const f32x16_t (&acc)[RB][NDB], float scale,
-                                                 uint16_t* dst, long long row_stride, int rows, int cols) {
-  static_assert(NRG * NCG == 8 && NCG * NDB * 32 <= 512, "8 waves, at most 512 columns");
+                                                 void* dst, long long row_stride, int rows, int cols) {
+  using S = BlockStore<F32, NCG, NDB>;
+  constexpr int RGP = NRG < S::RGP_MAX ? NRG : S::RGP_MAX;
+  static_assert(NRG * NCG == 8 && NRG % RGP == 0, "8 waves; whole row groups per pass");
+  constexpr int SROWS = 32 * RGP;       // stage rows per pass
+  constexpr int PER_WAVE = SROWS / 8;   // stage rows each wave copies out
+  constexpr int PARTS = S::RS / 1024;   // 1 KB store instructions per stage row
   const int w = wave_id();
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5;
@@ -333,33 +351,46 @@ __device__ __forceinline__ void store_block_rows(lds_t* stage, const f32x16_t (&
   const int cg = w % NCG;
   lds_barrier();  // every wave is past its last read of the streamed tiles
 #pragma unroll
-  for (int b = 0; b < RB; ++b) {
-    {
-      const int srow = 32 * rg + l32;
-      const int base = srow * 1024 + 8 * hh;
+  for (int b = 0; b < RB; ++b)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+    for (int pr = 0; pr < NRG / RGP; ++pr) {
+      if (rg / RGP == pr) {
+        const int srow = 32 * (rg % RGP) + l32;
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int chunk = (NDB * cg + db) * 4 + i4;
-          const f32x16_t& a = acc[b][db];
-          const u32x2_t pk = {Elt<T>::pack2(a[4 * i4] * scale, a[4 * i4 + 1] * scale),
-                              Elt<T>::pack2(a[4 * i4 + 2] * scale, a[4 * i4 + 3] * scale)};
-          *(__attribute__((address_space(3))) u32x2_t*)(stage + base + ((chunk ^ (srow & 15)) << 4)) = pk;
-        }
-    }
-    lds_barrier();
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int rr = 0; rr < 4 * NRG; ++rr) {
-      const int srow = 4 * NRG * w + rr;
-      const int brow = 32 * (RB * (srow >> 5) + b) + (srow & 31);
-      if (brow < rows && 8 * lane < cols) {
-        const u32x4_t x = lds_read_b128(stage, srow * 1024 + ((lane ^ (srow & 15)) << 4));
-        *(u32x4_t*)(dst + brow * row_stride + 8 * lane) = x;
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x16_t& a = acc[b][db];
+            if constexpr (F32) {
+              const int chunk = (NDB * cg + db) * 8 + 2 * i4 + hh;
+              lds_write_f4(stage, srow * S::RS + ((chunk ^ (srow & 15)) << 4),
+                           (f32x4_t){a[4 * i4] * scale, a[4 * i4 + 1] * scale, a[4 * i4 + 2] * scale,
+                                     a[4 * i4 + 3] * scale});
+            } else {
+              const int chunk = (NDB * cg + db) * 4 + i4;
+              const u32x2_t pk = {Elt<T>::pack2(a[4 * i4] * scale, a[4 * i4 + 1] * scale),
+                                  Elt<T>::pack2(a[4 * i4 + 2] * scale, a[4 * i4 + 3] * scale)};
+              *(__attribute__((address_space(3))) u32x2_t*)(stage + srow * S::RS + ((chunk ^ (srow & 15)) << 4) +
+                                                            8 * hh) = pk;
+            }
+          }
       }
+      lds_barrier();
+#pragma unroll
+      for (int rr = 0; rr < PER_WAVE; ++rr) {
+        const int srow = PER_WAVE * w + rr;
+        const int brow = 32 * (RB * (RGP * pr + srow / 32) + b) + (srow & 31);
+#pragma unroll
+        for (int part = 0; part < PARTS; ++part) {
+          const int chunk = 64 * part + lane;
+          if (brow < rows && chunk * (16 / S::ES) < cols) {
+            const u32x4_t x = lds_read_b128(stage, srow * S::RS + ((chunk ^ (srow & 15)) << 4));
+            *(u32x4_t*)((char*)dst + (brow * row_stride + chunk * (16 / S::ES)) * S::ES) = x;
+          }
+        }
+      }
+      if (b + 1 < RB || pr + 1 < NRG / RGP) lds_barrier();  // the stage is rewritten by the next pass
     }
-    if (b + 1 < RB) lds_barrier();  // the stage is rewritten by the next pass
-  }
 }
 
 // Tile item -> (sequence or batch s, query head h, tile t). Dense grids put the G query heads of

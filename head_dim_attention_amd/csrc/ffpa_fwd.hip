@@ -72,11 +72,12 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   using C = FwdCfg<NC, NDB, QB, NBUF, NW>;
   static_assert(!DEC || (QB == 1 && NW == NC), "decode: one 32-row block per workgroup");
   static_assert(!SPL || (QB == 1 && !DEC), "key-range split: one query block per wave, prefill form");
-  __shared__ __attribute__((aligned(1024))) char k0_raw[C::TILE], v0_raw[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char k1_raw[NBUF == 2 ? C::TILE : 16], v1_raw[NBUF == 2 ? C::TILE : 16];
-  __shared__ __attribute__((aligned(1024))) char x_raw[C::XBYTES];
-  auto kbuf = [&](int b) { return b ? (lds_t*)k1_raw : (lds_t*)k0_raw; };
-  auto vbuf = [&](int b) { return b ? (lds_t*)v1_raw : (lds_t*)v0_raw; };
+  // LDS: K and V tiles of buffer 0, those of buffer 1 (double-buffered forms), the exchange of
+  // partial scores; the epilogue reuses the tile space to write whole rows of O.
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
+  lds_t* const smem = (lds_t*)smem_raw;
+  auto kbuf = [&](int b) { return smem + (b ? 2 * C::TILE : 0); };
+  auto vbuf = [&](int b) { return smem + (b ? 3 * C::TILE : C::TILE); };
 
   // Work item: XCD-aware decode (xcd_item): each XCD runs whole heads, so the tiles of one KV head
   // share that XCD's L2.
@@ -189,7 +190,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     for (int db = 0; db < NDB; ++db) oacc[qb][db] = (f32x16_t){};
   }
 
-  lds_t* const xbuf = (lds_t*)x_raw;
+  lds_t* const xbuf = smem + NBUF * 2 * C::TILE;
 
   // DMA: instruction ii of this wave fills LDS bytes [1024 i, 1024 i + 1024) of a tile, i = w + 4 ii,
   // i.e. tile row R = i / (RS / 1024) (uniform per instruction). Lane l writes physical chunk
@@ -675,11 +676,22 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   // Copies issued during the last step land in LDS that the next workgroup may own.
   wait_vmcnt<0>();
 
+  // Eight-wave prefill forms write O through LDS, whole rows per store (store_block_rows).
+  constexpr bool kRowStore = NW == 8 && !DEC;
+  static_assert(!kRowStore || C::LDS >= store_block_lds<SPL, NW / NC, NC, NDB>(), "epilogue stage");
   if constexpr (DEC || SPL) {
     // ---- decode / split epilogue: this key range's normalised O (fp32) and its LSE in log2 units
     // (-inf and 0 when no key of the range is legal for the row), for the combine pass.
     const float lt = half_sum(lsum[0]);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    if constexpr (kRowStore) {
+      const long long prow0 = ((long long)s * p.hq + h) * sv.lq + qt0;
+      store_block_rows<T, true, NW / NC, NC, 1, NDB>(smem, oacc, inv, p.part_o + (prow0 * p.nsplit + split) * p.d,
+                                                     (long long)p.nsplit * p.d, sv.lq - qt0, p.d);
+      if (row_ok && cg == 0 && hh == 0)
+        p.part_lse[((prow0 + 32 * rg + l32) * p.nsplit) + split] = lt > 0.f ? mref[0] + fast_log2(lt) : -INFINITY;
+      return;
+    }
     if (row_ok) {
       const long long prow = ((long long)s * p.hq + hl) * sv.lq + qi_l;
       float* orow = p.part_o + (prow * p.nsplit + split) * p.d;
@@ -700,6 +712,19 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln(2) * (mref + log2 l); empty rows give 0 and -inf
+  if constexpr (kRowStore) {
+    static_assert(QB == 1, "one query block per wave");
+    const float lt = half_sum(lsum[0]);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    store_block_rows<T, false, NW / NC, NC, 1, NDB>(smem, oacc, inv,
+                                                    (uint16_t*)p.o + sv.o_off + (long long)h * p.o_head +
+                                                        (long long)qt0 * p.o_row,
+                                                    p.o_row, sv.lq - qt0, p.d);
+    const int qi = qw0 + l32;
+    if (qi < sv.lq && cg == 0 && hh == 0)
+      p.lse[sv.lse_off + (long long)h * p.lse_head + qi] = lt > 0.f ? (mref[0] + fast_log2(lt)) * kLn2 : -INFINITY;
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = half_sum(lsum[qb]);
