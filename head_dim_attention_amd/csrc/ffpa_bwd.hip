@@ -1678,8 +1678,7 @@ __device__ __forceinline__ void dq_from_ds_body(const AttnParams& p, int nchunk,
 
   // ---- epilogue: scale, round once, store rows < lq and columns < D (whole rows, through LDS)
   uint16_t* dqh = (uint16_t*)p.dq + sv.q_off + (long long)h * p.q_head;
-  static_assert(C::LDS >= store_block_lds<false, 2, 4, NDB>(), "epilogue stage");
-  store_block_rows<T, false, 2, 4, C::QB, NDB>(smem, acc, p.scale, dqh + (long long)q0 * p.q_row + d0, p.q_row,
+  store_block_rows<T, false, 2, 4, C::QB, NDB, C::LDS>(smem, acc, p.scale, dqh + (long long)q0 * p.q_row + d0, p.q_row,
                                                sv.lq - q0, min(C::DWG, p.d - d0));
 }
 
@@ -1949,8 +1948,7 @@ __device__ __forceinline__ void dv_from_p_body(const AttnParams& p, int nchunk, 
 
   // ---- epilogue: round once, store keys < Lk and columns < D (whole rows, through LDS)
   uint16_t* dvh = (uint16_t*)(DK ? p.dk : p.dv) + sv.k_off + (long long)kvh * p.k_head;
-  static_assert(C::LDS >= store_block_lds<false, 2, 4, NDB>(), "epilogue stage");
-  store_block_rows<T, false, 2, 4, C::KB, NDB>(smem, acc, DK ? p.scale : 1.0f, dvh + (long long)k0 * p.k_row + d0,
+  store_block_rows<T, false, 2, 4, C::KB, NDB, C::LDS>(smem, acc, DK ? p.scale : 1.0f, dvh + (long long)k0 * p.k_row + d0,
                                                p.k_row, sv.lk - k0, min(C::DWG, p.d - d0));
 }
 

@@ -321,25 +321,31 @@ __device__ __forceinline__ int xcd_item(int L, int grid, bool varlen, int heads,
 // chunk c ^ (s % 16)); after a barrier the 8 waves copy them to dst (block row 0, column 0; row
 // stride in elements). Rows at or past `rows` and columns at or past `cols` (a multiple of 8)
 // are not stored. Called by all 8 waves after their last LDS read and DMA wait of the main loop;
-// uses store_block_lds() bytes of LDS at `stage`.
+// uses store_block_lds<..., LDSB>() bytes of LDS at `stage`, at most LDSB (RGP is the largest
+// power of two of row groups whose stage fits in LDSB and 128 KB).
 template <bool F32, int NCG, int NDB>
 struct BlockStore {
   static constexpr int ES = F32 ? 4 : 2;                 // bytes per stored element
   static constexpr int ROWB = NCG * NDB * 32 * ES;       // bytes of a block row
   static constexpr int RS = ROWB <= 1024 ? 1024 : ROWB <= 2048 ? 2048 : 4096;
-  static constexpr int RGP_MAX = 4096 / RS;              // row groups per pass (128 KB of LDS)
 };
-template <bool F32, int NRG, int NCG, int NDB>
-constexpr int store_block_lds() {
-  using S = BlockStore<F32, NCG, NDB>;
-  return 32 * (NRG < S::RGP_MAX ? NRG : S::RGP_MAX) * S::RS;
+template <bool F32, int NRG, int NCG, int NDB, int LDSB>
+constexpr int store_block_rgp() {
+  constexpr int RS = BlockStore<F32, NCG, NDB>::RS;
+  int r = NRG;
+  while (r > 1 && (32 * r * RS > LDSB || 32 * r * RS > 131072)) r /= 2;
+  return r;
 }
-template <class T, bool F32, int NRG, int NCG, int RB, int NDB>
+template <bool F32, int NRG, int NCG, int NDB, int LDSB = 163840>
+constexpr int store_block_lds() {
+  return 32 * store_block_rgp<F32, NRG, NCG, NDB, LDSB>() * BlockStore<F32, NCG, NDB>::RS;
+}
+template <class T, bool F32, int NRG, int NCG, int RB, int NDB, int LDSB = 163840>
 __device__ __forceinline__ void store_block_rows(lds_t* stage, const f32x16_t (&acc)[RB][NDB], float scale,
                                                  void* dst, long long row_stride, int rows, int cols) {
   using S = BlockStore<F32, NCG, NDB>;
-  constexpr int RGP = NRG < S::RGP_MAX ? NRG : S::RGP_MAX;
-  static_assert(NRG * NCG == 8 && NRG % RGP == 0, "8 waves; whole row groups per pass");
+  constexpr int RGP = store_block_rgp<F32, NRG, NCG, NDB, LDSB>();
+  static_assert(NRG * NCG == 8 && NRG % RGP == 0 && 32 * RGP * S::RS <= LDSB, "8 waves; whole row groups per pass");
   constexpr int SROWS = 32 * RGP;       // stage rows per pass
   constexpr int PER_WAVE = SROWS / 8;   // stage rows each wave copies out
   constexpr int PARTS = S::RS / 1024;   // 1 KB store instructions per stage row

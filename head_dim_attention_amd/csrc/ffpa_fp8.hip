@@ -480,23 +480,14 @@ __global__ void __launch_bounds__(512, 2) ffpa_fwd_fp8_kernel(AttnParams p, cons
   const float lp = *(const __attribute__((address_space(3))) float*)(xmbuf + ((w ^ 1) * 32 + l32) * 4);
   const float lt = cg == 0 ? lw + lp : lp + lw;
   const float inv = lt > 0.f ? (av / (448.0f * 448.0f)) / lt : 0.f;
-  if (qi < p.nq) {
-    uint16_t* orow = (uint16_t*)p.o + ((long long)s * p.hq + h) * p.o_head + (long long)qi * p.o_row;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = cg * C::DW + 32 * db + 8 * i4 + 4 * hh;
-        if (d < p.d) {
-          const f32x16_t& o = oacc[db];
-          *(u32x2_t*)(orow + d) = (u32x2_t){Elt<T>::pack2(o[4 * i4] * inv, o[4 * i4 + 1] * inv),
-                                            Elt<T>::pack2(o[4 * i4 + 2] * inv, o[4 * i4 + 3] * inv)};
-        }
-      }
-    if (cg == 0 && hh == 0)
-      p.lse[(long long)s * p.lse_batch + (long long)h * p.lse_head + qi] =
-          lt > 0.f ? (mref + fast_log2(lt)) * kLn2 : -INFINITY;
-  }
+  // O through LDS, whole rows per store (the block: 4 row groups x 2 head-dim halves)
+  wait_vmcnt<0>();
+  store_block_rows<T, false, 4, 2, 1, NDB, C::LDS>(
+      smem, reinterpret_cast<const f32x16_t(&)[1][NDB]>(oacc), inv,
+      (uint16_t*)p.o + ((long long)s * p.hq + h) * p.o_head + (long long)qt0 * p.o_row, p.o_row, p.nq - qt0, p.d);
+  if (qi < p.nq && cg == 0 && hh == 0)
+    p.lse[(long long)s * p.lse_batch + (long long)h * p.lse_head + qi] =
+        lt > 0.f ? (mref + fast_log2(lt)) * kLn2 : -INFINITY;
 }
 
 // ---- forward kernel for D > 512 --------------------------------------------------------------
@@ -753,23 +744,14 @@ __global__ void __launch_bounds__(512, 2) ffpa_fwd_fp8_wide_kernel(AttnParams p,
 #pragma unroll
   for (int c = 0; c < 4; ++c) lt += *(const __attribute__((address_space(3))) float*)(xmbuf + ((4 * rg + c) * 32 + l32) * 4);
   const float inv = lt > 0.f ? (av / (448.0f * 448.0f)) / lt : 0.f;
-  if (qi < p.nq) {
-    uint16_t* orow = (uint16_t*)p.o + ((long long)s * p.hq + h) * p.o_head + (long long)qi * p.o_row;
-#pragma unroll
-    for (int i = 0; i < NQ; ++i)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = oq * C::DQW + 32 * i + 8 * i4 + 4 * hh;
-        if (d < p.d) {
-          const f32x16_t& o = oacc[i];
-          *(u32x2_t*)(orow + d) = (u32x2_t){Elt<T>::pack2(o[4 * i4] * inv, o[4 * i4 + 1] * inv),
-                                            Elt<T>::pack2(o[4 * i4 + 2] * inv, o[4 * i4 + 3] * inv)};
-        }
-      }
-    if (oq == 0 && hh == 0)
-      p.lse[(long long)s * p.lse_batch + (long long)h * p.lse_head + qi] =
-          lt > 0.f ? (mref + fast_log2(lt)) * kLn2 : -INFINITY;
-  }
+  // O through LDS, whole rows per store (the block: 2 row groups x 4 head-dim quarters)
+  wait_vmcnt<0>();
+  store_block_rows<T, false, 2, 4, 1, NQ, C::LDS>(
+      smem, reinterpret_cast<const f32x16_t(&)[1][NQ]>(oacc), inv,
+      (uint16_t*)p.o + ((long long)s * p.hq + h) * p.o_head + (long long)qt0 * p.o_row, p.o_row, p.nq - qt0, p.d);
+  if (qi < p.nq && oq == 0 && hh == 0)
+    p.lse[(long long)s * p.lse_batch + (long long)h * p.lse_head + qi] =
+        lt > 0.f ? (mref + fast_log2(lt)) * kLn2 : -INFINITY;
 }
 
 // Workspace: amax of Q (B Hq floats), K and V (B Hkv each), then K8 (B Hkv Nkv D bytes), then V8^T

@@ -678,7 +678,6 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
 
   // Eight-wave prefill forms write O through LDS, whole rows per store (store_block_rows).
   constexpr bool kRowStore = NW == 8 && !DEC;
-  static_assert(!kRowStore || C::LDS >= store_block_lds<SPL, NW / NC, NC, NDB>(), "epilogue stage");
   if constexpr (DEC || SPL) {
     // ---- decode / split epilogue: this key range's normalised O (fp32) and its LSE in log2 units
     // (-inf and 0 when no key of the range is legal for the row), for the combine pass.
@@ -686,7 +685,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     if constexpr (kRowStore) {
       const long long prow0 = ((long long)s * p.hq + h) * sv.lq + qt0;
-      store_block_rows<T, true, NW / NC, NC, 1, NDB>(smem, oacc, inv, p.part_o + (prow0 * p.nsplit + split) * p.d,
+      store_block_rows<T, true, NW / NC, NC, 1, NDB, C::LDS>(smem, oacc, inv, p.part_o + (prow0 * p.nsplit + split) * p.d,
                                                      (long long)p.nsplit * p.d, sv.lq - qt0, p.d);
       if (row_ok && cg == 0 && hh == 0)
         p.part_lse[((prow0 + 32 * rg + l32) * p.nsplit) + split] = lt > 0.f ? mref[0] + fast_log2(lt) : -INFINITY;
@@ -716,7 +715,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     static_assert(QB == 1, "one query block per wave");
     const float lt = half_sum(lsum[0]);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    store_block_rows<T, false, NW / NC, NC, 1, NDB>(smem, oacc, inv,
+    store_block_rows<T, false, NW / NC, NC, 1, NDB, C::LDS>(smem, oacc, inv,
                                                     (uint16_t*)p.o + sv.o_off + (long long)h * p.o_head +
                                                         (long long)qt0 * p.o_row,
                                                     p.o_row, sv.lq - qt0, p.d);
