@@ -83,7 +83,7 @@ def test_varlen_workload(lib):
                          to64(dv[a:b, h]), o_r, lse_r, dq_r, dk_r, dv_r)
 
 
-@pytest.mark.parametrize("name", ["dense_d512_n8192", "gqa_causal_d1024_n8192"])
+@pytest.mark.parametrize("name", ["dense_d512_n8192", "gqa_causal_d1024_n8192", "causal_d512_n4096"])
 def test_dense_workload_every_group_equal(lib, name):
     """Whole-tensor check of the head and XCD mapping at full size: with every KV group given the
     same inputs, every group's O, LSE, dQ, dK and dV must be bit-identical (the kernels are
@@ -104,6 +104,23 @@ def test_dense_workload_every_group_equal(lib, name):
         assert torch.equal(o[:, hs], o[:, h0]) and torch.equal(lse[:, hs], lse[:, h0]), f"group {grp} forward"
         assert torch.equal(dq[:, hs], dq[:, h0]), f"group {grp} dq"
         assert torch.equal(dk[:, grp], dk[:, 0]) and torch.equal(dv[:, grp], dv[:, 0]), f"group {grp} dk/dv"
+
+
+def test_small_causal_workload_run_to_run(lib):
+    """The small causal grid takes the key-range split forward and the one-launch products (their
+    item orders balance the load at run time, but every output element is still formed by one
+    workgroup in a fixed order): two runs give bit-identical O, LSE, dQ, dK and dV."""
+    w = W.get("causal_d512_n4096")
+    q, k, v, do = W.workload_inputs(w, seed=2026)
+    print("workload causal_d512_n4096: two runs", flush=True)
+    qc, kc, vc, doc = (x.cuda() for x in (q, k, v, do))
+    runs = []
+    for _ in range(2):
+        o, lse = lib.ffpa_fwd(qc, kc, vc, causal=True)
+        runs.append((o, lse, *lib.ffpa_bwd(qc, kc, vc, o, doc, lse, causal=True)))
+    torch.cuda.synchronize()
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
 
 
 def test_varlen_workload_every_head_equal(lib):
