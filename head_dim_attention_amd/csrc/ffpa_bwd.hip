@@ -503,7 +503,6 @@ __global__ void __launch_bounds__(512, 2) ffpa_bwd_pp_kernel(AttnParams p) {
   static_assert(MODE == kDQ || MODE == kDK, "dK and dQ only");
   constexpr bool OWN_Q = MODE == kDQ;
   using C = PpCfg<NDB>;
-  constexpr int NC = C::NC;
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
   lds_t* smem = (lds_t*)smem_raw;
 

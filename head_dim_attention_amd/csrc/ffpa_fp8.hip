@@ -85,7 +85,7 @@ __device__ __forceinline__ float quant_factor(float amax) { return amax > 0.f ? 
 // K8[head][row][d] = e4m3(K * 448 / amax): 16 values per thread.
 template <class T>
 __global__ void __launch_bounds__(256) ffpa_fp8_quant_rows_kernel(const uint16_t* x, uint8_t* x8, const float* amax,
-                                                                  long long head_elems, int d) {
+                                                                  long long head_elems) {
   const int head = blockIdx.y;
   const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 16;
   if (i >= head_elems) return;
@@ -791,7 +791,7 @@ static hipError_t launch_fp8_cfg(AttnParams p, char* ws, hipStream_t st) {
   hipLaunchKernelGGL(ffpa_fp8_amax_kernel<T>, dim3((unsigned)((kvelems + kAmaxChunk - 1) / kAmaxChunk), p.batch * p.hkv),
                      dim3(256), 0, st, (const uint16_t*)p.v, kvelems, amax_v);
   hipLaunchKernelGGL(ffpa_fp8_quant_rows_kernel<T>, dim3((unsigned)((kvelems / 16 + 255) / 256), p.batch * p.hkv),
-                     dim3(256), 0, st, (const uint16_t*)p.k, k8, amax_k, kvelems, p.d);
+                     dim3(256), 0, st, (const uint16_t*)p.k, k8, amax_k, kvelems);
   hipLaunchKernelGGL(ffpa_fp8_quant_vt_kernel<T>, dim3(lay.np / 64, (p.d + 63) / 64, p.batch * p.hkv), dim3(256), 0,
                      st, (const uint16_t*)p.v, v8t, amax_v, p.nkv, p.d, lay.np);
   if constexpr (NDB <= 8) {

@@ -263,15 +263,10 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   };
 
   // ---- pipeline pieces (each runs the same barriers in every wave) --------------------------
-  auto top = [&](int j) {
-    if constexpr (NBUF == 2) {
-      // In flight: K_j (issued during the scores of step j - 1), then V_j. K_j is needed now.
-      wait_vmcnt<C::NINSTR>();
-      lds_barrier();
-    } else {
-      wait_vmcnt<C::NINSTR>();  // K_j has landed; V_j may still be in flight
-      lds_barrier();
-    }
+  // Start of a step: K_j has landed (in flight behind it: V_j, which is waited for later).
+  auto top = [&]() {
+    wait_vmcnt<C::NINSTR>();
+    lds_barrier();
   };
 
   // attn_mask: this lane's mask rows and the raw bits of one tile (mask_fetch). The two-group
@@ -632,7 +627,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   // needs rescaling here and exp2 stays below 256.
   int j = jbeg;
   for (; j < jend; ++j) {
-    top(j);
+    top();
     scores(j, sacc);
     float mt[QB];
     tile_max(sacc, mt);
@@ -652,7 +647,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   // softmax with a lazily updated reference. Tile j's scores are already in sacc.
   for (bool fresh = false; j < jend; ++j, fresh = true) {
     if (fresh) {
-      top(j);
+      top();
       scores(j, sacc);
     }
     float mt[QB];
