@@ -492,9 +492,9 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
     //           softmax, P V)
     //   slot 1: group 0 finishes tile j                 | group 1 forms partial scores of tile j
     // so in every slot one wave of each SIMD multiplies scores while the other does the softmax
-    // and then multiplies P V. Group 0 copies K of tile j + 1 during its score MFMAs (K_{j-1},
+    // and then multiplies P V. Group 0 copies K of tile j + 1 after its score MFMAs (K_{j-1},
     // last read in slot 1 of step j - 1, has been released) and completes it before slot 0 of
-    // step j + 1; group 1 copies V of tile j + 1 during its score MFMAs (V_{j-1}, last read in
+    // step j + 1; group 1 copies V of tile j + 1 after its score MFMAs (V_{j-1}, last read in
     // slot 0 of step j, has been released) and completes it before slot 1 of step j + 1. Every
     // wave keeps its own exchange slot, which its partner reads in the next slot.
     const int grp = w >> 2, wg = w & 3;
@@ -508,12 +508,15 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
       lds_t* dst = (grp == 0 ? kbuf(j & 1) : vbuf(j & 1)) + i * 1024;
       dma16_buf(gsrc.rs, gvoff[ii & 3], min(j * 32 + i, sv.lk - 1) * gsrc.rb, dst);
     };
+    // The group's copies go after its score products (and their exchange writes), not between
+    // them: a wave held at a copy issue then no longer holds back its own MFMAs, which are in the
+    // pipe, and the partner's P V products have the pipe to themselves (4.40 -> 4.06 ms at the
+    // headline shape). The tile has the rest of this slot and the next one to land.
     auto s_phase = [&](int j) {
-      s_partial(j, sacc, [&](int kb) {
+      s_partial(j, sacc, [&](int) {});
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ii = 0; ii < GCOPY; ++ii)
-          if (kb == (ii * 2 * NDB) / GCOPY) gcopy(j + 1, ii);
-      });
+      for (int ii = 0; ii < GCOPY; ++ii) gcopy(j + 1, ii);
     };
     auto p_phase = [&](int j) {
       s_combine(j, sacc);
