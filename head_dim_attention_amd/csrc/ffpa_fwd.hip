@@ -440,10 +440,12 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
   auto pv_mma = [&](int j, const uint32_t (&pb)[QB][2][4], auto&& copy_at) {
     const lds_t* vt = vbuf(NBUF == 2 ? (j & 1) : 0);
     const uint32_t vta = kFreshOff ? (uint32_t)opaque_v((int)lds_addr(vt)) : lds_addr(vt);
+    // keys 0..15 of the tile (P registers 0..7) for every column block first, so the first half
+    // of the products needs only the first half of P
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int db = 0; db < NDB; ++db) {
         const s16x4_t lo = lds_read_tr16_at(v_addr(vta, db, kb2, 0));
         const s16x4_t hi = lds_read_tr16_at(v_addr(vta, db, kb2, 1));
         const u32x4_t a = join_tr(lo, hi);
@@ -452,7 +454,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
           const u32x4_t bop = {pb[qb][kb2][0], pb[qb][kb2][1], pb[qb][kb2][2], pb[qb][kb2][3]};
           oacc[qb][db] = Elt<T>::mma(a, bop, oacc[qb][db]);
         }
-        copy_at(2 * db + kb2);
+        copy_at(NDB * kb2 + db);
       }
     }
     if constexpr (QB == 1) pin_lds_mfma_pipeline<2 * NDB, fwd_ahead<NC, NDB>(), 2>();
