@@ -520,7 +520,21 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
 #pragma unroll
       for (int ii = 0; ii < GCOPY; ++ii) gcopy(j + 1, ii);
     };
+    // Without a mask, the V^T operand of the first P V product is requested ahead of the exchange
+    // reads, so that its LDS latency overlaps the wait for the partner's partial scores (0.9% at
+    // the headline shape; the masked form has no registers to spare for it).
+    const uint32_t vta0 = lds_addr(vbuf(0)), vta1 = lds_addr(vbuf(1));
     auto p_phase = [&](int j) {
+      const uint32_t vta = (j & 1) ? vta1 : vta0;
+      auto vread = [&](int m) {
+        const int kb2 = m / NDB, db = m % NDB;
+        return join_tr(lds_read_tr16_at(v_addr(vta, db, kb2, 0)), lds_read_tr16_at(v_addr(vta, db, kb2, 1)));
+      };
+      u32x4_t a0 = {};
+      if constexpr (!MASK) {
+        a0 = vread(0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       s_combine(j, sacc);
       // Online softmax with a lazily updated reference max: a row's reference is its first finite
       // tile max, raised (with the matching rescale of O and l) only when a tile max exceeds it
@@ -548,8 +562,28 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) ffpa_fwd_kernel(AttnParams p)
       make_p(sacc, pb);
       if constexpr (MASK) {
         if (cg == 0) mask_fetch(j + 1);  // past the last tile: clamped to the row, unused
+        pv_mma(j, pb, [](int) {});
+      } else {
+        // keys-first order as in pv_mma; operand m = NDB kb2 + db, the first one already read
+        static_assert(QB == 1, "one query block per wave");
+#pragma unroll
+        for (int m = 0; m < 2 * NDB; ++m) {
+          const int kb2 = m / NDB, db = m % NDB;
+          const u32x4_t a = m == 0 ? a0 : vread(m);
+          const u32x4_t bop = {pb[0][kb2][0], pb[0][kb2][1], pb[0][kb2][2], pb[0][kb2][3]};
+          oacc[0][db] = Elt<T>::mma(a, bop, oacc[0][db]);
+        }
+        // the operand reads run AHEAD MFMAs ahead, as in pin_lds_mfma_pipeline, the first operand
+        // already read
+        constexpr int AHEAD = fwd_ahead<NC, NDB>();
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (AHEAD - 1), 0);
+#pragma unroll
+        for (int i = 0; i < 2 * NDB - AHEAD; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
       }
-      pv_mma(j, pb, [](int) {});
     };
     if constexpr (MASK) {
       if (cg == 0) mask_fetch(jbeg);
