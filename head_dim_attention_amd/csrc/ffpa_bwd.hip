@@ -887,6 +887,37 @@ static hipError_t launch_bwd_pp(AttnParams p, hipStream_t st) {
 // finishing group: the multiplying waves issue nothing but LDS reads and MFMAs. (j counts the
 // item's steps; with a key-range split, step j covers key tile split + j nsplit.)
 // ------------------------------------------------------------------------------------------------
+// Stationary B operands of a P/dS wave (its 32 queries x one head-dim part of at most 512 bytes),
+// staged through 16 KB of LDS so that the copies read whole rows: copy i brings rows 2 i and
+// 2 i + 1 (lane (h', c): row 2 i + h', 16-byte chunk c ^ row of the part, so that the reads below
+// hit distinct banks), then lane (h, n) reads query n, columns col0 + 16 kb + 8 h + 0..7. Loading
+// the B layout directly reads 32 rows x 32 bytes per instruction, which takes about twice as long
+// per workgroup. Rows at or past lq repeat row lq - 1; columns at or past the head dim are zero.
+// Only the calling wave touches `stage`; it waits for its own reads before returning.
+template <int KSTEPS>
+__device__ __forceinline__ void stage_b_operand(const uint16_t* head, long long row_elems, int row0, int lq,
+                                                int col0, int d, lds_t* stage, u32x4_t (&dst)[KSTEPS]) {
+  constexpr int NCH = 2 * KSTEPS;  // 16-byte chunks of the part
+  static_assert(NCH <= 32, "at most 512 bytes of columns per wave");
+  const int lane = threadIdx.x & 63, hh = lane >> 5, l32 = lane & 31;
+  const uint32_t span = (uint32_t)min(((long long)(lq - 1) * row_elems + d) * 2, (long long)0xFFFFFFF0);
+  const i32x4_t rs = make_rsrc(head, span);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 2 * i + hh;
+    const long long row = min(row0 + r, lq - 1);
+    const int col = min(col0 + min(l32 ^ r, NCH - 1) * 8, d - 8);
+    dma16_buf(rs, (int)(uint32_t)((row * row_elems + col) * 2), 0, stage + i * 1024);
+  }
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int kb = 0; kb < KSTEPS; ++kb) {
+    const u32x4_t x = lds_read_b128(stage, l32 * 512 + (((2 * kb + hh) ^ l32) << 4));
+    dst[kb] = col0 + kb * 16 + hh * 8 < d ? x : (u32x4_t){0u, 0u, 0u, 0u};
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));  // the reads are done: `stage` may be rewritten
+}
+
 // LDS operands requested ahead in the P/dS kernel's score products.
 constexpr int kPdsAhead = 2;
 template <int NDB>
@@ -963,22 +994,22 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_kernel(AttnParams p) {
   auto tile_of = [&](int jj) { return split + jj * p.nsplit; };
   if (nsteps == 0 && split > 0) return;
 
-  // Q and dO columns of this wave as B operands: lane (h, n) holds query n, dims 16 kb + 8 h + 0..7.
-  const int qi = qw0 + l32;
-  const long long qrow = sv.q_off + (long long)h * p.q_head + (long long)min(qi, sv.lq - 1) * p.q_row;
-  u32x4_t qreg[C::KSTEPS], oreg[C::KSTEPS];
-#pragma unroll
-  for (int kb = 0; kb < C::KSTEPS; ++kb) {
-    const int dim = cg * C::DW + kb * 16 + hh * 8;
-    const bool in = dim < p.d;
-    qreg[kb] = in ? *(const u32x4_t*)((const uint16_t*)p.q + qrow + dim) : (u32x4_t){0u, 0u, 0u, 0u};
-    oreg[kb] = in ? *(const u32x4_t*)((const uint16_t*)p.dout + qrow + dim) : (u32x4_t){0u, 0u, 0u, 0u};
-  }
   // The query's LSE in log2 units (+inf for a row without a legal key makes P = 0) and Delta.
+  const int qi = qw0 + l32;
   const long long li = sv.lse_off + (long long)h * p.lse_head + min(qi, sv.lq - 1);
   const float lse_raw = p.lse_in[li];
   const float lse2 = lse_raw == -INFINITY ? INFINITY : lse_raw * kLog2e;
   const float dlt = p.delta[li];
+  // Q and dO columns of this wave as B operands: lane (h, n) holds query n, dims 16 kb + 8 h + 0..7,
+  // staged through the tile buffers (16 KB per wave) before the first tile is copied.
+  u32x4_t qreg[C::KSTEPS], oreg[C::KSTEPS];
+  {
+    const long long hq0 = sv.q_off + (long long)h * p.q_head;
+    lds_t* const stage = smem + w * 16384;
+    stage_b_operand<C::KSTEPS>((const uint16_t*)p.q + hq0, p.q_row, qw0, sv.lq, cg * C::DW, p.d, stage, qreg);
+    stage_b_operand<C::KSTEPS>((const uint16_t*)p.dout + hq0, p.q_row, qw0, sv.lq, cg * C::DW, p.d, stage, oreg);
+  }
+  lds_barrier();  // every wave has read its staged operands: the tile buffers are free
 
   // The head's P and dS blocks (Lk rows of round_up(Lq, 8) queries).
   const long long hoff = dsv.base + (long long)h * dsv.head;
@@ -1262,23 +1293,23 @@ __global__ void __launch_bounds__(512, 2) ffpa_pds_wide_kernel(AttnParams p) {
   const int jb = min(split * per, ntk), je = min(jb + per, ntk);
   if (jb >= je && split > 0) return;
 
-  // Q and dO columns of this wave's quarter as B operands: lane (h, n) holds query n, dims
-  // 16 kb + 8 h + 0..7 of the quarter.
-  const int qi = qw0 + l32;
-  const long long qrow = sv.q_off + (long long)h * p.q_head + (long long)min(qi, sv.lq - 1) * p.q_row;
-  u32x4_t qreg[C::KSTEPS], oreg[C::KSTEPS];
-#pragma unroll
-  for (int kb = 0; kb < C::KSTEPS; ++kb) {
-    const int dim = cg * C::DW + kb * 16 + hh * 8;
-    const bool in = dim < p.d;
-    qreg[kb] = in ? *(const u32x4_t*)((const uint16_t*)p.q + qrow + dim) : (u32x4_t){0u, 0u, 0u, 0u};
-    oreg[kb] = in ? *(const u32x4_t*)((const uint16_t*)p.dout + qrow + dim) : (u32x4_t){0u, 0u, 0u, 0u};
-  }
   // The query's LSE in log2 units (+inf for a row without a legal key makes P = 0) and Delta.
+  const int qi = qw0 + l32;
   const long long li = sv.lse_off + (long long)h * p.lse_head + min(qi, sv.lq - 1);
   const float lse_raw = p.lse_in[li];
   const float lse2 = lse_raw == -INFINITY ? INFINITY : lse_raw * kLog2e;
   const float dlt = p.delta[li];
+  // Q and dO columns of this wave's quarter as B operands: lane (h, n) holds query n, dims
+  // 16 kb + 8 h + 0..7 of the quarter, staged through the K and V tiles (16 KB per wave) before
+  // the first tile is copied.
+  u32x4_t qreg[C::KSTEPS], oreg[C::KSTEPS];
+  {
+    const long long hq0 = sv.q_off + (long long)h * p.q_head;
+    lds_t* const stage = kbuf + w * 16384;
+    stage_b_operand<C::KSTEPS>((const uint16_t*)p.q + hq0, p.q_row, qw0, sv.lq, cg * C::DW, p.d, stage, qreg);
+    stage_b_operand<C::KSTEPS>((const uint16_t*)p.dout + hq0, p.q_row, qw0, sv.lq, cg * C::DW, p.d, stage, oreg);
+  }
+  lds_barrier();  // every wave has read its staged operands: the tile buffers are free
 
   // The head's P and dS blocks (Lk rows of round_up(Lq, 8) queries).
   const long long hoff = dsv.base + (long long)h * dsv.head;
