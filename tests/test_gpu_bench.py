@@ -27,6 +27,11 @@ def test_bench_json_line():
         assert key in d, key
     assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1 and d["value"] > 0 and d["dtype"] == "bf16"
     assert d["config"]["workload"] == "dense_d512_n8192"
+    # the step is timed with events only between steps; the per-launch pass is reported beside it,
+    # and both lie within a few percent of the host wall time of a step
+    assert d["event_ms_per_step"] > 0 and d["stage_event_sum_ms"] > 0
+    assert abs(d["event_ms_per_step"] - d["ms_per_step"]) < 0.05 * d["ms_per_step"]
+    assert set(d["kernels"]) >= {"fwd", "pds", "dk", "dv", "dq"}
     roof = d["roofline"]
     assert set(roof) >= {"bound", "achieved", "peak", "unit", "frac", "traffic"}
     assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and 0 < roof["frac"] < 1
@@ -43,6 +48,8 @@ def test_bench_json_line():
         c = cfg[name]
         assert 0 < c["fwd_frac"] < 1 and 0 < c["fwdbwd_frac"] < 1, name
         assert c["fwdbwd_ms"] > c["fwd_ms"] > 0, name
+        if name != "varlen_causal_d512":
+            assert c["stage_event_sum_ms"] > c["fwd_ms"] and c["bwd_ms"] > 0, name
     assert cfg["gqa_causal_d1024_n8192"]["kernels"]["dk"]["ms"] > 0
     assert cfg["varlen_causal_d512"]["workspace_gib"] <= cfg["varlen_causal_d512"]["workspace_bound_gib"]
     rec = d["recompute_bwd"]
